@@ -1,0 +1,342 @@
+"""Pins for the fp64 oracle: every check compares it with something other
+than itself (closed forms, special cases that reduce to DeltaNet, Gated
+DeltaNet and linear attention, exact-rational brute force through dense
+transition matrices, hand-derived values, invariants).
+
+Sources: "Kimi Delta Attention 徹底解説" (tech-tide.dev) sections
+"なぜ今「線形アテンション」なのか" and "Kimi Delta Attention の仕組み";
+"Kimi Linear、独自の土俵でFull Attentionを上回る" (remio.ai) sections
+"Kimi Linearがより賢いRecurrent Memoryを使う方法" and
+"オープンコード…リスク" (state layout, chunk boundaries, batching, needle).
+"""
+
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import kda_chunked, kda_decode_step, kda_recurrent, kda_recurrent_varlen, max_rel_err
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rand_inputs(rng, B, T, H, DK, DV, s0=True):
+    q = rng.standard_normal((B, T, H, DK))
+    k = rng.standard_normal((B, T, H, DK))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    v = rng.standard_normal((B, T, H, DV))
+    a = np.exp(-np.exp(rng.uniform(-5, -1, (B, T, H, DK))))
+    b = 1 / (1 + np.exp(-rng.standard_normal((B, T, H))))
+    S0 = rng.standard_normal((B, H, DK, DV)) if s0 else None
+    return q, k, v, a, b, S0
+
+
+# ---------------------------------------------------------------- golden ---
+def test_golden_hand_worked():
+    """Hand-derived values (fixture cites its derivation from the explainer's
+    definition of the recurrence)."""
+    with open(os.path.join(GOLDEN, "hand_worked_kda.json")) as f:
+        fx = json.load(f)
+    for case in fx["cases"]:
+        q = np.array(case["q"], float)[None, :, None, :]
+        k = np.array(case["k"], float)[None, :, None, :]
+        v = np.array(case["v"], float)[None, :, None, :]
+        a = np.array(case["alpha"], float)[None, :, None, :]
+        b = np.array(case["beta"], float)[None, :, None]
+        S0 = np.array(case["S0"], float)[None, None]
+        o, S = kda_recurrent(q, k, v, a, b, S0)
+        np.testing.assert_allclose(o[0, :, 0], np.array(case["o"], float), rtol=0, atol=1e-15)
+        np.testing.assert_allclose(S[0, 0], np.array(case["S_final"], float), rtol=0, atol=1e-15)
+
+
+# ------------------------------------------------------------------- P1 ---
+@pytest.mark.parametrize("chunk", [1, 7, 16, 64, 300])
+def test_p1_chunk_form_equals_recurrence(chunk):
+    """The chunked regrouping reaches the token recurrence's result (the
+    explainer: both modes come from one formulation), for any chunk size,
+    partial last chunk and a non-zero incoming state."""
+    rng = np.random.default_rng(1)
+    q, k, v, a, b, S0 = rand_inputs(rng, 2, 203, 2, 12, 9)
+    o_r, S_r = kda_recurrent(q, k, v, a, b, S0)
+    o_c, S_c = kda_chunked(q, k, v, a, b, S0, chunk=chunk)
+    assert max_rel_err(o_c, o_r) < 1e-12
+    assert max_rel_err(S_c, S_r) < 1e-12
+
+
+# ------------------------------------------------------------------- P2 ---
+def test_p2_beta_zero_is_decay_only():
+    """beta = 0 writes nothing: only the channel-wise forget acts, so
+    S_T = Diag(prod_t alpha_t) S0 and o_t = (Diag(gamma_t) S0)^T q_t."""
+    rng = np.random.default_rng(2)
+    q, k, v, a, b, S0 = rand_inputs(rng, 1, 40, 3, 8, 5)
+    b[:] = 0.0
+    o, S = kda_recurrent(q, k, v, a, b, S0)
+    gam = np.cumprod(a, axis=1)  # [B,T,H,DK]
+    o_cf = np.einsum("bthk,bhkv,bthk->bthv", gam, S0, q)
+    S_cf = gam[:, -1][..., None] * S0
+    assert max_rel_err(o, o_cf) < 1e-13
+    assert max_rel_err(S, S_cf) < 1e-13
+
+
+def test_p2_decay_acts_on_key_channels():
+    """One channel forgets completely fast, the rest keep: only that row of S
+    shrinks (the gate is per key channel, i.e. per row of S)."""
+    DK, DV, T = 4, 3, 5
+    S0 = np.arange(1, DK * DV + 1, dtype=float).reshape(1, 1, DK, DV)
+    a = np.ones((1, T, 1, DK))
+    a[..., 2] = 0.5
+    q = np.zeros((1, T, 1, DK))
+    k = np.zeros((1, T, 1, DK))
+    k[..., 0] = 1.0
+    v = np.zeros((1, T, 1, DV))
+    b = np.zeros((1, T, 1))
+    _, S = kda_recurrent(q, k, v, a, b, S0)
+    expect = S0.copy()
+    expect[0, 0, 2] *= 0.5 ** T
+    np.testing.assert_array_equal(S, expect)
+
+
+# ------------------------------------------------------------------- P3 ---
+def test_p3_delta_rule_exact_replacement():
+    """alpha = 1, beta = 1 (DeltaNet): after writing v under a unit key the
+    state returns exactly v for that key, and rewriting a key replaces its
+    value instead of adding to it (the explainer's contrast of additive
+    linear attention with the delta rule)."""
+    rng = np.random.default_rng(3)
+    DK, DV = 16, 6
+    Q, _ = np.linalg.qr(rng.standard_normal((DK, DK)))
+    keys = Q.T[:5]                      # 5 orthonormal keys
+    vals = rng.standard_normal((5, DV))
+    newv = rng.standard_normal(DV)
+    seq_k = np.concatenate([keys, keys[1:2]])          # rewrite key 1 at the end
+    seq_v = np.concatenate([vals, newv[None]])
+    T = len(seq_k)
+    k = seq_k[None, :, None, :]
+    v = seq_v[None, :, None, :]
+    a = np.ones((1, T, 1, DK))
+    b = np.ones((1, T, 1))
+    q = k.copy()
+    o, S = kda_recurrent(q, k, v, a, b)
+    # reading with the key just written returns the value just written
+    np.testing.assert_allclose(o[0, :, 0], seq_v, atol=1e-13)
+    # afterwards: key 1 holds the new value only, other keys keep theirs
+    expect = vals.copy()
+    expect[1] = newv
+    np.testing.assert_allclose(keys @ S[0, 0], expect, atol=1e-13)
+
+
+def test_p3_prediction_error_is_zero_after_write():
+    """With alpha = 1, beta = 1 and a unit key, S_t^T k_t = v_t for any prior
+    state: the write removes the whole prediction error."""
+    rng = np.random.default_rng(31)
+    q, k, v, a, b, S0 = rand_inputs(rng, 1, 1, 4, 10, 7)
+    a[:] = 1.0
+    b[:] = 1.0
+    _, S = kda_recurrent(q, k, v, a, b, S0)
+    np.testing.assert_allclose(np.einsum("bhkv,bhk->bhv", S, k[:, 0]), v[:, 0], atol=1e-13)
+
+
+# ------------------------------------------------------------------- P4 ---
+def test_p4_scalar_gate_is_gated_deltanet():
+    """With alpha_t the same for every channel, KDA is Gated DeltaNet:
+    S_t = a_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T (decay the
+    whole state by one scalar, then the delta write)."""
+    rng = np.random.default_rng(4)
+    q, k, v, a, b, S0 = rand_inputs(rng, 1, 30, 2, 8, 5)
+    sc = a[..., :1]
+    a = np.broadcast_to(sc, a.shape).copy()
+    o, S = kda_recurrent(q, k, v, a, b, S0)
+    DK = q.shape[-1]
+    for h in range(2):
+        St = S0[0, h].copy()
+        for t in range(30):
+            kt = k[0, t, h]
+            M = sc[0, t, h, 0] * (np.eye(DK) - b[0, t, h] * np.outer(kt, kt))
+            St = M @ St + b[0, t, h] * np.outer(kt, v[0, t, h])
+            np.testing.assert_allclose(o[0, t, h], St.T @ q[0, t, h], atol=1e-12)
+        np.testing.assert_allclose(S[0, h], St, atol=1e-12)
+
+
+# ------------------------------------------------------------------- P5 ---
+def test_p5_orthogonal_keys_reduce_to_linear_attention():
+    """alpha = 1 and mutually orthogonal keys (not unit length): the delta
+    rule never sees a prediction, so KDA is linear attention,
+    o_t = sum_{i<=t} beta_i <k_i|q_t> v_i (the re-association of the
+    explainer's linear-attention section)."""
+    rng = np.random.default_rng(5)
+    DK, DV, T = 12, 4, 9
+    Q, _ = np.linalg.qr(rng.standard_normal((DK, DK)))
+    keys = Q.T[:T] * rng.uniform(0.5, 2.0, (T, 1))
+    q = rng.standard_normal((1, T, 1, DK))
+    v = rng.standard_normal((1, T, 1, DV))
+    b = rng.uniform(0.1, 1.0, (1, T, 1))
+    a = np.ones((1, T, 1, DK))
+    o, _ = kda_recurrent(q, keys[None, :, None, :], v, a, b)
+    for t in range(T):
+        ref = sum(b[0, i, 0] * (keys[i] @ q[0, t, 0]) * v[0, i, 0] for i in range(t + 1))
+        np.testing.assert_allclose(o[0, t, 0], ref, atol=1e-13)
+
+
+# ------------------------------------------------------------------- P6 ---
+def _dyadic(rng, shape, choices):
+    return np.array([Fraction(choices[i]) for i in rng.integers(0, len(choices), size=int(np.prod(shape)))],
+                    dtype=object).reshape(shape)
+
+
+def _brute_transitions(q, k, v, a, b, S0):
+    """Multiply out S_t = A_t S_{t-1} + beta_t k_t v_t^T with the explicit
+    d_k x d_k transition A_t = Diag(alpha_t) - beta_t k_t (alpha_t * k_t)^T
+    (the diagonal-plus-low-rank transition), in whatever number type the
+    arrays hold."""
+    T, DK = k.shape
+    S = S0.copy()
+    outs = []
+    for t in range(T):
+        A = np.zeros((DK, DK), dtype=object)
+        for i in range(DK):
+            for j in range(DK):
+                A[i, j] = (a[t, i] if i == j else 0) - b[t] * k[t, i] * a[t, j] * k[t, j]
+        S = A.dot(S) + b[t] * np.outer(k[t], v[t])
+        outs.append(S.T.dot(q[t]))
+    return np.array(outs), S
+
+
+def test_p6_exact_rational_brute_force():
+    """Exact arithmetic on dyadic inputs (T <= 16, d = 4): the fp64 oracle
+    must agree with the exact dense-transition product to rounding."""
+    rng = np.random.default_rng(6)
+    T, DK, DV = 16, 4, 3
+    vals = ["-1", "-1/2", "-1/4", "0", "1/4", "1/2", "3/4", "1"]
+    q = _dyadic(rng, (T, DK), vals)
+    k = _dyadic(rng, (T, DK), vals)
+    v = _dyadic(rng, (T, DV), vals + ["2", "-3"])
+    a = _dyadic(rng, (T, DK), ["1/4", "1/2", "3/4", "7/8", "1"])
+    b = _dyadic(rng, (T,), ["0", "1/4", "1/2", "1", "3/2"])
+    S0 = _dyadic(rng, (DK, DV), vals)
+    o_ex, S_ex = _brute_transitions(q, k, v, a, b, S0)
+    f = lambda x: np.array(x, dtype=float)  # noqa: E731
+    o, S = kda_recurrent(f(q)[None, :, None], f(k)[None, :, None], f(v)[None, :, None],
+                         f(a)[None, :, None], f(b)[None, :, None], f(S0)[None, None])
+    o_ex, S_ex = f(o_ex), f(S_ex)
+    assert max_rel_err(o[0, :, 0], o_ex) < 1e-14
+    assert max_rel_err(S[0, 0], S_ex) < 1e-14
+
+
+def test_p6_dense_transition_fp64_d64():
+    """The same dense-transition route in fp64 at d = 64."""
+    rng = np.random.default_rng(61)
+    q, k, v, a, b, S0 = rand_inputs(rng, 1, 12, 1, 64, 64)
+    o, S = kda_recurrent(q, k, v, a, b, S0)
+    S_ref = S0[0, 0]
+    for t in range(12):
+        kt, at, bt = k[0, t, 0], a[0, t, 0], b[0, t, 0]
+        A = np.diag(at) - bt * np.outer(kt, at * kt)
+        S_ref = A @ S_ref + bt * np.outer(kt, v[0, t, 0])
+        np.testing.assert_allclose(o[0, t, 0], S_ref.T @ q[0, t, 0], rtol=0, atol=1e-12)
+    assert max_rel_err(S[0, 0], S_ref) < 1e-13
+
+
+# ------------------------------------------------------------------- P7 ---
+def test_p7_linear_in_values_and_state():
+    """For fixed keys, gates and queries, (V, S0) -> (O, S_T) is linear."""
+    rng = np.random.default_rng(7)
+    q, k, v1, a, b, S1 = rand_inputs(rng, 1, 50, 2, 8, 6)
+    v2 = rng.standard_normal(v1.shape)
+    S2 = rng.standard_normal(S1.shape)
+    c1, c2 = 0.7, -1.9
+    o1, T1 = kda_recurrent(q, k, v1, a, b, S1)
+    o2, T2 = kda_recurrent(q, k, v2, a, b, S2)
+    o3, T3 = kda_recurrent(q, k, c1 * v1 + c2 * v2, a, b, c1 * S1 + c2 * S2)
+    assert max_rel_err(o3, c1 * o1 + c2 * o2) < 1e-12
+    assert max_rel_err(T3, c1 * T1 + c2 * T2) < 1e-12
+
+
+# ------------------------------------------------------------------- P8 ---
+def needle_inputs(T, p, DK, DV, rng):
+    """Needle under key e_0 at position p; channel 0 never decays and no other
+    key touches it.  Any read with q = e_0 after p must return the needle."""
+    q, k, v, a, b, _ = rand_inputs(rng, 1, T, 1, DK, DV, s0=False)
+    k[..., 0] = 0.0
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    a[..., 0] = 1.0
+    k[0, p, 0] = 0.0
+    k[0, p, 0, 0] = 1.0
+    b[0, p, 0] = 1.0
+    q[0, p + 1:, 0] = 0.0
+    q[0, p + 1:, 0, 0] = 1.0
+    return q, k, v, a, b
+
+
+def test_p8_needle_retrieval_and_orientation():
+    """A needle written early is read back exactly at every later position
+    (the long-context retrieval failure that a transposed state layout caused
+    in a serving stack); reading a column instead of a row fails this."""
+    rng = np.random.default_rng(8)
+    T, p, DK, DV = 3000, 17, 8, 5
+    q, k, v, a, b = needle_inputs(T, p, DK, DV, rng)
+    o, S = kda_recurrent(q, k, v, a, b)
+    np.testing.assert_array_equal(o[0, p + 1:, 0], np.broadcast_to(v[0, p, 0], (T - p - 1, DV)))
+    np.testing.assert_array_equal(S[0, 0, 0], v[0, p, 0])
+
+
+# ------------------------------------------------------------------- P9 ---
+def test_p9_split_calls_and_prefill_then_decode():
+    """State carried across calls: prefill(T1) then prefill(T2 | S) equals
+    prefill(T1+T2); prefill(T) then one decode step equals prefill(T+1) at
+    token T+1 (checked through the independent chunk form)."""
+    rng = np.random.default_rng(9)
+    q, k, v, a, b, S0 = rand_inputs(rng, 2, 130, 2, 8, 6)
+    o_full, S_full = kda_chunked(q, k, v, a, b, S0, chunk=64)
+    o1, S1 = kda_recurrent(q[:, :77], k[:, :77], v[:, :77], a[:, :77], b[:, :77], S0)
+    o2, S2 = kda_recurrent(q[:, 77:129], k[:, 77:129], v[:, 77:129], a[:, 77:129], b[:, 77:129], S1)
+    od, Sd = kda_decode_step(q[:, 129], k[:, 129], v[:, 129], a[:, 129], b[:, 129], S2)
+    assert max_rel_err(np.concatenate([o1, o2, od[:, None]], axis=1), o_full) < 1e-12
+    assert max_rel_err(Sd, S_full) < 1e-12
+
+
+# ------------------------------------------------------------------ P10 ---
+def test_p10_varlen_equals_separate_and_permutes():
+    """Packed sequences behave as separate calls (nothing crosses a sequence
+    boundary), zero-length sequences pass their state through, and permuting
+    the packed sequences permutes the outputs."""
+    rng = np.random.default_rng(10)
+    lens = [5, 0, 70, 1, 64, 33]
+    H, DK, DV = 2, 8, 4
+    parts = [rand_inputs(rng, 1, L, H, DK, DV) for L in lens]
+    cat = lambda i: np.concatenate([p[i][0] for p in parts], axis=0)  # noqa: E731
+    q, k, v, a = cat(0), cat(1), cat(2), cat(3)
+    b = np.concatenate([p[4][0] for p in parts], axis=0)
+    S0 = np.concatenate([p[5] for p in parts], axis=0)
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    o, S = kda_recurrent_varlen(q, k, v, a, b, cu, S0)
+    for n, p in enumerate(parts):
+        on, Sn = kda_chunked(*p[:5], p[5], chunk=16)
+        assert max_rel_err(o[cu[n]:cu[n + 1]], on[0]) < 1e-12
+        assert max_rel_err(S[n], Sn[0]) < 1e-12
+    np.testing.assert_array_equal(S[1], S0[1])
+    perm = [3, 0, 5, 2, 1, 4]
+    pl = [lens[i] for i in perm]
+    pcu = np.concatenate([[0], np.cumsum(pl)])
+    sl = lambda x: np.concatenate([x[cu[i]:cu[i + 1]] for i in perm], axis=0)  # noqa: E731
+    op, Sp = kda_recurrent_varlen(sl(q), sl(k), sl(v), sl(a), sl(b), pcu, S0[perm])
+    np.testing.assert_array_equal(op, sl(o))
+    np.testing.assert_array_equal(Sp, S[perm])
+
+
+# -------------------------------------------------------------- domain ---
+def test_alpha_domain_is_checked():
+    z = np.zeros((1, 2, 1, 2))
+    with pytest.raises(ValueError):
+        kda_recurrent(z, z, z, np.full((1, 2, 1, 2), 1.5), np.zeros((1, 2, 1)))
+    with pytest.raises(ValueError):
+        kda_recurrent(z, z, z, np.zeros((1, 2, 1, 2)), np.zeros((1, 2, 1)))
+
+
+def test_max_rel_err_definition():
+    ref = np.array([0.0, 2.0, -4.0])
+    assert max_rel_err(ref, ref) == 0.0
+    assert max_rel_err(ref + np.array([0.0, 0.0, 0.004]), ref) == pytest.approx(0.001)
+    assert max_rel_err(np.array([0.0, np.nan, 0.0]), ref) == float("inf")
