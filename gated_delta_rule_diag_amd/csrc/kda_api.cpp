@@ -1,0 +1,223 @@
+// Host side of the KDA C ABI: argument checks and dispatch.
+//
+// Every check runs before the first HIP call, so an invalid call returns its
+// status having enqueued nothing and touched no output.  This file has no HIP
+// dependency; the launchers live in the .hip sources.
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "kda.h"
+#include "kda_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kda_status_t fail(kda_status_t s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+
+kda_status_t fail(kda_status_t s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+kda_status_t ok() {
+  g_last_error.clear();
+  return KDA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
+  if (a == nullptr || b == nullptr || an == 0 || bn == 0) return false;
+  uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + bn && b0 < a0 + an;
+}
+
+bool dims_ok(int d) { return d == 64 || d == 128; }
+
+// Shared checks of the prefill entry points.  `ntok` is the number of tokens
+// on the packed axis, `nseq` the number of states.
+kda_status_t check_prefill(int nseq, int64_t ntok, int H, int DK, int DV, int chunk,
+                           kda_dtype_t dt, const void* q, const void* k, const void* v,
+                           const float* alpha, const float* beta, const float* s_in,
+                           const float* o, const float* s_out) {
+  if (nseq < 0 || ntok < 0 || H < 0)
+    return fail(KDA_ERR_SHAPE, "negative size (sequences=%d tokens=%lld H=%d)", nseq,
+                (long long)ntok, H);
+  if (!dims_ok(DK) || !dims_ok(DV))
+    return fail(KDA_ERR_UNSUPPORTED, "DK=%d DV=%d: only 64 and 128 are supported", DK, DV);
+  if (chunk != 64) return fail(KDA_ERR_UNSUPPORTED, "chunk=%d: only 64 is supported", chunk);
+  if (dt != KDA_F32 && dt != KDA_BF16) return fail(KDA_ERR_DTYPE, "unknown in_dtype %d", (int)dt);
+  if (ntok > (int64_t(1) << 31) - 1 || int64_t(nseq) * H > (int64_t(1) << 24))
+    return fail(KDA_ERR_UNSUPPORTED, "too large: tokens=%lld sequences*H=%lld", (long long)ntok,
+                (long long)nseq * H);
+  const size_t esz = dt == KDA_BF16 ? 2 : 4;
+  const size_t nk = size_t(ntok) * H * DK, nv = size_t(ntok) * H * DV, nb = size_t(ntok) * H;
+  const size_t ns = size_t(nseq) * H * DK * DV;
+  if (nk > 0) {
+    if (!q || !k || !v || !alpha || !beta || !o)
+      return fail(KDA_ERR_NULL, "q, k, v, alpha, beta and o must be non-NULL");
+  }
+  if (ns > 0 && !s_out && !o && ntok == 0) return fail(KDA_ERR_NULL, "no output given");
+  const void* ptrs[] = {q, k, v, alpha, beta, s_in, o, s_out};
+  const char* names[] = {"q", "k", "v", "alpha", "beta", "state_in", "o", "state_out"};
+  for (int i = 0; i < 8; ++i)
+    if (ptrs[i] && !aligned16(ptrs[i]))
+      return fail(KDA_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
+  // o must not overlap any input or state; state_out may only equal state_in.
+  const size_t obytes = nv * 4;
+  if (overlaps(o, obytes, q, nk * esz) || overlaps(o, obytes, k, nk * esz) ||
+      overlaps(o, obytes, v, nv * esz) || overlaps(o, obytes, alpha, nk * 4) ||
+      overlaps(o, obytes, beta, nb * 4) || overlaps(o, obytes, s_in, ns * 4) ||
+      overlaps(o, obytes, s_out, ns * 4))
+    return fail(KDA_ERR_SHAPE, "o overlaps an input or a state");
+  if (s_out && s_out != s_in &&
+      (overlaps(s_out, ns * 4, q, nk * esz) || overlaps(s_out, ns * 4, k, nk * esz) ||
+       overlaps(s_out, ns * 4, v, nv * esz) || overlaps(s_out, ns * 4, alpha, nk * 4) ||
+       overlaps(s_out, ns * 4, beta, nb * 4) || overlaps(s_out, ns * 4, s_in, ns * 4)))
+    return fail(KDA_ERR_SHAPE, "state_out overlaps an input (only state_out == state_in is allowed)");
+  return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_abi_version(void) { return (1 << 16) | 0; }
+
+const char* kda_status_string(kda_status_t s) {
+  switch (s) {
+    case KDA_OK: return "KDA_OK";
+    case KDA_ERR_NULL: return "KDA_ERR_NULL";
+    case KDA_ERR_SHAPE: return "KDA_ERR_SHAPE";
+    case KDA_ERR_DTYPE: return "KDA_ERR_DTYPE";
+    case KDA_ERR_ALIGN: return "KDA_ERR_ALIGN";
+    case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
+    case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE";
+    case KDA_ERR_HIP: return "KDA_ERR_HIP";
+  }
+  return "KDA_ERR_UNKNOWN";
+}
+
+const char* kda_last_error_message(void) { return g_last_error.c_str(); }
+
+size_t kda_chunk_prefill_workspace_size(int B, int T, int H, int DK, int DV, int chunk) {
+  if (B < 0 || T < 0 || H < 0 || !dims_ok(DK) || !dims_ok(DV) || chunk != 64) return 0;
+  return kda::prefill_workspace_bytes(B, int64_t(B) * T, H, DK, DV);
+}
+
+size_t kda_chunk_prefill_varlen_workspace_size(int N, int T_total, int H, int DK, int DV,
+                                               int chunk) {
+  if (N < 0 || T_total < 0 || H < 0 || !dims_ok(DK) || !dims_ok(DV) || chunk != 64) return 0;
+  return kda::prefill_workspace_bytes(N, T_total, H, DK, DV);
+}
+
+static kda_status_t run_prefill(kda::PrefillArgs& a, size_t need, void* stream) {
+  if (need > 0 && (a.workspace == nullptr || a.workspace_bytes < need))
+    return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need,
+                a.workspace ? a.workspace_bytes : size_t(0));
+  if (a.workspace && !aligned16(a.workspace))
+    return fail(KDA_ERR_ALIGN, "workspace is not 16-byte aligned");
+  if (a.N == 0 || a.H == 0) return ok();
+  const char* msg = nullptr;
+  if (kda::launch_prefill(a, stream, &msg) != 0)
+    return fail(KDA_ERR_HIP, "prefill launch failed: %s", msg ? msg : "?");
+  return ok();
+}
+
+kda_status_t kda_chunk_prefill(int B, int T, int H, int DK, int DV, int chunk,
+                               kda_dtype_t in_dtype, const void* q, const void* k,
+                               const void* v, const float* alpha, const float* beta,
+                               const float* state_in, float* o, float* state_out,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 0 || T < 0) return fail(KDA_ERR_SHAPE, "negative size (B=%d T=%d)", B, T);
+  kda_status_t s = check_prefill(B, int64_t(B) * T, H, DK, DV, chunk, in_dtype, q, k, v, alpha,
+                                 beta, state_in, o, state_out);
+  if (s != KDA_OK) return s;
+  kda::PrefillArgs a{};
+  a.N = B;
+  a.T_fixed = T;
+  a.cu_seqlens = nullptr;
+  a.T_total = int64_t(B) * T;
+  a.H = H; a.DK = DK; a.DV = DV;
+  a.in_bf16 = in_dtype == KDA_BF16;
+  a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta;
+  a.state_in = state_in; a.o = o; a.state_out = state_out;
+  a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+  return run_prefill(a, kda::prefill_workspace_bytes(B, a.T_total, H, DK, DV), stream);
+}
+
+kda_status_t kda_chunk_prefill_varlen(int N, int T_total, const int32_t* cu_seqlens, int H,
+                                      int DK, int DV, int chunk, kda_dtype_t in_dtype,
+                                      const void* q, const void* k, const void* v,
+                                      const float* alpha, const float* beta,
+                                      const float* state_in, float* o, float* state_out,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (N < 0 || T_total < 0) return fail(KDA_ERR_SHAPE, "negative size (N=%d T_total=%d)", N, T_total);
+  if (N > 0 && cu_seqlens == nullptr) return fail(KDA_ERR_NULL, "cu_seqlens must be non-NULL");
+  if (cu_seqlens && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u))
+    return fail(KDA_ERR_ALIGN, "cu_seqlens is not 4-byte aligned");
+  kda_status_t s = check_prefill(N, T_total, H, DK, DV, chunk, in_dtype, q, k, v, alpha, beta,
+                                 state_in, o, state_out);
+  if (s != KDA_OK) return s;
+  kda::PrefillArgs a{};
+  a.N = N;
+  a.T_fixed = 0;
+  a.cu_seqlens = cu_seqlens;
+  a.T_total = T_total;
+  a.H = H; a.DK = DK; a.DV = DV;
+  a.in_bf16 = in_dtype == KDA_BF16;
+  a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta;
+  a.state_in = state_in; a.o = o; a.state_out = state_out;
+  a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+  return run_prefill(a, kda::prefill_workspace_bytes(N, T_total, H, DK, DV), stream);
+}
+
+kda_status_t kda_decode_step(int N, int H, int DK, int DV, kda_dtype_t in_dtype, const void* q,
+                             const void* k, const void* v, const float* alpha,
+                             const float* beta, float* state, float* o, void* stream) {
+  if (N < 0 || H < 0) return fail(KDA_ERR_SHAPE, "negative size (N=%d H=%d)", N, H);
+  if (!dims_ok(DK) || !dims_ok(DV))
+    return fail(KDA_ERR_UNSUPPORTED, "DK=%d DV=%d: only 64 and 128 are supported", DK, DV);
+  if (in_dtype != KDA_F32 && in_dtype != KDA_BF16)
+    return fail(KDA_ERR_DTYPE, "unknown in_dtype %d", (int)in_dtype);
+  if (int64_t(N) * H > (int64_t(1) << 30))
+    return fail(KDA_ERR_UNSUPPORTED, "too large: N*H=%lld", (long long)N * H);
+  if (N == 0 || H == 0) return ok();
+  if (!q || !k || !v || !alpha || !beta || !state || !o)
+    return fail(KDA_ERR_NULL, "q, k, v, alpha, beta, state and o must be non-NULL");
+  const void* ptrs[] = {q, k, v, alpha, beta, state, o};
+  const char* names[] = {"q", "k", "v", "alpha", "beta", "state", "o"};
+  for (int i = 0; i < 7; ++i)
+    if (!aligned16(ptrs[i])) return fail(KDA_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
+  const size_t esz = in_dtype == KDA_BF16 ? 2 : 4;
+  const size_t nh = size_t(N) * H;
+  const size_t obytes = nh * DV * 4, sbytes = nh * DK * DV * 4;
+  if (overlaps(o, obytes, q, nh * DK * esz) || overlaps(o, obytes, k, nh * DK * esz) ||
+      overlaps(o, obytes, v, nh * DV * esz) || overlaps(o, obytes, alpha, nh * DK * 4) ||
+      overlaps(o, obytes, beta, nh * 4) || overlaps(o, obytes, state, sbytes))
+    return fail(KDA_ERR_SHAPE, "o overlaps an input or the state");
+  if (overlaps(state, sbytes, q, nh * DK * esz) || overlaps(state, sbytes, k, nh * DK * esz) ||
+      overlaps(state, sbytes, v, nh * DV * esz) || overlaps(state, sbytes, alpha, nh * DK * 4) ||
+      overlaps(state, sbytes, beta, nh * 4))
+    return fail(KDA_ERR_SHAPE, "state overlaps an input");
+  kda::DecodeArgs a{};
+  a.N = N; a.H = H; a.DK = DK; a.DV = DV;
+  a.in_bf16 = in_dtype == KDA_BF16;
+  a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.state = state; a.o = o;
+  const char* msg = nullptr;
+  if (kda::launch_decode(a, stream, &msg) != 0)
+    return fail(KDA_ERR_HIP, "decode launch failed: %s", msg ? msg : "?");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,48 @@
+// Internal contract between the host-side argument checks (kda_api.cpp, plain
+// C++ with no HIP dependency) and the kernel launchers (*.hip).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+// One prefill launch.  Fixed-length batches are described by cu_seqlens ==
+// nullptr and T_fixed > 0 (sequence n owns tokens [n*T_fixed, (n+1)*T_fixed)).
+struct PrefillArgs {
+  int N;                       // number of sequences
+  int64_t T_fixed;             // tokens per sequence when cu_seqlens == nullptr
+  const int32_t* cu_seqlens;   // device [N+1] or nullptr
+  int64_t T_total;             // tokens on the packed axis
+  int H, DK, DV;
+  bool in_bf16;
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* alpha;
+  const float* beta;
+  const float* state_in;       // may be nullptr (zero state)
+  float* o;
+  float* state_out;            // may be nullptr
+  void* workspace;
+  size_t workspace_bytes;
+};
+
+struct DecodeArgs {
+  int N, H, DK, DV;
+  bool in_bf16;
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* alpha;
+  const float* beta;
+  float* state;
+  float* o;
+};
+
+// Launchers return 0 on success, else a non-zero code and a static message.
+int launch_prefill(const PrefillArgs& a, void* stream, const char** msg);
+int launch_decode(const DecodeArgs& a, void* stream, const char** msg);
+size_t prefill_workspace_bytes(int N, int64_t T_total, int H, int DK, int DV);
+
+}  // namespace kda

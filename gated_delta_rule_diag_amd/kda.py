@@ -1,0 +1,211 @@
+"""Thin Python binding of libkda.so (ctypes).
+
+Argument marshalling only: every step of the operator runs in the HIP kernels
+behind the C ABI (include/kda.h).  PyTorch provides device memory and the
+current stream; nothing here computes any part of the result.  If the built
+library is missing the import fails loudly: there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
+
+KDA_OK = 0
+KDA_F32 = 0
+KDA_BF16 = 1
+
+STATUS_NAMES = {
+    0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE",
+    4: "KDA_ERR_ALIGN", 5: "KDA_ERR_UNSUPPORTED", 6: "KDA_ERR_WORKSPACE", 7: "KDA_ERR_HIP",
+}
+
+EXPORTED = (
+    "kda_abi_version",
+    "kda_chunk_prefill_workspace_size",
+    "kda_chunk_prefill",
+    "kda_chunk_prefill_varlen_workspace_size",
+    "kda_chunk_prefill_varlen",
+    "kda_decode_step",
+    "kda_status_string",
+    "kda_last_error_message",
+)
+
+
+class KDAError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+def load_library(path: str = _LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is not built; run `python -m gated_delta_rule_diag_amd.build` "
+            "(there is no non-HIP fallback)")
+    lib = ctypes.CDLL(path)
+    vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.kda_abi_version.restype = i
+    lib.kda_abi_version.argtypes = []
+    lib.kda_chunk_prefill_workspace_size.restype = sz
+    lib.kda_chunk_prefill_workspace_size.argtypes = [i, i, i, i, i, i]
+    lib.kda_chunk_prefill.restype = i
+    lib.kda_chunk_prefill.argtypes = [i, i, i, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.kda_chunk_prefill_varlen_workspace_size.restype = sz
+    lib.kda_chunk_prefill_varlen_workspace_size.argtypes = [i, i, i, i, i, i]
+    lib.kda_chunk_prefill_varlen.restype = i
+    lib.kda_chunk_prefill_varlen.argtypes = [i, i, vp, i, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp,
+                                             vp, sz, vp]
+    lib.kda_decode_step.restype = i
+    lib.kda_decode_step.argtypes = [i, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_status_string.argtypes = [i]
+    lib.kda_last_error_message.restype = ctypes.c_char_p
+    lib.kda_last_error_message.argtypes = []
+    return lib
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        _lib = load_library()
+    return _lib
+
+
+def _check(status):
+    if status != KDA_OK:
+        raise KDAError(status, lib().kda_last_error_message().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _in_dtype(t):
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_F32
+    raise ValueError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+
+
+def _need(t, name, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def chunk_prefill(q, k, v, alpha, beta, initial_state=None, output_final_state=True, chunk=64,
+                  out=None, final_state=None, workspace=None):
+    """KDA chunked prefill, fixed length.
+
+    q, k: [B,T,H,DK], v: [B,T,H,DV] (bfloat16 or float32, same dtype);
+    alpha: [B,T,H,DK] float32; beta: [B,T,H] float32;
+    initial_state: [B,H,DK,DV] float32 or None (zeros).
+    Returns (o [B,T,H,DV] float32, final_state [B,H,DK,DV] float32 or None).
+    """
+    B, T, H, DK = q.shape
+    DV = v.shape[-1]
+    dt = _in_dtype(q)
+    _need(q, "q", q.dtype)
+    _need(k, "k", q.dtype, (B, T, H, DK))
+    _need(v, "v", q.dtype, (B, T, H, DV))
+    _need(alpha, "alpha", torch.float32, (B, T, H, DK))
+    _need(beta, "beta", torch.float32, (B, T, H))
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, (B, H, DK, DV))
+    dev = q.device
+    o = out if out is not None else torch.empty((B, T, H, DV), device=dev, dtype=torch.float32)
+    _need(o, "out", torch.float32, (B, T, H, DV))
+    st = None
+    if output_final_state:
+        st = final_state if final_state is not None else torch.empty(
+            (B, H, DK, DV), device=dev, dtype=torch.float32)
+        _need(st, "final_state", torch.float32, (B, H, DK, DV))
+    wsz = lib().kda_chunk_prefill_workspace_size(B, T, H, DK, DV, chunk)
+    if wsz and workspace is None:
+        workspace = torch.empty(wsz, device=dev, dtype=torch.uint8)
+    _check(lib().kda_chunk_prefill(
+        B, T, H, DK, DV, chunk, dt, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+        _ptr(initial_state), _ptr(o), _ptr(st), _ptr(workspace),
+        0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(dev)))
+    return o, st
+
+
+def chunk_prefill_varlen(q, k, v, alpha, beta, cu_seqlens, initial_state=None,
+                         output_final_state=True, chunk=64, out=None, final_state=None,
+                         workspace=None):
+    """KDA chunked prefill over packed sequences.
+
+    q, k: [T_total,H,DK], v: [T_total,H,DV]; alpha [T_total,H,DK]; beta [T_total,H];
+    cu_seqlens: int32 device tensor [N+1]; initial_state [N,H,DK,DV] or None.
+    Returns (o [T_total,H,DV], final_state [N,H,DK,DV] or None).
+    """
+    Tt, H, DK = q.shape
+    DV = v.shape[-1]
+    dt = _in_dtype(q)
+    _need(q, "q", q.dtype)
+    _need(k, "k", q.dtype, (Tt, H, DK))
+    _need(v, "v", q.dtype, (Tt, H, DV))
+    _need(alpha, "alpha", torch.float32, (Tt, H, DK))
+    _need(beta, "beta", torch.float32, (Tt, H))
+    _need(cu_seqlens, "cu_seqlens", torch.int32)
+    N = cu_seqlens.numel() - 1
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, (N, H, DK, DV))
+    dev = q.device
+    o = out if out is not None else torch.empty((Tt, H, DV), device=dev, dtype=torch.float32)
+    _need(o, "out", torch.float32, (Tt, H, DV))
+    st = None
+    if output_final_state:
+        st = final_state if final_state is not None else torch.empty(
+            (N, H, DK, DV), device=dev, dtype=torch.float32)
+        _need(st, "final_state", torch.float32, (N, H, DK, DV))
+    wsz = lib().kda_chunk_prefill_varlen_workspace_size(N, Tt, H, DK, DV, chunk)
+    if wsz and workspace is None:
+        workspace = torch.empty(wsz, device=dev, dtype=torch.uint8)
+    _check(lib().kda_chunk_prefill_varlen(
+        N, Tt, _ptr(cu_seqlens), H, DK, DV, chunk, dt, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+        _ptr(beta), _ptr(initial_state), _ptr(o), _ptr(st), _ptr(workspace),
+        0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(dev)))
+    return o, st
+
+
+def decode_step(q, k, v, alpha, beta, state, out=None):
+    """One recurrent decode step; ``state`` [N,H,DK,DV] float32 is updated in place.
+
+    q, k: [N,H,DK], v: [N,H,DV]; alpha [N,H,DK]; beta [N,H].  Returns o [N,H,DV].
+    """
+    N, H, DK = q.shape
+    DV = v.shape[-1]
+    dt = _in_dtype(q)
+    _need(q, "q", q.dtype)
+    _need(k, "k", q.dtype, (N, H, DK))
+    _need(v, "v", q.dtype, (N, H, DV))
+    _need(alpha, "alpha", torch.float32, (N, H, DK))
+    _need(beta, "beta", torch.float32, (N, H))
+    _need(state, "state", torch.float32, (N, H, DK, DV))
+    dev = q.device
+    o = out if out is not None else torch.empty((N, H, DV), device=dev, dtype=torch.float32)
+    _need(o, "out", torch.float32, (N, H, DV))
+    _check(lib().kda_decode_step(N, H, DK, DV, dt, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                 _ptr(beta), _ptr(state), _ptr(o), _stream(dev)))
+    return o

@@ -1,0 +1,125 @@
+/*
+ * kda.h — C ABI of the Kimi Delta Attention (KDA) operator for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The operator (per sequence n and head h, state S of d_k x d_v, fp32):
+ *     for every token t, in order:
+ *         S   <- Diag(alpha_t) S                       channel-wise forget, first
+ *         S   <- S + beta_t k_t (v_t - S^T k_t)^T      delta-rule write
+ *         o_t  = S^T q_t                                read after the write
+ * as defined by "Kimi Delta Attention 徹底解説" (tech-tide.dev), section
+ * "Kimi Delta Attention の仕組み — 「忘れ方」を鍛える": DeltaNet writes the
+ * prediction error scaled by a write strength beta; Gated DeltaNet decays the
+ * state before writing; KDA makes the decay a diagonal (per-channel) matrix;
+ * decode is the token recurrence and prefill the same computation regrouped
+ * into chunked matrix products.  The decay is given per token ("Kimi Linear、
+ * 独自の土俵でFull Attentionを上回る" (remio.ai), section "Kimi Linearがより
+ * 賢いRecurrent Memoryを使う方法").
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller, C-contiguous
+ *     (row-major), 16-byte aligned.  The library never allocates, frees or
+ *     synchronises, and never reads device memory on the host.
+ *   - q, k, v are KDA_F32 (float) or KDA_BF16 (bfloat16 bit patterns);
+ *     alpha, beta, states and o are always float (fp32).
+ *   - State layout: S[n][h][i][j] at ((n*H + h)*DK + i)*DV + j, where i is the
+ *     KEY channel (the axis Diag(alpha) scales) and j the VALUE channel.
+ *   - Supported sizes: DK, DV in {64, 128}; chunk == 64.
+ *   - Data domain (not checked: violating it gives unspecified output):
+ *     alpha in [0.07, 1] and finite inputs.  The chunked prefill scales rows by
+ *     decay ratios taken about each chunk's midpoint; the product of alpha over
+ *     any 32 consecutive tokens of one channel must stay above ~1e-37.
+ *   - Errors: argument errors are detected on the host before anything is
+ *     enqueued; the call then returns a non-zero status, enqueues nothing and
+ *     leaves every output untouched.  KDA_ERR_HIP means a launch failed.
+ *     kda_last_error_message() gives a thread-local description.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *     stream).
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_ERR_NULL = 1,        /* a required pointer is NULL                          */
+  KDA_ERR_SHAPE = 2,       /* a size is negative or tensors overlap illegally     */
+  KDA_ERR_DTYPE = 3,       /* unknown kda_dtype_t                                 */
+  KDA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                    */
+  KDA_ERR_UNSUPPORTED = 5, /* DK/DV not in {64,128}, chunk != 64, or too large    */
+  KDA_ERR_WORKSPACE = 6,   /* workspace missing or smaller than required          */
+  KDA_ERR_HIP = 7          /* a HIP launch failed                                 */
+} kda_status_t;
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype_t; /* dtype of q, k, v only */
+
+/* Version of this ABI: (major << 16) | minor. */
+int kda_abi_version(void);
+
+/*
+ * Chunked prefill, fixed length: B sequences of T tokens, H heads.
+ *   q, k       [B,T,H,DK]  (in_dtype)
+ *   v          [B,T,H,DV]  (in_dtype)
+ *   alpha      [B,T,H,DK]  float, per-token per-channel decay
+ *   beta       [B,T,H]     float, per-token write strength (any finite value)
+ *   state_in   [B,H,DK,DV] float, or NULL for a zero initial state
+ *   o          [B,T,H,DV]  float output; must not overlap any input
+ *   state_out  [B,H,DK,DV] float, or NULL; may be equal to state_in (in place)
+ *   workspace  device scratch of at least kda_chunk_prefill_workspace_size()
+ *              bytes (may be NULL when that size is 0)
+ * Computes exactly the token recurrence (up to rounding) by the chunk form:
+ * per chunk a unit-lower-triangular solve and dense products, and a
+ * sequential pass of the state over the chunks.
+ */
+size_t kda_chunk_prefill_workspace_size(int B, int T, int H, int DK, int DV, int chunk);
+kda_status_t kda_chunk_prefill(int B, int T, int H, int DK, int DV, int chunk,
+                               kda_dtype_t in_dtype, const void* q, const void* k,
+                               const void* v, const float* alpha, const float* beta,
+                               const float* state_in, float* o, float* state_out,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Chunked prefill, packed variable length: N sequences concatenated on the
+ * token axis; sequence n owns tokens [cu_seqlens[n], cu_seqlens[n+1]).
+ *   cu_seqlens  int32 DEVICE array [N+1], cu_seqlens[0] == 0, non-decreasing,
+ *               cu_seqlens[N] == T_total (not checked: it is never read on
+ *               the host)
+ *   q, k, alpha [T_total,H,DK];  v, o [T_total,H,DV];  beta [T_total,H]
+ *   state_in / state_out  [N,H,DK,DV] as above (one state per sequence)
+ * Chunks restart at every sequence start; a zero-length sequence passes its
+ * state through.
+ */
+size_t kda_chunk_prefill_varlen_workspace_size(int N, int T_total, int H, int DK, int DV,
+                                               int chunk);
+kda_status_t kda_chunk_prefill_varlen(int N, int T_total, const int32_t* cu_seqlens, int H,
+                                      int DK, int DV, int chunk, kda_dtype_t in_dtype,
+                                      const void* q, const void* k, const void* v,
+                                      const float* alpha, const float* beta,
+                                      const float* state_in, float* o, float* state_out,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One recurrent decode step for N sequences x H heads (one token each); the
+ * explainer's token-wise mode.
+ *   q, k, alpha [N,H,DK];  v [N,H,DV];  beta [N,H]
+ *   state       [N,H,DK,DV] float, read and updated IN PLACE
+ *   o           [N,H,DV] float output; must not overlap any input or state
+ */
+kda_status_t kda_decode_step(int N, int H, int DK, int DV, kda_dtype_t in_dtype, const void* q,
+                             const void* k, const void* v, const float* alpha,
+                             const float* beta, float* state, float* o, void* stream);
+
+const char* kda_status_string(kda_status_t s);
+const char* kda_last_error_message(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */
