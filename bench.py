@@ -1,0 +1,216 @@
+"""KDA operator benchmark on one MI355X.
+
+One step = the whole hot path once:
+  * chunked prefill, bf16 q/k/v, fp32 alpha/beta/state/o:
+    B=1, H=32, T=8192, d_k=d_v=128, chunk 64, zero initial state
+  * one recurrent decode step: 256 sequences x 32 heads, d=128, fp32 state
+    (256x32x128x128) updated in place, bf16 q/k/v; the states are prefill
+    end-states of 64 seeded tokens per (sequence, head).
+Inputs are seeded synthetic data resident in HBM before timing starts.
+
+Prints ONE JSON line.  `value` is prefill tokens/s (tokens of the 8192-token
+sequence per second of prefill-kernel time); decode us/step is reported next
+to it.  Kernel times come from HIP events recorded on the stream the kernels
+are launched on (torch's current stream), averaged over the timed steps.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense
+
+
+def prefill_algorithmic_bytes(T, H, DK, DV, state_in, state_out):
+    """q, k, v (bf16) + alpha (fp32) + beta (fp32) + o (fp32) per token-head,
+    plus the fp32 states read/written once per (sequence, head)."""
+    per_tok_head = 2 * DK + 2 * DK + 2 * DV + 4 * DK + 4 + 4 * DV
+    st = 4 * DK * DV * H * (int(state_in) + int(state_out))
+    return T * H * per_tok_head + st
+
+
+def decode_algorithmic_bytes(N, H, DK, DV):
+    """fp32 state read + write, bf16 q, k, v, fp32 alpha, beta and o."""
+    return N * H * (2 * 4 * DK * DV + 2 * DK + 2 * DK + 2 * DV + 4 * DK + 4 + 4 * DV)
+
+
+def prefill_algorithmic_flops(T, H, DK, DV, C=64):
+    """Triangle-aware plain-product FLOPs per token-head of the chunk form:
+    6 DK DV (state products) + (3C+1) DK + 2 (C+1) DV + C^2/3."""
+    return T * H * (6 * DK * DV + (3 * C + 1) * DK + 2 * (C + 1) * DV + C * C / 3)
+
+
+def cpu_baseline(seconds, q, k, v, a, b):
+    """The fp64 oracle (as it stands) on the same seeded prefill arrays the GPU
+    gets: all heads, the sequence's tokens in order, until `seconds` elapse."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import kda_recurrent
+
+    B, T, H, D = q.shape
+    step = 256
+    done, t_used, S = 0, 0.0, None
+    with threadpool_limits(limits=1):
+        while t_used < seconds and done < T:
+            sl = slice(done, min(done + step, T))
+            t0 = time.perf_counter()
+            _, S = kda_recurrent(q[:, sl], k[:, sl], v[:, sl], a[:, sl], b[:, sl], S)
+            t_used += time.perf_counter() - t0
+            done = sl.stop
+    return {
+        "value": done / t_used,
+        "unit": "tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"fp64 numpy token recurrence on the benchmark's own inputs: all {H} heads, "
+                  f"first {done} of {T} tokens ({t_used:.1f} s, BLAS limited to 1 thread); "
+                  f"host {platform.machine()}, {len(os.sched_getaffinity(0))} cores visible",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the KDA operator here runs on a single MI355X "
+              "(multi-GPU sharding is not built); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from gated_delta_rule_diag_amd import inputs as I
+    from gated_delta_rule_diag_amd import kda
+
+    dev = torch.device("cuda:0")
+    B, T, H, D = 1, 8192, 32, 128
+    ND = 256
+
+    # ---- prefill workload (seeded, host-generated, copied to HBM once) ----
+    q, k, v, a, b = I.batch_inputs(1, B, T, H, D, D, "bf16")
+    bf = torch.bfloat16
+    to = lambda x, dt=torch.float32: torch.from_numpy(x).to(dev).to(dt).contiguous()  # noqa: E731
+    pq, pk, pv, pa, pb = to(q, bf), to(k, bf), to(v, bf), to(a), to(b)
+    po = torch.empty((B, T, H, D), device=dev, dtype=torch.float32)
+    pst = torch.empty((B, H, D, D), device=dev, dtype=torch.float32)
+
+    # ---- decode workload ----
+    dq, dk_, dv_, da, db = I.decode_inputs(2, ND, H, D, D, "bf16")
+    dq, dk_, dv_, da, db = to(dq, bf), to(dk_, bf), to(dv_, bf), to(da), to(db)
+    # start states: prefill end-states of 64 seeded tokens per (sequence, head)
+    L0 = 64
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(I.SEED + 2)
+    x = torch.randn((ND, L0, H, D), generator=gen, device=dev)
+    wq = x / x.norm(dim=-1, keepdim=True)
+    x = torch.randn((ND, L0, H, D), generator=gen, device=dev)
+    wk = x / x.norm(dim=-1, keepdim=True)
+    wv = torch.randn((ND, L0, H, D), generator=gen, device=dev)
+    wa = torch.exp(-torch.exp(torch.rand((ND, L0, H, D), generator=gen, device=dev) * 4 - 5))
+    wb = torch.sigmoid(torch.randn((ND, L0, H), generator=gen, device=dev))
+    _, dstate = kda.chunk_prefill(wq.to(bf), wk.to(bf), wv.to(bf), wa.contiguous(), wb.contiguous())
+    del x, wq, wk, wv, wa, wb
+    do = torch.empty((ND, H, D), device=dev, dtype=torch.float32)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        kda.chunk_prefill(pq, pk, pv, pa, pb, None, True, 64, po, pst)
+        if ev is not None:
+            ev[1].record()
+        kda.decode_step(dq, dk_, dv_, da, db, dstate, do)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pre_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    dec_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+
+    pre_bytes = prefill_algorithmic_bytes(T, H, D, D, False, True)
+    dec_bytes = decode_algorithmic_bytes(ND, H, D, D)
+    pre_gbs = pre_bytes / (pre_ms * 1e-3) / 1e9
+    dec_gbs = dec_bytes / (dec_ms * 1e-3) / 1e9
+    pre_tflops = prefill_algorithmic_flops(T, H, D, D) / (pre_ms * 1e-3) / 1e12
+
+    # HBM traffic measured by rocprofv3 counters (FETCH_SIZE + WRITE_SIZE,
+    # scaled by a plain-copy calibration) for the kernels as they are now.
+    traffic = None
+    tfile = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "traffic.json")
+    if os.path.exists(tfile):
+        with open(tfile) as f:
+            tj = json.load(f)
+        traffic = tj.get("prefill_bytes_per_launch")
+
+    out = {
+        "metric": "KDA prefill tokens/s + decode us/step (B=256); % of MFMA / HBM peak",
+        "value": T / (pre_ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "KDA chunked prefill B=1 H=32 T=8192 d=128 bf16 (chunk 64, zero initial "
+                        "state) + one decode step 256 seq x 32 heads d=128 (fp32 state in place)",
+            "prefill": {"B": B, "T": T, "H": H, "d_k": D, "d_v": D, "chunk": 64},
+            "decode": {"N": ND, "H": H, "d_k": D, "d_v": D},
+        },
+        "prefill_us": pre_ms * 1e3,
+        "decode_us_per_step": dec_ms * 1e3,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "kda_prefill_kernel",
+            "achieved": pre_gbs,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": pre_gbs / HBM_PEAK_GBS,
+            "traffic": traffic,
+            "algorithmic_bytes": pre_bytes,
+            "algorithmic_tflops": pre_tflops,
+            "mfma_frac_algorithmic": pre_tflops / BF16_MFMA_PEAK_TFLOPS,
+        },
+        "roofline_decode": {
+            "bound": "hbm",
+            "kernel": "kda_decode_kernel",
+            "achieved": dec_gbs,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": dec_gbs / HBM_PEAK_GBS,
+            "algorithmic_bytes": dec_bytes,
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.cpu_seconds, q, k, v, a, b)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

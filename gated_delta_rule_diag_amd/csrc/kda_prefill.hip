@@ -40,8 +40,6 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
 
 constexpr int kC = 64;    // chunk length
-constexpr int kNT = 256;  // threads per workgroup (4 waves)
-constexpr int kRef = 31;  // reference position inside a chunk (rows 0..31 | 32..63)
 
 struct Params {
   int N;
@@ -66,9 +64,11 @@ struct Params {
 // fragment reads).
 template <int DK>
 struct Lay {
+  static constexpr int NW = DK / 16;        // waves: one 16-row tile of the state each
+  static constexpr int NT = 64 * NW;        // threads
   static constexpr int P_OP = DK * 4 + 16;  // rows of DK elements
   static constexpr int P_T = kC * 4 + 16;   // rows of 64 elements (272 B)
-  static constexpr int P_AF = kC + 4;       // fp32 pitch (floats) of A / L^-1 (272 B)
+  static constexpr int P_AF = kC + 4;       // fp32 pitch (floats) of A and L^-1 (272 B)
   static constexpr int OFF_KL = 0;
   static constexpr int OFF_QL = OFF_KL + kC * P_OP;
   static constexpr int OFF_KRT = OFF_QL + kC * P_OP;         // Kr^T [DK][64]
@@ -80,17 +80,26 @@ struct Lay {
   static constexpr int OFF_XT = OFF_SBT + 16 * P_OP;         // X^T [16][64]
   static constexpr int OFF_UT = OFF_XT + 16 * P_T;           // U^T [16][64]
   static constexpr int OFF_T = OFF_X + SZ_X;                 // T [64][64] (fp32 L^-1 first)
-  static constexpr int OFF_TMP = OFF_T + kC * P_T;           // 3 x 16x16 fp32
-  static constexpr int RG = 512 / DK;                        // row groups in the decay prep
+  static constexpr int OFF_TMP = OFF_T + kC * P_T;           // 3 x 16x16 fp32 (solve)
+  static constexpr int RG = 8;                               // row groups of the decay prep
   static constexpr int OFF_GP = OFF_TMP + 3 * 256 * 4;       // group products [RG][DK]
   static constexpr int OFF_GM = OFF_GP + RG * DK * 4;        // gamma_m [DK]
   static constexpr int OFF_DL = OFF_GM + DK * 4;             // gamma_n / gamma_m [DK]
   static constexpr int OFF_GN = OFF_DL + DK * 4;             // gamma_n [DK]
   static constexpr int OFF_BE = OFF_GN + DK * 4;             // beta [64]
   static constexpr int TOTAL = OFF_BE + kC * 4;
+  static_assert(NT == RG * DK / 2, "decay prep: one thread per (channel pair, row group)");
   static_assert(OFF_UT + 16 * P_T <= OFF_X + kC * P_T, "step buffers fit in A's space");
   static_assert(TOTAL <= 160 * 1024, "LDS budget");
 };
+
+// Workgroup barrier that orders LDS only: pending global loads (prefetches)
+// and stores stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
@@ -237,15 +246,80 @@ __device__ __forceinline__ float ld1(const void* p, int64_t i) {
 
 __device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
+// Raw (unconverted) input words, so that prefetched loads are not consumed
+// before they are needed: a bf16 pair / bf16 value, or fp32.
+template <bool BF> struct Raw { typedef uint32_t two; typedef uint32_t one; };
+template <> struct Raw<false> { typedef float2 two; typedef float one; };
+
+template <bool BF>
+__device__ __forceinline__ typename Raw<BF>::two ldraw2(const void* p, int64_t i) {
+  if constexpr (BF) return *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p) + i);
+  else return *reinterpret_cast<const float2*>(static_cast<const float*>(p) + i);
+}
+template <bool BF>
+__device__ __forceinline__ typename Raw<BF>::one ldraw1(const void* p, int64_t i) {
+  if constexpr (BF) return uint32_t(static_cast<const uint16_t*>(p)[i]);
+  else return static_cast<const float*>(p)[i];
+}
+template <bool BF>
+__device__ __forceinline__ float2 cvt2(typename Raw<BF>::two r) {
+  if constexpr (BF) return make_float2(__uint_as_float(r << 16), __uint_as_float(r & 0xffff0000u));
+  else return r;
+}
+template <bool BF>
+__device__ __forceinline__ float cvt1(typename Raw<BF>::one r) {
+  if constexpr (BF) return __uint_as_float(r << 16);
+  else return r;
+}
+
+
+// Destination of output stores for rows past the end of a sequence (never read).
+__device__ float g_sink[256 * 64];
+
+// A and P tiles of up to three (R, I) pairs (R < 0: unused) of one wave.
+// Each row block of Kl/Ql and column block of Kr is loaded once per K chunk
+// and shared by the pair's two products (the LDS read bandwidth, not the
+// MFMA rate, bounds this step).
+template <bool BF, int DK, int R0, int I0, int R1, int I1, int R2, int I2>
+__device__ __forceinline__ void ap_tiles(const char* sKl, const char* sQl, const char* sKr,
+                                         f4 (&accA)[3], f4 (&accP)[3]) {
+  using M = Mma<BF>;
+  constexpr int P = DK * 4 + 16;
+#pragma unroll
+  for (int kc = 0; kc < DK / M::KU; ++kc) {
+    const auto kr0 = M::load(sKr, P, 16 * I0, kc);
+    const auto kl0 = M::load(sKl, P, 16 * R0, kc);
+    const auto ql0 = M::load(sQl, P, 16 * R0, kc);
+    accA[0] = M::mma(kl0, kr0, accA[0]);
+    accP[0] = M::mma(ql0, kr0, accP[0]);
+    if constexpr (R1 >= 0) {
+      const auto kr1 = M::load(sKr, P, 16 * I1, kc);
+      const auto kl1 = (R1 == R0) ? kl0 : M::load(sKl, P, 16 * R1, kc);
+      const auto ql1 = (R1 == R0) ? ql0 : M::load(sQl, P, 16 * R1, kc);
+      accA[1] = M::mma(kl1, kr1, accA[1]);
+      accP[1] = M::mma(ql1, kr1, accP[1]);
+      if constexpr (R2 >= 0) {
+        const auto kr2 = (I2 == I0) ? kr0 : ((I2 == I1) ? kr1 : M::load(sKr, P, 16 * I2, kc));
+        const auto kl2 = (R2 == R1) ? kl1 : M::load(sKl, P, 16 * R2, kc);
+        const auto ql2 = (R2 == R1) ? ql1 : M::load(sQl, P, 16 * R2, kc);
+        accA[2] = M::mma(kl2, kr2, accA[2]);
+        accP[2] = M::mma(ql2, kr2, accP[2]);
+      }
+    }
+  }
+}
+
+
 // ------------------------------------------------------------------ kernel --
 template <int DK, int NSUB, bool BF>
-__global__ __launch_bounds__(kNT, 1) void kda_prefill_kernel(Params p) {
+__global__ __launch_bounds__(64 * (DK / 16), 1) void kda_prefill_kernel(Params p) {
   using L = Lay<DK>;
   using M = Mma<BF>;
+  constexpr int NW = L::NW;         // waves; wave w owns rows 16w..16w+15 of the state
+  constexpr int NT = L::NT;
   constexpr int NP = DK / 2;        // channel pairs in the decay prep
   constexpr int RG = L::RG;         // row groups in the decay prep
-  constexpr int RPG = kC / RG;      // rows per group
-  constexpr int TPW = DK / 64;      // 16-row tiles of the state per wave
+  constexpr int RPG = kC / RG;      // rows per group (8)
   constexpr int VS = 16 * NSUB;     // value columns of this workgroup
 
   __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
@@ -295,65 +369,101 @@ __global__ __launch_bounds__(kNT, 1) void kda_prefill_kernel(Params p) {
     s1 = s0 + p.T_fixed;
   }
 
-  // State slab in registers: S[js][tt][q] = S[c][col0 + 16 js + lr] with
-  // c = 16 (w*TPW + tt) + 4 lg + q.
-  f4 S[NSUB][TPW];
+  // State slab in registers: S[js][q] = S[16w + 4lg + q][col0 + 16js + lr].
+  f4 S[NSUB];
   const int64_t sbase = (int64_t(n) * H + h) * DK * DV;
 #pragma unroll
   for (int js = 0; js < NSUB; ++js)
 #pragma unroll
-    for (int tt = 0; tt < TPW; ++tt)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int c = 16 * (w * TPW + tt) + 4 * lg + q;
-        S[js][tt][q] = p.s_in ? p.s_in[sbase + int64_t(c) * DV + col0 + 16 * js + lr] : 0.f;
-      }
+    for (int q = 0; q < 4; ++q)
+      S[js][q] = p.s_in ? p.s_in[sbase + int64_t(16 * w + 4 * lg + q) * DV + col0 + 16 * js + lr]
+                        : 0.f;
 
+  // Decay prep: thread = (channel pair, group of 8 rows).
   const int cp = t % NP, grp = t / NP;
   const int ch0 = 2 * cp;
   const int rb = grp * RPG;
 
+  // Raw inputs of the next chunk, loaded one chunk ahead.  Every load is
+  // unconditional: rows past the sequence end are clamped to its last row
+  // and their values discarded.
+  typename Raw<BF>::two pk[RPG], pq[RPG];
+  float2 pa[RPG];
+  float pb = 0.f;
+  typename Raw<BF>::one pv[NSUB][4];
+  const int rsk = H * DK, rsv = H * DV;  // token strides (elements)
+  auto load_chunk = [&](int64_t c0, int nvv) {
+    const int64_t kb = (c0 * H + h) * int64_t(DK) + ch0;
+#pragma unroll
+    for (int i = 0; i < RPG; ++i) {
+      const int r = rb + i < nvv ? rb + i : nvv - 1;
+      const int64_t idx = kb + r * rsk;
+      pa[i] = *reinterpret_cast<const float2*>(p.alpha + idx);
+      pk[i] = ldraw2<BF>(p.k, idx);
+      pq[i] = ldraw2<BF>(p.q, idx);
+    }
+    pb = p.beta[(c0 + ((t & 63) < nvv ? (t & 63) : nvv - 1)) * H + h];
+    {
+      // (waves 4.. load the rows of waves 0..3 again: keeps the loads unconditional)
+      const int64_t vb = (c0 * H + h) * int64_t(DV) + col0 + lr;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r0 = 16 * (w & 3) + 4 * lg + q;
+        const int r = r0 < nvv ? r0 : nvv - 1;
+#pragma unroll
+        for (int js = 0; js < NSUB; ++js) pv[js][q] = ldraw1<BF>(p.v, vb + r * rsv + 16 * js);
+      }
+    }
+  };
+  if (s0 < s1) load_chunk(s0, int(s1 - s0 < kC ? s1 - s0 : kC));
+  {
+    // Mirror the output stores that follow the prefetch in every later chunk,
+    // so that the first chunk and the steady state agree on how many memory
+    // operations are in flight after the prefetched loads (otherwise the
+    // compiler's wait for them degrades to waiting for every store).
+    volatile float* sink = g_sink + ((blockIdx.x & 255) << 6) + l;
+#pragma unroll
+    for (int i = 0; i < 4 * NSUB; ++i) *sink = 0.f;
+  }
+
   for (int64_t tok0 = s0; tok0 < s1; tok0 += kC) {
     const int nv = int(s1 - tok0 < kC ? s1 - tok0 : kC);
 
-    // ---- values of this workgroup's columns, in accumulator layout -------
+    // ---- take this chunk's inputs, start loading the next chunk's --------
+    float2 av[RPG], kv[RPG], qv[RPG];
+#pragma unroll
+    for (int i = 0; i < RPG; ++i) {
+      const bool ok = rb + i < nv;
+      av[i] = ok ? pa[i] : make_float2(1.f, 1.f);
+      const float2 kk = cvt2<BF>(pk[i]), qq = cvt2<BF>(pq[i]);
+      kv[i] = ok ? kk : make_float2(0.f, 0.f);
+      qv[i] = ok ? qq : make_float2(0.f, 0.f);
+    }
+    const float bev = (t & 63) < nv ? pb : 0.f;
     float vreg[NSUB][4];
 #pragma unroll
     for (int js = 0; js < NSUB; ++js)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int r = 16 * w + 4 * lg + q;
-        vreg[js][q] = r < nv ? ld1<BF>(p.v, ((tok0 + r) * H + h) * int64_t(DV) + col0 + 16 * js + lr)
-                             : 0.f;
-      }
+      for (int q = 0; q < 4; ++q)
+        vreg[js][q] = (16 * (w & 3) + 4 * lg + q) < nv ? cvt1<BF>(pv[js][q]) : 0.f;
+    if (tok0 + kC < s1) load_chunk(tok0 + kC, int(s1 - tok0 - kC < kC ? s1 - tok0 - kC : kC));
 
     // ---- step 1: decay factors and decayed operands ------------------------
-    float2 av[RPG], kv[RPG], qv[RPG];
-    float2 gp = make_float2(1.f, 1.f);
+    {
+      float2 gp = make_float2(1.f, 1.f);
 #pragma unroll
-    for (int i = 0; i < RPG; ++i) {
-      const int r = rb + i;
-      if (r < nv) {
-        const int64_t idx = ((tok0 + r) * H + h) * int64_t(DK) + ch0;
-        av[i] = *reinterpret_cast<const float2*>(p.alpha + idx);
-        kv[i] = ld2<BF>(p.k, idx);
-        qv[i] = ld2<BF>(p.q, idx);
-      } else {
-        av[i] = make_float2(1.f, 1.f);
-        kv[i] = make_float2(0.f, 0.f);
-        qv[i] = make_float2(0.f, 0.f);
+      for (int i = 0; i < RPG; ++i) {
+        gp.x *= av[i].x;
+        gp.y *= av[i].y;
       }
-      gp.x *= av[i].x;
-      gp.y *= av[i].y;
+      sGP[grp * DK + ch0] = gp.x;
+      sGP[grp * DK + ch0 + 1] = gp.y;
+      if (t < kC) sBe[t] = bev;
     }
-    sGP[grp * DK + ch0] = gp.x;
-    sGP[grp * DK + ch0 + 1] = gp.y;
-    if (t < kC) sBe[t] = t < nv ? p.beta[(tok0 + t) * H + h] : 0.f;
-    __syncthreads();
-
+    lds_barrier();
     {
       float2 krs[RPG];
-      constexpr int half = RG / 2;
+      constexpr int half = RG / 2;  // groups before / after the reference row
       if (grp >= half) {
         // rows after the reference: f = prod_{m < s <= r} alpha_s <= 1
         float2 P = make_float2(1.f, 1.f);
@@ -391,20 +501,18 @@ __global__ __launch_bounds__(kNT, 1) void kda_prefill_kernel(Params p) {
           Q.y *= av[i].y;
         }
       }
-      // Kr^T rows (= key channels), 8 tokens at a time.
+      // Kr^T rows (= key channels): this thread's 8 tokens of two channels.
+      float x0[RPG], x1[RPG];
 #pragma unroll
-      for (int j = 0; j < RPG / 8; ++j) {
-        float x0[8], x1[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          x0[e] = krs[8 * j + e].x;
-          x1[e] = krs[8 * j + e].y;
-        }
-        st8<BF>(sKrT, L::P_T, ch0, rb + 8 * j, x0);
-        st8<BF>(sKrT, L::P_T, ch0 + 1, rb + 8 * j, x1);
+      for (int e = 0; e < RPG; ++e) {
+        x0[e] = krs[e].x;
+        x1[e] = krs[e].y;
       }
+      st8<BF>(sKrT, L::P_T, ch0, rb, x0);
+      st8<BF>(sKrT, L::P_T, ch0 + 1, rb, x1);
       if (grp == 0) {
         float2 gm = make_float2(1.f, 1.f), dl = make_float2(1.f, 1.f);
+#pragma unroll
         for (int g2 = 0; g2 < RG; ++g2) {
           const float a0 = sGP[g2 * DK + ch0], a1 = sGP[g2 * DK + ch0 + 1];
           if (g2 < half) {
@@ -423,67 +531,78 @@ __global__ __launch_bounds__(kNT, 1) void kda_prefill_kernel(Params p) {
         sGN[ch0 + 1] = gm.y * dl.y;
       }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- step 2: A = beta * strict_lower(Kl Kr^T), P = lower(Ql Kr^T) -------
     {
-      // 16x16 tile pairs (R, I), I <= R, spread over the waves.
-      int tr[3], ti[3], np;
-      if (w == 0) { tr[0] = 3; ti[0] = 0; tr[1] = 3; ti[1] = 1; tr[2] = 0; ti[2] = 0; np = 3; }
-      else if (w == 1) { tr[0] = 3; ti[0] = 2; tr[1] = 3; ti[1] = 3; tr[2] = 1; ti[2] = 0; np = 3; }
-      else if (w == 2) { tr[0] = 2; ti[0] = 0; tr[1] = 2; ti[1] = 1; tr[2] = 0; ti[2] = 0; np = 2; }
-      else { tr[0] = 2; ti[0] = 2; tr[1] = 1; ti[1] = 1; tr[2] = 0; ti[2] = 0; np = 2; }
+      // The 10 tile pairs (R, I), I <= R, grouped per wave by shared blocks.
       f4 accA[3], accP[3];
 #pragma unroll
-      for (int j = 0; j < 3; ++j) {
-        accA[j] = f4{0.f, 0.f, 0.f, 0.f};
-        accP[j] = accA[j];
-        if (j < np) {
-#pragma unroll 2
-          for (int kc = 0; kc < DK / M::KU; ++kc) {
-            auto bk = M::load(sKr, L::P_OP, 16 * ti[j], kc);
-            auto ak = M::load(sKl, L::P_OP, 16 * tr[j], kc);
-            auto aq = M::load(sQl, L::P_OP, 16 * tr[j], kc);
-            accA[j] = M::mma(ak, bk, accA[j]);
-            accP[j] = M::mma(aq, bk, accP[j]);
-          }
+      for (int j = 0; j < 3; ++j) accA[j] = accP[j] = f4{0.f, 0.f, 0.f, 0.f};
+      int pR[3] = {-1, -1, -1}, pI[3] = {0, 0, 0};
+      if constexpr (NW >= 8) {
+        switch (w) {
+          case 0: ap_tiles<BF, DK, 3, 0, 3, 1, -1, 0>(sKl, sQl, sKr, accA, accP); pR[0] = 3; pI[0] = 0; pR[1] = 3; pI[1] = 1; break;
+          case 1: ap_tiles<BF, DK, 3, 2, 3, 3, -1, 0>(sKl, sQl, sKr, accA, accP); pR[0] = 3; pI[0] = 2; pR[1] = 3; pI[1] = 3; break;
+          case 2: ap_tiles<BF, DK, 2, 0, 2, 1, -1, 0>(sKl, sQl, sKr, accA, accP); pR[0] = 2; pI[0] = 0; pR[1] = 2; pI[1] = 1; break;
+          case 3: ap_tiles<BF, DK, 2, 2, -1, 0, -1, 0>(sKl, sQl, sKr, accA, accP); pR[0] = 2; pI[0] = 2; break;
+          case 4: ap_tiles<BF, DK, 1, 0, 1, 1, -1, 0>(sKl, sQl, sKr, accA, accP); pR[0] = 1; pI[0] = 0; pR[1] = 1; pI[1] = 1; break;
+          case 5: ap_tiles<BF, DK, 0, 0, -1, 0, -1, 0>(sKl, sQl, sKr, accA, accP); pR[0] = 0; pI[0] = 0; break;
+          default: break;
+        }
+      } else {
+        switch (w) {
+          case 0: ap_tiles<BF, DK, 3, 0, 3, 1, 3, 2>(sKl, sQl, sKr, accA, accP); pR[0] = 3; pI[0] = 0; pR[1] = 3; pI[1] = 1; pR[2] = 3; pI[2] = 2; break;
+          case 1: ap_tiles<BF, DK, 3, 3, 2, 2, 1, 1>(sKl, sQl, sKr, accA, accP); pR[0] = 3; pI[0] = 3; pR[1] = 2; pI[1] = 2; pR[2] = 1; pI[2] = 1; break;
+          case 2: ap_tiles<BF, DK, 2, 0, 2, 1, 1, 0>(sKl, sQl, sKr, accA, accP); pR[0] = 2; pI[0] = 0; pR[1] = 2; pI[1] = 1; pR[2] = 1; pI[2] = 0; break;
+          default: ap_tiles<BF, DK, 0, 0, -1, 0, -1, 0>(sKl, sQl, sKr, accA, accP); pR[0] = 0; pI[0] = 0; break;
         }
       }
-      __syncthreads();  // every read of Kr is done: A and P overwrite it
+      lds_barrier();  // every read of Kr is done: A and P overwrite it
 #pragma unroll
       for (int j = 0; j < 3; ++j) {
-        if (j < np) {
+        if (pR[j] >= 0) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int r = 16 * tr[j] + 4 * lg + q;
-            const int i = 16 * ti[j] + lr;
-            sA[r * L::P_AF + i] = i < r ? sBe[r] * accA[j][q] : 0.f;
+            const int r = 16 * pR[j] + 4 * lg + q;
+            const int i = 16 * pI[j] + lr;
             st1<BF>(sP, L::P_T, r, i, i <= r ? accP[j][q] : 0.f);
+            sA[r * L::P_AF + i] = i < r ? sBe[r] * accA[j][q] : 0.f;
           }
         }
       }
       // Upper tiles of P that the 32-wide K chunks of the P U product touch.
-      if (w == 2 || w == 3) {
-        const int R = w == 2 ? 0 : 2;
+      if (w == NW - 1) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) st1<BF>(sP, L::P_T, 16 * R + 4 * lg + q, 16 * (R + 1) + lr, 0.f);
+        for (int q = 0; q < 4; ++q) {
+          st1<BF>(sP, L::P_T, 4 * lg + q, 16 + lr, 0.f);
+          st1<BF>(sP, L::P_T, 32 + 4 * lg + q, 48 + lr, 0.f);
+        }
       }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- step 3: T = (I + A)^-1 Diag(beta) ---------------------------------
-    // 3a: inverses of the four 16x16 unit-lower diagonal blocks by forward
-    // substitution (lane = (block, column)); the other waves clear the upper
-    // blocks.
+    // 3a: inverses D_R of the four 16x16 unit-lower diagonal blocks by forward
+    // substitution (wave 0, lane = (block, column)); the other waves clear the
+    // upper blocks of L^-1.
     if (w == 0) {
       const int R = lg, j = lr;
       const float* Ab = sA + 16 * R * L::P_AF + 16 * R;
       float x[16];
 #pragma unroll
+      for (int r = 0; r < 16; ++r) x[r] = 0.f;
+#pragma unroll
       for (int r = 0; r < 16; ++r) {
         float s = r == j ? 1.f : 0.f;
 #pragma unroll
-        for (int i = 0; i < r; ++i) s -= Ab[r * L::P_AF + i] * x[i];
+        for (int i4 = 0; i4 < r; i4 += 4) {
+          const float4 a4 = *reinterpret_cast<const float4*>(Ab + r * L::P_AF + i4);
+          s -= a4.x * x[i4];
+          if (i4 + 1 < r) s -= a4.y * x[i4 + 1];
+          if (i4 + 2 < r) s -= a4.z * x[i4 + 2];
+          if (i4 + 3 < r) s -= a4.w * x[i4 + 3];
+        }
         x[r] = s;
       }
       float* Lb = sLi + 16 * R * L::P_AF + 16 * R;
@@ -491,52 +610,48 @@ __global__ __launch_bounds__(kNT, 1) void kda_prefill_kernel(Params p) {
       for (int r = 0; r < 16; ++r) Lb[r * L::P_AF + j] = x[r];
     } else {
       // blocks (R, I) with I > R: (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
-      for (int e = t - 64; e < 6 * 256; e += 192) {
+      for (int e = t - 64; e < 6 * 256; e += NT - 64) {
         const int blk = e >> 8, rr = (e >> 4) & 15, cc = e & 15;
         const int R = blk < 3 ? 0 : (blk < 5 ? 1 : 2);
         const int I = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
         sLi[(16 * R + rr) * L::P_AF + 16 * I + cc] = 0.f;
       }
     }
-    __syncthreads();
-    // 3b: off-diagonal blocks, L^-1_RI = -D_R sum_{I<=J<R} A_RJ L^-1_JI,
-    // level by level; each thread computes one element of each 16x16 block.
-    {
-      const int rr = t >> 4, cc = t & 15;
-      auto Ab = [&](int R, int I) { return sA + 16 * R * L::P_AF + 16 * I; };
-      auto Lb = [&](int R, int I) { return sLi + 16 * R * L::P_AF + 16 * I; };
-      auto mm = [&](const float* X, int xp, const float* Y, int yp) {
-        float s = 0.f;
+    lds_barrier();
+    // 3b: off-diagonal blocks row block by row block:
+    //     L^-1_{R,I} = -D_R (sum_{I<=J<R} A_{R,J} L^-1_{J,I}),  wave I, fp32 MFMA.
 #pragma unroll
-        for (int kk = 0; kk < 16; ++kk) s += X[rr * xp + kk] * Y[kk * yp + cc];
-        return s;
-      };
-      constexpr int pf = L::P_AF;
-      // level 1: X_{s,s-1} = -D_s A_{s,s-1} D_{s-1}
+    for (int R = 1; R < 4; ++R) {
+      if (w < R) {
+        const int I = w;
+        f4 y = f4{0.f, 0.f, 0.f, 0.f};
+        for (int J = I; J < R; ++J) {
 #pragma unroll
-      for (int s = 1; s < 4; ++s) sTmp[(s - 1) * 256 + t] = mm(Ab(s, s - 1), pf, Lb(s - 1, s - 1), pf);
-      __syncthreads();
+          for (int s4 = 0; s4 < 4; ++s4) {
+            const float a = sA[(16 * R + lr) * L::P_AF + 16 * J + 4 * s4 + lg];
+            const float bb = sLi[(16 * J + 4 * s4 + lg) * L::P_AF + 16 * I + lr];
+            y = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bb, y, 0, 0, 0);
+          }
+        }
+        float* tmp = sTmp + 256 * I;
 #pragma unroll
-      for (int s = 1; s < 4; ++s) Lb(s, s - 1)[rr * pf + cc] = -mm(Lb(s, s), pf, sTmp + (s - 1) * 256, 16);
-      __syncthreads();
-      // level 2: X_20 = -D_2 (A_20 D_0 + A_21 X_10), X_31 = -D_3 (A_31 D_1 + A_32 X_21)
-      sTmp[t] = mm(Ab(2, 0), pf, Lb(0, 0), pf) + mm(Ab(2, 1), pf, Lb(1, 0), pf);
-      sTmp[256 + t] = mm(Ab(3, 1), pf, Lb(1, 1), pf) + mm(Ab(3, 2), pf, Lb(2, 1), pf);
-      __syncthreads();
-      Lb(2, 0)[rr * pf + cc] = -mm(Lb(2, 2), pf, sTmp, 16);
-      Lb(3, 1)[rr * pf + cc] = -mm(Lb(3, 3), pf, sTmp + 256, 16);
-      __syncthreads();
-      // level 3: X_30 = -D_3 (A_30 D_0 + A_31 X_10 + A_32 X_20)
-      sTmp[t] = mm(Ab(3, 0), pf, Lb(0, 0), pf) + mm(Ab(3, 1), pf, Lb(1, 0), pf) +
-                mm(Ab(3, 2), pf, Lb(2, 0), pf);
-      __syncthreads();
-      Lb(3, 0)[rr * pf + cc] = -mm(Lb(3, 3), pf, sTmp, 16);
-      __syncthreads();
+        for (int q = 0; q < 4; ++q) tmp[(4 * lg + q) * 16 + lr] = y[q];
+        f4 x = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+          const float a = sLi[(16 * R + lr) * L::P_AF + 16 * R + 4 * s4 + lg];
+          const float bb = tmp[(4 * s4 + lg) * 16 + lr];
+          x = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bb, x, 0, 0, 0);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sLi[(16 * R + 4 * lg + q) * L::P_AF + 16 * I + lr] = -x[q];
+      }
+      lds_barrier();
     }
     // 3c: T = L^-1 Diag(beta), converted in place to the operand format
     // (an 8-element group of fp32 occupies exactly the bytes of its hi/lo form).
 #pragma unroll
-    for (int e = t; e < kC * 8; e += kNT) {
+    for (int e = t; e < kC * 8; e += NT) {
       const int r = e >> 3, g8 = e & 7;
       float x[8];
       const float* src = sLi + r * L::P_AF + 8 * g8;
@@ -544,60 +659,77 @@ __global__ __launch_bounds__(kNT, 1) void kda_prefill_kernel(Params p) {
       for (int i = 0; i < 8; ++i) x[i] = src[i] * sBe[8 * g8 + i];
       st8<BF>(sT, L::P_T, r, 8 * g8, x);
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- step 4: the state pass, 16 value columns at a time ----------------
+    // Waves 0..3 compute X and U for rows 16w..; the output rows 16*ow.. are
+    // computed by waves 4..7 when there are eight waves (their Ql S_B product
+    // overlaps X and U), else by waves 0..3 after U.
+    constexpr bool kSplitO = NW >= 8;
+    const bool xw = w < 4;
+    const bool owave = kSplitO ? (w >= 4) : (w < 4);
+    const int ow = w & 3;
+    const int kend_u = BF ? 32 * ((w + 2) >> 1) : 16 * (w + 1);
+    const int kend_o = BF ? 32 * ((ow + 2) >> 1) : 16 * (ow + 1);
 #pragma unroll
     for (int js = 0; js < NSUB; ++js) {
       // 4a: S_B^T = (Diag(gamma_m) S)^T for these columns.
-#pragma unroll
-      for (int tt = 0; tt < TPW; ++tt) {
-        const int c0 = 16 * (w * TPW + tt) + 4 * lg;
+      {
+        const int c0 = 16 * w + 4 * lg;
         float x[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) x[q] = S[js][tt][q] * sGM[c0 + q];
+        for (int q = 0; q < 4; ++q) x[q] = S[js][q] * sGM[c0 + q];
         st4<BF>(sSBT, L::P_OP, lr, c0, x);
       }
-      __syncthreads();
-      // 4b: X = V - Kl S_B  (rows 16w..16w+15)
-      {
+      lds_barrier();
+      // 4b: X = V - Kl S_B; the output waves start O = Ql S_B.
+      f4 acco = f4{0.f, 0.f, 0.f, 0.f};
+      if (xw) {
         f4 acc = gemm<BF>(f4{0.f, 0.f, 0.f, 0.f}, sKl, L::P_OP, 16 * w, sSBT, L::P_OP, 0, 0, DK);
         float x[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) x[q] = vreg[js][q] - acc[q];
         st4<BF>(sXT, L::P_T, lr, 16 * w + 4 * lg, x);
       }
-      __syncthreads();
+      if (kSplitO && owave)
+        acco = gemm<BF>(acco, sQl, L::P_OP, 16 * ow, sSBT, L::P_OP, 0, 0, DK);
+      lds_barrier();
       // 4c: U = T X  (T is lower triangular: K up to the end of this row block)
-      const int kend = BF ? 32 * ((w + 2) >> 1) : 16 * (w + 1);
-      {
-        f4 acc = gemm<BF>(f4{0.f, 0.f, 0.f, 0.f}, sT, L::P_T, 16 * w, sXT, L::P_T, 0, 0, kend);
+      if (xw) {
+        f4 acc = gemm<BF>(f4{0.f, 0.f, 0.f, 0.f}, sT, L::P_T, 16 * w, sXT, L::P_T, 0, 0, kend_u);
         float x[4] = {acc[0], acc[1], acc[2], acc[3]};
         st4<BF>(sUT, L::P_T, lr, 16 * w + 4 * lg, x);
       }
-      __syncthreads();
+      lds_barrier();
       // 4d: O = Ql S_B + P U
+      if (owave) {
+        if constexpr (!kSplitO)
+          acco = gemm<BF>(acco, sQl, L::P_OP, 16 * ow, sSBT, L::P_OP, 0, 0, DK);
+        acco = gemm<BF>(acco, sP, L::P_T, 16 * ow, sUT, L::P_T, 0, 0, kend_o);
+      }
       {
-        f4 acc = gemm<BF>(f4{0.f, 0.f, 0.f, 0.f}, sQl, L::P_OP, 16 * w, sSBT, L::P_OP, 0, 0, DK);
-        acc = gemm<BF>(acc, sP, L::P_T, 16 * w, sUT, L::P_T, 0, 0, kend);
+        // Every wave issues the stores; rows past the end of the sequence and
+        // waves without output rows store into a sink.  Unconditional stores
+        // stay visible to the compiler's memory-counter bookkeeping, so taking
+        // the prefetched inputs never waits for output stores to drain.
+        float* orow = p.o + ((tok0 + 16 * ow + 4 * lg) * H + h) * int64_t(DV) + col0 + 16 * js + lr;
+        float* sink = g_sink + ((blockIdx.x & 255) << 6) + l;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int r = 16 * w + 4 * lg + q;
-          if (r < nv) p.o[((tok0 + r) * H + h) * int64_t(DV) + col0 + 16 * js + lr] = acc[q];
+          float* dst = owave && 16 * ow + 4 * lg + q < nv ? orow + int64_t(q) * H * DV : sink;
+          *dst = acco[q];
         }
       }
-      // 4e: S' = Diag(gamma_n) S + Diag(gamma_n / gamma_m) Kr^T U
-#pragma unroll
-      for (int tt = 0; tt < TPW; ++tt) {
-        const int tc = w * TPW + tt;
-        f4 acc = gemm<BF>(f4{0.f, 0.f, 0.f, 0.f}, sKrT, L::P_T, 16 * tc, sUT, L::P_T, 0, 0, kC);
+      // 4e: S' = Diag(gamma_n) S + Diag(gamma_n / gamma_m) Kr^T U  (rows 16w..)
+      {
+        f4 acc = gemm<BF>(f4{0.f, 0.f, 0.f, 0.f}, sKrT, L::P_T, 16 * w, sUT, L::P_T, 0, 0, kC);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int c = 16 * tc + 4 * lg + q;
-          S[js][tt][q] = sGN[c] * S[js][tt][q] + sDL[c] * acc[q];
+          const int c = 16 * w + 4 * lg + q;
+          S[js][q] = sGN[c] * S[js][q] + sDL[c] * acc[q];
         }
       }
-      __syncthreads();
+      lds_barrier();
     }
   }
 
@@ -605,19 +737,15 @@ __global__ __launch_bounds__(kNT, 1) void kda_prefill_kernel(Params p) {
 #pragma unroll
     for (int js = 0; js < NSUB; ++js)
 #pragma unroll
-      for (int tt = 0; tt < TPW; ++tt)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int c = 16 * (w * TPW + tt) + 4 * lg + q;
-          p.s_out[sbase + int64_t(c) * DV + col0 + 16 * js + lr] = S[js][tt][q];
-        }
+      for (int q = 0; q < 4; ++q)
+        p.s_out[sbase + int64_t(16 * w + 4 * lg + q) * DV + col0 + 16 * js + lr] = S[js][q];
   }
 }
 
 template <int DK, int NSUB, bool BF>
 void launch_t(const Params& p, int64_t nblocks, hipStream_t st) {
-  hipLaunchKernelGGL((kda_prefill_kernel<DK, NSUB, BF>), dim3(unsigned(nblocks)), dim3(kNT), 0,
-                     st, p);
+  hipLaunchKernelGGL((kda_prefill_kernel<DK, NSUB, BF>), dim3(unsigned(nblocks)),
+                     dim3(Lay<DK>::NT), 0, st, p);
 }
 
 template <int DK, bool BF>
