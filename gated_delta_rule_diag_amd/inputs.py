@@ -162,7 +162,7 @@ def device_head_inputs(c, n, h, L, DK, DV, device, torch_dtype):
     import torch
 
     g = torch.Generator(device=device)
-    g.manual_seed(((SEED * 1000003 + c) * 1000003 + n) * 1000003 + h)
+    g.manual_seed((((SEED * 1000003 + c) * 1000003 + n) * 1000003 + h) % (1 << 63))
     f32 = torch.float32
     q = torch.randn((L, DK), generator=g, device=device, dtype=f32)
     k = torch.randn((L, DK), generator=g, device=device, dtype=f32)
