@@ -83,6 +83,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one plain 512 MiB device-to-device copy before the timed region "
+                         "(reference for HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -124,6 +127,11 @@ def main():
     _, dstate = kda.chunk_prefill(wq.to(bf), wk.to(bf), wv.to(bf), wa.contiguous(), wb.contiguous())
     del x, wq, wk, wv, wa, wb
     do = torch.empty((ND, H, D), device=dev, dtype=torch.float32)
+    if args.copy_calibration:
+        src = torch.ones(512 << 18, device=dev, dtype=torch.float32)  # 512 MiB
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        del src, dst
     torch.cuda.synchronize()
 
     def step(ev=None):
@@ -156,13 +164,26 @@ def main():
     pre_tflops = prefill_algorithmic_flops(T, H, D, D) / (pre_ms * 1e-3) / 1e12
 
     # HBM traffic measured by rocprofv3 counters (FETCH_SIZE + WRITE_SIZE,
-    # scaled by a plain-copy calibration) for the kernels as they are now.
-    traffic = None
-    tfile = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "traffic.json")
+    # scaled by a plain-copy calibration), used only while the kernel source
+    # is the one the counters were taken on.
+    traffic, traffic_dec = None, None
+    here = os.path.dirname(os.path.abspath(__file__))
+    tfile = os.path.join(here, "profiles", "traffic.json")
     if os.path.exists(tfile):
+        import hashlib
+
         with open(tfile) as f:
             tj = json.load(f)
-        traffic = tj.get("prefill_bytes_per_launch")
+        csrc = os.path.join(here, "gated_delta_rule_diag_amd", "csrc")
+
+        def sha16(name):
+            with open(os.path.join(csrc, name), "rb") as f:
+                return hashlib.sha256(f.read()).hexdigest()[:16]
+
+        if tj.get("prefill_kernel_source_sha256_16") == sha16("kda_prefill.hip"):
+            traffic = tj.get("prefill_bytes_per_launch")
+        if tj.get("decode_kernel_source_sha256_16") == sha16("kda_decode.hip"):
+            traffic_dec = tj.get("decode_bytes_per_launch")
 
     out = {
         "metric": "KDA prefill tokens/s + decode us/step (B=256); % of MFMA / HBM peak",
@@ -204,6 +225,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": dec_gbs / HBM_PEAK_GBS,
+            "traffic": traffic_dec,
             "algorithmic_bytes": dec_bytes,
         },
     }
