@@ -112,13 +112,13 @@ const char* kda_last_error_message(void) { return g_last_error.c_str(); }
 
 size_t kda_chunk_prefill_workspace_size(int B, int T, int H, int DK, int DV, int chunk) {
   if (B < 0 || T < 0 || H < 0 || !dims_ok(DK) || !dims_ok(DV) || chunk != 64) return 0;
-  return kda::prefill_workspace_bytes(B, int64_t(B) * T, H, DK, DV);
+  return kda::prefill_workspace_bytes(B, int64_t(B) * T, H, DK, DV, false);
 }
 
 size_t kda_chunk_prefill_varlen_workspace_size(int N, int T_total, int H, int DK, int DV,
                                                int chunk) {
   if (N < 0 || T_total < 0 || H < 0 || !dims_ok(DK) || !dims_ok(DV) || chunk != 64) return 0;
-  return kda::prefill_workspace_bytes(N, T_total, H, DK, DV);
+  return kda::prefill_workspace_bytes(N, T_total, H, DK, DV, true);
 }
 
 static kda_status_t run_prefill(kda::PrefillArgs& a, size_t need, void* stream) {
@@ -153,7 +153,7 @@ kda_status_t kda_chunk_prefill(int B, int T, int H, int DK, int DV, int chunk,
   a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta;
   a.state_in = state_in; a.o = o; a.state_out = state_out;
   a.workspace = workspace; a.workspace_bytes = workspace_bytes;
-  return run_prefill(a, kda::prefill_workspace_bytes(B, a.T_total, H, DK, DV), stream);
+  return run_prefill(a, kda::prefill_workspace_bytes(B, a.T_total, H, DK, DV, false), stream);
 }
 
 kda_status_t kda_chunk_prefill_varlen(int N, int T_total, const int32_t* cu_seqlens, int H,
@@ -179,7 +179,7 @@ kda_status_t kda_chunk_prefill_varlen(int N, int T_total, const int32_t* cu_seql
   a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta;
   a.state_in = state_in; a.o = o; a.state_out = state_out;
   a.workspace = workspace; a.workspace_bytes = workspace_bytes;
-  return run_prefill(a, kda::prefill_workspace_bytes(N, T_total, H, DK, DV), stream);
+  return run_prefill(a, kda::prefill_workspace_bytes(N, T_total, H, DK, DV, true), stream);
 }
 
 kda_status_t kda_decode_step(int N, int H, int DK, int DV, kda_dtype_t in_dtype, const void* q,

@@ -43,6 +43,6 @@ struct DecodeArgs {
 // Launchers return 0 on success, else a non-zero code and a static message.
 int launch_prefill(const PrefillArgs& a, void* stream, const char** msg);
 int launch_decode(const DecodeArgs& a, void* stream, const char** msg);
-size_t prefill_workspace_bytes(int N, int64_t T_total, int H, int DK, int DV);
+size_t prefill_workspace_bytes(int N, int64_t T_total, int H, int DK, int DV, bool varlen);
 
 }  // namespace kda

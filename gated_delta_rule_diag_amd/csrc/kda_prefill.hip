@@ -30,6 +30,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdlib.h>
+#include <string.h>
 
 #include "kda_internal.h"
 
@@ -144,17 +145,22 @@ struct Mma<false> {  // fp32 MFMA
   }
 };
 
-// acc += A[arow0.., k0:k1] * B[brow0.., k0:k1]^T  (both stored [row][K]).
-template <bool BF>
+// acc += A[arow0.., 0:K] * B[brow0.., 0:K]^T  (both stored [row][K]).  All
+// fragments are loaded before the first product, so the LDS latency is paid
+// once per call rather than once per K chunk.
+template <bool BF, int K>
 __device__ __forceinline__ f4 gemm(f4 acc, const char* A, int ap, int arow0, const char* B,
-                                   int bp, int brow0, int k0, int k1) {
+                                   int bp, int brow0) {
   using M = Mma<BF>;
-#pragma unroll 4
-  for (int kc = k0 / M::KU; kc < k1 / M::KU; ++kc) {
-    auto a = M::load(A, ap, arow0, kc);
-    auto b = M::load(B, bp, brow0, kc);
-    acc = M::mma(a, b, acc);
+  constexpr int NKC = K / M::KU;
+  typename M::Frag a[NKC], b[NKC];
+#pragma unroll
+  for (int kc = 0; kc < NKC; ++kc) {
+    a[kc] = M::load(A, ap, arow0, kc);
+    b[kc] = M::load(B, bp, brow0, kc);
   }
+#pragma unroll
+  for (int kc = 0; kc < NKC; ++kc) acc = M::mma(a[kc], b[kc], acc);
   return acc;
 }
 
@@ -252,12 +258,12 @@ template <bool BF> struct Raw { typedef uint32_t two; typedef uint32_t one; };
 template <> struct Raw<false> { typedef float2 two; typedef float one; };
 
 template <bool BF>
-__device__ __forceinline__ typename Raw<BF>::two ldraw2(const void* p, int64_t i) {
+__device__ __forceinline__ typename Raw<BF>::two ldraw2(const void* p, uint32_t i) {
   if constexpr (BF) return *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p) + i);
   else return *reinterpret_cast<const float2*>(static_cast<const float*>(p) + i);
 }
 template <bool BF>
-__device__ __forceinline__ typename Raw<BF>::one ldraw1(const void* p, int64_t i) {
+__device__ __forceinline__ typename Raw<BF>::one ldraw1(const void* p, uint32_t i) {
   if constexpr (BF) return uint32_t(static_cast<const uint16_t*>(p)[i]);
   else return static_cast<const float*>(p)[i];
 }
@@ -276,39 +282,320 @@ __device__ __forceinline__ float cvt1(typename Raw<BF>::one r) {
 // Destination of output stores for rows past the end of a sequence (never read).
 __device__ float g_sink[256 * 64];
 
-// A and P tiles of up to three (R, I) pairs (R < 0: unused) of one wave.
-// Each row block of Kl/Ql and column block of Kr is loaded once per K chunk
-// and shared by the pair's two products (the LDS read bandwidth, not the
-// MFMA rate, bounds this step).
-template <bool BF, int DK, int R0, int I0, int R1, int I1, int R2, int I2>
-__device__ __forceinline__ void ap_tiles(const char* sKl, const char* sQl, const char* sKr,
-                                         f4 (&accA)[3], f4 (&accP)[3]) {
+// One wave's tiles of the intra-chunk Gram matrices, A = Kl Kr^T (type 0)
+// and P = Ql Kr^T (type 1): up to three (type, R, I) tiles (type < 0:
+// unused).  Row and column blocks shared by the tiles are loaded once per K
+// chunk (this step is bound by LDS read bandwidth, not by the MFMA rate).
+template <bool BF, int DK, int T0, int R0, int I0, int T1, int R1, int I1, int T2, int R2, int I2>
+__device__ __forceinline__ void gram_tiles(const char* sKl, const char* sQl, const char* sKr,
+                                           f4 (&acc)[3]) {
   using M = Mma<BF>;
   constexpr int P = DK * 4 + 16;
 #pragma unroll
   for (int kc = 0; kc < DK / M::KU; ++kc) {
-    const auto kr0 = M::load(sKr, P, 16 * I0, kc);
-    const auto kl0 = M::load(sKl, P, 16 * R0, kc);
-    const auto ql0 = M::load(sQl, P, 16 * R0, kc);
-    accA[0] = M::mma(kl0, kr0, accA[0]);
-    accP[0] = M::mma(ql0, kr0, accP[0]);
-    if constexpr (R1 >= 0) {
-      const auto kr1 = M::load(sKr, P, 16 * I1, kc);
-      const auto kl1 = (R1 == R0) ? kl0 : M::load(sKl, P, 16 * R1, kc);
-      const auto ql1 = (R1 == R0) ? ql0 : M::load(sQl, P, 16 * R1, kc);
-      accA[1] = M::mma(kl1, kr1, accA[1]);
-      accP[1] = M::mma(ql1, kr1, accP[1]);
-      if constexpr (R2 >= 0) {
-        const auto kr2 = (I2 == I0) ? kr0 : ((I2 == I1) ? kr1 : M::load(sKr, P, 16 * I2, kc));
-        const auto kl2 = (R2 == R1) ? kl1 : M::load(sKl, P, 16 * R2, kc);
-        const auto ql2 = (R2 == R1) ? ql1 : M::load(sQl, P, 16 * R2, kc);
-        accA[2] = M::mma(kl2, kr2, accA[2]);
-        accP[2] = M::mma(ql2, kr2, accP[2]);
+    const auto c0 = M::load(sKr, P, 16 * I0, kc);
+    const auto r0 = M::load(T0 == 0 ? sKl : sQl, P, 16 * R0, kc);
+    acc[0] = M::mma(r0, c0, acc[0]);
+    if constexpr (T1 >= 0) {
+      const auto c1 = (I1 == I0) ? c0 : M::load(sKr, P, 16 * I1, kc);
+      const auto r1 = (T1 == T0 && R1 == R0) ? r0 : M::load(T1 == 0 ? sKl : sQl, P, 16 * R1, kc);
+      acc[1] = M::mma(r1, c1, acc[1]);
+      if constexpr (T2 >= 0) {
+        const auto c2 = (I2 == I0) ? c0 : ((I2 == I1) ? c1 : M::load(sKr, P, 16 * I2, kc));
+        const auto r2 = (T2 == T0 && R2 == R0)
+                            ? r0
+                            : ((T2 == T1 && R2 == R1) ? r1 : M::load(T2 == 0 ? sKl : sQl, P, 16 * R2, kc));
+        acc[2] = M::mma(r2, c2, acc[2]);
       }
     }
   }
 }
 
+// Steps 1-3 of one chunk (everything that does not depend on the state):
+// decay factors and decayed operands, the Gram tiles A and P, and
+// T = (I + A)^-1 Diag(beta).  On return the LDS holds Kl, Ql, Kr^T, T, P and
+// gamma_m, gamma_n / gamma_m, gamma_n for the chunk.  av/kv/qv are this
+// thread's 8 rows of two channels (rows past the sequence end: alpha = 1,
+// k = q = 0), bev is beta of token (threadIdx.x & 63) (0 past the end).
+template <int DK, bool BF>
+__device__ __forceinline__ void prep_chunk(char* smem, const float2 (&av)[kC / 8],
+                                           const float2 (&kv)[kC / 8], const float2 (&qv)[kC / 8],
+                                           float bev) {
+  using L = Lay<DK>;
+  using M = Mma<BF>;
+  constexpr int NW = L::NW;
+  constexpr int NT = L::NT;
+  constexpr int NP = DK / 2;
+  constexpr int RG = L::RG;
+  constexpr int RPG = kC / RG;
+  char* const sKl = smem + L::OFF_KL;
+  char* const sQl = smem + L::OFF_QL;
+  char* const sKrT = smem + L::OFF_KRT;
+  char* const sKr = smem + L::OFF_X;
+  float* const sA = reinterpret_cast<float*>(smem + L::OFF_A);
+  char* const sP = smem + L::OFF_P;
+  char* const sT = smem + L::OFF_T;
+  float* const sLi = reinterpret_cast<float*>(smem + L::OFF_T);
+  float* const sTmp = reinterpret_cast<float*>(smem + L::OFF_TMP);
+  float* const sGP = reinterpret_cast<float*>(smem + L::OFF_GP);
+  float* const sGM = reinterpret_cast<float*>(smem + L::OFF_GM);
+  float* const sDL = reinterpret_cast<float*>(smem + L::OFF_DL);
+  float* const sGN = reinterpret_cast<float*>(smem + L::OFF_GN);
+  float* const sBe = reinterpret_cast<float*>(smem + L::OFF_BE);
+  const int t = threadIdx.x;
+  const int l = t & 63;
+  const int w = t >> 6;
+  const int lr = l & 15;
+  const int lg = l >> 4;
+  const int cp = t % NP, grp = t / NP;
+  const int ch0 = 2 * cp;
+  const int rb = grp * RPG;
+  (void)l;
+
+  // ---- step 1: decay factors and decayed operands ------------------------
+  {
+    float2 gp = make_float2(1.f, 1.f);
+#pragma unroll
+    for (int i = 0; i < RPG; ++i) {
+      gp.x *= av[i].x;
+      gp.y *= av[i].y;
+    }
+    sGP[grp * DK + ch0] = gp.x;
+    sGP[grp * DK + ch0 + 1] = gp.y;
+    if (t < kC) sBe[t] = bev;
+  }
+  lds_barrier();
+  {
+    float2 krs[RPG];
+    constexpr int half = RG / 2;  // groups before / after the reference row
+    if (grp >= half) {
+      // rows after the reference: f = prod_{m < s <= r} alpha_s <= 1
+      float2 P = make_float2(1.f, 1.f);
+      for (int g2 = half; g2 < grp; ++g2) {
+        P.x *= sGP[g2 * DK + ch0];
+        P.y *= sGP[g2 * DK + ch0 + 1];
+      }
+#pragma unroll
+      for (int i = 0; i < RPG; ++i) {
+        P.x *= av[i].x;
+        P.y *= av[i].y;
+        const float ix = rcp(P.x), iy = rcp(P.y);
+        const int r = rb + i;
+        st2<BF>(sKl, L::P_OP, r, ch0, kv[i].x * P.x, kv[i].y * P.y);
+        st2<BF>(sQl, L::P_OP, r, ch0, qv[i].x * P.x, qv[i].y * P.y);
+        krs[i] = make_float2(kv[i].x * ix, kv[i].y * iy);
+        st2<BF>(sKr, L::P_OP, r, ch0, krs[i].x, krs[i].y);
+      }
+    } else {
+      // rows up to the reference: 1/f = prod_{r < s <= m} alpha_s <= 1
+      float2 Q = make_float2(1.f, 1.f);
+      for (int g2 = grp + 1; g2 < half; ++g2) {
+        Q.x *= sGP[g2 * DK + ch0];
+        Q.y *= sGP[g2 * DK + ch0 + 1];
+      }
+#pragma unroll
+      for (int i = RPG - 1; i >= 0; --i) {
+        const float fx = rcp(Q.x), fy = rcp(Q.y);
+        const int r = rb + i;
+        st2<BF>(sKl, L::P_OP, r, ch0, kv[i].x * fx, kv[i].y * fy);
+        st2<BF>(sQl, L::P_OP, r, ch0, qv[i].x * fx, qv[i].y * fy);
+        krs[i] = make_float2(kv[i].x * Q.x, kv[i].y * Q.y);
+        st2<BF>(sKr, L::P_OP, r, ch0, krs[i].x, krs[i].y);
+        Q.x *= av[i].x;
+        Q.y *= av[i].y;
+      }
+    }
+    // Kr^T rows (= key channels): this thread's 8 tokens of two channels.
+    float x0[RPG], x1[RPG];
+#pragma unroll
+    for (int e = 0; e < RPG; ++e) {
+      x0[e] = krs[e].x;
+      x1[e] = krs[e].y;
+    }
+    st8<BF>(sKrT, L::P_T, ch0, rb, x0);
+    st8<BF>(sKrT, L::P_T, ch0 + 1, rb, x1);
+    if (grp == 0) {
+      float2 gm = make_float2(1.f, 1.f), dl = make_float2(1.f, 1.f);
+#pragma unroll
+      for (int g2 = 0; g2 < RG; ++g2) {
+        const float a0 = sGP[g2 * DK + ch0], a1 = sGP[g2 * DK + ch0 + 1];
+        if (g2 < half) {
+          gm.x *= a0;
+          gm.y *= a1;
+        } else {
+          dl.x *= a0;
+          dl.y *= a1;
+        }
+      }
+      sGM[ch0] = gm.x;
+      sGM[ch0 + 1] = gm.y;
+      sDL[ch0] = dl.x;
+      sDL[ch0 + 1] = dl.y;
+      sGN[ch0] = gm.x * dl.x;
+      sGN[ch0 + 1] = gm.y * dl.y;
+    }
+  }
+  lds_barrier();
+
+  // ---- step 2: A = beta * strict_lower(Kl Kr^T), P = lower(Ql Kr^T) -------
+  {
+    // The 20 lower 16x16 tiles (10 of A, 10 of P), spread so that the two
+    // waves sharing a SIMD (w and w + 4) together do 5 tiles per K chunk.
+    f4 acc[2][3];
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int j = 0; j < 3; ++j) acc[g][j] = f4{0.f, 0.f, 0.f, 0.f};
+    int tT[2][3], tR[2][3], tI[2][3];
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int j = 0; j < 3; ++j) tT[g][j] = -1, tR[g][j] = 0, tI[g][j] = 0;
+#define KDA_TILES(g, a0, b0, c0_, a1, b1, c1_, a2, b2, c2_)                                      \
+gram_tiles<BF, DK, a0, b0, c0_, a1, b1, c1_, a2, b2, c2_>(sKl, sQl, sKr, acc[g]);              \
+tT[g][0] = a0; tR[g][0] = b0; tI[g][0] = c0_;                                                  \
+tT[g][1] = a1; tR[g][1] = b1; tI[g][1] = c1_;                                                  \
+tT[g][2] = a2; tR[g][2] = b2; tI[g][2] = c2_;
+    if constexpr (NW >= 8) {
+      switch (w) {
+        case 0: KDA_TILES(0, 0, 3, 0, 0, 3, 1, 0, 3, 2) break;
+        case 1: KDA_TILES(0, 1, 3, 0, 1, 3, 1, 1, 3, 2) break;
+        case 2: KDA_TILES(0, 0, 2, 0, 0, 2, 1, 0, 1, 1) break;
+        case 3: KDA_TILES(0, 1, 1, 1, 1, 1, 0, 0, 1, 0) break;
+        case 4: KDA_TILES(0, 0, 3, 3, 0, 2, 2, -1, 0, 0) break;
+        case 5: KDA_TILES(0, 1, 3, 3, 1, 2, 2, -1, 0, 0) break;
+        case 6: KDA_TILES(0, 1, 2, 0, 1, 2, 1, -1, 0, 0) break;
+        default: KDA_TILES(0, 0, 0, 0, 1, 0, 0, -1, 0, 0) break;
+      }
+    } else {
+      switch (w) {
+        case 0: KDA_TILES(0, 0, 3, 0, 0, 3, 1, 0, 3, 2) KDA_TILES(1, 1, 3, 0, 1, 3, 1, -1, 0, 0) break;
+        case 1: KDA_TILES(0, 1, 3, 2, 0, 3, 3, 1, 3, 3) KDA_TILES(1, 0, 2, 2, 1, 2, 2, -1, 0, 0) break;
+        case 2: KDA_TILES(0, 0, 2, 0, 0, 2, 1, 1, 2, 0) KDA_TILES(1, 1, 2, 1, 0, 1, 1, -1, 0, 0) break;
+        default: KDA_TILES(0, 1, 1, 1, 0, 1, 0, 1, 1, 0) KDA_TILES(1, 0, 0, 0, 1, 0, 0, -1, 0, 0) break;
+      }
+    }
+#undef KDA_TILES
+    lds_barrier();  // every read of Kr is done: A and P overwrite it
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        if (tT[g][j] >= 0) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int r = 16 * tR[g][j] + 4 * lg + q;
+            const int i = 16 * tI[g][j] + lr;
+            if (tT[g][j] == 1) st1<BF>(sP, L::P_T, r, i, i <= r ? acc[g][j][q] : 0.f);
+            else sA[r * L::P_AF + i] = i < r ? sBe[r] * acc[g][j][q] : 0.f;
+          }
+        }
+      }
+    // Upper tiles of P are zero (the P U product runs over the whole chunk).
+    if (w >= NW - 2) {
+#pragma unroll
+      for (int e = 0; e < 3; ++e) {
+        const int blk = (w - (NW - 2)) * 3 + e;  // (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
+        const int R = blk < 3 ? 0 : (blk < 5 ? 1 : 2);
+        const int I = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) st1<BF>(sP, L::P_T, 16 * R + 4 * lg + q, 16 * I + lr, 0.f);
+      }
+    }
+  }
+  lds_barrier();
+
+  // ---- step 3: T = (I + A)^-1 Diag(beta) ---------------------------------
+  // 3a: inverses D_R of the four 16x16 unit-lower diagonal blocks by forward
+  // substitution (wave 0, lane = (block, column)); the other waves clear the
+  // upper blocks of L^-1.
+  if (w == 0) {
+    const int R = lg, j = lr;
+    const float* Ab = sA + 16 * R * L::P_AF + 16 * R;
+    // Rows are loaded two rows ahead of the substitution, so each row's LDS
+    // latency overlaps the previous rows' arithmetic.
+    float4 ar[16][4];
+#pragma unroll
+    for (int r = 1; r < 3; ++r)
+#pragma unroll
+      for (int i4 = 0; i4 < r; i4 += 4) ar[r][i4 >> 2] = *reinterpret_cast<const float4*>(Ab + r * L::P_AF + i4);
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[r] = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      if (r + 2 < 16) {
+#pragma unroll
+        for (int i4 = 0; i4 < r + 2; i4 += 4)
+          ar[r + 2][i4 >> 2] = *reinterpret_cast<const float4*>(Ab + (r + 2) * L::P_AF + i4);
+      }
+      float s = r == j ? 1.f : 0.f;
+#pragma unroll
+      for (int i4 = 0; i4 < r; i4 += 4) {
+        const float4 a4 = ar[r][i4 >> 2];
+        s -= a4.x * x[i4];
+        if (i4 + 1 < r) s -= a4.y * x[i4 + 1];
+        if (i4 + 2 < r) s -= a4.z * x[i4 + 2];
+        if (i4 + 3 < r) s -= a4.w * x[i4 + 3];
+      }
+      x[r] = s;
+    }
+    float* Lb = sLi + 16 * R * L::P_AF + 16 * R;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) Lb[r * L::P_AF + j] = x[r];
+  } else {
+    // blocks (R, I) with I > R: (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
+    for (int e = t - 64; e < 6 * 256; e += NT - 64) {
+      const int blk = e >> 8, rr = (e >> 4) & 15, cc = e & 15;
+      const int R = blk < 3 ? 0 : (blk < 5 ? 1 : 2);
+      const int I = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
+      sLi[(16 * R + rr) * L::P_AF + 16 * I + cc] = 0.f;
+    }
+  }
+  lds_barrier();
+  // 3b: off-diagonal blocks row block by row block:
+  //     L^-1_{R,I} = -D_R (sum_{I<=J<R} A_{R,J} L^-1_{J,I}),  wave I, fp32 MFMA.
+#pragma unroll
+  for (int R = 1; R < 4; ++R) {
+    if (w < R) {
+      const int I = w;
+      f4 y = f4{0.f, 0.f, 0.f, 0.f};
+      for (int J = I; J < R; ++J) {
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+          const float a = sA[(16 * R + lr) * L::P_AF + 16 * J + 4 * s4 + lg];
+          const float bb = sLi[(16 * J + 4 * s4 + lg) * L::P_AF + 16 * I + lr];
+          y = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bb, y, 0, 0, 0);
+        }
+      }
+      float* tmp = sTmp + 256 * I;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) tmp[(4 * lg + q) * 16 + lr] = y[q];
+      f4 x = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const float a = sLi[(16 * R + lr) * L::P_AF + 16 * R + 4 * s4 + lg];
+        const float bb = tmp[(4 * s4 + lg) * 16 + lr];
+        x = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bb, x, 0, 0, 0);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sLi[(16 * R + 4 * lg + q) * L::P_AF + 16 * I + lr] = -x[q];
+    }
+    lds_barrier();
+  }
+  // 3c: T = L^-1 Diag(beta), converted in place to the operand format
+  // (an 8-element group of fp32 occupies exactly the bytes of its hi/lo form).
+#pragma unroll
+  for (int e = t; e < kC * 8; e += NT) {
+    const int r = e >> 3, g8 = e & 7;
+    float x[8];
+    const float* src = sLi + r * L::P_AF + 8 * g8;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = src[i] * sBe[8 * g8 + i];
+    st8<BF>(sT, L::P_T, r, 8 * g8, x);
+  }
+  lds_barrier();
+}
 
 // ------------------------------------------------------------------ kernel --
 template <int DK, int NSUB, bool BF>
@@ -392,26 +679,32 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_prefill_kernel(Params p
   float pb = 0.f;
   typename Raw<BF>::one pv[NSUB][4];
   const int rsk = H * DK, rsv = H * DV;  // token strides (elements)
+  constexpr int ESZ = BF ? 2 : 4;        // bytes per q/k/v element
   auto load_chunk = [&](int64_t c0, int nvv) {
-    const int64_t kb = (c0 * H + h) * int64_t(DK) + ch0;
+    // Wave-uniform base pointers for the chunk and 32-bit per-lane offsets
+    // (scalar-base addressing: one vector add per load).
+    const int64_t row0 = c0 * H + h;
+    const float* ab = p.alpha + row0 * DK;
+    const char* kb = static_cast<const char*>(p.k) + row0 * DK * ESZ;
+    const char* qb = static_cast<const char*>(p.q) + row0 * DK * ESZ;
 #pragma unroll
     for (int i = 0; i < RPG; ++i) {
       const int r = rb + i < nvv ? rb + i : nvv - 1;
-      const int64_t idx = kb + r * rsk;
-      pa[i] = *reinterpret_cast<const float2*>(p.alpha + idx);
-      pk[i] = ldraw2<BF>(p.k, idx);
-      pq[i] = ldraw2<BF>(p.q, idx);
+      const uint32_t off = uint32_t(r * rsk + ch0);
+      pa[i] = *reinterpret_cast<const float2*>(ab + off);
+      pk[i] = ldraw2<BF>(kb, off);
+      pq[i] = ldraw2<BF>(qb, off);
     }
-    pb = p.beta[(c0 + ((t & 63) < nvv ? (t & 63) : nvv - 1)) * H + h];
+    pb = p.beta[row0 + uint32_t(((t & 63) < nvv ? (t & 63) : nvv - 1) * H)];
     {
       // (waves 4.. load the rows of waves 0..3 again: keeps the loads unconditional)
-      const int64_t vb = (c0 * H + h) * int64_t(DV) + col0 + lr;
+      const char* vb = static_cast<const char*>(p.v) + (row0 * DV + col0) * ESZ;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int r0 = 16 * (w & 3) + 4 * lg + q;
         const int r = r0 < nvv ? r0 : nvv - 1;
 #pragma unroll
-        for (int js = 0; js < NSUB; ++js) pv[js][q] = ldraw1<BF>(p.v, vb + r * rsv + 16 * js);
+        for (int js = 0; js < NSUB; ++js) pv[js][q] = ldraw1<BF>(vb, uint32_t(r * rsv + 16 * js + lr));
       }
     }
   };
@@ -448,218 +741,7 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_prefill_kernel(Params p
         vreg[js][q] = (16 * (w & 3) + 4 * lg + q) < nv ? cvt1<BF>(pv[js][q]) : 0.f;
     if (tok0 + kC < s1) load_chunk(tok0 + kC, int(s1 - tok0 - kC < kC ? s1 - tok0 - kC : kC));
 
-    // ---- step 1: decay factors and decayed operands ------------------------
-    {
-      float2 gp = make_float2(1.f, 1.f);
-#pragma unroll
-      for (int i = 0; i < RPG; ++i) {
-        gp.x *= av[i].x;
-        gp.y *= av[i].y;
-      }
-      sGP[grp * DK + ch0] = gp.x;
-      sGP[grp * DK + ch0 + 1] = gp.y;
-      if (t < kC) sBe[t] = bev;
-    }
-    lds_barrier();
-    {
-      float2 krs[RPG];
-      constexpr int half = RG / 2;  // groups before / after the reference row
-      if (grp >= half) {
-        // rows after the reference: f = prod_{m < s <= r} alpha_s <= 1
-        float2 P = make_float2(1.f, 1.f);
-        for (int g2 = half; g2 < grp; ++g2) {
-          P.x *= sGP[g2 * DK + ch0];
-          P.y *= sGP[g2 * DK + ch0 + 1];
-        }
-#pragma unroll
-        for (int i = 0; i < RPG; ++i) {
-          P.x *= av[i].x;
-          P.y *= av[i].y;
-          const float ix = rcp(P.x), iy = rcp(P.y);
-          const int r = rb + i;
-          st2<BF>(sKl, L::P_OP, r, ch0, kv[i].x * P.x, kv[i].y * P.y);
-          st2<BF>(sQl, L::P_OP, r, ch0, qv[i].x * P.x, qv[i].y * P.y);
-          krs[i] = make_float2(kv[i].x * ix, kv[i].y * iy);
-          st2<BF>(sKr, L::P_OP, r, ch0, krs[i].x, krs[i].y);
-        }
-      } else {
-        // rows up to the reference: 1/f = prod_{r < s <= m} alpha_s <= 1
-        float2 Q = make_float2(1.f, 1.f);
-        for (int g2 = grp + 1; g2 < half; ++g2) {
-          Q.x *= sGP[g2 * DK + ch0];
-          Q.y *= sGP[g2 * DK + ch0 + 1];
-        }
-#pragma unroll
-        for (int i = RPG - 1; i >= 0; --i) {
-          const float fx = rcp(Q.x), fy = rcp(Q.y);
-          const int r = rb + i;
-          st2<BF>(sKl, L::P_OP, r, ch0, kv[i].x * fx, kv[i].y * fy);
-          st2<BF>(sQl, L::P_OP, r, ch0, qv[i].x * fx, qv[i].y * fy);
-          krs[i] = make_float2(kv[i].x * Q.x, kv[i].y * Q.y);
-          st2<BF>(sKr, L::P_OP, r, ch0, krs[i].x, krs[i].y);
-          Q.x *= av[i].x;
-          Q.y *= av[i].y;
-        }
-      }
-      // Kr^T rows (= key channels): this thread's 8 tokens of two channels.
-      float x0[RPG], x1[RPG];
-#pragma unroll
-      for (int e = 0; e < RPG; ++e) {
-        x0[e] = krs[e].x;
-        x1[e] = krs[e].y;
-      }
-      st8<BF>(sKrT, L::P_T, ch0, rb, x0);
-      st8<BF>(sKrT, L::P_T, ch0 + 1, rb, x1);
-      if (grp == 0) {
-        float2 gm = make_float2(1.f, 1.f), dl = make_float2(1.f, 1.f);
-#pragma unroll
-        for (int g2 = 0; g2 < RG; ++g2) {
-          const float a0 = sGP[g2 * DK + ch0], a1 = sGP[g2 * DK + ch0 + 1];
-          if (g2 < half) {
-            gm.x *= a0;
-            gm.y *= a1;
-          } else {
-            dl.x *= a0;
-            dl.y *= a1;
-          }
-        }
-        sGM[ch0] = gm.x;
-        sGM[ch0 + 1] = gm.y;
-        sDL[ch0] = dl.x;
-        sDL[ch0 + 1] = dl.y;
-        sGN[ch0] = gm.x * dl.x;
-        sGN[ch0 + 1] = gm.y * dl.y;
-      }
-    }
-    lds_barrier();
-
-    // ---- step 2: A = beta * strict_lower(Kl Kr^T), P = lower(Ql Kr^T) -------
-    {
-      // The 10 tile pairs (R, I), I <= R, grouped per wave by shared blocks.
-      f4 accA[3], accP[3];
-#pragma unroll
-      for (int j = 0; j < 3; ++j) accA[j] = accP[j] = f4{0.f, 0.f, 0.f, 0.f};
-      int pR[3] = {-1, -1, -1}, pI[3] = {0, 0, 0};
-      if constexpr (NW >= 8) {
-        switch (w) {
-          case 0: ap_tiles<BF, DK, 3, 0, 3, 1, -1, 0>(sKl, sQl, sKr, accA, accP); pR[0] = 3; pI[0] = 0; pR[1] = 3; pI[1] = 1; break;
-          case 1: ap_tiles<BF, DK, 3, 2, 3, 3, -1, 0>(sKl, sQl, sKr, accA, accP); pR[0] = 3; pI[0] = 2; pR[1] = 3; pI[1] = 3; break;
-          case 2: ap_tiles<BF, DK, 2, 0, 2, 1, -1, 0>(sKl, sQl, sKr, accA, accP); pR[0] = 2; pI[0] = 0; pR[1] = 2; pI[1] = 1; break;
-          case 3: ap_tiles<BF, DK, 2, 2, -1, 0, -1, 0>(sKl, sQl, sKr, accA, accP); pR[0] = 2; pI[0] = 2; break;
-          case 4: ap_tiles<BF, DK, 1, 0, 1, 1, -1, 0>(sKl, sQl, sKr, accA, accP); pR[0] = 1; pI[0] = 0; pR[1] = 1; pI[1] = 1; break;
-          case 5: ap_tiles<BF, DK, 0, 0, -1, 0, -1, 0>(sKl, sQl, sKr, accA, accP); pR[0] = 0; pI[0] = 0; break;
-          default: break;
-        }
-      } else {
-        switch (w) {
-          case 0: ap_tiles<BF, DK, 3, 0, 3, 1, 3, 2>(sKl, sQl, sKr, accA, accP); pR[0] = 3; pI[0] = 0; pR[1] = 3; pI[1] = 1; pR[2] = 3; pI[2] = 2; break;
-          case 1: ap_tiles<BF, DK, 3, 3, 2, 2, 1, 1>(sKl, sQl, sKr, accA, accP); pR[0] = 3; pI[0] = 3; pR[1] = 2; pI[1] = 2; pR[2] = 1; pI[2] = 1; break;
-          case 2: ap_tiles<BF, DK, 2, 0, 2, 1, 1, 0>(sKl, sQl, sKr, accA, accP); pR[0] = 2; pI[0] = 0; pR[1] = 2; pI[1] = 1; pR[2] = 1; pI[2] = 0; break;
-          default: ap_tiles<BF, DK, 0, 0, -1, 0, -1, 0>(sKl, sQl, sKr, accA, accP); pR[0] = 0; pI[0] = 0; break;
-        }
-      }
-      lds_barrier();  // every read of Kr is done: A and P overwrite it
-#pragma unroll
-      for (int j = 0; j < 3; ++j) {
-        if (pR[j] >= 0) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int r = 16 * pR[j] + 4 * lg + q;
-            const int i = 16 * pI[j] + lr;
-            st1<BF>(sP, L::P_T, r, i, i <= r ? accP[j][q] : 0.f);
-            sA[r * L::P_AF + i] = i < r ? sBe[r] * accA[j][q] : 0.f;
-          }
-        }
-      }
-      // Upper tiles of P that the 32-wide K chunks of the P U product touch.
-      if (w == NW - 1) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          st1<BF>(sP, L::P_T, 4 * lg + q, 16 + lr, 0.f);
-          st1<BF>(sP, L::P_T, 32 + 4 * lg + q, 48 + lr, 0.f);
-        }
-      }
-    }
-    lds_barrier();
-
-    // ---- step 3: T = (I + A)^-1 Diag(beta) ---------------------------------
-    // 3a: inverses D_R of the four 16x16 unit-lower diagonal blocks by forward
-    // substitution (wave 0, lane = (block, column)); the other waves clear the
-    // upper blocks of L^-1.
-    if (w == 0) {
-      const int R = lg, j = lr;
-      const float* Ab = sA + 16 * R * L::P_AF + 16 * R;
-      float x[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) x[r] = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float s = r == j ? 1.f : 0.f;
-#pragma unroll
-        for (int i4 = 0; i4 < r; i4 += 4) {
-          const float4 a4 = *reinterpret_cast<const float4*>(Ab + r * L::P_AF + i4);
-          s -= a4.x * x[i4];
-          if (i4 + 1 < r) s -= a4.y * x[i4 + 1];
-          if (i4 + 2 < r) s -= a4.z * x[i4 + 2];
-          if (i4 + 3 < r) s -= a4.w * x[i4 + 3];
-        }
-        x[r] = s;
-      }
-      float* Lb = sLi + 16 * R * L::P_AF + 16 * R;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) Lb[r * L::P_AF + j] = x[r];
-    } else {
-      // blocks (R, I) with I > R: (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
-      for (int e = t - 64; e < 6 * 256; e += NT - 64) {
-        const int blk = e >> 8, rr = (e >> 4) & 15, cc = e & 15;
-        const int R = blk < 3 ? 0 : (blk < 5 ? 1 : 2);
-        const int I = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
-        sLi[(16 * R + rr) * L::P_AF + 16 * I + cc] = 0.f;
-      }
-    }
-    lds_barrier();
-    // 3b: off-diagonal blocks row block by row block:
-    //     L^-1_{R,I} = -D_R (sum_{I<=J<R} A_{R,J} L^-1_{J,I}),  wave I, fp32 MFMA.
-#pragma unroll
-    for (int R = 1; R < 4; ++R) {
-      if (w < R) {
-        const int I = w;
-        f4 y = f4{0.f, 0.f, 0.f, 0.f};
-        for (int J = I; J < R; ++J) {
-#pragma unroll
-          for (int s4 = 0; s4 < 4; ++s4) {
-            const float a = sA[(16 * R + lr) * L::P_AF + 16 * J + 4 * s4 + lg];
-            const float bb = sLi[(16 * J + 4 * s4 + lg) * L::P_AF + 16 * I + lr];
-            y = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bb, y, 0, 0, 0);
-          }
-        }
-        float* tmp = sTmp + 256 * I;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) tmp[(4 * lg + q) * 16 + lr] = y[q];
-        f4 x = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) {
-          const float a = sLi[(16 * R + lr) * L::P_AF + 16 * R + 4 * s4 + lg];
-          const float bb = tmp[(4 * s4 + lg) * 16 + lr];
-          x = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bb, x, 0, 0, 0);
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) sLi[(16 * R + 4 * lg + q) * L::P_AF + 16 * I + lr] = -x[q];
-      }
-      lds_barrier();
-    }
-    // 3c: T = L^-1 Diag(beta), converted in place to the operand format
-    // (an 8-element group of fp32 occupies exactly the bytes of its hi/lo form).
-#pragma unroll
-    for (int e = t; e < kC * 8; e += NT) {
-      const int r = e >> 3, g8 = e & 7;
-      float x[8];
-      const float* src = sLi + r * L::P_AF + 8 * g8;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = src[i] * sBe[8 * g8 + i];
-      st8<BF>(sT, L::P_T, r, 8 * g8, x);
-    }
-    lds_barrier();
+    prep_chunk<DK, BF>(smem, av, kv, qv, bev);
 
     // ---- step 4: the state pass, 16 value columns at a time ----------------
     // Waves 0..3 compute X and U for rows 16w..; the output rows 16*ow.. are
@@ -669,8 +751,6 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_prefill_kernel(Params p
     const bool xw = w < 4;
     const bool owave = kSplitO ? (w >= 4) : (w < 4);
     const int ow = w & 3;
-    const int kend_u = BF ? 32 * ((w + 2) >> 1) : 16 * (w + 1);
-    const int kend_o = BF ? 32 * ((ow + 2) >> 1) : 16 * (ow + 1);
 #pragma unroll
     for (int js = 0; js < NSUB; ++js) {
       // 4a: S_B^T = (Diag(gamma_m) S)^T for these columns.
@@ -685,18 +765,18 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_prefill_kernel(Params p
       // 4b: X = V - Kl S_B; the output waves start O = Ql S_B.
       f4 acco = f4{0.f, 0.f, 0.f, 0.f};
       if (xw) {
-        f4 acc = gemm<BF>(f4{0.f, 0.f, 0.f, 0.f}, sKl, L::P_OP, 16 * w, sSBT, L::P_OP, 0, 0, DK);
+        f4 acc = gemm<BF, DK>(f4{0.f, 0.f, 0.f, 0.f}, sKl, L::P_OP, 16 * w, sSBT, L::P_OP, 0);
         float x[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) x[q] = vreg[js][q] - acc[q];
         st4<BF>(sXT, L::P_T, lr, 16 * w + 4 * lg, x);
       }
       if (kSplitO && owave)
-        acco = gemm<BF>(acco, sQl, L::P_OP, 16 * ow, sSBT, L::P_OP, 0, 0, DK);
+        acco = gemm<BF, DK>(acco, sQl, L::P_OP, 16 * ow, sSBT, L::P_OP, 0);
       lds_barrier();
       // 4c: U = T X  (T is lower triangular: K up to the end of this row block)
       if (xw) {
-        f4 acc = gemm<BF>(f4{0.f, 0.f, 0.f, 0.f}, sT, L::P_T, 16 * w, sXT, L::P_T, 0, 0, kend_u);
+        f4 acc = gemm<BF, kC>(f4{0.f, 0.f, 0.f, 0.f}, sT, L::P_T, 16 * w, sXT, L::P_T, 0);
         float x[4] = {acc[0], acc[1], acc[2], acc[3]};
         st4<BF>(sUT, L::P_T, lr, 16 * w + 4 * lg, x);
       }
@@ -704,25 +784,26 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_prefill_kernel(Params p
       // 4d: O = Ql S_B + P U
       if (owave) {
         if constexpr (!kSplitO)
-          acco = gemm<BF>(acco, sQl, L::P_OP, 16 * ow, sSBT, L::P_OP, 0, 0, DK);
-        acco = gemm<BF>(acco, sP, L::P_T, 16 * ow, sUT, L::P_T, 0, 0, kend_o);
+          acco = gemm<BF, DK>(acco, sQl, L::P_OP, 16 * ow, sSBT, L::P_OP, 0);
+        acco = gemm<BF, kC>(acco, sP, L::P_T, 16 * ow, sUT, L::P_T, 0);
       }
       {
         // Every wave issues the stores; rows past the end of the sequence and
         // waves without output rows store into a sink.  Unconditional stores
         // stay visible to the compiler's memory-counter bookkeeping, so taking
         // the prefetched inputs never waits for output stores to drain.
-        float* orow = p.o + ((tok0 + 16 * ow + 4 * lg) * H + h) * int64_t(DV) + col0 + 16 * js + lr;
+        float* ob = p.o + (tok0 * H + h) * int64_t(DV) + col0 + 16 * js;  // uniform
         float* sink = g_sink + ((blockIdx.x & 255) << 6) + l;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          float* dst = owave && 16 * ow + 4 * lg + q < nv ? orow + int64_t(q) * H * DV : sink;
+          const int r = 16 * ow + 4 * lg + q;
+          float* dst = owave && r < nv ? ob + uint32_t(r * rsv + lr) : sink;
           *dst = acco[q];
         }
       }
       // 4e: S' = Diag(gamma_n) S + Diag(gamma_n / gamma_m) Kr^T U  (rows 16w..)
       {
-        f4 acc = gemm<BF>(f4{0.f, 0.f, 0.f, 0.f}, sKrT, L::P_T, 16 * w, sUT, L::P_T, 0, 0, kC);
+        f4 acc = gemm<BF, kC>(f4{0.f, 0.f, 0.f, 0.f}, sKrT, L::P_T, 16 * w, sUT, L::P_T, 0);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int c = 16 * w + 4 * lg + q;
@@ -730,6 +811,515 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_prefill_kernel(Params p
         }
       }
       lds_barrier();
+    }
+  }
+
+  if (p.s_out) {
+#pragma unroll
+    for (int js = 0; js < NSUB; ++js)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        p.s_out[sbase + int64_t(16 * w + 4 * lg + q) * DV + col0 + 16 * js + lr] = S[js][q];
+  }
+}
+
+
+// ==================================================================== staged ==
+// Staged form for workloads with few (sequence, head) chains.  The fused
+// kernel above repeats steps 1-3 in every value slab of a chain; here they run
+// once per chunk, for all chunks at once (kda_stage_kernel), together with the
+// state-independent parts of steps 4b-4e folded into four matrices:
+//     W  = T Kl Diag(gamma_m)     [64 x DK]    so that  U = Uv - W S
+//     Uv = T V                    [64 x DV]
+//     Qg = Ql Diag(gamma_m)       [64 x DK]    so that  O = Qg S + P U
+//     Kg = Diag(delta) Kr^T       [DK x 64]    so that  S' = Diag(gamma_n) S + Kg U
+// (delta = gamma_n / gamma_m).  The sequential pass (kda_chain_kernel) then
+// streams them from a workspace straight into MFMA registers: two dependent
+// products and two barriers per chunk.
+//
+// Workspace slot of one (chunk, sequence, head), "fragment order": every
+// matrix is stored as the MFMA A-operand fragments of its 16-row blocks, in
+// the order a wave loads them, so that each load instruction reads 1 KiB of
+// consecutive bytes.
+//   split bf16: fragment (rb, kc) covers rows 16rb.., K 32kc.. and takes
+//     2 KiB: lane l's 8 hi parts at 16l, its 8 lo parts at 1024 + 16l (lane l:
+//     row 16rb + l%16, K 32kc + 8(l/16) + e).
+//   fp32: unit (rb, g) covers rows 16rb.., K 16g.. and takes 1 KiB: lane l
+//     holds 4 floats, fragment kc = 4g + i at row 16rb + l%16, K 4kc + l/16.
+// Uv is stored as MFMA result tiles (rb, 16-column block): 1 KiB, lane l's 4
+// floats (rows 16rb + 4(l/16) + q, column l%16) at 16l.  gamma_n last.
+template <int DK, int DV>
+struct Slot {
+  static constexpr int OFF_W = 0;
+  static constexpr int OFF_Q = OFF_W + 64 * DK * 4;
+  static constexpr int OFF_K = OFF_Q + 64 * DK * 4;
+  static constexpr int OFF_P = OFF_K + DK * 64 * 4;
+  static constexpr int OFF_U = OFF_P + 64 * 64 * 4;
+  static constexpr int OFF_G = OFF_U + 64 * DV * 4;
+  static constexpr int BYTES = OFF_G + DK * 4;
+  static_assert(BYTES % 256 == 0, "slot alignment");
+};
+
+struct StageParams {
+  int H, DV, nslab;
+  int64_t T_fixed;   // tokens per sequence
+  int64_t pairs;     // sequences x heads
+  int64_t c_begin;   // first chunk (of every sequence) of this segment
+  int64_t nseg;      // chunks per sequence in this segment
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* alpha;
+  const float* beta;
+  const float* s_in;
+  float* o;
+  float* s_out;
+  char* ws;          // slot of item i = (c - c_begin) * pairs + pair
+};
+
+template <bool BF> struct FL;
+template <> struct FL<true> {
+  static constexpr int KU = 32;       // K per fragment
+  static constexpr int UNIT = 2048;   // bytes per fragment
+  template <int NKC>
+  __device__ static void load(Mma<true>::Frag (&f)[NKC], const char* rb) {
+    const int l = lane_id();
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      f[kc].hi = *reinterpret_cast<const bf8*>(rb + kc * 2048 + 16 * l);
+      f[kc].lo = *reinterpret_cast<const bf8*>(rb + kc * 2048 + 1024 + 16 * l);
+    }
+  }
+};
+template <> struct FL<false> {
+  static constexpr int KU = 16;       // K per 1 KiB unit (four fragments)
+  static constexpr int UNIT = 1024;
+  template <int NKC>
+  __device__ static void load(float (&f)[NKC], const char* rb) {
+    static_assert(NKC % 4 == 0, "fp32 fragments come in fours");
+    const int l = lane_id();
+#pragma unroll
+    for (int g = 0; g < NKC / 4; ++g) {
+      const float4 x = *reinterpret_cast<const float4*>(rb + g * 1024 + 16 * l);
+      f[4 * g] = x.x;
+      f[4 * g + 1] = x.y;
+      f[4 * g + 2] = x.z;
+      f[4 * g + 3] = x.w;
+    }
+  }
+};
+
+__device__ __forceinline__ float bf_lo16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Writes an LDS operand array (ROWS x K, layout of the operand arrays above)
+// to global memory in fragment order, each element times rs[row] (RS) and
+// cs[k] (CS).  The fragments are dealt out to the waves round-robin; every
+// wave writes the same number.
+template <bool BF, int K, int ROWS, int NW, bool RS, bool CS>
+__device__ __forceinline__ void export_frags(char* dst, const char* src, int pitch, const float* rs,
+                                             const float* cs) {
+  using F = FL<BF>;
+  constexpr int NU = K / F::KU;                 // units per row block
+  constexpr int NF = (ROWS / 16) * NU;
+  static_assert(NF % NW == 0, "equal share per wave");
+  const int l = lane_id(), w = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < NF / NW; ++i) {
+    const int f = w + NW * i;
+    const int rb = f / NU, u = f - rb * NU;
+    const int row = 16 * rb + (l & 15);
+    const float r = RS ? rs[row] : 1.f;
+    if constexpr (BF) {
+      const char* s = src + row * pitch + (u * 4 + (l >> 4)) * 32;
+      uint4 hi = *reinterpret_cast<const uint4*>(s);
+      uint4 lo = *reinterpret_cast<const uint4*>(s + 16);
+      if constexpr (RS || CS) {
+        const int k0 = u * 32 + 8 * (l >> 4);
+        const uint32_t hw[4] = {hi.x, hi.y, hi.z, hi.w}, lw[4] = {lo.x, lo.y, lo.z, lo.w};
+        uint32_t nh[4], nl[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float x0 = bf_lo16(hw[j]) + bf_lo16(lw[j]);
+          float x1 = bf_hi16(hw[j]) + bf_hi16(lw[j]);
+          x0 *= r * (CS ? cs[k0 + 2 * j] : 1.f);
+          x1 *= r * (CS ? cs[k0 + 2 * j + 1] : 1.f);
+          uint16_t h0, l0, h1, l1;
+          split(x0, h0, l0);
+          split(x1, h1, l1);
+          nh[j] = uint32_t(h0) | (uint32_t(h1) << 16);
+          nl[j] = uint32_t(l0) | (uint32_t(l1) << 16);
+        }
+        hi = make_uint4(nh[0], nh[1], nh[2], nh[3]);
+        lo = make_uint4(nl[0], nl[1], nl[2], nl[3]);
+      }
+      *reinterpret_cast<uint4*>(dst + f * 2048 + 16 * l) = hi;
+      *reinterpret_cast<uint4*>(dst + f * 2048 + 1024 + 16 * l) = lo;
+    } else {
+      float x[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int k = (4 * u + j) * 4 + (l >> 4);
+        x[j] = *reinterpret_cast<const float*>(src + row * pitch + 4 * k) * r * (CS ? cs[k] : 1.f);
+      }
+      *reinterpret_cast<float4*>(dst + f * 1024 + 16 * l) = make_float4(x[0], x[1], x[2], x[3]);
+    }
+  }
+}
+
+// Steps 1-3 and the folded products for every (chunk, sequence, head) of a
+// segment.  Persistent: workgroup b takes items b, b + G, ...; the raw inputs
+// of its next item are loaded while it works on the current one.
+template <int DK, int DV, bool BF>
+__global__ __launch_bounds__(64 * (DK / 16), 1) void kda_stage_kernel(StageParams p) {
+  using L = Lay<DK>;
+  using SL = Slot<DK, DV>;
+  using M = Mma<BF>;
+  constexpr int NW = L::NW;
+  constexpr int NT = L::NT;
+  constexpr int NP = DK / 2;                 // channel pairs of the decay prep
+  constexpr int RPG = kC / L::RG;            // its rows per thread (8)
+  constexpr int NPV = DV / 2;                // value column pairs
+  constexpr int RV = kC * NPV / NT;          // rows per thread of V (4, 8 or 16)
+  constexpr int KCC = kC / M::KU;
+  constexpr int ESZ = BF ? 2 : 4;
+  static_assert(RV % 4 == 0, "V rows per thread");
+  __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
+  static_assert(DV * L::P_T <= L::SZ_X, "V^T fits the A/P space");
+
+  const int t = threadIdx.x;
+  const int l = t & 63;
+  const int w = t >> 6;
+  const int lr = l & 15, lg = l >> 4;
+  const int H = p.H;
+  const int64_t items = p.nseg * p.pairs;
+
+  const int cp = t % NP, grp = t / NP;
+  const int ch0 = 2 * cp, rb0 = grp * RPG;
+  const int cpv = t % NPV, gv = t / NPV;
+  const int vc0 = 2 * cpv, vr0 = gv * RV;
+
+  typename Raw<BF>::two pk[RPG], pq[RPG], pv[RV];
+  float2 pa[RPG];
+  float pb = 0.f;
+  // V of item `it`: loaded after steps 1-3 (it is first needed by the folded
+  // products; keeping it in registers through steps 1-3 would spill).
+  auto load_v = [&](int64_t it) {
+    const int64_t c = p.c_begin + it / p.pairs;
+    const int64_t pr = it - (it / p.pairs) * p.pairs;
+    const int h = int(pr % H);
+    const int64_t n = pr / H;
+    const int64_t tok0 = n * p.T_fixed + c * kC;
+    const int64_t rem = p.T_fixed - c * kC;
+    const int nvv = int(rem < kC ? rem : kC);
+    const char* vb = static_cast<const char*>(p.v) + (tok0 * H + h) * DV * ESZ;
+    const int rsv = H * DV;
+#pragma unroll
+    for (int i = 0; i < RV; ++i) {
+      const int r = vr0 + i < nvv ? vr0 + i : nvv - 1;
+      pv[i] = ldraw2<BF>(vb, uint32_t(r * rsv + vc0));
+    }
+  };
+  auto load_item = [&](int64_t it) {
+    const int64_t c = p.c_begin + it / p.pairs;
+    const int64_t pr = it - (it / p.pairs) * p.pairs;
+    const int h = int(pr % H);
+    const int64_t n = pr / H;
+    const int64_t tok0 = n * p.T_fixed + c * kC;
+    const int64_t rem = p.T_fixed - c * kC;
+    const int nvv = int(rem < kC ? rem : kC);
+    const int64_t row0 = tok0 * H + h;
+    const float* ab = p.alpha + row0 * DK;
+    const char* kb = static_cast<const char*>(p.k) + row0 * DK * ESZ;
+    const char* qb = static_cast<const char*>(p.q) + row0 * DK * ESZ;
+    const int rsk = H * DK;
+#pragma unroll
+    for (int i = 0; i < RPG; ++i) {
+      const int r = rb0 + i < nvv ? rb0 + i : nvv - 1;
+      const uint32_t off = uint32_t(r * rsk + ch0);
+      pa[i] = *reinterpret_cast<const float2*>(ab + off);
+      pk[i] = ldraw2<BF>(kb, off);
+      pq[i] = ldraw2<BF>(qb, off);
+    }
+    pb = p.beta[row0 + uint32_t((l < nvv ? l : nvv - 1) * H)];
+  };
+
+  if (int64_t(blockIdx.x) < items) load_item(blockIdx.x);
+  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+    const int64_t c = p.c_begin + it / p.pairs;
+    const int64_t rem = p.T_fixed - c * kC;
+    const int nv = int(rem < kC ? rem : kC);
+
+    float2 av[RPG], kv[RPG], qv[RPG];
+#pragma unroll
+    for (int i = 0; i < RPG; ++i) {
+      const bool ok = rb0 + i < nv;
+      av[i] = ok ? pa[i] : make_float2(1.f, 1.f);
+      const float2 kk = cvt2<BF>(pk[i]), qq = cvt2<BF>(pq[i]);
+      kv[i] = ok ? kk : make_float2(0.f, 0.f);
+      qv[i] = ok ? qq : make_float2(0.f, 0.f);
+    }
+    const float bev = l < nv ? pb : 0.f;
+    if (it + gridDim.x < items) load_item(it + gridDim.x);
+
+    prep_chunk<DK, BF>(smem, av, kv, qv, bev);
+
+    load_v(it);
+    char* slot = p.ws + it * int64_t(SL::BYTES);
+    const float* sGM = reinterpret_cast<const float*>(smem + L::OFF_GM);
+    const float* sDL = reinterpret_cast<const float*>(smem + L::OFF_DL);
+    const float* sGN = reinterpret_cast<const float*>(smem + L::OFF_GN);
+
+    // F1: Qg = Ql Diag(gamma_m), Kg = Diag(delta) Kr^T, P, gamma_n.
+    export_frags<BF, DK, kC, NW, false, true>(slot + SL::OFF_Q, smem + L::OFF_QL, L::P_OP, nullptr, sGM);
+    export_frags<BF, kC, DK, NW, true, false>(slot + SL::OFF_K, smem + L::OFF_KRT, L::P_T, sDL, nullptr);
+    export_frags<BF, kC, kC, NW, false, false>(slot + SL::OFF_P, smem + L::OFF_P, L::P_T, nullptr, nullptr);
+    reinterpret_cast<float*>(slot + SL::OFF_G)[t % DK] = sGN[t % DK];
+    lds_barrier();
+
+    // F2: (Kl Diag(gamma_m))^T into the Kr^T space, V^T into the A/P space.
+    char* const sKgT = smem + L::OFF_KRT;
+    char* const sVT = smem + L::OFF_X;
+    {
+      float x0[RPG], x1[RPG];
+      const float g0 = sGM[ch0], g1 = sGM[ch0 + 1];
+#pragma unroll
+      for (int i = 0; i < RPG; ++i) {
+        const char* s = smem + L::OFF_KL + (rb0 + i) * L::P_OP;
+        if constexpr (BF) {
+          const char* e = s + (ch0 >> 3) * 32 + (ch0 & 7) * 2;
+          const uint32_t hw = *reinterpret_cast<const uint32_t*>(e);
+          const uint32_t lw = *reinterpret_cast<const uint32_t*>(e + 16);
+          x0[i] = (bf_lo16(hw) + bf_lo16(lw)) * g0;
+          x1[i] = (bf_hi16(hw) + bf_hi16(lw)) * g1;
+        } else {
+          const float2 e = *reinterpret_cast<const float2*>(s + 4 * ch0);
+          x0[i] = e.x * g0;
+          x1[i] = e.y * g1;
+        }
+      }
+      st8<BF>(sKgT, L::P_T, ch0, rb0, x0);
+      st8<BF>(sKgT, L::P_T, ch0 + 1, rb0, x1);
+      float2 vv[RV];
+#pragma unroll
+      for (int i = 0; i < RV; ++i) {
+        const float2 x = cvt2<BF>(pv[i]);
+        vv[i] = vr0 + i < nv ? x : make_float2(0.f, 0.f);
+      }
+#pragma unroll
+      for (int j = 0; j < RV / 4; ++j) {
+        const float y0[4] = {vv[4 * j].x, vv[4 * j + 1].x, vv[4 * j + 2].x, vv[4 * j + 3].x};
+        const float y1[4] = {vv[4 * j].y, vv[4 * j + 1].y, vv[4 * j + 2].y, vv[4 * j + 3].y};
+        st4<BF>(sVT, L::P_T, vc0, vr0 + 4 * j, y0);
+        st4<BF>(sVT, L::P_T, vc0 + 1, vr0 + 4 * j, y1);
+      }
+    }
+    lds_barrier();
+
+    // F3: W = T (Kl Diag(gamma_m)) into a staging array (the Ql space);
+    // Uv = T V straight to the slot.  Wave w: row block w % 4 of T.
+    char* const sW = smem + L::OFF_QL;
+    {
+      const int rb = w & 3;
+      typename M::Frag ta[KCC];
+#pragma unroll
+      for (int kc = 0; kc < KCC; ++kc) ta[kc] = M::load(smem + L::OFF_T, L::P_T, 16 * rb, kc);
+      constexpr int NBW = (DK / 16) * 4 / NW;   // column blocks of W per wave
+      constexpr int NBU = (DV / 16) * 4 / NW;   // column blocks of Uv per wave
+#pragma unroll
+      for (int i = 0; i < NBW; ++i) {
+        const int nb = NBW * (w >> 2) + i;
+        f4 acc = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kc = 0; kc < KCC; ++kc) acc = M::mma(ta[kc], M::load(sKgT, L::P_T, 16 * nb, kc), acc);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) st1<BF>(sW, L::P_OP, 16 * rb + 4 * lg + q, 16 * nb + lr, acc[q]);
+      }
+#pragma unroll
+      for (int i = 0; i < NBU; ++i) {
+        const int nb = NBU * (w >> 2) + i;
+        f4 acc = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kc = 0; kc < KCC; ++kc) acc = M::mma(ta[kc], M::load(sVT, L::P_T, 16 * nb, kc), acc);
+        *reinterpret_cast<f4*>(slot + SL::OFF_U + (rb * (DV / 16) + nb) * 1024 + 16 * l) = acc;
+      }
+    }
+    lds_barrier();
+
+    // F4: W to the slot.
+    export_frags<BF, DK, kC, NW, false, false>(slot + SL::OFF_W, sW, L::P_OP, nullptr, nullptr);
+    lds_barrier();
+  }
+}
+
+// acc += A B^T with the A fragments already in registers and B [16][K] in LDS.
+template <bool BF, int NKC>
+__device__ __forceinline__ f4 gemm_ra(f4 acc, const typename Mma<BF>::Frag (&a)[NKC],
+                                      const char* B, int bp) {
+  using M = Mma<BF>;
+  typename M::Frag b[NKC];
+#pragma unroll
+  for (int kc = 0; kc < NKC; ++kc) b[kc] = M::load(B, bp, 0, kc);
+#pragma unroll
+  for (int kc = 0; kc < NKC; ++kc) acc = M::mma(a[kc], b[kc], acc);
+  return acc;
+}
+
+// The state pass over the chunks of a segment, operands from the slots.  One
+// workgroup per (sequence, head, value slab of 16*NSUB columns); the slab of S
+// lives in registers, wave w holding rows 16w..16w+15.
+template <int DK, int NSUB, bool BF>
+__global__ __launch_bounds__(64 * (DK / 16), 1) void kda_chain_kernel(StageParams p) {
+  using M = Mma<BF>;
+  using F = FL<BF>;
+  using Frag = typename M::Frag;
+  constexpr int NW = DK / 16;
+  constexpr int VS = 16 * NSUB;
+  constexpr int KCK = DK / M::KU;               // fragments over the key channels
+  constexpr int KCC = kC / M::KU;               // fragments over the tokens of a chunk
+  constexpr int RBK = DK / F::KU * F::UNIT;     // bytes per 16-row block, K = DK
+  constexpr int RBC = kC / F::KU * F::UNIT;     // bytes per 16-row block, K = 64
+  constexpr int SP_S = DK * 4 + 16, SP_U = kC * 4 + 16;
+  constexpr int OFF_W = 0, OFF_Q = 64 * DK * 4, OFF_K = 128 * DK * 4, OFF_P = 192 * DK * 4;
+  constexpr int OFF_U = OFF_P + 64 * 64 * 4;
+  __shared__ __attribute__((aligned(16))) char smem[VS * SP_S + VS * SP_U];
+  char* const sS = smem;               // S^T of the slab [VS][DK]
+  char* const sU = smem + VS * SP_S;   // U^T of the slab [VS][64]
+
+  const int t = threadIdx.x;
+  const int l = t & 63;
+  const int w = t >> 6;
+  const int lr = l & 15;
+  const int lg = l >> 4;
+
+  int64_t b = blockIdx.x;
+  const int64_t G = gridDim.x;
+  if ((G & 7) == 0) b = (b & 7) * (G >> 3) + (b >> 3);
+  const int slab = int(b % p.nslab);
+  const int64_t pr = b / p.nslab;
+  const int H = p.H, DV = p.DV;
+  const int h = int(pr % H);
+  const int64_t n = pr / H;
+  const int col0 = slab * VS;
+  const int rsv = H * DV;
+  const int64_t slot_bytes = OFF_U + 64 * DV * 4 + DK * 4;
+  const int off_g = OFF_U + 64 * DV * 4;
+
+  f4 S[NSUB];
+  const int64_t sbase = pr * DK * DV;
+#pragma unroll
+  for (int js = 0; js < NSUB; ++js)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      S[js][q] = p.s_in ? p.s_in[sbase + int64_t(16 * w + 4 * lg + q) * DV + col0 + 16 * js + lr]
+                        : 0.f;
+
+  // With 8 waves, waves 0-3 compute X and U for token rows 16w.. and waves
+  // 4-7 the output rows 16(w-4)..; with 4 waves every wave does both.
+  constexpr bool kSplitO = NW >= 8;
+  const bool xw = w < 4;
+  const bool owave = kSplitO ? (w >= 4) : true;
+  const int ow = w & 3;
+  constexpr int NA = kSplitO ? 1 : 2;   // row blocks of W / Qg held by a wave
+
+  // Operands of the next chunk, loaded one chunk ahead.
+  Frag na[NA][KCK], npp[KCC], nkg[KCC];
+  f4 nu[NSUB];
+  float4 ng;
+  auto load_chunk = [&](int64_t c) {
+    const char* slot = p.ws + ((c - p.c_begin) * p.pairs + pr) * slot_bytes;
+#pragma unroll
+    for (int a = 0; a < NA; ++a) {
+      const bool wside = kSplitO ? xw : (a == 0);
+      F::load(na[a], slot + (wside ? OFF_W : OFF_Q) + ow * RBK);
+    }
+    if (owave) F::load(npp, slot + OFF_P + ow * RBC);
+    F::load(nkg, slot + OFF_K + w * RBC);
+    if (xw) {
+#pragma unroll
+      for (int js = 0; js < NSUB; ++js)
+        nu[js] = *reinterpret_cast<const f4*>(slot + OFF_U + (ow * (DV / 16) + (col0 >> 4) + js) * 1024 + 16 * l);
+    }
+    ng = *reinterpret_cast<const float4*>(slot + off_g + (16 * w + 4 * lg) * 4);
+  };
+  const int64_t c_end = p.c_begin + p.nseg;
+  load_chunk(p.c_begin);
+  {
+    // The output stores that follow the prefetch in every chunk, mirrored
+    // before the first one (keeps the compiler's memory-counter waits for the
+    // prefetched operands from covering the stores as well).
+    volatile float* sink = g_sink + ((blockIdx.x & 255) << 6) + l;
+#pragma unroll
+    for (int i = 0; i < 4 * NSUB; ++i) *sink = 0.f;
+  }
+
+  for (int64_t c = p.c_begin; c < c_end; ++c) {
+    const int64_t tok0 = n * p.T_fixed + c * kC;
+    const int64_t rem = p.T_fixed - c * kC;
+    const int nv = int(rem < kC ? rem : kC);
+    Frag a[NA][KCK], pp[KCC], kg[KCC];
+    f4 u[NSUB];
+    float4 g;
+#pragma unroll
+    for (int i = 0; i < NA; ++i)
+#pragma unroll
+      for (int kc = 0; kc < KCK; ++kc) a[i][kc] = na[i][kc];
+#pragma unroll
+    for (int kc = 0; kc < KCC; ++kc) pp[kc] = npp[kc], kg[kc] = nkg[kc];
+#pragma unroll
+    for (int js = 0; js < NSUB; ++js) u[js] = nu[js];
+    g = ng;
+    if (c + 1 < c_end) load_chunk(c + 1);
+
+    // S^T of the slab to LDS.
+#pragma unroll
+    for (int js = 0; js < NSUB; ++js) {
+      const float x[4] = {S[js][0], S[js][1], S[js][2], S[js][3]};
+      st4<BF>(sS, SP_S, 16 * js + lr, 16 * w + 4 * lg, x);
+    }
+    lds_barrier();
+    // U = Uv - W S  (X side);  O = Qg S  (O side).
+    f4 acco[NSUB];
+#pragma unroll
+    for (int js = 0; js < NSUB; ++js) acco[js] = f4{0.f, 0.f, 0.f, 0.f};
+    if (xw) {
+#pragma unroll
+      for (int js = 0; js < NSUB; ++js) {
+        const f4 x = gemm_ra<BF, KCK>(f4{0.f, 0.f, 0.f, 0.f}, a[0], sS + 16 * js * SP_S, SP_S);
+        const float y[4] = {u[js][0] - x[0], u[js][1] - x[1], u[js][2] - x[2], u[js][3] - x[3]};
+        st4<BF>(sU, SP_U, 16 * js + lr, 16 * ow + 4 * lg, y);
+      }
+    }
+    if (owave) {
+#pragma unroll
+      for (int js = 0; js < NSUB; ++js)
+        acco[js] = gemm_ra<BF, KCK>(acco[js], a[NA - 1], sS + 16 * js * SP_S, SP_S);
+    }
+    lds_barrier();
+    // O += P U, stored;  S' = Diag(gamma_n) S + Kg U.
+    if (owave) {
+#pragma unroll
+      for (int js = 0; js < NSUB; ++js)
+        acco[js] = gemm_ra<BF, KCC>(acco[js], pp, sU + 16 * js * SP_U, SP_U);
+    }
+#pragma unroll
+    for (int js = 0; js < NSUB; ++js) {
+      float* ob = p.o + (tok0 * H + h) * int64_t(DV) + col0 + 16 * js;
+      float* sink = g_sink + ((blockIdx.x & 255) << 6) + l;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = 16 * ow + 4 * lg + q;
+        float* dst = owave && r < nv ? ob + uint32_t(r * rsv + lr) : sink;
+        *dst = acco[js][q];
+      }
+    }
+#pragma unroll
+    for (int js = 0; js < NSUB; ++js) {
+      const f4 y = gemm_ra<BF, KCC>(f4{0.f, 0.f, 0.f, 0.f}, kg, sU + 16 * js * SP_U, SP_U);
+      S[js][0] = g.x * S[js][0] + y[0];
+      S[js][1] = g.y * S[js][1] + y[1];
+      S[js][2] = g.z * S[js][2] + y[2];
+      S[js][3] = g.w * S[js][3] + y[3];
     }
   }
 
@@ -770,12 +1360,118 @@ int choose_nsub(int64_t pairs, int DV) {
   return 1;
 }
 
+// The staged form pays off when the chains are too few to fill the GPU
+// without value slabs, i.e. when the fused kernel would repeat steps 1-3 per
+// slab.  Fixed-length batches only.
+bool use_staged(bool varlen, int64_t pairs, int64_t nchunks) {
+  if (varlen || nchunks < 2) return false;
+  if (const char* e = getenv("KDA_PREFILL_PATH")) {
+    if (!strcmp(e, "fused")) return false;
+    if (!strcmp(e, "split")) return true;
+  }
+  return pairs < 128;
+}
+
+size_t slot_bytes(int DK, int DV) { return size_t(4) * (3 * 64 * DK + 64 * 64 + 64 * DV + DK); }
+
+// Chunks per sequence handled by one stage + chain pair of launches.
+int64_t seg_chunks(int64_t pairs, int64_t nchunks, int DK, int DV) {
+  const int64_t budget = int64_t(1) << 30;  // workspace for the slots, bytes
+  int64_t seg = budget / (pairs * int64_t(slot_bytes(DK, DV)));
+  if (const char* e = getenv("KDA_PREFILL_SEG")) {
+    const long v = atol(e);
+    if (v > 0 && v < seg) seg = v;
+  }
+  if (seg < 1) seg = 1;
+  return seg < nchunks ? seg : nchunks;
+}
+
+// Compute units of the current device (persistent stage kernel grid).
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = 256;
+    cus[dev] = v;
+  }
+  return cus[dev];
+}
+
+template <int DK, int DV, bool BF>
+void launch_staged_t(const Params& base, int64_t T, int nsub, hipStream_t st, char* ws, int64_t seg,
+                     int64_t nchunks, float* state_ws) {
+  StageParams sp;
+  sp.H = base.H;
+  sp.DV = DV;
+  sp.nslab = DV / (16 * nsub);
+  sp.T_fixed = T;
+  sp.pairs = int64_t(base.N) * base.H;
+  sp.q = base.q;
+  sp.k = base.k;
+  sp.v = base.v;
+  sp.alpha = base.alpha;
+  sp.beta = base.beta;
+  sp.o = base.o;
+  sp.ws = ws;
+  const int64_t nsegs = (nchunks + seg - 1) / seg;
+  const int64_t cus = device_cus();
+  for (int64_t si = 0; si < nsegs; ++si) {
+    sp.c_begin = si * seg;
+    sp.nseg = (si + 1) * seg <= nchunks ? seg : nchunks - si * seg;
+    sp.s_in = si == 0 ? base.s_in : state_ws;
+    sp.s_out = si == nsegs - 1 ? base.s_out : state_ws;
+    const int64_t items = sp.pairs * sp.nseg;
+    hipLaunchKernelGGL((kda_stage_kernel<DK, DV, BF>), dim3(unsigned(items < cus ? items : cus)),
+                       dim3(Lay<DK>::NT), 0, st, sp);
+    const unsigned nb = unsigned(sp.pairs * sp.nslab);
+    if (nsub == 2)
+      hipLaunchKernelGGL((kda_chain_kernel<DK, 2, BF>), dim3(nb), dim3(Lay<DK>::NT), 0, st, sp);
+    else
+      hipLaunchKernelGGL((kda_chain_kernel<DK, 1, BF>), dim3(nb), dim3(Lay<DK>::NT), 0, st, sp);
+  }
+}
+
+template <int DK, bool BF>
+void launch_staged(const Params& base, int64_t T, int nsub, hipStream_t st, char* ws, int64_t seg,
+                   int64_t nchunks, float* state_ws) {
+  if (base.DV == 128) launch_staged_t<DK, 128, BF>(base, T, nsub, st, ws, seg, nchunks, state_ws);
+  else launch_staged_t<DK, 64, BF>(base, T, nsub, st, ws, seg, nchunks, state_ws);
+}
+
+// Value columns per chain workgroup of the staged form (1 or 2 blocks of 16).
+int staged_nsub(int64_t pairs, int DV) {
+  if (const char* e = getenv("KDA_PREFILL_NSUB")) {
+    const int v = atoi(e);
+    if (v == 1 || v == 2) return v;
+  }
+  (void)pairs;
+  (void)DV;
+  return 1;
+}
+
 }  // namespace
 
-size_t prefill_workspace_bytes(int, int64_t, int, int, int) { return 0; }
+size_t prefill_workspace_bytes(int N, int64_t T_total, int H, int DK, int DV, bool varlen) {
+  const int64_t pairs = int64_t(N) * H;
+  if (pairs == 0 || varlen) return 0;
+  const int64_t T = T_total / N;
+  const int64_t nchunks = (T + kC - 1) / kC;
+  if (!use_staged(varlen, pairs, nchunks)) return 0;
+  const int64_t seg = seg_chunks(pairs, nchunks, DK, DV);
+  size_t bytes = size_t(pairs) * size_t(seg) * slot_bytes(DK, DV);
+  if (seg < nchunks) bytes += size_t(pairs) * DK * DV * 4;  // state carried between segments
+  return bytes;
+}
 
 int launch_prefill(const PrefillArgs& a, void* stream, const char** msg) {
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (a.DK != 128 && a.DK != 64) {
+    *msg = "unsupported DK";
+    return 1;
+  }
   Params p;
   p.N = a.N;
   p.T_fixed = a.T_fixed;
@@ -791,19 +1487,34 @@ int launch_prefill(const PrefillArgs& a, void* stream, const char** msg) {
   p.o = a.o;
   p.s_out = a.state_out;
   const int64_t pairs = int64_t(a.N) * a.H;
-  const int nsub = choose_nsub(pairs, a.DV);
-  p.nslab = a.DV / (16 * nsub);
-  const int64_t nblocks = pairs * p.nslab;
+  const bool varlen = a.cu_seqlens != nullptr;
+  const int64_t nchunks = varlen ? 0 : (a.T_fixed + kC - 1) / kC;
   (void)hipGetLastError();
-  if (a.DK == 128) {
-    if (a.in_bf16) launch_dk<128, true>(p, nsub, nblocks, st);
-    else launch_dk<128, false>(p, nsub, nblocks, st);
-  } else if (a.DK == 64) {
-    if (a.in_bf16) launch_dk<64, true>(p, nsub, nblocks, st);
-    else launch_dk<64, false>(p, nsub, nblocks, st);
+  if (use_staged(varlen, pairs, nchunks)) {
+    const int nsub = staged_nsub(pairs, a.DV);
+    const int64_t seg = seg_chunks(pairs, nchunks, a.DK, a.DV);
+    char* ws = static_cast<char*>(a.workspace);
+    float* state_ws = seg < nchunks
+        ? reinterpret_cast<float*>(ws + size_t(pairs) * size_t(seg) * slot_bytes(a.DK, a.DV))
+        : nullptr;
+    if (a.DK == 128) {
+      if (a.in_bf16) launch_staged<128, true>(p, a.T_fixed, nsub, st, ws, seg, nchunks, state_ws);
+      else launch_staged<128, false>(p, a.T_fixed, nsub, st, ws, seg, nchunks, state_ws);
+    } else {
+      if (a.in_bf16) launch_staged<64, true>(p, a.T_fixed, nsub, st, ws, seg, nchunks, state_ws);
+      else launch_staged<64, false>(p, a.T_fixed, nsub, st, ws, seg, nchunks, state_ws);
+    }
   } else {
-    *msg = "unsupported DK";
-    return 1;
+    const int nsub = choose_nsub(pairs, a.DV);
+    p.nslab = a.DV / (16 * nsub);
+    const int64_t nblocks = pairs * p.nslab;
+    if (a.DK == 128) {
+      if (a.in_bf16) launch_dk<128, true>(p, nsub, nblocks, st);
+      else launch_dk<128, false>(p, nsub, nblocks, st);
+    } else {
+      if (a.in_bf16) launch_dk<64, true>(p, nsub, nblocks, st);
+      else launch_dk<64, false>(p, nsub, nblocks, st);
+    }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) {

@@ -72,10 +72,19 @@ int kda_abi_version(void);
  *   o          [B,T,H,DV]  float output; must not overlap any input
  *   state_out  [B,H,DK,DV] float, or NULL; may be equal to state_in (in place)
  *   workspace  device scratch of at least kda_chunk_prefill_workspace_size()
- *              bytes (may be NULL when that size is 0)
+ *              bytes, 16-byte aligned, not overlapping any other argument;
+ *              may be NULL when that size is 0.  Its contents on entry are
+ *              ignored and on return are unspecified.  The size is nonzero
+ *              when B*H < 128 and T > 64: the per-chunk operands of the
+ *              state pass are then computed for all chunks at once and staged
+ *              here (at most about 1 GiB plus one B*H*DK*DV float state; long
+ *              sequences are processed in segments of chunks).
  * Computes exactly the token recurrence (up to rounding) by the chunk form:
  * per chunk a unit-lower-triangular solve and dense products, and a
  * sequential pass of the state over the chunks.
+ * The environment variable KDA_PREFILL_PATH=fused|split forces the one-kernel
+ * or the staged two-kernel form (both give the same result up to rounding);
+ * it must not change between the size query and the call.
  */
 size_t kda_chunk_prefill_workspace_size(int B, int T, int H, int DK, int DV, int chunk);
 kda_status_t kda_chunk_prefill(int B, int T, int H, int DK, int DV, int chunk,

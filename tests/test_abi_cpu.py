@@ -95,10 +95,38 @@ def test_prefill_empty_is_ok_without_launch(lib):
     assert prefill(lib, B=0, ptrs=p) == OK
 
 
-def test_workspace_size_queries(lib):
-    assert lib.kda_chunk_prefill_workspace_size(1, 8192, 32, 128, 128, 64) == 0
+def test_workspace_size_queries(lib, monkeypatch):
+    # staged form (few chains): one slot per (chunk, sequence, head) holding
+    # W, Qg [64 x DK], Kg [DK x 64], P [64 x 64], Uv [64 x DV] at 4 bytes per
+    # element, plus gamma_n [DK]
+    slot = lambda dk, dv=128: 4 * (3 * 64 * dk + 64 * 64 + 64 * dv + dk)  # noqa: E731
+    assert slot(128) == 147968 and slot(64, 64) == 82176
+    assert lib.kda_chunk_prefill_workspace_size(1, 8192, 32, 128, 128, 64) == 32 * 128 * slot(128)
+    assert lib.kda_chunk_prefill_workspace_size(2, 130, 3, 64, 128, 64) == 6 * 3 * slot(64)
+    # long sequences: segments of floor(2^30 / (pairs * slot)) chunks + a state
+    seg = (1 << 30) // (32 * slot(128))
+    assert lib.kda_chunk_prefill_workspace_size(1, 1 << 20, 32, 128, 128, 64) == \
+        32 * seg * slot(128) + 32 * 128 * 128 * 4
+    # one chunk, many chains, varlen, unsupported sizes: no workspace
+    assert lib.kda_chunk_prefill_workspace_size(1, 64, 32, 128, 128, 64) == 0
+    assert lib.kda_chunk_prefill_workspace_size(4, 8192, 32, 128, 128, 64) == 0
     assert lib.kda_chunk_prefill_varlen_workspace_size(64, 540000, 32, 128, 128, 64) == 0
     assert lib.kda_chunk_prefill_workspace_size(1, 64, 2, 96, 64, 64) == 0
+    monkeypatch.setenv("KDA_PREFILL_PATH", "fused")
+    assert lib.kda_chunk_prefill_workspace_size(1, 8192, 32, 128, 128, 64) == 0
+    monkeypatch.setenv("KDA_PREFILL_PATH", "split")
+    seg = (1 << 30) // (128 * slot(128))
+    assert lib.kda_chunk_prefill_workspace_size(4, 8192, 32, 128, 128, 64) == \
+        128 * seg * slot(128) + 128 * 128 * 128 * 4
+    monkeypatch.delenv("KDA_PREFILL_PATH")
+    # a call that needs a workspace is refused without one, or with one too small
+    # (B=1, T=130, H=2, d=64: 3 chunks x 2 chains)
+    need = 2 * 3 * slot(64, 64)
+    assert lib.kda_chunk_prefill_workspace_size(1, 130, 2, 64, 64, 64) == need
+    assert prefill(lib, T=130) == WS
+    assert prefill(lib, T=130, ws=P[9], wsb=need - 1) == WS
+    assert "workspace" in lib.kda_last_error_message().decode()
+    assert prefill(lib, T=130, ws=ctypes.c_void_p(P[9].value + 8), wsb=need) == ALIGN
 
 
 def test_varlen_argument_errors(lib):

@@ -14,15 +14,29 @@ from oracle import kda_decode_step, kda_recurrent, kda_recurrent_varlen, max_rel
 pytestmark = pytest.mark.gpu
 
 
-def test_prefill_bf16_b1_h32_t8192_full():
-    """B=1, H=32, T=8192, d=128, bf16 q/k/v, zero initial state: every head."""
-    B, T, H, D = 1, 8192, 32, 128
-    flush("[config] prefill B=1 H=32 T=8192 d=128 bf16 (all heads)")
-    q, k, v, a, b = I.batch_inputs(1, B, T, H, D, D, "bf16")
+_CFG1 = {}
+
+
+def _cfg1_oracle():
+    """Inputs and oracle result of the B=1, H=32, T=8192, d=128 workload
+    (computed once, shared by both prefill forms)."""
+    if not _CFG1:
+        q, k, v, a, b = I.batch_inputs(1, 1, 8192, 32, 128, 128, "bf16")
+        _CFG1["in"] = (q, k, v, a, b)
+        _CFG1["ref"] = kda_recurrent(q, k, v, a, b)
+    return _CFG1["in"], _CFG1["ref"]
+
+
+@pytest.mark.parametrize("path", ["split", "fused"])
+def test_prefill_bf16_b1_h32_t8192_full(path, monkeypatch):
+    """B=1, H=32, T=8192, d=128, bf16 q/k/v, zero initial state: every head,
+    in both prefill forms (the staged form is the default at this size)."""
+    monkeypatch.setenv("KDA_PREFILL_PATH", path)
+    flush(f"[config] prefill B=1 H=32 T=8192 d=128 bf16 (all heads) path={path}")
+    (q, k, v, a, b), (o_ref, S_ref) = _cfg1_oracle()
     bf = torch.bfloat16
     o, S = kda.chunk_prefill(dev(q, bf), dev(k, bf), dev(v, bf), dev(a), dev(b))
     torch.cuda.synchronize()
-    o_ref, S_ref = kda_recurrent(q, k, v, a, b)
     eo, es = max_rel_err(host(o), o_ref), max_rel_err(host(S), S_ref)
     flush(f"    err o={eo:.2e} S={es:.2e}")
     assert eo <= TOL["bf16"] and es <= TOL["bf16"]

@@ -89,7 +89,11 @@ def test_prefill_then_decode_equals_longer_prefill():
     assert max_rel_err(host(S), host(S_full)) <= TOL["bf16"]
 
 
-def test_varlen_equals_separate_calls_and_permutes():
+def test_varlen_equals_separate_calls_and_permutes(monkeypatch):
+    """Packed varlen == one fixed-length call per sequence, bitwise, when both
+    run the one-kernel form (the staged form computes the same products in
+    another order: equal up to rounding); permuting the sequences permutes the
+    results."""
     lengths = [300, 64, 0, 1, 129, 65]
     H, D = 2, 128
     q, k, v, a, b, cu = I.packed_inputs(802, lengths, H, D, D, "bf16")
@@ -104,12 +108,20 @@ def test_varlen_equals_separate_calls_and_permutes():
         if L == 0:
             np.testing.assert_array_equal(Sn[n], S0[n])  # passes the state through
             continue
-        o1, S1 = kda.chunk_prefill(t(q[None, s:e], bf), t(k[None, s:e], bf), t(v[None, s:e], bf),
-                                   t(a[None, s:e]), t(b[None, s:e]), t(S0[n:n + 1]))
+        args = (t(q[None, s:e], bf), t(k[None, s:e], bf), t(v[None, s:e], bf),
+                t(a[None, s:e]), t(b[None, s:e]), t(S0[n:n + 1]))
+        monkeypatch.setenv("KDA_PREFILL_PATH", "fused")
+        o1, S1 = kda.chunk_prefill(*args)
         torch.cuda.synchronize()
         # the same kernels on the same data: identical results
         np.testing.assert_array_equal(host(o1)[0], on[s:e])
         np.testing.assert_array_equal(host(S1)[0], Sn[n])
+        monkeypatch.setenv("KDA_PREFILL_PATH", "split")
+        o2, S2 = kda.chunk_prefill(*args)
+        torch.cuda.synchronize()
+        assert max_rel_err(host(o2)[0], on[s:e]) <= 1e-4
+        assert max_rel_err(host(S2)[0], Sn[n]) <= 1e-4
+        monkeypatch.delenv("KDA_PREFILL_PATH")
     perm = [4, 0, 5, 2, 1, 3]
     pl = [lengths[i] for i in perm]
     pcu = np.concatenate([[0], np.cumsum(pl)]).astype(np.int32)
@@ -123,7 +135,9 @@ def test_varlen_equals_separate_calls_and_permutes():
     assert max_rel_err(on, o_ref) <= TOL["bf16"] and max_rel_err(Sn, S_ref) <= TOL["bf16"]
 
 
-def test_deterministic_bitwise():
+@pytest.mark.parametrize("path", ["fused", "split"])
+def test_deterministic_bitwise(path, monkeypatch):
+    monkeypatch.setenv("KDA_PREFILL_PATH", path)
     q, k, v, a, b = I.batch_inputs(803, 1, 1000, 8, 128, 128, "bf16")
     args = (dev(q, bf), dev(k, bf), dev(v, bf), dev(a), dev(b))
     o1, S1 = kda.chunk_prefill(*args)
@@ -140,7 +154,9 @@ def test_deterministic_bitwise():
     assert torch.equal(x1, x2) and torch.equal(st1, st2)
 
 
-def test_nan_stays_in_its_own_sequence_and_head():
+@pytest.mark.parametrize("path", ["fused", "split"])
+def test_nan_stays_in_its_own_sequence_and_head(path, monkeypatch):
+    monkeypatch.setenv("KDA_PREFILL_PATH", path)
     B, T, H, D = 3, 150, 4, 128
     q, k, v, a, b = I.batch_inputs(804, B, T, H, D, D, "bf16")
     v = v.copy()
