@@ -109,6 +109,8 @@ def main():
     pq, pk, pv, pa, pb = to(q, bf), to(k, bf), to(v, bf), to(a), to(b)
     po = torch.empty((B, T, H, D), device=dev, dtype=torch.float32)
     pst = torch.empty((B, H, D, D), device=dev, dtype=torch.float32)
+    wsz = kda.lib().kda_chunk_prefill_workspace_size(B, T, H, D, D, 64)
+    pws = torch.empty(max(wsz, 1), device=dev, dtype=torch.uint8)
 
     # ---- decode workload ----
     dq, dk_, dv_, da, db = I.decode_inputs(2, ND, H, D, D, "bf16")
@@ -137,7 +139,7 @@ def main():
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        kda.chunk_prefill(pq, pk, pv, pa, pb, None, True, 64, po, pst)
+        kda.chunk_prefill(pq, pk, pv, pa, pb, None, True, 64, po, pst, pws)
         if ev is not None:
             ev[1].record()
         kda.decode_step(dq, dk_, dv_, da, db, dstate, do)
@@ -181,10 +183,16 @@ def main():
                 return hashlib.sha256(f.read()).hexdigest()[:16]
 
         if tj.get("prefill_kernel_source_sha256_16") == sha16("kda_prefill.hip"):
-            traffic = tj.get("prefill_bytes_per_launch")
+            traffic = tj.get("prefill_bytes_per_call")
         if tj.get("decode_kernel_source_sha256_16") == sha16("kda_decode.hip"):
             traffic_dec = tj.get("decode_bytes_per_launch")
 
+    # Which prefill form the library takes for this shape (the same rule as in
+    # the library: the staged two-kernel form below 128 (sequence, head) pairs).
+    forced = os.environ.get("KDA_PREFILL_PATH")
+    staged = forced == "split" or (forced != "fused" and B * H < 128 and T > 64)
+    pre_kernels = ("kda_stage_kernel + kda_chain_kernel (staged form: 2 launches per call)"
+                   if staged else "kda_prefill_kernel")
     out = {
         "metric": "KDA prefill tokens/s + decode us/step (B=256); % of MFMA / HBM peak",
         "value": T / (pre_ms * 1e-3),
@@ -206,9 +214,10 @@ def main():
         },
         "prefill_us": pre_ms * 1e3,
         "decode_us_per_step": dec_ms * 1e3,
+        "prefill_form": "staged" if staged else "fused",
         "roofline": {
             "bound": "hbm",
-            "kernel": "kda_prefill_kernel",
+            "kernel": pre_kernels,
             "achieved": pre_gbs,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

@@ -284,7 +284,8 @@ __device__ float g_sink[256 * 64];
 
 // One wave's tiles of the intra-chunk Gram matrices, A = Kl Kr^T (type 0)
 // and P = Ql Kr^T (type 1): up to three (type, R, I) tiles (type < 0:
-// unused).  Row and column blocks shared by the tiles are loaded once per K
+// unused), each computed transposed (Kr rows as the first operand) so that a
+// lane ends up with four consecutive columns of one row.  Row and column blocks shared by the tiles are loaded once per K
 // chunk (this step is bound by LDS read bandwidth, not by the MFMA rate).
 template <bool BF, int DK, int T0, int R0, int I0, int T1, int R1, int I1, int T2, int R2, int I2>
 __device__ __forceinline__ void gram_tiles(const char* sKl, const char* sQl, const char* sKr,
@@ -295,17 +296,17 @@ __device__ __forceinline__ void gram_tiles(const char* sKl, const char* sQl, con
   for (int kc = 0; kc < DK / M::KU; ++kc) {
     const auto c0 = M::load(sKr, P, 16 * I0, kc);
     const auto r0 = M::load(T0 == 0 ? sKl : sQl, P, 16 * R0, kc);
-    acc[0] = M::mma(r0, c0, acc[0]);
+    acc[0] = M::mma(c0, r0, acc[0]);
     if constexpr (T1 >= 0) {
       const auto c1 = (I1 == I0) ? c0 : M::load(sKr, P, 16 * I1, kc);
       const auto r1 = (T1 == T0 && R1 == R0) ? r0 : M::load(T1 == 0 ? sKl : sQl, P, 16 * R1, kc);
-      acc[1] = M::mma(r1, c1, acc[1]);
+      acc[1] = M::mma(c1, r1, acc[1]);
       if constexpr (T2 >= 0) {
         const auto c2 = (I2 == I0) ? c0 : ((I2 == I1) ? c1 : M::load(sKr, P, 16 * I2, kc));
         const auto r2 = (T2 == T0 && R2 == R0)
                             ? r0
                             : ((T2 == T1 && R2 == R1) ? r1 : M::load(T2 == 0 ? sKl : sQl, P, 16 * R2, kc));
-        acc[2] = M::mma(r2, c2, acc[2]);
+        acc[2] = M::mma(c2, r2, acc[2]);
       }
     }
   }
@@ -477,75 +478,109 @@ tT[g][2] = a2; tR[g][2] = b2; tI[g][2] = c2_;
     }
 #undef KDA_TILES
     lds_barrier();  // every read of Kr is done: A and P overwrite it
+    // Tile (R, I) transposed: lane (lr, lg) holds row 16R + lr, columns
+    // 16I + 4lg .. +3.
 #pragma unroll
     for (int g = 0; g < 2; ++g)
 #pragma unroll
       for (int j = 0; j < 3; ++j) {
         if (tT[g][j] >= 0) {
+          const int r = 16 * tR[g][j] + lr;
+          const int i0 = 16 * tI[g][j] + 4 * lg;
+          float x[4];
+          if (tT[g][j] == 1) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int r = 16 * tR[g][j] + 4 * lg + q;
-            const int i = 16 * tI[g][j] + lr;
-            if (tT[g][j] == 1) st1<BF>(sP, L::P_T, r, i, i <= r ? acc[g][j][q] : 0.f);
-            else sA[r * L::P_AF + i] = i < r ? sBe[r] * acc[g][j][q] : 0.f;
+            for (int q = 0; q < 4; ++q) x[q] = i0 + q <= r ? acc[g][j][q] : 0.f;
+            st4<BF>(sP, L::P_T, r, i0, x);
+          } else {
+            const float be = sBe[r];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) x[q] = i0 + q < r ? be * acc[g][j][q] : 0.f;
+            *reinterpret_cast<float4*>(sA + r * L::P_AF + i0) = make_float4(x[0], x[1], x[2], x[3]);
           }
         }
       }
     // Upper tiles of P are zero (the P U product runs over the whole chunk).
     if (w >= NW - 2) {
+      const float z[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int e = 0; e < 3; ++e) {
         const int blk = (w - (NW - 2)) * 3 + e;  // (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
         const int R = blk < 3 ? 0 : (blk < 5 ? 1 : 2);
         const int I = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) st1<BF>(sP, L::P_T, 16 * R + 4 * lg + q, 16 * I + lr, 0.f);
+        st4<BF>(sP, L::P_T, 16 * R + lr, 16 * I + 4 * lg, z);
       }
     }
   }
   lds_barrier();
 
   // ---- step 3: T = (I + A)^-1 Diag(beta) ---------------------------------
-  // 3a: inverses D_R of the four 16x16 unit-lower diagonal blocks by forward
-  // substitution (wave 0, lane = (block, column)); the other waves clear the
-  // upper blocks of L^-1.
-  if (w == 0) {
-    const int R = lg, j = lr;
-    const float* Ab = sA + 16 * R * L::P_AF + 16 * R;
-    // Rows are loaded two rows ahead of the substitution, so each row's LDS
-    // latency overlaps the previous rows' arithmetic.
-    float4 ar[16][4];
+  // 3a: inverses D_R = (I + N)^-1 of the four 16x16 unit-lower diagonal
+  // blocks (N = A_RR strictly lower, so N^16 = 0):
+  //     (I + N)^-1 = (I - N)(I + N^2)(I + N^4)(I + N^8),
+  // wave R < 4 for block R, fp32 MFMA, the powers of N in place of A_RR (not
+  // needed later) and the partial products in the diagonal block of L^-1.
+  // Waves 4.. (or all waves after their block) clear the upper blocks of L^-1.
+  if (w < 4) {
+    const int R = w;
+    float* const Nb = sA + 16 * R * L::P_AF + 16 * R;   // N, then N^2, N^4, N^8
+    float* const Xb = sLi + 16 * R * L::P_AF + 16 * R;  // partial products
+    // fp32 16x16x4 operands: A lane = (row lr, k = 4s + lg), B lane = (k = 4s +
+    // lg, column lr); result lane = (rows 4lg + q, column lr).
+    auto ldA = [&](const float* m, float (&f)[4]) {
 #pragma unroll
-    for (int r = 1; r < 3; ++r)
+      for (int s4 = 0; s4 < 4; ++s4) f[s4] = m[lr * L::P_AF + 4 * s4 + lg];
+    };
+    auto ldB = [&](const float* m, float (&f)[4]) {
 #pragma unroll
-      for (int i4 = 0; i4 < r; i4 += 4) ar[r][i4 >> 2] = *reinterpret_cast<const float4*>(Ab + r * L::P_AF + i4);
-    float x[16];
+      for (int s4 = 0; s4 < 4; ++s4) f[s4] = m[(4 * s4 + lg) * L::P_AF + lr];
+    };
+    auto stC = [&](float* m, const f4& c) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) x[r] = 0.f;
+      for (int q = 0; q < 4; ++q) m[(4 * lg + q) * L::P_AF + lr] = c[q];
+    };
+    auto mm = [&](const float (&fa)[4], const float (&fb)[4], f4 c) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      if (r + 2 < 16) {
+      for (int s4 = 0; s4 < 4; ++s4) c = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[s4], fb[s4], c, 0, 0, 0);
+      return c;
+    };
+    // LDS accesses of one wave execute in order; only the compiler must not
+    // move them across each other.
+    auto order = [] { __atomic_signal_fence(__ATOMIC_SEQ_CST); };
+    float aN[4], bN[4], aX[4], aP[4], bP[4];
+    f4 xc;  // current partial product, result layout
+    ldA(Nb, aN);
+    ldB(Nb, bN);
 #pragma unroll
-        for (int i4 = 0; i4 < r + 2; i4 += 4)
-          ar[r + 2][i4 >> 2] = *reinterpret_cast<const float4*>(Ab + (r + 2) * L::P_AF + i4);
+    for (int q = 0; q < 4; ++q) xc[q] = (4 * lg + q == lr ? 1.f : 0.f) - Nb[(4 * lg + q) * L::P_AF + lr];
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) aX[s4] = (4 * s4 + lg == lr ? 1.f : 0.f) - aN[s4];
+    f4 pc = mm(aN, bN, f4{0.f, 0.f, 0.f, 0.f});  // N^2
+#pragma unroll
+    for (int e = 0; e < 3; ++e) {
+      // pc = N^(2^(e+1)); X <- X + X pc
+      order();
+      stC(Nb, pc);
+      order();
+      ldA(Nb, aP);
+      ldB(Nb, bP);
+      xc = mm(aX, bP, xc);
+      if (e < 2) {
+        pc = mm(aP, bP, f4{0.f, 0.f, 0.f, 0.f});
+        order();
+        stC(Xb, xc);
+        order();
+        ldA(Xb, aX);
       }
-      float s = r == j ? 1.f : 0.f;
-#pragma unroll
-      for (int i4 = 0; i4 < r; i4 += 4) {
-        const float4 a4 = ar[r][i4 >> 2];
-        s -= a4.x * x[i4];
-        if (i4 + 1 < r) s -= a4.y * x[i4 + 1];
-        if (i4 + 2 < r) s -= a4.z * x[i4 + 2];
-        if (i4 + 3 < r) s -= a4.w * x[i4 + 3];
-      }
-      x[r] = s;
     }
-    float* Lb = sLi + 16 * R * L::P_AF + 16 * R;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) Lb[r * L::P_AF + j] = x[r];
-  } else {
-    // blocks (R, I) with I > R: (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
-    for (int e = t - 64; e < 6 * 256; e += NT - 64) {
+    order();
+    stC(Xb, xc);
+  }
+  constexpr int w0 = NW > 4 ? 4 : 0;
+  if (w >= w0) {
+    // blocks (R, I) with I > R: (0,1) (0,2) (0,3) (1,2) (1,3) (2,3); waves
+    // 4.. when there are 8, else every wave after its block
+    for (int e = t - 64 * w0; e < 6 * 256; e += NT - 64 * w0) {
       const int blk = e >> 8, rr = (e >> 4) & 15, cc = e & 15;
       const int R = blk < 3 ? 0 : (blk < 5 ? 1 : 2);
       const int I = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
@@ -810,7 +845,11 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_prefill_kernel(Params p
           S[js][q] = sGN[c] * S[js][q] + sDL[c] * acc[q];
         }
       }
-      lds_barrier();
+      // With 8 waves the next column block rewrites S_B^T, X^T and U^T only
+      // after barriers that every wave reaches after its reads of them here
+      // (S_B^T is last read in 4b).  With 4 waves S_B^T is read in 4d, and the
+      // next chunk's steps 1-3 overwrite everything: barrier.
+      if (js == NSUB - 1 || !kSplitO) lds_barrier();
     }
   }
 
@@ -1129,11 +1168,12 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_stage_kernel(StageParam
 #pragma unroll
       for (int i = 0; i < NBW; ++i) {
         const int nb = NBW * (w >> 2) + i;
+        // W^T tile: lane (lr, lg) holds W[16rb + lr][16nb + 4lg .. +3]
         f4 acc = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kc = 0; kc < KCC; ++kc) acc = M::mma(ta[kc], M::load(sKgT, L::P_T, 16 * nb, kc), acc);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) st1<BF>(sW, L::P_OP, 16 * rb + 4 * lg + q, 16 * nb + lr, acc[q]);
+        for (int kc = 0; kc < KCC; ++kc) acc = M::mma(M::load(sKgT, L::P_T, 16 * nb, kc), ta[kc], acc);
+        const float x[4] = {acc[0], acc[1], acc[2], acc[3]};
+        st4<BF>(sW, L::P_OP, 16 * rb + lr, 16 * nb + 4 * lg, x);
       }
 #pragma unroll
       for (int i = 0; i < NBU; ++i) {
@@ -1226,24 +1266,35 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_chain_kernel(StageParam
   Frag na[NA][KCK], npp[KCC], nkg[KCC];
   f4 nu[NSUB];
   float4 ng;
-  auto load_chunk = [&](int64_t c) {
-    const char* slot = p.ws + ((c - p.c_begin) * p.pairs + pr) * slot_bytes;
+  // The loads are issued in three parts spread over the chunk, so that the
+  // memory pipeline works while the waves compute.
+  auto slot_of = [&](int64_t c) { return p.ws + ((c - p.c_begin) * p.pairs + pr) * slot_bytes; };
+  auto load_part1 = [&](const char* slot) {
 #pragma unroll
     for (int a = 0; a < NA; ++a) {
       const bool wside = kSplitO ? xw : (a == 0);
       F::load(na[a], slot + (wside ? OFF_W : OFF_Q) + ow * RBK);
     }
-    if (owave) F::load(npp, slot + OFF_P + ow * RBC);
+  };
+  auto load_part2 = [&](const char* slot) {
     F::load(nkg, slot + OFF_K + w * RBC);
+    ng = *reinterpret_cast<const float4*>(slot + off_g + (16 * w + 4 * lg) * 4);
+  };
+  auto load_part3 = [&](const char* slot) {
+    if (owave) F::load(npp, slot + OFF_P + ow * RBC);
     if (xw) {
 #pragma unroll
       for (int js = 0; js < NSUB; ++js)
         nu[js] = *reinterpret_cast<const f4*>(slot + OFF_U + (ow * (DV / 16) + (col0 >> 4) + js) * 1024 + 16 * l);
     }
-    ng = *reinterpret_cast<const float4*>(slot + off_g + (16 * w + 4 * lg) * 4);
   };
   const int64_t c_end = p.c_begin + p.nseg;
-  load_chunk(p.c_begin);
+  {
+    const char* s0 = slot_of(p.c_begin);
+    load_part1(s0);
+    load_part2(s0);
+    load_part3(s0);
+  }
   {
     // The output stores that follow the prefetch in every chunk, mirrored
     // before the first one (keeps the compiler's memory-counter waits for the
@@ -1269,7 +1320,9 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_chain_kernel(StageParam
 #pragma unroll
     for (int js = 0; js < NSUB; ++js) u[js] = nu[js];
     g = ng;
-    if (c + 1 < c_end) load_chunk(c + 1);
+    const bool more = c + 1 < c_end;
+    const char* sn = slot_of(more ? c + 1 : c);
+    if (more) load_part1(sn);
 
     // S^T of the slab to LDS.
 #pragma unroll
@@ -1278,6 +1331,7 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_chain_kernel(StageParam
       st4<BF>(sS, SP_S, 16 * js + lr, 16 * w + 4 * lg, x);
     }
     lds_barrier();
+    if (more) load_part2(sn);
     // U = Uv - W S  (X side);  O = Qg S  (O side).
     f4 acco[NSUB];
 #pragma unroll
@@ -1296,6 +1350,7 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_chain_kernel(StageParam
         acco[js] = gemm_ra<BF, KCK>(acco[js], a[NA - 1], sS + 16 * js * SP_S, SP_S);
     }
     lds_barrier();
+    if (more) load_part3(sn);
     // O += P U, stored;  S' = Diag(gamma_n) S + Kg U.
     if (owave) {
 #pragma unroll
@@ -1355,7 +1410,9 @@ int choose_nsub(int64_t pairs, int DV) {
     const int v = atoi(e);
     if ((v == 1 || v == 2 || v == 4 || v == 8) && 16 * v <= DV) return v;
   }
-  for (int nsub = DV / 16; nsub > 1; nsub >>= 1)
+  // (at most 4 column blocks: with 8 the state slab, the prefetched values and
+  // steps 1-3 together exceed the register file)
+  for (int nsub = DV / 16 < 4 ? DV / 16 : 4; nsub > 1; nsub >>= 1)
     if (pairs * (DV / (16 * nsub)) >= 256) return nsub;
   return 1;
 }
