@@ -223,11 +223,29 @@ __device__ __forceinline__ void st4(char* base, int pitch, int row, int kk, cons
   }
 }
 
-// Eight consecutive elements starting at kk (kk % 8 == 0).
+// Eight consecutive elements starting at kk (kk % 8 == 0): one 8-group.
 template <bool BF>
 __device__ __forceinline__ void st8(char* base, int pitch, int row, int kk, const float* x) {
-  st4<BF>(base, pitch, row, kk, x);
-  st4<BF>(base, pitch, row, kk + 4, x + 4);
+  if constexpr (BF) {
+    uint16_t h[8], l[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) split(x[i], h[i], l[i]);
+    char* p = base + row * pitch + (kk >> 3) * 32;
+    uint4 hv, lv;
+    hv.x = uint32_t(h[0]) | (uint32_t(h[1]) << 16);
+    hv.y = uint32_t(h[2]) | (uint32_t(h[3]) << 16);
+    hv.z = uint32_t(h[4]) | (uint32_t(h[5]) << 16);
+    hv.w = uint32_t(h[6]) | (uint32_t(h[7]) << 16);
+    lv.x = uint32_t(l[0]) | (uint32_t(l[1]) << 16);
+    lv.y = uint32_t(l[2]) | (uint32_t(l[3]) << 16);
+    lv.z = uint32_t(l[4]) | (uint32_t(l[5]) << 16);
+    lv.w = uint32_t(l[6]) | (uint32_t(l[7]) << 16);
+    *reinterpret_cast<uint4*>(p) = hv;
+    *reinterpret_cast<uint4*>(p + 16) = lv;
+  } else {
+    st4<BF>(base, pitch, row, kk, x);
+    st4<BF>(base, pitch, row, kk + 4, x + 4);
+  }
 }
 
 // -------------------------------------------------------- global inputs -----
@@ -314,7 +332,8 @@ __device__ __forceinline__ void gram_tiles(const char* sKl, const char* sQl, con
 
 // Steps 1-3 of one chunk (everything that does not depend on the state):
 // decay factors and decayed operands, the Gram tiles A and P, and
-// T = (I + A)^-1 Diag(beta).  On return the LDS holds Kl, Ql, Kr^T, T, P and
+// T = (I + A)^-1 Diag(beta).  On return the LDS holds Kl, Ql,
+// Kg = Diag(gamma_n / gamma_m) Kr^T (in the Kr^T array), T, P and
 // gamma_m, gamma_n / gamma_m, gamma_n for the chunk.  av/kv/qv are this
 // thread's 8 rows of two channels (rows past the sequence end: alpha = 1,
 // k = q = 0), bev is beta of token (threadIdx.x & 63) (0 past the end).
@@ -406,12 +425,20 @@ __device__ __forceinline__ void prep_chunk(char* smem, const float2 (&av)[kC / 8
         Q.y *= av[i].y;
       }
     }
-    // Kr^T rows (= key channels): this thread's 8 tokens of two channels.
+    // Kg = Diag(gamma_n / gamma_m) Kr^T, rows = key channels: this thread's 8
+    // tokens of two channels.  (gamma_n / gamma_m = the product of alpha over
+    // the rows after the reference row.)
+    float2 dl = make_float2(1.f, 1.f);
+#pragma unroll
+    for (int g2 = half; g2 < RG; ++g2) {
+      dl.x *= sGP[g2 * DK + ch0];
+      dl.y *= sGP[g2 * DK + ch0 + 1];
+    }
     float x0[RPG], x1[RPG];
 #pragma unroll
     for (int e = 0; e < RPG; ++e) {
-      x0[e] = krs[e].x;
-      x1[e] = krs[e].y;
+      x0[e] = krs[e].x * dl.x;
+      x1[e] = krs[e].y * dl.y;
     }
     st8<BF>(sKrT, L::P_T, ch0, rb, x0);
     st8<BF>(sKrT, L::P_T, ch0 + 1, rb, x1);
@@ -836,13 +863,13 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_prefill_kernel(Params p
           *dst = acco[q];
         }
       }
-      // 4e: S' = Diag(gamma_n) S + Diag(gamma_n / gamma_m) Kr^T U  (rows 16w..)
+      // 4e: S' = Diag(gamma_n) S + Kg U, Kg = Diag(gamma_n / gamma_m) Kr^T  (rows 16w..)
       {
         f4 acc = gemm<BF, kC>(f4{0.f, 0.f, 0.f, 0.f}, sKrT, L::P_T, 16 * w, sUT, L::P_T, 0);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int c = 16 * w + 4 * lg + q;
-          S[js][q] = sGN[c] * S[js][q] + sDL[c] * acc[q];
+          S[js][q] = sGN[c] * S[js][q] + acc[q];
         }
       }
       // With 8 waves the next column block rewrites S_B^T, X^T and U^T only
@@ -920,13 +947,16 @@ template <bool BF> struct FL;
 template <> struct FL<true> {
   static constexpr int KU = 32;       // K per fragment
   static constexpr int UNIT = 2048;   // bytes per fragment
+  // Fragments kc < n of a row block (n wave-uniform; the rest untouched).
   template <int NKC>
-  __device__ static void load(Mma<true>::Frag (&f)[NKC], const char* rb) {
+  __device__ static void load(Mma<true>::Frag (&f)[NKC], const char* rb, int n = NKC) {
     const int l = lane_id();
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc) {
-      f[kc].hi = *reinterpret_cast<const bf8*>(rb + kc * 2048 + 16 * l);
-      f[kc].lo = *reinterpret_cast<const bf8*>(rb + kc * 2048 + 1024 + 16 * l);
+      if (kc < n) {
+        f[kc].hi = *reinterpret_cast<const bf8*>(rb + kc * 2048 + 16 * l);
+        f[kc].lo = *reinterpret_cast<const bf8*>(rb + kc * 2048 + 1024 + 16 * l);
+      }
     }
   }
 };
@@ -934,11 +964,12 @@ template <> struct FL<false> {
   static constexpr int KU = 16;       // K per 1 KiB unit (four fragments)
   static constexpr int UNIT = 1024;
   template <int NKC>
-  __device__ static void load(float (&f)[NKC], const char* rb) {
+  __device__ static void load(float (&f)[NKC], const char* rb, int n = NKC) {
     static_assert(NKC % 4 == 0, "fp32 fragments come in fours");
     const int l = lane_id();
 #pragma unroll
     for (int g = 0; g < NKC / 4; ++g) {
+      if (4 * g >= n) continue;
       const float4 x = *reinterpret_cast<const float4*>(rb + g * 1024 + 16 * l);
       f[4 * g] = x.x;
       f[4 * g + 1] = x.y;
@@ -1106,12 +1137,11 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_stage_kernel(StageParam
     load_v(it);
     char* slot = p.ws + it * int64_t(SL::BYTES);
     const float* sGM = reinterpret_cast<const float*>(smem + L::OFF_GM);
-    const float* sDL = reinterpret_cast<const float*>(smem + L::OFF_DL);
     const float* sGN = reinterpret_cast<const float*>(smem + L::OFF_GN);
 
-    // F1: Qg = Ql Diag(gamma_m), Kg = Diag(delta) Kr^T, P, gamma_n.
+    // F1: Qg = Ql Diag(gamma_m), Kg (already scaled in step 1), P, gamma_n.
     export_frags<BF, DK, kC, NW, false, true>(slot + SL::OFF_Q, smem + L::OFF_QL, L::P_OP, nullptr, sGM);
-    export_frags<BF, kC, DK, NW, true, false>(slot + SL::OFF_K, smem + L::OFF_KRT, L::P_T, sDL, nullptr);
+    export_frags<BF, kC, DK, NW, false, false>(slot + SL::OFF_K, smem + L::OFF_KRT, L::P_T, nullptr, nullptr);
     export_frags<BF, kC, kC, NW, false, false>(slot + SL::OFF_P, smem + L::OFF_P, L::P_T, nullptr, nullptr);
     reinterpret_cast<float*>(slot + SL::OFF_G)[t % DK] = sGN[t % DK];
     lds_barrier();
@@ -1156,10 +1186,14 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_stage_kernel(StageParam
     lds_barrier();
 
     // F3: W = T (Kl Diag(gamma_m)) into a staging array (the Ql space);
-    // Uv = T V straight to the slot.  Wave w: row block w % 4 of T.
+    // Uv = T V straight to the slot.  Wave w takes row block rb of T (rb = w
+    // for waves 0-3, 3 - (w - 4) for waves 4-7, so that the two waves of a
+    // SIMD together cover 3 of the 4 nonzero K blocks of the lower-triangular
+    // T) and skips the K chunks above the diagonal.
     char* const sW = smem + L::OFF_QL;
     {
-      const int rb = w & 3;
+      const int rb = w < 4 ? w : 3 - (w & 3);
+      const int kmax = 16 * rb + 16;   // K (tokens) past which T's row block is zero
       typename M::Frag ta[KCC];
 #pragma unroll
       for (int kc = 0; kc < KCC; ++kc) ta[kc] = M::load(smem + L::OFF_T, L::P_T, 16 * rb, kc);
@@ -1171,7 +1205,8 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_stage_kernel(StageParam
         // W^T tile: lane (lr, lg) holds W[16rb + lr][16nb + 4lg .. +3]
         f4 acc = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kc = 0; kc < KCC; ++kc) acc = M::mma(M::load(sKgT, L::P_T, 16 * nb, kc), ta[kc], acc);
+        for (int kc = 0; kc < KCC; ++kc)
+          if (kc * M::KU < kmax) acc = M::mma(M::load(sKgT, L::P_T, 16 * nb, kc), ta[kc], acc);
         const float x[4] = {acc[0], acc[1], acc[2], acc[3]};
         st4<BF>(sW, L::P_OP, 16 * rb + lr, 16 * nb + 4 * lg, x);
       }
@@ -1180,7 +1215,8 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_stage_kernel(StageParam
         const int nb = NBU * (w >> 2) + i;
         f4 acc = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kc = 0; kc < KCC; ++kc) acc = M::mma(ta[kc], M::load(sVT, L::P_T, 16 * nb, kc), acc);
+        for (int kc = 0; kc < KCC; ++kc)
+          if (kc * M::KU < kmax) acc = M::mma(ta[kc], M::load(sVT, L::P_T, 16 * nb, kc), acc);
         *reinterpret_cast<f4*>(slot + SL::OFF_U + (rb * (DV / 16) + nb) * 1024 + 16 * l) = acc;
       }
     }
@@ -1192,16 +1228,19 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_stage_kernel(StageParam
   }
 }
 
-// acc += A B^T with the A fragments already in registers and B [16][K] in LDS.
+// acc += A B^T with the A fragments already in registers and B [16][K] in LDS;
+// K chunks kc >= n (wave-uniform) are zero in A and skipped.
 template <bool BF, int NKC>
 __device__ __forceinline__ f4 gemm_ra(f4 acc, const typename Mma<BF>::Frag (&a)[NKC],
-                                      const char* B, int bp) {
+                                      const char* B, int bp, int n = NKC) {
   using M = Mma<BF>;
   typename M::Frag b[NKC];
 #pragma unroll
-  for (int kc = 0; kc < NKC; ++kc) b[kc] = M::load(B, bp, 0, kc);
+  for (int kc = 0; kc < NKC; ++kc)
+    if (kc < n) b[kc] = M::load(B, bp, 0, kc);
 #pragma unroll
-  for (int kc = 0; kc < NKC; ++kc) acc = M::mma(a[kc], b[kc], acc);
+  for (int kc = 0; kc < NKC; ++kc)
+    if (kc < n) acc = M::mma(a[kc], b[kc], acc);
   return acc;
 }
 
@@ -1261,6 +1300,8 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_chain_kernel(StageParam
   const bool owave = kSplitO ? (w >= 4) : true;
   const int ow = w & 3;
   constexpr int NA = kSplitO ? 1 : 2;   // row blocks of W / Qg held by a wave
+  // P is lower triangular: its row block ow is zero past token 16 ow + 15.
+  const int npk = (16 * ow + 16 + M::KU - 1) / M::KU;
 
   // Operands of the next chunk, loaded one chunk ahead.
   Frag na[NA][KCK], npp[KCC], nkg[KCC];
@@ -1281,7 +1322,7 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_chain_kernel(StageParam
     ng = *reinterpret_cast<const float4*>(slot + off_g + (16 * w + 4 * lg) * 4);
   };
   auto load_part3 = [&](const char* slot) {
-    if (owave) F::load(npp, slot + OFF_P + ow * RBC);
+    if (owave) F::load(npp, slot + OFF_P + ow * RBC, npk);
     if (xw) {
 #pragma unroll
       for (int js = 0; js < NSUB; ++js)
@@ -1355,7 +1396,7 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_chain_kernel(StageParam
     if (owave) {
 #pragma unroll
       for (int js = 0; js < NSUB; ++js)
-        acco[js] = gemm_ra<BF, KCC>(acco[js], pp, sU + 16 * js * SP_U, SP_U);
+        acco[js] = gemm_ra<BF, KCC>(acco[js], pp, sU + 16 * js * SP_U, SP_U, npk);
     }
 #pragma unroll
     for (int js = 0; js < NSUB; ++js) {
