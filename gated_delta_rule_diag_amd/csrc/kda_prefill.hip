@@ -82,14 +82,15 @@ struct Lay {
   static constexpr int OFF_UT = OFF_XT + 16 * P_T;           // U^T [16][64]
   static constexpr int OFF_T = OFF_X + SZ_X;                 // T [64][64] (fp32 L^-1 first)
   static constexpr int OFF_TMP = OFF_T + kC * P_T;           // 3 x 16x16 fp32 (solve)
-  static constexpr int RG = 8;                               // row groups of the decay prep
-  static constexpr int OFF_GP = OFF_TMP + 3 * 256 * 4;       // group products [RG][DK]
-  static constexpr int OFF_GM = OFF_GP + RG * DK * 4;        // gamma_m [DK]
+  static constexpr int RG = 16;                              // row groups (4 rows) of the decay prep
+  static constexpr int OFF_GP = OFF_T;                       // group products [RG][DK] (step 1 only)
+  static constexpr int OFF_GM = OFF_TMP + 3 * 256 * 4;       // gamma_m [DK]
   static constexpr int OFF_DL = OFF_GM + DK * 4;             // gamma_n / gamma_m [DK]
   static constexpr int OFF_GN = OFF_DL + DK * 4;             // gamma_n [DK]
   static constexpr int OFF_BE = OFF_GN + DK * 4;             // beta [64]
   static constexpr int TOTAL = OFF_BE + kC * 4;
-  static_assert(NT == RG * DK / 2, "decay prep: one thread per (channel pair, row group)");
+  static_assert(NT == RG * DK / 4, "decay prep: one thread per (channel quad, row group)");
+  static_assert(RG * DK * 4 <= kC * P_T, "group products fit the T space");
   static_assert(OFF_UT + 16 * P_T <= OFF_X + kC * P_T, "step buffers fit in A's space");
   static_assert(TOTAL <= 160 * 1024, "LDS budget");
 };
@@ -272,8 +273,8 @@ __device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x);
 
 // Raw (unconverted) input words, so that prefetched loads are not consumed
 // before they are needed: a bf16 pair / bf16 value, or fp32.
-template <bool BF> struct Raw { typedef uint32_t two; typedef uint32_t one; };
-template <> struct Raw<false> { typedef float2 two; typedef float one; };
+template <bool BF> struct Raw { typedef uint2 four; typedef uint32_t two; typedef uint32_t one; };
+template <> struct Raw<false> { typedef float4 four; typedef float2 two; typedef float one; };
 
 template <bool BF>
 __device__ __forceinline__ typename Raw<BF>::two ldraw2(const void* p, uint32_t i) {
@@ -284,6 +285,18 @@ template <bool BF>
 __device__ __forceinline__ typename Raw<BF>::one ldraw1(const void* p, uint32_t i) {
   if constexpr (BF) return uint32_t(static_cast<const uint16_t*>(p)[i]);
   else return static_cast<const float*>(p)[i];
+}
+template <bool BF>
+__device__ __forceinline__ typename Raw<BF>::four ldraw4(const void* p, uint32_t i) {
+  if constexpr (BF) return *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + i);
+  else return *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
+}
+template <bool BF>
+__device__ __forceinline__ float4 cvt4(typename Raw<BF>::four r) {
+  if constexpr (BF)
+    return make_float4(__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u),
+                       __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u));
+  else return r;
 }
 template <bool BF>
 __device__ __forceinline__ float2 cvt2(typename Raw<BF>::two r) {
@@ -299,6 +312,16 @@ __device__ __forceinline__ float cvt1(typename Raw<BF>::one r) {
 
 // Destination of output stores for rows past the end of a sequence (never read).
 __device__ float g_sink[256 * 64];
+
+// Thread -> (column quad cq, group grp of consecutive rows) of a 64-row chunk
+// with QUADS column quads: consecutive threads take consecutive quads
+// of one row group (a wave's loads read whole rows).  (A wave-blocked mapping,
+// 8 quads x 8 groups per wave, measured slower.)
+template <int QUADS>
+__device__ __forceinline__ void quad_map(int t, int& cq, int& grp) {
+  cq = t % QUADS;
+  grp = t / QUADS;
+}
 
 // One wave's tiles of the intra-chunk Gram matrices, A = Kl Kr^T (type 0)
 // and P = Ql Kr^T (type 1): up to three (type, R, I) tiles (type < 0:
@@ -335,19 +358,18 @@ __device__ __forceinline__ void gram_tiles(const char* sKl, const char* sQl, con
 // T = (I + A)^-1 Diag(beta).  On return the LDS holds Kl, Ql,
 // Kg = Diag(gamma_n / gamma_m) Kr^T (in the Kr^T array), T, P and
 // gamma_m, gamma_n / gamma_m, gamma_n for the chunk.  av/kv/qv are this
-// thread's 8 rows of two channels (rows past the sequence end: alpha = 1,
-// k = q = 0), bev is beta of token (threadIdx.x & 63) (0 past the end).
-template <int DK, bool BF>
-__device__ __forceinline__ void prep_chunk(char* smem, const float2 (&av)[kC / 8],
-                                           const float2 (&kv)[kC / 8], const float2 (&qv)[kC / 8],
-                                           float bev) {
+// thread's 4 rows (4g .. 4g+3) of 4 channels (4c .. 4c+3), c = t % (DK/4),
+// g = t / (DK/4) (rows past the sequence end: alpha = 1, k = q = 0), bev is
+// beta of token (threadIdx.x & 63) (0 past the end).
+// after_gram() runs between steps 2 and 3 (callers issue global loads there,
+// when the memory pipeline is idle).
+template <int DK, bool BF, typename Hook>
+__device__ __forceinline__ void prep_chunk(char* smem, const float4 (&av)[4], const float4 (&kv)[4],
+                                           const float4 (&qv)[4], float bev, Hook&& after_gram) {
   using L = Lay<DK>;
-  using M = Mma<BF>;
   constexpr int NW = L::NW;
   constexpr int NT = L::NT;
-  constexpr int NP = DK / 2;
-  constexpr int RG = L::RG;
-  constexpr int RPG = kC / RG;
+  constexpr int RG = L::RG;        // row groups of 4 rows
   char* const sKl = smem + L::OFF_KL;
   char* const sQl = smem + L::OFF_QL;
   char* const sKrT = smem + L::OFF_KRT;
@@ -367,100 +389,82 @@ __device__ __forceinline__ void prep_chunk(char* smem, const float2 (&av)[kC / 8
   const int w = t >> 6;
   const int lr = l & 15;
   const int lg = l >> 4;
-  const int cp = t % NP, grp = t / NP;
-  const int ch0 = 2 * cp;
-  const int rb = grp * RPG;
+  int cq, grp;
+  quad_map<DK / 4>(t, cq, grp);
+  const int c0 = 4 * cq;           // this thread's channels c0 .. c0+3
+  const int r0 = 4 * grp;          // this thread's rows r0 .. r0+3
   (void)l;
+  auto mul4 = [](float4 a, float4 b) { return make_float4(a.x * b.x, a.y * b.y, a.z * b.z, a.w * b.w); };
+  auto gp4 = [&](int g) { return *reinterpret_cast<const float4*>(sGP + g * DK + c0); };
 
   // ---- step 1: decay factors and decayed operands ------------------------
   {
-    float2 gp = make_float2(1.f, 1.f);
-#pragma unroll
-    for (int i = 0; i < RPG; ++i) {
-      gp.x *= av[i].x;
-      gp.y *= av[i].y;
-    }
-    sGP[grp * DK + ch0] = gp.x;
-    sGP[grp * DK + ch0 + 1] = gp.y;
+    float4 gp = mul4(mul4(av[0], av[1]), mul4(av[2], av[3]));
+    *reinterpret_cast<float4*>(sGP + grp * DK + c0) = gp;
     if (t < kC) sBe[t] = bev;
   }
   lds_barrier();
   {
-    float2 krs[RPG];
-    constexpr int half = RG / 2;  // groups before / after the reference row
+    float4 krs[4];
+    constexpr int half = RG / 2;  // groups 0..7 = rows 0..31, up to the reference row 31
     if (grp >= half) {
       // rows after the reference: f = prod_{m < s <= r} alpha_s <= 1
-      float2 P = make_float2(1.f, 1.f);
-      for (int g2 = half; g2 < grp; ++g2) {
-        P.x *= sGP[g2 * DK + ch0];
-        P.y *= sGP[g2 * DK + ch0 + 1];
-      }
+      float4 P = make_float4(1.f, 1.f, 1.f, 1.f);
+      for (int g2 = half; g2 < grp; ++g2) P = mul4(P, gp4(g2));
 #pragma unroll
-      for (int i = 0; i < RPG; ++i) {
-        P.x *= av[i].x;
-        P.y *= av[i].y;
-        const float ix = rcp(P.x), iy = rcp(P.y);
-        const int r = rb + i;
-        st2<BF>(sKl, L::P_OP, r, ch0, kv[i].x * P.x, kv[i].y * P.y);
-        st2<BF>(sQl, L::P_OP, r, ch0, qv[i].x * P.x, qv[i].y * P.y);
-        krs[i] = make_float2(kv[i].x * ix, kv[i].y * iy);
-        st2<BF>(sKr, L::P_OP, r, ch0, krs[i].x, krs[i].y);
+      for (int i = 0; i < 4; ++i) {
+        P = mul4(P, av[i]);
+        const float4 iv = make_float4(rcp(P.x), rcp(P.y), rcp(P.z), rcp(P.w));
+        const int r = r0 + i;
+        const float4 a = mul4(kv[i], P), b = mul4(qv[i], P);
+        krs[i] = mul4(kv[i], iv);
+        const float xa[4] = {a.x, a.y, a.z, a.w}, xb[4] = {b.x, b.y, b.z, b.w};
+        const float xc[4] = {krs[i].x, krs[i].y, krs[i].z, krs[i].w};
+        st4<BF>(sKl, L::P_OP, r, c0, xa);
+        st4<BF>(sQl, L::P_OP, r, c0, xb);
+        st4<BF>(sKr, L::P_OP, r, c0, xc);
       }
     } else {
       // rows up to the reference: 1/f = prod_{r < s <= m} alpha_s <= 1
-      float2 Q = make_float2(1.f, 1.f);
-      for (int g2 = grp + 1; g2 < half; ++g2) {
-        Q.x *= sGP[g2 * DK + ch0];
-        Q.y *= sGP[g2 * DK + ch0 + 1];
-      }
+      float4 Q = make_float4(1.f, 1.f, 1.f, 1.f);
+      for (int g2 = grp + 1; g2 < half; ++g2) Q = mul4(Q, gp4(g2));
 #pragma unroll
-      for (int i = RPG - 1; i >= 0; --i) {
-        const float fx = rcp(Q.x), fy = rcp(Q.y);
-        const int r = rb + i;
-        st2<BF>(sKl, L::P_OP, r, ch0, kv[i].x * fx, kv[i].y * fy);
-        st2<BF>(sQl, L::P_OP, r, ch0, qv[i].x * fx, qv[i].y * fy);
-        krs[i] = make_float2(kv[i].x * Q.x, kv[i].y * Q.y);
-        st2<BF>(sKr, L::P_OP, r, ch0, krs[i].x, krs[i].y);
-        Q.x *= av[i].x;
-        Q.y *= av[i].y;
+      for (int i = 3; i >= 0; --i) {
+        const float4 f = make_float4(rcp(Q.x), rcp(Q.y), rcp(Q.z), rcp(Q.w));
+        const int r = r0 + i;
+        const float4 a = mul4(kv[i], f), b = mul4(qv[i], f);
+        krs[i] = mul4(kv[i], Q);
+        const float xa[4] = {a.x, a.y, a.z, a.w}, xb[4] = {b.x, b.y, b.z, b.w};
+        const float xc[4] = {krs[i].x, krs[i].y, krs[i].z, krs[i].w};
+        st4<BF>(sKl, L::P_OP, r, c0, xa);
+        st4<BF>(sQl, L::P_OP, r, c0, xb);
+        st4<BF>(sKr, L::P_OP, r, c0, xc);
+        Q = mul4(Q, av[i]);
       }
     }
-    // Kg = Diag(gamma_n / gamma_m) Kr^T, rows = key channels: this thread's 8
-    // tokens of two channels.  (gamma_n / gamma_m = the product of alpha over
+    // Kg = Diag(gamma_n / gamma_m) Kr^T, rows = key channels: this thread's 4
+    // tokens of four channels.  (gamma_n / gamma_m = the product of alpha over
     // the rows after the reference row.)
-    float2 dl = make_float2(1.f, 1.f);
+    float4 dl = make_float4(1.f, 1.f, 1.f, 1.f);
 #pragma unroll
-    for (int g2 = half; g2 < RG; ++g2) {
-      dl.x *= sGP[g2 * DK + ch0];
-      dl.y *= sGP[g2 * DK + ch0 + 1];
+    for (int g2 = half; g2 < RG; ++g2) dl = mul4(dl, gp4(g2));
+    {
+      const float x0[4] = {krs[0].x * dl.x, krs[1].x * dl.x, krs[2].x * dl.x, krs[3].x * dl.x};
+      const float x1[4] = {krs[0].y * dl.y, krs[1].y * dl.y, krs[2].y * dl.y, krs[3].y * dl.y};
+      const float x2[4] = {krs[0].z * dl.z, krs[1].z * dl.z, krs[2].z * dl.z, krs[3].z * dl.z};
+      const float x3[4] = {krs[0].w * dl.w, krs[1].w * dl.w, krs[2].w * dl.w, krs[3].w * dl.w};
+      st4<BF>(sKrT, L::P_T, c0, r0, x0);
+      st4<BF>(sKrT, L::P_T, c0 + 1, r0, x1);
+      st4<BF>(sKrT, L::P_T, c0 + 2, r0, x2);
+      st4<BF>(sKrT, L::P_T, c0 + 3, r0, x3);
     }
-    float x0[RPG], x1[RPG];
-#pragma unroll
-    for (int e = 0; e < RPG; ++e) {
-      x0[e] = krs[e].x * dl.x;
-      x1[e] = krs[e].y * dl.y;
-    }
-    st8<BF>(sKrT, L::P_T, ch0, rb, x0);
-    st8<BF>(sKrT, L::P_T, ch0 + 1, rb, x1);
     if (grp == 0) {
-      float2 gm = make_float2(1.f, 1.f), dl = make_float2(1.f, 1.f);
+      float4 gm = make_float4(1.f, 1.f, 1.f, 1.f);
 #pragma unroll
-      for (int g2 = 0; g2 < RG; ++g2) {
-        const float a0 = sGP[g2 * DK + ch0], a1 = sGP[g2 * DK + ch0 + 1];
-        if (g2 < half) {
-          gm.x *= a0;
-          gm.y *= a1;
-        } else {
-          dl.x *= a0;
-          dl.y *= a1;
-        }
-      }
-      sGM[ch0] = gm.x;
-      sGM[ch0 + 1] = gm.y;
-      sDL[ch0] = dl.x;
-      sDL[ch0 + 1] = dl.y;
-      sGN[ch0] = gm.x * dl.x;
-      sGN[ch0 + 1] = gm.y * dl.y;
+      for (int g2 = 0; g2 < half; ++g2) gm = mul4(gm, gp4(g2));
+      *reinterpret_cast<float4*>(sGM + c0) = gm;
+      *reinterpret_cast<float4*>(sDL + c0) = dl;
+      *reinterpret_cast<float4*>(sGN + c0) = mul4(gm, dl);
     }
   }
   lds_barrier();
@@ -540,6 +544,7 @@ tT[g][2] = a2; tR[g][2] = b2; tI[g][2] = c2_;
     }
   }
   lds_barrier();
+  after_gram();
 
   // ---- step 3: T = (I + A)^-1 Diag(beta) ---------------------------------
   // 3a: inverses D_R = (I + N)^-1 of the four 16x16 unit-lower diagonal
@@ -663,32 +668,20 @@ tT[g][2] = a2; tR[g][2] = b2; tI[g][2] = c2_;
 template <int DK, int NSUB, bool BF>
 __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_prefill_kernel(Params p) {
   using L = Lay<DK>;
-  using M = Mma<BF>;
   constexpr int NW = L::NW;         // waves; wave w owns rows 16w..16w+15 of the state
-  constexpr int NT = L::NT;
-  constexpr int NP = DK / 2;        // channel pairs in the decay prep
-  constexpr int RG = L::RG;         // row groups in the decay prep
-  constexpr int RPG = kC / RG;      // rows per group (8)
   constexpr int VS = 16 * NSUB;     // value columns of this workgroup
 
   __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
   char* const sKl = smem + L::OFF_KL;
   char* const sQl = smem + L::OFF_QL;
   char* const sKrT = smem + L::OFF_KRT;
-  char* const sKr = smem + L::OFF_X;
-  float* const sA = reinterpret_cast<float*>(smem + L::OFF_A);
   char* const sP = smem + L::OFF_P;
   char* const sSBT = smem + L::OFF_SBT;
   char* const sXT = smem + L::OFF_XT;
   char* const sUT = smem + L::OFF_UT;
   char* const sT = smem + L::OFF_T;
-  float* const sLi = reinterpret_cast<float*>(smem + L::OFF_T);
-  float* const sTmp = reinterpret_cast<float*>(smem + L::OFF_TMP);
-  float* const sGP = reinterpret_cast<float*>(smem + L::OFF_GP);
   float* const sGM = reinterpret_cast<float*>(smem + L::OFF_GM);
-  float* const sDL = reinterpret_cast<float*>(smem + L::OFF_DL);
   float* const sGN = reinterpret_cast<float*>(smem + L::OFF_GN);
-  float* const sBe = reinterpret_cast<float*>(smem + L::OFF_BE);
 
   const int t = threadIdx.x;
   const int l = t & 63;
@@ -728,34 +721,34 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_prefill_kernel(Params p
       S[js][q] = p.s_in ? p.s_in[sbase + int64_t(16 * w + 4 * lg + q) * DV + col0 + 16 * js + lr]
                         : 0.f;
 
-  // Decay prep: thread = (channel pair, group of 8 rows).
-  const int cp = t % NP, grp = t / NP;
-  const int ch0 = 2 * cp;
-  const int rb = grp * RPG;
+  // Decay prep: thread = (channel quad, group of 4 rows).
+  int cq, grp;
+  quad_map<DK / 4>(t, cq, grp);
+  const int c0 = 4 * cq, r0 = 4 * grp;
 
   // Raw inputs of the next chunk, loaded one chunk ahead.  Every load is
   // unconditional: rows past the sequence end are clamped to its last row
   // and their values discarded.
-  typename Raw<BF>::two pk[RPG], pq[RPG];
-  float2 pa[RPG];
+  typename Raw<BF>::four pk[4], pq[4];
+  float4 pa[4];
   float pb = 0.f;
   typename Raw<BF>::one pv[NSUB][4];
   const int rsk = H * DK, rsv = H * DV;  // token strides (elements)
   constexpr int ESZ = BF ? 2 : 4;        // bytes per q/k/v element
-  auto load_chunk = [&](int64_t c0, int nvv) {
+  auto load_chunk = [&](int64_t tk0, int nvv) {
     // Wave-uniform base pointers for the chunk and 32-bit per-lane offsets
     // (scalar-base addressing: one vector add per load).
-    const int64_t row0 = c0 * H + h;
+    const int64_t row0 = tk0 * H + h;
     const float* ab = p.alpha + row0 * DK;
     const char* kb = static_cast<const char*>(p.k) + row0 * DK * ESZ;
     const char* qb = static_cast<const char*>(p.q) + row0 * DK * ESZ;
 #pragma unroll
-    for (int i = 0; i < RPG; ++i) {
-      const int r = rb + i < nvv ? rb + i : nvv - 1;
-      const uint32_t off = uint32_t(r * rsk + ch0);
-      pa[i] = *reinterpret_cast<const float2*>(ab + off);
-      pk[i] = ldraw2<BF>(kb, off);
-      pq[i] = ldraw2<BF>(qb, off);
+    for (int i = 0; i < 4; ++i) {
+      const int r = r0 + i < nvv ? r0 + i : nvv - 1;
+      const uint32_t off = uint32_t(r * rsk + c0);
+      pa[i] = *reinterpret_cast<const float4*>(ab + off);
+      pk[i] = ldraw4<BF>(kb, off);
+      pq[i] = ldraw4<BF>(qb, off);
     }
     pb = p.beta[row0 + uint32_t(((t & 63) < nvv ? (t & 63) : nvv - 1) * H)];
     {
@@ -763,8 +756,8 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_prefill_kernel(Params p
       const char* vb = static_cast<const char*>(p.v) + (row0 * DV + col0) * ESZ;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int r0 = 16 * (w & 3) + 4 * lg + q;
-        const int r = r0 < nvv ? r0 : nvv - 1;
+        const int rv = 16 * (w & 3) + 4 * lg + q;
+        const int r = rv < nvv ? rv : nvv - 1;
 #pragma unroll
         for (int js = 0; js < NSUB; ++js) pv[js][q] = ldraw1<BF>(vb, uint32_t(r * rsv + 16 * js + lr));
       }
@@ -785,14 +778,14 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_prefill_kernel(Params p
     const int nv = int(s1 - tok0 < kC ? s1 - tok0 : kC);
 
     // ---- take this chunk's inputs, start loading the next chunk's --------
-    float2 av[RPG], kv[RPG], qv[RPG];
+    float4 av[4], kv[4], qv[4];
 #pragma unroll
-    for (int i = 0; i < RPG; ++i) {
-      const bool ok = rb + i < nv;
-      av[i] = ok ? pa[i] : make_float2(1.f, 1.f);
-      const float2 kk = cvt2<BF>(pk[i]), qq = cvt2<BF>(pq[i]);
-      kv[i] = ok ? kk : make_float2(0.f, 0.f);
-      qv[i] = ok ? qq : make_float2(0.f, 0.f);
+    for (int i = 0; i < 4; ++i) {
+      const bool ok = r0 + i < nv;
+      av[i] = ok ? pa[i] : make_float4(1.f, 1.f, 1.f, 1.f);
+      const float4 kk = cvt4<BF>(pk[i]), qq = cvt4<BF>(pq[i]);
+      kv[i] = ok ? kk : make_float4(0.f, 0.f, 0.f, 0.f);
+      qv[i] = ok ? qq : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     const float bev = (t & 63) < nv ? pb : 0.f;
     float vreg[NSUB][4];
@@ -803,7 +796,7 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_prefill_kernel(Params p
         vreg[js][q] = (16 * (w & 3) + 4 * lg + q) < nv ? cvt1<BF>(pv[js][q]) : 0.f;
     if (tok0 + kC < s1) load_chunk(tok0 + kC, int(s1 - tok0 - kC < kC ? s1 - tok0 - kC : kC));
 
-    prep_chunk<DK, BF>(smem, av, kv, qv, bev);
+    prep_chunk<DK, BF>(smem, av, kv, qv, bev, [] {});
 
     // ---- step 4: the state pass, 16 value columns at a time ----------------
     // Waves 0..3 compute X and U for rows 16w..; the output rows 16*ow.. are
@@ -817,11 +810,11 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_prefill_kernel(Params p
     for (int js = 0; js < NSUB; ++js) {
       // 4a: S_B^T = (Diag(gamma_m) S)^T for these columns.
       {
-        const int c0 = 16 * w + 4 * lg;
+        const int kr = 16 * w + 4 * lg;
         float x[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) x[q] = S[js][q] * sGM[c0 + q];
-        st4<BF>(sSBT, L::P_OP, lr, c0, x);
+        for (int q = 0; q < 4; ++q) x[q] = S[js][q] * sGM[kr + q];
+        st4<BF>(sSBT, L::P_OP, lr, kr, x);
       }
       lds_barrier();
       // 4b: X = V - Kl S_B; the output waves start O = Ql S_B.
@@ -1047,13 +1040,11 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_stage_kernel(StageParam
   using M = Mma<BF>;
   constexpr int NW = L::NW;
   constexpr int NT = L::NT;
-  constexpr int NP = DK / 2;                 // channel pairs of the decay prep
-  constexpr int RPG = kC / L::RG;            // its rows per thread (8)
-  constexpr int NPV = DV / 2;                // value column pairs
-  constexpr int RV = kC * NPV / NT;          // rows per thread of V (4, 8 or 16)
+  constexpr int NQV = DV / 4;                // value column quads
+  constexpr int RV = kC * NQV / NT;          // rows per thread of V (2, 4 or 8)
   constexpr int KCC = kC / M::KU;
   constexpr int ESZ = BF ? 2 : 4;
-  static_assert(RV % 4 == 0, "V rows per thread");
+  static_assert(RV == 2 || RV == 4 || RV == 8, "V rows per thread");
   __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
   static_assert(DV * L::P_T <= L::SZ_X, "V^T fits the A/P space");
 
@@ -1064,13 +1055,15 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_stage_kernel(StageParam
   const int H = p.H;
   const int64_t items = p.nseg * p.pairs;
 
-  const int cp = t % NP, grp = t / NP;
-  const int ch0 = 2 * cp, rb0 = grp * RPG;
-  const int cpv = t % NPV, gv = t / NPV;
-  const int vc0 = 2 * cpv, vr0 = gv * RV;
+  int cq, grp;
+  quad_map<DK / 4>(t, cq, grp);
+  const int c0 = 4 * cq, r0 = 4 * grp;       // prep: channels c0.., rows r0..
+  int cqv, gv;
+  quad_map<DV / 4>(t, cqv, gv);
+  const int vc0 = 4 * cqv, vr0 = gv * RV;    // V: columns vc0.., rows vr0..
 
-  typename Raw<BF>::two pk[RPG], pq[RPG], pv[RV];
-  float2 pa[RPG];
+  typename Raw<BF>::four pk[4], pq[4], pv[RV];
+  float4 pa[4];
   float pb = 0.f;
   // V of item `it`: loaded after steps 1-3 (it is first needed by the folded
   // products; keeping it in registers through steps 1-3 would spill).
@@ -1087,7 +1080,7 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_stage_kernel(StageParam
 #pragma unroll
     for (int i = 0; i < RV; ++i) {
       const int r = vr0 + i < nvv ? vr0 + i : nvv - 1;
-      pv[i] = ldraw2<BF>(vb, uint32_t(r * rsv + vc0));
+      pv[i] = ldraw4<BF>(vb, uint32_t(r * rsv + vc0));
     }
   };
   auto load_item = [&](int64_t it) {
@@ -1104,12 +1097,12 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_stage_kernel(StageParam
     const char* qb = static_cast<const char*>(p.q) + row0 * DK * ESZ;
     const int rsk = H * DK;
 #pragma unroll
-    for (int i = 0; i < RPG; ++i) {
-      const int r = rb0 + i < nvv ? rb0 + i : nvv - 1;
-      const uint32_t off = uint32_t(r * rsk + ch0);
-      pa[i] = *reinterpret_cast<const float2*>(ab + off);
-      pk[i] = ldraw2<BF>(kb, off);
-      pq[i] = ldraw2<BF>(qb, off);
+    for (int i = 0; i < 4; ++i) {
+      const int r = r0 + i < nvv ? r0 + i : nvv - 1;
+      const uint32_t off = uint32_t(r * rsk + c0);
+      pa[i] = *reinterpret_cast<const float4*>(ab + off);
+      pk[i] = ldraw4<BF>(kb, off);
+      pq[i] = ldraw4<BF>(qb, off);
     }
     pb = p.beta[row0 + uint32_t((l < nvv ? l : nvv - 1) * H)];
   };
@@ -1120,21 +1113,25 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_stage_kernel(StageParam
     const int64_t rem = p.T_fixed - c * kC;
     const int nv = int(rem < kC ? rem : kC);
 
-    float2 av[RPG], kv[RPG], qv[RPG];
+    float4 av[4], kv[4], qv[4];
 #pragma unroll
-    for (int i = 0; i < RPG; ++i) {
-      const bool ok = rb0 + i < nv;
-      av[i] = ok ? pa[i] : make_float2(1.f, 1.f);
-      const float2 kk = cvt2<BF>(pk[i]), qq = cvt2<BF>(pq[i]);
-      kv[i] = ok ? kk : make_float2(0.f, 0.f);
-      qv[i] = ok ? qq : make_float2(0.f, 0.f);
+    for (int i = 0; i < 4; ++i) {
+      const bool ok = r0 + i < nv;
+      av[i] = ok ? pa[i] : make_float4(1.f, 1.f, 1.f, 1.f);
+      const float4 kk = cvt4<BF>(pk[i]), qq = cvt4<BF>(pq[i]);
+      kv[i] = ok ? kk : make_float4(0.f, 0.f, 0.f, 0.f);
+      qv[i] = ok ? qq : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     const float bev = l < nv ? pb : 0.f;
-    if (it + gridDim.x < items) load_item(it + gridDim.x);
 
-    prep_chunk<DK, BF>(smem, av, kv, qv, bev);
+    // The next item's raw inputs and this item's V are requested between
+    // steps 2 and 3: behind this item's computation, not behind the previous
+    // item's slot stores.
+    prep_chunk<DK, BF>(smem, av, kv, qv, bev, [&] {
+      load_v(it);
+      if (it + gridDim.x < items) load_item(it + gridDim.x);
+    });
 
-    load_v(it);
     char* slot = p.ws + it * int64_t(SL::BYTES);
     const float* sGM = reinterpret_cast<const float*>(smem + L::OFF_GM);
     const float* sGN = reinterpret_cast<const float*>(smem + L::OFF_GN);
@@ -1150,37 +1147,43 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_stage_kernel(StageParam
     char* const sKgT = smem + L::OFF_KRT;
     char* const sVT = smem + L::OFF_X;
     {
-      float x0[RPG], x1[RPG];
-      const float g0 = sGM[ch0], g1 = sGM[ch0 + 1];
+      const float4 gmv = *reinterpret_cast<const float4*>(sGM + c0);
+      float x[4][4];   // [channel c0 + c][token r0 + i]
 #pragma unroll
-      for (int i = 0; i < RPG; ++i) {
-        const char* s = smem + L::OFF_KL + (rb0 + i) * L::P_OP;
+      for (int i = 0; i < 4; ++i) {
+        const char* s = smem + L::OFF_KL + (r0 + i) * L::P_OP;
+        float4 e;
         if constexpr (BF) {
-          const char* e = s + (ch0 >> 3) * 32 + (ch0 & 7) * 2;
-          const uint32_t hw = *reinterpret_cast<const uint32_t*>(e);
-          const uint32_t lw = *reinterpret_cast<const uint32_t*>(e + 16);
-          x0[i] = (bf_lo16(hw) + bf_lo16(lw)) * g0;
-          x1[i] = (bf_hi16(hw) + bf_hi16(lw)) * g1;
+          const char* g = s + (c0 >> 3) * 32 + (c0 & 7) * 2;
+          const uint2 hw = *reinterpret_cast<const uint2*>(g);
+          const uint2 lw = *reinterpret_cast<const uint2*>(g + 16);
+          e = make_float4(bf_lo16(hw.x) + bf_lo16(lw.x), bf_hi16(hw.x) + bf_hi16(lw.x),
+                          bf_lo16(hw.y) + bf_lo16(lw.y), bf_hi16(hw.y) + bf_hi16(lw.y));
         } else {
-          const float2 e = *reinterpret_cast<const float2*>(s + 4 * ch0);
-          x0[i] = e.x * g0;
-          x1[i] = e.y * g1;
+          e = *reinterpret_cast<const float4*>(s + 4 * c0);
         }
+        x[0][i] = e.x * gmv.x;
+        x[1][i] = e.y * gmv.y;
+        x[2][i] = e.z * gmv.z;
+        x[3][i] = e.w * gmv.w;
       }
-      st8<BF>(sKgT, L::P_T, ch0, rb0, x0);
-      st8<BF>(sKgT, L::P_T, ch0 + 1, rb0, x1);
-      float2 vv[RV];
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) st4<BF>(sKgT, L::P_T, c0 + cc, r0, x[cc]);
+      float y[4][RV];  // [column vc0 + c][token vr0 + i]
 #pragma unroll
       for (int i = 0; i < RV; ++i) {
-        const float2 x = cvt2<BF>(pv[i]);
-        vv[i] = vr0 + i < nv ? x : make_float2(0.f, 0.f);
+        float4 v4 = cvt4<BF>(pv[i]);
+        if (vr0 + i >= nv) v4 = make_float4(0.f, 0.f, 0.f, 0.f);
+        y[0][i] = v4.x;
+        y[1][i] = v4.y;
+        y[2][i] = v4.z;
+        y[3][i] = v4.w;
       }
 #pragma unroll
-      for (int j = 0; j < RV / 4; ++j) {
-        const float y0[4] = {vv[4 * j].x, vv[4 * j + 1].x, vv[4 * j + 2].x, vv[4 * j + 3].x};
-        const float y1[4] = {vv[4 * j].y, vv[4 * j + 1].y, vv[4 * j + 2].y, vv[4 * j + 3].y};
-        st4<BF>(sVT, L::P_T, vc0, vr0 + 4 * j, y0);
-        st4<BF>(sVT, L::P_T, vc0 + 1, vr0 + 4 * j, y1);
+      for (int cc = 0; cc < 4; ++cc) {
+        if constexpr (RV == 2) st2<BF>(sVT, L::P_T, vc0 + cc, vr0, y[cc][0], y[cc][1]);
+        else if constexpr (RV == 4) st4<BF>(sVT, L::P_T, vc0 + cc, vr0, y[cc]);
+        else st8<BF>(sVT, L::P_T, vc0 + cc, vr0, y[cc]);
       }
     }
     lds_barrier();
