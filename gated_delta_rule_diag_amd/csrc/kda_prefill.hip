@@ -310,6 +310,93 @@ __device__ __forceinline__ float cvt1(typename Raw<BF>::one r) {
 }
 
 
+// ------------------------------------------------------ MFMA transposes -----
+// Transposing through the MFMA: with B a column selector (B[n][k] = s_n when k
+// is column n, else 0), A B^T picks out columns of A, scaled by s, in the
+// result layout, where a lane holds four consecutive rows of one column, i.e.
+// four consecutive elements of one row of the transposed array.  One 8-byte
+// LDS store per hi/lo part and lane then writes the transposed tile without
+// bank conflicts (stores of a [channel][token] array from a per-thread block
+// of channels x tokens conflict many ways).
+//   dst[16cb + lr][16rb + 4lg + q] = A[16rb + 4lg + q][16cb + lr] * s
+__device__ __forceinline__ uint32_t bf16_bits_rne(float x) {
+  return uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(x)));
+}
+
+// Split bf16: `a` covers the 32 columns 32kc.. (tiles cb = 2kc, 2kc+1) of row
+// block rb; s0 / s1 are this lane's column scales for the two tiles (column
+// 16cb + lr).  With hi_only the lo parts of `a` are zero and s0 = s1 = 1.
+template <bool HI_ONLY>
+__device__ __forceinline__ void xpose32_bf(const Mma<true>::Frag& a, int rb, int kc, float s0, float s1,
+                                           char* dst, int dpitch) {
+  const int l = lane_id(), lr = l & 15, lg = l >> 4;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const float sc = h ? s1 : s0;
+    const bool mine = lg == 2 * h + (lr >> 3);
+    const int e = lr & 7;
+    const uint32_t sh = bf16_bits_rne(sc);
+    const uint32_t sl = HI_ONLY ? 0u : bf16_bits_rne(sc - __uint_as_float(sh << 16));
+    uint32_t wh[4], wl[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool here = mine && (e >> 1) == j;
+      wh[j] = here ? ((e & 1) ? (sh << 16) : sh) : 0u;
+      wl[j] = here ? ((e & 1) ? (sl << 16) : sl) : 0u;
+    }
+    Mma<true>::Frag b;
+    b.hi = __builtin_bit_cast(bf8, make_uint4(wh[0], wh[1], wh[2], wh[3]));
+    b.lo = __builtin_bit_cast(bf8, make_uint4(wl[0], wl[1], wl[2], wl[3]));
+    f4 acc = f4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (HI_ONLY) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.hi, acc, 0, 0, 0);
+    else acc = Mma<true>::mma(a, b, acc);
+    const float x[4] = {acc[0], acc[1], acc[2], acc[3]};
+    st4<true>(dst, dpitch, 32 * kc + 16 * h + lr, 16 * rb + 4 * lg, x);
+  }
+}
+
+// fp32: a4[j] is this lane's element of row 16rb + lr, column 16cb + 4lg + j;
+// s is this lane's column scale (column 16cb + lr).
+__device__ __forceinline__ void xpose16_f32(const float (&a4)[4], int rb, int cb, float s, char* dst,
+                                            int dpitch) {
+  const int l = lane_id(), lr = l & 15, lg = l >> 4;
+  f4 acc = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[j], 4 * lg + j == lr ? s : 0.f, acc, 0, 0, 0);
+  const float x[4] = {acc[0], acc[1], acc[2], acc[3]};
+  st4<false>(dst, dpitch, 16 * cb + lr, 16 * rb + 4 * lg, x);
+}
+
+// Transposes the columns of a [64][DK] LDS operand array (rows = tokens) into
+// a [DK][64] array, scaled per column by scale[] (LDS): the work is spread
+// over the NW waves.
+template <bool BF, int DK, int NW>
+__device__ __forceinline__ void xpose_lds(const char* src, int spitch, const float* scale, char* dst,
+                                          int dpitch) {
+  const int l = lane_id(), lr = l & 15, lg = l >> 4, w = threadIdx.x >> 6;
+  if constexpr (BF) {
+    constexpr int NU = 4 * (DK / 32);   // (row block, 32-column chunk) units
+    static_assert(NU % NW == 0, "equal share per wave");
+#pragma unroll
+    for (int i = 0; i < NU / NW; ++i) {
+      const int u = w + NW * i, rb = u & 3, kc = u >> 2;
+      const Mma<true>::Frag a = Mma<true>::load(src, spitch, 16 * rb, kc);
+      xpose32_bf<false>(a, rb, kc, scale[32 * kc + lr], scale[32 * kc + 16 + lr], dst, dpitch);
+    }
+  } else {
+    constexpr int NU = 4 * (DK / 16);   // (row block, 16-column block) units
+    static_assert(NU % NW == 0, "equal share per wave");
+#pragma unroll
+    for (int i = 0; i < NU / NW; ++i) {
+      const int u = w + NW * i, rb = u & 3, cb = u >> 2;
+      const float4 v = *reinterpret_cast<const float4*>(src + (16 * rb + lr) * spitch + 4 * (16 * cb + 4 * lg));
+      const float a4[4] = {v.x, v.y, v.z, v.w};
+      xpose16_f32(a4, rb, cb, scale[16 * cb + lr], dst, dpitch);
+    }
+  }
+}
+
 // Destination of output stores for rows past the end of a sequence (never read).
 __device__ float g_sink[256 * 64];
 
@@ -442,26 +529,14 @@ __device__ __forceinline__ void prep_chunk(char* smem, const float4 (&av)[4], co
         Q = mul4(Q, av[i]);
       }
     }
-    // Kg = Diag(gamma_n / gamma_m) Kr^T, rows = key channels: this thread's 4
-    // tokens of four channels.  (gamma_n / gamma_m = the product of alpha over
-    // the rows after the reference row.)
-    float4 dl = make_float4(1.f, 1.f, 1.f, 1.f);
-#pragma unroll
-    for (int g2 = half; g2 < RG; ++g2) dl = mul4(dl, gp4(g2));
-    {
-      const float x0[4] = {krs[0].x * dl.x, krs[1].x * dl.x, krs[2].x * dl.x, krs[3].x * dl.x};
-      const float x1[4] = {krs[0].y * dl.y, krs[1].y * dl.y, krs[2].y * dl.y, krs[3].y * dl.y};
-      const float x2[4] = {krs[0].z * dl.z, krs[1].z * dl.z, krs[2].z * dl.z, krs[3].z * dl.z};
-      const float x3[4] = {krs[0].w * dl.w, krs[1].w * dl.w, krs[2].w * dl.w, krs[3].w * dl.w};
-      st4<BF>(sKrT, L::P_T, c0, r0, x0);
-      st4<BF>(sKrT, L::P_T, c0 + 1, r0, x1);
-      st4<BF>(sKrT, L::P_T, c0 + 2, r0, x2);
-      st4<BF>(sKrT, L::P_T, c0 + 3, r0, x3);
-    }
     if (grp == 0) {
-      float4 gm = make_float4(1.f, 1.f, 1.f, 1.f);
+      // gamma_m = product of alpha up to the reference row, gamma_n / gamma_m =
+      // over the rows after it
+      float4 gm = make_float4(1.f, 1.f, 1.f, 1.f), dl = make_float4(1.f, 1.f, 1.f, 1.f);
 #pragma unroll
       for (int g2 = 0; g2 < half; ++g2) gm = mul4(gm, gp4(g2));
+#pragma unroll
+      for (int g2 = half; g2 < RG; ++g2) dl = mul4(dl, gp4(g2));
       *reinterpret_cast<float4*>(sGM + c0) = gm;
       *reinterpret_cast<float4*>(sDL + c0) = dl;
       *reinterpret_cast<float4*>(sGN + c0) = mul4(gm, dl);
@@ -508,6 +583,8 @@ tT[g][2] = a2; tR[g][2] = b2; tI[g][2] = c2_;
       }
     }
 #undef KDA_TILES
+    // Kg = Diag(gamma_n / gamma_m) Kr^T, rows = key channels (from the Kr rows)
+    xpose_lds<BF, DK, NW>(sKr, L::P_OP, sDL, sKrT, L::P_T);
     lds_barrier();  // every read of Kr is done: A and P overwrite it
     // Tile (R, I) transposed: lane (lr, lg) holds row 16R + lr, columns
     // 16I + 4lg .. +3.
@@ -1039,12 +1116,14 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_stage_kernel(StageParam
   using SL = Slot<DK, DV>;
   using M = Mma<BF>;
   constexpr int NW = L::NW;
-  constexpr int NT = L::NT;
-  constexpr int NQV = DV / 4;                // value column quads
-  constexpr int RV = kC * NQV / NT;          // rows per thread of V (2, 4 or 8)
+  // V is loaded straight in MFMA operand layout, one unit per (16-row block,
+  // 32 (fp32: 16) columns): lane (lr, lg) holds row 16rb + lr, columns
+  // 32kc + 8lg .. +7 (fp32: 16cb + 4lg .. +3).
+  constexpr int NUV = 4 * (BF ? DV / 32 : DV / 16);
+  static_assert(NUV % NW == 0, "V units per wave");
+  constexpr int UV = NUV / NW;
   constexpr int KCC = kC / M::KU;
   constexpr int ESZ = BF ? 2 : 4;
-  static_assert(RV == 2 || RV == 4 || RV == 8, "V rows per thread");
   __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
   static_assert(DV * L::P_T <= L::SZ_X, "V^T fits the A/P space");
 
@@ -1058,11 +1137,8 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_stage_kernel(StageParam
   int cq, grp;
   quad_map<DK / 4>(t, cq, grp);
   const int c0 = 4 * cq, r0 = 4 * grp;       // prep: channels c0.., rows r0..
-  int cqv, gv;
-  quad_map<DV / 4>(t, cqv, gv);
-  const int vc0 = 4 * cqv, vr0 = gv * RV;    // V: columns vc0.., rows vr0..
-
-  typename Raw<BF>::four pk[4], pq[4], pv[RV];
+  typename Raw<BF>::four pk[4], pq[4];
+  uint4 pv[UV];
   float4 pa[4];
   float pb = 0.f;
   // V of item `it`: loaded after steps 1-3 (it is first needed by the folded
@@ -1078,9 +1154,12 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_stage_kernel(StageParam
     const char* vb = static_cast<const char*>(p.v) + (tok0 * H + h) * DV * ESZ;
     const int rsv = H * DV;
 #pragma unroll
-    for (int i = 0; i < RV; ++i) {
-      const int r = vr0 + i < nvv ? vr0 + i : nvv - 1;
-      pv[i] = ldraw4<BF>(vb, uint32_t(r * rsv + vc0));
+    for (int i = 0; i < UV; ++i) {
+      const int u = w + NW * i, rb = u & 3, cu = u >> 2;
+      const int r0v = 16 * rb + lr;
+      const int r = r0v < nvv ? r0v : nvv - 1;
+      const int col = BF ? 32 * cu + 8 * lg : 16 * cu + 4 * lg;
+      pv[i] = *reinterpret_cast<const uint4*>(vb + uint32_t(r * rsv + col) * ESZ);
     }
   };
   auto load_item = [&](int64_t it) {
@@ -1146,44 +1225,20 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_stage_kernel(StageParam
     // F2: (Kl Diag(gamma_m))^T into the Kr^T space, V^T into the A/P space.
     char* const sKgT = smem + L::OFF_KRT;
     char* const sVT = smem + L::OFF_X;
-    {
-      const float4 gmv = *reinterpret_cast<const float4*>(sGM + c0);
-      float x[4][4];   // [channel c0 + c][token r0 + i]
+    xpose_lds<BF, DK, NW>(smem + L::OFF_KL, L::P_OP, sGM, sKgT, L::P_T);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const char* s = smem + L::OFF_KL + (r0 + i) * L::P_OP;
-        float4 e;
-        if constexpr (BF) {
-          const char* g = s + (c0 >> 3) * 32 + (c0 & 7) * 2;
-          const uint2 hw = *reinterpret_cast<const uint2*>(g);
-          const uint2 lw = *reinterpret_cast<const uint2*>(g + 16);
-          e = make_float4(bf_lo16(hw.x) + bf_lo16(lw.x), bf_hi16(hw.x) + bf_hi16(lw.x),
-                          bf_lo16(hw.y) + bf_lo16(lw.y), bf_hi16(hw.y) + bf_hi16(lw.y));
-        } else {
-          e = *reinterpret_cast<const float4*>(s + 4 * c0);
-        }
-        x[0][i] = e.x * gmv.x;
-        x[1][i] = e.y * gmv.y;
-        x[2][i] = e.z * gmv.z;
-        x[3][i] = e.w * gmv.w;
-      }
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc) st4<BF>(sKgT, L::P_T, c0 + cc, r0, x[cc]);
-      float y[4][RV];  // [column vc0 + c][token vr0 + i]
-#pragma unroll
-      for (int i = 0; i < RV; ++i) {
-        float4 v4 = cvt4<BF>(pv[i]);
-        if (vr0 + i >= nv) v4 = make_float4(0.f, 0.f, 0.f, 0.f);
-        y[0][i] = v4.x;
-        y[1][i] = v4.y;
-        y[2][i] = v4.z;
-        y[3][i] = v4.w;
-      }
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc) {
-        if constexpr (RV == 2) st2<BF>(sVT, L::P_T, vc0 + cc, vr0, y[cc][0], y[cc][1]);
-        else if constexpr (RV == 4) st4<BF>(sVT, L::P_T, vc0 + cc, vr0, y[cc]);
-        else st8<BF>(sVT, L::P_T, vc0 + cc, vr0, y[cc]);
+    for (int i = 0; i < UV; ++i) {
+      const int u = w + NW * i, rb = u & 3, cu = u >> 2;
+      const uint4 x = 16 * rb + lr < nv ? pv[i] : make_uint4(0u, 0u, 0u, 0u);
+      if constexpr (BF) {
+        Mma<true>::Frag a;
+        a.hi = __builtin_bit_cast(bf8, x);
+        a.lo = __builtin_bit_cast(bf8, make_uint4(0u, 0u, 0u, 0u));
+        xpose32_bf<true>(a, rb, cu, 1.f, 1.f, sVT, L::P_T);
+      } else {
+        const float a4[4] = {__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z),
+                             __uint_as_float(x.w)};
+        xpose16_f32(a4, rb, cu, 1.f, sVT, L::P_T);
       }
     }
     lds_barrier();
