@@ -9,6 +9,7 @@ the HIP path (``gated_delta_rule_diag_amd``) and imports nothing from it.
 from .kda_oracle import (  # noqa: F401
     kda_recurrent,
     kda_recurrent_varlen,
+    kda_recurrent_snapshots,
     kda_decode_step,
     kda_chunked,
     max_rel_err,

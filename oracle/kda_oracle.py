@@ -50,6 +50,7 @@ import numpy as np
 __all__ = [
     "kda_recurrent",
     "kda_recurrent_varlen",
+    "kda_recurrent_snapshots",
     "kda_decode_step",
     "kda_chunked",
     "max_rel_err",
@@ -132,6 +133,39 @@ def kda_recurrent_varlen(q, k, v, alpha, beta, cu_seqlens, S0=None):
         o[s:e] = on[0]
         Sf[n] = Sn[0]
     return o, Sf
+
+
+def kda_recurrent_snapshots(q, k, v, alpha, beta, every, S0=None, chunk=64):
+    """Token recurrence that also records the state at block boundaries, for
+    prefix caching: serving stacks keep a KDA sequence's state at block
+    boundaries so that a later request sharing the prefix resumes from it
+    ("Kimi Linearは広がりつつある：検証できるすべてのモデルが実際にKDAを実行する"
+    (orcarouter.ai), section "既に起こった採用はサービングスタックの中にあります";
+    [NEWS] section "オープンコードにより主張は検証可能になる": the state across
+    chunk boundaries is what a deployment must test).
+
+    With L = chunk * every, snapshot j (j = 0 .. T // L - 1) is by definition
+    the state after the first L * (j + 1) tokens, i.e. the final state that
+    kda_recurrent returns for that prefix; a tail shorter than L gets none.
+    The recurrence is sequential, so it runs block by block carrying S.
+    Returns (o [B,T,H,DV], S_T [B,H,DK,DV], snaps [B, T // L, H, DK, DV]).
+    """
+    q, k, v, alpha, beta = _f64(q), _f64(k), _f64(v), _f64(alpha), _f64(beta)
+    if every < 1 or chunk < 1:
+        raise ValueError("every and chunk must be >= 1")
+    B, T, H, DK = q.shape
+    DV = v.shape[-1]
+    L = chunk * every
+    snaps = np.zeros((B, T // L, H, DK, DV))
+    o = np.zeros((B, T, H, DV))
+    S = np.zeros((B, H, DK, DV)) if S0 is None else _f64(S0).copy()
+    for s in range(0, T, L):
+        e = min(s + L, T)
+        o[:, s:e], S = kda_recurrent(q[:, s:e], k[:, s:e], v[:, s:e], alpha[:, s:e],
+                                     beta[:, s:e], S)
+        if e - s == L:
+            snaps[:, s // L] = S
+    return o, S, snaps
 
 
 def kda_decode_step(q, k, v, alpha, beta, S):

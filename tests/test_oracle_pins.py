@@ -17,7 +17,8 @@ from fractions import Fraction
 import numpy as np
 import pytest
 
-from oracle import kda_chunked, kda_decode_step, kda_recurrent, kda_recurrent_varlen, max_rel_err
+from oracle import (kda_chunked, kda_decode_step, kda_recurrent, kda_recurrent_snapshots,
+                    kda_recurrent_varlen, max_rel_err)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -327,6 +328,85 @@ def test_p10_varlen_equals_separate_and_permutes():
 
 
 # -------------------------------------------------------------- domain ---
+# ------------------------------------------------------------------ P11 ---
+def test_p11_snapshots_one_hot_keys_closed_form():
+    """alpha = 1, beta = 1, one-hot keys e_c: each write replaces row c of the
+    state with the value written, so the state after any prefix is known in
+    closed form (row c = value of the last token keyed c, else the initial
+    row).  Snapshot j must be that state after exactly L (j + 1) tokens,
+    L = chunk * every; the ragged tail gets no snapshot."""
+    rng = np.random.default_rng(11)
+    B, H, DK, DV, chunk, every = 2, 2, 6, 5, 4, 2
+    L = chunk * every
+    T = 3 * L + 5
+    ch = rng.integers(0, DK, (B, T, H))
+    k = np.zeros((B, T, H, DK))
+    for b_ in range(B):
+        for t in range(T):
+            for h in range(H):
+                k[b_, t, h, ch[b_, t, h]] = 1.0
+    v = rng.standard_normal((B, T, H, DV))
+    q = rng.standard_normal((B, T, H, DK))
+    a = np.ones((B, T, H, DK))
+    bt = np.ones((B, T, H))
+    S0 = rng.standard_normal((B, H, DK, DV))
+    o, ST, snaps = kda_recurrent_snapshots(q, k, v, a, bt, every, S0, chunk=chunk)
+    assert snaps.shape == (B, 3, H, DK, DV)
+    for b_ in range(B):
+        for h in range(H):
+            S = S0[b_, h].copy()
+            for t in range(T):
+                S[ch[b_, t, h]] = v[b_, t, h]       # the replacement, written out
+                np.testing.assert_allclose(o[b_, t, h], q[b_, t, h] @ S, atol=1e-13)
+                if (t + 1) % L == 0:
+                    np.testing.assert_allclose(snaps[b_, (t + 1) // L - 1, h], S, atol=1e-13)
+            np.testing.assert_allclose(ST[b_, h], S, atol=1e-13)
+
+
+def test_p11_snapshots_beta_zero_is_decayed_initial_state():
+    """beta = 0: snapshot j = Diag(prod of alpha over the first L (j + 1)
+    tokens) S0, per sequence and head."""
+    rng = np.random.default_rng(12)
+    q, k, v, a, b, S0 = rand_inputs(rng, 2, 70, 3, 5, 4)
+    b[:] = 0.0
+    _, _, snaps = kda_recurrent_snapshots(q, k, v, a, b, 1, S0, chunk=16)
+    assert snaps.shape == (2, 4, 3, 5, 4)
+    for j in range(4):
+        decay = np.prod(a[:, : 16 * (j + 1)], axis=1)          # [B,H,DK]
+        np.testing.assert_allclose(snaps[:, j], decay[..., None] * S0, rtol=1e-13, atol=1e-15)
+
+
+def test_p11_snapshots_match_chunk_form_on_prefixes():
+    """Snapshot j equals the final state of the independent chunk form run on
+    the prefix of L (j + 1) tokens; o and the final state equal the chunk form
+    over the whole sequence; resuming the chunk form from snapshot j
+    reproduces the outputs of the remaining tokens."""
+    rng = np.random.default_rng(13)
+    q, k, v, a, b, S0 = rand_inputs(rng, 2, 200, 2, 8, 6)
+    every, chunk = 2, 16
+    L = every * chunk
+    o, ST, snaps = kda_recurrent_snapshots(q, k, v, a, b, every, S0, chunk=chunk)
+    assert snaps.shape[1] == 200 // L == 6
+    for j in range(6):
+        e = L * (j + 1)
+        _, Sp = kda_chunked(q[:, :e], k[:, :e], v[:, :e], a[:, :e], b[:, :e], S0, chunk=chunk)
+        assert max_rel_err(snaps[:, j], Sp) < 1e-12
+    o_c, S_c = kda_chunked(q, k, v, a, b, S0, chunk=chunk)
+    assert max_rel_err(o, o_c) < 1e-12 and max_rel_err(ST, S_c) < 1e-12
+    e = 3 * L
+    o_r, S_r = kda_chunked(q[:, e:], k[:, e:], v[:, e:], a[:, e:], b[:, e:], snaps[:, 2], chunk=chunk)
+    assert max_rel_err(o_r, o_c[:, e:]) < 1e-12 and max_rel_err(S_r, S_c) < 1e-12
+
+
+def test_p11_snapshot_count_and_arguments():
+    rng = np.random.default_rng(14)
+    q, k, v, a, b, _ = rand_inputs(rng, 1, 63, 1, 4, 4, s0=False)
+    assert kda_recurrent_snapshots(q, k, v, a, b, 1)[2].shape == (1, 0, 1, 4, 4)
+    assert kda_recurrent_snapshots(q, k, v, a, b, 1, chunk=21)[2].shape == (1, 3, 1, 4, 4)
+    with pytest.raises(ValueError):
+        kda_recurrent_snapshots(q, k, v, a, b, 0)
+
+
 def test_alpha_domain_is_checked():
     z = np.zeros((1, 2, 1, 2))
     with pytest.raises(ValueError):
