@@ -4,6 +4,8 @@ Hand-written HIP kernels behind a C ABI (``include/kda.h``, ``libkda.so``)
 with a thin ctypes binding:
 
     chunk_prefill(q, k, v, alpha, beta, initial_state=None) -> (o, final_state)
+    chunk_prefill_snapshots(q, k, v, alpha, beta, every, initial_state=None)
+        -> (o, final_state, snapshots)
     chunk_prefill_varlen(q, k, v, alpha, beta, cu_seqlens, initial_state=None)
     decode_step(q, k, v, alpha, beta, state) -> o        (state updated in place)
 
@@ -11,7 +13,8 @@ The binding is imported lazily so that ``gated_delta_rule_diag_amd.inputs``
 (seeded workload generation, numpy only) does not need torch.
 """
 
-__all__ = ["chunk_prefill", "chunk_prefill_varlen", "decode_step", "KDAError"]
+__all__ = ["chunk_prefill", "chunk_prefill_snapshots", "chunk_prefill_varlen", "decode_step",
+           "KDAError"]
 
 
 def __getattr__(name):

@@ -127,6 +127,19 @@ static kda_status_t run_prefill(kda::PrefillArgs& a, size_t need, void* stream) 
                 a.workspace ? a.workspace_bytes : size_t(0));
   if (a.workspace && !aligned16(a.workspace))
     return fail(KDA_ERR_ALIGN, "workspace is not 16-byte aligned");
+  if (need > 0) {
+    const size_t esz = a.in_bf16 ? 2 : 4;
+    const size_t nk = size_t(a.T_total) * a.H * a.DK, nv = size_t(a.T_total) * a.H * a.DV;
+    const size_t nb = size_t(a.T_total) * a.H, ns = size_t(a.N) * a.H * a.DK * a.DV;
+    const size_t nsnap = a.snapshots ? size_t(a.N) * size_t(a.T_fixed / (64 * a.snap_every)) * a.H *
+                                           a.DK * a.DV : 0;
+    const void* ptrs[] = {a.q, a.k, a.v, a.alpha, a.beta, a.state_in, a.o, a.state_out, a.snapshots};
+    const size_t sizes[] = {nk * esz, nk * esz, nv * esz, nk * 4, nb * 4, ns * 4, nv * 4, ns * 4,
+                            nsnap * 4};
+    for (int i = 0; i < 9; ++i)
+      if (overlaps(a.workspace, need, ptrs[i], sizes[i]))
+        return fail(KDA_ERR_SHAPE, "workspace overlaps another argument");
+  }
   if (a.N == 0 || a.H == 0) return ok();
   const char* msg = nullptr;
   if (kda::launch_prefill(a, stream, &msg) != 0)
@@ -153,6 +166,47 @@ kda_status_t kda_chunk_prefill(int B, int T, int H, int DK, int DV, int chunk,
   a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta;
   a.state_in = state_in; a.o = o; a.state_out = state_out;
   a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+  return run_prefill(a, kda::prefill_workspace_bytes(B, a.T_total, H, DK, DV, false), stream);
+}
+
+kda_status_t kda_chunk_prefill_snapshots(int B, int T, int H, int DK, int DV, int chunk,
+                                         kda_dtype_t in_dtype, const void* q, const void* k,
+                                         const void* v, const float* alpha, const float* beta,
+                                         const float* state_in, float* o, float* state_out,
+                                         int every, float* snapshots, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+  if (B < 0 || T < 0) return fail(KDA_ERR_SHAPE, "negative size (B=%d T=%d)", B, T);
+  if (every < 1) return fail(KDA_ERR_SHAPE, "every=%d: must be >= 1", every);
+  kda_status_t s = check_prefill(B, int64_t(B) * T, H, DK, DV, chunk, in_dtype, q, k, v, alpha,
+                                 beta, state_in, o, state_out);
+  if (s != KDA_OK) return s;
+  const int64_t nsnap = int64_t(T) / (int64_t(64) * every);
+  const size_t sbytes = size_t(B) * size_t(nsnap) * H * DK * DV * 4;
+  if (sbytes > 0) {
+    if (!snapshots) return fail(KDA_ERR_NULL, "snapshots must be non-NULL (%lld per sequence)",
+                                (long long)nsnap);
+    if (!aligned16(snapshots)) return fail(KDA_ERR_ALIGN, "snapshots is not 16-byte aligned");
+    const size_t esz = in_dtype == KDA_BF16 ? 2 : 4;
+    const size_t nk = size_t(B) * T * H * DK, nv = size_t(B) * T * H * DV, nb = size_t(B) * T * H;
+    const size_t ns = size_t(B) * H * DK * DV;
+    if (overlaps(snapshots, sbytes, q, nk * esz) || overlaps(snapshots, sbytes, k, nk * esz) ||
+        overlaps(snapshots, sbytes, v, nv * esz) || overlaps(snapshots, sbytes, alpha, nk * 4) ||
+        overlaps(snapshots, sbytes, beta, nb * 4) || overlaps(snapshots, sbytes, state_in, ns * 4) ||
+        overlaps(snapshots, sbytes, o, nv * 4) || overlaps(snapshots, sbytes, state_out, ns * 4))
+      return fail(KDA_ERR_SHAPE, "snapshots overlaps another argument");
+  }
+  kda::PrefillArgs a{};
+  a.N = B;
+  a.T_fixed = T;
+  a.cu_seqlens = nullptr;
+  a.T_total = int64_t(B) * T;
+  a.H = H; a.DK = DK; a.DV = DV;
+  a.in_bf16 = in_dtype == KDA_BF16;
+  a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta;
+  a.state_in = state_in; a.o = o; a.state_out = state_out;
+  a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+  a.snapshots = sbytes > 0 ? snapshots : nullptr;
+  a.snap_every = every;
   return run_prefill(a, kda::prefill_workspace_bytes(B, a.T_total, H, DK, DV, false), stream);
 }
 

@@ -26,6 +26,8 @@ struct PrefillArgs {
   float* state_out;            // may be nullptr
   void* workspace;
   size_t workspace_bytes;
+  float* snapshots;            // [N, T_fixed / (64 * snap_every), H, DK, DV] or nullptr
+  int snap_every;              // chunks between snapshots (with snapshots != nullptr)
 };
 
 struct DecodeArgs {

@@ -55,6 +55,9 @@ struct Params {
   const float* s_in;
   float* o;
   float* s_out;
+  float* snap;        // state snapshots [N][snap_per_seq][H][DK][DV] (SNAP kernels)
+  int snap_every;     // a snapshot after every snap_every-th full chunk
+  int64_t snap_per_seq;
 };
 
 // ---------------------------------------------------------------- layout ----
@@ -742,7 +745,20 @@ tT[g][2] = a2; tR[g][2] = b2; tI[g][2] = c2_;
 }
 
 // ------------------------------------------------------------------ kernel --
-template <int DK, int NSUB, bool BF>
+// Store the state slab S[js][q] (rows 16w + 4lg + q, columns col0 + 16js + lr)
+// as snapshot j of chain (n, h).
+template <int DK, int NSUB>
+__device__ __forceinline__ void store_snapshot(float* snap, int64_t per_seq, int64_t n, int h, int H,
+                                               int DV, int64_t j, int col0, const f4 (&S)[NSUB]) {
+  const int l = lane_id(), w = threadIdx.x >> 6;
+  float* dst = snap + ((n * per_seq + j) * H + h) * int64_t(DK) * DV + col0 + (l & 15);
+#pragma unroll
+  for (int js = 0; js < NSUB; ++js)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dst[uint32_t((16 * w + 4 * (l >> 4) + q) * DV + 16 * js)] = S[js][q];
+}
+
+template <int DK, int NSUB, bool BF, bool SNAP>
 __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_prefill_kernel(Params p) {
   using L = Lay<DK>;
   constexpr int NW = L::NW;         // waves; wave w owns rows 16w..16w+15 of the state
@@ -948,6 +964,12 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_prefill_kernel(Params p
       // next chunk's steps 1-3 overwrite everything: barrier.
       if (js == NSUB - 1 || !kSplitO) lds_barrier();
     }
+    if constexpr (SNAP) {
+      // State after a complete interval of snap_every full chunks.
+      const int64_t done = (tok0 - s0) / kC + 1;
+      if (nv == kC && done % p.snap_every == 0)
+        store_snapshot<DK, NSUB>(p.snap, p.snap_per_seq, n, h, H, DV, done / p.snap_every - 1, col0, S);
+    }
   }
 
   if (p.s_out) {
@@ -1011,6 +1033,9 @@ struct StageParams {
   float* o;
   float* s_out;
   char* ws;          // slot of item i = (c - c_begin) * pairs + pair
+  float* snap;       // state snapshots [N][snap_per_seq][H][DK][DV] (SNAP chain kernels)
+  int snap_every;
+  int64_t snap_per_seq;
 };
 
 template <bool BF> struct FL;
@@ -1305,7 +1330,7 @@ __device__ __forceinline__ f4 gemm_ra(f4 acc, const typename Mma<BF>::Frag (&a)[
 // The state pass over the chunks of a segment, operands from the slots.  One
 // workgroup per (sequence, head, value slab of 16*NSUB columns); the slab of S
 // lives in registers, wave w holding rows 16w..16w+15.
-template <int DK, int NSUB, bool BF>
+template <int DK, int NSUB, bool BF, bool SNAP>
 __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_chain_kernel(StageParams p) {
   using M = Mma<BF>;
   using F = FL<BF>;
@@ -1475,6 +1500,10 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_chain_kernel(StageParam
       S[js][2] = g.z * S[js][2] + y[2];
       S[js][3] = g.w * S[js][3] + y[3];
     }
+    if constexpr (SNAP) {
+      if (nv == kC && (c + 1) % p.snap_every == 0)
+        store_snapshot<DK, NSUB>(p.snap, p.snap_per_seq, n, h, H, DV, (c + 1) / p.snap_every - 1, col0, S);
+    }
   }
 
   if (p.s_out) {
@@ -1488,8 +1517,12 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_chain_kernel(StageParam
 
 template <int DK, int NSUB, bool BF>
 void launch_t(const Params& p, int64_t nblocks, hipStream_t st) {
-  hipLaunchKernelGGL((kda_prefill_kernel<DK, NSUB, BF>), dim3(unsigned(nblocks)),
-                     dim3(Lay<DK>::NT), 0, st, p);
+  if (p.snap)
+    hipLaunchKernelGGL((kda_prefill_kernel<DK, NSUB, BF, true>), dim3(unsigned(nblocks)),
+                       dim3(Lay<DK>::NT), 0, st, p);
+  else
+    hipLaunchKernelGGL((kda_prefill_kernel<DK, NSUB, BF, false>), dim3(unsigned(nblocks)),
+                       dim3(Lay<DK>::NT), 0, st, p);
 }
 
 template <int DK, bool BF>
@@ -1572,6 +1605,9 @@ void launch_staged_t(const Params& base, int64_t T, int nsub, hipStream_t st, ch
   sp.beta = base.beta;
   sp.o = base.o;
   sp.ws = ws;
+  sp.snap = base.snap;
+  sp.snap_every = base.snap_every;
+  sp.snap_per_seq = base.snap_per_seq;
   const int64_t nsegs = (nchunks + seg - 1) / seg;
   const int64_t cus = device_cus();
   for (int64_t si = 0; si < nsegs; ++si) {
@@ -1583,10 +1619,17 @@ void launch_staged_t(const Params& base, int64_t T, int nsub, hipStream_t st, ch
     hipLaunchKernelGGL((kda_stage_kernel<DK, DV, BF>), dim3(unsigned(items < cus ? items : cus)),
                        dim3(Lay<DK>::NT), 0, st, sp);
     const unsigned nb = unsigned(sp.pairs * sp.nslab);
-    if (nsub == 2)
-      hipLaunchKernelGGL((kda_chain_kernel<DK, 2, BF>), dim3(nb), dim3(Lay<DK>::NT), 0, st, sp);
-    else
-      hipLaunchKernelGGL((kda_chain_kernel<DK, 1, BF>), dim3(nb), dim3(Lay<DK>::NT), 0, st, sp);
+    if (nsub == 2) {
+      if (sp.snap)
+        hipLaunchKernelGGL((kda_chain_kernel<DK, 2, BF, true>), dim3(nb), dim3(Lay<DK>::NT), 0, st, sp);
+      else
+        hipLaunchKernelGGL((kda_chain_kernel<DK, 2, BF, false>), dim3(nb), dim3(Lay<DK>::NT), 0, st, sp);
+    } else {
+      if (sp.snap)
+        hipLaunchKernelGGL((kda_chain_kernel<DK, 1, BF, true>), dim3(nb), dim3(Lay<DK>::NT), 0, st, sp);
+      else
+        hipLaunchKernelGGL((kda_chain_kernel<DK, 1, BF, false>), dim3(nb), dim3(Lay<DK>::NT), 0, st, sp);
+    }
   }
 }
 
@@ -1642,6 +1685,9 @@ int launch_prefill(const PrefillArgs& a, void* stream, const char** msg) {
   p.s_in = a.state_in;
   p.o = a.o;
   p.s_out = a.state_out;
+  p.snap = a.snapshots;
+  p.snap_every = a.snap_every > 0 ? a.snap_every : 1;
+  p.snap_per_seq = a.snapshots ? a.T_fixed / (int64_t(kC) * p.snap_every) : 0;
   const int64_t pairs = int64_t(a.N) * a.H;
   const bool varlen = a.cu_seqlens != nullptr;
   const int64_t nchunks = varlen ? 0 : (a.T_fixed + kC - 1) / kC;

@@ -28,6 +28,7 @@ EXPORTED = (
     "kda_abi_version",
     "kda_chunk_prefill_workspace_size",
     "kda_chunk_prefill",
+    "kda_chunk_prefill_snapshots",
     "kda_chunk_prefill_varlen_workspace_size",
     "kda_chunk_prefill_varlen",
     "kda_decode_step",
@@ -55,6 +56,9 @@ def load_library(path: str = _LIB_PATH) -> ctypes.CDLL:
     lib.kda_chunk_prefill_workspace_size.argtypes = [i, i, i, i, i, i]
     lib.kda_chunk_prefill.restype = i
     lib.kda_chunk_prefill.argtypes = [i, i, i, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.kda_chunk_prefill_snapshots.restype = i
+    lib.kda_chunk_prefill_snapshots.argtypes = [i, i, i, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                i, vp, vp, sz, vp]
     lib.kda_chunk_prefill_varlen_workspace_size.restype = sz
     lib.kda_chunk_prefill_varlen_workspace_size.argtypes = [i, i, i, i, i, i]
     lib.kda_chunk_prefill_varlen.restype = i
@@ -148,6 +152,50 @@ def chunk_prefill(q, k, v, alpha, beta, initial_state=None, output_final_state=T
         _ptr(initial_state), _ptr(o), _ptr(st), _ptr(workspace),
         0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(dev)))
     return o, st
+
+
+def chunk_prefill_snapshots(q, k, v, alpha, beta, every, initial_state=None,
+                            output_final_state=True, chunk=64, out=None, final_state=None,
+                            snapshots=None, workspace=None):
+    """KDA chunked prefill that also returns the state after every ``every``-th
+    chunk of 64 tokens (prefix caching).
+
+    Arguments as for :func:`chunk_prefill`.  Returns (o, final_state, snapshots)
+    with snapshots [B, T // (64 * every), H, DK, DV] float32: entry j is the
+    state after the first 64 * every * (j + 1) tokens of each sequence.
+    """
+    B, T, H, DK = q.shape
+    DV = v.shape[-1]
+    dt = _in_dtype(q)
+    _need(q, "q", q.dtype)
+    _need(k, "k", q.dtype, (B, T, H, DK))
+    _need(v, "v", q.dtype, (B, T, H, DV))
+    _need(alpha, "alpha", torch.float32, (B, T, H, DK))
+    _need(beta, "beta", torch.float32, (B, T, H))
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, (B, H, DK, DV))
+    if every < 1:
+        raise ValueError("every must be >= 1")
+    dev = q.device
+    o = out if out is not None else torch.empty((B, T, H, DV), device=dev, dtype=torch.float32)
+    _need(o, "out", torch.float32, (B, T, H, DV))
+    st = None
+    if output_final_state:
+        st = final_state if final_state is not None else torch.empty(
+            (B, H, DK, DV), device=dev, dtype=torch.float32)
+        _need(st, "final_state", torch.float32, (B, H, DK, DV))
+    ns = T // (chunk * every)
+    snaps = snapshots if snapshots is not None else torch.empty(
+        (B, ns, H, DK, DV), device=dev, dtype=torch.float32)
+    _need(snaps, "snapshots", torch.float32, (B, ns, H, DK, DV))
+    wsz = lib().kda_chunk_prefill_workspace_size(B, T, H, DK, DV, chunk)
+    if wsz and workspace is None:
+        workspace = torch.empty(wsz, device=dev, dtype=torch.uint8)
+    _check(lib().kda_chunk_prefill_snapshots(
+        B, T, H, DK, DV, chunk, dt, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+        _ptr(initial_state), _ptr(o), _ptr(st), every, _ptr(snaps), _ptr(workspace),
+        0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(dev)))
+    return o, st, snaps
 
 
 def chunk_prefill_varlen(q, k, v, alpha, beta, cu_seqlens, initial_state=None,

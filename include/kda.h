@@ -94,6 +94,33 @@ kda_status_t kda_chunk_prefill(int B, int T, int H, int DK, int DV, int chunk,
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Chunked prefill with state snapshots at chunk boundaries (prefix caching):
+ * the same computation as kda_chunk_prefill, and in addition the state after
+ * every `every`-th chunk, i.e. after the first 64*every*(j+1) tokens of each
+ * sequence, for j = 0 .. T/(64*every) - 1 (complete intervals only):
+ *   snapshots  [B, T/(64*every), H, DK, DV] float (row = key channel), device,
+ *              16-byte aligned, not overlapping any other argument; may be NULL
+ *              only when T < 64*every (nothing to write).
+ *   every      >= 1 chunks of 64 tokens.
+ * A prefill started from snapshot j over the tokens that follow it continues
+ * the sequence exactly (up to rounding).  Workspace: as for kda_chunk_prefill
+ * (kda_chunk_prefill_workspace_size with the same arguments).
+ * Serving stacks cache prefixes of KDA sequences as states at block
+ * boundaries: "Kimi Linearは広がりつつある：検証できるすべてのモデルが実際に
+ * KDAを実行する" (orcarouter.ai), section "既に起こった採用はサービングスタッ
+ * クの中にあります" (KDA prefix caching went into the serving engine), and
+ * "Kimi Linear、独自の土俵でFull Attentionを上回る" (remio.ai), section
+ * "オープンコードにより主張は検証可能になる" (prefix caching and the state
+ * across chunk boundaries are what deployments must test).
+ */
+kda_status_t kda_chunk_prefill_snapshots(int B, int T, int H, int DK, int DV, int chunk,
+                                         kda_dtype_t in_dtype, const void* q, const void* k,
+                                         const void* v, const float* alpha, const float* beta,
+                                         const float* state_in, float* o, float* state_out,
+                                         int every, float* snapshots, void* workspace,
+                                         size_t workspace_bytes, void* stream);
+
+/*
  * Chunked prefill, packed variable length: N sequences concatenated on the
  * token axis; sequence n owns tokens [cu_seqlens[n], cu_seqlens[n+1]).
  *   cu_seqlens  int32 DEVICE array [N+1], cu_seqlens[0] == 0, non-decreasing,

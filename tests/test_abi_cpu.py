@@ -129,6 +129,38 @@ def test_workspace_size_queries(lib, monkeypatch):
     assert prefill(lib, T=130, ws=ctypes.c_void_p(P[9].value + 8), wsb=need) == ALIGN
 
 
+def test_snapshot_argument_errors(lib):
+    # B=1, T=128, H=2, d=64: two chunks x two chains, staged form (workspace
+    # 2 * 2 * 82176 bytes); snapshots [1, 2, 2, 64, 64] float = 64 KiB
+    need = lib.kda_chunk_prefill_workspace_size(1, 128, 2, 64, 64, 64)
+    assert need == 4 * 82176
+
+    def call(B=1, T=128, H=2, DK=64, every=1, snap=P[10], ws=P[9], wsb=need, ptrs=None):
+        return lib.kda_chunk_prefill_snapshots(B, T, H, DK, 64, 64, 1, *(ptrs or P[:8]), every, snap,
+                                               ws, wsb, None)
+
+    assert call(every=0) == SHAPE
+    assert call(every=-3) == SHAPE
+    assert call(DK=96) == UNSUP
+    assert call(snap=None) == NULL
+    assert "snapshots" in lib.kda_last_error_message().decode()
+    assert call(snap=ctypes.c_void_p(P[10].value + 4)) == ALIGN
+    assert call(snap=ctypes.c_void_p(P[6].value + 4096)) == SHAPE      # inside o
+    assert call(snap=ctypes.c_void_p(P[0].value - 4096)) == SHAPE      # runs into q
+    assert call(ws=ctypes.c_void_p(P[10].value + 65536 - 16)) == SHAPE  # workspace over snapshots
+    assert call(ws=None) == WS
+    # nothing to write: B = 0, or H = 0
+    assert call(B=0, snap=None) == OK
+    assert call(H=0, snap=None) == OK
+
+
+def test_workspace_must_not_overlap_arguments(lib):
+    need = lib.kda_chunk_prefill_workspace_size(1, 130, 2, 64, 64, 64)
+    assert prefill(lib, T=130, ws=ctypes.c_void_p(P[6].value + 256), wsb=need) == SHAPE
+    assert "workspace" in lib.kda_last_error_message().decode()
+    assert prefill(lib, T=130, ws=ctypes.c_void_p(P[0].value - 256), wsb=need) == SHAPE
+
+
 def test_varlen_argument_errors(lib):
     def call(N=2, Tt=100, cu=P[8], H=2, DK=128, DV=128, chunk=64, dt=1):
         return lib.kda_chunk_prefill_varlen(N, Tt, cu, H, DK, DV, chunk, dt, *P[:8], None, 0, None)

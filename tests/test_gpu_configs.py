@@ -9,7 +9,8 @@ import torch
 from gated_delta_rule_diag_amd import inputs as I
 from gated_delta_rule_diag_amd import kda
 from kda_testlib import TOL, dev, flush, host
-from oracle import kda_decode_step, kda_recurrent, kda_recurrent_varlen, max_rel_err
+from oracle import (kda_decode_step, kda_recurrent, kda_recurrent_snapshots, kda_recurrent_varlen,
+                    max_rel_err)
 
 pytestmark = pytest.mark.gpu
 
@@ -17,13 +18,18 @@ pytestmark = pytest.mark.gpu
 _CFG1 = {}
 
 
+def _cfg1_inputs():
+    """Inputs of the B=1, H=32, T=8192, d=128 bf16 workload (drawn once)."""
+    if "in" not in _CFG1:
+        _CFG1["in"] = I.batch_inputs(1, 1, 8192, 32, 128, 128, "bf16")
+    return _CFG1["in"]
+
+
 def _cfg1_oracle():
     """Inputs and oracle result of the B=1, H=32, T=8192, d=128 workload
     (computed once, shared by both prefill forms)."""
-    if not _CFG1:
-        q, k, v, a, b = I.batch_inputs(1, 1, 8192, 32, 128, 128, "bf16")
-        _CFG1["in"] = (q, k, v, a, b)
-        _CFG1["ref"] = kda_recurrent(q, k, v, a, b)
+    if "ref" not in _CFG1:
+        _CFG1["ref"] = kda_recurrent(*_cfg1_inputs())
     return _CFG1["in"], _CFG1["ref"]
 
 
@@ -40,6 +46,31 @@ def test_prefill_bf16_b1_h32_t8192_full(path, monkeypatch):
     eo, es = max_rel_err(host(o), o_ref), max_rel_err(host(S), S_ref)
     flush(f"    err o={eo:.2e} S={es:.2e}")
     assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("path", ["split", "fused"])
+def test_prefill_snapshots_b1_h32_t8192_head_subset(path, monkeypatch):
+    """The B=1, H=32, T=8192, d=128 bf16 prefill with a state snapshot every
+    16 chunks (1024 tokens): 8 snapshots per head.  Heads {0, 13, 31} are
+    checked against the oracle's snapshots; o and the final state of the
+    snapshot call equal the plain prefill's bit for bit."""
+    monkeypatch.setenv("KDA_PREFILL_PATH", path)
+    flush(f"[config] prefill+snapshots B=1 H=32 T=8192 d=128 bf16 every=16 path={path}")
+    q, k, v, a, b = _cfg1_inputs()
+    bf = torch.bfloat16
+    x = (dev(q, bf), dev(k, bf), dev(v, bf), dev(a), dev(b))
+    o, S, sn = kda.chunk_prefill_snapshots(*x, 16)
+    o1, S1 = kda.chunk_prefill(*x)
+    torch.cuda.synchronize()
+    assert tuple(sn.shape) == (1, 8, 32, 128, 128)
+    assert torch.equal(o, o1) and torch.equal(S, S1)
+    assert torch.equal(sn[:, 7], S)
+    heads = [0, 13, 31]
+    _, _, sn_ref = kda_recurrent_snapshots(q[:, :, heads], k[:, :, heads], v[:, :, heads],
+                                           a[:, :, heads], b[:, :, heads], 16)
+    errs = [max_rel_err(host(sn[:, j][:, heads]), sn_ref[:, j]) for j in range(8)]
+    flush("    snapshot errors " + " ".join(f"{e:.1e}" for e in errs))
+    assert max(errs) <= TOL["bf16"]
 
 
 def test_decode_n256_h32_full():
