@@ -52,6 +52,7 @@ __all__ = [
     "kda_recurrent_varlen",
     "kda_recurrent_snapshots",
     "kda_decode_step",
+    "kda_decode_pool",
     "kda_chunked",
     "max_rel_err",
 ]
@@ -180,6 +181,52 @@ def kda_decode_step(q, k, v, alpha, beta, S):
         _f64(alpha)[:, None], _f64(beta)[:, None], S,
     )
     return o[:, 0], Sn
+
+
+def kda_decode_pool(q, k, v, alpha, beta, pool, state_idx=None, num_tokens=None):
+    """Decode of up to L tokens per sequence with the states kept in a pool
+    (continuous batching; verification of speculative drafts).  Deployment
+    tools must support continuous batching and speculative decoding without
+    breaking KDA's state handling ([NEWS] section "Kimi Linearリリース後に注目
+    すべき点"); decode itself is the token recurrence ([EXPLAINER]).
+
+    Shapes: q, k, alpha [N,L,H,DK]; v [N,L,H,DV]; beta [N,L,H];
+    pool [P,H,DK,DV]; state_idx [N] ints or None (sequence n uses slot n);
+    num_tokens [N] ints or None (all L).  Sequence n with slot
+    s = state_idx[n] in [0, P) runs the recurrence over its first
+    len_n = min(max(num_tokens[n], 0), L) tokens starting from pool[s]; the
+    pool slot then holds the state after the last of them.  Any other slot
+    value marks a padding row.  Returns
+      o            [N,L,H,DV]      outputs; 0 for padding rows and unprocessed tokens
+      new_pool     [P,H,DK,DV]     the pool after the call (untouched slots copied)
+      token_states [N,L,H,DK,DV]   state after each processed token (NaN elsewhere)
+    Slots referenced by two sequences are an error (the order would matter).
+    """
+    q, k, v, alpha, beta = _f64(q), _f64(k), _f64(v), _f64(alpha), _f64(beta)
+    N, L, H, DK = q.shape
+    DV = v.shape[-1]
+    pool = _f64(pool)
+    P = pool.shape[0]
+    idx = np.arange(N) if state_idx is None else np.asarray(state_idx, dtype=np.int64)
+    lens = np.full(N, L) if num_tokens is None else np.clip(np.asarray(num_tokens), 0, L)
+    valid = (idx >= 0) & (idx < P)
+    if len(set(idx[valid].tolist())) != int(valid.sum()):
+        raise ValueError("a pool slot is referenced by two sequences")
+    o = np.zeros((N, L, H, DV))
+    new_pool = pool.copy()
+    states = np.full((N, L, H, DK, DV), np.nan)
+    for n in range(N):
+        if not valid[n] or lens[n] == 0:
+            continue
+        e = int(lens[n])
+        sl = slice(n, n + 1)
+        # states after every token = snapshots with an interval of one token
+        on, Sn, sn = kda_recurrent_snapshots(q[sl, :e], k[sl, :e], v[sl, :e], alpha[sl, :e],
+                                             beta[sl, :e], 1, pool[idx[n]][None], chunk=1)
+        o[n, :e] = on[0]
+        states[n, :e] = sn[0]
+        new_pool[idx[n]] = Sn[0]
+    return o, new_pool, states
 
 
 def kda_chunked(q, k, v, alpha, beta, S0=None, chunk=64):

@@ -17,8 +17,8 @@ from fractions import Fraction
 import numpy as np
 import pytest
 
-from oracle import (kda_chunked, kda_decode_step, kda_recurrent, kda_recurrent_snapshots,
-                    kda_recurrent_varlen, max_rel_err)
+from oracle import (kda_chunked, kda_decode_pool, kda_decode_step, kda_recurrent,
+                    kda_recurrent_snapshots, kda_recurrent_varlen, max_rel_err)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -405,6 +405,101 @@ def test_p11_snapshot_count_and_arguments():
     assert kda_recurrent_snapshots(q, k, v, a, b, 1, chunk=21)[2].shape == (1, 3, 1, 4, 4)
     with pytest.raises(ValueError):
         kda_recurrent_snapshots(q, k, v, a, b, 0)
+
+
+# ------------------------------------------------------------------ P12 ---
+def test_p12_pool_one_hot_keys_closed_form():
+    """alpha = 1, beta = 1, one-hot keys (each write replaces one row of the
+    state): pool slots, padding rows (negative or out-of-range slot), per-
+    sequence token counts, outputs and per-token states in closed form;
+    slots nobody references stay bit-identical."""
+    rng = np.random.default_rng(21)
+    N, L, H, DK, DV, P = 4, 3, 2, 5, 4, 6
+    idx = np.array([3, -1, 0, 9])
+    lens = np.array([3, 2, 1, 3])
+    ch = rng.integers(0, DK, (N, L, H))
+    k = np.zeros((N, L, H, DK))
+    for n in range(N):
+        for j in range(L):
+            for h in range(H):
+                k[n, j, h, ch[n, j, h]] = 1.0
+    q = rng.standard_normal((N, L, H, DK))
+    v = rng.standard_normal((N, L, H, DV))
+    a = np.ones((N, L, H, DK))
+    b = np.ones((N, L, H))
+    pool = rng.standard_normal((P, H, DK, DV))
+    o, new_pool, st = kda_decode_pool(q, k, v, a, b, pool, idx, lens)
+    expect_pool = pool.copy()
+    for n in range(N):
+        if not 0 <= idx[n] < P:
+            assert np.all(o[n] == 0) and np.all(np.isnan(st[n]))
+            continue
+        for h in range(H):
+            S = pool[idx[n], h].copy()
+            for j in range(L):
+                if j >= lens[n]:
+                    assert np.all(o[n, j, h] == 0) and np.all(np.isnan(st[n, j, h]))
+                    continue
+                S[ch[n, j, h]] = v[n, j, h]             # the replacement, written out
+                np.testing.assert_allclose(o[n, j, h], q[n, j, h] @ S, atol=1e-13)
+                np.testing.assert_allclose(st[n, j, h], S, atol=1e-13)
+            expect_pool[idx[n], h] = S
+    np.testing.assert_allclose(new_pool, expect_pool, atol=1e-13)
+    for s_ in (1, 2, 4, 5):
+        np.testing.assert_array_equal(new_pool[s_], pool[s_])
+
+
+def test_p12_pool_beta_zero_is_decay():
+    """beta = 0: after j + 1 tokens slot s holds Diag(prod alpha) pool[s] and
+    o_j reads that state."""
+    rng = np.random.default_rng(22)
+    N, L, H, DK, DV, P = 3, 4, 2, 6, 5, 3
+    q = rng.standard_normal((N, L, H, DK))
+    k = rng.standard_normal((N, L, H, DK))
+    v = rng.standard_normal((N, L, H, DV))
+    a = np.exp(-np.exp(rng.uniform(-5, -1, (N, L, H, DK))))
+    b = np.zeros((N, L, H))
+    pool = rng.standard_normal((P, H, DK, DV))
+    idx = np.array([2, 0, 1])
+    o, new_pool, st = kda_decode_pool(q, k, v, a, b, pool, idx)
+    for n in range(N):
+        for j in range(L):
+            S = np.prod(a[n, : j + 1], axis=0)[..., None] * pool[idx[n]]
+            np.testing.assert_allclose(st[n, j], S, rtol=1e-13, atol=1e-15)
+            np.testing.assert_allclose(o[n, j], np.einsum("hkv,hk->hv", S, q[n, j]), rtol=1e-12,
+                                       atol=1e-14)
+        np.testing.assert_allclose(new_pool[idx[n]], st[n, L - 1], rtol=0, atol=0)
+
+
+def test_p12_pool_matches_chunk_form_on_gathered_states():
+    """Each sequence's tokens run from its gathered slot through the
+    independent chunk form give the same outputs and final states."""
+    rng = np.random.default_rng(23)
+    N, L, H, DK, DV, P = 5, 6, 2, 8, 6, 8
+    q, k, v, a, b, _ = rand_inputs(rng, N, L, H, DK, DV, s0=False)
+    pool = rng.standard_normal((P, H, DK, DV))
+    idx = rng.permutation(P)[:N]
+    o, new_pool, _ = kda_decode_pool(q, k, v, a, b, pool, idx)
+    o_c, S_c = kda_chunked(q, k, v, a, b, pool[idx], chunk=4)
+    assert max_rel_err(o, o_c) < 1e-12 and max_rel_err(new_pool[idx], S_c) < 1e-12
+
+
+def test_p12_tokens_past_count_are_ignored_and_duplicates_rejected():
+    rng = np.random.default_rng(24)
+    N, L, H, DK, DV = 3, 5, 1, 4, 4
+    q, k, v, a, b, _ = rand_inputs(rng, N, L, H, DK, DV, s0=False)
+    pool = rng.standard_normal((N, H, DK, DV))
+    lens = np.array([2, 5, 0])
+    r1 = kda_decode_pool(q, k, v, a, b, pool, None, lens)
+    q2, v2 = q.copy(), v.copy()
+    q2[0, 2:] += 1.0
+    v2[2] -= 3.0
+    r2 = kda_decode_pool(q2, k, v2, a, b, pool, None, lens)
+    for x, y in zip(r1, r2):
+        np.testing.assert_array_equal(x, y)
+    np.testing.assert_array_equal(r1[1][2], pool[2])       # zero tokens: slot untouched
+    with pytest.raises(ValueError):
+        kda_decode_pool(q, k, v, a, b, pool, [0, 1, 0])
 
 
 def test_alpha_domain_is_checked():
