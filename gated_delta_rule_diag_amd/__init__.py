@@ -8,13 +8,15 @@ with a thin ctypes binding:
         -> (o, final_state, snapshots)
     chunk_prefill_varlen(q, k, v, alpha, beta, cu_seqlens, initial_state=None)
     decode_step(q, k, v, alpha, beta, state) -> o        (state updated in place)
+    decode_pool(q, k, v, alpha, beta, state_pool, state_idx=None, num_tokens=None)
+        -> (o, token_states)                             (L tokens per sequence, pooled states)
 
 The binding is imported lazily so that ``gated_delta_rule_diag_amd.inputs``
 (seeded workload generation, numpy only) does not need torch.
 """
 
 __all__ = ["chunk_prefill", "chunk_prefill_snapshots", "chunk_prefill_varlen", "decode_step",
-           "KDAError"]
+           "decode_pool", "KDAError"]
 
 
 def __getattr__(name):

@@ -274,4 +274,60 @@ kda_status_t kda_decode_step(int N, int H, int DK, int DV, kda_dtype_t in_dtype,
   return ok();
 }
 
+kda_status_t kda_decode_pool(int N, int L, int H, int DK, int DV, kda_dtype_t in_dtype,
+                             const void* q, const void* k, const void* v, const float* alpha,
+                             const float* beta, const int32_t* state_idx,
+                             const int32_t* num_tokens, float* state_pool, int pool_size,
+                             float* o, float* token_states, void* stream) {
+  if (N < 0 || H < 0 || pool_size < 0)
+    return fail(KDA_ERR_SHAPE, "negative size (N=%d H=%d pool_size=%d)", N, H, pool_size);
+  if (L < 1 || L > 64) return fail(KDA_ERR_UNSUPPORTED, "L=%d: 1 <= L <= 64 tokens per sequence", L);
+  if (!dims_ok(DK) || !dims_ok(DV))
+    return fail(KDA_ERR_UNSUPPORTED, "DK=%d DV=%d: only 64 and 128 are supported", DK, DV);
+  if (in_dtype != KDA_F32 && in_dtype != KDA_BF16)
+    return fail(KDA_ERR_DTYPE, "unknown in_dtype %d", (int)in_dtype);
+  if (int64_t(N) * H > (int64_t(1) << 30) || int64_t(pool_size) * H > (int64_t(1) << 30))
+    return fail(KDA_ERR_UNSUPPORTED, "too large: N*H=%lld pool_size*H=%lld", (long long)N * H,
+                (long long)pool_size * H);
+  if (!state_idx && pool_size < N)
+    return fail(KDA_ERR_SHAPE, "state_idx is NULL, so pool_size (%d) must be >= N (%d)",
+                pool_size, N);
+  if (N == 0 || H == 0) return ok();
+  if (!q || !k || !v || !alpha || !beta || !o || (!state_pool && pool_size > 0))
+    return fail(KDA_ERR_NULL, "q, k, v, alpha, beta, o and state_pool must be non-NULL");
+  const void* ptrs[] = {q, k, v, alpha, beta, state_pool, o, token_states};
+  const char* names[] = {"q", "k", "v", "alpha", "beta", "state_pool", "o", "token_states"};
+  for (int i = 0; i < 8; ++i)
+    if (ptrs[i] && !aligned16(ptrs[i])) return fail(KDA_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
+  if ((reinterpret_cast<uintptr_t>(state_idx) | reinterpret_cast<uintptr_t>(num_tokens)) & 3u)
+    return fail(KDA_ERR_ALIGN, "state_idx and num_tokens must be 4-byte aligned");
+  const size_t esz = in_dtype == KDA_BF16 ? 2 : 4;
+  const size_t rows = size_t(N) * L * H;
+  const size_t bk = rows * DK * esz, bv = rows * DV * esz, ba = rows * DK * 4, bb = rows * 4;
+  const size_t bo = rows * DV * 4, bp = size_t(pool_size) * H * DK * DV * 4;
+  const size_t bt = token_states ? rows * DK * DV * 4 : 0, bi = size_t(N) * 4;
+  const void* in[] = {q, k, v, alpha, beta, state_idx, num_tokens};
+  const size_t in_b[] = {bk, bk, bv, ba, bb, bi, bi};
+  const void* out[] = {state_pool, o, token_states};
+  const size_t out_b[] = {bp, bo, bt};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 7; ++j)
+      if (overlaps(out[i], out_b[i], in[j], in_b[j]))
+        return fail(KDA_ERR_SHAPE, "an output (state_pool, o, token_states) overlaps an input");
+    for (int j = i + 1; j < 3; ++j)
+      if (overlaps(out[i], out_b[i], out[j], out_b[j]))
+        return fail(KDA_ERR_SHAPE, "state_pool, o and token_states must not overlap");
+  }
+  kda::PoolDecodeArgs a{};
+  a.N = N; a.L = L; a.H = H; a.DK = DK; a.DV = DV;
+  a.in_bf16 = in_dtype == KDA_BF16;
+  a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta;
+  a.state_idx = state_idx; a.num_tokens = num_tokens;
+  a.pool = state_pool; a.pool_size = pool_size; a.o = o; a.token_states = token_states;
+  const char* msg = nullptr;
+  if (kda::launch_decode_pool(a, stream, &msg) != 0)
+    return fail(KDA_ERR_HIP, "decode launch failed: %s", msg ? msg : "?");
+  return ok();
+}
+
 }  // extern "C"

@@ -42,9 +42,27 @@ struct DecodeArgs {
   float* o;
 };
 
+// Decode of up to L tokens per sequence over a pool of states.
+struct PoolDecodeArgs {
+  int N, L, H, DK, DV;
+  bool in_bf16;
+  const void* q;               // [N, L, H, DK]
+  const void* k;
+  const void* v;               // [N, L, H, DV]
+  const float* alpha;          // [N, L, H, DK]
+  const float* beta;           // [N, L, H]
+  const int32_t* state_idx;    // device [N] or nullptr (slot n)
+  const int32_t* num_tokens;   // device [N] or nullptr (L each)
+  float* pool;                 // [pool_size, H, DK, DV]
+  int pool_size;
+  float* o;                    // [N, L, H, DV]
+  float* token_states;         // [N, L, H, DK, DV] or nullptr
+};
+
 // Launchers return 0 on success, else a non-zero code and a static message.
 int launch_prefill(const PrefillArgs& a, void* stream, const char** msg);
 int launch_decode(const DecodeArgs& a, void* stream, const char** msg);
+int launch_decode_pool(const PoolDecodeArgs& a, void* stream, const char** msg);
 size_t prefill_workspace_bytes(int N, int64_t T_total, int H, int DK, int DV, bool varlen);
 
 }  // namespace kda

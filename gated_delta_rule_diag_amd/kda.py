@@ -32,6 +32,7 @@ EXPORTED = (
     "kda_chunk_prefill_varlen_workspace_size",
     "kda_chunk_prefill_varlen",
     "kda_decode_step",
+    "kda_decode_pool",
     "kda_status_string",
     "kda_last_error_message",
 )
@@ -66,6 +67,8 @@ def load_library(path: str = _LIB_PATH) -> ctypes.CDLL:
                                              vp, sz, vp]
     lib.kda_decode_step.restype = i
     lib.kda_decode_step.argtypes = [i, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.kda_decode_pool.restype = i
+    lib.kda_decode_pool.argtypes = [i, i, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp, i, vp, vp, vp]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_status_string.argtypes = [i]
     lib.kda_last_error_message.restype = ctypes.c_char_p
@@ -257,3 +260,43 @@ def decode_step(q, k, v, alpha, beta, state, out=None):
     _check(lib().kda_decode_step(N, H, DK, DV, dt, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
                                  _ptr(beta), _ptr(state), _ptr(o), _stream(dev)))
     return o
+
+
+def decode_pool(q, k, v, alpha, beta, state_pool, state_idx=None, num_tokens=None,
+                return_token_states=False, out=None, token_states=None):
+    """Decode of up to L tokens per sequence with states in a pool.
+
+    q, k, alpha: [N,L,H,DK]; v: [N,L,H,DV]; beta: [N,L,H];
+    state_pool: [P,H,DK,DV] float32, updated in place;
+    state_idx: int32 device tensor [N] or None (slot n; P >= N); a slot outside
+    [0, P) marks a padding row (its outputs are 0, the pool is untouched);
+    num_tokens: int32 device tensor [N] or None (all L).
+    Returns (o [N,L,H,DV], token_states [N,L,H,DK,DV] or None).
+    """
+    N, L, H, DK = q.shape
+    DV = v.shape[-1]
+    dt = _in_dtype(q)
+    _need(q, "q", q.dtype)
+    _need(k, "k", q.dtype, (N, L, H, DK))
+    _need(v, "v", q.dtype, (N, L, H, DV))
+    _need(alpha, "alpha", torch.float32, (N, L, H, DK))
+    _need(beta, "beta", torch.float32, (N, L, H))
+    _need(state_pool, "state_pool", torch.float32)
+    if state_pool.dim() != 4 or tuple(state_pool.shape[1:]) != (H, DK, DV):
+        raise ValueError(f"state_pool must have shape [P,{H},{DK},{DV}], got {tuple(state_pool.shape)}")
+    if state_idx is not None:
+        _need(state_idx, "state_idx", torch.int32, (N,))
+    if num_tokens is not None:
+        _need(num_tokens, "num_tokens", torch.int32, (N,))
+    dev = q.device
+    o = out if out is not None else torch.empty((N, L, H, DV), device=dev, dtype=torch.float32)
+    _need(o, "out", torch.float32, (N, L, H, DV))
+    ts = None
+    if return_token_states:
+        ts = token_states if token_states is not None else torch.empty(
+            (N, L, H, DK, DV), device=dev, dtype=torch.float32)
+        _need(ts, "token_states", torch.float32, (N, L, H, DK, DV))
+    _check(lib().kda_decode_pool(
+        N, L, H, DK, DV, dt, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state_idx),
+        _ptr(num_tokens), _ptr(state_pool), state_pool.shape[0], _ptr(o), _ptr(ts), _stream(dev)))
+    return o, ts

@@ -151,6 +151,38 @@ kda_status_t kda_decode_step(int N, int H, int DK, int DV, kda_dtype_t in_dtype,
                              const void* k, const void* v, const float* alpha,
                              const float* beta, float* state, float* o, void* stream);
 
+/*
+ * Decode of up to L tokens per sequence over a pool of states (continuous
+ * batching: the batch's sequences index their states in a shared pool;
+ * speculative decoding: L draft tokens are run and the state after each is
+ * kept for the verifier).  Deployment tools must support both without
+ * breaking KDA's state handling ("Kimi Linear、独自の土俵でFull Attentionを
+ * 上回る" (remio.ai), section "Kimi Linearリリース後に注目すべき点"); each
+ * token is one step of the token recurrence defined above.
+ *   q, k, alpha  [N,L,H,DK];  v [N,L,H,DV];  beta [N,L,H]   (token j of
+ *                sequence n is row n*L + j)
+ *   state_idx    int32 DEVICE [N], 4-byte aligned, or NULL (sequence n uses
+ *                slot n; then pool_size >= N).  A slot outside
+ *                [0, pool_size) marks a padding row: its o rows are set to 0
+ *                and nothing else is read or written for it.  Valid slots
+ *                must be distinct (not checked: two sequences on one slot race).
+ *   num_tokens   int32 DEVICE [N], 4-byte aligned, or NULL (L each): sequence
+ *                n runs its first min(max(num_tokens[n], 0), L) tokens; the o
+ *                rows of the others are set to 0.
+ *   state_pool   [pool_size,H,DK,DV] float, read and updated IN PLACE: a slot
+ *                ends holding the state after its sequence's last token.
+ *   o            [N,L,H,DV] float output.
+ *   token_states [N,L,H,DK,DV] float or NULL: the state after each processed
+ *                token (entries of unprocessed tokens are not written).
+ *   1 <= L <= 64.  No output may overlap an input or another output.
+ * With L = 1, state_idx = NULL and num_tokens = NULL this is kda_decode_step.
+ */
+kda_status_t kda_decode_pool(int N, int L, int H, int DK, int DV, kda_dtype_t in_dtype,
+                             const void* q, const void* k, const void* v, const float* alpha,
+                             const float* beta, const int32_t* state_idx,
+                             const int32_t* num_tokens, float* state_pool, int pool_size,
+                             float* o, float* token_states, void* stream);
+
 const char* kda_status_string(kda_status_t s);
 const char* kda_last_error_message(void);
 

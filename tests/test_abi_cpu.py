@@ -193,6 +193,32 @@ def test_decode_argument_errors(lib):
     assert call(N=0) == OK
 
 
+def test_decode_pool_argument_errors(lib):
+    def call(N=4, L=2, H=2, DK=128, DV=128, dt=1, idx=P[9], ntok=P[10], pool=P[5], P_=8, o=P[6],
+             ts=None, ptrs=None):
+        q, k, v, a, b = ptrs or P[:5]
+        return lib.kda_decode_pool(N, L, H, DK, DV, dt, q, k, v, a, b, idx, ntok, pool, P_, o, ts,
+                                   None)
+
+    assert call(L=0) == UNSUP
+    assert call(L=65) == UNSUP
+    assert call(DV=96) == UNSUP
+    assert call(dt=5) == DTYPE
+    assert call(N=-1) == SHAPE
+    assert call(P_=-1) == SHAPE
+    assert call(idx=None, P_=3) == SHAPE                 # slot n needs pool_size >= N
+    assert call(pool=None) == NULL
+    assert call(o=None) == NULL
+    assert call(idx=ctypes.c_void_p(P[9].value + 2)) == ALIGN
+    assert call(ts=ctypes.c_void_p(P[11].value + 8)) == ALIGN
+    assert call(o=ctypes.c_void_p(P[2].value + 16)) == SHAPE           # o over v
+    assert call(pool=ctypes.c_void_p(P[0].value + 1024)) == SHAPE      # pool over q
+    assert call(ts=ctypes.c_void_p(P[6].value + 1024)) == SHAPE        # token states over o
+    assert call(o=ctypes.c_void_p(P[9].value)) == SHAPE                # o over state_idx
+    assert call(N=0) == OK
+    assert call(H=0) == OK
+
+
 def test_binding_fails_loudly_without_library(tmp_path):
     from gated_delta_rule_diag_amd.kda import load_library
 

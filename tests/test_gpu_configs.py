@@ -9,8 +9,8 @@ import torch
 from gated_delta_rule_diag_amd import inputs as I
 from gated_delta_rule_diag_amd import kda
 from kda_testlib import TOL, dev, flush, host
-from oracle import (kda_decode_step, kda_recurrent, kda_recurrent_snapshots, kda_recurrent_varlen,
-                    max_rel_err)
+from oracle import (kda_decode_pool, kda_decode_step, kda_recurrent, kda_recurrent_snapshots,
+                    kda_recurrent_varlen, max_rel_err)
 
 pytestmark = pytest.mark.gpu
 
@@ -100,6 +100,31 @@ def test_decode_n256_h32_full():
     # the oracle-prefilled sequences on their own
     sel = [0, 97, 255]
     assert max_rel_err(host(o)[sel], o_ref[sel]) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("L", [1, 4])
+def test_decode_pool_n256_h32_full(L):
+    """The decode workload's batch (256 sequences x 32 heads, d=128, bf16) as
+    continuous batching over a pool of 512 states in permuted slots: L=1 (one
+    token each) and L=4 (speculative drafts).  Every pair and every pool slot
+    is checked."""
+    N, H, D, P = 256, 32, 128, 512
+    flush(f"[config] decode pool N=256 L={L} H=32 d=128 bf16 pool=512")
+    rng = np.random.default_rng([I.SEED, 5, L])
+    q, k, v, a, b = (x.reshape((N, L) + x.shape[1:]) for x in I.decode_inputs(5 + L, N * L, H, D, D, "bf16"))
+    pool0 = (0.3 * rng.standard_normal((P, H, D, D), dtype=np.float32))
+    idx = rng.permutation(P)[:N].astype(np.int32)
+    bf = torch.bfloat16
+    pool = dev(pool0)
+    o, _ = kda.decode_pool(dev(q, bf), dev(k, bf), dev(v, bf), dev(a), dev(b), pool,
+                           torch.from_numpy(idx).cuda())
+    torch.cuda.synchronize()
+    o_ref, pool_ref, _ = kda_decode_pool(q, k, v, a, b, pool0, idx)
+    eo, ep = max_rel_err(host(o), o_ref), max_rel_err(host(pool)[idx], pool_ref[idx])
+    flush(f"    err o={eo:.2e} pool={ep:.2e}")
+    assert eo <= TOL["bf16"] and ep <= TOL["bf16"]
+    rest = np.setdiff1d(np.arange(P), idx)
+    assert torch.equal(pool[torch.from_numpy(rest).cuda()], dev(pool0[rest]))
 
 
 def _device_packed(c, lengths, H, D, dt):
