@@ -159,6 +159,42 @@ def main():
     pre_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     dec_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
 
+    # ---- the serving variants, timed after (and outside) the steps above ----
+    def time_call(fn, reps=max(args.steps, 5)):
+        fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        for _ in range(reps):
+            fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / reps * 1e3   # us per call
+
+    # decode steps back to back (no prefill in between: the previous step's
+    # writes are not drained while HBM idles)
+    dec_b2b_us = time_call(lambda: kda.decode_step(dq, dk_, dv_, da, db, dstate, do))
+    snaps = torch.empty((B, T // (64 * 16), H, D, D), device=dev, dtype=torch.float32)
+    snap_us = time_call(lambda: kda.chunk_prefill_snapshots(
+        pq, pk, pv, pa, pb, 16, None, True, 64, po, pst, snaps, pws))
+    del snaps
+    P = 2 * ND
+    gen_p = torch.Generator()
+    gen_p.manual_seed(I.SEED + 5)
+    slots = torch.randperm(P, generator=gen_p)[:ND].to(torch.int32).to(dev)
+    pool = torch.zeros((P, H, D, D), device=dev, dtype=torch.float32)
+    pool[slots.long()] = dstate
+    pool1_us = time_call(lambda: kda.decode_pool(dq[:, None], dk_[:, None], dv_[:, None],
+                                                 da[:, None], db[:, None], pool, slots,
+                                                 out=do[:, None]))
+    L4 = 4
+    rq, rk, rv = (x[:, None].expand(ND, L4, H, D).contiguous() for x in (dq, dk_, dv_))
+    ra = da[:, None].expand(ND, L4, H, D).contiguous()
+    rb = db[:, None].expand(ND, L4, H).contiguous()
+    o4 = torch.empty((ND, L4, H, D), device=dev, dtype=torch.float32)
+    pool4_us = time_call(lambda: kda.decode_pool(rq, rk, rv, ra, rb, pool, slots, out=o4))
+    del pool, rq, rk, rv, ra, rb, o4
+
     pre_bytes = prefill_algorithmic_bytes(T, H, D, D, False, True)
     dec_bytes = decode_algorithmic_bytes(ND, H, D, D)
     pre_gbs = pre_bytes / (pre_ms * 1e-3) / 1e9
@@ -226,6 +262,15 @@ def main():
             "algorithmic_bytes": pre_bytes,
             "algorithmic_tflops": pre_tflops,
             "mfma_frac_algorithmic": pre_tflops / BF16_MFMA_PEAK_TFLOPS,
+        },
+        "decode_back_to_back_us_per_step": dec_b2b_us,
+        "decode_back_to_back_hbm_frac": dec_bytes / (dec_b2b_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+        "serving_variants": {
+            "prefill_with_snapshots_every_1024_tokens_us": snap_us,
+            "decode_pool_512_slots_L1_us": pool1_us,
+            "decode_pool_512_slots_L1_hbm_frac": dec_bytes / (pool1_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "decode_pool_512_slots_L4_us": pool4_us,
+            "decode_pool_512_slots_L4_us_per_token": pool4_us / L4,
         },
         "roofline_decode": {
             "bound": "hbm",
