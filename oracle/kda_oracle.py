@@ -51,6 +51,7 @@ __all__ = [
     "kda_recurrent",
     "kda_recurrent_varlen",
     "kda_recurrent_snapshots",
+    "gdn_recurrent",
     "kda_decode_step",
     "kda_decode_pool",
     "kda_chunked",
@@ -102,6 +103,30 @@ def kda_recurrent(q, k, v, alpha, beta, S0=None):
         delta = b_t[..., None] * (v_t - pred)
         S = S + k_t[..., :, None] * delta[..., None, :]
         # 3. read.
+        o[:, t] = np.einsum("bhkv,bhk->bhv", S, q[:, t])
+    return o, S
+
+
+def gdn_recurrent(q, k, v, gate, beta, S0=None):
+    """Gated DeltaNet: the scalar-gate case KDA generalises ([EXPLAINER]
+    "Kimi Delta Attention の仕組み": Gated DeltaNet decays the whole state by
+    one scalar before the delta write; KDA turns that scalar into a diagonal).
+
+    Shapes: q, k [B,T,H,DK]; v [B,T,H,DV]; gate, beta [B,T,H];
+    S0 [B,H,DK,DV] or None.  Per token: S <- gate_t S; then the delta write
+    and the read exactly as in kda_recurrent.  Returns (o, S_T) in fp64.
+    """
+    q, k, v, beta = _f64(q), _f64(k), _f64(v), _f64(beta)
+    g = _check_alpha(gate)
+    B, T, H, DK = q.shape
+    DV = v.shape[-1]
+    assert g.shape == (B, T, H) and beta.shape == (B, T, H)
+    S = np.zeros((B, H, DK, DV)) if S0 is None else _f64(S0).copy()
+    o = np.zeros((B, T, H, DV))
+    for t in range(T):
+        S = g[:, t, :, None, None] * S                       # one scalar per head
+        pred = np.einsum("bhkv,bhk->bhv", S, k[:, t])
+        S = S + k[:, t, :, :, None] * (beta[:, t, :, None] * (v[:, t] - pred))[..., None, :]
         o[:, t] = np.einsum("bhkv,bhk->bhv", S, q[:, t])
     return o, S
 

@@ -17,7 +17,7 @@ from fractions import Fraction
 import numpy as np
 import pytest
 
-from oracle import (kda_chunked, kda_decode_pool, kda_decode_step, kda_recurrent,
+from oracle import (gdn_recurrent, kda_chunked, kda_decode_pool, kda_decode_step, kda_recurrent,
                     kda_recurrent_snapshots, kda_recurrent_varlen, max_rel_err)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -159,6 +159,41 @@ def test_p4_scalar_gate_is_gated_deltanet():
             St = M @ St + b[0, t, h] * np.outer(kt, v[0, t, h])
             np.testing.assert_allclose(o[0, t, h], St.T @ q[0, t, h], atol=1e-12)
         np.testing.assert_allclose(S[0, h], St, atol=1e-12)
+
+
+def test_p4_gdn_oracle_dense_transition():
+    """The scalar-gate oracle against the dense transition written out:
+    S_t = g_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T, o_t = S_t^T q_t;
+    with a gate that varies across tokens and heads."""
+    rng = np.random.default_rng(41)
+    q, k, v, a, b, S0 = rand_inputs(rng, 2, 25, 3, 6, 4)
+    g = a[..., 0]
+    o, S = gdn_recurrent(q, k, v, g, b, S0)
+    DK = q.shape[-1]
+    for bb in range(2):
+        for h in range(3):
+            St = S0[bb, h].copy()
+            for t in range(25):
+                kt = k[bb, t, h]
+                St = g[bb, t, h] * (np.eye(DK) - b[bb, t, h] * np.outer(kt, kt)) @ St \
+                    + b[bb, t, h] * np.outer(kt, v[bb, t, h])
+                np.testing.assert_allclose(o[bb, t, h], St.T @ q[bb, t, h], atol=1e-12)
+            np.testing.assert_allclose(S[bb, h], St, atol=1e-12)
+
+
+def test_p4_gdn_oracle_gate_one_is_deltanet_and_zero_write_is_decay():
+    """gate = 1: DeltaNet (exact replacement under unit keys); beta = 0: the
+    state is the product of the gates times S0."""
+    rng = np.random.default_rng(42)
+    q, k, v, a, b, S0 = rand_inputs(rng, 1, 12, 2, 5, 3)
+    g = a[..., 0]
+    _, S = gdn_recurrent(q, k, v, g, np.zeros_like(b), S0)
+    np.testing.assert_allclose(S, np.prod(g, axis=1)[..., None, None] * S0, rtol=1e-13)
+    Q, _ = np.linalg.qr(rng.standard_normal((5, 5)))
+    kk = np.broadcast_to(Q.T[None, :, None, :], (1, 5, 2, 5)).copy()
+    vv = rng.standard_normal((1, 5, 2, 3))
+    o, _ = gdn_recurrent(kk, kk, vv, np.ones((1, 5, 2)), np.ones((1, 5, 2)))
+    np.testing.assert_allclose(o, vv, atol=1e-13)
 
 
 # ------------------------------------------------------------------- P5 ---
