@@ -178,6 +178,9 @@ def main():
     snap_us = time_call(lambda: kda.chunk_prefill_snapshots(
         pq, pk, pv, pa, pb, 16, None, True, 64, po, pst, snaps, pws))
     del snaps
+    pg = pa[..., 0].contiguous()   # one gate per token and head (Gated DeltaNet)
+    gate_us = time_call(lambda: kda.chunk_prefill(pq, pk, pv, pg, pb, None, True, 64, po, pst, pws))
+    del pg
     P = 2 * ND
     gen_p = torch.Generator()
     gen_p.manual_seed(I.SEED + 5)
@@ -267,6 +270,7 @@ def main():
         "decode_back_to_back_hbm_frac": dec_bytes / (dec_b2b_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
         "serving_variants": {
             "prefill_with_snapshots_every_1024_tokens_us": snap_us,
+            "prefill_scalar_gate_us": gate_us,
             "decode_pool_512_slots_L1_us": pool1_us,
             "decode_pool_512_slots_L1_hbm_frac": dec_bytes / (pool1_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
             "decode_pool_512_slots_L4_us": pool4_us,

@@ -49,7 +49,7 @@ bool dims_ok(int d) { return d == 64 || d == 128; }
 kda_status_t check_prefill(int nseq, int64_t ntok, int H, int DK, int DV, int chunk,
                            kda_dtype_t dt, const void* q, const void* k, const void* v,
                            const float* alpha, const float* beta, const float* s_in,
-                           const float* o, const float* s_out) {
+                           const float* o, const float* s_out, bool alpha_scalar) {
   if (nseq < 0 || ntok < 0 || H < 0)
     return fail(KDA_ERR_SHAPE, "negative size (sequences=%d tokens=%lld H=%d)", nseq,
                 (long long)ntok, H);
@@ -63,6 +63,7 @@ kda_status_t check_prefill(int nseq, int64_t ntok, int H, int DK, int DV, int ch
   const size_t esz = dt == KDA_BF16 ? 2 : 4;
   const size_t nk = size_t(ntok) * H * DK, nv = size_t(ntok) * H * DV, nb = size_t(ntok) * H;
   const size_t ns = size_t(nseq) * H * DK * DV;
+  const size_t na = (alpha_scalar ? nb : nk) * 4;   // bytes of alpha
   if (nk > 0) {
     if (!q || !k || !v || !alpha || !beta || !o)
       return fail(KDA_ERR_NULL, "q, k, v, alpha, beta and o must be non-NULL");
@@ -76,13 +77,13 @@ kda_status_t check_prefill(int nseq, int64_t ntok, int H, int DK, int DV, int ch
   // o must not overlap any input or state; state_out may only equal state_in.
   const size_t obytes = nv * 4;
   if (overlaps(o, obytes, q, nk * esz) || overlaps(o, obytes, k, nk * esz) ||
-      overlaps(o, obytes, v, nv * esz) || overlaps(o, obytes, alpha, nk * 4) ||
+      overlaps(o, obytes, v, nv * esz) || overlaps(o, obytes, alpha, na) ||
       overlaps(o, obytes, beta, nb * 4) || overlaps(o, obytes, s_in, ns * 4) ||
       overlaps(o, obytes, s_out, ns * 4))
     return fail(KDA_ERR_SHAPE, "o overlaps an input or a state");
   if (s_out && s_out != s_in &&
       (overlaps(s_out, ns * 4, q, nk * esz) || overlaps(s_out, ns * 4, k, nk * esz) ||
-       overlaps(s_out, ns * 4, v, nv * esz) || overlaps(s_out, ns * 4, alpha, nk * 4) ||
+       overlaps(s_out, ns * 4, v, nv * esz) || overlaps(s_out, ns * 4, alpha, na) ||
        overlaps(s_out, ns * 4, beta, nb * 4) || overlaps(s_out, ns * 4, s_in, ns * 4)))
     return fail(KDA_ERR_SHAPE, "state_out overlaps an input (only state_out == state_in is allowed)");
   return KDA_OK;
@@ -134,8 +135,8 @@ static kda_status_t run_prefill(kda::PrefillArgs& a, size_t need, void* stream) 
     const size_t nsnap = a.snapshots ? size_t(a.N) * size_t(a.T_fixed / (64 * a.snap_every)) * a.H *
                                            a.DK * a.DV : 0;
     const void* ptrs[] = {a.q, a.k, a.v, a.alpha, a.beta, a.state_in, a.o, a.state_out, a.snapshots};
-    const size_t sizes[] = {nk * esz, nk * esz, nv * esz, nk * 4, nb * 4, ns * 4, nv * 4, ns * 4,
-                            nsnap * 4};
+    const size_t sizes[] = {nk * esz, nk * esz, nv * esz, (a.alpha_scalar ? nb : nk) * 4, nb * 4,
+                            ns * 4, nv * 4, ns * 4, nsnap * 4};
     for (int i = 0; i < 9; ++i)
       if (overlaps(a.workspace, need, ptrs[i], sizes[i]))
         return fail(KDA_ERR_SHAPE, "workspace overlaps another argument");
@@ -147,14 +148,15 @@ static kda_status_t run_prefill(kda::PrefillArgs& a, size_t need, void* stream) 
   return ok();
 }
 
-kda_status_t kda_chunk_prefill(int B, int T, int H, int DK, int DV, int chunk,
-                               kda_dtype_t in_dtype, const void* q, const void* k,
-                               const void* v, const float* alpha, const float* beta,
-                               const float* state_in, float* o, float* state_out,
-                               void* workspace, size_t workspace_bytes, void* stream) {
+static kda_status_t prefill_fixed(int B, int T, int H, int DK, int DV, int chunk,
+                                  kda_dtype_t in_dtype, const void* q, const void* k,
+                                  const void* v, const float* alpha, const float* beta,
+                                  const float* state_in, float* o, float* state_out,
+                                  void* workspace, size_t workspace_bytes, void* stream,
+                                  bool alpha_scalar) {
   if (B < 0 || T < 0) return fail(KDA_ERR_SHAPE, "negative size (B=%d T=%d)", B, T);
   kda_status_t s = check_prefill(B, int64_t(B) * T, H, DK, DV, chunk, in_dtype, q, k, v, alpha,
-                                 beta, state_in, o, state_out);
+                                 beta, state_in, o, state_out, alpha_scalar);
   if (s != KDA_OK) return s;
   kda::PrefillArgs a{};
   a.N = B;
@@ -166,7 +168,27 @@ kda_status_t kda_chunk_prefill(int B, int T, int H, int DK, int DV, int chunk,
   a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta;
   a.state_in = state_in; a.o = o; a.state_out = state_out;
   a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+  a.alpha_scalar = alpha_scalar;
   return run_prefill(a, kda::prefill_workspace_bytes(B, a.T_total, H, DK, DV, false), stream);
+}
+
+kda_status_t kda_chunk_prefill(int B, int T, int H, int DK, int DV, int chunk,
+                               kda_dtype_t in_dtype, const void* q, const void* k,
+                               const void* v, const float* alpha, const float* beta,
+                               const float* state_in, float* o, float* state_out,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  return prefill_fixed(B, T, H, DK, DV, chunk, in_dtype, q, k, v, alpha, beta, state_in, o,
+                       state_out, workspace, workspace_bytes, stream, false);
+}
+
+kda_status_t kda_chunk_prefill_scalar_gate(int B, int T, int H, int DK, int DV, int chunk,
+                                           kda_dtype_t in_dtype, const void* q, const void* k,
+                                           const void* v, const float* gate, const float* beta,
+                                           const float* state_in, float* o, float* state_out,
+                                           void* workspace, size_t workspace_bytes,
+                                           void* stream) {
+  return prefill_fixed(B, T, H, DK, DV, chunk, in_dtype, q, k, v, gate, beta, state_in, o,
+                       state_out, workspace, workspace_bytes, stream, true);
 }
 
 kda_status_t kda_chunk_prefill_snapshots(int B, int T, int H, int DK, int DV, int chunk,
@@ -178,7 +200,7 @@ kda_status_t kda_chunk_prefill_snapshots(int B, int T, int H, int DK, int DV, in
   if (B < 0 || T < 0) return fail(KDA_ERR_SHAPE, "negative size (B=%d T=%d)", B, T);
   if (every < 1) return fail(KDA_ERR_SHAPE, "every=%d: must be >= 1", every);
   kda_status_t s = check_prefill(B, int64_t(B) * T, H, DK, DV, chunk, in_dtype, q, k, v, alpha,
-                                 beta, state_in, o, state_out);
+                                 beta, state_in, o, state_out, false);
   if (s != KDA_OK) return s;
   const int64_t nsnap = int64_t(T) / (int64_t(64) * every);
   const size_t sbytes = size_t(B) * size_t(nsnap) * H * DK * DV * 4;
@@ -210,18 +232,19 @@ kda_status_t kda_chunk_prefill_snapshots(int B, int T, int H, int DK, int DV, in
   return run_prefill(a, kda::prefill_workspace_bytes(B, a.T_total, H, DK, DV, false), stream);
 }
 
-kda_status_t kda_chunk_prefill_varlen(int N, int T_total, const int32_t* cu_seqlens, int H,
-                                      int DK, int DV, int chunk, kda_dtype_t in_dtype,
-                                      const void* q, const void* k, const void* v,
-                                      const float* alpha, const float* beta,
-                                      const float* state_in, float* o, float* state_out,
-                                      void* workspace, size_t workspace_bytes, void* stream) {
+static kda_status_t prefill_varlen(int N, int T_total, const int32_t* cu_seqlens, int H,
+                                   int DK, int DV, int chunk, kda_dtype_t in_dtype,
+                                   const void* q, const void* k, const void* v,
+                                   const float* alpha, const float* beta,
+                                   const float* state_in, float* o, float* state_out,
+                                   void* workspace, size_t workspace_bytes, void* stream,
+                                   bool alpha_scalar) {
   if (N < 0 || T_total < 0) return fail(KDA_ERR_SHAPE, "negative size (N=%d T_total=%d)", N, T_total);
   if (N > 0 && cu_seqlens == nullptr) return fail(KDA_ERR_NULL, "cu_seqlens must be non-NULL");
   if (cu_seqlens && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u))
     return fail(KDA_ERR_ALIGN, "cu_seqlens is not 4-byte aligned");
   kda_status_t s = check_prefill(N, T_total, H, DK, DV, chunk, in_dtype, q, k, v, alpha, beta,
-                                 state_in, o, state_out);
+                                 state_in, o, state_out, alpha_scalar);
   if (s != KDA_OK) return s;
   kda::PrefillArgs a{};
   a.N = N;
@@ -233,12 +256,35 @@ kda_status_t kda_chunk_prefill_varlen(int N, int T_total, const int32_t* cu_seql
   a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta;
   a.state_in = state_in; a.o = o; a.state_out = state_out;
   a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+  a.alpha_scalar = alpha_scalar;
   return run_prefill(a, kda::prefill_workspace_bytes(N, T_total, H, DK, DV, true), stream);
 }
 
-kda_status_t kda_decode_step(int N, int H, int DK, int DV, kda_dtype_t in_dtype, const void* q,
-                             const void* k, const void* v, const float* alpha,
-                             const float* beta, float* state, float* o, void* stream) {
+kda_status_t kda_chunk_prefill_varlen(int N, int T_total, const int32_t* cu_seqlens, int H,
+                                      int DK, int DV, int chunk, kda_dtype_t in_dtype,
+                                      const void* q, const void* k, const void* v,
+                                      const float* alpha, const float* beta,
+                                      const float* state_in, float* o, float* state_out,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  return prefill_varlen(N, T_total, cu_seqlens, H, DK, DV, chunk, in_dtype, q, k, v, alpha, beta,
+                        state_in, o, state_out, workspace, workspace_bytes, stream, false);
+}
+
+kda_status_t kda_chunk_prefill_varlen_scalar_gate(int N, int T_total, const int32_t* cu_seqlens,
+                                                  int H, int DK, int DV, int chunk,
+                                                  kda_dtype_t in_dtype, const void* q,
+                                                  const void* k, const void* v, const float* gate,
+                                                  const float* beta, const float* state_in,
+                                                  float* o, float* state_out, void* workspace,
+                                                  size_t workspace_bytes, void* stream) {
+  return prefill_varlen(N, T_total, cu_seqlens, H, DK, DV, chunk, in_dtype, q, k, v, gate, beta,
+                        state_in, o, state_out, workspace, workspace_bytes, stream, true);
+}
+
+static kda_status_t decode_step(int N, int H, int DK, int DV, kda_dtype_t in_dtype, const void* q,
+                                const void* k, const void* v, const float* alpha,
+                                const float* beta, float* state, float* o, void* stream,
+                                bool alpha_scalar) {
   if (N < 0 || H < 0) return fail(KDA_ERR_SHAPE, "negative size (N=%d H=%d)", N, H);
   if (!dims_ok(DK) || !dims_ok(DV))
     return fail(KDA_ERR_UNSUPPORTED, "DK=%d DV=%d: only 64 and 128 are supported", DK, DV);
@@ -256,22 +302,37 @@ kda_status_t kda_decode_step(int N, int H, int DK, int DV, kda_dtype_t in_dtype,
   const size_t esz = in_dtype == KDA_BF16 ? 2 : 4;
   const size_t nh = size_t(N) * H;
   const size_t obytes = nh * DV * 4, sbytes = nh * DK * DV * 4;
+  const size_t abytes = (alpha_scalar ? nh : nh * DK) * 4;
   if (overlaps(o, obytes, q, nh * DK * esz) || overlaps(o, obytes, k, nh * DK * esz) ||
-      overlaps(o, obytes, v, nh * DV * esz) || overlaps(o, obytes, alpha, nh * DK * 4) ||
+      overlaps(o, obytes, v, nh * DV * esz) || overlaps(o, obytes, alpha, abytes) ||
       overlaps(o, obytes, beta, nh * 4) || overlaps(o, obytes, state, sbytes))
     return fail(KDA_ERR_SHAPE, "o overlaps an input or the state");
   if (overlaps(state, sbytes, q, nh * DK * esz) || overlaps(state, sbytes, k, nh * DK * esz) ||
-      overlaps(state, sbytes, v, nh * DV * esz) || overlaps(state, sbytes, alpha, nh * DK * 4) ||
+      overlaps(state, sbytes, v, nh * DV * esz) || overlaps(state, sbytes, alpha, abytes) ||
       overlaps(state, sbytes, beta, nh * 4))
     return fail(KDA_ERR_SHAPE, "state overlaps an input");
   kda::DecodeArgs a{};
   a.N = N; a.H = H; a.DK = DK; a.DV = DV;
   a.in_bf16 = in_dtype == KDA_BF16;
   a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.state = state; a.o = o;
+  a.alpha_scalar = alpha_scalar;
   const char* msg = nullptr;
   if (kda::launch_decode(a, stream, &msg) != 0)
     return fail(KDA_ERR_HIP, "decode launch failed: %s", msg ? msg : "?");
   return ok();
+}
+
+kda_status_t kda_decode_step(int N, int H, int DK, int DV, kda_dtype_t in_dtype, const void* q,
+                             const void* k, const void* v, const float* alpha,
+                             const float* beta, float* state, float* o, void* stream) {
+  return decode_step(N, H, DK, DV, in_dtype, q, k, v, alpha, beta, state, o, stream, false);
+}
+
+kda_status_t kda_decode_step_scalar_gate(int N, int H, int DK, int DV, kda_dtype_t in_dtype,
+                                         const void* q, const void* k, const void* v,
+                                         const float* gate, const float* beta, float* state,
+                                         float* o, void* stream) {
+  return decode_step(N, H, DK, DV, in_dtype, q, k, v, gate, beta, state, o, stream, true);
 }
 
 kda_status_t kda_decode_pool(int N, int L, int H, int DK, int DV, kda_dtype_t in_dtype,

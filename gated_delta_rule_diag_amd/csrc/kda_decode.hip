@@ -118,7 +118,7 @@ __global__ __launch_bounds__(kThreads) void kda_decode_kernel(PoolDecodeArgs p) 
   if (t < DK) {
     const float kk = load_in<BF16>(k, pair * DK + t);
     const float qq = load_in<BF16>(q, pair * DK + t);
-    const float aa = alpha[pair * DK + t];
+    const float aa = p.alpha_scalar ? alpha[pair] : alpha[pair * DK + t];
     s_ak[t] = aa * kk;
     s_aq[t] = aa * qq;
     s_a[t] = aa;
@@ -232,7 +232,7 @@ __global__ __launch_bounds__(kThreads) void kda_decode_pool_kernel(PoolDecodeArg
     if (t < DK) {
       pk = load_in<BF16>(p.k, r * DK + t);
       pq = load_in<BF16>(p.q, r * DK + t);
-      pa = p.alpha[r * DK + t];
+      pa = p.alpha_scalar ? p.alpha[r] : p.alpha[r * DK + t];
     }
     if (t < kVC) {
       pv = load_in<BF16>(p.v, r * DV + c0 + t);
@@ -371,6 +371,7 @@ int launch_decode(const DecodeArgs& a, void* stream, const char** msg) {
   pa.state_idx = nullptr; pa.num_tokens = nullptr;
   pa.pool = a.state; pa.pool_size = a.N;
   pa.o = a.o; pa.token_states = nullptr;
+  pa.alpha_scalar = a.alpha_scalar;
   return launch_decode_pool(pa, stream, msg);
 }
 

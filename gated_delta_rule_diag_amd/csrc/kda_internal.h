@@ -28,6 +28,7 @@ struct PrefillArgs {
   size_t workspace_bytes;
   float* snapshots;            // [N, T_fixed / (64 * snap_every), H, DK, DV] or nullptr
   int snap_every;              // chunks between snapshots (with snapshots != nullptr)
+  bool alpha_scalar;           // alpha is [tokens, H]: one gate per token and head
 };
 
 struct DecodeArgs {
@@ -40,6 +41,7 @@ struct DecodeArgs {
   const float* beta;
   float* state;
   float* o;
+  bool alpha_scalar;           // alpha is [N, H]
 };
 
 // Decode of up to L tokens per sequence over a pool of states.
@@ -57,6 +59,7 @@ struct PoolDecodeArgs {
   int pool_size;
   float* o;                    // [N, L, H, DV]
   float* token_states;         // [N, L, H, DK, DV] or nullptr
+  bool alpha_scalar;           // alpha is [N, L, H]
 };
 
 // Launchers return 0 on success, else a non-zero code and a static message.

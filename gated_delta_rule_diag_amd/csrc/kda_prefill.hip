@@ -58,6 +58,7 @@ struct Params {
   float* snap;        // state snapshots [N][snap_per_seq][H][DK][DV] (SNAP kernels)
   int snap_every;     // a snapshot after every snap_every-th full chunk
   int64_t snap_per_seq;
+  int alpha_scalar;   // alpha is [tokens][H] (one gate per token and head)
 };
 
 // ---------------------------------------------------------------- layout ----
@@ -832,14 +833,20 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_prefill_kernel(Params p
     // Wave-uniform base pointers for the chunk and 32-bit per-lane offsets
     // (scalar-base addressing: one vector add per load).
     const int64_t row0 = tk0 * H + h;
-    const float* ab = p.alpha + row0 * DK;
+    const bool sg = p.alpha_scalar != 0;
+    const float* ab = p.alpha + (sg ? row0 : row0 * DK);
     const char* kb = static_cast<const char*>(p.k) + row0 * DK * ESZ;
     const char* qb = static_cast<const char*>(p.q) + row0 * DK * ESZ;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = r0 + i < nvv ? r0 + i : nvv - 1;
       const uint32_t off = uint32_t(r * rsk + c0);
-      pa[i] = *reinterpret_cast<const float4*>(ab + off);
+      if (sg) {
+        const float x = ab[uint32_t(r * H)];
+        pa[i] = make_float4(x, x, x, x);
+      } else {
+        pa[i] = *reinterpret_cast<const float4*>(ab + off);
+      }
       pk[i] = ldraw4<BF>(kb, off);
       pq[i] = ldraw4<BF>(qb, off);
     }
@@ -1036,6 +1043,7 @@ struct StageParams {
   float* snap;       // state snapshots [N][snap_per_seq][H][DK][DV] (SNAP chain kernels)
   int snap_every;
   int64_t snap_per_seq;
+  int alpha_scalar;  // alpha is [tokens][H]
 };
 
 template <bool BF> struct FL;
@@ -1196,7 +1204,8 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_stage_kernel(StageParam
     const int64_t rem = p.T_fixed - c * kC;
     const int nvv = int(rem < kC ? rem : kC);
     const int64_t row0 = tok0 * H + h;
-    const float* ab = p.alpha + row0 * DK;
+    const bool sg = p.alpha_scalar != 0;
+    const float* ab = p.alpha + (sg ? row0 : row0 * DK);
     const char* kb = static_cast<const char*>(p.k) + row0 * DK * ESZ;
     const char* qb = static_cast<const char*>(p.q) + row0 * DK * ESZ;
     const int rsk = H * DK;
@@ -1204,7 +1213,12 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_stage_kernel(StageParam
     for (int i = 0; i < 4; ++i) {
       const int r = r0 + i < nvv ? r0 + i : nvv - 1;
       const uint32_t off = uint32_t(r * rsk + c0);
-      pa[i] = *reinterpret_cast<const float4*>(ab + off);
+      if (sg) {
+        const float x = ab[uint32_t(r * H)];
+        pa[i] = make_float4(x, x, x, x);
+      } else {
+        pa[i] = *reinterpret_cast<const float4*>(ab + off);
+      }
       pk[i] = ldraw4<BF>(kb, off);
       pq[i] = ldraw4<BF>(qb, off);
     }
@@ -1608,6 +1622,7 @@ void launch_staged_t(const Params& base, int64_t T, int nsub, hipStream_t st, ch
   sp.snap = base.snap;
   sp.snap_every = base.snap_every;
   sp.snap_per_seq = base.snap_per_seq;
+  sp.alpha_scalar = base.alpha_scalar;
   const int64_t nsegs = (nchunks + seg - 1) / seg;
   const int64_t cus = device_cus();
   for (int64_t si = 0; si < nsegs; ++si) {
@@ -1688,6 +1703,7 @@ int launch_prefill(const PrefillArgs& a, void* stream, const char** msg) {
   p.snap = a.snapshots;
   p.snap_every = a.snap_every > 0 ? a.snap_every : 1;
   p.snap_per_seq = a.snapshots ? a.T_fixed / (int64_t(kC) * p.snap_every) : 0;
+  p.alpha_scalar = a.alpha_scalar ? 1 : 0;
   const int64_t pairs = int64_t(a.N) * a.H;
   const bool varlen = a.cu_seqlens != nullptr;
   const int64_t nchunks = varlen ? 0 : (a.T_fixed + kC - 1) / kC;

@@ -33,6 +33,9 @@ EXPORTED = (
     "kda_chunk_prefill_varlen",
     "kda_decode_step",
     "kda_decode_pool",
+    "kda_chunk_prefill_scalar_gate",
+    "kda_chunk_prefill_varlen_scalar_gate",
+    "kda_decode_step_scalar_gate",
     "kda_status_string",
     "kda_last_error_message",
 )
@@ -67,6 +70,12 @@ def load_library(path: str = _LIB_PATH) -> ctypes.CDLL:
                                              vp, sz, vp]
     lib.kda_decode_step.restype = i
     lib.kda_decode_step.argtypes = [i, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.kda_chunk_prefill_scalar_gate.restype = i
+    lib.kda_chunk_prefill_scalar_gate.argtypes = list(lib.kda_chunk_prefill.argtypes)
+    lib.kda_chunk_prefill_varlen_scalar_gate.restype = i
+    lib.kda_chunk_prefill_varlen_scalar_gate.argtypes = list(lib.kda_chunk_prefill_varlen.argtypes)
+    lib.kda_decode_step_scalar_gate.restype = i
+    lib.kda_decode_step_scalar_gate.argtypes = list(lib.kda_decode_step.argtypes)
     lib.kda_decode_pool.restype = i
     lib.kda_decode_pool.argtypes = [i, i, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp, i, vp, vp, vp]
     lib.kda_status_string.restype = ctypes.c_char_p
@@ -125,7 +134,8 @@ def chunk_prefill(q, k, v, alpha, beta, initial_state=None, output_final_state=T
     """KDA chunked prefill, fixed length.
 
     q, k: [B,T,H,DK], v: [B,T,H,DV] (bfloat16 or float32, same dtype);
-    alpha: [B,T,H,DK] float32; beta: [B,T,H] float32;
+    alpha: [B,T,H,DK] float32 (per-channel decay), or [B,T,H] for the scalar
+    gate of Gated DeltaNet; beta: [B,T,H] float32;
     initial_state: [B,H,DK,DV] float32 or None (zeros).
     Returns (o [B,T,H,DV] float32, final_state [B,H,DK,DV] float32 or None).
     """
@@ -135,7 +145,8 @@ def chunk_prefill(q, k, v, alpha, beta, initial_state=None, output_final_state=T
     _need(q, "q", q.dtype)
     _need(k, "k", q.dtype, (B, T, H, DK))
     _need(v, "v", q.dtype, (B, T, H, DV))
-    _need(alpha, "alpha", torch.float32, (B, T, H, DK))
+    scalar = alpha.dim() == 3
+    _need(alpha, "alpha", torch.float32, (B, T, H) if scalar else (B, T, H, DK))
     _need(beta, "beta", torch.float32, (B, T, H))
     if initial_state is not None:
         _need(initial_state, "initial_state", torch.float32, (B, H, DK, DV))
@@ -150,7 +161,8 @@ def chunk_prefill(q, k, v, alpha, beta, initial_state=None, output_final_state=T
     wsz = lib().kda_chunk_prefill_workspace_size(B, T, H, DK, DV, chunk)
     if wsz and workspace is None:
         workspace = torch.empty(wsz, device=dev, dtype=torch.uint8)
-    _check(lib().kda_chunk_prefill(
+    fn = lib().kda_chunk_prefill_scalar_gate if scalar else lib().kda_chunk_prefill
+    _check(fn(
         B, T, H, DK, DV, chunk, dt, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
         _ptr(initial_state), _ptr(o), _ptr(st), _ptr(workspace),
         0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(dev)))
@@ -206,7 +218,8 @@ def chunk_prefill_varlen(q, k, v, alpha, beta, cu_seqlens, initial_state=None,
                          workspace=None):
     """KDA chunked prefill over packed sequences.
 
-    q, k: [T_total,H,DK], v: [T_total,H,DV]; alpha [T_total,H,DK]; beta [T_total,H];
+    q, k: [T_total,H,DK], v: [T_total,H,DV]; alpha [T_total,H,DK] (or [T_total,H]
+    for a scalar gate); beta [T_total,H];
     cu_seqlens: int32 device tensor [N+1]; initial_state [N,H,DK,DV] or None.
     Returns (o [T_total,H,DV], final_state [N,H,DK,DV] or None).
     """
@@ -216,7 +229,8 @@ def chunk_prefill_varlen(q, k, v, alpha, beta, cu_seqlens, initial_state=None,
     _need(q, "q", q.dtype)
     _need(k, "k", q.dtype, (Tt, H, DK))
     _need(v, "v", q.dtype, (Tt, H, DV))
-    _need(alpha, "alpha", torch.float32, (Tt, H, DK))
+    scalar = alpha.dim() == 2
+    _need(alpha, "alpha", torch.float32, (Tt, H) if scalar else (Tt, H, DK))
     _need(beta, "beta", torch.float32, (Tt, H))
     _need(cu_seqlens, "cu_seqlens", torch.int32)
     N = cu_seqlens.numel() - 1
@@ -233,7 +247,8 @@ def chunk_prefill_varlen(q, k, v, alpha, beta, cu_seqlens, initial_state=None,
     wsz = lib().kda_chunk_prefill_varlen_workspace_size(N, Tt, H, DK, DV, chunk)
     if wsz and workspace is None:
         workspace = torch.empty(wsz, device=dev, dtype=torch.uint8)
-    _check(lib().kda_chunk_prefill_varlen(
+    fn = lib().kda_chunk_prefill_varlen_scalar_gate if scalar else lib().kda_chunk_prefill_varlen
+    _check(fn(
         N, Tt, _ptr(cu_seqlens), H, DK, DV, chunk, dt, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
         _ptr(beta), _ptr(initial_state), _ptr(o), _ptr(st), _ptr(workspace),
         0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(dev)))
@@ -243,7 +258,8 @@ def chunk_prefill_varlen(q, k, v, alpha, beta, cu_seqlens, initial_state=None,
 def decode_step(q, k, v, alpha, beta, state, out=None):
     """One recurrent decode step; ``state`` [N,H,DK,DV] float32 is updated in place.
 
-    q, k: [N,H,DK], v: [N,H,DV]; alpha [N,H,DK]; beta [N,H].  Returns o [N,H,DV].
+    q, k: [N,H,DK], v: [N,H,DV]; alpha [N,H,DK] (or [N,H] for a scalar gate);
+    beta [N,H].  Returns o [N,H,DV].
     """
     N, H, DK = q.shape
     DV = v.shape[-1]
@@ -251,14 +267,16 @@ def decode_step(q, k, v, alpha, beta, state, out=None):
     _need(q, "q", q.dtype)
     _need(k, "k", q.dtype, (N, H, DK))
     _need(v, "v", q.dtype, (N, H, DV))
-    _need(alpha, "alpha", torch.float32, (N, H, DK))
+    scalar = alpha.dim() == 2
+    _need(alpha, "alpha", torch.float32, (N, H) if scalar else (N, H, DK))
     _need(beta, "beta", torch.float32, (N, H))
     _need(state, "state", torch.float32, (N, H, DK, DV))
     dev = q.device
     o = out if out is not None else torch.empty((N, H, DV), device=dev, dtype=torch.float32)
     _need(o, "out", torch.float32, (N, H, DV))
-    _check(lib().kda_decode_step(N, H, DK, DV, dt, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
-                                 _ptr(beta), _ptr(state), _ptr(o), _stream(dev)))
+    fn = lib().kda_decode_step_scalar_gate if scalar else lib().kda_decode_step
+    _check(fn(N, H, DK, DV, dt, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state),
+              _ptr(o), _stream(dev)))
     return o
 
 

@@ -152,6 +152,38 @@ kda_status_t kda_decode_step(int N, int H, int DK, int DV, kda_dtype_t in_dtype,
                              const float* beta, float* state, float* o, void* stream);
 
 /*
+ * Scalar-gate (Gated DeltaNet) forms: the same operator with one decay gate
+ * per token and head instead of one per key channel, i.e. alpha_t = g_t * 1.
+ * Gated DeltaNet decays the whole state by one scalar before the delta write,
+ * and KDA generalises that scalar to a diagonal ("Kimi Delta Attention 徹底
+ * 解説" (tech-tide.dev), section "Kimi Delta Attention の仕組み — 「忘れ方」を
+ * 鍛える").  Arguments as in the per-channel entry points above, except
+ *   gate  [B,T,H] (fixed), [T_total,H] (varlen), [N,H] (decode) float, in the
+ *         same data domain as alpha.
+ * Same kernels, same results as passing alpha with every channel equal to the
+ * gate (bit for bit); the gate costs 4 bytes per token-head instead of 4*DK.
+ * Workspace sizes: kda_chunk_prefill_workspace_size and
+ * kda_chunk_prefill_varlen_workspace_size.
+ */
+kda_status_t kda_chunk_prefill_scalar_gate(int B, int T, int H, int DK, int DV, int chunk,
+                                           kda_dtype_t in_dtype, const void* q, const void* k,
+                                           const void* v, const float* gate, const float* beta,
+                                           const float* state_in, float* o, float* state_out,
+                                           void* workspace, size_t workspace_bytes,
+                                           void* stream);
+kda_status_t kda_chunk_prefill_varlen_scalar_gate(int N, int T_total, const int32_t* cu_seqlens,
+                                                  int H, int DK, int DV, int chunk,
+                                                  kda_dtype_t in_dtype, const void* q,
+                                                  const void* k, const void* v, const float* gate,
+                                                  const float* beta, const float* state_in,
+                                                  float* o, float* state_out, void* workspace,
+                                                  size_t workspace_bytes, void* stream);
+kda_status_t kda_decode_step_scalar_gate(int N, int H, int DK, int DV, kda_dtype_t in_dtype,
+                                         const void* q, const void* k, const void* v,
+                                         const float* gate, const float* beta, float* state,
+                                         float* o, void* stream);
+
+/*
  * Decode of up to L tokens per sequence over a pool of states (continuous
  * batching: the batch's sequences index their states in a shared pool;
  * speculative decoding: L draft tokens are run and the state after each is

@@ -193,6 +193,28 @@ def test_decode_argument_errors(lib):
     assert call(N=0) == OK
 
 
+def test_scalar_gate_argument_errors(lib):
+    # the gate is [B,T,H] floats: an o placed right after a [B,T,H,DK]-sized
+    # alpha region would overlap a per-channel alpha but not the gate
+    B, T, H, DK = 1, 64, 2, 64
+    gate_bytes = B * T * H * 4
+    p = list(P[:8])
+    p[6] = ctypes.c_void_p(P[3].value + gate_bytes)          # o just after the gate
+    args = (B, T, H, DK, 64, 64, 1)
+    assert lib.kda_chunk_prefill(*args, *p, None, 0, None) == SHAPE
+    p[6] = ctypes.c_void_p(P[3].value + gate_bytes - 16)     # o over the gate's end
+    assert lib.kda_chunk_prefill_scalar_gate(*args, *p, None, 0, None) == SHAPE
+    assert lib.kda_chunk_prefill_scalar_gate(1, 64, 2, 96, 64, 64, 1, *P[:8], None, 0, None) == UNSUP
+    assert lib.kda_chunk_prefill_scalar_gate(0, 64, 2, 64, 64, 64, 1, *P[:8], None, 0, None) == OK
+    assert lib.kda_chunk_prefill_varlen_scalar_gate(2, 100, None, 2, 64, 64, 64, 1, *P[:8], None, 0,
+                                                    None) == NULL
+    assert lib.kda_decode_step_scalar_gate(4, 2, 64, 64, 9, *P[:7], None) == DTYPE
+    d = list(P[:7])
+    d[6] = ctypes.c_void_p(P[3].value + 4 * 2 * 4 - 16)       # o over the [4,2] gate
+    assert lib.kda_decode_step_scalar_gate(4, 2, 64, 64, 1, *d, None) == SHAPE
+    assert lib.kda_decode_step_scalar_gate(0, 2, 64, 64, 1, *P[:7], None) == OK
+
+
 def test_decode_pool_argument_errors(lib):
     def call(N=4, L=2, H=2, DK=128, DV=128, dt=1, idx=P[9], ntok=P[10], pool=P[5], P_=8, o=P[6],
              ts=None, ptrs=None):
