@@ -83,6 +83,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the serving variants timed after the steps (profiled runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one plain 512 MiB device-to-device copy before the timed region "
                          "(reference for HBM byte counters)")
@@ -171,35 +173,49 @@ def main():
         torch.cuda.synchronize()
         return ev[0].elapsed_time(ev[1]) / reps * 1e3   # us per call
 
-    # decode steps back to back (no prefill in between: the previous step's
-    # writes are not drained while HBM idles)
-    dec_b2b_us = time_call(lambda: kda.decode_step(dq, dk_, dv_, da, db, dstate, do))
-    snaps = torch.empty((B, T // (64 * 16), H, D, D), device=dev, dtype=torch.float32)
-    snap_us = time_call(lambda: kda.chunk_prefill_snapshots(
-        pq, pk, pv, pa, pb, 16, None, True, 64, po, pst, snaps, pws))
-    del snaps
-    pg = pa[..., 0].contiguous()   # one gate per token and head (Gated DeltaNet)
-    gate_us = time_call(lambda: kda.chunk_prefill(pq, pk, pv, pg, pb, None, True, 64, po, pst, pws))
-    del pg
-    P = 2 * ND
-    gen_p = torch.Generator()
-    gen_p.manual_seed(I.SEED + 5)
-    slots = torch.randperm(P, generator=gen_p)[:ND].to(torch.int32).to(dev)
-    pool = torch.zeros((P, H, D, D), device=dev, dtype=torch.float32)
-    pool[slots.long()] = dstate
-    pool1_us = time_call(lambda: kda.decode_pool(dq[:, None], dk_[:, None], dv_[:, None],
-                                                 da[:, None], db[:, None], pool, slots,
-                                                 out=do[:, None]))
-    L4 = 4
-    rq, rk, rv = (x[:, None].expand(ND, L4, H, D).contiguous() for x in (dq, dk_, dv_))
-    ra = da[:, None].expand(ND, L4, H, D).contiguous()
-    rb = db[:, None].expand(ND, L4, H).contiguous()
-    o4 = torch.empty((ND, L4, H, D), device=dev, dtype=torch.float32)
-    pool4_us = time_call(lambda: kda.decode_pool(rq, rk, rv, ra, rb, pool, slots, out=o4))
-    del pool, rq, rk, rv, ra, rb, o4
+    dec_bytes = decode_algorithmic_bytes(ND, H, D, D)
+    variants = None
+    if not args.no_variants:
+        hbm = lambda us: dec_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS  # noqa: E731
+        # decode steps back to back (no prefill in between: the previous
+        # step's writes are not drained while HBM idles)
+        b2b_us = time_call(lambda: kda.decode_step(dq, dk_, dv_, da, db, dstate, do))
+        snaps = torch.empty((B, T // (64 * 16), H, D, D), device=dev, dtype=torch.float32)
+        snap_us = time_call(lambda: kda.chunk_prefill_snapshots(
+            pq, pk, pv, pa, pb, 16, None, True, 64, po, pst, snaps, pws))
+        del snaps
+        pg = pa[..., 0].contiguous()   # one gate per token and head (Gated DeltaNet)
+        gate_us = time_call(lambda: kda.chunk_prefill(pq, pk, pv, pg, pb, None, True, 64, po, pst,
+                                                      pws))
+        del pg
+        P = 2 * ND
+        gen_p = torch.Generator()
+        gen_p.manual_seed(I.SEED + 5)
+        slots = torch.randperm(P, generator=gen_p)[:ND].to(torch.int32).to(dev)
+        pool = torch.zeros((P, H, D, D), device=dev, dtype=torch.float32)
+        pool[slots.long()] = dstate
+        pool1_us = time_call(lambda: kda.decode_pool(dq[:, None], dk_[:, None], dv_[:, None],
+                                                     da[:, None], db[:, None], pool, slots,
+                                                     out=do[:, None]))
+        L4 = 4
+        rq, rk, rv = (x[:, None].expand(ND, L4, H, D).contiguous() for x in (dq, dk_, dv_))
+        ra = da[:, None].expand(ND, L4, H, D).contiguous()
+        rb = db[:, None].expand(ND, L4, H).contiguous()
+        o4 = torch.empty((ND, L4, H, D), device=dev, dtype=torch.float32)
+        pool4_us = time_call(lambda: kda.decode_pool(rq, rk, rv, ra, rb, pool, slots, out=o4))
+        del pool, rq, rk, rv, ra, rb, o4
+        variants = {
+            "decode_back_to_back_us_per_step": b2b_us,
+            "decode_back_to_back_hbm_frac": hbm(b2b_us),
+            "prefill_with_snapshots_every_1024_tokens_us": snap_us,
+            "prefill_scalar_gate_us": gate_us,
+            "decode_pool_512_slots_L1_us": pool1_us,
+            "decode_pool_512_slots_L1_hbm_frac": hbm(pool1_us),
+            "decode_pool_512_slots_L4_us": pool4_us,
+            "decode_pool_512_slots_L4_us_per_token": pool4_us / L4,
+        }
 
     pre_bytes = prefill_algorithmic_bytes(T, H, D, D, False, True)
-    dec_bytes = decode_algorithmic_bytes(ND, H, D, D)
     pre_gbs = pre_bytes / (pre_ms * 1e-3) / 1e9
     dec_gbs = dec_bytes / (dec_ms * 1e-3) / 1e9
     pre_tflops = prefill_algorithmic_flops(T, H, D, D) / (pre_ms * 1e-3) / 1e12
@@ -266,16 +282,7 @@ def main():
             "algorithmic_tflops": pre_tflops,
             "mfma_frac_algorithmic": pre_tflops / BF16_MFMA_PEAK_TFLOPS,
         },
-        "decode_back_to_back_us_per_step": dec_b2b_us,
-        "decode_back_to_back_hbm_frac": dec_bytes / (dec_b2b_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
-        "serving_variants": {
-            "prefill_with_snapshots_every_1024_tokens_us": snap_us,
-            "prefill_scalar_gate_us": gate_us,
-            "decode_pool_512_slots_L1_us": pool1_us,
-            "decode_pool_512_slots_L1_hbm_frac": dec_bytes / (pool1_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
-            "decode_pool_512_slots_L4_us": pool4_us,
-            "decode_pool_512_slots_L4_us_per_token": pool4_us / L4,
-        },
+        "serving_variants": variants,
         "roofline_decode": {
             "bound": "hbm",
             "kernel": "kda_decode_kernel",
