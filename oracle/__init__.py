@@ -11,6 +11,7 @@ from .kda_oracle import (  # noqa: F401
     kda_recurrent_varlen,
     kda_recurrent_snapshots,
     gdn_recurrent,
+    kda_backward,
     kda_decode_step,
     kda_decode_pool,
     kda_chunked,

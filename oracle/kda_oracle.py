@@ -52,6 +52,7 @@ __all__ = [
     "kda_recurrent_varlen",
     "kda_recurrent_snapshots",
     "gdn_recurrent",
+    "kda_backward",
     "kda_decode_step",
     "kda_decode_pool",
     "kda_chunked",
@@ -129,6 +130,57 @@ def gdn_recurrent(q, k, v, gate, beta, S0=None):
         S = S + k[:, t, :, :, None] * (beta[:, t, :, None] * (v[:, t] - pred))[..., None, :]
         o[:, t] = np.einsum("bhkv,bhk->bhv", S, q[:, t])
     return o, S
+
+
+def kda_backward(q, k, v, alpha, beta, S0, do, dST=None):
+    """Gradients of L = sum(o * do) + sum(S_T * dST) through the token
+    recurrence (the chunk algorithm was designed for training as well
+    ([NEWS] section "Kimi Linearがより賢いRecurrent Memoryを使う方法"); its
+    gradient is that of the recurrence it regroups).
+
+    Shapes as in kda_recurrent; do [B,T,H,DV]; dST [B,H,DK,DV] or None;
+    S0 [B,H,DK,DV] or None.  Returns (dq, dk, dv, dalpha, dbeta, dS0), fp64.
+
+    Reverse mode of each token's steps, written out.  Forward, per token:
+        St = Diag(a) S;  p = St^T k;  u = b (v - p);  S' = St + k u^T;  o = S'^T q.
+    With G the adjoint of S' (it includes o's term q do^T):
+        dq = S' do;  du = G^T k;  dv = b du;  db = du . (v - p);  dp = -b du;
+        dSt = G + k dp^T;  dk = G u + St dp;  da = rowsum(dSt * S);  G_prev = Diag(a) dSt.
+    The forward states are recomputed and kept for the whole sequence.
+    """
+    q, k, v, beta, do = _f64(q), _f64(k), _f64(v), _f64(beta), _f64(do)
+    a = _check_alpha(alpha)
+    B, T, H, DK = q.shape
+    DV = v.shape[-1]
+    S = np.zeros((B, H, DK, DV)) if S0 is None else _f64(S0).copy()
+    states = np.zeros((T + 1, B, H, DK, DV))
+    states[0] = S
+    for t in range(T):
+        St = a[:, t, ..., None] * S
+        p = np.einsum("bhkv,bhk->bhv", St, k[:, t])
+        u = beta[:, t, :, None] * (v[:, t] - p)
+        S = St + k[:, t, ..., None] * u[..., None, :]
+        states[t + 1] = S
+    G = np.zeros((B, H, DK, DV)) if dST is None else _f64(dST).copy()
+    dq, dk, da = np.zeros_like(q), np.zeros_like(k), np.zeros_like(a)
+    dv, db = np.zeros_like(v), np.zeros_like(beta)
+    for t in range(T - 1, -1, -1):
+        Sp = states[t]                                   # state before token t
+        St = a[:, t, ..., None] * Sp
+        p = np.einsum("bhkv,bhk->bhv", St, k[:, t])
+        u = beta[:, t, :, None] * (v[:, t] - p)
+        Sn = states[t + 1]
+        G = G + q[:, t, ..., None] * do[:, t, :, :][..., None, :]   # o_t = S'^T q_t
+        dq[:, t] = np.einsum("bhkv,bhv->bhk", Sn, do[:, t])
+        du = np.einsum("bhkv,bhk->bhv", G, k[:, t])
+        dv[:, t] = beta[:, t, :, None] * du
+        db[:, t] = np.sum(du * (v[:, t] - p), axis=-1)
+        dp = -beta[:, t, :, None] * du
+        dSt = G + k[:, t, ..., None] * dp[..., None, :]
+        dk[:, t] = np.einsum("bhkv,bhv->bhk", G, u) + np.einsum("bhkv,bhv->bhk", St, dp)
+        da[:, t] = np.sum(dSt * Sp, axis=-1)
+        G = a[:, t, ..., None] * dSt
+    return dq, dk, dv, da, db, G
 
 
 def kda_recurrent_varlen(q, k, v, alpha, beta, cu_seqlens, S0=None):

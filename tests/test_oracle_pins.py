@@ -17,8 +17,8 @@ from fractions import Fraction
 import numpy as np
 import pytest
 
-from oracle import (gdn_recurrent, kda_chunked, kda_decode_pool, kda_decode_step, kda_recurrent,
-                    kda_recurrent_snapshots, kda_recurrent_varlen, max_rel_err)
+from oracle import (gdn_recurrent, kda_backward, kda_chunked, kda_decode_pool, kda_decode_step,
+                    kda_recurrent, kda_recurrent_snapshots, kda_recurrent_varlen, max_rel_err)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -535,6 +535,87 @@ def test_p12_tokens_past_count_are_ignored_and_duplicates_rejected():
     np.testing.assert_array_equal(r1[1][2], pool[2])       # zero tokens: slot untouched
     with pytest.raises(ValueError):
         kda_decode_pool(q, k, v, a, b, pool, [0, 1, 0])
+
+
+# ------------------------------------------------------------------ P13 ---
+def _torch_loss_grads(q, k, v, a, b, S0, do, dST):
+    """fp64 torch autograd through a recurrence written with torch ops (the
+    dense transition form, independent of the oracle's code)."""
+    import torch
+
+    t = {n: torch.tensor(x, dtype=torch.float64, requires_grad=True)
+         for n, x in dict(q=q, k=k, v=v, a=a, b=b, S0=S0).items()}
+    B, T, H, DK = q.shape
+    S = t["S0"]
+    eye = torch.eye(DK, dtype=torch.float64)
+    loss = 0.0
+    for s_ in range(T):
+        kt = t["k"][:, s_]                                            # [B,H,DK]
+        M = eye - t["b"][:, s_, :, None, None] * kt[..., :, None] * kt[..., None, :]
+        S = M @ (t["a"][:, s_, ..., None] * S) + \
+            t["b"][:, s_, :, None, None] * kt[..., :, None] * t["v"][:, s_][..., None, :]
+        o = torch.einsum("bhkv,bhk->bhv", S, t["q"][:, s_])
+        loss = loss + (o * torch.tensor(do[:, s_])).sum()
+    loss = loss + (S * torch.tensor(dST)).sum()
+    loss.backward()
+    return [t[n].grad.numpy() for n in ("q", "k", "v", "a", "b", "S0")]
+
+
+def test_p13_backward_matches_torch_autograd():
+    """The hand-written reverse mode against fp64 autograd of the dense
+    transition form S_t = (I - b k k^T) Diag(a) S + b k v^T."""
+    rng = np.random.default_rng(51)
+    q, k, v, a, b, S0 = rand_inputs(rng, 2, 23, 2, 5, 4)
+    do = rng.standard_normal(v.shape)
+    dST = rng.standard_normal(S0.shape)
+    got = kda_backward(q, k, v, a, b, S0, do, dST)
+    ref = _torch_loss_grads(q, k, v, a, b, S0, do, dST)
+    for g, r, name in zip(got, ref, ("dq", "dk", "dv", "dalpha", "dbeta", "dS0")):
+        assert max_rel_err(g, r) < 1e-12, name
+
+
+def test_p13_backward_finite_differences():
+    """Central differences of L = sum(o do) + sum(S_T dST) on sampled
+    coordinates of every input."""
+    rng = np.random.default_rng(52)
+    q, k, v, a, b, S0 = rand_inputs(rng, 1, 9, 1, 4, 3)
+    do = rng.standard_normal(v.shape)
+    dST = rng.standard_normal(S0.shape)
+
+    def loss(q_, k_, v_, a_, b_, S0_):
+        o, S = kda_recurrent(q_, k_, v_, a_, b_, S0_)
+        return float(np.sum(o * do) + np.sum(S * dST))
+
+    grads = kda_backward(q, k, v, a, b, S0, do, dST)
+    args = [q, k, v, a, b, S0]
+    h = 1e-6
+    for i, (x, g) in enumerate(zip(args, grads)):
+        for idx in list(np.ndindex(x.shape))[:: max(1, x.size // 7)]:
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            ap, am = list(args), list(args)
+            ap[i], am[i] = xp, xm
+            fd = (loss(*ap) - loss(*am)) / (2 * h)
+            assert abs(fd - g[idx]) < 1e-6 * max(1.0, abs(fd)), (i, idx, fd, g[idx])
+
+
+def test_p13_backward_beta_zero_closed_form():
+    """beta = 0: v and k do not reach the output (dv = dk = 0, dbeta from the
+    error term), and dS0 = sum_t Diag(prod_{s<=t} a_s) q_t do_t^T + Diag(prod a) dST."""
+    rng = np.random.default_rng(53)
+    q, k, v, a, b, S0 = rand_inputs(rng, 1, 11, 2, 5, 3)
+    b[:] = 0.0
+    do = rng.standard_normal(v.shape)
+    dST = rng.standard_normal(S0.shape)
+    dq, dk, dv, da, db, dS0 = kda_backward(q, k, v, a, b, S0, do, dST)
+    assert np.all(dv == 0) and np.all(dk == 0)
+    cum = np.cumprod(a, axis=1)                                   # [B,T,H,DK]
+    expect = np.einsum("bthk,bthv->bhkv", cum * q, do) + cum[:, -1][..., None] * dST
+    np.testing.assert_allclose(dS0, expect, rtol=1e-12, atol=1e-12)
+    # dq_t = S_t do_t with S_t = Diag(prod a) S0
+    np.testing.assert_allclose(dq, np.einsum("bthk,bhkv,bthv->bthk", cum, S0, do), rtol=1e-12,
+                               atol=1e-12)
 
 
 def test_alpha_domain_is_checked():
