@@ -204,6 +204,13 @@ def main():
         o4 = torch.empty((ND, L4, H, D), device=dev, dtype=torch.float32)
         pool4_us = time_call(lambda: kda.decode_pool(rq, rk, rv, ra, rb, pool, slots, out=o4))
         del pool, rq, rk, rv, ra, rb, o4
+        # backward pass (training) of the same prefill workload
+        d_o = torch.randn((B, T, H, D), device=dev, dtype=torch.float32)
+        bws = torch.empty(kda.lib().kda_chunk_backward_workspace_size(B, T, H, D, D, 64),
+                          device=dev, dtype=torch.uint8)
+        bwd_us = time_call(lambda: kda.chunk_backward(pq, pk, pv, pa, pb, d_o, workspace=bws),
+                           reps=3)
+        del d_o, bws
         variants = {
             "decode_back_to_back_us_per_step": b2b_us,
             "decode_back_to_back_hbm_frac": hbm(b2b_us),
@@ -213,6 +220,7 @@ def main():
             "decode_pool_512_slots_L1_hbm_frac": hbm(pool1_us),
             "decode_pool_512_slots_L4_us": pool4_us,
             "decode_pool_512_slots_L4_us_per_token": pool4_us / L4,
+            "backward_b1_h32_t8192_us": bwd_us,
         }
 
     pre_bytes = prefill_algorithmic_bytes(T, H, D, D, False, True)

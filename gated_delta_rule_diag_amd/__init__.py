@@ -8,6 +8,8 @@ with a thin ctypes binding:
         -> (o, final_state, snapshots)
     chunk_prefill_varlen(q, k, v, alpha, beta, cu_seqlens, initial_state=None)
     decode_step(q, k, v, alpha, beta, state) -> o        (state updated in place)
+    chunk_backward(q, k, v, alpha, beta, d_o, initial_state=None, d_final_state=None)
+        -> (dq, dk, dv, dalpha, dbeta, d_initial_state)
     decode_pool(q, k, v, alpha, beta, state_pool, state_idx=None, num_tokens=None)
         -> (o, token_states)                             (L tokens per sequence, pooled states)
 
@@ -16,7 +18,7 @@ The binding is imported lazily so that ``gated_delta_rule_diag_amd.inputs``
 """
 
 __all__ = ["chunk_prefill", "chunk_prefill_snapshots", "chunk_prefill_varlen", "decode_step",
-           "decode_pool", "KDAError"]
+           "decode_pool", "chunk_backward", "KDAError"]
 
 
 def __getattr__(name):

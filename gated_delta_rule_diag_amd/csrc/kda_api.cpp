@@ -391,4 +391,122 @@ kda_status_t kda_decode_pool(int N, int L, int H, int DK, int DV, kda_dtype_t in
   return ok();
 }
 
+namespace {
+
+// Byte offsets of the backward workspace: [forward prefill workspace, later the
+// per-slab partial sums | o of the forward | snapshots | token-state scratch].
+struct BwdLayout {
+  size_t fwd_or_part, o, snaps, scratch, total;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+BwdLayout bwd_layout(int B, int T, int H, int DK, int DV) {
+  BwdLayout L{};
+  const size_t rows = size_t(B) * T * H, nslab = size_t(DV) / 16;
+  const size_t pw = kda::prefill_workspace_bytes(B, int64_t(B) * T, H, DK, DV, false);
+  const size_t part = (3 * nslab * rows * DK + nslab * rows) * 4;
+  L.fwd_or_part = 0;
+  L.o = align256(pw > part ? pw : part);
+  L.snaps = L.o + align256(rows * DV * 4);
+  L.scratch = L.snaps + align256(size_t(B) * (T / 64) * H * DK * DV * 4);
+  L.total = L.scratch + align256(kda::backward_scratch_bytes(B, H, DK, DV));
+  return L;
+}
+
+}  // namespace
+
+size_t kda_chunk_backward_workspace_size(int B, int T, int H, int DK, int DV, int chunk) {
+  if (B <= 0 || T <= 0 || H <= 0 || !dims_ok(DK) || !dims_ok(DV) || chunk != 64) return 0;
+  return bwd_layout(B, T, H, DK, DV).total;
+}
+
+kda_status_t kda_chunk_backward(int B, int T, int H, int DK, int DV, int chunk,
+                                kda_dtype_t in_dtype, const void* q, const void* k,
+                                const void* v, const float* alpha, const float* beta,
+                                const float* state_in, const float* d_o,
+                                const float* d_state_out, float* dq, float* dk, float* dv,
+                                float* dalpha, float* dbeta, float* d_state_in, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (B < 0 || T < 0 || H < 0) return fail(KDA_ERR_SHAPE, "negative size (B=%d T=%d H=%d)", B, T, H);
+  if (!dims_ok(DK) || !dims_ok(DV))
+    return fail(KDA_ERR_UNSUPPORTED, "DK=%d DV=%d: only 64 and 128 are supported", DK, DV);
+  if (chunk != 64) return fail(KDA_ERR_UNSUPPORTED, "chunk=%d: only 64 is supported", chunk);
+  if (in_dtype != KDA_F32 && in_dtype != KDA_BF16)
+    return fail(KDA_ERR_DTYPE, "unknown in_dtype %d", (int)in_dtype);
+  if (int64_t(B) * T * H > (int64_t(1) << 31) / 128 || int64_t(B) * H > (int64_t(1) << 24))
+    return fail(KDA_ERR_UNSUPPORTED, "too large: B*T*H=%lld", (long long)B * T * H);
+  if (B == 0 || T == 0 || H == 0) return ok();
+  const void* need[] = {q, k, v, alpha, beta, d_o, dq, dk, dv, dalpha, dbeta};
+  for (const void* x : need)
+    if (!x)
+      return fail(KDA_ERR_NULL,
+                  "q, k, v, alpha, beta, d_o, dq, dk, dv, dalpha and dbeta must be non-NULL");
+  const size_t esz = in_dtype == KDA_BF16 ? 2 : 4;
+  const size_t rows = size_t(B) * T * H, ns = size_t(B) * H * DK * DV * 4;
+  const void* in[] = {q, k, v, alpha, beta, state_in, d_o, d_state_out};
+  const size_t in_b[] = {rows * DK * esz, rows * DK * esz, rows * DV * esz, rows * DK * 4,
+                         rows * 4, ns, rows * DV * 4, ns};
+  const char* in_n[] = {"q", "k", "v", "alpha", "beta", "state_in", "d_o", "d_state_out"};
+  const void* out[] = {dq, dk, dv, dalpha, dbeta, d_state_in};
+  const size_t out_b[] = {rows * DK * 4, rows * DK * 4, rows * DV * 4, rows * DK * 4, rows * 4, ns};
+  const char* out_n[] = {"dq", "dk", "dv", "dalpha", "dbeta", "d_state_in"};
+  for (int i = 0; i < 8; ++i)
+    if (in[i] && !aligned16(in[i])) return fail(KDA_ERR_ALIGN, "%s is not 16-byte aligned", in_n[i]);
+  for (int i = 0; i < 6; ++i)
+    if (out[i] && !aligned16(out[i]))
+      return fail(KDA_ERR_ALIGN, "%s is not 16-byte aligned", out_n[i]);
+  for (int i = 0; i < 6; ++i) {
+    for (int j = 0; j < 8; ++j)
+      if (overlaps(out[i], out_b[i], in[j], in_b[j]))
+        return fail(KDA_ERR_SHAPE, "%s overlaps %s", out_n[i], in_n[j]);
+    for (int j = i + 1; j < 6; ++j)
+      if (overlaps(out[i], out_b[i], out[j], out_b[j]))
+        return fail(KDA_ERR_SHAPE, "%s overlaps %s", out_n[i], out_n[j]);
+  }
+  const BwdLayout L = bwd_layout(B, T, H, DK, DV);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", L.total,
+                workspace ? workspace_bytes : size_t(0));
+  if (!aligned16(workspace)) return fail(KDA_ERR_ALIGN, "workspace is not 16-byte aligned");
+  for (int j = 0; j < 8; ++j)
+    if (overlaps(workspace, L.total, in[j], in_b[j]))
+      return fail(KDA_ERR_SHAPE, "workspace overlaps %s", in_n[j]);
+  for (int j = 0; j < 6; ++j)
+    if (overlaps(workspace, L.total, out[j], out_b[j]))
+      return fail(KDA_ERR_SHAPE, "workspace overlaps %s", out_n[j]);
+
+  char* ws = static_cast<char*>(workspace);
+  // 1. forward with a snapshot after every chunk
+  kda::PrefillArgs f{};
+  f.N = B; f.T_fixed = T; f.cu_seqlens = nullptr; f.T_total = int64_t(B) * T;
+  f.H = H; f.DK = DK; f.DV = DV; f.in_bf16 = in_dtype == KDA_BF16;
+  f.q = q; f.k = k; f.v = v; f.alpha = alpha; f.beta = beta;
+  f.state_in = state_in; f.o = reinterpret_cast<float*>(ws + L.o); f.state_out = nullptr;
+  f.workspace = ws + L.fwd_or_part; f.workspace_bytes = L.o;
+  f.snapshots = T >= 64 ? reinterpret_cast<float*>(ws + L.snaps) : nullptr;
+  f.snap_every = 1;
+  const char* msg = nullptr;
+  if (kda::launch_prefill(f, stream, &msg) != 0)
+    return fail(KDA_ERR_HIP, "backward: forward launch failed: %s", msg ? msg : "?");
+  // 2-3. reverse pass and the reduction of the per-slab sums
+  kda::BackwardArgs a{};
+  a.N = B; a.H = H; a.DK = DK; a.DV = DV; a.T = T; a.rows = int64_t(rows);
+  a.in_bf16 = in_dtype == KDA_BF16;
+  a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.state_in = state_in;
+  a.d_o = d_o; a.d_state_out = d_state_out;
+  a.snapshots = reinterpret_cast<const float*>(ws + L.snaps); a.snap_per_seq = T / 64;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.dalpha = dalpha; a.dbeta = dbeta; a.d_state_in = d_state_in;
+  a.scratch = reinterpret_cast<float*>(ws + L.scratch);
+  const size_t nslab = size_t(DV) / 16;
+  float* part = reinterpret_cast<float*>(ws + L.fwd_or_part);
+  a.part_dq = part;
+  a.part_dk = part + nslab * rows * DK;
+  a.part_da = part + 2 * nslab * rows * DK;
+  a.part_db = part + 3 * nslab * rows * DK;
+  if (kda::launch_backward(a, stream, &msg) != 0)
+    return fail(KDA_ERR_HIP, "backward launch failed: %s", msg ? msg : "?");
+  return ok();
+}
+
 }  // extern "C"

@@ -62,10 +62,41 @@ struct PoolDecodeArgs {
   bool alpha_scalar;           // alpha is [N, L, H]
 };
 
+// Backward pass (fixed-length batches, per-channel alpha).
+struct BackwardArgs {
+  int N, H, DK, DV;
+  int64_t T;                   // tokens per sequence
+  int64_t rows;                // N * T * H token rows
+  bool in_bf16;
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* alpha;
+  const float* beta;
+  const float* state_in;       // [N, H, DK, DV] or nullptr
+  const float* d_o;            // [N, T, H, DV]
+  const float* d_state_out;    // [N, H, DK, DV] or nullptr
+  const float* snapshots;      // state after every chunk: [N, snap_per_seq, H, DK, DV]
+  int64_t snap_per_seq;        // T / 64
+  float* dq;                   // [N, T, H, DK]
+  float* dk;
+  float* dv;                   // [N, T, H, DV]
+  float* dalpha;               // [N, T, H, DK]
+  float* dbeta;                // [N, T, H]
+  float* d_state_in;           // [N, H, DK, DV] or nullptr
+  float* scratch;              // backward_scratch_bytes()
+  float* part_dq;              // [DV / 16][rows][DK] each
+  float* part_dk;
+  float* part_da;
+  float* part_db;              // [DV / 16][rows]
+};
+
 // Launchers return 0 on success, else a non-zero code and a static message.
 int launch_prefill(const PrefillArgs& a, void* stream, const char** msg);
 int launch_decode(const DecodeArgs& a, void* stream, const char** msg);
 int launch_decode_pool(const PoolDecodeArgs& a, void* stream, const char** msg);
+int launch_backward(const BackwardArgs& a, void* stream, const char** msg);
+size_t backward_scratch_bytes(int N, int H, int DK, int DV);
 size_t prefill_workspace_bytes(int N, int64_t T_total, int H, int DK, int DV, bool varlen);
 
 }  // namespace kda

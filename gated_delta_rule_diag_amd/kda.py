@@ -36,6 +36,8 @@ EXPORTED = (
     "kda_chunk_prefill_scalar_gate",
     "kda_chunk_prefill_varlen_scalar_gate",
     "kda_decode_step_scalar_gate",
+    "kda_chunk_backward_workspace_size",
+    "kda_chunk_backward",
     "kda_status_string",
     "kda_last_error_message",
 )
@@ -76,6 +78,10 @@ def load_library(path: str = _LIB_PATH) -> ctypes.CDLL:
     lib.kda_chunk_prefill_varlen_scalar_gate.argtypes = list(lib.kda_chunk_prefill_varlen.argtypes)
     lib.kda_decode_step_scalar_gate.restype = i
     lib.kda_decode_step_scalar_gate.argtypes = list(lib.kda_decode_step.argtypes)
+    lib.kda_chunk_backward_workspace_size.restype = sz
+    lib.kda_chunk_backward_workspace_size.argtypes = [i, i, i, i, i, i]
+    lib.kda_chunk_backward.restype = i
+    lib.kda_chunk_backward.argtypes = [i, i, i, i, i, i, i] + [vp] * 15 + [sz, vp]
     lib.kda_decode_pool.restype = i
     lib.kda_decode_pool.argtypes = [i, i, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp, i, vp, vp, vp]
     lib.kda_status_string.restype = ctypes.c_char_p
@@ -318,3 +324,42 @@ def decode_pool(q, k, v, alpha, beta, state_pool, state_idx=None, num_tokens=Non
         N, L, H, DK, DV, dt, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state_idx),
         _ptr(num_tokens), _ptr(state_pool), state_pool.shape[0], _ptr(o), _ptr(ts), _stream(dev)))
     return o, ts
+
+
+def chunk_backward(q, k, v, alpha, beta, d_o, initial_state=None, d_final_state=None,
+                   chunk=64, workspace=None):
+    """Gradients of L = sum(o * d_o) + sum(S_T * d_final_state) for the
+    fixed-length prefill (per-channel alpha).
+
+    Inputs as for :func:`chunk_prefill`; d_o [B,T,H,DV] float32;
+    d_final_state [B,H,DK,DV] float32 or None.
+    Returns (dq, dk, dv, dalpha, dbeta, d_initial_state), all float32.
+    """
+    B, T, H, DK = q.shape
+    DV = v.shape[-1]
+    dt = _in_dtype(q)
+    _need(q, "q", q.dtype)
+    _need(k, "k", q.dtype, (B, T, H, DK))
+    _need(v, "v", q.dtype, (B, T, H, DV))
+    _need(alpha, "alpha", torch.float32, (B, T, H, DK))
+    _need(beta, "beta", torch.float32, (B, T, H))
+    _need(d_o, "d_o", torch.float32, (B, T, H, DV))
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, (B, H, DK, DV))
+    if d_final_state is not None:
+        _need(d_final_state, "d_final_state", torch.float32, (B, H, DK, DV))
+    dev = q.device
+    f32 = dict(device=dev, dtype=torch.float32)
+    dq, dk, dal = (torch.empty((B, T, H, DK), **f32) for _ in range(3))
+    dv = torch.empty((B, T, H, DV), **f32)
+    db = torch.empty((B, T, H), **f32)
+    ds0 = torch.empty((B, H, DK, DV), **f32)
+    wsz = lib().kda_chunk_backward_workspace_size(B, T, H, DK, DV, chunk)
+    if wsz and workspace is None:
+        workspace = torch.empty(wsz, device=dev, dtype=torch.uint8)
+    _check(lib().kda_chunk_backward(
+        B, T, H, DK, DV, chunk, dt, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+        _ptr(initial_state), _ptr(d_o), _ptr(d_final_state), _ptr(dq), _ptr(dk), _ptr(dv),
+        _ptr(dal), _ptr(db), _ptr(ds0), _ptr(workspace),
+        0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(dev)))
+    return dq, dk, dv, dal, db, ds0

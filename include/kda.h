@@ -215,6 +215,33 @@ kda_status_t kda_decode_pool(int N, int L, int H, int DK, int DV, kda_dtype_t in
                              const int32_t* num_tokens, float* state_pool, int pool_size,
                              float* o, float* token_states, void* stream);
 
+/*
+ * Backward pass (training): gradients of L = sum(o * d_o) + sum(S_T * d_state_out)
+ * for a fixed-length prefill with per-channel alpha.  The chunk algorithm is
+ * the training form of the recurrence ("Kimi Linear、独自の土俵でFull Attention
+ * を上回る" (remio.ai), section "Kimi Linearがより賢いRecurrent Memoryを使う方法");
+ * its gradient is that of the token recurrence defined above.
+ *   q, k, v, alpha, beta, state_in   as for kda_chunk_prefill (state_in may be NULL)
+ *   d_o          [B,T,H,DV] float, gradient of o
+ *   d_state_out  [B,H,DK,DV] float or NULL (zero), gradient of the final state
+ *   dq, dk, dalpha [B,T,H,DK], dv [B,T,H,DV], dbeta [B,T,H]  float outputs
+ *   d_state_in   [B,H,DK,DV] float or NULL: gradient of the initial state
+ *   workspace    at least kda_chunk_backward_workspace_size() bytes, 16-byte
+ *                aligned, not overlapping any argument (holds the forward's
+ *                chunk-boundary states, its outputs and per-slab partial sums).
+ * Outputs must not overlap inputs or each other.  The forward is recomputed
+ * (with a state checkpoint per chunk); the reverse pass walks every chunk
+ * backwards from its checkpoint; the result is deterministic.
+ */
+size_t kda_chunk_backward_workspace_size(int B, int T, int H, int DK, int DV, int chunk);
+kda_status_t kda_chunk_backward(int B, int T, int H, int DK, int DV, int chunk,
+                                kda_dtype_t in_dtype, const void* q, const void* k,
+                                const void* v, const float* alpha, const float* beta,
+                                const float* state_in, const float* d_o,
+                                const float* d_state_out, float* dq, float* dk, float* dv,
+                                float* dalpha, float* dbeta, float* d_state_in, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
 const char* kda_status_string(kda_status_t s);
 const char* kda_last_error_message(void);
 

@@ -215,6 +215,40 @@ def test_scalar_gate_argument_errors(lib):
     assert lib.kda_decode_step_scalar_gate(0, 2, 64, 64, 1, *P[:7], None) == OK
 
 
+def test_backward_argument_errors(lib):
+    # B=1, T=64, H=2, d=64 (f32): rows = 128
+    need = lib.kda_chunk_backward_workspace_size(1, 64, 2, 64, 64, 64)
+    # partial sums (3 * 4 slabs * 128 rows * 64 + 4 * 128) floats, o of the
+    # forward, one snapshot per sequence-head, 512 KiB token-state scratch per workgroup
+    part = (3 * 4 * 128 * 64 + 4 * 128) * 4
+    al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    assert need == al(part) + al(128 * 64 * 4) + al(2 * 64 * 64 * 4) + al(8 * 64 * 128 * 8 * 4)
+    assert lib.kda_chunk_backward_workspace_size(1, 64, 2, 96, 64, 64) == 0
+    big = ctypes.c_void_p(0x40000000)
+    Q = [ctypes.c_void_p(0x100000 * (i + 1)) for i in range(14)]
+
+    def call(T=64, DK=64, dt=0, ptrs=None, ws=big, wsb=need):
+        return lib.kda_chunk_backward(1, T, 2, DK, 64, 64, dt, *(ptrs or Q), ws, wsb, None)
+
+    assert call(DK=32) == UNSUP
+    assert call(dt=4) == DTYPE
+    assert call(T=-1) == SHAPE
+    p = list(Q)
+    p[5] = None                                    # state_in may be NULL ...
+    p[0] = None                                    # ... q may not
+    assert call(ptrs=p) == NULL
+    p = list(Q)
+    p[9] = ctypes.c_void_p(Q[9].value + 8)         # dk misaligned
+    assert call(ptrs=p) == ALIGN
+    p = list(Q)
+    p[8] = ctypes.c_void_p(Q[6].value + 64)        # dq over d_o
+    assert call(ptrs=p) == SHAPE
+    assert call(ws=None) == WS
+    assert call(wsb=need - 1) == WS
+    assert call(ws=ctypes.c_void_p(Q[0].value)) == SHAPE   # workspace over q
+    assert call(T=0) == OK
+
+
 def test_decode_pool_argument_errors(lib):
     def call(N=4, L=2, H=2, DK=128, DV=128, dt=1, idx=P[9], ntok=P[10], pool=P[5], P_=8, o=P[6],
              ts=None, ptrs=None):

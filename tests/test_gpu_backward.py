@@ -1,0 +1,78 @@
+"""GPU parity of the backward pass against the fp64 oracle's reverse mode:
+every gradient (q, k, v, alpha, beta, initial state) with and without an
+initial state and a final-state gradient, both forward forms feeding the
+checkpoints, ragged last chunks, and the 8192-token 32-head shape."""
+
+import numpy as np
+import pytest
+import torch
+
+from gated_delta_rule_diag_amd import inputs as I
+from gated_delta_rule_diag_amd import kda
+from kda_testlib import TOL, dev, flush, host, random_state, tdtype
+from oracle import kda_backward, max_rel_err
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("dq", "dk", "dv", "dalpha", "dbeta", "dS0")
+
+
+def run_case(B, T, H, dk, dv, dt, c, with_state, heads=None):
+    q, k, v, a, b = I.batch_inputs(c, B, T, H, dk, dv, dt)
+    rng = np.random.default_rng(c)
+    do = rng.standard_normal((B, T, H, dv)).astype(np.float32)
+    S0 = random_state(rng, (B, H, dk, dv)) if with_state else None
+    dST = random_state(rng, (B, H, dk, dv)) if with_state else None
+    td = tdtype(dt)
+    got = kda.chunk_backward(dev(q, td), dev(k, td), dev(v, td), dev(a), dev(b), dev(do),
+                             None if S0 is None else dev(S0), None if dST is None else dev(dST))
+    torch.cuda.synchronize()
+    got = [host(g) for g in got]
+    if heads is not None:
+        sel = lambda x: x[:, :, heads]  # noqa: E731
+        ref = kda_backward(sel(q), sel(k), sel(v), sel(a), b[:, :, heads], None, sel(do), None)
+        got = [g[:, :, heads] if g.ndim == 4 and g.shape[1] == T else
+               (g[:, :, heads] if g.ndim == 3 else g[:, heads]) for g in got]
+    else:
+        ref = kda_backward(q, k, v, a, b, S0, do, dST)
+    errs = {n: max_rel_err(g, r) for n, g, r in zip(NAMES, got, ref)}
+    flush("    " + " ".join(f"{n}={e:.1e}" for n, e in errs.items()))
+    return errs
+
+
+@pytest.mark.parametrize("path", ["fused", "split"])
+@pytest.mark.parametrize("T", [1, 37, 64, 65, 200])
+@pytest.mark.parametrize("dt,d", [("bf16", 128), ("f32", 64)])
+def test_backward_matches_oracle(dt, d, T, path, monkeypatch):
+    monkeypatch.setenv("KDA_PREFILL_PATH", path)
+    flush(f"[backward] B=2 T={T} H=3 d={d} {dt} path={path}")
+    errs = run_case(2, T, 3, d, d, dt, 700 + T, with_state=True)
+    assert max(errs.values()) <= TOL[dt], errs
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 64), (64, 128)])
+def test_backward_rectangular_zero_state(dk, dv):
+    flush(f"[backward] B=1 T=130 H=2 DK={dk} DV={dv} bf16, zero state, no final-state gradient")
+    errs = run_case(1, 130, 2, dk, dv, "bf16", 710, with_state=False)
+    assert max(errs.values()) <= TOL["bf16"], errs
+
+
+def test_backward_is_deterministic():
+    B, T, H, D = 1, 300, 4, 128
+    flush(f"[backward] determinism B={B} T={T} H={H} d={D}")
+    q, k, v, a, b = I.batch_inputs(720, B, T, H, D, D, "bf16")
+    do = np.random.default_rng(1).standard_normal((B, T, H, D)).astype(np.float32)
+    bf = torch.bfloat16
+    x = (dev(q, bf), dev(k, bf), dev(v, bf), dev(a), dev(b), dev(do))
+    g1 = kda.chunk_backward(*x)
+    g2 = kda.chunk_backward(*x)
+    torch.cuda.synchronize()
+    for u, w in zip(g1, g2):
+        assert torch.equal(u, w)
+
+
+def test_backward_b1_h32_t8192_head_subset():
+    """The benchmark prefill shape; heads {0, 31} against the oracle."""
+    flush("[backward] B=1 T=8192 H=32 d=128 bf16, heads 0 and 31")
+    errs = run_case(1, 8192, 32, 128, 128, "bf16", 730, with_state=False, heads=[0, 31])
+    assert max(errs.values()) <= TOL["bf16"], errs
