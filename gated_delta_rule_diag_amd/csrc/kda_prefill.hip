@@ -1634,7 +1634,12 @@ void launch_staged_t(const Params& base, int64_t T, int nsub, hipStream_t st, ch
     hipLaunchKernelGGL((kda_stage_kernel<DK, DV, BF>), dim3(unsigned(items < cus ? items : cus)),
                        dim3(Lay<DK>::NT), 0, st, sp);
     const unsigned nb = unsigned(sp.pairs * sp.nslab);
-    if (nsub == 2) {
+    if (nsub == 4) {
+      if (sp.snap)
+        hipLaunchKernelGGL((kda_chain_kernel<DK, 4, BF, true>), dim3(nb), dim3(Lay<DK>::NT), 0, st, sp);
+      else
+        hipLaunchKernelGGL((kda_chain_kernel<DK, 4, BF, false>), dim3(nb), dim3(Lay<DK>::NT), 0, st, sp);
+    } else if (nsub == 2) {
       if (sp.snap)
         hipLaunchKernelGGL((kda_chain_kernel<DK, 2, BF, true>), dim3(nb), dim3(Lay<DK>::NT), 0, st, sp);
       else
@@ -1659,7 +1664,7 @@ void launch_staged(const Params& base, int64_t T, int nsub, hipStream_t st, char
 int staged_nsub(int64_t pairs, int DV) {
   if (const char* e = getenv("KDA_PREFILL_NSUB")) {
     const int v = atoi(e);
-    if (v == 1 || v == 2) return v;
+    if ((v == 1 || v == 2 || v == 4) && 16 * v <= DV) return v;
   }
   (void)pairs;
   (void)DV;

@@ -219,10 +219,11 @@ def test_backward_argument_errors(lib):
     # B=1, T=64, H=2, d=64 (f32): rows = 128
     need = lib.kda_chunk_backward_workspace_size(1, 64, 2, 64, 64, 64)
     # partial sums (3 * 4 slabs * 128 rows * 64 + 4 * 128) floats, o of the
-    # forward, one snapshot per sequence-head, 512 KiB token-state scratch per workgroup
+    # forward, one snapshot per sequence-head, and per workgroup (8 of them) the
+    # token states of two chunks: 2 * 64 tokens * 64 rows * 16 columns floats
     part = (3 * 4 * 128 * 64 + 4 * 128) * 4
     al = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    assert need == al(part) + al(128 * 64 * 4) + al(2 * 64 * 64 * 4) + al(8 * 64 * 128 * 8 * 4)
+    assert need == al(part) + al(128 * 64 * 4) + al(2 * 64 * 64 * 4) + al(8 * 2 * 64 * 64 * 16 * 4)
     assert lib.kda_chunk_backward_workspace_size(1, 64, 2, 96, 64, 64) == 0
     big = ctypes.c_void_p(0x40000000)
     Q = [ctypes.c_void_p(0x100000 * (i + 1)) for i in range(14)]
