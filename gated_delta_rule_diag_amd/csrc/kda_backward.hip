@@ -346,22 +346,26 @@ __global__ __launch_bounds__(DK / kRPT * kTPR) void kda_bwd_kernel(BackwardArgs 
   if (p.d_state_in) st_slab(p.d_state_in + state_off, DV, G);
 }
 
-// dq, dk, dalpha (per row) and dbeta: sums of the per-slab partials.
+// dq, dk, dalpha (per row) and dbeta: sums of the per-slab partials.  A
+// thread adds four consecutive elements (rows * DK is a multiple of 64).
 template <int DK>
 __global__ __launch_bounds__(256) void kda_bwd_reduce_kernel(BackwardArgs p) {
-  const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;   // (token row, key row)
+  const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
   const int64_t total = p.rows * DK;
   const int nslab = p.DV / kVS;
-  if (idx < total) {
-    float q = 0.f, k = 0.f, a = 0.f;
+  if (4 * idx < total) {
+    float4 q = make_float4(0.f, 0.f, 0.f, 0.f), k = q, a = q;
     for (int s = 0; s < nslab; ++s) {
-      q += p.part_dq[s * total + idx];
-      k += p.part_dk[s * total + idx];
-      a += p.part_da[s * total + idx];
+      const float4 x = reinterpret_cast<const float4*>(p.part_dq + s * total)[idx];
+      const float4 y = reinterpret_cast<const float4*>(p.part_dk + s * total)[idx];
+      const float4 z = reinterpret_cast<const float4*>(p.part_da + s * total)[idx];
+      q.x += x.x; q.y += x.y; q.z += x.z; q.w += x.w;
+      k.x += y.x; k.y += y.y; k.z += y.z; k.w += y.w;
+      a.x += z.x; a.y += z.y; a.z += z.z; a.w += z.w;
     }
-    p.dq[idx] = q;
-    p.dk[idx] = k;
-    p.dalpha[idx] = a;
+    reinterpret_cast<float4*>(p.dq)[idx] = q;
+    reinterpret_cast<float4*>(p.dk)[idx] = k;
+    reinterpret_cast<float4*>(p.dalpha)[idx] = a;
   }
   if (idx < p.rows) {
     float b = 0.f;
@@ -374,8 +378,9 @@ template <int DK, bool BF16>
 void launch_bwd_t(const BackwardArgs& a, hipStream_t st) {
   const unsigned nb = unsigned(int64_t(a.N) * a.H * (a.DV / kVS));
   hipLaunchKernelGGL((kda_bwd_kernel<DK, BF16>), dim3(nb), dim3(DK / kRPT * kTPR), 0, st, a);
-  const int64_t total = a.rows * DK;
-  hipLaunchKernelGGL((kda_bwd_reduce_kernel<DK>), dim3(unsigned((total + 255) / 256)), dim3(256),
+  // threads: max(rows * DK / 4, rows) = rows * DK / 4 (DK >= 64)
+  const int64_t threads = a.rows * DK / 4;
+  hipLaunchKernelGGL((kda_bwd_reduce_kernel<DK>), dim3(unsigned((threads + 255) / 256)), dim3(256),
                      0, st, a);
 }
 
