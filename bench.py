@@ -204,6 +204,22 @@ def main():
         o4 = torch.empty((ND, L4, H, D), device=dev, dtype=torch.float32)
         pool4_us = time_call(lambda: kda.decode_pool(rq, rk, rv, ra, rb, pool, slots, out=o4))
         del pool, rq, rk, rv, ra, rb, o4
+        # one sequence x 32 heads: launch-bound; eager calls vs 16 steps in one HIP graph
+        x1 = [t[:1].contiguous() for t in (dq, dk_, dv_, da, db)]
+        s1 = dstate[:1].clone()
+        o1 = torch.empty((1, H, D), device=dev, dtype=torch.float32)
+        n1_eager_us = time_call(lambda: kda.decode_step(*x1, s1, o1), reps=200)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            kda.decode_step(*x1, s1, o1)
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(16):
+                kda.decode_step(*x1, s1, o1)
+        n1_graph_us = time_call(graph.replay, reps=20) / 16
+        del graph, x1, s1, o1
         # backward pass (training) of the same prefill workload
         d_o = torch.randn((B, T, H, D), device=dev, dtype=torch.float32)
         bws = torch.empty(kda.lib().kda_chunk_backward_workspace_size(B, T, H, D, D, 64),
@@ -221,6 +237,8 @@ def main():
             "decode_pool_512_slots_L4_us": pool4_us,
             "decode_pool_512_slots_L4_us_per_token": pool4_us / L4,
             "backward_b1_h32_t8192_us": bwd_us,
+            "decode_n1_h32_eager_us_per_step": n1_eager_us,
+            "decode_n1_h32_hip_graph_us_per_step": n1_graph_us,
         }
 
     pre_bytes = prefill_algorithmic_bytes(T, H, D, D, False, True)

@@ -1,0 +1,83 @@
+"""The entry points under HIP graph capture (torch.cuda.CUDAGraph): the
+captured decode step and staged prefill are replayed several times, with the
+program's own eager work and synchronisations between replays, and every
+replay is checked against the eager result.  None of the kernels records a
+memset or allocates, so the captured launches are plain kernel nodes."""
+
+import numpy as np
+import pytest
+import torch
+
+from gated_delta_rule_diag_amd import inputs as I
+from gated_delta_rule_diag_amd import kda
+from kda_testlib import dev, flush, random_state
+
+pytestmark = pytest.mark.gpu
+
+
+def test_decode_step_replays_match_eager():
+    N, H, D = 8, 4, 128
+    flush(f"[graph] decode N={N} H={H} d={D}: 4 replays")
+    q, k, v, a, b = I.decode_inputs(800, N, H, D, D, "bf16")
+    S0 = random_state(np.random.default_rng(1), (N, H, D, D))
+    bf = torch.bfloat16
+    x = [dev(q, bf), dev(k, bf), dev(v, bf), dev(a), dev(b)]
+    state = dev(S0)
+    out = torch.empty((N, H, D), device="cuda")
+    # eager reference: four consecutive steps from S0
+    S_ref = dev(S0)
+    o_ref, S_after = [], []
+    for _ in range(4):
+        o_ref.append(kda.decode_step(*x, S_ref).clone())
+        S_after.append(S_ref.clone())
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        kda.decode_step(*x, state, out)          # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    state.copy_(dev(S0))
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        kda.decode_step(*x, state, out)
+    state.copy_(dev(S0))
+    torch.cuda.synchronize()
+    for i in range(4):
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, o_ref[i]), i
+        assert torch.equal(state, S_after[i]), i
+        _ = (x[3] * 2).sum()                     # unrelated eager work between replays
+        torch.cuda.synchronize()
+
+
+def test_staged_prefill_replays_match_eager():
+    B, T, H, D = 1, 640, 4, 128
+    flush(f"[graph] staged prefill B={B} T={T} H={H} d={D}: 3 replays")
+    q, k, v, a, b = I.batch_inputs(801, B, T, H, D, D, "bf16")
+    bf = torch.bfloat16
+    x = [dev(q, bf), dev(k, bf), dev(v, bf), dev(a), dev(b)]
+    S0 = dev(random_state(np.random.default_rng(2), (B, H, D, D)))
+    ws = torch.empty(kda.lib().kda_chunk_prefill_workspace_size(B, T, H, D, D, 64), device="cuda",
+                     dtype=torch.uint8)
+    assert ws.numel() > 0                        # the two-kernel form with a workspace
+    o_ref, S_ref = kda.chunk_prefill(*x, S0)
+    o = torch.empty_like(o_ref)
+    S = torch.empty_like(S_ref)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        kda.chunk_prefill(*x, S0, True, 64, o, S, ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        kda.chunk_prefill(*x, S0, True, 64, o, S, ws)
+    for i in range(3):
+        o.zero_()
+        S.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(S, S_ref), i
