@@ -323,12 +323,13 @@ __global__ __launch_bounds__(DK / kRPT * kTPR) void kda_bwd_kernel(BackwardArgs 
           da[r] = row_sum(xa[r]);
         }
         if ((t % kTPR) == 0) {
-          const int64_t prow = (int64_t(slab) * p.rows + brow) * DK + i0;
+          // partials are slab-minor: [token row][key row][slab]
+          const int64_t prow = (brow * DK + i0) * nslab + slab;
 #pragma unroll
           for (int r = 0; r < kRPT; ++r) {
-            p.part_dq[prow + r] = dq[r];
-            p.part_dk[prow + r] = dk[r];
-            p.part_da[prow + r] = da[r];
+            p.part_dq[prow + r * nslab] = dq[r];
+            p.part_dk[prow + r * nslab] = dk[r];
+            p.part_da[prow + r * nslab] = da[r];
           }
         }
         if (i0 == 0) {
@@ -337,7 +338,7 @@ __global__ __launch_bounds__(DK / kRPT * kTPR) void kda_bwd_kernel(BackwardArgs 
           for (int e = 0; e < kCPT; ++e) dv4[e] = bt * du[e];
           stf4(p.dv + brow * DV + col, dv4);
           const float db = row_sum(xb);
-          if (t == 0) p.part_db[int64_t(slab) * p.rows + brow] = db;
+          if (t == 0) p.part_db[brow * nslab + slab] = db;
         }
       }
     }
@@ -346,42 +347,39 @@ __global__ __launch_bounds__(DK / kRPT * kTPR) void kda_bwd_kernel(BackwardArgs 
   if (p.d_state_in) st_slab(p.d_state_in + state_off, DV, G);
 }
 
-// dq, dk, dalpha (per row) and dbeta: sums of the per-slab partials.  A
-// thread adds four consecutive elements (rows * DK is a multiple of 64).
-template <int DK>
+// dq, dk, dalpha (per element) and dbeta: sums of the NS per-slab partials,
+// which are stored slab-minor, so a thread reads NS consecutive floats per
+// output and a wave streams contiguous memory.
+template <int NS>
+__device__ __forceinline__ float sum_ns(const float* p) {
+  float s = 0.f;
+#pragma unroll
+  for (int v = 0; v < NS; v += 4) {
+    const float4 x = *reinterpret_cast<const float4*>(p + v);
+    s += (x.x + x.y) + (x.z + x.w);
+  }
+  return s;
+}
+
+template <int DK, int NS>
 __global__ __launch_bounds__(256) void kda_bwd_reduce_kernel(BackwardArgs p) {
-  const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  const int64_t total = p.rows * DK;
-  const int nslab = p.DV / kVS;
-  if (4 * idx < total) {
-    float4 q = make_float4(0.f, 0.f, 0.f, 0.f), k = q, a = q;
-    for (int s = 0; s < nslab; ++s) {
-      const float4 x = reinterpret_cast<const float4*>(p.part_dq + s * total)[idx];
-      const float4 y = reinterpret_cast<const float4*>(p.part_dk + s * total)[idx];
-      const float4 z = reinterpret_cast<const float4*>(p.part_da + s * total)[idx];
-      q.x += x.x; q.y += x.y; q.z += x.z; q.w += x.w;
-      k.x += y.x; k.y += y.y; k.z += y.z; k.w += y.w;
-      a.x += z.x; a.y += z.y; a.z += z.z; a.w += z.w;
-    }
-    reinterpret_cast<float4*>(p.dq)[idx] = q;
-    reinterpret_cast<float4*>(p.dk)[idx] = k;
-    reinterpret_cast<float4*>(p.dalpha)[idx] = a;
+  const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;   // token row * DK + key row
+  if (idx < p.rows * DK) {
+    p.dq[idx] = sum_ns<NS>(p.part_dq + idx * NS);
+    p.dk[idx] = sum_ns<NS>(p.part_dk + idx * NS);
+    p.dalpha[idx] = sum_ns<NS>(p.part_da + idx * NS);
   }
-  if (idx < p.rows) {
-    float b = 0.f;
-    for (int s = 0; s < nslab; ++s) b += p.part_db[s * p.rows + idx];
-    p.dbeta[idx] = b;
-  }
+  if (idx < p.rows) p.dbeta[idx] = sum_ns<NS>(p.part_db + idx * NS);
 }
 
 template <int DK, bool BF16>
 void launch_bwd_t(const BackwardArgs& a, hipStream_t st) {
   const unsigned nb = unsigned(int64_t(a.N) * a.H * (a.DV / kVS));
   hipLaunchKernelGGL((kda_bwd_kernel<DK, BF16>), dim3(nb), dim3(DK / kRPT * kTPR), 0, st, a);
-  // threads: max(rows * DK / 4, rows) = rows * DK / 4 (DK >= 64)
-  const int64_t threads = a.rows * DK / 4;
-  hipLaunchKernelGGL((kda_bwd_reduce_kernel<DK>), dim3(unsigned((threads + 255) / 256)), dim3(256),
-                     0, st, a);
+  const int64_t threads = a.rows * DK;
+  const dim3 grid(unsigned((threads + 255) / 256));
+  if (a.DV == 128) hipLaunchKernelGGL((kda_bwd_reduce_kernel<DK, 8>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((kda_bwd_reduce_kernel<DK, 4>), grid, dim3(256), 0, st, a);
 }
 
 }  // namespace
