@@ -57,9 +57,11 @@ kda_status_t check_prefill(int nseq, int64_t ntok, int H, int DK, int DV, int ch
     return fail(KDA_ERR_UNSUPPORTED, "DK=%d DV=%d: only 64 and 128 are supported", DK, DV);
   if (chunk != 64) return fail(KDA_ERR_UNSUPPORTED, "chunk=%d: only 64 is supported", chunk);
   if (dt != KDA_F32 && dt != KDA_BF16) return fail(KDA_ERR_DTYPE, "unknown in_dtype %d", (int)dt);
-  if (ntok > (int64_t(1) << 31) - 1 || int64_t(nseq) * H > (int64_t(1) << 24))
-    return fail(KDA_ERR_UNSUPPORTED, "too large: tokens=%lld sequences*H=%lld", (long long)ntok,
-                (long long)nseq * H);
+  // (the kernels address the rows of one chunk with 32-bit offsets:
+  // 64 * H * 128 elements of 4 bytes stay below 2^31 for H <= 65536)
+  if (ntok > (int64_t(1) << 31) - 1 || int64_t(nseq) * H > (int64_t(1) << 24) || H > 65536)
+    return fail(KDA_ERR_UNSUPPORTED, "too large: tokens=%lld sequences*H=%lld H=%d (at most 65536)",
+                (long long)ntok, (long long)nseq * H, H);
   const size_t esz = dt == KDA_BF16 ? 2 : 4;
   const size_t nk = size_t(ntok) * H * DK, nv = size_t(ntok) * H * DV, nb = size_t(ntok) * H;
   const size_t ns = size_t(nseq) * H * DK * DV;
@@ -68,7 +70,6 @@ kda_status_t check_prefill(int nseq, int64_t ntok, int H, int DK, int DV, int ch
     if (!q || !k || !v || !alpha || !beta || !o)
       return fail(KDA_ERR_NULL, "q, k, v, alpha, beta and o must be non-NULL");
   }
-  if (ns > 0 && !s_out && !o && ntok == 0) return fail(KDA_ERR_NULL, "no output given");
   const void* ptrs[] = {q, k, v, alpha, beta, s_in, o, s_out};
   const char* names[] = {"q", "k", "v", "alpha", "beta", "state_in", "o", "state_out"};
   for (int i = 0; i < 8; ++i)
@@ -434,8 +435,9 @@ kda_status_t kda_chunk_backward(int B, int T, int H, int DK, int DV, int chunk,
   if (chunk != 64) return fail(KDA_ERR_UNSUPPORTED, "chunk=%d: only 64 is supported", chunk);
   if (in_dtype != KDA_F32 && in_dtype != KDA_BF16)
     return fail(KDA_ERR_DTYPE, "unknown in_dtype %d", (int)in_dtype);
-  if (int64_t(B) * T * H > (int64_t(1) << 31) / 128 || int64_t(B) * H > (int64_t(1) << 24))
-    return fail(KDA_ERR_UNSUPPORTED, "too large: B*T*H=%lld", (long long)B * T * H);
+  if (int64_t(B) * T * H > (int64_t(1) << 31) / 128 || int64_t(B) * H > (int64_t(1) << 24) ||
+      H > 65536)
+    return fail(KDA_ERR_UNSUPPORTED, "too large: B*T*H=%lld H=%d", (long long)B * T * H, H);
   if (B == 0 || T == 0 || H == 0) return ok();
   const void* need[] = {q, k, v, alpha, beta, d_o, dq, dk, dv, dalpha, dbeta};
   for (const void* x : need)

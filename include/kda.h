@@ -24,7 +24,8 @@
  *     alpha, beta, states and o are always float (fp32).
  *   - State layout: S[n][h][i][j] at ((n*H + h)*DK + i)*DV + j, where i is the
  *     KEY channel (the axis Diag(alpha) scales) and j the VALUE channel.
- *   - Supported sizes: DK, DV in {64, 128}; chunk == 64.
+ *   - Supported sizes: DK, DV in {64, 128}; chunk == 64; prefill and backward
+ *     at most 65536 heads.
  *   - Data domain (not checked: violating it gives unspecified output):
  *     alpha in [0.07, 1] and finite inputs.  The chunked prefill scales rows by
  *     decay ratios taken about each chunk's midpoint; the product of alpha over

@@ -67,6 +67,7 @@ def test_prefill_argument_errors(lib):
     assert prefill(lib, chunk=32) == UNSUP
     assert prefill(lib, dt=7) == DTYPE
     assert prefill(lib, T=-1) == SHAPE
+    assert prefill(lib, H=65537) == UNSUP      # 32-bit row offsets inside a chunk
     assert prefill(lib, H=-2) == SHAPE
     p = list(P[:8])
     p[0] = None
