@@ -401,8 +401,27 @@ __device__ __forceinline__ void xpose_lds(const char* src, int spitch, const flo
   }
 }
 
-// Destination of output stores for rows past the end of a sequence (never read).
-__device__ float g_sink[256 * 64];
+// Destination of output stores for rows past the end of a sequence, and of
+// the mirrored stores below (never read): 32 stores of 64 lanes per workgroup
+// slot, workgroups taken modulo 256.
+constexpr int kSinkStores = 32;
+}  // namespace
+// (external linkage: stores to it are not dead to the compiler)
+__device__ float g_kda_sink[256 * kSinkStores * 64];
+namespace {
+
+// N stores to distinct sink addresses (plain stores: the compiler keeps them,
+// since they reach memory other code could read, and does not wait for them).
+// Issued after a kernel's first prefetch, they stand in for the stores that
+// follow the prefetch in every later iteration, so that the compiler's
+// memory-counter waits for prefetched values need not cover those stores.
+template <int N>
+__device__ __forceinline__ void mirror_stores() {
+  static_assert(N <= kSinkStores, "sink size");
+  float* sink = g_kda_sink + (blockIdx.x & 255) * (kSinkStores * 64) + (threadIdx.x & 63);
+#pragma unroll
+  for (int i = 0; i < N; ++i) sink[64 * i] = 0.f;
+}
 
 // Thread -> (column quad cq, group grp of consecutive rows) of a 64-row chunk
 // with QUADS column quads: consecutive threads take consecutive quads
@@ -841,12 +860,10 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_prefill_kernel(Params p
     for (int i = 0; i < 4; ++i) {
       const int r = r0 + i < nvv ? r0 + i : nvv - 1;
       const uint32_t off = uint32_t(r * rsk + c0);
-      if (sg) {
-        const float x = ab[uint32_t(r * H)];
-        pa[i] = make_float4(x, x, x, x);
-      } else {
-        pa[i] = *reinterpret_cast<const float4*>(ab + off);
-      }
+      // (a scalar gate stays in .x until the values are taken: a broadcast
+      // here would make the wave wait for the load right away)
+      if (sg) pa[i].x = ab[uint32_t(r * H)];
+      else pa[i] = *reinterpret_cast<const float4*>(ab + off);
       pk[i] = ldraw4<BF>(kb, off);
       pq[i] = ldraw4<BF>(qb, off);
     }
@@ -869,7 +886,7 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_prefill_kernel(Params p
     // so that the first chunk and the steady state agree on how many memory
     // operations are in flight after the prefetched loads (otherwise the
     // compiler's wait for them degrades to waiting for every store).
-    volatile float* sink = g_sink + ((blockIdx.x & 255) << 6) + l;
+    volatile float* sink = g_kda_sink + (blockIdx.x & 255) * (kSinkStores * 64) + l;
 #pragma unroll
     for (int i = 0; i < 4 * NSUB; ++i) *sink = 0.f;
   }
@@ -882,7 +899,8 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_prefill_kernel(Params p
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const bool ok = r0 + i < nv;
-      av[i] = ok ? pa[i] : make_float4(1.f, 1.f, 1.f, 1.f);
+      const float4 ai = p.alpha_scalar ? make_float4(pa[i].x, pa[i].x, pa[i].x, pa[i].x) : pa[i];
+      av[i] = ok ? ai : make_float4(1.f, 1.f, 1.f, 1.f);
       const float4 kk = cvt4<BF>(pk[i]), qq = cvt4<BF>(pq[i]);
       kv[i] = ok ? kk : make_float4(0.f, 0.f, 0.f, 0.f);
       qv[i] = ok ? qq : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -948,7 +966,7 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_prefill_kernel(Params p
         // stay visible to the compiler's memory-counter bookkeeping, so taking
         // the prefetched inputs never waits for output stores to drain.
         float* ob = p.o + (tok0 * H + h) * int64_t(DV) + col0 + 16 * js;  // uniform
-        float* sink = g_sink + ((blockIdx.x & 255) << 6) + l;
+        float* sink = g_kda_sink + (blockIdx.x & 255) * (kSinkStores * 64) + l;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int r = 16 * ow + 4 * lg + q;
@@ -1213,12 +1231,10 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_stage_kernel(StageParam
     for (int i = 0; i < 4; ++i) {
       const int r = r0 + i < nvv ? r0 + i : nvv - 1;
       const uint32_t off = uint32_t(r * rsk + c0);
-      if (sg) {
-        const float x = ab[uint32_t(r * H)];
-        pa[i] = make_float4(x, x, x, x);
-      } else {
-        pa[i] = *reinterpret_cast<const float4*>(ab + off);
-      }
+      // (a scalar gate stays in .x until the values are taken: a broadcast
+      // here would make the wave wait for the load right away)
+      if (sg) pa[i].x = ab[uint32_t(r * H)];
+      else pa[i] = *reinterpret_cast<const float4*>(ab + off);
       pk[i] = ldraw4<BF>(kb, off);
       pq[i] = ldraw4<BF>(qb, off);
     }
@@ -1226,6 +1242,19 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_stage_kernel(StageParam
   };
 
   if (int64_t(blockIdx.x) < items) load_item(blockIdx.x);
+  {
+    // Every item's slot stores follow the prefetch of the next item's inputs.
+    // The same number of stores, mirrored before the first item, keeps the
+    // compiler's memory-counter waits for the prefetched inputs from also
+    // waiting for the previous item's slot stores.
+    using F = FL<BF>;
+    constexpr int SPF = BF ? 2 : 1;                    // stores per fragment
+    constexpr int NQ = 4 * (DK / F::KU) / NW;          // Qg and W fragments per wave
+    constexpr int NK = (DK / 16) * (kC / F::KU) / NW;  // Kg
+    constexpr int NP = 4 * (kC / F::KU) / NW;          // P
+    constexpr int NBU = (DV / 16) * 4 / NW;            // Uv tiles
+    mirror_stores<(2 * NQ + NK + NP) * SPF + 1 + NBU>();
+  }
   for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
     const int64_t c = p.c_begin + it / p.pairs;
     const int64_t rem = p.T_fixed - c * kC;
@@ -1235,7 +1264,8 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_stage_kernel(StageParam
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const bool ok = r0 + i < nv;
-      av[i] = ok ? pa[i] : make_float4(1.f, 1.f, 1.f, 1.f);
+      const float4 ai = p.alpha_scalar ? make_float4(pa[i].x, pa[i].x, pa[i].x, pa[i].x) : pa[i];
+      av[i] = ok ? ai : make_float4(1.f, 1.f, 1.f, 1.f);
       const float4 kk = cvt4<BF>(pk[i]), qq = cvt4<BF>(pq[i]);
       kv[i] = ok ? kk : make_float4(0.f, 0.f, 0.f, 0.f);
       qv[i] = ok ? qq : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -1437,7 +1467,7 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_chain_kernel(StageParam
     // The output stores that follow the prefetch in every chunk, mirrored
     // before the first one (keeps the compiler's memory-counter waits for the
     // prefetched operands from covering the stores as well).
-    volatile float* sink = g_sink + ((blockIdx.x & 255) << 6) + l;
+    volatile float* sink = g_kda_sink + (blockIdx.x & 255) * (kSinkStores * 64) + l;
 #pragma unroll
     for (int i = 0; i < 4 * NSUB; ++i) *sink = 0.f;
   }
@@ -1498,7 +1528,7 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_chain_kernel(StageParam
 #pragma unroll
     for (int js = 0; js < NSUB; ++js) {
       float* ob = p.o + (tok0 * H + h) * int64_t(DV) + col0 + 16 * js;
-      float* sink = g_sink + ((blockIdx.x & 255) << 6) + l;
+      float* sink = g_kda_sink + (blockIdx.x & 255) * (kSinkStores * 64) + l;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int r = 16 * ow + 4 * lg + q;
