@@ -1430,38 +1430,43 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_chain_kernel(StageParam
   // P is lower triangular: its row block ow is zero past token 16 ow + 15.
   const int npk = (16 * ow + 16 + M::KU - 1) / M::KU;
 
-  // Operands of the next chunk, loaded one chunk ahead.
-  Frag na[NA][KCK], npp[KCC], nkg[KCC];
-  f4 nu[NSUB];
-  float4 ng;
+  // Operands of a chunk: two sets, ping-ponged between consecutive chunks
+  // (no register copies, so the wait for each prefetched part sits at its
+  // first use, not at the start of the chunk).
+  struct Ops {
+    Frag a[NA][KCK], pp[KCC], kg[KCC];
+    f4 u[NSUB];
+    float4 g;
+  };
   // The loads are issued in three parts spread over the chunk, so that the
   // memory pipeline works while the waves compute.
   auto slot_of = [&](int64_t c) { return p.ws + ((c - p.c_begin) * p.pairs + pr) * slot_bytes; };
-  auto load_part1 = [&](const char* slot) {
+  auto load_part1 = [&](Ops& o, const char* slot) {
 #pragma unroll
     for (int a = 0; a < NA; ++a) {
       const bool wside = kSplitO ? xw : (a == 0);
-      F::load(na[a], slot + (wside ? OFF_W : OFF_Q) + ow * RBK);
+      F::load(o.a[a], slot + (wside ? OFF_W : OFF_Q) + ow * RBK);
     }
   };
-  auto load_part2 = [&](const char* slot) {
-    F::load(nkg, slot + OFF_K + w * RBC);
-    ng = *reinterpret_cast<const float4*>(slot + off_g + (16 * w + 4 * lg) * 4);
+  auto load_part2 = [&](Ops& o, const char* slot) {
+    F::load(o.kg, slot + OFF_K + w * RBC);
+    o.g = *reinterpret_cast<const float4*>(slot + off_g + (16 * w + 4 * lg) * 4);
   };
-  auto load_part3 = [&](const char* slot) {
-    if (owave) F::load(npp, slot + OFF_P + ow * RBC, npk);
+  auto load_part3 = [&](Ops& o, const char* slot) {
+    if (owave) F::load(o.pp, slot + OFF_P + ow * RBC, npk);
     if (xw) {
 #pragma unroll
       for (int js = 0; js < NSUB; ++js)
-        nu[js] = *reinterpret_cast<const f4*>(slot + OFF_U + (ow * (DV / 16) + (col0 >> 4) + js) * 1024 + 16 * l);
+        o.u[js] = *reinterpret_cast<const f4*>(slot + OFF_U + (ow * (DV / 16) + (col0 >> 4) + js) * 1024 + 16 * l);
     }
   };
   const int64_t c_end = p.c_begin + p.nseg;
+  Ops A, B;
   {
     const char* s0 = slot_of(p.c_begin);
-    load_part1(s0);
-    load_part2(s0);
-    load_part3(s0);
+    load_part1(A, s0);
+    load_part2(A, s0);
+    load_part3(A, s0);
   }
   {
     // The output stores that follow the prefetch in every chunk, mirrored
@@ -1472,25 +1477,15 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_chain_kernel(StageParam
     for (int i = 0; i < 4 * NSUB; ++i) *sink = 0.f;
   }
 
-  for (int64_t c = p.c_begin; c < c_end; ++c) {
+  // One chunk with operands `cur`; the next chunk's operands go to `nxt`
+  // (past the last chunk the last one is loaded again: loads stay
+  // unconditional).
+  auto step = [&](int64_t c, Ops& cur, Ops& nxt) {
     const int64_t tok0 = n * p.T_fixed + c * kC;
     const int64_t rem = p.T_fixed - c * kC;
     const int nv = int(rem < kC ? rem : kC);
-    Frag a[NA][KCK], pp[KCC], kg[KCC];
-    f4 u[NSUB];
-    float4 g;
-#pragma unroll
-    for (int i = 0; i < NA; ++i)
-#pragma unroll
-      for (int kc = 0; kc < KCK; ++kc) a[i][kc] = na[i][kc];
-#pragma unroll
-    for (int kc = 0; kc < KCC; ++kc) pp[kc] = npp[kc], kg[kc] = nkg[kc];
-#pragma unroll
-    for (int js = 0; js < NSUB; ++js) u[js] = nu[js];
-    g = ng;
-    const bool more = c + 1 < c_end;
-    const char* sn = slot_of(more ? c + 1 : c);
-    if (more) load_part1(sn);
+    const char* sn = slot_of(c + 1 < c_end ? c + 1 : c);
+    load_part1(nxt, sn);
 
     // S^T of the slab to LDS.
 #pragma unroll
@@ -1499,7 +1494,7 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_chain_kernel(StageParam
       st4<BF>(sS, SP_S, 16 * js + lr, 16 * w + 4 * lg, x);
     }
     lds_barrier();
-    if (more) load_part2(sn);
+    load_part2(nxt, sn);
     // U = Uv - W S  (X side);  O = Qg S  (O side).
     f4 acco[NSUB];
 #pragma unroll
@@ -1507,23 +1502,24 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_chain_kernel(StageParam
     if (xw) {
 #pragma unroll
       for (int js = 0; js < NSUB; ++js) {
-        const f4 x = gemm_ra<BF, KCK>(f4{0.f, 0.f, 0.f, 0.f}, a[0], sS + 16 * js * SP_S, SP_S);
-        const float y[4] = {u[js][0] - x[0], u[js][1] - x[1], u[js][2] - x[2], u[js][3] - x[3]};
+        const f4 x = gemm_ra<BF, KCK>(f4{0.f, 0.f, 0.f, 0.f}, cur.a[0], sS + 16 * js * SP_S, SP_S);
+        const float y[4] = {cur.u[js][0] - x[0], cur.u[js][1] - x[1], cur.u[js][2] - x[2],
+                            cur.u[js][3] - x[3]};
         st4<BF>(sU, SP_U, 16 * js + lr, 16 * ow + 4 * lg, y);
       }
     }
     if (owave) {
 #pragma unroll
       for (int js = 0; js < NSUB; ++js)
-        acco[js] = gemm_ra<BF, KCK>(acco[js], a[NA - 1], sS + 16 * js * SP_S, SP_S);
+        acco[js] = gemm_ra<BF, KCK>(acco[js], cur.a[NA - 1], sS + 16 * js * SP_S, SP_S);
     }
     lds_barrier();
-    if (more) load_part3(sn);
+    load_part3(nxt, sn);
     // O += P U, stored;  S' = Diag(gamma_n) S + Kg U.
     if (owave) {
 #pragma unroll
       for (int js = 0; js < NSUB; ++js)
-        acco[js] = gemm_ra<BF, KCC>(acco[js], pp, sU + 16 * js * SP_U, SP_U, npk);
+        acco[js] = gemm_ra<BF, KCC>(acco[js], cur.pp, sU + 16 * js * SP_U, SP_U, npk);
     }
 #pragma unroll
     for (int js = 0; js < NSUB; ++js) {
@@ -1538,16 +1534,25 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_chain_kernel(StageParam
     }
 #pragma unroll
     for (int js = 0; js < NSUB; ++js) {
-      const f4 y = gemm_ra<BF, KCC>(f4{0.f, 0.f, 0.f, 0.f}, kg, sU + 16 * js * SP_U, SP_U);
-      S[js][0] = g.x * S[js][0] + y[0];
-      S[js][1] = g.y * S[js][1] + y[1];
-      S[js][2] = g.z * S[js][2] + y[2];
-      S[js][3] = g.w * S[js][3] + y[3];
+      const f4 y = gemm_ra<BF, KCC>(f4{0.f, 0.f, 0.f, 0.f}, cur.kg, sU + 16 * js * SP_U, SP_U);
+      S[js][0] = cur.g.x * S[js][0] + y[0];
+      S[js][1] = cur.g.y * S[js][1] + y[1];
+      S[js][2] = cur.g.z * S[js][2] + y[2];
+      S[js][3] = cur.g.w * S[js][3] + y[3];
     }
     if constexpr (SNAP) {
       if (nv == kC && (c + 1) % p.snap_every == 0)
         store_snapshot<DK, NSUB>(p.snap, p.snap_per_seq, n, h, H, DV, (c + 1) / p.snap_every - 1, col0, S);
     }
+  };
+
+  // The first chunk is peeled: it is the only one that reads the state as
+  // loaded from state_in, so the loop's waits never cover that load.
+  step(p.c_begin, A, B);
+  for (int64_t c = p.c_begin + 1; c < c_end; c += 2) {
+    step(c, B, A);
+    if (c + 1 >= c_end) break;
+    step(c + 1, A, B);
   }
 
   if (p.s_out) {
