@@ -133,8 +133,10 @@ static kda_status_t run_prefill(kda::PrefillArgs& a, size_t need, void* stream) 
     const size_t esz = a.in_bf16 ? 2 : 4;
     const size_t nk = size_t(a.T_total) * a.H * a.DK, nv = size_t(a.T_total) * a.H * a.DV;
     const size_t nb = size_t(a.T_total) * a.H, ns = size_t(a.N) * a.H * a.DK * a.DV;
-    const size_t nsnap = a.snapshots ? size_t(a.N) * size_t(a.T_fixed / (64 * a.snap_every)) * a.H *
-                                           a.DK * a.DV : 0;
+    const size_t nsnap = !a.snapshots ? 0
+                         : (a.snap_offsets ? size_t(a.snap_rows)
+                                           : size_t(a.N) * size_t(a.T_fixed / (64 * a.snap_every))) *
+                               a.H * a.DK * a.DV;
     const void* ptrs[] = {a.q, a.k, a.v, a.alpha, a.beta, a.state_in, a.o, a.state_out, a.snapshots};
     const size_t sizes[] = {nk * esz, nk * esz, nv * esz, (a.alpha_scalar ? nb : nk) * 4, nb * 4,
                             ns * 4, nv * 4, ns * 4, nsnap * 4};
@@ -269,6 +271,56 @@ kda_status_t kda_chunk_prefill_varlen(int N, int T_total, const int32_t* cu_seql
                                       void* workspace, size_t workspace_bytes, void* stream) {
   return prefill_varlen(N, T_total, cu_seqlens, H, DK, DV, chunk, in_dtype, q, k, v, alpha, beta,
                         state_in, o, state_out, workspace, workspace_bytes, stream, false);
+}
+
+kda_status_t kda_chunk_prefill_varlen_snapshots(int N, int T_total, const int32_t* cu_seqlens,
+                                                int H, int DK, int DV, int chunk,
+                                                kda_dtype_t in_dtype, const void* q, const void* k,
+                                                const void* v, const float* alpha,
+                                                const float* beta, const float* state_in,
+                                                float* o, float* state_out, int every,
+                                                const int32_t* snap_offsets, int num_snapshots,
+                                                float* snapshots, void* workspace,
+                                                size_t workspace_bytes, void* stream) {
+  if (N < 0 || T_total < 0) return fail(KDA_ERR_SHAPE, "negative size (N=%d T_total=%d)", N, T_total);
+  if (every < 1) return fail(KDA_ERR_SHAPE, "every=%d: must be >= 1", every);
+  if (num_snapshots < 0) return fail(KDA_ERR_SHAPE, "num_snapshots=%d is negative", num_snapshots);
+  if (N > 0 && cu_seqlens == nullptr) return fail(KDA_ERR_NULL, "cu_seqlens must be non-NULL");
+  if (N > 0 && snap_offsets == nullptr) return fail(KDA_ERR_NULL, "snap_offsets must be non-NULL");
+  if ((reinterpret_cast<uintptr_t>(cu_seqlens) | reinterpret_cast<uintptr_t>(snap_offsets)) & 3u)
+    return fail(KDA_ERR_ALIGN, "cu_seqlens and snap_offsets must be 4-byte aligned");
+  kda_status_t s = check_prefill(N, T_total, H, DK, DV, chunk, in_dtype, q, k, v, alpha, beta,
+                                 state_in, o, state_out, false);
+  if (s != KDA_OK) return s;
+  const size_t sbytes = size_t(num_snapshots) * H * DK * DV * 4;
+  if (sbytes > 0) {
+    if (!snapshots) return fail(KDA_ERR_NULL, "snapshots must be non-NULL (%d rows)", num_snapshots);
+    if (!aligned16(snapshots)) return fail(KDA_ERR_ALIGN, "snapshots is not 16-byte aligned");
+    const size_t esz = in_dtype == KDA_BF16 ? 2 : 4;
+    const size_t nk = size_t(T_total) * H * DK, nv = size_t(T_total) * H * DV, nb = size_t(T_total) * H;
+    const size_t ns = size_t(N) * H * DK * DV;
+    const void* others[] = {q, k, v, alpha, beta, state_in, o, state_out, cu_seqlens, snap_offsets};
+    const size_t ob[] = {nk * esz, nk * esz, nv * esz, nk * 4, nb * 4, ns * 4, nv * 4, ns * 4,
+                         size_t(N + 1) * 4, size_t(N + 1) * 4};
+    for (int i = 0; i < 10; ++i)
+      if (overlaps(snapshots, sbytes, others[i], ob[i]))
+        return fail(KDA_ERR_SHAPE, "snapshots overlaps another argument");
+  }
+  kda::PrefillArgs a{};
+  a.N = N;
+  a.T_fixed = 0;
+  a.cu_seqlens = cu_seqlens;
+  a.T_total = T_total;
+  a.H = H; a.DK = DK; a.DV = DV;
+  a.in_bf16 = in_dtype == KDA_BF16;
+  a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta;
+  a.state_in = state_in; a.o = o; a.state_out = state_out;
+  a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+  a.snapshots = sbytes > 0 ? snapshots : nullptr;
+  a.snap_every = every;
+  a.snap_offsets = snap_offsets;
+  a.snap_rows = num_snapshots;
+  return run_prefill(a, kda::prefill_workspace_bytes(N, T_total, H, DK, DV, true), stream);
 }
 
 kda_status_t kda_chunk_prefill_varlen_scalar_gate(int N, int T_total, const int32_t* cu_seqlens,

@@ -26,8 +26,11 @@ struct PrefillArgs {
   float* state_out;            // may be nullptr
   void* workspace;
   size_t workspace_bytes;
-  float* snapshots;            // [N, T_fixed / (64 * snap_every), H, DK, DV] or nullptr
+  float* snapshots;            // fixed: [N, T_fixed / (64 * snap_every), H, DK, DV]; varlen:
+                               // [snap_rows, H, DK, DV]; or nullptr
   int snap_every;              // chunks between snapshots (with snapshots != nullptr)
+  const int32_t* snap_offsets; // varlen: device [N+1], sequence n owns rows [off[n], off[n+1])
+  int64_t snap_rows;           // varlen: rows of snapshots
   bool alpha_scalar;           // alpha is [tokens, H]: one gate per token and head
 };
 

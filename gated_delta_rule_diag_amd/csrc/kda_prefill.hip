@@ -55,9 +55,11 @@ struct Params {
   const float* s_in;
   float* o;
   float* s_out;
-  float* snap;        // state snapshots [N][snap_per_seq][H][DK][DV] (SNAP kernels)
+  float* snap;        // state snapshots [rows][H][DK][DV] (SNAP kernels)
   int snap_every;     // a snapshot after every snap_every-th full chunk
-  int64_t snap_per_seq;
+  int64_t snap_per_seq;   // fixed length: sequence n's snapshot j is row n * snap_per_seq + j
+  const int32_t* snap_off;  // varlen: row snap_off[n] + j, j < snap_off[n+1] - snap_off[n]
+  int64_t snap_rows;        // varlen: rows of snap (rows outside [0, snap_rows) are skipped)
   int alpha_scalar;   // alpha is [tokens][H] (one gate per token and head)
 };
 
@@ -766,12 +768,12 @@ tT[g][2] = a2; tR[g][2] = b2; tI[g][2] = c2_;
 
 // ------------------------------------------------------------------ kernel --
 // Store the state slab S[js][q] (rows 16w + 4lg + q, columns col0 + 16js + lr)
-// as snapshot j of chain (n, h).
+// as snapshot row `row` of head h.
 template <int DK, int NSUB>
-__device__ __forceinline__ void store_snapshot(float* snap, int64_t per_seq, int64_t n, int h, int H,
-                                               int DV, int64_t j, int col0, const f4 (&S)[NSUB]) {
+__device__ __forceinline__ void store_snapshot(float* snap, int64_t row, int h, int H, int DV, int col0,
+                                               const f4 (&S)[NSUB]) {
   const int l = lane_id(), w = threadIdx.x >> 6;
-  float* dst = snap + ((n * per_seq + j) * H + h) * int64_t(DK) * DV + col0 + (l & 15);
+  float* dst = snap + (row * H + h) * int64_t(DK) * DV + col0 + (l & 15);
 #pragma unroll
   for (int js = 0; js < NSUB; ++js)
 #pragma unroll
@@ -816,6 +818,11 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_prefill_kernel(Params p
   const int col0 = slab * VS;
 
   int64_t s0, s1;
+  int64_t snap_base = 0, snap_cnt = 0;   // varlen snapshot rows of sequence n
+  if (SNAP && p.snap_off != nullptr) {
+    snap_base = p.snap_off[n];
+    snap_cnt = p.snap_off[n + 1] - snap_base;
+  }
   if (p.cu != nullptr) {
     s0 = p.cu[n];
     s1 = p.cu[n + 1];
@@ -992,8 +999,14 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_prefill_kernel(Params p
     if constexpr (SNAP) {
       // State after a complete interval of snap_every full chunks.
       const int64_t done = (tok0 - s0) / kC + 1;
-      if (nv == kC && done % p.snap_every == 0)
-        store_snapshot<DK, NSUB>(p.snap, p.snap_per_seq, n, h, H, DV, done / p.snap_every - 1, col0, S);
+      if (nv == kC && done % p.snap_every == 0) {
+        const int64_t j = done / p.snap_every - 1;
+        if (p.snap_off == nullptr) {
+          store_snapshot<DK, NSUB>(p.snap, n * p.snap_per_seq + j, h, H, DV, col0, S);
+        } else if (j < snap_cnt && snap_base + j >= 0 && snap_base + j < p.snap_rows) {
+          store_snapshot<DK, NSUB>(p.snap, snap_base + j, h, H, DV, col0, S);
+        }
+      }
     }
   }
 
@@ -1542,7 +1555,7 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_chain_kernel(StageParam
     }
     if constexpr (SNAP) {
       if (nv == kC && (c + 1) % p.snap_every == 0)
-        store_snapshot<DK, NSUB>(p.snap, p.snap_per_seq, n, h, H, DV, (c + 1) / p.snap_every - 1, col0, S);
+        store_snapshot<DK, NSUB>(p.snap, n * p.snap_per_seq + (c + 1) / p.snap_every - 1, h, H, DV, col0, S);
     }
   };
 
@@ -1743,6 +1756,8 @@ int launch_prefill(const PrefillArgs& a, void* stream, const char** msg) {
   p.snap = a.snapshots;
   p.snap_every = a.snap_every > 0 ? a.snap_every : 1;
   p.snap_per_seq = a.snapshots ? a.T_fixed / (int64_t(kC) * p.snap_every) : 0;
+  p.snap_off = a.snap_offsets;
+  p.snap_rows = a.snap_rows;
   p.alpha_scalar = a.alpha_scalar ? 1 : 0;
   const int64_t pairs = int64_t(a.N) * a.H;
   const bool varlen = a.cu_seqlens != nullptr;

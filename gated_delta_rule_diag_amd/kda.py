@@ -38,6 +38,7 @@ EXPORTED = (
     "kda_decode_step_scalar_gate",
     "kda_chunk_backward_workspace_size",
     "kda_chunk_backward",
+    "kda_chunk_prefill_varlen_snapshots",
     "kda_status_string",
     "kda_last_error_message",
 )
@@ -82,6 +83,9 @@ def load_library(path: str = _LIB_PATH) -> ctypes.CDLL:
     lib.kda_chunk_backward_workspace_size.argtypes = [i, i, i, i, i, i]
     lib.kda_chunk_backward.restype = i
     lib.kda_chunk_backward.argtypes = [i, i, i, i, i, i, i] + [vp] * 15 + [sz, vp]
+    lib.kda_chunk_prefill_varlen_snapshots.restype = i
+    lib.kda_chunk_prefill_varlen_snapshots.argtypes = [i, i, vp, i, i, i, i, i] + [vp] * 8 + \
+        [i, vp, i, vp, vp, sz, vp]
     lib.kda_decode_pool.restype = i
     lib.kda_decode_pool.argtypes = [i, i, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp, i, vp, vp, vp]
     lib.kda_status_string.restype = ctypes.c_char_p
@@ -363,3 +367,62 @@ def chunk_backward(q, k, v, alpha, beta, d_o, initial_state=None, d_final_state=
         _ptr(dal), _ptr(db), _ptr(ds0), _ptr(workspace),
         0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(dev)))
     return dq, dk, dv, dal, db, ds0
+
+
+def chunk_prefill_varlen_snapshots(q, k, v, alpha, beta, cu_seqlens, every, initial_state=None,
+                                   output_final_state=True, chunk=64, snap_offsets=None,
+                                   out=None, final_state=None, snapshots=None, workspace=None):
+    """Packed variable-length prefill that also returns each sequence's state
+    after every ``every``-th chunk of 64 tokens.
+
+    Arguments as for :func:`chunk_prefill_varlen`.  ``snap_offsets`` (int32
+    device [N+1]) places sequence n's snapshots at rows snap_offsets[n] ..; by
+    default it is built from the sequence lengths (a host copy of cu_seqlens).
+    Returns (o, final_state, snapshots [rows, H, DK, DV], snap_offsets).
+    """
+    Tt, H, DK = q.shape
+    DV = v.shape[-1]
+    dt = _in_dtype(q)
+    _need(q, "q", q.dtype)
+    _need(k, "k", q.dtype, (Tt, H, DK))
+    _need(v, "v", q.dtype, (Tt, H, DV))
+    _need(alpha, "alpha", torch.float32, (Tt, H, DK))
+    _need(beta, "beta", torch.float32, (Tt, H))
+    _need(cu_seqlens, "cu_seqlens", torch.int32)
+    if every < 1:
+        raise ValueError("every must be >= 1")
+    N = cu_seqlens.numel() - 1
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, (N, H, DK, DV))
+    dev = q.device
+    if snap_offsets is None:
+        lens = (cu_seqlens[1:] - cu_seqlens[:-1]).to("cpu", torch.int64)
+        per = lens // (chunk * every)
+        offs = torch.zeros(N + 1, dtype=torch.int64)
+        offs[1:] = torch.cumsum(per, 0)
+        snap_offsets = offs.to(torch.int32).to(dev)
+        rows = int(offs[-1])
+    else:
+        _need(snap_offsets, "snap_offsets", torch.int32, (N + 1,))
+        rows = int(snap_offsets[-1].item()) if snapshots is None else snapshots.shape[0]
+    o = out if out is not None else torch.empty((Tt, H, DV), device=dev, dtype=torch.float32)
+    _need(o, "out", torch.float32, (Tt, H, DV))
+    st = None
+    if output_final_state:
+        st = final_state if final_state is not None else torch.empty(
+            (N, H, DK, DV), device=dev, dtype=torch.float32)
+        _need(st, "final_state", torch.float32, (N, H, DK, DV))
+    snaps = snapshots if snapshots is not None else torch.empty(
+        (rows, H, DK, DV), device=dev, dtype=torch.float32)
+    _need(snaps, "snapshots", torch.float32)
+    if snaps.dim() != 4 or tuple(snaps.shape[1:]) != (H, DK, DV):
+        raise ValueError(f"snapshots must have shape [rows,{H},{DK},{DV}]")
+    wsz = lib().kda_chunk_prefill_varlen_workspace_size(N, Tt, H, DK, DV, chunk)
+    if wsz and workspace is None:
+        workspace = torch.empty(wsz, device=dev, dtype=torch.uint8)
+    _check(lib().kda_chunk_prefill_varlen_snapshots(
+        N, Tt, _ptr(cu_seqlens), H, DK, DV, chunk, dt, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+        _ptr(beta), _ptr(initial_state), _ptr(o), _ptr(st), every, _ptr(snap_offsets),
+        snaps.shape[0], _ptr(snaps), _ptr(workspace),
+        0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(dev)))
+    return o, st, snaps, snap_offsets

@@ -122,6 +122,35 @@ kda_status_t kda_chunk_prefill_snapshots(int B, int T, int H, int DK, int DV, in
                                          size_t workspace_bytes, void* stream);
 
 /*
+ * Packed variable-length prefill with snapshots (prefix caching for a
+ * continuous-batching prefill): as kda_chunk_prefill_varlen, and sequence n's
+ * state after its first 64*every*(j+1) tokens is written to row
+ * snap_offsets[n] + j of `snapshots`, for j < floor(len_n / (64*every)) and
+ * j < snap_offsets[n+1] - snap_offsets[n] (rows the offsets do not provide
+ * are skipped).
+ *   snap_offsets   int32 DEVICE [N+1], 4-byte aligned, non-decreasing
+ *                  (normally snap_offsets[n+1] - snap_offsets[n] =
+ *                  floor(len_n / (64*every)))
+ *   num_snapshots  host int = snap_offsets[N], the rows of `snapshots`; rows
+ *                  outside [0, num_snapshots) are never written, whatever the
+ *                  device offsets hold
+ *   snapshots      [num_snapshots, H, DK, DV] float, may be NULL when
+ *                  num_snapshots == 0
+ * Prefix reuse and the state at chunk boundaries under continuous batching
+ * are what serving has to get right ("Kimi Linear、独自の土俵でFull Attention
+ * を上回る" (remio.ai), section "Kimi Linearリリース後に注目すべき点").
+ */
+kda_status_t kda_chunk_prefill_varlen_snapshots(int N, int T_total, const int32_t* cu_seqlens,
+                                                int H, int DK, int DV, int chunk,
+                                                kda_dtype_t in_dtype, const void* q, const void* k,
+                                                const void* v, const float* alpha,
+                                                const float* beta, const float* state_in,
+                                                float* o, float* state_out, int every,
+                                                const int32_t* snap_offsets, int num_snapshots,
+                                                float* snapshots, void* workspace,
+                                                size_t workspace_bytes, void* stream);
+
+/*
  * Chunked prefill, packed variable length: N sequences concatenated on the
  * token axis; sequence n owns tokens [cu_seqlens[n], cu_seqlens[n+1]).
  *   cu_seqlens  int32 DEVICE array [N+1], cu_seqlens[0] == 0, non-decreasing,

@@ -174,6 +174,31 @@ def test_varlen_argument_errors(lib):
     assert call(N=0, Tt=0) == OK
 
 
+def test_varlen_snapshot_argument_errors(lib):
+    # N=2, T_total=100, H=2, d=64; 2 snapshot rows of [2, 64, 64] float = 64 KiB.
+    # The packed form needs no workspace.  No call below reaches a launch.
+    need = lib.kda_chunk_prefill_varlen_workspace_size(2, 100, 2, 64, 64, 64)
+    assert need == 0
+
+    def call(N=2, Tt=100, cu=P[8], every=1, offs=P[11], rows=2, snap=P[10], ws=P[9], wsb=need):
+        return lib.kda_chunk_prefill_varlen_snapshots(N, Tt, cu, 2, 64, 64, 64, 1, *P[:8], every,
+                                                      offs, rows, snap, ws, wsb, None)
+
+    assert call(every=0) == SHAPE
+    assert call(rows=-1) == SHAPE
+    assert call(offs=None) == NULL
+    assert "snap_offsets" in lib.kda_last_error_message().decode()
+    assert call(offs=ctypes.c_void_p(P[11].value + 2)) == ALIGN
+    assert call(cu=None) == NULL
+    assert call(snap=None) == NULL
+    assert call(snap=ctypes.c_void_p(P[10].value + 4)) == ALIGN
+    assert call(snap=ctypes.c_void_p(P[6].value + 4096)) == SHAPE      # inside o
+    assert call(snap=ctypes.c_void_p(P[8].value - 4096)) == SHAPE      # runs into cu_seqlens
+    assert call(offs=ctypes.c_void_p(P[10].value + 4096)) == SHAPE     # offsets inside snapshots
+    # no rows: snapshots may be NULL; N = 0 needs no offsets
+    assert call(rows=0, snap=None, ws=None, wsb=0, N=0, Tt=0, offs=None, cu=None) == OK
+
+
 def test_decode_argument_errors(lib):
     def call(N=4, H=2, DK=128, DV=128, dt=1, ptrs=None):
         q, k, v, a, b, s, o = ptrs or P[:7]

@@ -119,3 +119,68 @@ def test_snapshots_across_staged_segments(seg, monkeypatch):
                   max_rel_err(host(sn), sn_ref))
     flush(f"    err o={eo:.2e} S={es:.2e} snapshots={en:.2e}")
     assert eo <= TOL["bf16"] and es <= TOL["bf16"] and en <= TOL["bf16"]
+
+
+def varlen_snapshot_reference(q, k, v, a, b, cu, every, S0):
+    """Per-sequence oracle snapshots, packed in sequence order."""
+    o, S, rows = [], [], []
+    for n in range(len(cu) - 1):
+        s, e = cu[n], cu[n + 1]
+        on, Sn, sn = kda_recurrent_snapshots(q[None, s:e], k[None, s:e], v[None, s:e],
+                                             a[None, s:e], b[None, s:e], every, S0[n:n + 1])
+        o.append(on[0]); S.append(Sn[0]); rows.append(sn[0])
+    return np.concatenate(o), np.stack(S), np.concatenate(rows)
+
+
+@pytest.mark.parametrize("every", [1, 2])
+@pytest.mark.parametrize("dt,dk,dv", [("bf16", 128, 128), ("f32", 64, 64)])
+def test_varlen_snapshots_match_oracle(dt, dk, dv, every):
+    """Packed sequences of mixed lengths (empty, shorter than one interval,
+    exact multiples, ragged tails): each sequence's snapshots land at its own
+    rows, and o and the final states match the plain varlen prefill."""
+    lengths = [5, 0, 200, 64, 128, 33, 257]
+    H = 3
+    flush(f"[snapshots] varlen lengths={lengths} H={H} DK={dk} DV={dv} {dt} every={every}")
+    q, k, v, a, b, cu = I.packed_inputs(550 + every, lengths, H, dk, dv, dt)
+    S0 = random_state(np.random.default_rng(11), (len(lengths), H, dk, dv))
+    o_ref, S_ref, sn_ref = varlen_snapshot_reference(q, k, v, a, b, cu, every, S0)
+    td = tdtype(dt)
+    x = (dev(q, td), dev(k, td), dev(v, td), dev(a), dev(b), torch.from_numpy(cu).cuda())
+    o, S, sn, offs = kda.chunk_prefill_varlen_snapshots(*x, every, dev(S0))
+    o1, S1 = kda.chunk_prefill_varlen(*x, dev(S0))
+    torch.cuda.synchronize()
+    per = [n // (64 * every) for n in lengths]
+    assert offs.cpu().tolist() == list(np.concatenate([[0], np.cumsum(per)]))
+    assert sn.shape[0] == sum(per) == sn_ref.shape[0]
+    assert torch.equal(o, o1) and torch.equal(S, S1)
+    eo, es = max_rel_err(host(o), o_ref), max_rel_err(host(S), S_ref)
+    flush(f"    err o={eo:.2e} S={es:.2e}")
+    assert eo <= TOL[dt] and es <= TOL[dt]
+    for r in range(sn.shape[0]):
+        assert max_rel_err(host(sn[r]), sn_ref[r]) <= TOL[dt], r
+
+
+def test_varlen_snapshots_follow_given_offsets():
+    """Caller-chosen offsets: rows the offsets leave out keep their contents,
+    a sequence given fewer rows than it has boundaries writes only those, and
+    device offsets that point past num_snapshots write nothing there."""
+    lengths = [130, 260, 70]          # 2, 4 and 1 boundaries at every=1
+    H, d = 2, 64
+    flush(f"[snapshots] varlen given offsets lengths={lengths} H={H} d={d}")
+    q, k, v, a, b, cu = I.packed_inputs(560, lengths, H, d, d, "bf16")
+    S0 = np.zeros((3, H, d, d))
+    _, _, sn_ref = varlen_snapshot_reference(q, k, v, a, b, cu, 1, S0)   # rows 0-1, 2-5, 6
+    bf = torch.bfloat16
+    x = (dev(q, bf), dev(k, bf), dev(v, bf), dev(a), dev(b), torch.from_numpy(cu).cuda())
+    # sequence 0 -> rows 1..2; sequence 1 -> rows 4..5 only (2 of its 4);
+    # sequence 2 -> row 6, but only 6 rows are passed (a view of the first 6
+    # of 8), so row 6 is out of range and skipped
+    offs = torch.tensor([1, 4, 6, 9], dtype=torch.int32, device="cuda")
+    sent = torch.full((8, H, d, d), -7.0, device="cuda")
+    kda.chunk_prefill_varlen_snapshots(*x, 1, snap_offsets=offs, snapshots=sent[:6])
+    torch.cuda.synchronize()
+    got = host(sent)
+    untouched = [0, 3, 6, 7]
+    assert (got[untouched] == -7.0).all()
+    for row, ref in [(1, 0), (2, 1), (4, 2), (5, 3)]:
+        assert max_rel_err(got[row], sn_ref[ref]) <= TOL["bf16"], row
