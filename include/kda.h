@@ -78,8 +78,10 @@ int kda_abi_version(void);
  *              ignored and on return are unspecified.  The size is nonzero
  *              when B*H < 128 and T > 64: the per-chunk operands of the
  *              state pass are then computed for all chunks at once and staged
- *              here (at most about 1 GiB plus one B*H*DK*DV float state; long
- *              sequences are processed in segments of chunks).
+ *              here.  Long sequences are processed in equal segments of
+ *              chunks whose operands take at most 160 MiB (so that they stay
+ *              in the memory-side cache between the two kernels), plus one
+ *              B*H*DK*DV float state carried between segments.
  * Computes exactly the token recurrence (up to rounding) by the chunk form:
  * per chunk a unit-lower-triangular solve and dense products, and a
  * sequential pass of the state over the chunks.

@@ -102,12 +102,30 @@ def test_workspace_size_queries(lib, monkeypatch):
     # element, plus gamma_n [DK]
     slot = lambda dk, dv=128: 4 * (3 * 64 * dk + 64 * 64 + 64 * dv + dk)  # noqa: E731
     assert slot(128) == 147968 and slot(64, 64) == 82176
-    assert lib.kda_chunk_prefill_workspace_size(1, 8192, 32, 128, 128, 64) == 32 * 128 * slot(128)
+    # segments: at most floor(160 MiB / (pairs * slot)) chunks, the chunks
+    # split into equal segments; a state is carried between segments
+    def seg(pairs, nchunks, dk=128, dv=128):
+        cap = max(1, (160 << 20) // (pairs * slot(dk, dv)))
+        if cap >= nchunks:
+            return nchunks
+        nseg = -(-nchunks // cap)
+        return -(-nchunks // nseg)
+
+    def ws(pairs, nchunks, dk=128, dv=128):
+        s = seg(pairs, nchunks, dk, dv)
+        return pairs * s * slot(dk, dv) + (pairs * dk * dv * 4 if s < nchunks else 0)
+
+    assert seg(32, 128) == 32                      # B=1, H=32, T=8192: 4 segments of 32
+    assert lib.kda_chunk_prefill_workspace_size(1, 8192, 32, 128, 128, 64) == \
+        32 * 32 * slot(128) + 32 * 128 * 128 * 4
     assert lib.kda_chunk_prefill_workspace_size(2, 130, 3, 64, 128, 64) == 6 * 3 * slot(64)
-    # long sequences: segments of floor(2^30 / (pairs * slot)) chunks + a state
-    seg = (1 << 30) // (32 * slot(128))
-    assert lib.kda_chunk_prefill_workspace_size(1, 1 << 20, 32, 128, 128, 64) == \
-        32 * seg * slot(128) + 32 * 128 * 128 * 4
+    assert lib.kda_chunk_prefill_workspace_size(1, 1 << 20, 32, 128, 128, 64) == ws(32, 1 << 14)
+    assert lib.kda_chunk_prefill_workspace_size(1, 4096, 8, 128, 128, 64) == ws(8, 64)
+    assert ws(8, 64) == 8 * 64 * slot(128)         # fits: one segment, no carried state
+    monkeypatch.setenv("KDA_PREFILL_SEG", "5")
+    assert lib.kda_chunk_prefill_workspace_size(1, 8192, 32, 128, 128, 64) == \
+        32 * 5 * slot(128) + 32 * 128 * 128 * 4
+    monkeypatch.delenv("KDA_PREFILL_SEG")
     # one chunk, many chains, varlen, unsupported sizes: no workspace
     assert lib.kda_chunk_prefill_workspace_size(1, 64, 32, 128, 128, 64) == 0
     assert lib.kda_chunk_prefill_workspace_size(4, 8192, 32, 128, 128, 64) == 0
@@ -116,9 +134,7 @@ def test_workspace_size_queries(lib, monkeypatch):
     monkeypatch.setenv("KDA_PREFILL_PATH", "fused")
     assert lib.kda_chunk_prefill_workspace_size(1, 8192, 32, 128, 128, 64) == 0
     monkeypatch.setenv("KDA_PREFILL_PATH", "split")
-    seg = (1 << 30) // (128 * slot(128))
-    assert lib.kda_chunk_prefill_workspace_size(4, 8192, 32, 128, 128, 64) == \
-        128 * seg * slot(128) + 128 * 128 * 128 * 4
+    assert lib.kda_chunk_prefill_workspace_size(4, 8192, 32, 128, 128, 64) == ws(128, 128)
     monkeypatch.delenv("KDA_PREFILL_PATH")
     # a call that needs a workspace is refused without one, or with one too small
     # (B=1, T=130, H=2, d=64: 3 chunks x 2 chains)
