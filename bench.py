@@ -272,7 +272,8 @@ def main():
     # the library: the staged two-kernel form below 128 (sequence, head) pairs).
     forced = os.environ.get("KDA_PREFILL_PATH")
     staged = forced == "split" or (forced != "fused" and B * H < 128 and T > 64)
-    pre_kernels = ("kda_stage_kernel + kda_chain_kernel (staged form: 2 launches per call)"
+    pre_kernels = ("kda_stage_kernel + kda_chain_kernel (staged form: one pair of launches per "
+                   "segment of chunks)"
                    if staged else "kda_prefill_kernel")
     out = {
         "metric": "KDA prefill tokens/s + decode us/step (B=256); % of MFMA / HBM peak",
