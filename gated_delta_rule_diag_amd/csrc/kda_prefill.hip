@@ -87,10 +87,9 @@ struct Lay {
   static constexpr int OFF_XT = OFF_SBT + 16 * P_OP;         // X^T [16][64]
   static constexpr int OFF_UT = OFF_XT + 16 * P_T;           // U^T [16][64]
   static constexpr int OFF_T = OFF_X + SZ_X;                 // T [64][64] (fp32 L^-1 first)
-  static constexpr int OFF_TMP = OFF_T + kC * P_T;           // 3 x 16x16 fp32 (solve)
   static constexpr int RG = 16;                              // row groups (4 rows) of the decay prep
   static constexpr int OFF_GP = OFF_T;                       // group products [RG][DK] (step 1 only)
-  static constexpr int OFF_GM = OFF_TMP + 3 * 256 * 4;       // gamma_m [DK]
+  static constexpr int OFF_GM = OFF_T + kC * P_T;           // gamma_m [DK]
   static constexpr int OFF_DL = OFF_GM + DK * 4;             // gamma_n / gamma_m [DK]
   static constexpr int OFF_GN = OFF_DL + DK * 4;             // gamma_n [DK]
   static constexpr int OFF_BE = OFF_GN + DK * 4;             // beta [64]
@@ -490,7 +489,6 @@ __device__ __forceinline__ void prep_chunk(char* smem, const float4 (&av)[4], co
   char* const sP = smem + L::OFF_P;
   char* const sT = smem + L::OFF_T;
   float* const sLi = reinterpret_cast<float*>(smem + L::OFF_T);
-  float* const sTmp = reinterpret_cast<float*>(smem + L::OFF_TMP);
   float* const sGP = reinterpret_cast<float*>(smem + L::OFF_GP);
   float* const sGM = reinterpret_cast<float*>(smem + L::OFF_GM);
   float* const sDL = reinterpret_cast<float*>(smem + L::OFF_DL);
@@ -652,63 +650,48 @@ tT[g][2] = a2; tR[g][2] = b2; tI[g][2] = c2_;
   // 3a: inverses D_R = (I + N)^-1 of the four 16x16 unit-lower diagonal
   // blocks (N = A_RR strictly lower, so N^16 = 0):
   //     (I + N)^-1 = (I - N)(I + N^2)(I + N^4)(I + N^8),
-  // wave R < 4 for block R, fp32 MFMA, the powers of N in place of A_RR (not
-  // needed later) and the partial products in the diagonal block of L^-1.
-  // Waves 4.. (or all waves after their block) clear the upper blocks of L^-1.
+  // wave R < 4 for block R, fp32 MFMA, entirely in registers.  A 16x16 matrix
+  // M is held twice, in the MFMA result layout of M (lane (lr, lg) element q
+  // = M[4lg + q][lr]) and of M^T (= M[lr][4lg + q]).  With the product index
+  // k = 4lg + s in step s of four 16x16x4 MFMAs, M^T's copy is an A operand
+  // and M's a B operand, so (XY) = mm(X^T copy, Y copy) and
+  // (XY)^T = mm(Y copy, X^T copy) need no layout change; every factor is a
+  // polynomial in N, so all of them commute.  Waves 4.. (or all waves after
+  // their block) clear the upper blocks of L^-1.
   if (w < 4) {
     const int R = w;
-    float* const Nb = sA + 16 * R * L::P_AF + 16 * R;   // N, then N^2, N^4, N^8
-    float* const Xb = sLi + 16 * R * L::P_AF + 16 * R;  // partial products
-    // fp32 16x16x4 operands: A lane = (row lr, k = 4s + lg), B lane = (k = 4s +
-    // lg, column lr); result lane = (rows 4lg + q, column lr).
-    auto ldA = [&](const float* m, float (&f)[4]) {
-#pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) f[s4] = m[lr * L::P_AF + 4 * s4 + lg];
-    };
-    auto ldB = [&](const float* m, float (&f)[4]) {
-#pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) f[s4] = m[(4 * s4 + lg) * L::P_AF + lr];
-    };
-    auto stC = [&](float* m, const f4& c) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) m[(4 * lg + q) * L::P_AF + lr] = c[q];
-    };
-    auto mm = [&](const float (&fa)[4], const float (&fb)[4], f4 c) {
+    const float* const Nb = sA + 16 * R * L::P_AF + 16 * R;
+    float* const Xb = sLi + 16 * R * L::P_AF + 16 * R;
+    auto mm = [&](const f4& fa, const f4& fb, f4 c) {
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) c = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[s4], fb[s4], c, 0, 0, 0);
       return c;
     };
-    // LDS accesses of one wave execute in order; only the compiler must not
-    // move them across each other.
-    auto order = [] { __atomic_signal_fence(__ATOMIC_SEQ_CST); };
-    float aN[4], bN[4], aX[4], aP[4], bP[4];
-    f4 xc;  // current partial product, result layout
-    ldA(Nb, aN);
-    ldB(Nb, bN);
+    f4 No, Nt, Xo, Xt;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) xc[q] = (4 * lg + q == lr ? 1.f : 0.f) - Nb[(4 * lg + q) * L::P_AF + lr];
-#pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) aX[s4] = (4 * s4 + lg == lr ? 1.f : 0.f) - aN[s4];
-    f4 pc = mm(aN, bN, f4{0.f, 0.f, 0.f, 0.f});  // N^2
+    for (int q = 0; q < 4; ++q) {
+      No[q] = Nb[(4 * lg + q) * L::P_AF + lr];
+      Nt[q] = Nb[lr * L::P_AF + 4 * lg + q];
+      const float id = 4 * lg + q == lr ? 1.f : 0.f;
+      Xo[q] = id - No[q];
+      Xt[q] = id - Nt[q];
+    }
+    const f4 zero = f4{0.f, 0.f, 0.f, 0.f};
+    f4 Po = mm(Nt, No, zero), Pt = mm(No, Nt, zero);   // N^2
 #pragma unroll
     for (int e = 0; e < 3; ++e) {
-      // pc = N^(2^(e+1)); X <- X + X pc
-      order();
-      stC(Nb, pc);
-      order();
-      ldA(Nb, aP);
-      ldB(Nb, bP);
-      xc = mm(aX, bP, xc);
+      // X <- X + X P with P = N^(2^(e+1)); then P <- P P
+      const f4 Xo2 = mm(Xt, Po, Xo), Xt2 = mm(Po, Xt, Xt);
       if (e < 2) {
-        pc = mm(aP, bP, f4{0.f, 0.f, 0.f, 0.f});
-        order();
-        stC(Xb, xc);
-        order();
-        ldA(Xb, aX);
+        const f4 Po2 = mm(Pt, Po, zero), Pt2 = mm(Po, Pt, zero);
+        Po = Po2;
+        Pt = Pt2;
       }
+      Xo = Xo2;
+      Xt = Xt2;
     }
-    order();
-    stC(Xb, xc);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) Xb[(4 * lg + q) * L::P_AF + lr] = Xo[q];
   }
   constexpr int w0 = NW > 4 ? 4 : 0;
   if (w >= w0) {
@@ -723,30 +706,28 @@ tT[g][2] = a2; tR[g][2] = b2; tI[g][2] = c2_;
   }
   lds_barrier();
   // 3b: off-diagonal blocks row block by row block:
-  //     L^-1_{R,I} = -D_R (sum_{I<=J<R} A_{R,J} L^-1_{J,I}),  wave I, fp32 MFMA.
+  //     L^-1_{R,I} = -D_R (sum_{I<=J<R} A_{R,J} L^-1_{J,I}),  wave I, fp32 MFMA,
+  // product index k = 4lg + s in step s (A rows read as float4); the sum,
+  // in the result layout, is directly the B operand of the product with D_R.
 #pragma unroll
   for (int R = 1; R < 4; ++R) {
     if (w < R) {
       const int I = w;
       f4 y = f4{0.f, 0.f, 0.f, 0.f};
       for (int J = I; J < R; ++J) {
-#pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) {
-          const float a = sA[(16 * R + lr) * L::P_AF + 16 * J + 4 * s4 + lg];
-          const float bb = sLi[(16 * J + 4 * s4 + lg) * L::P_AF + 16 * I + lr];
-          y = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bb, y, 0, 0, 0);
-        }
+        const float4 a = *reinterpret_cast<const float4*>(sA + (16 * R + lr) * L::P_AF + 16 * J + 4 * lg);
+        const float* bb = sLi + (16 * J + 4 * lg) * L::P_AF + 16 * I + lr;
+        y = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, bb[0], y, 0, 0, 0);
+        y = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, bb[L::P_AF], y, 0, 0, 0);
+        y = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, bb[2 * L::P_AF], y, 0, 0, 0);
+        y = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, bb[3 * L::P_AF], y, 0, 0, 0);
       }
-      float* tmp = sTmp + 256 * I;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) tmp[(4 * lg + q) * 16 + lr] = y[q];
+      const float4 d = *reinterpret_cast<const float4*>(sLi + (16 * R + lr) * L::P_AF + 16 * R + 4 * lg);
       f4 x = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) {
-        const float a = sLi[(16 * R + lr) * L::P_AF + 16 * R + 4 * s4 + lg];
-        const float bb = tmp[(4 * s4 + lg) * 16 + lr];
-        x = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bb, x, 0, 0, 0);
-      }
+      x = __builtin_amdgcn_mfma_f32_16x16x4f32(d.x, y[0], x, 0, 0, 0);
+      x = __builtin_amdgcn_mfma_f32_16x16x4f32(d.y, y[1], x, 0, 0, 0);
+      x = __builtin_amdgcn_mfma_f32_16x16x4f32(d.z, y[2], x, 0, 0, 0);
+      x = __builtin_amdgcn_mfma_f32_16x16x4f32(d.w, y[3], x, 0, 0, 0);
 #pragma unroll
       for (int q = 0; q < 4; ++q) sLi[(16 * R + 4 * lg + q) * L::P_AF + 16 * I + lr] = -x[q];
     }
