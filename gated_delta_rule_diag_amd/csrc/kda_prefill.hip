@@ -180,6 +180,35 @@ __device__ __forceinline__ void split(float x, uint16_t& h, uint16_t& l) {
   l = bf_bits(lb);
 }
 
+// c + A B for 16x16 blocks: lane (lr, lg) holds a[j] = A[lr][4lg + j] and
+// b[j] = B[4lg + j][lr]; the result lane holds rows 4lg + q of column lr.
+// bf16 inputs: split operands on the 16x16x16 bf16 MFMA (three products);
+// fp32 inputs: four 16x16x4 fp32 MFMAs.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+template <bool BF>
+__device__ __forceinline__ f4 mm16x16(const f4& a, const f4& b, f4 c) {
+  if constexpr (BF) {
+    s16x4 ah, al, bh, bl;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint16_t h, l;
+      split(a[j], h, l);
+      ah[j] = short(h);
+      al[j] = short(l);
+      split(b[j], h, l);
+      bh[j] = short(h);
+      bl[j] = short(l);
+    }
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, bh, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bl, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bh, c, 0, 0, 0);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], c, 0, 0, 0);
+  }
+  return c;
+}
+
 // One element (row, kk).
 template <bool BF>
 __device__ __forceinline__ void st1(char* base, int pitch, int row, int kk, float x) {
@@ -650,45 +679,35 @@ tT[g][2] = a2; tR[g][2] = b2; tI[g][2] = c2_;
   // 3a: inverses D_R = (I + N)^-1 of the four 16x16 unit-lower diagonal
   // blocks (N = A_RR strictly lower, so N^16 = 0):
   //     (I + N)^-1 = (I - N)(I + N^2)(I + N^4)(I + N^8),
-  // wave R < 4 for block R, fp32 MFMA, entirely in registers.  A 16x16 matrix
-  // M is held twice, in the MFMA result layout of M (lane (lr, lg) element q
-  // = M[4lg + q][lr]) and of M^T (= M[lr][4lg + q]).  With the product index
-  // k = 4lg + s in step s of four 16x16x4 MFMAs, M^T's copy is an A operand
-  // and M's a B operand, so (XY) = mm(X^T copy, Y copy) and
-  // (XY)^T = mm(Y copy, X^T copy) need no layout change; every factor is a
-  // polynomial in N, so all of them commute.  Waves 4.. (or all waves after
-  // their block) clear the upper blocks of L^-1.
+  // wave R < 4 for block R, entirely in registers.  In the result layout a
+  // lane holds M[4lg + q][lr] of a 16x16 matrix M (its B-operand quad for
+  // mm16x16); the same layout of M^T holds M[lr][4lg + q] (M's A-operand
+  // quad).  Every factor is a polynomial in N, so all of them commute: X P is
+  // computed as P X from P^T's copy and X's, and each power P is kept with its
+  // transpose, (P P)^T = mm(P's copy, P^T's copy).  Waves 4.. (or all waves
+  // after their block) clear the upper blocks of L^-1.
   if (w < 4) {
     const int R = w;
     const float* const Nb = sA + 16 * R * L::P_AF + 16 * R;
     float* const Xb = sLi + 16 * R * L::P_AF + 16 * R;
-    auto mm = [&](const f4& fa, const f4& fb, f4 c) {
-#pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) c = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[s4], fb[s4], c, 0, 0, 0);
-      return c;
-    };
-    f4 No, Nt, Xo, Xt;
+    f4 No, Nt, Xo;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       No[q] = Nb[(4 * lg + q) * L::P_AF + lr];
       Nt[q] = Nb[lr * L::P_AF + 4 * lg + q];
-      const float id = 4 * lg + q == lr ? 1.f : 0.f;
-      Xo[q] = id - No[q];
-      Xt[q] = id - Nt[q];
+      Xo[q] = (4 * lg + q == lr ? 1.f : 0.f) - No[q];
     }
     const f4 zero = f4{0.f, 0.f, 0.f, 0.f};
-    f4 Po = mm(Nt, No, zero), Pt = mm(No, Nt, zero);   // N^2
+    f4 Po = mm16x16<BF>(Nt, No, zero), Pt = mm16x16<BF>(No, Nt, zero);   // N^2
 #pragma unroll
     for (int e = 0; e < 3; ++e) {
-      // X <- X + X P with P = N^(2^(e+1)); then P <- P P
-      const f4 Xo2 = mm(Xt, Po, Xo), Xt2 = mm(Po, Xt, Xt);
+      // X <- X + P X with P = N^(2^(e+1)); then P <- P P
+      Xo = mm16x16<BF>(Pt, Xo, Xo);
       if (e < 2) {
-        const f4 Po2 = mm(Pt, Po, zero), Pt2 = mm(Po, Pt, zero);
+        const f4 Po2 = mm16x16<BF>(Pt, Po, zero), Pt2 = mm16x16<BF>(Po, Pt, zero);
         Po = Po2;
         Pt = Pt2;
       }
-      Xo = Xo2;
-      Xt = Xt2;
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) Xb[(4 * lg + q) * L::P_AF + lr] = Xo[q];
@@ -706,28 +725,23 @@ tT[g][2] = a2; tR[g][2] = b2; tI[g][2] = c2_;
   }
   lds_barrier();
   // 3b: off-diagonal blocks row block by row block:
-  //     L^-1_{R,I} = -D_R (sum_{I<=J<R} A_{R,J} L^-1_{J,I}),  wave I, fp32 MFMA,
-  // product index k = 4lg + s in step s (A rows read as float4); the sum,
-  // in the result layout, is directly the B operand of the product with D_R.
+  //     L^-1_{R,I} = -D_R (sum_{I<=J<R} A_{R,J} L^-1_{J,I}),  wave I
+  // (the sum, in the result layout, is directly the B operand of the
+  // product with D_R).
 #pragma unroll
   for (int R = 1; R < 4; ++R) {
     if (w < R) {
       const int I = w;
       f4 y = f4{0.f, 0.f, 0.f, 0.f};
       for (int J = I; J < R; ++J) {
-        const float4 a = *reinterpret_cast<const float4*>(sA + (16 * R + lr) * L::P_AF + 16 * J + 4 * lg);
+        const float4 a4 = *reinterpret_cast<const float4*>(sA + (16 * R + lr) * L::P_AF + 16 * J + 4 * lg);
         const float* bb = sLi + (16 * J + 4 * lg) * L::P_AF + 16 * I + lr;
-        y = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, bb[0], y, 0, 0, 0);
-        y = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, bb[L::P_AF], y, 0, 0, 0);
-        y = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, bb[2 * L::P_AF], y, 0, 0, 0);
-        y = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, bb[3 * L::P_AF], y, 0, 0, 0);
+        const f4 a = f4{a4.x, a4.y, a4.z, a4.w};
+        const f4 b = f4{bb[0], bb[L::P_AF], bb[2 * L::P_AF], bb[3 * L::P_AF]};
+        y = mm16x16<BF>(a, b, y);
       }
-      const float4 d = *reinterpret_cast<const float4*>(sLi + (16 * R + lr) * L::P_AF + 16 * R + 4 * lg);
-      f4 x = f4{0.f, 0.f, 0.f, 0.f};
-      x = __builtin_amdgcn_mfma_f32_16x16x4f32(d.x, y[0], x, 0, 0, 0);
-      x = __builtin_amdgcn_mfma_f32_16x16x4f32(d.y, y[1], x, 0, 0, 0);
-      x = __builtin_amdgcn_mfma_f32_16x16x4f32(d.z, y[2], x, 0, 0, 0);
-      x = __builtin_amdgcn_mfma_f32_16x16x4f32(d.w, y[3], x, 0, 0, 0);
+      const float4 d4 = *reinterpret_cast<const float4*>(sLi + (16 * R + lr) * L::P_AF + 16 * R + 4 * lg);
+      const f4 x = mm16x16<BF>(f4{d4.x, d4.y, d4.z, d4.w}, y, f4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
       for (int q = 0; q < 4; ++q) sLi[(16 * R + 4 * lg + q) * L::P_AF + 16 * I + lr] = -x[q];
     }
