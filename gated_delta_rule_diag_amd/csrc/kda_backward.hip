@@ -19,14 +19,18 @@
 //      the last to the first.  While chunk c is walked backwards, chunk c-1's
 //      token states are recomputed forward from its checkpoint into the other
 //      half of a per-workgroup scratch: the two token chains are independent,
-//      so their latencies overlap and one column-sum barrier serves both;
+//      so their latencies overlap;
 //   3. kda_bwd_reduce_kernel: sums the per-slab partials (a fixed order, so
 //      the result is deterministic).
 //
-// Thread layout: thread t owns key rows 2 (t / 4) and 2 (t / 4) + 1 and value
-// columns 4 (t % 4) .. +3 of the workgroup's 16: row sums are four local adds
-// and two lane exchanges, column sums two local adds, four lane exchanges and
-// the waves through LDS (double-buffered by step parity: one barrier per step).
+// Layout: wave w of a workgroup owns value columns 4w .. 4w+3 of the
+// workgroup's 16 and every key row (lane l holds rows DK/64 * l ..), so the
+// column sums of a step (St^T k and G^T k) are reductions inside one wave
+// (DPP within rows of 16 lanes, then the four row sums read out): no barrier
+// per token.  The row sums (dq, dk, da, over the wave's 4 columns) and db are
+// outputs only: each wave stages them in LDS and after one barrier per token
+// the workgroup adds the four waves' values in a fixed order and writes the
+// slab's partials.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -36,12 +40,11 @@
 namespace kda {
 namespace {
 
-constexpr int kC = 64;    // chunk length (checkpoint interval)
-constexpr int kVS = 16;   // value columns per workgroup
-constexpr int kCPT = 4;   // value columns per thread
-constexpr int kRPT = 2;   // key rows per thread
-constexpr int kTPR = kVS / kCPT;   // threads per row pair
-constexpr int kE = kRPT * kCPT;    // state elements per thread
+constexpr int kC = 64;     // chunk length (checkpoint interval)
+constexpr int kVS = 16;    // value columns per workgroup
+constexpr int kCPW = 4;    // value columns per wave
+constexpr int kNW = kVS / kCPW;   // waves per workgroup
+constexpr int kNT = 64 * kNW;     // threads per workgroup
 
 __device__ __forceinline__ void lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
@@ -49,18 +52,43 @@ __device__ __forceinline__ void lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-template <bool BF16>
-__device__ __forceinline__ float ld_in(const void* p, int64_t i) {
+// Consecutive values of a bf16 or float array.
+template <bool BF16, int N>
+__device__ __forceinline__ void ld_in(const void* p, int64_t i, float (&x)[N]) {
+  static_assert(N == 1 || N == 2, "one or two values");
   if constexpr (BF16) {
-    return __uint_as_float(uint32_t(static_cast<const uint16_t*>(p)[i]) << 16);
+    if constexpr (N == 2) {
+      const uint32_t r = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p) + i);
+      x[0] = __uint_as_float(r << 16);
+      x[1] = __uint_as_float(r & 0xffff0000u);
+    } else {
+      x[0] = __uint_as_float(uint32_t(static_cast<const uint16_t*>(p)[i]) << 16);
+    }
   } else {
-    return static_cast<const float*>(p)[i];
+    if constexpr (N == 2) {
+      const float2 a = *reinterpret_cast<const float2*>(static_cast<const float*>(p) + i);
+      x[0] = a.x;
+      x[1] = a.y;
+    } else {
+      x[0] = static_cast<const float*>(p)[i];
+    }
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void ld_f(const float* p, float (&x)[N]) {
+  if constexpr (N == 2) {
+    const float2 a = *reinterpret_cast<const float2*>(p);
+    x[0] = a.x;
+    x[1] = a.y;
+  } else {
+    x[0] = p[0];
   }
 }
 
 // Four consecutive values (8-byte aligned for bf16, 16-byte for float).
 template <bool BF16>
-__device__ __forceinline__ void ld4(const void* p, int64_t i, float (&x)[kCPT]) {
+__device__ __forceinline__ void ld4(const void* p, int64_t i, float (&x)[kCPW]) {
   if constexpr (BF16) {
     const uint2 r = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + i);
     x[0] = __uint_as_float(r.x << 16);
@@ -82,67 +110,92 @@ __device__ __forceinline__ void stf4(float* p, const float* x) {
   *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
 }
 
-// The thread's 2 x 4 slab elements of a [DK][DV] state (row stride DV).
-__device__ __forceinline__ void ld_slab(const float* p, int DV, float (&x)[kE]) {
-  ldf4(p, x);
-  ldf4(p + DV, x + kCPT);
-}
-
-__device__ __forceinline__ void st_slab(float* p, int DV, const float (&x)[kE]) {
-  stf4(p, x);
-  stf4(p + DV, x + kCPT);
-}
-
-// Sum over the workgroup's 16 columns of a row: 4 local values and the 3
-// partner lanes.
-__device__ __forceinline__ float row_sum(const float* x) {
-  float s = (x[0] + x[1]) + (x[2] + x[3]);
-  s += __shfl_xor(s, 1);
-  return s + __shfl_xor(s, 2);
-}
-
-// Column sums over all DK rows for NV vectors of this thread's four columns
-// (x[v][e]: vector v, column e, already summed over the thread's two rows).
-template <int NW, int NV>
-__device__ __forceinline__ void col_sums(float (&x)[NV][kCPT], float (*red)[NW][NV][kVS],
-                                         int parity) {
-  const int t = threadIdx.x, l = t & 63, w = t >> 6;
-#pragma unroll
-  for (int v = 0; v < NV; ++v)
-#pragma unroll
-    for (int e = 0; e < kCPT; ++e)
-#pragma unroll
-      for (int off = kTPR; off < 64; off <<= 1) x[v][e] += __shfl_xor(x[v][e], off);
-  if (l < kTPR) {
-#pragma unroll
-    for (int v = 0; v < NV; ++v)
-#pragma unroll
-      for (int e = 0; e < kCPT; ++e) red[parity][w][v][kCPT * l + e] = x[v][e];
+// Key rows (RPL of them) or four value columns of a bf16 or float input, kept
+// as loaded and converted at use (so that a prefetched value is not waited
+// for where it is loaded).
+template <bool BF16, int RPL>
+struct RowsIn;
+template <int RPL>
+struct RowsIn<true, RPL> {
+  uint32_t w;
+  __device__ void load(const void* p, int64_t i) {
+    const uint16_t* b = static_cast<const uint16_t*>(p) + i;
+    if constexpr (RPL == 2) w = *reinterpret_cast<const uint32_t*>(b);
+    else w = *b;
   }
-  lds_sync();
-  const int c0 = kCPT * (t % kTPR);
+  __device__ float operator[](int r) const {
+    return r == 0 ? __uint_as_float(w << 16) : __uint_as_float(w & 0xffff0000u);
+  }
+};
+template <int RPL>
+struct RowsIn<false, RPL> {
+  float x[RPL];
+  __device__ void load(const void* p, int64_t i) { ld_f<RPL>(static_cast<const float*>(p) + i, x); }
+  __device__ float operator[](int r) const { return x[r]; }
+};
+template <bool BF16>
+struct ColsIn;
+template <>
+struct ColsIn<true> {
+  uint2 w;
+  __device__ void load(const void* p, int64_t i) {
+    w = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + i);
+  }
+  __device__ float operator[](int e) const {
+    const uint32_t x = e < 2 ? w.x : w.y;
+    return (e & 1) ? __uint_as_float(x & 0xffff0000u) : __uint_as_float(x << 16);
+  }
+};
+template <>
+struct ColsIn<false> {
+  float x[kCPW];
+  __device__ void load(const void* p, int64_t i) { ldf4(static_cast<const float*>(p) + i, x); }
+  __device__ float operator[](int e) const { return x[e]; }
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
+                                                                0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float lane_val(float x, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
+}
+
+// Sums over the 64 lanes of a wave of N values each (every lane gets the
+// totals): lane pairs and quads, then rotations by 4 and 8 inside each row
+// of 16 lanes, then the four row sums added in a fixed order.
+template <int N>
+__device__ __forceinline__ void wave_sums(float (&x)[N]) {
 #pragma unroll
-  for (int v = 0; v < NV; ++v)
+  for (int i = 0; i < N; ++i) x[i] += dpp<0xB1>(x[i]);    // quad_perm [1,0,3,2]
 #pragma unroll
-    for (int e = 0; e < kCPT; ++e) {
-      float s = 0.f;
+  for (int i = 0; i < N; ++i) x[i] += dpp<0x4E>(x[i]);    // quad_perm [2,3,0,1]
 #pragma unroll
-      for (int ww = 0; ww < NW; ++ww) s += red[parity][ww][v][c0 + e];
-      x[v][e] = s;
-    }
+  for (int i = 0; i < N; ++i) x[i] += dpp<0x124>(x[i]);   // row_ror:4
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] += dpp<0x128>(x[i]);   // row_ror:8
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    x[i] = (lane_val(x[i], 0) + lane_val(x[i], 16)) + (lane_val(x[i], 32) + lane_val(x[i], 48));
 }
 
 template <int DK, bool BF16>
-__global__ __launch_bounds__(DK / kRPT * kTPR) void kda_bwd_kernel(BackwardArgs p) {
-  constexpr int NT = DK / kRPT * kTPR;
-  constexpr int NW = NT / 64;
-  __shared__ float red[2][NW][2][kVS];
+__global__ __launch_bounds__(kNT) void kda_bwd_kernel(BackwardArgs p) {
+  static_assert(kNW == 4, "the flush adds four waves' partials");
+  constexpr int RPL = DK / 64;       // key rows per lane
+  constexpr int E = RPL * kCPW;      // state elements per lane
   __shared__ float sU[2][kC][kVS];   // u of a chunk's tokens (this slab), two chunks
   __shared__ float sR[2][kC][kVS];   // v - p
+  __shared__ float ring[2][3][kNW][DK];   // dq, dk, da per wave, two tokens
+  __shared__ float ringb[2][kNW];         // db per wave
 
   const int t = threadIdx.x;
-  const int i0 = kRPT * (t / kTPR);      // first key row
-  const int jc = kCPT * (t % kTPR);      // first of this thread's columns in the slab
+  const int l = t & 63;
+  const int w = t >> 6;
+  const int i0 = RPL * l;                // first key row of this lane
+  const int jc = kCPW * w;               // first of this wave's columns in the slab
   const int H = p.H, DV = p.DV;
   const int nslab = DV / kVS;
 
@@ -155,196 +208,237 @@ __global__ __launch_bounds__(DK / kRPT * kTPR) void kda_bwd_kernel(BackwardArgs 
   const int64_t pr = b / nslab;
   const int h = int(pr % H);
   const int64_t n = pr / H;
-  const int col = slab * kVS + jc;       // first value column of this thread
+  const int col = slab * kVS + jc;       // first value column of this wave
   const int64_t T = p.T;
   const int64_t nchunks = (T + kC - 1) / kC;
   const int64_t state_off = pr * DK * DV + int64_t(i0) * DV + col;
-  // token states: [2 chunk buffers][64 tokens][NT threads][8 floats]
-  float* scratch = p.scratch + b * (2 * int64_t(kC) * NT * kE) + int64_t(t) * kE;
-  auto slot = [&](int64_t c, int s) { return scratch + ((c & 1) * kC + s) * int64_t(NT) * kE; };
+  // token states: [2 chunk buffers][64 tokens][kNT threads][E floats]
+  float* scratch = p.scratch + b * (2 * int64_t(kC) * kNT * E) + int64_t(t) * E;
+  auto slot = [&](int64_t c, int s) { return scratch + ((c & 1) * kC + s) * int64_t(kNT) * E; };
   auto row_of = [&](int64_t c, int s) { return (n * T + c * kC + s) * H + h; };
 
+  auto ld_state = [&](const float* src, float (&S)[E]) {
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) ldf4(src + int64_t(r) * DV, S + r * kCPW);
+  };
   // state at the start of chunk c (snapshot c-1 is the state after chunk c-1)
-  auto checkpoint = [&](int64_t c, float (&S)[kE]) {
+  auto checkpoint = [&](int64_t c, float (&S)[E]) {
     if (c > 0) {
-      ld_slab(p.snapshots + ((n * p.snap_per_seq + (c - 1)) * H + h) * int64_t(DK) * DV +
-                  int64_t(i0) * DV + col, DV, S);
+      ld_state(p.snapshots + ((n * p.snap_per_seq + (c - 1)) * H + h) * int64_t(DK) * DV +
+                   int64_t(i0) * DV + col, S);
     } else if (p.state_in) {
-      ld_slab(p.state_in + state_off, DV, S);
+      ld_state(p.state_in + state_off, S);
     } else {
 #pragma unroll
-      for (int e = 0; e < kE; ++e) S[e] = 0.f;
+      for (int e = 0; e < E; ++e) S[e] = 0.f;
     }
   };
 
-  float G[kE], S[kE];
+  float G[E], S[E];
   if (p.d_state_out) {
-    ld_slab(p.d_state_out + state_off, DV, G);
+    ld_state(p.d_state_out + state_off, G);
   } else {
 #pragma unroll
-    for (int e = 0; e < kE; ++e) G[e] = 0.f;
+    for (int e = 0; e < E; ++e) G[e] = 0.f;
   }
 
-  // One forward token of chunk c (full or the last one): keeps S before the
-  // token, then S <- Diag(a) S + k u^T.  The column sum p = St^T k is shared
-  // with the backward token of the same step (slot 1 of the sums).
-  float fa[kRPT], fk[kRPT], fb = 0.f, fv[kCPT];
-  auto fwd_pre = [&](int64_t c, int s, float (&x)[kCPT]) {
-    const int64_t row = row_of(c, s);
-#pragma unroll
-    for (int r = 0; r < kRPT; ++r) {
-      fa[r] = p.alpha[row * DK + i0 + r];
-      fk[r] = ld_in<BF16>(p.k, row * DK + i0 + r);
-    }
-    fb = p.beta[row];
-    ld4<BF16>(p.v, row * DV + col, fv);
-    float* dst = slot(c, s);
-    stf4(dst, S);
-    stf4(dst + kCPT, S + kCPT);
-#pragma unroll
-    for (int r = 0; r < kRPT; ++r)
-#pragma unroll
-      for (int e = 0; e < kCPT; ++e) S[r * kCPT + e] *= fa[r];
-#pragma unroll
-    for (int e = 0; e < kCPT; ++e) x[e] = S[e] * fk[0] + S[kCPT + e] * fk[1];
+  // Inputs of one forward token and of one backward token, loaded a step
+  // ahead of their use (within a chunk: the backward token's state was
+  // stored when its chunk was recomputed, a pass earlier).
+  struct FIn {
+    float a[RPL], b;
+    RowsIn<BF16, RPL> k;
+    ColsIn<BF16> v;
   };
-  auto fwd_post = [&](int64_t c, int s, const float (&pcol)[kCPT]) {
+  struct BIn {
+    float a[RPL], b, dout[kCPW], Sp[E];
+    RowsIn<BF16, RPL> k, q;
+  };
+  auto load_f = [&](int64_t c, int s, FIn& x) {
+    const int64_t row = row_of(c, s);
+    ld_f<RPL>(p.alpha + row * DK + i0, x.a);
+    x.k.load(p.k, row * DK + i0);
+    x.b = p.beta[row];
+    x.v.load(p.v, row * DV + col);
+  };
+  auto load_b = [&](int64_t c, int sb, BIn& x) {
+    const int64_t row = row_of(c, sb);
+    ld_f<RPL>(p.alpha + row * DK + i0, x.a);
+    x.k.load(p.k, row * DK + i0);
+    x.q.load(p.q, row * DK + i0);
+    x.b = p.beta[row];
+    ldf4(p.d_o + row * DV + col, x.dout);
+    const float* src = slot(c, sb);
 #pragma unroll
-    for (int e = 0; e < kCPT; ++e) {
-      const float r_ = fv[e] - pcol[e];   // v - p
-      const float u = fb * r_;
+    for (int e = 0; e < E; e += 4) ldf4(src + e, x.Sp + e);
+  };
+
+  // One forward token of chunk c: keeps S before the token, then
+  // S <- Diag(a) S + k u^T with u = b (v - St^T k).
+  auto fwd_token = [&](int64_t c, int s, const FIn& f) {
+    float* dst = slot(c, s);
 #pragma unroll
-      for (int r = 0; r < kRPT; ++r) S[r * kCPT + e] += fk[r] * u;
-      if (i0 == 0) {
+    for (int e = 0; e < E; e += 4) stf4(dst + e, S + e);
+    float x[kCPW];
+#pragma unroll
+    for (int e = 0; e < kCPW; ++e) {
+      x[e] = 0.f;
+#pragma unroll
+      for (int r = 0; r < RPL; ++r) {
+        S[r * kCPW + e] *= f.a[r];
+        x[e] += S[r * kCPW + e] * f.k[r];
+      }
+    }
+    wave_sums<kCPW>(x);
+#pragma unroll
+    for (int e = 0; e < kCPW; ++e) {
+      const float r_ = f.v[e] - x[e];   // v - p
+      const float u = f.b * r_;
+#pragma unroll
+      for (int r = 0; r < RPL; ++r) S[r * kCPW + e] += f.k[r] * u;
+      if (l == 0) {
         sU[c & 1][s][jc + e] = u;
         sR[c & 1][s][jc + e] = r_;
       }
     }
   };
 
+  // Backward token sb of chunk c with inputs x (and, when f is given, the
+  // forward token s of chunk c-1 between its two halves).  Every memory
+  // instruction is issued by every lane, so each step issues the same number
+  // of them and the memory-counter waits for loads issued a step earlier do
+  // not cover the stores in between: the per-wave row sums go through LDS
+  // (one barrier per token) and all threads write the slab's sums; values
+  // that are the same in every lane (dv, db) are stored by all lanes.
+  int par = 0;
+  auto bwd_token = [&](int64_t c, int sb, const BIn& x, int64_t cf_c, int cf_s, const FIn* f) {
+    const int64_t brow = row_of(c, sb);
+    float u[kCPW], rr[kCPW], St[E];
+#pragma unroll
+    for (int e = 0; e < kCPW; ++e) {
+      u[e] = sU[c & 1][sb][jc + e];
+      rr[e] = sR[c & 1][sb][jc + e];
+    }
+    // G += q do^T (o_t = S'^T q_t); dq = S' do; du = G^T k
+    float dq[RPL], du[kCPW];
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+      float xq = 0.f;
+#pragma unroll
+      for (int e = 0; e < kCPW; ++e) {
+        const int q_ = r * kCPW + e;
+        St[q_] = x.a[r] * x.Sp[q_];
+        G[q_] += x.q[r] * x.dout[e];
+        xq += (St[q_] + x.k[r] * u[e]) * x.dout[e];
+      }
+      dq[r] = xq;
+    }
+#pragma unroll
+    for (int e = 0; e < kCPW; ++e) {
+      du[e] = 0.f;
+#pragma unroll
+      for (int r = 0; r < RPL; ++r) du[e] += G[r * kCPW + e] * x.k[r];
+    }
+    // the forward token of chunk c-1 at the same step: its column sum is
+    // independent of this one, so the two reductions overlap
+    if (f) fwd_token(cf_c, cf_s, *f);
+    wave_sums<kCPW>(du);
+    float dk[RPL], da[RPL], db = 0.f;
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) dk[r] = da[r] = 0.f;
+#pragma unroll
+    for (int e = 0; e < kCPW; ++e) {
+      const float dp = -x.b * du[e];
+      db += du[e] * rr[e];
+#pragma unroll
+      for (int r = 0; r < RPL; ++r) {
+        const int q_ = r * kCPW + e;
+        const float dSt = G[q_] + x.k[r] * dp;
+        dk[r] += G[q_] * u[e] + St[q_] * dp;
+        da[r] += dSt * x.Sp[q_];
+        G[q_] = x.a[r] * dSt;
+      }
+    }
+    float dv4[kCPW];
+#pragma unroll
+    for (int e = 0; e < kCPW; ++e) dv4[e] = x.b * du[e];
+    stf4(p.dv + brow * DV + col, dv4);
+    if (l == 0) ringb[par][w] = db;
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+      ring[par][0][w][i0 + r] = dq[r];
+      ring[par][1][w][i0 + r] = dk[r];
+      ring[par][2][w][i0 + r] = da[r];
+    }
+    lds_sync();
+    // the slab's sums over the four waves, in a fixed order: thread t writes
+    // (dq or dk, row t % DK) and da of row t % DK (threads t and t + DK
+    // write the same da value when DK < 256), and db
+    {
+      const int i = t % DK;
+      const int qa = t < DK ? 0 : 1;
+      const float* r0 = &ring[par][qa][0][i];
+      const float* r2 = &ring[par][2][0][i];
+      const float v0 = (r0[0] + r0[DK]) + (r0[2 * DK] + r0[3 * DK]);
+      const float v2 = (r2[0] + r2[DK]) + (r2[2 * DK] + r2[3 * DK]);
+      const int64_t prow = (brow * DK + i) * nslab + slab;
+      (qa == 0 ? p.part_dq : p.part_dk)[prow] = v0;
+      p.part_da[prow] = v2;
+      const float* rb = ringb[par];
+      p.part_db[brow * nslab + slab] = (rb[0] + rb[1]) + (rb[2] + rb[3]);
+    }
+    par ^= 1;
+  };
+
+  FIn cf, nf;
+  BIn cb, nb;
   // prologue: the last chunk's token states
   {
     const int64_t c = nchunks - 1;
     const int len = int(T - c * kC);
     checkpoint(c, S);
-    int parity = 0;
     for (int s = 0; s < len; ++s) {
-      float x[2][kCPT];
-      fwd_pre(c, s, x[1]);
-#pragma unroll
-      for (int e = 0; e < kCPT; ++e) x[0][e] = 0.f;
-      col_sums<NW, 2>(x, red, parity);
-      parity ^= 1;
-      fwd_post(c, s, x[1]);
+      load_f(c, s, cf);
+      fwd_token(c, s, cf);
     }
   }
-  lds_sync();
 
-  int parity = 0;
   for (int64_t c = nchunks - 1; c >= 0; --c) {
     const int len = int(T - c * kC < kC ? T - c * kC : kC);
     const bool fwd = c > 0;                 // chunk c-1 is recomputed meanwhile (always full)
     if (fwd) checkpoint(c - 1, S);
-    const int steps = fwd ? kC : len;
-    for (int s = 0; s < steps; ++s) {
-      const bool bwd = s < len;
-      const int sb = len - 1 - s;           // backward token of chunk c
-      float x[2][kCPT];
-      // backward, first half: G += q do^T, dq = S' do, du partial = G^T k
-      float a[kRPT], kk[kRPT], qq[kRPT], bt = 0.f, dout[kCPT], Sp[kE], u[kCPT], rr[kCPT];
-      float St[kE], dq[kRPT] = {0.f, 0.f};
-      int64_t brow = 0;
-      if (bwd) {
-        brow = row_of(c, sb);
-#pragma unroll
-        for (int r = 0; r < kRPT; ++r) {
-          a[r] = p.alpha[brow * DK + i0 + r];
-          kk[r] = ld_in<BF16>(p.k, brow * DK + i0 + r);
-          qq[r] = ld_in<BF16>(p.q, brow * DK + i0 + r);
-        }
-        bt = p.beta[brow];
-        ldf4(p.d_o + brow * DV + col, dout);
-        const float* src = slot(c, sb);
-        ldf4(src, Sp);
-        ldf4(src + kCPT, Sp + kCPT);
-#pragma unroll
-        for (int e = 0; e < kCPT; ++e) {
-          u[e] = sU[c & 1][sb][jc + e];
-          rr[e] = sR[c & 1][sb][jc + e];
-        }
-#pragma unroll
-        for (int r = 0; r < kRPT; ++r) {
-          float xq[kCPT];
-#pragma unroll
-          for (int e = 0; e < kCPT; ++e) {
-            const int q_ = r * kCPT + e;
-            St[q_] = a[r] * Sp[q_];
-            G[q_] += qq[r] * dout[e];                  // o_t = S'^T q_t
-            xq[e] = (St[q_] + kk[r] * u[e]) * dout[e];  // dq: S' do
-          }
-          dq[r] = row_sum(xq);
-        }
-#pragma unroll
-        for (int e = 0; e < kCPT; ++e) x[0][e] = G[e] * kk[0] + G[kCPT + e] * kk[1];
-      } else {
-#pragma unroll
-        for (int e = 0; e < kCPT; ++e) x[0][e] = 0.f;
+    if (fwd && len == kC) {
+      // the steady state: both tokens in every step, inputs a step ahead in
+      // two sets used alternately (no register copies, so each wait sits at
+      // the first use of its input; the loads past the chunk's end repeat
+      // its last token: no branch)
+      load_f(c - 1, 0, cf);
+      load_b(c, kC - 1, cb);
+      for (int s = 0; s < kC; s += 2) {
+        load_b(c, kC - 2 - s, nb);
+        load_f(c - 1, s + 1, nf);
+        bwd_token(c, kC - 1 - s, cb, c - 1, s, &cf);
+        const int sn = s + 2 < kC ? s + 2 : kC - 1;
+        load_b(c, kC - 1 - sn, cb);
+        load_f(c - 1, sn, cf);
+        bwd_token(c, kC - 2 - s, nb, c - 1, s + 1, &nf);
       }
-      if (fwd) {
-        fwd_pre(c - 1, s, x[1]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < kCPT; ++e) x[1][e] = 0.f;
-      }
-      col_sums<NW, 2>(x, red, parity);
-      parity ^= 1;
-      if (fwd) fwd_post(c - 1, s, x[1]);
-      if (bwd) {
-        // backward, second half
-        const float* du = x[0];
-        float xk[kRPT][kCPT], xa[kRPT][kCPT], xb[kCPT];
-#pragma unroll
-        for (int e = 0; e < kCPT; ++e) {
-          const float dp = -bt * du[e];
-          xb[e] = du[e] * rr[e];
-#pragma unroll
-          for (int r = 0; r < kRPT; ++r) {
-            const int q_ = r * kCPT + e;
-            const float dSt = G[q_] + kk[r] * dp;
-            xk[r][e] = G[q_] * u[e] + St[q_] * dp;
-            xa[r][e] = dSt * Sp[q_];
-            G[q_] = a[r] * dSt;
-          }
-        }
-        float dk[kRPT], da[kRPT];
-#pragma unroll
-        for (int r = 0; r < kRPT; ++r) {
-          dk[r] = row_sum(xk[r]);
-          da[r] = row_sum(xa[r]);
-        }
-        if ((t % kTPR) == 0) {
-          // partials are slab-minor: [token row][key row][slab]
-          const int64_t prow = (brow * DK + i0) * nslab + slab;
-#pragma unroll
-          for (int r = 0; r < kRPT; ++r) {
-            p.part_dq[prow + r * nslab] = dq[r];
-            p.part_dk[prow + r * nslab] = dk[r];
-            p.part_da[prow + r * nslab] = da[r];
-          }
-        }
-        if (i0 == 0) {
-          float dv4[kCPT];
-#pragma unroll
-          for (int e = 0; e < kCPT; ++e) dv4[e] = bt * du[e];
-          stf4(p.dv + brow * DV + col, dv4);
-          const float db = row_sum(xb);
-          if (t == 0) p.part_db[brow * nslab + slab] = db;
+    } else {
+      const int steps = fwd ? kC : len;
+      for (int s = 0; s < steps; ++s) {
+        if (fwd) load_f(c - 1, s, cf);
+        if (s < len) {
+          load_b(c, len - 1 - s, cb);
+          bwd_token(c, len - 1 - s, cb, c - 1, s, fwd ? &cf : nullptr);
+        } else {
+          fwd_token(c - 1, s, cf);
         }
       }
     }
-    lds_sync();   // chunk c-1's u, v - p visible; chunk c's buffers free
   }
-  if (p.d_state_in) st_slab(p.d_state_in + state_off, DV, G);
+#pragma unroll
+  for (int r = 0; r < RPL; ++r)
+    if (p.d_state_in) stf4(p.d_state_in + state_off + int64_t(r) * DV, G + r * kCPW);
 }
 
 // dq, dk, dalpha (per element) and dbeta: sums of the NS per-slab partials,
@@ -375,7 +469,7 @@ __global__ __launch_bounds__(256) void kda_bwd_reduce_kernel(BackwardArgs p) {
 template <int DK, bool BF16>
 void launch_bwd_t(const BackwardArgs& a, hipStream_t st) {
   const unsigned nb = unsigned(int64_t(a.N) * a.H * (a.DV / kVS));
-  hipLaunchKernelGGL((kda_bwd_kernel<DK, BF16>), dim3(nb), dim3(DK / kRPT * kTPR), 0, st, a);
+  hipLaunchKernelGGL((kda_bwd_kernel<DK, BF16>), dim3(nb), dim3(kNT), 0, st, a);
   const int64_t threads = a.rows * DK;
   const dim3 grid(unsigned((threads + 255) / 256));
   if (a.DV == 128) hipLaunchKernelGGL((kda_bwd_reduce_kernel<DK, 8>), grid, dim3(256), 0, st, a);
