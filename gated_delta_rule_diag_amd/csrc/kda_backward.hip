@@ -101,6 +101,42 @@ __device__ __forceinline__ void ld4(const void* p, int64_t i, float (&x)[kCPW]) 
   }
 }
 
+// N = 2 or 4 consecutive floats (8- or 16-byte aligned).
+template <int N>
+__device__ __forceinline__ void ldfn(const float* p, float* x) {
+  if constexpr (N == 4) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  } else {
+    static_assert(N == 2, "two or four floats");
+    const float2 a = *reinterpret_cast<const float2*>(p);
+    x[0] = a.x; x[1] = a.y;
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void stfn(float* p, const float* x) {
+  if constexpr (N == 4) {
+    *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+  } else {
+    static_assert(N == 2, "two or four floats");
+    *reinterpret_cast<float2*>(p) = make_float2(x[0], x[1]);
+  }
+}
+
+// E floats in pieces of at most four.
+template <int E>
+__device__ __forceinline__ void ld_elems(const float* p, float* x) {
+#pragma unroll
+  for (int e = 0; e < E; e += (E >= 4 ? 4 : E)) ldfn<(E >= 4 ? 4 : E)>(p + e, x + e);
+}
+
+template <int E>
+__device__ __forceinline__ void st_elems(float* p, const float* x) {
+#pragma unroll
+  for (int e = 0; e < E; e += (E >= 4 ? 4 : E)) stfn<(E >= 4 ? 4 : E)>(p + e, x + e);
+}
+
 __device__ __forceinline__ void ldf4(const float* p, float* x) {
   const float4 a = *reinterpret_cast<const float4*>(p);
   x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
@@ -137,21 +173,40 @@ template <bool BF16>
 struct ColsIn;
 template <>
 struct ColsIn<true> {
-  uint2 w;
+  uint32_t w[kCPW / 2];
   __device__ void load(const void* p, int64_t i) {
-    w = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + i);
+    const uint16_t* b = static_cast<const uint16_t*>(p) + i;
+    if constexpr (kCPW == 4) {
+      const uint2 r = *reinterpret_cast<const uint2*>(b);
+      w[0] = r.x;
+      w[kCPW / 2 - 1] = r.y;
+    } else {
+      w[0] = *reinterpret_cast<const uint32_t*>(b);
+    }
   }
   __device__ float operator[](int e) const {
-    const uint32_t x = e < 2 ? w.x : w.y;
+    const uint32_t x = w[e >> 1];
     return (e & 1) ? __uint_as_float(x & 0xffff0000u) : __uint_as_float(x << 16);
   }
 };
 template <>
 struct ColsIn<false> {
   float x[kCPW];
-  __device__ void load(const void* p, int64_t i) { ldf4(static_cast<const float*>(p) + i, x); }
+  __device__ void load(const void* p, int64_t i) { ldfn<kCPW>(static_cast<const float*>(p) + i, x); }
   __device__ float operator[](int e) const { return x[e]; }
 };
+
+// Sum of the kNW per-wave values r[0], r[stride], ..., pairwise.
+__device__ __forceinline__ float sum_waves(const float* r, int stride) {
+  float x[kNW];
+#pragma unroll
+  for (int i = 0; i < kNW; ++i) x[i] = r[i * stride];
+#pragma unroll
+  for (int h = 1; h < kNW; h <<= 1)
+#pragma unroll
+    for (int i = 0; i + h < kNW; i += 2 * h) x[i] += x[i + h];
+  return x[0];
+}
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
@@ -163,9 +218,17 @@ __device__ __forceinline__ float lane_val(float x, int lane) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
 }
 
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_rows(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
+                                                                ROWS, 0xF, false));
+}
+
 // Sums over the 64 lanes of a wave of N values each (every lane gets the
 // totals): lane pairs and quads, then rotations by 4 and 8 inside each row
-// of 16 lanes, then the four row sums added in a fixed order.
+// of 16 lanes (every lane holds its row's sum), then lane 15 of rows 0 and 2
+// added into rows 1 and 3 and lane 31 into rows 2 and 3, so that lane 63
+// holds (r2 + r3) + (r0 + r1); it is read out for all lanes.
 template <int N>
 __device__ __forceinline__ void wave_sums(float (&x)[N]) {
 #pragma unroll
@@ -177,13 +240,15 @@ __device__ __forceinline__ void wave_sums(float (&x)[N]) {
 #pragma unroll
   for (int i = 0; i < N; ++i) x[i] += dpp<0x128>(x[i]);   // row_ror:8
 #pragma unroll
-  for (int i = 0; i < N; ++i)
-    x[i] = (lane_val(x[i], 0) + lane_val(x[i], 16)) + (lane_val(x[i], 32) + lane_val(x[i], 48));
+  for (int i = 0; i < N; ++i) x[i] += dpp_rows<0x142, 0xA>(x[i]);   // row_bcast:15 into rows 1, 3
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] += dpp_rows<0x143, 0xC>(x[i]);   // row_bcast:31 into rows 2, 3
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] = lane_val(x[i], 63);
 }
 
 template <int DK, bool BF16>
 __global__ __launch_bounds__(kNT) void kda_bwd_kernel(BackwardArgs p) {
-  static_assert(kNW == 4, "the flush adds four waves' partials");
   constexpr int RPL = DK / 64;       // key rows per lane
   constexpr int E = RPL * kCPW;      // state elements per lane
   __shared__ float sU[2][kC][kVS];   // u of a chunk's tokens (this slab), two chunks
@@ -219,7 +284,7 @@ __global__ __launch_bounds__(kNT) void kda_bwd_kernel(BackwardArgs p) {
 
   auto ld_state = [&](const float* src, float (&S)[E]) {
 #pragma unroll
-    for (int r = 0; r < RPL; ++r) ldf4(src + int64_t(r) * DV, S + r * kCPW);
+    for (int r = 0; r < RPL; ++r) ldfn<kCPW>(src + int64_t(r) * DV, S + r * kCPW);
   };
   // state at the start of chunk c (snapshot c-1 is the state after chunk c-1)
   auto checkpoint = [&](int64_t c, float (&S)[E]) {
@@ -267,18 +332,16 @@ __global__ __launch_bounds__(kNT) void kda_bwd_kernel(BackwardArgs p) {
     x.k.load(p.k, row * DK + i0);
     x.q.load(p.q, row * DK + i0);
     x.b = p.beta[row];
-    ldf4(p.d_o + row * DV + col, x.dout);
+    ldfn<kCPW>(p.d_o + row * DV + col, x.dout);
     const float* src = slot(c, sb);
-#pragma unroll
-    for (int e = 0; e < E; e += 4) ldf4(src + e, x.Sp + e);
+    ld_elems<E>(src, x.Sp);
   };
 
   // One forward token of chunk c: keeps S before the token, then
   // S <- Diag(a) S + k u^T with u = b (v - St^T k).
   auto fwd_token = [&](int64_t c, int s, const FIn& f) {
     float* dst = slot(c, s);
-#pragma unroll
-    for (int e = 0; e < E; e += 4) stf4(dst + e, S + e);
+    st_elems<E>(dst, S);
     float x[kCPW];
 #pragma unroll
     for (int e = 0; e < kCPW; ++e) {
@@ -362,7 +425,7 @@ __global__ __launch_bounds__(kNT) void kda_bwd_kernel(BackwardArgs p) {
     float dv4[kCPW];
 #pragma unroll
     for (int e = 0; e < kCPW; ++e) dv4[e] = x.b * du[e];
-    stf4(p.dv + brow * DV + col, dv4);
+    stfn<kCPW>(p.dv + brow * DV + col, dv4);
     if (l == 0) ringb[par][w] = db;
 #pragma unroll
     for (int r = 0; r < RPL; ++r) {
@@ -371,21 +434,21 @@ __global__ __launch_bounds__(kNT) void kda_bwd_kernel(BackwardArgs p) {
       ring[par][2][w][i0 + r] = da[r];
     }
     lds_sync();
-    // the slab's sums over the four waves, in a fixed order: thread t writes
-    // (dq or dk, row t % DK) and da of row t % DK (threads t and t + DK
-    // write the same da value when DK < 256), and db
+    // the slab's sums over the waves, in a fixed order: index x = t + kNT j
+    // is quantity min(x / DK, 2) (dq, dk, da) of row x % DK (indices past
+    // 3 DK write da values again), and every thread writes the same db
     {
-      const int i = t % DK;
-      const int qa = t < DK ? 0 : 1;
-      const float* r0 = &ring[par][qa][0][i];
-      const float* r2 = &ring[par][2][0][i];
-      const float v0 = (r0[0] + r0[DK]) + (r0[2 * DK] + r0[3 * DK]);
-      const float v2 = (r2[0] + r2[DK]) + (r2[2 * DK] + r2[3 * DK]);
-      const int64_t prow = (brow * DK + i) * nslab + slab;
-      (qa == 0 ? p.part_dq : p.part_dk)[prow] = v0;
-      p.part_da[prow] = v2;
-      const float* rb = ringb[par];
-      p.part_db[brow * nslab + slab] = (rb[0] + rb[1]) + (rb[2] + rb[3]);
+      constexpr int NPASS = (3 * DK + kNT - 1) / kNT;
+#pragma unroll
+      for (int j = 0; j < NPASS; ++j) {
+        const int x = t + kNT * j;
+        const int i = x % DK;
+        const int qn = x / DK < 2 ? x / DK : 2;
+        const float v = sum_waves(&ring[par][qn][0][i], DK);
+        const int64_t prow = (brow * DK + i) * nslab + slab;
+        (qn == 0 ? p.part_dq : (qn == 1 ? p.part_dk : p.part_da))[prow] = v;
+      }
+      p.part_db[brow * nslab + slab] = sum_waves(ringb[par], 1);
     }
     par ^= 1;
   };
@@ -438,7 +501,7 @@ __global__ __launch_bounds__(kNT) void kda_bwd_kernel(BackwardArgs p) {
   }
 #pragma unroll
   for (int r = 0; r < RPL; ++r)
-    if (p.d_state_in) stf4(p.d_state_in + state_off + int64_t(r) * DV, G + r * kCPW);
+    if (p.d_state_in) stfn<kCPW>(p.d_state_in + state_off + int64_t(r) * DV, G + r * kCPW);
 }
 
 // dq, dk, dalpha (per element) and dbeta: sums of the NS per-slab partials,
