@@ -76,6 +76,72 @@ def cpu_baseline(seconds, q, k, v, a, b):
     }
 
 
+def long_context(torch):
+    """Decode (B=1, H=32, d=128) from the end state of a prefill of T tokens,
+    T = 4K, 64K, 1M: the state does not grow with T, so neither does the step.
+    Prints one JSON line with the per-step times (eager, and with 16 steps in
+    one HIP graph) and the prefill times."""
+    from gated_delta_rule_diag_amd import kda
+
+    dev = torch.device("cuda:0")
+    H, D = 32, 128
+    g = torch.Generator(device=dev)
+    g.manual_seed(4)
+
+    def inputs(T):
+        q = torch.randn(1, T, H, D, device=dev, generator=g)
+        q = (q / q.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+        k = torch.randn(1, T, H, D, device=dev, generator=g)
+        k = (k / k.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+        v = torch.randn(1, T, H, D, device=dev, generator=g).to(torch.bfloat16)
+        a = torch.exp(-torch.exp(torch.rand(1, T, H, D, device=dev, generator=g) * 4 - 5))
+        b = torch.sigmoid(torch.randn(1, T, H, device=dev, generator=g))
+        return q, k, v, a, b
+
+    def elapsed_us(fn, reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3
+
+    dq, dk, dv, da, db = (t[:, 0].contiguous() for t in inputs(1))
+    o1 = torch.empty((1, H, D), device=dev, dtype=torch.float32)
+    rows = []
+    for T in (4096, 65536, 1 << 20):
+        x = inputs(T)
+        kda.chunk_prefill(*x)
+        torch.cuda.synchronize()
+        pre_us = elapsed_us(lambda: kda.chunk_prefill(*x), 2)
+        _, S = kda.chunk_prefill(*x)
+        del x
+        kda.decode_step(dq, dk, dv, da, db, S, o1)
+        torch.cuda.synchronize()
+        eager = elapsed_us(lambda: kda.decode_step(dq, dk, dv, da, db, S, o1), 1024)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            kda.decode_step(dq, dk, dv, da, db, S, o1)
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(16):
+                kda.decode_step(dq, dk, dv, da, db, S, o1)
+        graph.replay()
+        torch.cuda.synchronize()
+        in_graph = elapsed_us(graph.replay, 64) / 16
+        rows.append({"T": T, "prefill_us": pre_us, "prefill_tokens_per_s": T / (pre_us * 1e-6),
+                     "decode_us_per_step_eager": eager, "decode_us_per_step_hip_graph": in_graph})
+        del graph, S
+        torch.cuda.empty_cache()
+    print(json.dumps({"long_context": {"workload": "B=1 H=32 d=128 bf16 prefill of T tokens, then "
+                                                   "decode steps from its end state", "runs": rows}}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -88,6 +154,9 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one plain 512 MiB device-to-device copy before the timed region "
                          "(reference for HBM byte counters)")
+    ap.add_argument("--long-context", action="store_true",
+                    help="instead of the step: decode B=1 H=32 d=128 from the end states of "
+                         "prefills of 4K, 64K and 1M tokens (per-step time flat in T)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -96,6 +165,10 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.long_context:
+        long_context(torch)
+        return
 
     from gated_delta_rule_diag_amd import inputs as I
     from gated_delta_rule_diag_amd import kda
