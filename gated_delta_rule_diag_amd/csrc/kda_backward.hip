@@ -26,8 +26,9 @@
 // Layout: wave w of a workgroup owns value columns 4w .. 4w+3 of the
 // workgroup's 16 and every key row (lane l holds rows DK/64 * l ..), so the
 // column sums of a step (St^T k and G^T k) are reductions inside one wave
-// (DPP within rows of 16 lanes, then the four row sums read out): no barrier
-// per token.  The row sums (dq, dk, da, over the wave's 4 columns) and db are
+// (DPP within rows of 16 lanes, then row broadcasts into the last row, whose
+// lane 63 is read out): no barrier for them.  The row sums (dq, dk, da, over
+// the wave's 4 columns) and db are
 // outputs only: each wave stages them in LDS and after one barrier per token
 // the workgroup adds the four waves' values in a fixed order and writes the
 // slab's partials.
@@ -52,29 +53,6 @@ __device__ __forceinline__ void lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// Consecutive values of a bf16 or float array.
-template <bool BF16, int N>
-__device__ __forceinline__ void ld_in(const void* p, int64_t i, float (&x)[N]) {
-  static_assert(N == 1 || N == 2, "one or two values");
-  if constexpr (BF16) {
-    if constexpr (N == 2) {
-      const uint32_t r = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p) + i);
-      x[0] = __uint_as_float(r << 16);
-      x[1] = __uint_as_float(r & 0xffff0000u);
-    } else {
-      x[0] = __uint_as_float(uint32_t(static_cast<const uint16_t*>(p)[i]) << 16);
-    }
-  } else {
-    if constexpr (N == 2) {
-      const float2 a = *reinterpret_cast<const float2*>(static_cast<const float*>(p) + i);
-      x[0] = a.x;
-      x[1] = a.y;
-    } else {
-      x[0] = static_cast<const float*>(p)[i];
-    }
-  }
-}
-
 template <int N>
 __device__ __forceinline__ void ld_f(const float* p, float (&x)[N]) {
   if constexpr (N == 2) {
@@ -83,21 +61,6 @@ __device__ __forceinline__ void ld_f(const float* p, float (&x)[N]) {
     x[1] = a.y;
   } else {
     x[0] = p[0];
-  }
-}
-
-// Four consecutive values (8-byte aligned for bf16, 16-byte for float).
-template <bool BF16>
-__device__ __forceinline__ void ld4(const void* p, int64_t i, float (&x)[kCPW]) {
-  if constexpr (BF16) {
-    const uint2 r = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + i);
-    x[0] = __uint_as_float(r.x << 16);
-    x[1] = __uint_as_float(r.x & 0xffff0000u);
-    x[2] = __uint_as_float(r.y << 16);
-    x[3] = __uint_as_float(r.y & 0xffff0000u);
-  } else {
-    const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
-    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
   }
 }
 
@@ -135,15 +98,6 @@ template <int E>
 __device__ __forceinline__ void st_elems(float* p, const float* x) {
 #pragma unroll
   for (int e = 0; e < E; e += (E >= 4 ? 4 : E)) stfn<(E >= 4 ? 4 : E)>(p + e, x + e);
-}
-
-__device__ __forceinline__ void ldf4(const float* p, float* x) {
-  const float4 a = *reinterpret_cast<const float4*>(p);
-  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-}
-
-__device__ __forceinline__ void stf4(float* p, const float* x) {
-  *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
 }
 
 // Key rows (RPL of them) or four value columns of a bf16 or float input, kept
