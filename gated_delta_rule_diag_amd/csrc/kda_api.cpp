@@ -454,54 +454,71 @@ struct BwdLayout {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-BwdLayout bwd_layout(int B, int T, int H, int DK, int DV) {
+// Workspace of a backward call: the forward's workspace (fixed length only)
+// or the per-slab partial sums, whichever is larger (they are not live at
+// the same time), the forward's o, one state per full chunk, the reverse
+// pass's token-state scratch.  Packed sequences: T_fixed = 0, and the
+// snapshot rows are T_total / 64 (chunk j of the sequence starting at token
+// s is row s / 64 + j).
+BwdLayout bwd_layout(int N, int T_fixed, int64_t T_total, int H, int DK, int DV, bool varlen) {
   BwdLayout L{};
-  const size_t rows = size_t(B) * T * H, nslab = size_t(DV) / 16;
-  const size_t pw = kda::prefill_workspace_bytes(B, int64_t(B) * T, H, DK, DV, false);
+  const size_t rows = size_t(T_total) * H, nslab = size_t(DV) / 16;
+  const size_t pw = varlen ? 0 : kda::prefill_workspace_bytes(N, T_total, H, DK, DV, false);
   const size_t part = (3 * nslab * rows * DK + nslab * rows) * 4;
+  const size_t snap_rows = varlen ? size_t(T_total / 64) : size_t(N) * size_t(T_fixed / 64);
   L.fwd_or_part = 0;
   L.o = align256(pw > part ? pw : part);
   L.snaps = L.o + align256(rows * DV * 4);
-  L.scratch = L.snaps + align256(size_t(B) * (T / 64) * H * DK * DV * 4);
-  L.total = L.scratch + align256(kda::backward_scratch_bytes(B, H, DK, DV));
+  L.scratch = L.snaps + align256(snap_rows * H * DK * DV * 4);
+  L.total = L.scratch + align256(kda::backward_scratch_bytes(N, H, DK, DV));
   return L;
 }
 
-}  // namespace
-
-size_t kda_chunk_backward_workspace_size(int B, int T, int H, int DK, int DV, int chunk) {
-  if (B <= 0 || T <= 0 || H <= 0 || !dims_ok(DK) || !dims_ok(DV) || chunk != 64) return 0;
-  return bwd_layout(B, T, H, DK, DV).total;
-}
-
-kda_status_t kda_chunk_backward(int B, int T, int H, int DK, int DV, int chunk,
-                                kda_dtype_t in_dtype, const void* q, const void* k,
-                                const void* v, const float* alpha, const float* beta,
-                                const float* state_in, const float* d_o,
-                                const float* d_state_out, float* dq, float* dk, float* dv,
-                                float* dalpha, float* dbeta, float* d_state_in, void* workspace,
-                                size_t workspace_bytes, void* stream) {
-  if (B < 0 || T < 0 || H < 0) return fail(KDA_ERR_SHAPE, "negative size (B=%d T=%d H=%d)", B, T, H);
+kda_status_t run_backward(int N, int T_fixed, const int32_t* cu_seqlens, int64_t T_total, int H,
+                          int DK, int DV, int chunk, kda_dtype_t in_dtype, const void* q,
+                          const void* k, const void* v, const float* alpha, const float* beta,
+                          const float* state_in, const float* d_o, const float* d_state_out,
+                          float* dq, float* dk, float* dv, float* dalpha, float* dbeta,
+                          float* d_state_in, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  const bool varlen = cu_seqlens != nullptr;
   if (!dims_ok(DK) || !dims_ok(DV))
     return fail(KDA_ERR_UNSUPPORTED, "DK=%d DV=%d: only 64 and 128 are supported", DK, DV);
   if (chunk != 64) return fail(KDA_ERR_UNSUPPORTED, "chunk=%d: only 64 is supported", chunk);
   if (in_dtype != KDA_F32 && in_dtype != KDA_BF16)
     return fail(KDA_ERR_DTYPE, "unknown in_dtype %d", (int)in_dtype);
-  if (int64_t(B) * T * H > (int64_t(1) << 31) / 128 || int64_t(B) * H > (int64_t(1) << 24) ||
-      H > 65536)
-    return fail(KDA_ERR_UNSUPPORTED, "too large: B*T*H=%lld H=%d", (long long)B * T * H, H);
-  if (B == 0 || T == 0 || H == 0) return ok();
+  if (T_total * H > (int64_t(1) << 31) / 128 || int64_t(N) * H > (int64_t(1) << 24) || H > 65536)
+    return fail(KDA_ERR_UNSUPPORTED, "too large: tokens*H=%lld H=%d", (long long)(T_total * H), H);
+  if (N == 0 || H == 0) return ok();
+  const size_t ns = size_t(N) * H * DK * DV * 4;
+  if (T_total == 0) {
+    // no tokens: the initial state's gradient is the final state's
+    if (!d_state_in) return ok();
+    if (!aligned16(d_state_in) || (d_state_out && !aligned16(d_state_out)))
+      return fail(KDA_ERR_ALIGN, "d_state_in and d_state_out must be 16-byte aligned");
+    if (d_state_out && d_state_out != d_state_in && overlaps(d_state_in, ns, d_state_out, ns))
+      return fail(KDA_ERR_SHAPE, "d_state_in overlaps d_state_out");
+    kda::BackwardArgs a{};
+    a.N = N; a.H = H; a.DK = DK; a.DV = DV; a.T = 0; a.cu_seqlens = cu_seqlens; a.rows = 0;
+    a.in_bf16 = in_dtype == KDA_BF16;
+    a.d_state_out = d_state_out; a.d_state_in = d_state_in;
+    const char* msg = nullptr;
+    if (kda::launch_backward(a, stream, &msg) != 0)
+      return fail(KDA_ERR_HIP, "backward launch failed: %s", msg ? msg : "?");
+    return ok();
+  }
   const void* need[] = {q, k, v, alpha, beta, d_o, dq, dk, dv, dalpha, dbeta};
   for (const void* x : need)
     if (!x)
       return fail(KDA_ERR_NULL,
                   "q, k, v, alpha, beta, d_o, dq, dk, dv, dalpha and dbeta must be non-NULL");
   const size_t esz = in_dtype == KDA_BF16 ? 2 : 4;
-  const size_t rows = size_t(B) * T * H, ns = size_t(B) * H * DK * DV * 4;
-  const void* in[] = {q, k, v, alpha, beta, state_in, d_o, d_state_out};
+  const size_t rows = size_t(T_total) * H;
+  const void* in[] = {q, k, v, alpha, beta, state_in, d_o, d_state_out, cu_seqlens};
   const size_t in_b[] = {rows * DK * esz, rows * DK * esz, rows * DV * esz, rows * DK * 4,
-                         rows * 4, ns, rows * DV * 4, ns};
-  const char* in_n[] = {"q", "k", "v", "alpha", "beta", "state_in", "d_o", "d_state_out"};
+                         rows * 4, ns, rows * DV * 4, ns, size_t(N + 1) * 4};
+  const char* in_n[] = {"q", "k", "v", "alpha", "beta", "state_in", "d_o", "d_state_out",
+                        "cu_seqlens"};
   const void* out[] = {dq, dk, dv, dalpha, dbeta, d_state_in};
   const size_t out_b[] = {rows * DK * 4, rows * DK * 4, rows * DV * 4, rows * DK * 4, rows * 4, ns};
   const char* out_n[] = {"dq", "dk", "dv", "dalpha", "dbeta", "d_state_in"};
@@ -511,19 +528,19 @@ kda_status_t kda_chunk_backward(int B, int T, int H, int DK, int DV, int chunk,
     if (out[i] && !aligned16(out[i]))
       return fail(KDA_ERR_ALIGN, "%s is not 16-byte aligned", out_n[i]);
   for (int i = 0; i < 6; ++i) {
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < 9; ++j)
       if (overlaps(out[i], out_b[i], in[j], in_b[j]))
         return fail(KDA_ERR_SHAPE, "%s overlaps %s", out_n[i], in_n[j]);
     for (int j = i + 1; j < 6; ++j)
       if (overlaps(out[i], out_b[i], out[j], out_b[j]))
         return fail(KDA_ERR_SHAPE, "%s overlaps %s", out_n[i], out_n[j]);
   }
-  const BwdLayout L = bwd_layout(B, T, H, DK, DV);
+  const BwdLayout L = bwd_layout(N, T_fixed, T_total, H, DK, DV, varlen);
   if (!workspace || workspace_bytes < L.total)
     return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", L.total,
                 workspace ? workspace_bytes : size_t(0));
   if (!aligned16(workspace)) return fail(KDA_ERR_ALIGN, "workspace is not 16-byte aligned");
-  for (int j = 0; j < 8; ++j)
+  for (int j = 0; j < 9; ++j)
     if (overlaps(workspace, L.total, in[j], in_b[j]))
       return fail(KDA_ERR_SHAPE, "workspace overlaps %s", in_n[j]);
   for (int j = 0; j < 6; ++j)
@@ -533,23 +550,27 @@ kda_status_t kda_chunk_backward(int B, int T, int H, int DK, int DV, int chunk,
   char* ws = static_cast<char*>(workspace);
   // 1. forward with a snapshot after every chunk
   kda::PrefillArgs f{};
-  f.N = B; f.T_fixed = T; f.cu_seqlens = nullptr; f.T_total = int64_t(B) * T;
+  f.N = N; f.T_fixed = varlen ? 0 : T_fixed; f.cu_seqlens = cu_seqlens; f.T_total = T_total;
   f.H = H; f.DK = DK; f.DV = DV; f.in_bf16 = in_dtype == KDA_BF16;
   f.q = q; f.k = k; f.v = v; f.alpha = alpha; f.beta = beta;
   f.state_in = state_in; f.o = reinterpret_cast<float*>(ws + L.o); f.state_out = nullptr;
   f.workspace = ws + L.fwd_or_part; f.workspace_bytes = L.o;
-  f.snapshots = T >= 64 ? reinterpret_cast<float*>(ws + L.snaps) : nullptr;
+  const int64_t snap_rows = varlen ? T_total / 64 : int64_t(N) * (T_fixed / 64);
+  f.snapshots = snap_rows > 0 ? reinterpret_cast<float*>(ws + L.snaps) : nullptr;
   f.snap_every = 1;
+  f.snap_offsets = nullptr;
+  f.snap_rows = snap_rows;
   const char* msg = nullptr;
   if (kda::launch_prefill(f, stream, &msg) != 0)
     return fail(KDA_ERR_HIP, "backward: forward launch failed: %s", msg ? msg : "?");
   // 2-3. reverse pass and the reduction of the per-slab sums
   kda::BackwardArgs a{};
-  a.N = B; a.H = H; a.DK = DK; a.DV = DV; a.T = T; a.rows = int64_t(rows);
+  a.N = N; a.H = H; a.DK = DK; a.DV = DV; a.T = varlen ? 0 : T_fixed; a.cu_seqlens = cu_seqlens;
+  a.rows = int64_t(rows);
   a.in_bf16 = in_dtype == KDA_BF16;
   a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.state_in = state_in;
   a.d_o = d_o; a.d_state_out = d_state_out;
-  a.snapshots = reinterpret_cast<const float*>(ws + L.snaps); a.snap_per_seq = T / 64;
+  a.snapshots = reinterpret_cast<const float*>(ws + L.snaps); a.snap_per_seq = varlen ? 0 : T_fixed / 64;
   a.dq = dq; a.dk = dk; a.dv = dv; a.dalpha = dalpha; a.dbeta = dbeta; a.d_state_in = d_state_in;
   a.scratch = reinterpret_cast<float*>(ws + L.scratch);
   const size_t nslab = size_t(DV) / 16;
@@ -561,6 +582,50 @@ kda_status_t kda_chunk_backward(int B, int T, int H, int DK, int DV, int chunk,
   if (kda::launch_backward(a, stream, &msg) != 0)
     return fail(KDA_ERR_HIP, "backward launch failed: %s", msg ? msg : "?");
   return ok();
+}
+
+}  // namespace
+
+size_t kda_chunk_backward_workspace_size(int B, int T, int H, int DK, int DV, int chunk) {
+  if (B <= 0 || T <= 0 || H <= 0 || !dims_ok(DK) || !dims_ok(DV) || chunk != 64) return 0;
+  return bwd_layout(B, T, int64_t(B) * T, H, DK, DV, false).total;
+}
+
+kda_status_t kda_chunk_backward(int B, int T, int H, int DK, int DV, int chunk,
+                                kda_dtype_t in_dtype, const void* q, const void* k,
+                                const void* v, const float* alpha, const float* beta,
+                                const float* state_in, const float* d_o,
+                                const float* d_state_out, float* dq, float* dk, float* dv,
+                                float* dalpha, float* dbeta, float* d_state_in, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (B < 0 || T < 0 || H < 0) return fail(KDA_ERR_SHAPE, "negative size (B=%d T=%d H=%d)", B, T, H);
+  return run_backward(B, T, nullptr, int64_t(B) * T, H, DK, DV, chunk, in_dtype, q, k, v, alpha,
+                      beta, state_in, d_o, d_state_out, dq, dk, dv, dalpha, dbeta, d_state_in,
+                      workspace, workspace_bytes, stream);
+}
+
+size_t kda_chunk_backward_varlen_workspace_size(int N, int T_total, int H, int DK, int DV,
+                                                int chunk) {
+  if (N <= 0 || T_total <= 0 || H <= 0 || !dims_ok(DK) || !dims_ok(DV) || chunk != 64) return 0;
+  return bwd_layout(N, 0, T_total, H, DK, DV, true).total;
+}
+
+kda_status_t kda_chunk_backward_varlen(int N, int T_total, const int32_t* cu_seqlens, int H,
+                                       int DK, int DV, int chunk, kda_dtype_t in_dtype,
+                                       const void* q, const void* k, const void* v,
+                                       const float* alpha, const float* beta,
+                                       const float* state_in, const float* d_o,
+                                       const float* d_state_out, float* dq, float* dk, float* dv,
+                                       float* dalpha, float* dbeta, float* d_state_in,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  if (N < 0 || T_total < 0 || H < 0)
+    return fail(KDA_ERR_SHAPE, "negative size (N=%d T_total=%d H=%d)", N, T_total, H);
+  if (N > 0 && cu_seqlens == nullptr) return fail(KDA_ERR_NULL, "cu_seqlens must be non-NULL");
+  if (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u)
+    return fail(KDA_ERR_ALIGN, "cu_seqlens must be 4-byte aligned");
+  return run_backward(N, 0, N > 0 ? cu_seqlens : nullptr, T_total, H, DK, DV, chunk, in_dtype, q,
+                      k, v, alpha, beta, state_in, d_o, d_state_out, dq, dk, dv, dalpha, dbeta,
+                      d_state_in, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

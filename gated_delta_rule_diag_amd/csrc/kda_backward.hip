@@ -228,13 +228,15 @@ __global__ __launch_bounds__(kNT) void kda_bwd_kernel(BackwardArgs p) {
   const int h = int(pr % H);
   const int64_t n = pr / H;
   const int col = slab * kVS + jc;       // first value column of this wave
-  const int64_t T = p.T;
-  const int64_t nchunks = (T + kC - 1) / kC;
+  // this sequence's tokens: fixed length, or packed by cu_seqlens
+  const int64_t tok0 = p.cu_seqlens ? int64_t(p.cu_seqlens[n]) : n * p.T;
+  const int64_t T = p.cu_seqlens ? int64_t(p.cu_seqlens[n + 1]) - tok0 : p.T;
+  const int64_t nchunks = T > 0 ? (T + kC - 1) / kC : 0;
   const int64_t state_off = pr * DK * DV + int64_t(i0) * DV + col;
   // token states: [2 chunk buffers][64 tokens][kNT threads][E floats]
   float* scratch = p.scratch + b * (2 * int64_t(kC) * kNT * E) + int64_t(t) * E;
   auto slot = [&](int64_t c, int s) { return scratch + ((c & 1) * kC + s) * int64_t(kNT) * E; };
-  auto row_of = [&](int64_t c, int s) { return (n * T + c * kC + s) * H + h; };
+  auto row_of = [&](int64_t c, int s) { return (tok0 + c * kC + s) * H + h; };
 
   auto ld_state = [&](const float* src, float (&S)[E]) {
 #pragma unroll
@@ -243,8 +245,9 @@ __global__ __launch_bounds__(kNT) void kda_bwd_kernel(BackwardArgs p) {
   // state at the start of chunk c (snapshot c-1 is the state after chunk c-1)
   auto checkpoint = [&](int64_t c, float (&S)[E]) {
     if (c > 0) {
-      ld_state(p.snapshots + ((n * p.snap_per_seq + (c - 1)) * H + h) * int64_t(DK) * DV +
-                   int64_t(i0) * DV + col, S);
+      // snapshot of chunk c-1: row n * snap_per_seq + c - 1, or tok0 / 64 + c - 1 when packed
+      const int64_t srow = (p.cu_seqlens ? tok0 / kC : n * p.snap_per_seq) + (c - 1);
+      ld_state(p.snapshots + (srow * H + h) * int64_t(DK) * DV + int64_t(i0) * DV + col, S);
     } else if (p.state_in) {
       ld_state(p.state_in + state_off, S);
     } else {
@@ -410,7 +413,7 @@ __global__ __launch_bounds__(kNT) void kda_bwd_kernel(BackwardArgs p) {
   FIn cf, nf;
   BIn cb, nb;
   // prologue: the last chunk's token states
-  {
+  if (nchunks > 0) {
     const int64_t c = nchunks - 1;
     const int len = int(T - c * kC);
     checkpoint(c, S);
@@ -487,6 +490,7 @@ template <int DK, bool BF16>
 void launch_bwd_t(const BackwardArgs& a, hipStream_t st) {
   const unsigned nb = unsigned(int64_t(a.N) * a.H * (a.DV / kVS));
   hipLaunchKernelGGL((kda_bwd_kernel<DK, BF16>), dim3(nb), dim3(kNT), 0, st, a);
+  if (a.rows == 0) return;   // no tokens: only d_state_in (= d_state_out) is written
   const int64_t threads = a.rows * DK;
   const dim3 grid(unsigned((threads + 255) / 256));
   if (a.DV == 128) hipLaunchKernelGGL((kda_bwd_reduce_kernel<DK, 8>), grid, dim3(256), 0, st, a);

@@ -68,8 +68,9 @@ struct PoolDecodeArgs {
 // Backward pass (fixed-length batches, per-channel alpha).
 struct BackwardArgs {
   int N, H, DK, DV;
-  int64_t T;                   // tokens per sequence
-  int64_t rows;                // N * T * H token rows
+  int64_t T;                   // tokens per sequence (fixed length)
+  const int32_t* cu_seqlens;   // packed sequences: device [N + 1] (then T is unused), or nullptr
+  int64_t rows;                // token rows: N * T * H, or T_total * H when packed
   bool in_bf16;
   const void* q;
   const void* k;
@@ -79,7 +80,8 @@ struct BackwardArgs {
   const float* state_in;       // [N, H, DK, DV] or nullptr
   const float* d_o;            // [N, T, H, DV]
   const float* d_state_out;    // [N, H, DK, DV] or nullptr
-  const float* snapshots;      // state after every chunk: [N, snap_per_seq, H, DK, DV]
+  const float* snapshots;      // state after every chunk: [N, snap_per_seq, H, DK, DV]; packed:
+                               // chunk j of the sequence starting at token s is row s / 64 + j
   int64_t snap_per_seq;        // T / 64
   float* dq;                   // [N, T, H, DK]
   float* dk;

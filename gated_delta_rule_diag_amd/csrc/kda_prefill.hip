@@ -59,6 +59,7 @@ struct Params {
   int snap_every;     // a snapshot after every snap_every-th full chunk
   int64_t snap_per_seq;   // fixed length: sequence n's snapshot j is row n * snap_per_seq + j
   const int32_t* snap_off;  // varlen: row snap_off[n] + j, j < snap_off[n+1] - snap_off[n]
+                            // (NULL: row cu[n] / 64 + j)
   int64_t snap_rows;        // varlen: rows of snap (rows outside [0, snap_rows) are skipped)
   int alpha_scalar;   // alpha is [tokens][H] (one gate per token and head)
 };
@@ -996,8 +997,13 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_prefill_kernel(Params p
       const int64_t done = (tok0 - s0) / kC + 1;
       if (nv == kC && done % p.snap_every == 0) {
         const int64_t j = done / p.snap_every - 1;
-        if (p.snap_off == nullptr) {
+        if (p.snap_off == nullptr && p.cu == nullptr) {
           store_snapshot<DK, NSUB>(p.snap, n * p.snap_per_seq + j, h, H, DV, col0, S);
+        } else if (p.snap_off == nullptr) {
+          // packed sequences without offsets: chunk j of the sequence starting
+          // at token s0 goes to row s0 / 64 + j (rows of consecutive sequences
+          // never meet, and all are below T_total / 64)
+          if (s0 / kC + j < p.snap_rows) store_snapshot<DK, NSUB>(p.snap, s0 / kC + j, h, H, DV, col0, S);
         } else if (j < snap_cnt && snap_base + j >= 0 && snap_base + j < p.snap_rows) {
           store_snapshot<DK, NSUB>(p.snap, snap_base + j, h, H, DV, col0, S);
         }

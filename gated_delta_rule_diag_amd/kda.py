@@ -39,6 +39,8 @@ EXPORTED = (
     "kda_chunk_backward_workspace_size",
     "kda_chunk_backward",
     "kda_chunk_prefill_varlen_snapshots",
+    "kda_chunk_backward_varlen_workspace_size",
+    "kda_chunk_backward_varlen",
     "kda_status_string",
     "kda_last_error_message",
 )
@@ -83,6 +85,10 @@ def load_library(path: str = _LIB_PATH) -> ctypes.CDLL:
     lib.kda_chunk_backward_workspace_size.argtypes = [i, i, i, i, i, i]
     lib.kda_chunk_backward.restype = i
     lib.kda_chunk_backward.argtypes = [i, i, i, i, i, i, i] + [vp] * 15 + [sz, vp]
+    lib.kda_chunk_backward_varlen_workspace_size.restype = sz
+    lib.kda_chunk_backward_varlen_workspace_size.argtypes = [i] * 6
+    lib.kda_chunk_backward_varlen.restype = i
+    lib.kda_chunk_backward_varlen.argtypes = [i, i, vp, i, i, i, i, i] + [vp] * 15 + [sz, vp]
     lib.kda_chunk_prefill_varlen_snapshots.restype = i
     lib.kda_chunk_prefill_varlen_snapshots.argtypes = [i, i, vp, i, i, i, i, i] + [vp] * 8 + \
         [i, vp, i, vp, vp, sz, vp]
@@ -426,3 +432,44 @@ def chunk_prefill_varlen_snapshots(q, k, v, alpha, beta, cu_seqlens, every, init
         snaps.shape[0], _ptr(snaps), _ptr(workspace),
         0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(dev)))
     return o, st, snaps, snap_offsets
+
+
+def chunk_backward_varlen(q, k, v, alpha, beta, cu_seqlens, d_o, initial_state=None,
+                          d_final_state=None, chunk=64, workspace=None):
+    """Gradients of L = sum(o * d_o) + sum(S_T * d_final_state) for the packed
+    variable-length prefill (per-channel alpha).
+
+    Inputs as for :func:`chunk_prefill_varlen`; d_o [T_total,H,DV] float32;
+    d_final_state [N,H,DK,DV] float32 or None.
+    Returns (dq, dk, dv, dalpha, dbeta, d_initial_state), all float32.
+    """
+    Tt, H, DK = q.shape
+    DV = v.shape[-1]
+    dt = _in_dtype(q)
+    _need(q, "q", q.dtype)
+    _need(k, "k", q.dtype, (Tt, H, DK))
+    _need(v, "v", q.dtype, (Tt, H, DV))
+    _need(alpha, "alpha", torch.float32, (Tt, H, DK))
+    _need(beta, "beta", torch.float32, (Tt, H))
+    _need(d_o, "d_o", torch.float32, (Tt, H, DV))
+    _need(cu_seqlens, "cu_seqlens", torch.int32)
+    N = cu_seqlens.numel() - 1
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, (N, H, DK, DV))
+    if d_final_state is not None:
+        _need(d_final_state, "d_final_state", torch.float32, (N, H, DK, DV))
+    dev = q.device
+    f32 = dict(device=dev, dtype=torch.float32)
+    dq, dk, dal = (torch.empty((Tt, H, DK), **f32) for _ in range(3))
+    dv = torch.empty((Tt, H, DV), **f32)
+    db = torch.empty((Tt, H), **f32)
+    ds0 = torch.empty((N, H, DK, DV), **f32)
+    wsz = lib().kda_chunk_backward_varlen_workspace_size(N, Tt, H, DK, DV, chunk)
+    if wsz and workspace is None:
+        workspace = torch.empty(wsz, device=dev, dtype=torch.uint8)
+    _check(lib().kda_chunk_backward_varlen(
+        N, Tt, _ptr(cu_seqlens), H, DK, DV, chunk, dt, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+        _ptr(beta), _ptr(initial_state), _ptr(d_o), _ptr(d_final_state), _ptr(dq), _ptr(dk),
+        _ptr(dv), _ptr(dal), _ptr(db), _ptr(ds0), _ptr(workspace),
+        0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(dev)))
+    return dq, dk, dv, dal, db, ds0

@@ -263,7 +263,9 @@ kda_status_t kda_decode_pool(int N, int L, int H, int DK, int DV, kda_dtype_t in
  *                chunk-boundary states, its outputs and per-slab partial sums).
  * Outputs must not overlap inputs or each other.  The forward is recomputed
  * (with a state checkpoint per chunk); the reverse pass walks every chunk
- * backwards from its checkpoint; the result is deterministic.
+ * backwards from its checkpoint; the result is deterministic.  With T == 0
+ * only d_state_in is written (= d_state_out, or zeros) and no workspace is
+ * needed.
  */
 size_t kda_chunk_backward_workspace_size(int B, int T, int H, int DK, int DV, int chunk);
 kda_status_t kda_chunk_backward(int B, int T, int H, int DK, int DV, int chunk,
@@ -273,6 +275,29 @@ kda_status_t kda_chunk_backward(int B, int T, int H, int DK, int DV, int chunk,
                                 const float* d_state_out, float* dq, float* dk, float* dv,
                                 float* dalpha, float* dbeta, float* d_state_in, void* workspace,
                                 size_t workspace_bytes, void* stream);
+
+/*
+ * Backward pass of the packed variable-length prefill (training on packed
+ * sequences): as kda_chunk_backward, for the N sequences of
+ * kda_chunk_prefill_varlen (same cu_seqlens, token tensors [T_total,H,*],
+ * states [N,H,DK,DV]).
+ *   cu_seqlens   int32 DEVICE [N+1], 4-byte aligned, non-decreasing, from 0 to
+ *                T_total (not checked on the device)
+ *   workspace    at least kda_chunk_backward_varlen_workspace_size() bytes
+ *                (it depends on T_total only through the token count, so the
+ *                host never reads the lengths)
+ * A sequence of length 0 passes d_state_out through to d_state_in.
+ */
+size_t kda_chunk_backward_varlen_workspace_size(int N, int T_total, int H, int DK, int DV,
+                                                int chunk);
+kda_status_t kda_chunk_backward_varlen(int N, int T_total, const int32_t* cu_seqlens, int H,
+                                       int DK, int DV, int chunk, kda_dtype_t in_dtype,
+                                       const void* q, const void* k, const void* v,
+                                       const float* alpha, const float* beta,
+                                       const float* state_in, const float* d_o,
+                                       const float* d_state_out, float* dq, float* dk, float* dv,
+                                       float* dalpha, float* dbeta, float* d_state_in,
+                                       void* workspace, size_t workspace_bytes, void* stream);
 
 const char* kda_status_string(kda_status_t s);
 const char* kda_last_error_message(void);

@@ -289,7 +289,46 @@ def test_backward_argument_errors(lib):
     assert call(ws=None) == WS
     assert call(wsb=need - 1) == WS
     assert call(ws=ctypes.c_void_p(Q[0].value)) == SHAPE   # workspace over q
-    assert call(T=0) == OK
+    p = list(Q)
+    p[13] = None                                   # T = 0 and no d_state_in: nothing to do
+    assert call(T=0, ptrs=p) == OK
+
+
+def test_backward_varlen_argument_errors(lib):
+    # N=3 sequences, T_total=200 tokens, H=2, d=64 (f32): rows = 400; snapshot
+    # rows T_total // 64 = 3 (chunk j of the sequence starting at token s is
+    # row s // 64 + j); 3 * 2 * 4 slab workgroups of two-chunk token states
+    need = lib.kda_chunk_backward_varlen_workspace_size(3, 200, 2, 64, 64, 64)
+    part = (3 * 4 * 400 * 64 + 4 * 400) * 4
+    al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    assert need == al(part) + al(400 * 64 * 4) + al(3 * 2 * 64 * 64 * 4) + \
+        al(3 * 2 * 4 * 2 * 64 * 64 * 16 * 4)
+    assert lib.kda_chunk_backward_varlen_workspace_size(3, 200, 2, 96, 64, 64) == 0
+    assert lib.kda_chunk_backward_varlen_workspace_size(3, 0, 2, 64, 64, 64) == 0
+    big = ctypes.c_void_p(0x40000000)
+    Q = [ctypes.c_void_p(0x100000 * (i + 1)) for i in range(14)]
+    cu = ctypes.c_void_p(0x2000000)
+
+    def call(N=3, Tt=200, cu=cu, DK=64, ptrs=None, ws=big, wsb=need):
+        return lib.kda_chunk_backward_varlen(N, Tt, cu, 2, DK, 64, 64, 0, *(ptrs or Q), ws, wsb,
+                                             None)
+
+    assert call(N=-1) == SHAPE
+    assert call(Tt=-5) == SHAPE
+    assert call(cu=None) == NULL
+    assert "cu_seqlens" in lib.kda_last_error_message().decode()
+    assert call(cu=ctypes.c_void_p(cu.value + 2)) == ALIGN
+    assert call(DK=32) == UNSUP
+    assert call(ws=None) == WS
+    assert call(wsb=need - 1) == WS
+    p = list(Q)
+    p[8] = ctypes.c_void_p(Q[6].value + 64)        # dq over d_o
+    assert call(ptrs=p) == SHAPE
+    assert call(cu=ctypes.c_void_p(Q[8].value + 64)) == SHAPE   # dq over cu_seqlens
+    assert call(N=0, cu=None) == OK
+    p = list(Q)
+    p[13] = None
+    assert call(Tt=0, ptrs=p) == OK                # no tokens, no d_state_in: nothing to do
 
 
 def test_decode_pool_argument_errors(lib):

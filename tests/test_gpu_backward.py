@@ -76,3 +76,83 @@ def test_backward_b1_h32_t8192_head_subset():
     flush("[backward] B=1 T=8192 H=32 d=128 bf16, heads 0 and 31")
     errs = run_case(1, 8192, 32, 128, 128, "bf16", 730, with_state=False, heads=[0, 31])
     assert max(errs.values()) <= TOL["bf16"], errs
+
+
+def varlen_backward_reference(q, k, v, a, b, cu, do, S0, dST):
+    """Per-sequence oracle gradients, packed in sequence order."""
+    outs = [[] for _ in range(6)]
+    for n in range(len(cu) - 1):
+        s, e = cu[n], cu[n + 1]
+        sl = lambda x: x[None, s:e]  # noqa: E731
+        g = kda_backward(sl(q), sl(k), sl(v), sl(a), sl(b), S0[n:n + 1], sl(do), dST[n:n + 1])
+        for i in range(5):
+            outs[i].append(g[i][0])
+        outs[5].append(g[5][0])
+    return [np.concatenate(o) for o in outs[:5]] + [np.stack(outs[5])]
+
+
+@pytest.mark.parametrize("dt,d", [("bf16", 128), ("f32", 64)])
+def test_backward_varlen_matches_oracle(dt, d):
+    """Packed sequences of mixed lengths (empty, shorter than a chunk, exactly
+    one chunk, ragged multi-chunk), random initial states and final-state
+    gradients: every gradient against the per-sequence oracle."""
+    lengths = [37, 0, 64, 1, 200, 129]
+    H = 3
+    flush(f"[backward] varlen lengths={lengths} H={H} d={d} {dt}")
+    q, k, v, a, b, cu = I.packed_inputs(730, lengths, H, d, d, dt)
+    rng = np.random.default_rng(731)
+    do = rng.standard_normal((int(cu[-1]), H, d)).astype(np.float32)
+    S0 = random_state(rng, (len(lengths), H, d, d))
+    dST = random_state(rng, (len(lengths), H, d, d))
+    td = tdtype(dt)
+    got = kda.chunk_backward_varlen(dev(q, td), dev(k, td), dev(v, td), dev(a), dev(b),
+                                    torch.from_numpy(cu).cuda(), dev(do), dev(S0), dev(dST))
+    torch.cuda.synchronize()
+    got = [host(g) for g in got]
+    ref = varlen_backward_reference(q, k, v, a, b, cu, do, S0, dST)
+    errs = {n: max_rel_err(g, r) for n, g, r in zip(NAMES, got, ref)}
+    flush("    " + " ".join(f"{n}={e:.1e}" for n, e in errs.items()))
+    assert max(errs.values()) <= TOL[dt], errs
+    # the empty sequence passes the final-state gradient through unchanged
+    assert np.array_equal(got[5][1], dST[1].astype(np.float32))
+
+
+def test_backward_varlen_equals_fixed_length_call(monkeypatch):
+    """Equal-length packed sequences give the fixed-length backward (both
+    forwards in the one-kernel form, so the checkpoints agree)."""
+    monkeypatch.setenv("KDA_PREFILL_PATH", "fused")
+    B, T, H, D = 3, 150, 2, 128
+    flush(f"[backward] varlen == fixed B={B} T={T} H={H} d={D}")
+    q, k, v, a, b = I.batch_inputs(740, B, T, H, D, D, "bf16")
+    do = np.random.default_rng(741).standard_normal((B, T, H, D)).astype(np.float32)
+    S0 = random_state(np.random.default_rng(742), (B, H, D, D))
+    bf = torch.bfloat16
+    x = [dev(q, bf), dev(k, bf), dev(v, bf), dev(a), dev(b), dev(do)]
+    g_fix = kda.chunk_backward(*x[:5], x[5], dev(S0), None)
+    flat = [t.reshape(B * T, *t.shape[2:]).contiguous() for t in x]
+    cu = torch.tensor([0, T, 2 * T, 3 * T], dtype=torch.int32, device="cuda")
+    g_var = kda.chunk_backward_varlen(*flat[:5], cu, flat[5], dev(S0), None)
+    torch.cuda.synchronize()
+    for gf, gv in zip(g_fix[:5], g_var[:5]):
+        err = max_rel_err(host(gv), host(gf).reshape(host(gv).shape))
+        assert err <= 1e-6, err
+    assert max_rel_err(host(g_var[5]), host(g_fix[5])) <= 1e-6
+
+
+@pytest.mark.parametrize("varlen", [False, True])
+def test_backward_without_tokens_passes_state_gradient(varlen):
+    """T = 0: the initial state's gradient is the final state's."""
+    N, H, D = 2, 3, 64
+    flush(f"[backward] no tokens N={N} H={H} d={D} varlen={varlen}")
+    dST = random_state(np.random.default_rng(750), (N, H, D, D))
+    e = torch.empty((0, H, D), device="cuda", dtype=torch.float32)
+    if varlen:
+        cu = torch.zeros(N + 1, dtype=torch.int32, device="cuda")
+        g = kda.chunk_backward_varlen(e, e, e, e, torch.empty((0, H), device="cuda"), cu, e,
+                                      None, dev(dST))
+    else:
+        e4 = torch.empty((N, 0, H, D), device="cuda", dtype=torch.float32)
+        g = kda.chunk_backward(e4, e4, e4, e4, torch.empty((N, 0, H), device="cuda"), e4, None,
+                               dev(dST))
+    torch.cuda.synchronize()
+    assert torch.equal(g[5], dev(dST))
