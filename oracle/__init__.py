@@ -12,6 +12,7 @@ from .kda_oracle import (  # noqa: F401
     kda_recurrent_snapshots,
     gdn_recurrent,
     kda_backward,
+    gdn_backward,
     kda_decode_step,
     kda_decode_pool,
     kda_chunked,

@@ -183,6 +183,23 @@ def kda_backward(q, k, v, alpha, beta, S0, do, dST=None):
     return dq, dk, dv, da, db, G
 
 
+def gdn_backward(q, k, v, gate, beta, S0, do, dST=None):
+    """Gradients for the scalar-gate (Gated DeltaNet) recurrence of
+    gdn_recurrent: the same loss as kda_backward.  A scalar gate is KDA's
+    diagonal gate with every channel equal ([EXPLAINER] "Kimi Delta Attention
+    の仕組み"), so by the chain rule its gradient is the sum over channels of
+    the per-channel gate gradient; the other gradients are KDA's.
+
+    Shapes as in gdn_recurrent; returns (dq, dk, dv, dgate [B,T,H], dbeta,
+    dS0) in fp64.
+    """
+    g = _check_alpha(gate)
+    DK = np.shape(q)[-1]
+    dq, dk, dv, da, db, dS0 = kda_backward(q, k, v, np.repeat(g[..., None], DK, axis=-1), beta,
+                                           S0, do, dST)
+    return dq, dk, dv, da.sum(axis=-1), db, dS0
+
+
 def kda_recurrent_varlen(q, k, v, alpha, beta, cu_seqlens, S0=None):
     """Packed variable-length prefill: sequence n owns tokens
     [cu_seqlens[n], cu_seqlens[n+1]) of the packed token axis.

@@ -17,8 +17,9 @@ from fractions import Fraction
 import numpy as np
 import pytest
 
-from oracle import (gdn_recurrent, kda_backward, kda_chunked, kda_decode_pool, kda_decode_step,
-                    kda_recurrent, kda_recurrent_snapshots, kda_recurrent_varlen, max_rel_err)
+from oracle import (gdn_backward, gdn_recurrent, kda_backward, kda_chunked, kda_decode_pool,
+                    kda_decode_step, kda_recurrent, kda_recurrent_snapshots, kda_recurrent_varlen,
+                    max_rel_err)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -616,6 +617,36 @@ def test_p13_backward_beta_zero_closed_form():
     # dq_t = S_t do_t with S_t = Diag(prod a) S0
     np.testing.assert_allclose(dq, np.einsum("bthk,bhkv,bthv->bthk", cum, S0, do), rtol=1e-12,
                                atol=1e-12)
+
+
+# ------------------------------------------------------------------ P14 ---
+def test_p14_scalar_gate_backward_finite_differences():
+    """gdn_backward against central differences of the separately written
+    scalar-gate recurrence gdn_recurrent, on sampled coordinates of every
+    input (the gate's gradient is the one that differs from KDA's)."""
+    rng = np.random.default_rng(54)
+    q, k, v, a, b, S0 = rand_inputs(rng, 1, 9, 2, 4, 3)
+    g = a[..., 0].copy()                                    # one gate per token-head
+    do = rng.standard_normal(v.shape)
+    dST = rng.standard_normal(S0.shape)
+
+    def loss(q_, k_, v_, g_, b_, S0_):
+        o, S = gdn_recurrent(q_, k_, v_, g_, b_, S0_)
+        return float(np.sum(o * do) + np.sum(S * dST))
+
+    grads = gdn_backward(q, k, v, g, b, S0, do, dST)
+    assert grads[3].shape == g.shape
+    args = [q, k, v, g, b, S0]
+    h = 1e-6
+    for i, (x, gr) in enumerate(zip(args, grads)):
+        for idx in list(np.ndindex(x.shape))[:: max(1, x.size // 7)]:
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            ap, am = list(args), list(args)
+            ap[i], am[i] = xp, xm
+            fd = (loss(*ap) - loss(*am)) / (2 * h)
+            assert abs(fd - gr[idx]) < 1e-6 * max(1.0, abs(fd)), (i, idx, fd, gr[idx])
 
 
 def test_alpha_domain_is_checked():
