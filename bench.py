@@ -299,7 +299,10 @@ def main():
                           device=dev, dtype=torch.uint8)
         bwd_us = time_call(lambda: kda.chunk_backward(pq, pk, pv, pa, pb, d_o, workspace=bws),
                            reps=3)
-        del d_o, bws
+        pg = pa[..., 0].contiguous()
+        bwd_sg_us = time_call(lambda: kda.chunk_backward(pq, pk, pv, pg, pb, d_o, workspace=bws),
+                              reps=3)
+        del d_o, bws, pg
         variants = {
             "decode_back_to_back_us_per_step": b2b_us,
             "decode_back_to_back_hbm_frac": hbm(b2b_us),
@@ -310,6 +313,7 @@ def main():
             "decode_pool_512_slots_L4_us": pool4_us,
             "decode_pool_512_slots_L4_us_per_token": pool4_us / L4,
             "backward_b1_h32_t8192_us": bwd_us,
+            "backward_scalar_gate_b1_h32_t8192_us": bwd_sg_us,
             "decode_n1_h32_eager_us_per_step": n1_eager_us,
             "decode_n1_h32_hip_graph_us_per_step": n1_graph_us,
         }

@@ -480,8 +480,9 @@ kda_status_t run_backward(int N, int T_fixed, const int32_t* cu_seqlens, int64_t
                           const float* state_in, const float* d_o, const float* d_state_out,
                           float* dq, float* dk, float* dv, float* dalpha, float* dbeta,
                           float* d_state_in, void* workspace, size_t workspace_bytes,
-                          void* stream) {
+                          void* stream, bool alpha_scalar) {
   const bool varlen = cu_seqlens != nullptr;
+  const size_t nalpha = alpha_scalar ? 1 : size_t(DK);   // alpha (and dalpha) values per token row
   if (!dims_ok(DK) || !dims_ok(DV))
     return fail(KDA_ERR_UNSUPPORTED, "DK=%d DV=%d: only 64 and 128 are supported", DK, DV);
   if (chunk != 64) return fail(KDA_ERR_UNSUPPORTED, "chunk=%d: only 64 is supported", chunk);
@@ -501,6 +502,7 @@ kda_status_t run_backward(int N, int T_fixed, const int32_t* cu_seqlens, int64_t
     kda::BackwardArgs a{};
     a.N = N; a.H = H; a.DK = DK; a.DV = DV; a.T = 0; a.cu_seqlens = cu_seqlens; a.rows = 0;
     a.in_bf16 = in_dtype == KDA_BF16;
+    a.alpha_scalar = alpha_scalar;
     a.d_state_out = d_state_out; a.d_state_in = d_state_in;
     const char* msg = nullptr;
     if (kda::launch_backward(a, stream, &msg) != 0)
@@ -515,12 +517,12 @@ kda_status_t run_backward(int N, int T_fixed, const int32_t* cu_seqlens, int64_t
   const size_t esz = in_dtype == KDA_BF16 ? 2 : 4;
   const size_t rows = size_t(T_total) * H;
   const void* in[] = {q, k, v, alpha, beta, state_in, d_o, d_state_out, cu_seqlens};
-  const size_t in_b[] = {rows * DK * esz, rows * DK * esz, rows * DV * esz, rows * DK * 4,
+  const size_t in_b[] = {rows * DK * esz, rows * DK * esz, rows * DV * esz, rows * nalpha * 4,
                          rows * 4, ns, rows * DV * 4, ns, size_t(N + 1) * 4};
   const char* in_n[] = {"q", "k", "v", "alpha", "beta", "state_in", "d_o", "d_state_out",
                         "cu_seqlens"};
   const void* out[] = {dq, dk, dv, dalpha, dbeta, d_state_in};
-  const size_t out_b[] = {rows * DK * 4, rows * DK * 4, rows * DV * 4, rows * DK * 4, rows * 4, ns};
+  const size_t out_b[] = {rows * DK * 4, rows * DK * 4, rows * DV * 4, rows * nalpha * 4, rows * 4, ns};
   const char* out_n[] = {"dq", "dk", "dv", "dalpha", "dbeta", "d_state_in"};
   for (int i = 0; i < 8; ++i)
     if (in[i] && !aligned16(in[i])) return fail(KDA_ERR_ALIGN, "%s is not 16-byte aligned", in_n[i]);
@@ -552,7 +554,7 @@ kda_status_t run_backward(int N, int T_fixed, const int32_t* cu_seqlens, int64_t
   kda::PrefillArgs f{};
   f.N = N; f.T_fixed = varlen ? 0 : T_fixed; f.cu_seqlens = cu_seqlens; f.T_total = T_total;
   f.H = H; f.DK = DK; f.DV = DV; f.in_bf16 = in_dtype == KDA_BF16;
-  f.q = q; f.k = k; f.v = v; f.alpha = alpha; f.beta = beta;
+  f.q = q; f.k = k; f.v = v; f.alpha = alpha; f.beta = beta; f.alpha_scalar = alpha_scalar;
   f.state_in = state_in; f.o = reinterpret_cast<float*>(ws + L.o); f.state_out = nullptr;
   f.workspace = ws + L.fwd_or_part; f.workspace_bytes = L.o;
   const int64_t snap_rows = varlen ? T_total / 64 : int64_t(N) * (T_fixed / 64);
@@ -568,6 +570,7 @@ kda_status_t run_backward(int N, int T_fixed, const int32_t* cu_seqlens, int64_t
   a.N = N; a.H = H; a.DK = DK; a.DV = DV; a.T = varlen ? 0 : T_fixed; a.cu_seqlens = cu_seqlens;
   a.rows = int64_t(rows);
   a.in_bf16 = in_dtype == KDA_BF16;
+  a.alpha_scalar = alpha_scalar;
   a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.state_in = state_in;
   a.d_o = d_o; a.d_state_out = d_state_out;
   a.snapshots = reinterpret_cast<const float*>(ws + L.snaps); a.snap_per_seq = varlen ? 0 : T_fixed / 64;
@@ -601,7 +604,21 @@ kda_status_t kda_chunk_backward(int B, int T, int H, int DK, int DV, int chunk,
   if (B < 0 || T < 0 || H < 0) return fail(KDA_ERR_SHAPE, "negative size (B=%d T=%d H=%d)", B, T, H);
   return run_backward(B, T, nullptr, int64_t(B) * T, H, DK, DV, chunk, in_dtype, q, k, v, alpha,
                       beta, state_in, d_o, d_state_out, dq, dk, dv, dalpha, dbeta, d_state_in,
-                      workspace, workspace_bytes, stream);
+                      workspace, workspace_bytes, stream, false);
+}
+
+kda_status_t kda_chunk_backward_scalar_gate(int B, int T, int H, int DK, int DV, int chunk,
+                                            kda_dtype_t in_dtype, const void* q, const void* k,
+                                            const void* v, const float* gate, const float* beta,
+                                            const float* state_in, const float* d_o,
+                                            const float* d_state_out, float* dq, float* dk,
+                                            float* dv, float* dgate, float* dbeta,
+                                            float* d_state_in, void* workspace,
+                                            size_t workspace_bytes, void* stream) {
+  if (B < 0 || T < 0 || H < 0) return fail(KDA_ERR_SHAPE, "negative size (B=%d T=%d H=%d)", B, T, H);
+  return run_backward(B, T, nullptr, int64_t(B) * T, H, DK, DV, chunk, in_dtype, q, k, v, gate,
+                      beta, state_in, d_o, d_state_out, dq, dk, dv, dgate, dbeta, d_state_in,
+                      workspace, workspace_bytes, stream, true);
 }
 
 size_t kda_chunk_backward_varlen_workspace_size(int N, int T_total, int H, int DK, int DV,
@@ -625,7 +642,23 @@ kda_status_t kda_chunk_backward_varlen(int N, int T_total, const int32_t* cu_seq
     return fail(KDA_ERR_ALIGN, "cu_seqlens must be 4-byte aligned");
   return run_backward(N, 0, N > 0 ? cu_seqlens : nullptr, T_total, H, DK, DV, chunk, in_dtype, q,
                       k, v, alpha, beta, state_in, d_o, d_state_out, dq, dk, dv, dalpha, dbeta,
-                      d_state_in, workspace, workspace_bytes, stream);
+                      d_state_in, workspace, workspace_bytes, stream, false);
+}
+
+kda_status_t kda_chunk_backward_varlen_scalar_gate(
+    int N, int T_total, const int32_t* cu_seqlens, int H, int DK, int DV, int chunk,
+    kda_dtype_t in_dtype, const void* q, const void* k, const void* v, const float* gate,
+    const float* beta, const float* state_in, const float* d_o, const float* d_state_out,
+    float* dq, float* dk, float* dv, float* dgate, float* dbeta, float* d_state_in,
+    void* workspace, size_t workspace_bytes, void* stream) {
+  if (N < 0 || T_total < 0 || H < 0)
+    return fail(KDA_ERR_SHAPE, "negative size (N=%d T_total=%d H=%d)", N, T_total, H);
+  if (N > 0 && cu_seqlens == nullptr) return fail(KDA_ERR_NULL, "cu_seqlens must be non-NULL");
+  if (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u)
+    return fail(KDA_ERR_ALIGN, "cu_seqlens must be 4-byte aligned");
+  return run_backward(N, 0, N > 0 ? cu_seqlens : nullptr, T_total, H, DK, DV, chunk, in_dtype, q,
+                      k, v, gate, beta, state_in, d_o, d_state_out, dq, dk, dv, dgate, dbeta,
+                      d_state_in, workspace, workspace_bytes, stream, true);
 }
 
 }  // extern "C"

@@ -201,7 +201,8 @@ __device__ __forceinline__ void wave_sums(float (&x)[N]) {
   for (int i = 0; i < N; ++i) x[i] = lane_val(x[i], 63);
 }
 
-template <int DK, bool BF16>
+// SG: one gate per token and head (alpha [rows]), the same for every key row.
+template <int DK, bool BF16, bool SG>
 __global__ __launch_bounds__(kNT) void kda_bwd_kernel(BackwardArgs p) {
   constexpr int RPL = DK / 64;       // key rows per lane
   constexpr int E = RPL * kCPW;      // state elements per lane
@@ -276,16 +277,25 @@ __global__ __launch_bounds__(kNT) void kda_bwd_kernel(BackwardArgs p) {
     float a[RPL], b, dout[kCPW], Sp[E];
     RowsIn<BF16, RPL> k, q;
   };
+  auto load_alpha = [&](int64_t row, float (&a)[RPL]) {
+    if constexpr (SG) {
+      const float g = p.alpha[row];
+#pragma unroll
+      for (int r = 0; r < RPL; ++r) a[r] = g;
+    } else {
+      ld_f<RPL>(p.alpha + row * DK + i0, a);
+    }
+  };
   auto load_f = [&](int64_t c, int s, FIn& x) {
     const int64_t row = row_of(c, s);
-    ld_f<RPL>(p.alpha + row * DK + i0, x.a);
+    load_alpha(row, x.a);
     x.k.load(p.k, row * DK + i0);
     x.b = p.beta[row];
     x.v.load(p.v, row * DV + col);
   };
   auto load_b = [&](int64_t c, int sb, BIn& x) {
     const int64_t row = row_of(c, sb);
-    ld_f<RPL>(p.alpha + row * DK + i0, x.a);
+    load_alpha(row, x.a);
     x.k.load(p.k, row * DK + i0);
     x.q.load(p.q, row * DK + i0);
     x.b = p.beta[row];
@@ -475,26 +485,55 @@ __device__ __forceinline__ float sum_ns(const float* p) {
   return s;
 }
 
-template <int DK, int NS>
+template <int DK, int NS, bool SG>
 __global__ __launch_bounds__(256) void kda_bwd_reduce_kernel(BackwardArgs p) {
   const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;   // token row * DK + key row
   if (idx < p.rows * DK) {
     p.dq[idx] = sum_ns<NS>(p.part_dq + idx * NS);
     p.dk[idx] = sum_ns<NS>(p.part_dk + idx * NS);
-    p.dalpha[idx] = sum_ns<NS>(p.part_da + idx * NS);
+    if constexpr (!SG) p.dalpha[idx] = sum_ns<NS>(p.part_da + idx * NS);
   }
   if (idx < p.rows) p.dbeta[idx] = sum_ns<NS>(p.part_db + idx * NS);
 }
 
-template <int DK, bool BF16>
+// A scalar gate's gradient: the sum over key rows and slabs of the per-row
+// partials (chain rule: the gate is every row's decay), one wave per token
+// row; each lane adds DK * NS / 64 consecutive values, then the lanes are
+// added in a fixed order (deterministic).
+template <int DK, int NS>
+__global__ __launch_bounds__(256) void kda_bwd_dgate_kernel(BackwardArgs p) {
+  constexpr int PER = DK * NS / 64;
+  static_assert(PER % 4 == 0, "float4 pieces");
+  const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int l = threadIdx.x & 63;
+  if (row >= p.rows) return;
+  const float* src = p.part_da + row * (DK * NS) + l * PER;
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; i += 4) {
+    const float4 x = *reinterpret_cast<const float4*>(src + i);
+    s += (x.x + x.y) + (x.z + x.w);
+  }
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) s += __shfl_xor(s, off);
+  if (l == 0) p.dalpha[row] = s;
+}
+
+template <int DK, bool BF16, bool SG>
 void launch_bwd_t(const BackwardArgs& a, hipStream_t st) {
   const unsigned nb = unsigned(int64_t(a.N) * a.H * (a.DV / kVS));
-  hipLaunchKernelGGL((kda_bwd_kernel<DK, BF16>), dim3(nb), dim3(kNT), 0, st, a);
+  hipLaunchKernelGGL((kda_bwd_kernel<DK, BF16, SG>), dim3(nb), dim3(kNT), 0, st, a);
   if (a.rows == 0) return;   // no tokens: only d_state_in (= d_state_out) is written
   const int64_t threads = a.rows * DK;
   const dim3 grid(unsigned((threads + 255) / 256));
-  if (a.DV == 128) hipLaunchKernelGGL((kda_bwd_reduce_kernel<DK, 8>), grid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((kda_bwd_reduce_kernel<DK, 4>), grid, dim3(256), 0, st, a);
+  const dim3 grid_g(unsigned((a.rows + 3) / 4));
+  if (a.DV == 128) {
+    hipLaunchKernelGGL((kda_bwd_reduce_kernel<DK, 8, SG>), grid, dim3(256), 0, st, a);
+    if (SG) hipLaunchKernelGGL((kda_bwd_dgate_kernel<DK, 8>), grid_g, dim3(256), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((kda_bwd_reduce_kernel<DK, 4, SG>), grid, dim3(256), 0, st, a);
+    if (SG) hipLaunchKernelGGL((kda_bwd_dgate_kernel<DK, 4>), grid_g, dim3(256), 0, st, a);
+  }
 }
 
 }  // namespace
@@ -507,11 +546,21 @@ int launch_backward(const BackwardArgs& a, void* stream, const char** msg) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   if (a.DK == 128) {
-    if (a.in_bf16) launch_bwd_t<128, true>(a, st);
-    else launch_bwd_t<128, false>(a, st);
+    if (a.alpha_scalar) {
+      if (a.in_bf16) launch_bwd_t<128, true, true>(a, st);
+      else launch_bwd_t<128, false, true>(a, st);
+    } else {
+      if (a.in_bf16) launch_bwd_t<128, true, false>(a, st);
+      else launch_bwd_t<128, false, false>(a, st);
+    }
   } else if (a.DK == 64) {
-    if (a.in_bf16) launch_bwd_t<64, true>(a, st);
-    else launch_bwd_t<64, false>(a, st);
+    if (a.alpha_scalar) {
+      if (a.in_bf16) launch_bwd_t<64, true, true>(a, st);
+      else launch_bwd_t<64, false, true>(a, st);
+    } else {
+      if (a.in_bf16) launch_bwd_t<64, true, false>(a, st);
+      else launch_bwd_t<64, false, false>(a, st);
+    }
   } else {
     *msg = "unsupported DK";
     return 1;

@@ -72,6 +72,7 @@ struct BackwardArgs {
   const int32_t* cu_seqlens;   // packed sequences: device [N + 1] (then T is unused), or nullptr
   int64_t rows;                // token rows: N * T * H, or T_total * H when packed
   bool in_bf16;
+  bool alpha_scalar;           // alpha and dalpha are [rows] (one gate per token-head)
   const void* q;
   const void* k;
   const void* v;

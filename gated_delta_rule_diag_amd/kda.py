@@ -41,6 +41,8 @@ EXPORTED = (
     "kda_chunk_prefill_varlen_snapshots",
     "kda_chunk_backward_varlen_workspace_size",
     "kda_chunk_backward_varlen",
+    "kda_chunk_backward_scalar_gate",
+    "kda_chunk_backward_varlen_scalar_gate",
     "kda_status_string",
     "kda_last_error_message",
 )
@@ -89,6 +91,10 @@ def load_library(path: str = _LIB_PATH) -> ctypes.CDLL:
     lib.kda_chunk_backward_varlen_workspace_size.argtypes = [i] * 6
     lib.kda_chunk_backward_varlen.restype = i
     lib.kda_chunk_backward_varlen.argtypes = [i, i, vp, i, i, i, i, i] + [vp] * 15 + [sz, vp]
+    lib.kda_chunk_backward_scalar_gate.restype = i
+    lib.kda_chunk_backward_scalar_gate.argtypes = lib.kda_chunk_backward.argtypes
+    lib.kda_chunk_backward_varlen_scalar_gate.restype = i
+    lib.kda_chunk_backward_varlen_scalar_gate.argtypes = lib.kda_chunk_backward_varlen.argtypes
     lib.kda_chunk_prefill_varlen_snapshots.restype = i
     lib.kda_chunk_prefill_varlen_snapshots.argtypes = [i, i, vp, i, i, i, i, i] + [vp] * 8 + \
         [i, vp, i, vp, vp, sz, vp]
@@ -339,9 +345,10 @@ def decode_pool(q, k, v, alpha, beta, state_pool, state_idx=None, num_tokens=Non
 def chunk_backward(q, k, v, alpha, beta, d_o, initial_state=None, d_final_state=None,
                    chunk=64, workspace=None):
     """Gradients of L = sum(o * d_o) + sum(S_T * d_final_state) for the
-    fixed-length prefill (per-channel alpha).
+    fixed-length prefill.
 
-    Inputs as for :func:`chunk_prefill`; d_o [B,T,H,DV] float32;
+    Inputs as for :func:`chunk_prefill` (alpha [B,T,H,DK], or [B,T,H] for a
+    scalar gate, whose gradient then has that shape); d_o [B,T,H,DV] float32;
     d_final_state [B,H,DK,DV] float32 or None.
     Returns (dq, dk, dv, dalpha, dbeta, d_initial_state), all float32.
     """
@@ -351,7 +358,8 @@ def chunk_backward(q, k, v, alpha, beta, d_o, initial_state=None, d_final_state=
     _need(q, "q", q.dtype)
     _need(k, "k", q.dtype, (B, T, H, DK))
     _need(v, "v", q.dtype, (B, T, H, DV))
-    _need(alpha, "alpha", torch.float32, (B, T, H, DK))
+    sg = alpha.dim() == 3
+    _need(alpha, "alpha", torch.float32, (B, T, H) if sg else (B, T, H, DK))
     _need(beta, "beta", torch.float32, (B, T, H))
     _need(d_o, "d_o", torch.float32, (B, T, H, DV))
     if initial_state is not None:
@@ -360,14 +368,16 @@ def chunk_backward(q, k, v, alpha, beta, d_o, initial_state=None, d_final_state=
         _need(d_final_state, "d_final_state", torch.float32, (B, H, DK, DV))
     dev = q.device
     f32 = dict(device=dev, dtype=torch.float32)
-    dq, dk, dal = (torch.empty((B, T, H, DK), **f32) for _ in range(3))
+    dq, dk = (torch.empty((B, T, H, DK), **f32) for _ in range(2))
+    dal = torch.empty((B, T, H) if sg else (B, T, H, DK), **f32)
     dv = torch.empty((B, T, H, DV), **f32)
     db = torch.empty((B, T, H), **f32)
     ds0 = torch.empty((B, H, DK, DV), **f32)
     wsz = lib().kda_chunk_backward_workspace_size(B, T, H, DK, DV, chunk)
     if wsz and workspace is None:
         workspace = torch.empty(wsz, device=dev, dtype=torch.uint8)
-    _check(lib().kda_chunk_backward(
+    fn = lib().kda_chunk_backward_scalar_gate if sg else lib().kda_chunk_backward
+    _check(fn(
         B, T, H, DK, DV, chunk, dt, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
         _ptr(initial_state), _ptr(d_o), _ptr(d_final_state), _ptr(dq), _ptr(dk), _ptr(dv),
         _ptr(dal), _ptr(db), _ptr(ds0), _ptr(workspace),
@@ -439,7 +449,8 @@ def chunk_backward_varlen(q, k, v, alpha, beta, cu_seqlens, d_o, initial_state=N
     """Gradients of L = sum(o * d_o) + sum(S_T * d_final_state) for the packed
     variable-length prefill (per-channel alpha).
 
-    Inputs as for :func:`chunk_prefill_varlen`; d_o [T_total,H,DV] float32;
+    Inputs as for :func:`chunk_prefill_varlen` (alpha [T_total,H,DK], or
+    [T_total,H] for a scalar gate); d_o [T_total,H,DV] float32;
     d_final_state [N,H,DK,DV] float32 or None.
     Returns (dq, dk, dv, dalpha, dbeta, d_initial_state), all float32.
     """
@@ -449,7 +460,8 @@ def chunk_backward_varlen(q, k, v, alpha, beta, cu_seqlens, d_o, initial_state=N
     _need(q, "q", q.dtype)
     _need(k, "k", q.dtype, (Tt, H, DK))
     _need(v, "v", q.dtype, (Tt, H, DV))
-    _need(alpha, "alpha", torch.float32, (Tt, H, DK))
+    sg = alpha.dim() == 2
+    _need(alpha, "alpha", torch.float32, (Tt, H) if sg else (Tt, H, DK))
     _need(beta, "beta", torch.float32, (Tt, H))
     _need(d_o, "d_o", torch.float32, (Tt, H, DV))
     _need(cu_seqlens, "cu_seqlens", torch.int32)
@@ -460,14 +472,16 @@ def chunk_backward_varlen(q, k, v, alpha, beta, cu_seqlens, d_o, initial_state=N
         _need(d_final_state, "d_final_state", torch.float32, (N, H, DK, DV))
     dev = q.device
     f32 = dict(device=dev, dtype=torch.float32)
-    dq, dk, dal = (torch.empty((Tt, H, DK), **f32) for _ in range(3))
+    dq, dk = (torch.empty((Tt, H, DK), **f32) for _ in range(2))
+    dal = torch.empty((Tt, H) if sg else (Tt, H, DK), **f32)
     dv = torch.empty((Tt, H, DV), **f32)
     db = torch.empty((Tt, H), **f32)
     ds0 = torch.empty((N, H, DK, DV), **f32)
     wsz = lib().kda_chunk_backward_varlen_workspace_size(N, Tt, H, DK, DV, chunk)
     if wsz and workspace is None:
         workspace = torch.empty(wsz, device=dev, dtype=torch.uint8)
-    _check(lib().kda_chunk_backward_varlen(
+    fn = lib().kda_chunk_backward_varlen_scalar_gate if sg else lib().kda_chunk_backward_varlen
+    _check(fn(
         N, Tt, _ptr(cu_seqlens), H, DK, DV, chunk, dt, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
         _ptr(beta), _ptr(initial_state), _ptr(d_o), _ptr(d_final_state), _ptr(dq), _ptr(dk),
         _ptr(dv), _ptr(dal), _ptr(db), _ptr(ds0), _ptr(workspace),

@@ -261,6 +261,11 @@ kda_status_t kda_decode_pool(int N, int L, int H, int DK, int DV, kda_dtype_t in
  *   workspace    at least kda_chunk_backward_workspace_size() bytes, 16-byte
  *                aligned, not overlapping any argument (holds the forward's
  *                chunk-boundary states, its outputs and per-slab partial sums).
+ *                It grows with the token-heads: about 8 (3 DK + 1) + DV + DK DV / 64
+ *                floats each, plus 1 MiB per (sequence, head, 16 value columns)
+ *                (d=128: about 13.9 KB per token-head; B=1 H=32 T=8192: 3.9 GB).
+ *                Sequences are independent: a batch too large for one call can
+ *                be split into calls over groups of sequences.
  * Outputs must not overlap inputs or each other.  The forward is recomputed
  * (with a state checkpoint per chunk); the reverse pass walks every chunk
  * backwards from its checkpoint; the result is deterministic.  With T == 0
@@ -298,6 +303,33 @@ kda_status_t kda_chunk_backward_varlen(int N, int T_total, const int32_t* cu_seq
                                        const float* d_state_out, float* dq, float* dk, float* dv,
                                        float* dalpha, float* dbeta, float* d_state_in,
                                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward pass with a scalar gate (Gated DeltaNet, as
+ * kda_chunk_prefill_scalar_gate): as kda_chunk_backward and
+ * kda_chunk_backward_varlen, with the gate and its gradient one float per
+ * token and head:
+ *   gate, dgate  [B,T,H] (packed: [T_total,H]) float
+ * The gate decays every key channel, so dgate is the sum over the channels
+ * of the per-channel gradient ("Kimi Delta Attention 徹底解説"
+ * (tech-tide.dev), section "Kimi Delta Attention の仕組み": KDA turns Gated
+ * DeltaNet's scalar into a diagonal).  Workspace sizes: the queries of the
+ * per-channel calls.
+ */
+kda_status_t kda_chunk_backward_scalar_gate(int B, int T, int H, int DK, int DV, int chunk,
+                                            kda_dtype_t in_dtype, const void* q, const void* k,
+                                            const void* v, const float* gate, const float* beta,
+                                            const float* state_in, const float* d_o,
+                                            const float* d_state_out, float* dq, float* dk,
+                                            float* dv, float* dgate, float* dbeta,
+                                            float* d_state_in, void* workspace,
+                                            size_t workspace_bytes, void* stream);
+kda_status_t kda_chunk_backward_varlen_scalar_gate(
+    int N, int T_total, const int32_t* cu_seqlens, int H, int DK, int DV, int chunk,
+    kda_dtype_t in_dtype, const void* q, const void* k, const void* v, const float* gate,
+    const float* beta, const float* state_in, const float* d_o, const float* d_state_out,
+    float* dq, float* dk, float* dv, float* dgate, float* dbeta, float* d_state_in,
+    void* workspace, size_t workspace_bytes, void* stream);
 
 const char* kda_status_string(kda_status_t s);
 const char* kda_last_error_message(void);

@@ -331,6 +331,40 @@ def test_backward_varlen_argument_errors(lib):
     assert call(Tt=0, ptrs=p) == OK                # no tokens, no d_state_in: nothing to do
 
 
+def test_backward_scalar_gate_argument_errors(lib):
+    # B=1, T=64, H=2, d=64 (f32); the gate and its gradient are [B,T,H]
+    need = lib.kda_chunk_backward_workspace_size(1, 64, 2, 64, 64, 64)
+    big = ctypes.c_void_p(0x40000000)
+    Q = [ctypes.c_void_p(0x100000 * (i + 1)) for i in range(14)]
+
+    def call(T=64, DK=64, ptrs=None, ws=big, wsb=need):
+        return lib.kda_chunk_backward_scalar_gate(1, T, 2, DK, 64, 64, 0, *(ptrs or Q), ws, wsb,
+                                                  None)
+
+    assert call(DK=32) == UNSUP
+    assert call(T=-1) == SHAPE
+    p = list(Q)
+    p[3] = None                                    # gate
+    assert call(ptrs=p) == NULL
+    assert call(ws=None) == WS
+    # a [B,T,H] gate is 512 bytes: dgate 256 bytes past its start overlaps it
+    p = list(Q)
+    p[9] = ctypes.c_void_p(Q[3].value + 256)
+    assert call(ptrs=p) == SHAPE
+    p = list(Q)
+    p[13] = None
+    assert call(T=0, ptrs=p) == OK
+
+    def vcall(N=2, Tt=100, cu=ctypes.c_void_p(0x2000000), wsb=1 << 30):
+        return lib.kda_chunk_backward_varlen_scalar_gate(N, Tt, cu, 2, 64, 64, 64, 0, *Q, big,
+                                                         wsb, None)
+
+    assert vcall(cu=None) == NULL
+    assert vcall(cu=ctypes.c_void_p(0x2000002)) == ALIGN
+    assert vcall(N=-1) == SHAPE
+    assert vcall(wsb=16) == WS
+
+
 def test_decode_pool_argument_errors(lib):
     def call(N=4, L=2, H=2, DK=128, DV=128, dt=1, idx=P[9], ntok=P[10], pool=P[5], P_=8, o=P[6],
              ts=None, ptrs=None):

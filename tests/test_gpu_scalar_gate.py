@@ -10,7 +10,7 @@ import torch
 from gated_delta_rule_diag_amd import inputs as I
 from gated_delta_rule_diag_amd import kda
 from kda_testlib import TOL, dev, flush, host, random_state, tdtype
-from oracle import gdn_recurrent, max_rel_err
+from oracle import gdn_backward, gdn_recurrent, max_rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -104,3 +104,63 @@ def test_scalar_gate_prefill_b1_h32_t8192_head_subset(path, monkeypatch):
     es = max_rel_err(host(S)[:, heads], S_ref)
     flush(f"    err o={eo:.2e} S={es:.2e}")
     assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+GRADS = ("dq", "dk", "dv", "dgate", "dbeta", "dS0")
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("dt,T,d", [("bf16", 200, 128), ("f32", 130, 64), ("bf16", 37, 64)])
+def test_scalar_gate_backward_matches_oracle(dt, T, d, path, monkeypatch):
+    """Gradients of the scalar-gate prefill (the gate's: one value per
+    token-head) against the fp64 oracle, with an initial state and a
+    final-state gradient."""
+    monkeypatch.setenv("KDA_PREFILL_PATH", path)
+    B, H = 2, 3
+    flush(f"[scalar gate] backward B={B} T={T} H={H} d={d} {dt} path={path}")
+    q, k, v, a, b = I.batch_inputs(620 + T, B, T, H, d, d, dt)
+    g = gate_of(a)
+    rng = np.random.default_rng(T)
+    do = rng.standard_normal((B, T, H, d)).astype(np.float32)
+    S0 = random_state(rng, (B, H, d, d))
+    dST = random_state(rng, (B, H, d, d))
+    td = tdtype(dt)
+    got = kda.chunk_backward(dev(q, td), dev(k, td), dev(v, td), dev(g), dev(b), dev(do), dev(S0),
+                             dev(dST))
+    torch.cuda.synchronize()
+    assert tuple(got[3].shape) == (B, T, H)
+    ref = gdn_backward(q, k, v, g, b, S0, do, dST)
+    errs = {n: max_rel_err(host(x), r) for n, x, r in zip(GRADS, got, ref)}
+    flush("    " + " ".join(f"{n}={e:.1e}" for n, e in errs.items()))
+    assert max(errs.values()) <= TOL[dt], errs
+
+
+@pytest.mark.parametrize("dt,d", [("bf16", 128), ("f32", 64)])
+def test_scalar_gate_backward_varlen_matches_oracle(dt, d):
+    """Packed sequences (empty, short, ragged) with a scalar gate: every
+    gradient against the per-sequence oracle."""
+    lengths = [70, 0, 5, 128, 33]
+    H = 2
+    flush(f"[scalar gate] backward varlen lengths={lengths} H={H} d={d} {dt}")
+    q, k, v, a, b, cu = I.packed_inputs(640, lengths, H, d, d, dt)
+    g = gate_of(a)
+    rng = np.random.default_rng(641)
+    do = rng.standard_normal((int(cu[-1]), H, d)).astype(np.float32)
+    S0 = random_state(rng, (len(lengths), H, d, d))
+    dST = random_state(rng, (len(lengths), H, d, d))
+    td = tdtype(dt)
+    got = kda.chunk_backward_varlen(dev(q, td), dev(k, td), dev(v, td), dev(g), dev(b),
+                                    torch.from_numpy(cu).cuda(), dev(do), dev(S0), dev(dST))
+    torch.cuda.synchronize()
+    got = [host(x) for x in got]
+    parts = [[] for _ in range(6)]
+    for n in range(len(lengths)):
+        s_, e_ = cu[n], cu[n + 1]
+        sl = lambda x: x[None, s_:e_]  # noqa: E731
+        r = gdn_backward(sl(q), sl(k), sl(v), sl(g), sl(b), S0[n:n + 1], sl(do), dST[n:n + 1])
+        for i in range(6):
+            parts[i].append(r[i][0])
+    ref = [np.concatenate(x) for x in parts[:5]] + [np.stack(parts[5])]
+    errs = {n: max_rel_err(x, r) for n, x, r in zip(GRADS, got, ref)}
+    flush("    " + " ".join(f"{n}={e:.1e}" for n, e in errs.items()))
+    assert max(errs.values()) <= TOL[dt], errs
