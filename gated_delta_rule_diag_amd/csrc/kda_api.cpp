@@ -6,6 +6,7 @@
 
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <string>
@@ -449,32 +450,54 @@ namespace {
 // Byte offsets of the backward workspace: [forward prefill workspace, later the
 // per-slab partial sums | o of the forward | snapshots | token-state scratch].
 struct BwdLayout {
-  size_t fwd_or_part, o, snaps, scratch, total;
+  size_t fwd_or_part, o, snaps, scratch, carry, total;
+  int64_t win_k, nwin;   // chunks per window of the reverse pass, windows
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Workspace of a backward call: the forward's workspace (fixed length only)
-// or the per-slab partial sums, whichever is larger (they are not live at
-// the same time), the forward's o, one state per full chunk, the reverse
-// pass's token-state scratch.  Packed sequences: T_fixed = 0, and the
-// snapshot rows are T_total / 64 (chunk j of the sequence starting at token
-// s is row s / 64 + j).
-BwdLayout bwd_layout(int N, int T_fixed, int64_t T_total, int H, int DK, int DV, bool varlen) {
+// or the per-slab partial sums of one window of chunks, whichever is larger
+// (they are not live at the same time), the forward's o, one state per full
+// chunk, the reverse pass's token-state scratch, and the adjoint carried
+// between windows.  The reverse pass goes through the chunks in windows of
+// win_k chunks counted from each sequence's end, so that the partial sums
+// (8 (3 DK + 1) floats per token-head at DV = 128) take at most 4 GiB
+// whatever the length; KDA_BWD_WINDOW=k forces k chunks per window.
+// Packed sequences: T_fixed = 0, max_chunks from the longest sequence, and
+// the snapshot rows are T_total / 64 (chunk j of the sequence starting at
+// token s is row s / 64 + j).
+BwdLayout bwd_layout(int N, int T_fixed, int64_t T_total, int64_t max_chunks, int H, int DK,
+                     int DV, bool varlen) {
   BwdLayout L{};
   const size_t rows = size_t(T_total) * H, nslab = size_t(DV) / 16;
+  const size_t per_chunk = size_t(N) * 64 * H * (3 * size_t(DK) + 1) * nslab * 4;
+  int64_t k = int64_t((size_t(4) << 30) / per_chunk);
+  if (const char* e = getenv("KDA_BWD_WINDOW")) {
+    const long v = atol(e);
+    if (v > 0) k = v;
+  }
+  if (k < 1) k = 1;
+  if (max_chunks < 1) max_chunks = 1;
+  if (k > max_chunks) k = max_chunks;
+  L.win_k = k;
+  L.nwin = (max_chunks + k - 1) / k;
   const size_t pw = varlen ? 0 : kda::prefill_workspace_bytes(N, T_total, H, DK, DV, false);
-  const size_t part = (3 * nslab * rows * DK + nslab * rows) * 4;
+  const size_t part = size_t(k) * per_chunk;
   const size_t snap_rows = varlen ? size_t(T_total / 64) : size_t(N) * size_t(T_fixed / 64);
   L.fwd_or_part = 0;
   L.o = align256(pw > part ? pw : part);
   L.snaps = L.o + align256(rows * DV * 4);
   L.scratch = L.snaps + align256(snap_rows * H * DK * DV * 4);
-  L.total = L.scratch + align256(kda::backward_scratch_bytes(N, H, DK, DV));
+  L.carry = L.scratch + align256(kda::backward_scratch_bytes(N, H, DK, DV));
+  L.total = L.carry + (L.nwin > 1 ? align256(size_t(N) * H * DK * DV * 4) : 0);
   return L;
 }
 
-kda_status_t run_backward(int N, int T_fixed, const int32_t* cu_seqlens, int64_t T_total, int H,
+int64_t chunks_of(int64_t len) { return (len + 63) / 64; }
+
+kda_status_t run_backward(int N, int T_fixed, const int32_t* cu_seqlens, int64_t T_total,
+                          int64_t max_chunks, int H,
                           int DK, int DV, int chunk, kda_dtype_t in_dtype, const void* q,
                           const void* k, const void* v, const float* alpha, const float* beta,
                           const float* state_in, const float* d_o, const float* d_state_out,
@@ -488,8 +511,11 @@ kda_status_t run_backward(int N, int T_fixed, const int32_t* cu_seqlens, int64_t
   if (chunk != 64) return fail(KDA_ERR_UNSUPPORTED, "chunk=%d: only 64 is supported", chunk);
   if (in_dtype != KDA_F32 && in_dtype != KDA_BF16)
     return fail(KDA_ERR_DTYPE, "unknown in_dtype %d", (int)in_dtype);
-  if (T_total * H > (int64_t(1) << 31) / 128 || int64_t(N) * H > (int64_t(1) << 24) || H > 65536)
-    return fail(KDA_ERR_UNSUPPORTED, "too large: tokens*H=%lld H=%d", (long long)(T_total * H), H);
+  // (the same limits as the prefill: the forward runs first; the reverse
+  // pass indexes with 64-bit offsets and its reductions cover one window)
+  if (T_total > (int64_t(1) << 31) - 1 || int64_t(N) * H > (int64_t(1) << 24) || H > 65536)
+    return fail(KDA_ERR_UNSUPPORTED, "too large: tokens=%lld sequences*H=%lld H=%d",
+                (long long)T_total, (long long)N * H, H);
   if (N == 0 || H == 0) return ok();
   const size_t ns = size_t(N) * H * DK * DV * 4;
   if (T_total == 0) {
@@ -503,6 +529,7 @@ kda_status_t run_backward(int N, int T_fixed, const int32_t* cu_seqlens, int64_t
     a.N = N; a.H = H; a.DK = DK; a.DV = DV; a.T = 0; a.cu_seqlens = cu_seqlens; a.rows = 0;
     a.in_bf16 = in_dtype == KDA_BF16;
     a.alpha_scalar = alpha_scalar;
+    a.win_lo = 0; a.win_k = 1;
     a.d_state_out = d_state_out; a.d_state_in = d_state_in;
     const char* msg = nullptr;
     if (kda::launch_backward(a, stream, &msg) != 0)
@@ -537,7 +564,7 @@ kda_status_t run_backward(int N, int T_fixed, const int32_t* cu_seqlens, int64_t
       if (overlaps(out[i], out_b[i], out[j], out_b[j]))
         return fail(KDA_ERR_SHAPE, "%s overlaps %s", out_n[i], out_n[j]);
   }
-  const BwdLayout L = bwd_layout(N, T_fixed, T_total, H, DK, DV, varlen);
+  const BwdLayout L = bwd_layout(N, T_fixed, T_total, max_chunks, H, DK, DV, varlen);
   if (!workspace || workspace_bytes < L.total)
     return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", L.total,
                 workspace ? workspace_bytes : size_t(0));
@@ -577,13 +604,20 @@ kda_status_t run_backward(int N, int T_fixed, const int32_t* cu_seqlens, int64_t
   a.dq = dq; a.dk = dk; a.dv = dv; a.dalpha = dalpha; a.dbeta = dbeta; a.d_state_in = d_state_in;
   a.scratch = reinterpret_cast<float*>(ws + L.scratch);
   const size_t nslab = size_t(DV) / 16;
+  const size_t prows = size_t(N) * size_t(L.win_k) * 64 * H;
   float* part = reinterpret_cast<float*>(ws + L.fwd_or_part);
   a.part_dq = part;
-  a.part_dk = part + nslab * rows * DK;
-  a.part_da = part + 2 * nslab * rows * DK;
-  a.part_db = part + 3 * nslab * rows * DK;
-  if (kda::launch_backward(a, stream, &msg) != 0)
-    return fail(KDA_ERR_HIP, "backward launch failed: %s", msg ? msg : "?");
+  a.part_dk = part + nslab * prows * DK;
+  a.part_da = part + 2 * nslab * prows * DK;
+  a.part_db = part + 3 * nslab * prows * DK;
+  a.part_rows = int64_t(prows);
+  a.win_k = L.win_k;
+  a.g_carry = L.nwin > 1 ? reinterpret_cast<float*>(ws + L.carry) : nullptr;
+  for (int64_t w = 0; w < L.nwin; ++w) {
+    a.win_lo = w * L.win_k;
+    if (kda::launch_backward(a, stream, &msg) != 0)
+      return fail(KDA_ERR_HIP, "backward launch failed: %s", msg ? msg : "?");
+  }
   return ok();
 }
 
@@ -591,7 +625,7 @@ kda_status_t run_backward(int N, int T_fixed, const int32_t* cu_seqlens, int64_t
 
 size_t kda_chunk_backward_workspace_size(int B, int T, int H, int DK, int DV, int chunk) {
   if (B <= 0 || T <= 0 || H <= 0 || !dims_ok(DK) || !dims_ok(DV) || chunk != 64) return 0;
-  return bwd_layout(B, T, int64_t(B) * T, H, DK, DV, false).total;
+  return bwd_layout(B, T, int64_t(B) * T, chunks_of(T), H, DK, DV, false).total;
 }
 
 kda_status_t kda_chunk_backward(int B, int T, int H, int DK, int DV, int chunk,
@@ -602,7 +636,7 @@ kda_status_t kda_chunk_backward(int B, int T, int H, int DK, int DV, int chunk,
                                 float* dalpha, float* dbeta, float* d_state_in, void* workspace,
                                 size_t workspace_bytes, void* stream) {
   if (B < 0 || T < 0 || H < 0) return fail(KDA_ERR_SHAPE, "negative size (B=%d T=%d H=%d)", B, T, H);
-  return run_backward(B, T, nullptr, int64_t(B) * T, H, DK, DV, chunk, in_dtype, q, k, v, alpha,
+  return run_backward(B, T, nullptr, int64_t(B) * T, chunks_of(T), H, DK, DV, chunk, in_dtype, q, k, v, alpha,
                       beta, state_in, d_o, d_state_out, dq, dk, dv, dalpha, dbeta, d_state_in,
                       workspace, workspace_bytes, stream, false);
 }
@@ -616,19 +650,21 @@ kda_status_t kda_chunk_backward_scalar_gate(int B, int T, int H, int DK, int DV,
                                             float* d_state_in, void* workspace,
                                             size_t workspace_bytes, void* stream) {
   if (B < 0 || T < 0 || H < 0) return fail(KDA_ERR_SHAPE, "negative size (B=%d T=%d H=%d)", B, T, H);
-  return run_backward(B, T, nullptr, int64_t(B) * T, H, DK, DV, chunk, in_dtype, q, k, v, gate,
+  return run_backward(B, T, nullptr, int64_t(B) * T, chunks_of(T), H, DK, DV, chunk, in_dtype, q, k, v, gate,
                       beta, state_in, d_o, d_state_out, dq, dk, dv, dgate, dbeta, d_state_in,
                       workspace, workspace_bytes, stream, true);
 }
 
-size_t kda_chunk_backward_varlen_workspace_size(int N, int T_total, int H, int DK, int DV,
-                                                int chunk) {
+size_t kda_chunk_backward_varlen_workspace_size(int N, int T_total, int max_seqlen, int H, int DK,
+                                                int DV, int chunk) {
   if (N <= 0 || T_total <= 0 || H <= 0 || !dims_ok(DK) || !dims_ok(DV) || chunk != 64) return 0;
-  return bwd_layout(N, 0, T_total, H, DK, DV, true).total;
+  const int64_t ml = max_seqlen > 0 && max_seqlen < T_total ? max_seqlen : T_total;
+  return bwd_layout(N, 0, T_total, chunks_of(ml), H, DK, DV, true).total;
 }
 
-kda_status_t kda_chunk_backward_varlen(int N, int T_total, const int32_t* cu_seqlens, int H,
-                                       int DK, int DV, int chunk, kda_dtype_t in_dtype,
+kda_status_t kda_chunk_backward_varlen(int N, int T_total, const int32_t* cu_seqlens,
+                                       int max_seqlen, int H, int DK, int DV, int chunk,
+                                       kda_dtype_t in_dtype,
                                        const void* q, const void* k, const void* v,
                                        const float* alpha, const float* beta,
                                        const float* state_in, const float* d_o,
@@ -640,24 +676,26 @@ kda_status_t kda_chunk_backward_varlen(int N, int T_total, const int32_t* cu_seq
   if (N > 0 && cu_seqlens == nullptr) return fail(KDA_ERR_NULL, "cu_seqlens must be non-NULL");
   if (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u)
     return fail(KDA_ERR_ALIGN, "cu_seqlens must be 4-byte aligned");
-  return run_backward(N, 0, N > 0 ? cu_seqlens : nullptr, T_total, H, DK, DV, chunk, in_dtype, q,
-                      k, v, alpha, beta, state_in, d_o, d_state_out, dq, dk, dv, dalpha, dbeta,
+  const int64_t ml = max_seqlen > 0 && max_seqlen < T_total ? max_seqlen : T_total;
+  return run_backward(N, 0, N > 0 ? cu_seqlens : nullptr, T_total, chunks_of(ml), H, DK, DV, chunk,
+                      in_dtype, q, k, v, alpha, beta, state_in, d_o, d_state_out, dq, dk, dv, dalpha, dbeta,
                       d_state_in, workspace, workspace_bytes, stream, false);
 }
 
 kda_status_t kda_chunk_backward_varlen_scalar_gate(
-    int N, int T_total, const int32_t* cu_seqlens, int H, int DK, int DV, int chunk,
-    kda_dtype_t in_dtype, const void* q, const void* k, const void* v, const float* gate,
-    const float* beta, const float* state_in, const float* d_o, const float* d_state_out,
-    float* dq, float* dk, float* dv, float* dgate, float* dbeta, float* d_state_in,
-    void* workspace, size_t workspace_bytes, void* stream) {
+    int N, int T_total, const int32_t* cu_seqlens, int max_seqlen, int H, int DK, int DV,
+    int chunk, kda_dtype_t in_dtype, const void* q, const void* k, const void* v,
+    const float* gate, const float* beta, const float* state_in, const float* d_o,
+    const float* d_state_out, float* dq, float* dk, float* dv, float* dgate, float* dbeta,
+    float* d_state_in, void* workspace, size_t workspace_bytes, void* stream) {
   if (N < 0 || T_total < 0 || H < 0)
     return fail(KDA_ERR_SHAPE, "negative size (N=%d T_total=%d H=%d)", N, T_total, H);
   if (N > 0 && cu_seqlens == nullptr) return fail(KDA_ERR_NULL, "cu_seqlens must be non-NULL");
   if (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u)
     return fail(KDA_ERR_ALIGN, "cu_seqlens must be 4-byte aligned");
-  return run_backward(N, 0, N > 0 ? cu_seqlens : nullptr, T_total, H, DK, DV, chunk, in_dtype, q,
-                      k, v, gate, beta, state_in, d_o, d_state_out, dq, dk, dv, dgate, dbeta,
+  const int64_t ml = max_seqlen > 0 && max_seqlen < T_total ? max_seqlen : T_total;
+  return run_backward(N, 0, N > 0 ? cu_seqlens : nullptr, T_total, chunks_of(ml), H, DK, DV, chunk,
+                      in_dtype, q, k, v, gate, beta, state_in, d_o, d_state_out, dq, dk, dv, dgate, dbeta,
                       d_state_in, workspace, workspace_bytes, stream, true);
 }
 

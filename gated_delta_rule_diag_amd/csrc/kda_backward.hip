@@ -257,13 +257,35 @@ __global__ __launch_bounds__(kNT) void kda_bwd_kernel(BackwardArgs p) {
     }
   };
 
+  // This launch's window: the chunks c_lo .. c_hi, counted from the
+  // sequence's end (reverse indices win_lo .. win_lo + win_k - 1).  The
+  // adjoint G comes from d_state_out in the first window and from the
+  // previous window's carry otherwise.
+  const int64_t c_hi = nchunks - 1 - p.win_lo;
+  const int64_t c_lo = c_hi - p.win_k + 1 > 0 ? c_hi - p.win_k + 1 : 0;
   float G[E], S[E];
-  if (p.d_state_out) {
+  if (p.win_lo > 0) {
+    ld_state(p.g_carry + state_off, G);
+  } else if (p.d_state_out) {
     ld_state(p.d_state_out + state_off, G);
   } else {
 #pragma unroll
     for (int e = 0; e < E; ++e) G[e] = 0.f;
   }
+  if (c_hi < 0) {
+    // nothing of this sequence in the window; an empty sequence passes the
+    // final state's gradient through (once, in the first window)
+    if (nchunks == 0 && p.win_lo == 0 && p.d_state_in) {
+#pragma unroll
+      for (int r = 0; r < RPL; ++r)
+        stfn<kCPW>(p.d_state_in + state_off + int64_t(r) * DV, G + r * kCPW);
+    }
+    return;
+  }
+  // row of the window's partial sums for token sb of chunk c
+  auto prow_of = [&](int64_t c, int sb) {
+    return ((n * p.win_k + (nchunks - 1 - c - p.win_lo)) * kC + sb) * H + h;
+  };
 
   // Inputs of one forward token and of one backward token, loaded a step
   // ahead of their use (within a chunk: the backward token's state was
@@ -405,6 +427,7 @@ __global__ __launch_bounds__(kNT) void kda_bwd_kernel(BackwardArgs p) {
     // is quantity min(x / DK, 2) (dq, dk, da) of row x % DK (indices past
     // 3 DK write da values again), and every thread writes the same db
     {
+      const int64_t lrow = prow_of(c, sb);
       constexpr int NPASS = (3 * DK + kNT - 1) / kNT;
 #pragma unroll
       for (int j = 0; j < NPASS; ++j) {
@@ -412,20 +435,20 @@ __global__ __launch_bounds__(kNT) void kda_bwd_kernel(BackwardArgs p) {
         const int i = x % DK;
         const int qn = x / DK < 2 ? x / DK : 2;
         const float v = sum_waves(&ring[par][qn][0][i], DK);
-        const int64_t prow = (brow * DK + i) * nslab + slab;
+        const int64_t prow = (lrow * DK + i) * nslab + slab;
         (qn == 0 ? p.part_dq : (qn == 1 ? p.part_dk : p.part_da))[prow] = v;
       }
-      p.part_db[brow * nslab + slab] = sum_waves(ringb[par], 1);
+      p.part_db[lrow * nslab + slab] = sum_waves(ringb[par], 1);
     }
     par ^= 1;
   };
 
   FIn cf, nf;
   BIn cb, nb;
-  // prologue: the last chunk's token states
-  if (nchunks > 0) {
-    const int64_t c = nchunks - 1;
-    const int len = int(T - c * kC);
+  // prologue: the token states of the window's last chunk
+  {
+    const int64_t c = c_hi;
+    const int len = int(T - c * kC < kC ? T - c * kC : kC);
     checkpoint(c, S);
     for (int s = 0; s < len; ++s) {
       load_f(c, s, cf);
@@ -433,9 +456,9 @@ __global__ __launch_bounds__(kNT) void kda_bwd_kernel(BackwardArgs p) {
     }
   }
 
-  for (int64_t c = nchunks - 1; c >= 0; --c) {
+  for (int64_t c = c_hi; c >= c_lo; --c) {
     const int len = int(T - c * kC < kC ? T - c * kC : kC);
-    const bool fwd = c > 0;                 // chunk c-1 is recomputed meanwhile (always full)
+    const bool fwd = c > c_lo;              // chunk c-1 is recomputed meanwhile (always full)
     if (fwd) checkpoint(c - 1, S);
     if (fwd && len == kC) {
       // the steady state: both tokens in every step, inputs a step ahead in
@@ -466,9 +489,30 @@ __global__ __launch_bounds__(kNT) void kda_bwd_kernel(BackwardArgs p) {
       }
     }
   }
+  // after chunk 0 the initial state's gradient; otherwise the carry for
+  // the next window
+  float* gdst = c_lo == 0 ? p.d_state_in : p.g_carry;
 #pragma unroll
   for (int r = 0; r < RPL; ++r)
-    if (p.d_state_in) stfn<kCPW>(p.d_state_in + state_off + int64_t(r) * DV, G + r * kCPW);
+    if (gdst) stfn<kCPW>(gdst + state_off + int64_t(r) * DV, G + r * kCPW);
+}
+
+// The global token row of row lrow of a window's partial sums, or -1 when
+// that row is past its sequence (or before its first chunk).
+__device__ __forceinline__ int64_t window_row(const BackwardArgs& p, int64_t lrow) {
+  const int64_t h = lrow % p.H;
+  int64_t x = lrow / p.H;
+  const int s = int(x % 64);
+  x /= 64;
+  const int64_t jj = x % p.win_k;
+  const int64_t n = x / p.win_k;
+  const int64_t tok0 = p.cu_seqlens ? int64_t(p.cu_seqlens[n]) : n * p.T;
+  const int64_t T = p.cu_seqlens ? int64_t(p.cu_seqlens[n + 1]) - tok0 : p.T;
+  const int64_t nch = (T + 63) / 64;
+  const int64_t c = nch - 1 - (p.win_lo + jj);
+  const int64_t t = c * 64 + s;
+  if (c < 0 || t >= T) return -1;
+  return (tok0 + t) * p.H + h;
 }
 
 // dq, dk, dalpha (per element) and dbeta: sums of the NS per-slab partials,
@@ -487,13 +531,17 @@ __device__ __forceinline__ float sum_ns(const float* p) {
 
 template <int DK, int NS, bool SG>
 __global__ __launch_bounds__(256) void kda_bwd_reduce_kernel(BackwardArgs p) {
-  const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;   // token row * DK + key row
-  if (idx < p.rows * DK) {
-    p.dq[idx] = sum_ns<NS>(p.part_dq + idx * NS);
-    p.dk[idx] = sum_ns<NS>(p.part_dk + idx * NS);
-    if constexpr (!SG) p.dalpha[idx] = sum_ns<NS>(p.part_da + idx * NS);
-  }
-  if (idx < p.rows) p.dbeta[idx] = sum_ns<NS>(p.part_db + idx * NS);
+  const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;   // window row * DK + key row
+  if (idx >= p.part_rows * DK) return;
+  const int64_t lrow = idx / DK;
+  const int i = int(idx % DK);
+  const int64_t grow = window_row(p, lrow);
+  if (grow < 0) return;
+  const int64_t o = grow * DK + i;
+  p.dq[o] = sum_ns<NS>(p.part_dq + idx * NS);
+  p.dk[o] = sum_ns<NS>(p.part_dk + idx * NS);
+  if constexpr (!SG) p.dalpha[o] = sum_ns<NS>(p.part_da + idx * NS);
+  if (i == 0) p.dbeta[grow] = sum_ns<NS>(p.part_db + lrow * NS);
 }
 
 // A scalar gate's gradient: the sum over key rows and slabs of the per-row
@@ -504,10 +552,12 @@ template <int DK, int NS>
 __global__ __launch_bounds__(256) void kda_bwd_dgate_kernel(BackwardArgs p) {
   constexpr int PER = DK * NS / 64;
   static_assert(PER % 4 == 0, "float4 pieces");
-  const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int64_t lrow = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
   const int l = threadIdx.x & 63;
-  if (row >= p.rows) return;
-  const float* src = p.part_da + row * (DK * NS) + l * PER;
+  if (lrow >= p.part_rows) return;
+  const int64_t row = window_row(p, lrow);
+  if (row < 0) return;
+  const float* src = p.part_da + lrow * (DK * NS) + l * PER;
   float s = 0.f;
 #pragma unroll
   for (int i = 0; i < PER; i += 4) {
@@ -524,9 +574,9 @@ void launch_bwd_t(const BackwardArgs& a, hipStream_t st) {
   const unsigned nb = unsigned(int64_t(a.N) * a.H * (a.DV / kVS));
   hipLaunchKernelGGL((kda_bwd_kernel<DK, BF16, SG>), dim3(nb), dim3(kNT), 0, st, a);
   if (a.rows == 0) return;   // no tokens: only d_state_in (= d_state_out) is written
-  const int64_t threads = a.rows * DK;
+  const int64_t threads = a.part_rows * DK;
   const dim3 grid(unsigned((threads + 255) / 256));
-  const dim3 grid_g(unsigned((a.rows + 3) / 4));
+  const dim3 grid_g(unsigned((a.part_rows + 3) / 4));
   if (a.DV == 128) {
     hipLaunchKernelGGL((kda_bwd_reduce_kernel<DK, 8, SG>), grid, dim3(256), 0, st, a);
     if (SG) hipLaunchKernelGGL((kda_bwd_dgate_kernel<DK, 8>), grid_g, dim3(256), 0, st, a);

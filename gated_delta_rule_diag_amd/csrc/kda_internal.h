@@ -73,6 +73,9 @@ struct BackwardArgs {
   int64_t rows;                // token rows: N * T * H, or T_total * H when packed
   bool in_bf16;
   bool alpha_scalar;           // alpha and dalpha are [rows] (one gate per token-head)
+  int64_t win_lo, win_k;       // this launch: chunks with reverse index win_lo .. win_lo + win_k - 1
+  int64_t part_rows;           // rows of the window's partial sums: N * win_k * 64 * H
+  float* g_carry;              // [N, H, DK, DV]: the adjoint between windows (several windows only)
   const void* q;
   const void* k;
   const void* v;

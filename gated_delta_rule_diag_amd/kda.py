@@ -88,9 +88,9 @@ def load_library(path: str = _LIB_PATH) -> ctypes.CDLL:
     lib.kda_chunk_backward.restype = i
     lib.kda_chunk_backward.argtypes = [i, i, i, i, i, i, i] + [vp] * 15 + [sz, vp]
     lib.kda_chunk_backward_varlen_workspace_size.restype = sz
-    lib.kda_chunk_backward_varlen_workspace_size.argtypes = [i] * 6
+    lib.kda_chunk_backward_varlen_workspace_size.argtypes = [i] * 7
     lib.kda_chunk_backward_varlen.restype = i
-    lib.kda_chunk_backward_varlen.argtypes = [i, i, vp, i, i, i, i, i] + [vp] * 15 + [sz, vp]
+    lib.kda_chunk_backward_varlen.argtypes = [i, i, vp, i, i, i, i, i, i] + [vp] * 15 + [sz, vp]
     lib.kda_chunk_backward_scalar_gate.restype = i
     lib.kda_chunk_backward_scalar_gate.argtypes = lib.kda_chunk_backward.argtypes
     lib.kda_chunk_backward_varlen_scalar_gate.restype = i
@@ -445,13 +445,14 @@ def chunk_prefill_varlen_snapshots(q, k, v, alpha, beta, cu_seqlens, every, init
 
 
 def chunk_backward_varlen(q, k, v, alpha, beta, cu_seqlens, d_o, initial_state=None,
-                          d_final_state=None, chunk=64, workspace=None):
+                          d_final_state=None, chunk=64, workspace=None, max_seqlen=None):
     """Gradients of L = sum(o * d_o) + sum(S_T * d_final_state) for the packed
     variable-length prefill (per-channel alpha).
 
     Inputs as for :func:`chunk_prefill_varlen` (alpha [T_total,H,DK], or
     [T_total,H] for a scalar gate); d_o [T_total,H,DV] float32;
-    d_final_state [N,H,DK,DV] float32 or None.
+    d_final_state [N,H,DK,DV] float32 or None; max_seqlen: the longest
+    sequence (by default read from a host copy of cu_seqlens).
     Returns (dq, dk, dv, dalpha, dbeta, d_initial_state), all float32.
     """
     Tt, H, DK = q.shape
@@ -477,13 +478,16 @@ def chunk_backward_varlen(q, k, v, alpha, beta, cu_seqlens, d_o, initial_state=N
     dv = torch.empty((Tt, H, DV), **f32)
     db = torch.empty((Tt, H), **f32)
     ds0 = torch.empty((N, H, DK, DV), **f32)
-    wsz = lib().kda_chunk_backward_varlen_workspace_size(N, Tt, H, DK, DV, chunk)
+    if max_seqlen is None:
+        lens = cu_seqlens[1:] - cu_seqlens[:-1]
+        max_seqlen = int(lens.max().item()) if N > 0 else 0
+    wsz = lib().kda_chunk_backward_varlen_workspace_size(N, Tt, max_seqlen, H, DK, DV, chunk)
     if wsz and workspace is None:
         workspace = torch.empty(wsz, device=dev, dtype=torch.uint8)
     fn = lib().kda_chunk_backward_varlen_scalar_gate if sg else lib().kda_chunk_backward_varlen
     _check(fn(
-        N, Tt, _ptr(cu_seqlens), H, DK, DV, chunk, dt, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
-        _ptr(beta), _ptr(initial_state), _ptr(d_o), _ptr(d_final_state), _ptr(dq), _ptr(dk),
+        N, Tt, _ptr(cu_seqlens), max_seqlen, H, DK, DV, chunk, dt, _ptr(q), _ptr(k), _ptr(v),
+        _ptr(alpha), _ptr(beta), _ptr(initial_state), _ptr(d_o), _ptr(d_final_state), _ptr(dq), _ptr(dk),
         _ptr(dv), _ptr(dal), _ptr(db), _ptr(ds0), _ptr(workspace),
         0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(dev)))
     return dq, dk, dv, dal, db, ds0

@@ -260,12 +260,11 @@ kda_status_t kda_decode_pool(int N, int L, int H, int DK, int DV, kda_dtype_t in
  *   d_state_in   [B,H,DK,DV] float or NULL: gradient of the initial state
  *   workspace    at least kda_chunk_backward_workspace_size() bytes, 16-byte
  *                aligned, not overlapping any argument (holds the forward's
- *                chunk-boundary states, its outputs and per-slab partial sums).
- *                It grows with the token-heads: about 8 (3 DK + 1) + DV + DK DV / 64
- *                floats each, plus 1 MiB per (sequence, head, 16 value columns)
- *                (d=128: about 13.9 KB per token-head; B=1 H=32 T=8192: 3.9 GB).
- *                Sequences are independent: a batch too large for one call can
- *                be split into calls over groups of sequences.
+ *                chunk-boundary states and outputs, DV + DK DV / 64 floats per
+ *                token-head; the per-slab partial sums of the reverse pass, at
+ *                most 4 GiB: the chunks are processed in windows sized for that;
+ *                1 MiB per (sequence, head, 16 value columns) of token states;
+ *                one state per (sequence, head) when there are several windows).
  * Outputs must not overlap inputs or each other.  The forward is recomputed
  * (with a state checkpoint per chunk); the reverse pass walks every chunk
  * backwards from its checkpoint; the result is deterministic.  With T == 0
@@ -288,15 +287,20 @@ kda_status_t kda_chunk_backward(int B, int T, int H, int DK, int DV, int chunk,
  * states [N,H,DK,DV]).
  *   cu_seqlens   int32 DEVICE [N+1], 4-byte aligned, non-decreasing, from 0 to
  *                T_total (not checked on the device)
- *   workspace    at least kda_chunk_backward_varlen_workspace_size() bytes
- *                (it depends on T_total only through the token count, so the
- *                host never reads the lengths)
+ *   max_seqlen   host int: at least the longest sequence's length (not checked:
+ *                a smaller value leaves the first chunks of longer sequences
+ *                without gradients), or 0 if unknown (then T_total is assumed;
+ *                correct, but the reverse pass may run more, empty, windows)
+ *   workspace    at least kda_chunk_backward_varlen_workspace_size() bytes for
+ *                the same N, T_total, max_seqlen (the host never reads the
+ *                lengths)
  * A sequence of length 0 passes d_state_out through to d_state_in.
  */
-size_t kda_chunk_backward_varlen_workspace_size(int N, int T_total, int H, int DK, int DV,
-                                                int chunk);
-kda_status_t kda_chunk_backward_varlen(int N, int T_total, const int32_t* cu_seqlens, int H,
-                                       int DK, int DV, int chunk, kda_dtype_t in_dtype,
+size_t kda_chunk_backward_varlen_workspace_size(int N, int T_total, int max_seqlen, int H, int DK,
+                                                int DV, int chunk);
+kda_status_t kda_chunk_backward_varlen(int N, int T_total, const int32_t* cu_seqlens,
+                                       int max_seqlen, int H, int DK, int DV, int chunk,
+                                       kda_dtype_t in_dtype,
                                        const void* q, const void* k, const void* v,
                                        const float* alpha, const float* beta,
                                        const float* state_in, const float* d_o,
@@ -325,11 +329,11 @@ kda_status_t kda_chunk_backward_scalar_gate(int B, int T, int H, int DK, int DV,
                                             float* d_state_in, void* workspace,
                                             size_t workspace_bytes, void* stream);
 kda_status_t kda_chunk_backward_varlen_scalar_gate(
-    int N, int T_total, const int32_t* cu_seqlens, int H, int DK, int DV, int chunk,
-    kda_dtype_t in_dtype, const void* q, const void* k, const void* v, const float* gate,
-    const float* beta, const float* state_in, const float* d_o, const float* d_state_out,
-    float* dq, float* dk, float* dv, float* dgate, float* dbeta, float* d_state_in,
-    void* workspace, size_t workspace_bytes, void* stream);
+    int N, int T_total, const int32_t* cu_seqlens, int max_seqlen, int H, int DK, int DV,
+    int chunk, kda_dtype_t in_dtype, const void* q, const void* k, const void* v,
+    const float* gate, const float* beta, const float* state_in, const float* d_o,
+    const float* d_state_out, float* dq, float* dk, float* dv, float* dgate, float* dbeta,
+    float* d_state_in, void* workspace, size_t workspace_bytes, void* stream);
 
 const char* kda_status_string(kda_status_t s);
 const char* kda_last_error_message(void);

@@ -294,24 +294,36 @@ def test_backward_argument_errors(lib):
     assert call(T=0, ptrs=p) == OK
 
 
-def test_backward_varlen_argument_errors(lib):
-    # N=3 sequences, T_total=200 tokens, H=2, d=64 (f32): rows = 400; snapshot
-    # rows T_total // 64 = 3 (chunk j of the sequence starting at token s is
-    # row s // 64 + j); 3 * 2 * 4 slab workgroups of two-chunk token states
-    need = lib.kda_chunk_backward_varlen_workspace_size(3, 200, 2, 64, 64, 64)
-    part = (3 * 4 * 400 * 64 + 4 * 400) * 4
+def test_backward_varlen_argument_errors(lib, monkeypatch):
+    # N=3 sequences, T_total=200 tokens, longest 100, H=2, d=64 (f32): the
+    # reverse pass's partial sums cover a window of chunks counted from each
+    # sequence's end, N * 64 * H * (3 DK + 1) * (DV / 16) floats per chunk of
+    # the window (at most 4 GiB, here every chunk: ceil(100 / 64) = 2); the
+    # forward's o; snapshot rows T_total // 64 = 3 (chunk j of the sequence
+    # starting at token s is row s // 64 + j); 3 * 2 * 4 slab workgroups of
+    # two-chunk token states
+    per_chunk = 3 * 64 * 2 * (3 * 64 + 1) * 4 * 4
     al = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    assert need == al(part) + al(400 * 64 * 4) + al(3 * 2 * 64 * 64 * 4) + \
-        al(3 * 2 * 4 * 2 * 64 * 64 * 16 * 4)
-    assert lib.kda_chunk_backward_varlen_workspace_size(3, 200, 2, 96, 64, 64) == 0
-    assert lib.kda_chunk_backward_varlen_workspace_size(3, 0, 2, 64, 64, 64) == 0
+    rest = al(400 * 64 * 4) + al(3 * 2 * 64 * 64 * 4) + al(3 * 2 * 4 * 2 * 64 * 64 * 16 * 4)
+    need = lib.kda_chunk_backward_varlen_workspace_size(3, 200, 100, 2, 64, 64, 64)
+    assert need == al(2 * per_chunk) + rest
+    # max_seqlen unknown (0): T_total is assumed, 4 chunks
+    assert lib.kda_chunk_backward_varlen_workspace_size(3, 200, 0, 2, 64, 64, 64) == \
+        al(4 * per_chunk) + rest
+    # one chunk per window: two windows, and the adjoint carried between them
+    monkeypatch.setenv("KDA_BWD_WINDOW", "1")
+    assert lib.kda_chunk_backward_varlen_workspace_size(3, 200, 100, 2, 64, 64, 64) == \
+        al(per_chunk) + rest + al(3 * 2 * 64 * 64 * 4)
+    monkeypatch.delenv("KDA_BWD_WINDOW")
+    assert lib.kda_chunk_backward_varlen_workspace_size(3, 200, 100, 2, 96, 64, 64) == 0
+    assert lib.kda_chunk_backward_varlen_workspace_size(3, 0, 0, 2, 64, 64, 64) == 0
     big = ctypes.c_void_p(0x40000000)
     Q = [ctypes.c_void_p(0x100000 * (i + 1)) for i in range(14)]
     cu = ctypes.c_void_p(0x2000000)
 
     def call(N=3, Tt=200, cu=cu, DK=64, ptrs=None, ws=big, wsb=need):
-        return lib.kda_chunk_backward_varlen(N, Tt, cu, 2, DK, 64, 64, 0, *(ptrs or Q), ws, wsb,
-                                             None)
+        return lib.kda_chunk_backward_varlen(N, Tt, cu, 100, 2, DK, 64, 64, 0, *(ptrs or Q), ws,
+                                             wsb, None)
 
     assert call(N=-1) == SHAPE
     assert call(Tt=-5) == SHAPE
@@ -356,7 +368,7 @@ def test_backward_scalar_gate_argument_errors(lib):
     assert call(T=0, ptrs=p) == OK
 
     def vcall(N=2, Tt=100, cu=ctypes.c_void_p(0x2000000), wsb=1 << 30):
-        return lib.kda_chunk_backward_varlen_scalar_gate(N, Tt, cu, 2, 64, 64, 64, 0, *Q, big,
+        return lib.kda_chunk_backward_varlen_scalar_gate(N, Tt, cu, 0, 2, 64, 64, 64, 0, *Q, big,
                                                          wsb, None)
 
     assert vcall(cu=None) == NULL

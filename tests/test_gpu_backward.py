@@ -156,3 +156,57 @@ def test_backward_without_tokens_passes_state_gradient(varlen):
                                dev(dST))
     torch.cuda.synchronize()
     assert torch.equal(g[5], dev(dST))
+
+
+@pytest.mark.parametrize("window", ["1", "3"])
+def test_backward_windows_are_exact(window, monkeypatch):
+    """The reverse pass in windows of 1 or 3 chunks (the adjoint carried
+    between launches, each window's first chunk recomputed from its
+    checkpoint) gives bit for bit the single-window result."""
+    B, T, H, D = 2, 200, 3, 128
+    flush(f"[backward] windows of {window} chunks B={B} T={T} H={H} d={D}")
+    q, k, v, a, b = I.batch_inputs(760, B, T, H, D, D, "bf16")
+    rng = np.random.default_rng(761)
+    do = rng.standard_normal((B, T, H, D)).astype(np.float32)
+    S0 = random_state(rng, (B, H, D, D))
+    dST = random_state(rng, (B, H, D, D))
+    bf = torch.bfloat16
+    x = (dev(q, bf), dev(k, bf), dev(v, bf), dev(a), dev(b), dev(do), dev(S0), dev(dST))
+    ref = kda.chunk_backward(*x)
+    monkeypatch.setenv("KDA_BWD_WINDOW", window)
+    got = kda.chunk_backward(*x)
+    g_gate = kda.chunk_backward(*x[:3], x[3][..., 0].contiguous(), *x[4:])
+    monkeypatch.delenv("KDA_BWD_WINDOW")
+    r_gate = kda.chunk_backward(*x[:3], x[3][..., 0].contiguous(), *x[4:])
+    torch.cuda.synchronize()
+    for n, u, w in zip(NAMES, got, ref):
+        assert torch.equal(u, w), n
+    for n, u, w in zip(NAMES, g_gate, r_gate):
+        assert torch.equal(u, w), n
+
+
+@pytest.mark.parametrize("window,max_seqlen", [("1", None), ("2", 0), ("1", 0)])
+def test_backward_varlen_windows_are_exact(window, max_seqlen, monkeypatch):
+    """Packed sequences in windows (with the longest length given, or unknown:
+    then windows past every sequence's start do nothing) against the
+    single-window call, bit for bit, and against the oracle."""
+    lengths = [37, 0, 64, 1, 200, 129]
+    H, D = 2, 64
+    flush(f"[backward] varlen windows of {window} chunks, max_seqlen={max_seqlen} lengths={lengths}")
+    q, k, v, a, b, cu = I.packed_inputs(770, lengths, H, D, D, "f32")
+    rng = np.random.default_rng(771)
+    do = rng.standard_normal((int(cu[-1]), H, D)).astype(np.float32)
+    S0 = random_state(rng, (len(lengths), H, D, D))
+    dST = random_state(rng, (len(lengths), H, D, D))
+    x = (dev(q), dev(k), dev(v), dev(a), dev(b), torch.from_numpy(cu).cuda(), dev(do), dev(S0),
+         dev(dST))
+    ref = kda.chunk_backward_varlen(*x)
+    monkeypatch.setenv("KDA_BWD_WINDOW", window)
+    got = kda.chunk_backward_varlen(*x, max_seqlen=max_seqlen)
+    monkeypatch.delenv("KDA_BWD_WINDOW")
+    torch.cuda.synchronize()
+    for n, u, w in zip(NAMES, got, ref):
+        assert torch.equal(u, w), n
+    oref = varlen_backward_reference(q, k, v, a, b, cu, do, S0, dST)
+    errs = {n: max_rel_err(host(u), r) for n, u, r in zip(NAMES, got, oref)}
+    assert max(errs.values()) <= TOL["f32"], errs

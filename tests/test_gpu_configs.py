@@ -9,8 +9,8 @@ import torch
 from gated_delta_rule_diag_amd import inputs as I
 from gated_delta_rule_diag_amd import kda
 from kda_testlib import TOL, dev, flush, host
-from oracle import (kda_decode_pool, kda_decode_step, kda_recurrent, kda_recurrent_snapshots,
-                    kda_recurrent_varlen, max_rel_err)
+from oracle import (kda_backward, kda_decode_pool, kda_decode_step, kda_recurrent,
+                    kda_recurrent_snapshots, kda_recurrent_varlen, max_rel_err)
 
 pytestmark = pytest.mark.gpu
 
@@ -164,6 +164,36 @@ def test_varlen_n64_h32_lengths_512_16384_head_subset():
     es = max_rel_err(S[:, heads].cpu().numpy(), S_ref)
     flush(f"    err o={eo:.2e} S={es:.2e}")
     assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+def test_backward_varlen_n64_h32_sequence_head_subset():
+    """The backward pass of the 64-sequence packed workload (576,952 tokens,
+    H=32, d=128, bf16; the reverse pass in windows of chunks): every gradient
+    of the three shortest sequences on heads {0, 31} against the oracle's
+    reverse mode (which keeps every token state, hence the short ones)."""
+    H, D = 32, 128
+    lengths = I.varlen_lengths(3, 64, 512, 16384)
+    Tt = int(lengths.sum())
+    flush(f"[config] backward varlen N=64 total={Tt} H=32 d=128 bf16")
+    q, k, v, a, b, cu = _device_packed(3, lengths, H, D, torch.bfloat16)
+    cu_d = torch.from_numpy(cu.astype(np.int32)).cuda()
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(I.SEED + 31)
+    do = torch.randn((Tt, H, D), generator=gen, device="cuda")
+    grads = kda.chunk_backward_varlen(q, k, v, a, b, cu_d, do)
+    torch.cuda.synchronize()
+    heads = [0, 31]
+    names = ("dq", "dk", "dv", "dalpha", "dbeta")
+    for n in np.argsort(lengths)[:3]:
+        s_, e_ = int(cu[n]), int(cu[n + 1])
+        f = lambda t: t[s_:e_][:, heads].float().cpu().numpy()[None]  # noqa: E731
+        ref = kda_backward(f(q), f(k), f(v), f(a), f(b), None, f(do), None)
+        errs = {nm: max_rel_err(f(g)[0], r[0]) for nm, g, r in zip(names, grads[:5], ref[:5])}
+        errs["dS0"] = max_rel_err(grads[5][n, heads].cpu().numpy(), ref[5][0])
+        flush(f"    sequence {n} (length {e_ - s_}): " +
+              " ".join(f"{nm}={e:.1e}" for nm, e in errs.items()))
+        assert max(errs.values()) <= TOL["bf16"], (n, errs)
+    del grads
 
 
 def test_long_context_1m_prefill_then_1024_decode_steps_head_subset():
