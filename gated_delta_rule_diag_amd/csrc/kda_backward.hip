@@ -435,10 +435,10 @@ __global__ __launch_bounds__(kNT) void kda_bwd_kernel(BackwardArgs p) {
         const int i = x % DK;
         const int qn = x / DK < 2 ? x / DK : 2;
         const float v = sum_waves(&ring[par][qn][0][i], DK);
-        const int64_t prow = (lrow * DK + i) * nslab + slab;
+        const int64_t prow = (slab * p.part_rows + lrow) * DK + i;   // slab-major: one row is 512 B
         (qn == 0 ? p.part_dq : (qn == 1 ? p.part_dk : p.part_da))[prow] = v;
       }
-      p.part_db[lrow * nslab + slab] = sum_waves(ringb[par], 1);
+      p.part_db[slab * p.part_rows + lrow] = sum_waves(ringb[par], 1);
     }
     par ^= 1;
   };
@@ -516,17 +516,19 @@ __device__ __forceinline__ int64_t window_row(const BackwardArgs& p, int64_t lro
 }
 
 // dq, dk, dalpha (per element) and dbeta: sums of the NS per-slab partials,
-// which are stored slab-minor, so a thread reads NS consecutive floats per
-// output and a wave streams contiguous memory.
+// which are stored slab-major (the walk writes whole 512-byte rows), so a
+// thread reads NS values `stride` apart and a wave reads NS contiguous
+// streams; the slabs are added pairwise in a fixed order.
 template <int NS>
-__device__ __forceinline__ float sum_ns(const float* p) {
-  float s = 0.f;
+__device__ __forceinline__ float sum_ns(const float* p, int64_t stride) {
+  float x[NS];
 #pragma unroll
-  for (int v = 0; v < NS; v += 4) {
-    const float4 x = *reinterpret_cast<const float4*>(p + v);
-    s += (x.x + x.y) + (x.z + x.w);
-  }
-  return s;
+  for (int v = 0; v < NS; ++v) x[v] = p[v * stride];
+#pragma unroll
+  for (int h = 1; h < NS; h <<= 1)
+#pragma unroll
+    for (int v = 0; v + h < NS; v += 2 * h) x[v] += x[v + h];
+  return x[0];
 }
 
 template <int DK, int NS, bool SG>
@@ -538,32 +540,28 @@ __global__ __launch_bounds__(256) void kda_bwd_reduce_kernel(BackwardArgs p) {
   const int64_t grow = window_row(p, lrow);
   if (grow < 0) return;
   const int64_t o = grow * DK + i;
-  p.dq[o] = sum_ns<NS>(p.part_dq + idx * NS);
-  p.dk[o] = sum_ns<NS>(p.part_dk + idx * NS);
-  if constexpr (!SG) p.dalpha[o] = sum_ns<NS>(p.part_da + idx * NS);
-  if (i == 0) p.dbeta[grow] = sum_ns<NS>(p.part_db + lrow * NS);
+  const int64_t st = p.part_rows * DK;
+  p.dq[o] = sum_ns<NS>(p.part_dq + idx, st);
+  p.dk[o] = sum_ns<NS>(p.part_dk + idx, st);
+  if constexpr (!SG) p.dalpha[o] = sum_ns<NS>(p.part_da + idx, st);
+  if (i == 0) p.dbeta[grow] = sum_ns<NS>(p.part_db + lrow, p.part_rows);
 }
 
 // A scalar gate's gradient: the sum over key rows and slabs of the per-row
 // partials (chain rule: the gate is every row's decay), one wave per token
-// row; each lane adds DK * NS / 64 consecutive values, then the lanes are
+// row; each lane adds the slabs of its DK / 64 key rows, then the lanes are
 // added in a fixed order (deterministic).
 template <int DK, int NS>
 __global__ __launch_bounds__(256) void kda_bwd_dgate_kernel(BackwardArgs p) {
-  constexpr int PER = DK * NS / 64;
-  static_assert(PER % 4 == 0, "float4 pieces");
+  constexpr int PER = DK / 64;   // key rows per lane
   const int64_t lrow = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
   const int l = threadIdx.x & 63;
   if (lrow >= p.part_rows) return;
   const int64_t row = window_row(p, lrow);
   if (row < 0) return;
-  const float* src = p.part_da + lrow * (DK * NS) + l * PER;
   float s = 0.f;
 #pragma unroll
-  for (int i = 0; i < PER; i += 4) {
-    const float4 x = *reinterpret_cast<const float4*>(src + i);
-    s += (x.x + x.y) + (x.z + x.w);
-  }
+  for (int r = 0; r < PER; ++r) s += sum_ns<NS>(p.part_da + lrow * DK + l * PER + r, p.part_rows * DK);
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) s += __shfl_xor(s, off);
   if (l == 0) p.dalpha[row] = s;
