@@ -1,5 +1,5 @@
 """The entry points under HIP graph capture (torch.cuda.CUDAGraph): the
-captured decode step and staged prefill are replayed several times, with the
+captured decode step, staged prefill and backward are replayed several times, with the
 program's own eager work and synchronisations between replays, and every
 replay is checked against the eager result.  None of the kernels records a
 memset or allocates, so the captured launches are plain kernel nodes."""
@@ -81,3 +81,42 @@ def test_staged_prefill_replays_match_eager():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(o, o_ref) and torch.equal(S, S_ref), i
+
+
+@pytest.mark.parametrize("window", [None, "1"])
+def test_backward_replays_match_eager(window, monkeypatch):
+    """The backward call (forward with checkpoints, the reverse walk, the
+    reductions; with windows of one chunk, one walk and reduction per chunk
+    with the adjoint carried in the workspace) captured once and replayed;
+    every replay equals the eager call."""
+    if window:
+        monkeypatch.setenv("KDA_BWD_WINDOW", window)
+    B, T, H, D = 1, 200, 3, 128
+    flush(f"[graph] backward B={B} T={T} H={H} d={D} window={window}: 3 replays")
+    q, k, v, a, b = I.batch_inputs(802, B, T, H, D, D, "bf16")
+    rng = np.random.default_rng(803)
+    do = rng.standard_normal((B, T, H, D)).astype(np.float32)
+    S0 = random_state(rng, (B, H, D, D))
+    bf = torch.bfloat16
+    x = [dev(q, bf), dev(k, bf), dev(v, bf), dev(a), dev(b), dev(do), dev(S0)]
+    ws = torch.empty(kda.lib().kda_chunk_backward_workspace_size(B, T, H, D, D, 64),
+                     device="cuda", dtype=torch.uint8)
+    ref = kda.chunk_backward(*x, workspace=ws)
+    torch.cuda.synchronize()
+    ref = [r.clone() for r in ref]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        kda.chunk_backward(*x, workspace=ws)     # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out = kda.chunk_backward(*x, workspace=ws)
+    for i in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        for u, w in zip(out, ref):
+            assert torch.equal(u, w), i
+        _ = (x[3] * 2).sum()                     # unrelated eager work between replays
+        torch.cuda.synchronize()
