@@ -805,7 +805,11 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_prefill_kernel(Params p
   // read the same q/k/alpha, run on one XCD and share its L2.
   int64_t b = blockIdx.x;
   const int64_t G = gridDim.x;
-  if ((G & 7) == 0) b = (b & 7) * (G >> 3) + (b >> 3);
+  // The remap hands each XCD a contiguous range of sequences, so it is used
+  // only when there are several slabs per head to share: with one slab,
+  // a packed batch sorted by length would put its longest sequences on one
+  // XCD and leave the others idle (1.6x slower than round-robin).
+  if ((G & 7) == 0 && p.nslab > 1) b = (b & 7) * (G >> 3) + (b >> 3);
   const int slab = int(b % p.nslab);
   const int64_t pr = b / p.nslab;
   const int h = int(pr % p.H);

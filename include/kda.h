@@ -161,7 +161,8 @@ kda_status_t kda_chunk_prefill_varlen_snapshots(int N, int T_total, const int32_
  *   q, k, alpha [T_total,H,DK];  v, o [T_total,H,DV];  beta [T_total,H]
  *   state_in / state_out  [N,H,DK,DV] as above (one state per sequence)
  * Chunks restart at every sequence start; a zero-length sequence passes its
- * state through.
+ * state through.  The order of the sequences in the pack only affects speed:
+ * longest first finishes soonest (the long chains start first).
  */
 size_t kda_chunk_prefill_varlen_workspace_size(int N, int T_total, int H, int DK, int DV,
                                                int chunk);
