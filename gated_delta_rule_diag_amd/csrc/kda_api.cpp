@@ -467,11 +467,18 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // Packed sequences: T_fixed = 0, max_chunks from the longest sequence, and
 // the snapshot rows are T_total / 64 (chunk j of the sequence starting at
 // token s is row s / 64 + j).
+bool bwd_token_walk() {
+  const char* e = getenv("KDA_BWD_TOKEN");
+  return e && e[0] == '1';
+}
+
 BwdLayout bwd_layout(int N, int T_fixed, int64_t T_total, int64_t max_chunks, int H, int DK,
                      int DV, bool varlen) {
   BwdLayout L{};
   const size_t rows = size_t(T_total) * H, nslab = size_t(DV) / 16;
-  const size_t per_chunk = size_t(N) * 64 * H * (3 * size_t(DK) + 1) * nslab * 4;
+  const size_t per_chunk = bwd_token_walk()
+                               ? size_t(N) * 64 * H * (3 * size_t(DK) + 1) * nslab * 4
+                               : size_t(N) * H * kda::backward_chunk_floats(DK, DV) * 4;
   int64_t k = int64_t((size_t(4) << 30) / per_chunk);
   if (const char* e = getenv("KDA_BWD_WINDOW")) {
     const long v = atol(e);
@@ -489,7 +496,7 @@ BwdLayout bwd_layout(int N, int T_fixed, int64_t T_total, int64_t max_chunks, in
   L.o = align256(pw > part ? pw : part);
   L.snaps = L.o + align256(rows * DV * 4);
   L.scratch = L.snaps + align256(snap_rows * H * DK * DV * 4);
-  L.carry = L.scratch + align256(kda::backward_scratch_bytes(N, H, DK, DV));
+  L.carry = L.scratch + (bwd_token_walk() ? align256(kda::backward_scratch_bytes(N, H, DK, DV)) : 0);
   L.total = L.carry + (L.nwin > 1 ? align256(size_t(N) * H * DK * DV * 4) : 0);
   return L;
 }
@@ -525,14 +532,14 @@ kda_status_t run_backward(int N, int T_fixed, const int32_t* cu_seqlens, int64_t
       return fail(KDA_ERR_ALIGN, "d_state_in and d_state_out must be 16-byte aligned");
     if (d_state_out && d_state_out != d_state_in && overlaps(d_state_in, ns, d_state_out, ns))
       return fail(KDA_ERR_SHAPE, "d_state_in overlaps d_state_out");
-    kda::BackwardArgs a{};
-    a.N = N; a.H = H; a.DK = DK; a.DV = DV; a.T = 0; a.cu_seqlens = cu_seqlens; a.rows = 0;
-    a.in_bf16 = in_dtype == KDA_BF16;
-    a.alpha_scalar = alpha_scalar;
-    a.win_lo = 0; a.win_k = 1;
-    a.d_state_out = d_state_out; a.d_state_in = d_state_in;
     const char* msg = nullptr;
-    if (kda::launch_backward(a, stream, &msg) != 0)
+    kda::BwdChunkArgs c{};
+    c.N = N; c.H = H; c.DK = DK; c.DV = DV; c.T = 0; c.cu_seqlens = cu_seqlens;
+    c.in_bf16 = in_dtype == KDA_BF16;
+    c.alpha_scalar = alpha_scalar;
+    c.win_lo = 0; c.win_k = 1;
+    c.d_state_out = d_state_out; c.d_state_in = d_state_in;
+    if (kda::launch_backward_chunk(c, 1, stream, &msg) != 0)
       return fail(KDA_ERR_HIP, "backward launch failed: %s", msg ? msg : "?");
     return ok();
   }
@@ -592,6 +599,33 @@ kda_status_t run_backward(int N, int T_fixed, const int32_t* cu_seqlens, int64_t
   const char* msg = nullptr;
   if (kda::launch_prefill(f, stream, &msg) != 0)
     return fail(KDA_ERR_HIP, "backward: forward launch failed: %s", msg ? msg : "?");
+  if (!bwd_token_walk()) {
+    // 2. per window of chunks: per-chunk matrices, the adjoint's pass, gradients
+    kda::BwdChunkArgs c{};
+    c.N = N; c.H = H; c.DK = DK; c.DV = DV; c.T = varlen ? 0 : T_fixed; c.cu_seqlens = cu_seqlens;
+    c.in_bf16 = in_dtype == KDA_BF16;
+    c.alpha_scalar = alpha_scalar;
+    c.q = q; c.k = k; c.v = v; c.alpha = alpha; c.beta = beta; c.state_in = state_in;
+    c.d_o = d_o; c.d_state_out = d_state_out;
+    c.snapshots = reinterpret_cast<const float*>(ws + L.snaps);
+    c.dq = dq; c.dk = dk; c.dv = dv; c.dalpha = dalpha; c.dbeta = dbeta; c.d_state_in = d_state_in;
+    c.carry = L.nwin > 1 ? reinterpret_cast<float*>(ws + L.carry) : nullptr;
+    c.win_k = L.win_k;
+    const size_t per = size_t(N) * size_t(L.win_k) * H;   // chunk-heads of a window
+    c.Ac = reinterpret_cast<float*>(ws + L.fwd_or_part);
+    c.bc = c.Ac + per * DK * DK;
+    c.dSend = c.bc + per * DK * DV;
+    c.Mb = c.dSend + per * DK * DV;
+    c.Vnb = c.Mb + per * 64 * 64;
+    c.rho = c.Vnb + per * 64 * DV;
+    for (int64_t w = 0; w < L.nwin; ++w) {
+      c.win_lo = w * L.win_k;
+      for (int stage = 0; stage < 3; ++stage)
+        if (kda::launch_backward_chunk(c, stage, stream, &msg) != 0)
+          return fail(KDA_ERR_HIP, "backward launch failed: %s", msg ? msg : "?");
+    }
+    return ok();
+  }
   // 2-3. reverse pass and the reduction of the per-slab sums
   kda::BackwardArgs a{};
   a.N = N; a.H = H; a.DK = DK; a.DV = DV; a.T = varlen ? 0 : T_fixed; a.cu_seqlens = cu_seqlens;

@@ -1,0 +1,881 @@
+// KDA backward in chunk form (training).
+//
+// The gradient of the chunk algorithm of the Kimi Linear technical report
+// (section "Kimi Delta Attention", chunk-wise form with the WY representation
+// and the UT transform) taken through its own matrices instead of token by
+// token.  Per chunk of C = 64 tokens, with rho_r = gamma_r / gamma_m the decay
+// of row r relative to the midpoint row m = 31 (products of alpha, no logs):
+//   Kr = k rho,  Kh = k / rho,  Qr = q rho                 (per row and channel)
+//   X = strict_lower(Kr Kh^T),  M = (I + Diag(beta) X)^-1,  T = M Diag(beta)
+//   W = T Kr Diag(gamma_m)  (= T K_gamma),  U = T V,  Vn = U - W S
+//   P = lower(Qr Kh^T),  O = Qr Diag(gamma_m) S + P Vn
+//   S' = Diag(gamma_C) S + (Kh Diag(gamma_C / gamma_m))^T Vn
+// S is the state entering the chunk (the forward's snapshot).  The adjoint of
+// the state entering the chunk is affine in the adjoint of the state leaving
+// it: dS = b_c + A_c dS' with A_c = Diag(gamma_C) - W^T Kend and
+// b_c = (Qa - P W)^T dO, so the reverse pass is three launches per window of
+// chunks:
+//   prep   one workgroup per chunk-head: A_c, b_c, M, Vn and rho;
+//   chain  one workgroup per (sequence, head, 16 value columns): the adjoints
+//          dS' at every chunk end, sequentially from the last chunk;
+//   post   one workgroup per chunk-head: dq, dk, dv, dalpha, dbeta from
+//          S, dS', M, Vn (all products and the solve's adjoint in registers
+//          and LDS).
+// All products are fp32 MFMA (16x16x4) on LDS operands.
+#include <hip/hip_runtime.h>
+
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+constexpr int kC = 64;      // chunk
+constexpr int kMid = 31;    // reference row of the relative decays
+constexpr int kNW = 8;      // waves per workgroup (prep, post)
+constexpr int kNT = 64 * kNW;
+constexpr int kLS = 20;     // pitch (floats) of a 16-column slab
+constexpr int kL64 = 68;    // pitch of a 64-column array
+
+template <bool BF16>
+__device__ __forceinline__ float ld_in(const void* p, int64_t i) {
+  if constexpr (BF16) {
+    const uint16_t b = static_cast<const uint16_t*>(p)[i];
+    return __uint_as_float(uint32_t(b) << 16);
+  } else {
+    return static_cast<const float*>(p)[i];
+  }
+}
+
+// acc[s] += A(tile rows, 0:K) B(0:K, tile cols) for the tiles t = wv + 8 s of
+// the (M/16) x (N/16) tile grid (row-major), wv being the caller's wave slot.
+//   A(m, k) = AK ? a[m * lda + k] : a[k * lda + m]
+//   B(k, n) = BK ? b[n * ldb + k] : b[k * ldb + n]
+// Within each 16-wide block of K, lane group g takes k = 4g .. 4g + 3 over the
+// four products (lane i = row of A / column of B).  TRI skips work known to be
+// zero: 1 = tiles above the diagonal of the output; 2 = A lower triangular
+// (k <= m); 3 = A upper triangular (k >= m).  The result lane holds rows
+// 4g + q of column i of its tile.
+template <int M, int N, int K, bool AK, bool BK, int TRI, int NT>
+__device__ __forceinline__ void mm(f4 (&acc)[NT], const float* a, int lda, const float* b, int ldb,
+                                   int wv) {
+  constexpr int TN = N / 16, NTILE = (M / 16) * TN;
+  const int l = threadIdx.x & 63, i = l & 15, g = l >> 4;
+#pragma unroll
+  for (int s = 0; s < NT; ++s) {
+    const int t = wv + kNW * s;
+    if (t >= NTILE) break;
+    const int m0 = (t / TN) * 16, n0 = (t % TN) * 16;
+    if (TRI == 1 && n0 > m0) continue;
+    const int klo = TRI == 3 ? m0 : 0;
+    const int khi = TRI == 2 ? m0 + 16 : K;
+#pragma unroll
+    for (int k0 = 0; k0 < K; k0 += 16) {
+      if (k0 < klo || k0 >= khi) continue;
+      f4 av, bv;
+      if constexpr (AK) {
+        av = *reinterpret_cast<const f4*>(a + (m0 + i) * lda + k0 + 4 * g);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) av[j] = a[(k0 + 4 * g + j) * lda + m0 + i];
+      }
+      if constexpr (BK) {
+        bv = *reinterpret_cast<const f4*>(b + (n0 + i) * ldb + k0 + 4 * g);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bv[j] = b[(k0 + 4 * g + j) * ldb + n0 + i];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[s] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j], bv[j], acc[s], 0, 0, 0);
+    }
+  }
+}
+
+template <int NT>
+__device__ __forceinline__ void zero(f4 (&acc)[NT]) {
+#pragma unroll
+  for (int s = 0; s < NT; ++s) acc[s] = f4{0.f, 0.f, 0.f, 0.f};
+}
+
+// Tile s of a wave: first row m0, first column n0 (N columns in the grid).
+template <int N>
+__device__ __forceinline__ void tile_origin(int wv, int s, int& m0, int& n0) {
+  const int t = wv + kNW * s;
+  m0 = (t / (N / 16)) * 16;
+  n0 = (t % (N / 16)) * 16;
+}
+template <int M, int N>
+__device__ __forceinline__ bool tile_live(int wv, int s) {
+  return wv + kNW * s < (M / 16) * (N / 16);
+}
+
+// The chunk a workgroup works on: sequence n, chunk c counted from the start
+// (the window holds reverse indices win_lo .. win_lo + win_k - 1).
+struct Chunk {
+  int64_t n, c, s0, tok0, wi;
+  int nv, h;
+};
+
+__device__ __forceinline__ bool locate(const BwdChunkArgs& p, int64_t n, int64_t jw, int h,
+                                       Chunk& ck) {
+  int64_t s0, len;
+  if (p.cu_seqlens) {
+    s0 = p.cu_seqlens[n];
+    len = p.cu_seqlens[n + 1] - s0;
+  } else {
+    s0 = n * p.T;
+    len = p.T;
+  }
+  const int64_t nch = (len + kC - 1) / kC;
+  ck.n = n;
+  ck.h = h;
+  ck.s0 = s0;
+  ck.c = nch - 1 - (p.win_lo + jw);
+  if (ck.c < 0) return false;
+  ck.tok0 = s0 + ck.c * kC;
+  const int64_t rem = len - ck.c * kC;
+  ck.nv = int(rem < kC ? rem : kC);
+  ck.wi = (n * p.win_k + jw) * p.H + h;
+  return true;
+}
+
+// The state entering chunk c: state_in for the first chunk (nullptr = zero),
+// else the forward's snapshot after chunk c - 1.
+template <int DK>
+__device__ __forceinline__ const float* chunk_state(const BwdChunkArgs& p, const Chunk& ck) {
+  const int64_t hs = int64_t(DK) * p.DV;
+  if (ck.c == 0) return p.state_in ? p.state_in + (ck.n * p.H + ck.h) * hs : nullptr;
+  const int64_t base = p.cu_seqlens ? ck.s0 / kC : ck.n * (p.T / kC);
+  return p.snapshots + ((base + ck.c - 1) * p.H + ck.h) * hs;
+}
+
+// rho (relative decays) of the chunk into rho_out[64][ld] and the global copy;
+// gm = gamma_m, gq = gamma_C / gamma_m per channel.  Threads 0..DK-1, one
+// channel each; rows past the chunk's end take alpha = 1.
+template <int DK, bool SG>
+__device__ __forceinline__ void decays(const BwdChunkArgs& p, const Chunk& ck, float* rho, int ld,
+                                       float* rho_g, float* sgm, float* sgq) {
+  const int c = threadIdx.x;
+  if (c >= DK) return;
+  float a[kC];
+#pragma unroll
+  for (int r = 0; r < kC; ++r) {
+    const int64_t row = (ck.tok0 + r) * p.H + ck.h;
+    a[r] = r < ck.nv ? (SG ? p.alpha[row] : p.alpha[row * DK + c]) : 1.f;
+  }
+  float gm = 1.f;
+#pragma unroll
+  for (int r = 0; r <= kMid; ++r) gm *= a[r];
+  float x = 1.f;
+  rho[kMid * ld + c] = 1.f;
+  rho_g[kMid * DK + c] = 1.f;
+#pragma unroll
+  for (int r = kMid - 1; r >= 0; --r) {   // sigma_r = prod_{r < i <= m} alpha_i
+    x *= a[r + 1];
+    const float v = 1.f / x;
+    rho[r * ld + c] = v;
+    rho_g[r * DK + c] = v;
+  }
+  x = 1.f;
+#pragma unroll
+  for (int r = kMid + 1; r < kC; ++r) {
+    x *= a[r];
+    rho[r * ld + c] = x;
+    rho_g[r * DK + c] = x;
+  }
+  sgm[c] = gm;
+  sgq[c] = x;
+}
+
+// ---------------------------------------------------------------- prep ------
+template <int DK, bool BF16, bool SG>
+__global__ __launch_bounds__(kNT, 1) void kda_bwdc_prep_kernel(BwdChunkArgs p) {
+  constexpr int LD = DK + 4;
+  constexpr int NTW = (4 * (DK / 16) + kNW - 1) / kNW;          // 64 x DK tiles per wave
+  constexpr int NTA = ((DK / 16) * (DK / 16) + kNW - 1) / kNW;  // DK x DK
+  __shared__ __attribute__((aligned(16))) float sm[3 * 64 * LD + 2 * 64 * kL64 + 2 * DK + 64 +
+                                                   (128 + DK) * kLS];
+  float* const sKr = sm;             // Kr, then W
+  float* const sKh = sKr + 64 * LD;
+  float* const sQr = sKh + 64 * LD;
+  float* const sM = sQr + 64 * LD;   // Diag(beta) X, then M, then T
+  float* const sP = sM + 64 * kL64;
+  float* const sgm = sP + 64 * kL64;
+  float* const sgq = sgm + DK;
+  float* const sb = sgq + DK;
+  float* const sV = sb + 64;         // V slab, then Z slab (also the solve's scratch)
+  float* const sO = sV + 64 * kLS;   // dO slab
+  float* const sS = sO + 64 * kLS;   // S slab [DK][16]
+
+  const int t = threadIdx.x, w = t >> 6, l = t & 63, li = l & 15, g = l >> 4;
+  const int H = p.H, DV = p.DV;
+  const int64_t bid = blockIdx.x;
+  const int h = int(bid % H);
+  const int64_t jw = (bid / H) % p.win_k, n = bid / H / p.win_k;
+  Chunk ck;
+  if (!locate(p, n, jw, h, ck)) return;
+  const int nv = ck.nv;
+
+  // 1. decays, scaled keys and queries, beta
+  float* const rho_g = p.rho + ck.wi * (64 * DK);
+  decays<DK, SG>(p, ck, sQr, LD, rho_g, sgm, sgq);   // rho parked in sQr
+  if (t < 64) sb[t] = t < nv ? p.beta[(ck.tok0 + t) * H + h] : 0.f;
+  __syncthreads();
+  for (int e = t; e < 64 * DK; e += kNT) {
+    const int r = e / DK, c = e % DK;
+    const float rh = sQr[r * LD + c];
+    const int64_t x = ((ck.tok0 + r) * H + h) * int64_t(DK) + c;
+    const float kv = r < nv ? ld_in<BF16>(p.k, x) : 0.f;
+    const float qv = r < nv ? ld_in<BF16>(p.q, x) : 0.f;
+    sKr[r * LD + c] = kv * rh;
+    sKh[r * LD + c] = kv / rh;
+    sQr[r * LD + c] = qv * rh;
+  }
+  __syncthreads();
+
+  // 2. Diag(beta) X and P
+  {
+    f4 ax[2], ap[2];
+    zero(ax);
+    zero(ap);
+    mm<64, 64, DK, true, true, 1>(ax, sKr, LD, sKh, LD, w);
+    mm<64, 64, DK, true, true, 1>(ap, sQr, LD, sKh, LD, w);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      int m0, n0;
+      tile_origin<64>(w, s, m0, n0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = m0 + 4 * g + q, c = n0 + li;
+        sM[r * kL64 + c] = c < r ? sb[r] * ax[s][q] : 0.f;
+        sP[r * kL64 + c] = c <= r ? ap[s][q] : 0.f;
+      }
+    }
+  }
+  __syncthreads();
+
+  // 3. M = (I + Diag(beta) X)^-1 in place: the four diagonal 16x16 blocks by
+  // forward substitution (wave 0, lane = column of a block), then block rows
+  // 1..3: M_ij = -M_ii sum_{j <= k < i} A_ik M_kj.
+  if (w == 0) {
+    const int o = 16 * g;
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float s = r == li ? 1.f : 0.f;
+#pragma unroll
+      for (int u = 0; u < r; ++u) s -= sM[(o + r) * kL64 + o + u] * x[u];
+      x[r] = s;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sM[(o + r) * kL64 + o + li] = x[r];
+  }
+  __syncthreads();
+  for (int bi = 1; bi < 4; ++bi) {
+    f4 acc = f4{0.f, 0.f, 0.f, 0.f};
+    const int bj = w;
+    if (bj < bi) {
+      for (int bk = bj; bk < bi; ++bk) {
+        const f4 av = *reinterpret_cast<const f4*>(sM + (16 * bi + li) * kL64 + 16 * bk + 4 * g);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j], sM[(16 * bk + 4 * g + j) * kL64 + 16 * bj + li],
+                                                     acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sV[(16 * bj + 4 * g + q) * kLS + li] = acc[q];
+    }
+    __syncthreads();
+    f4 acc2 = f4{0.f, 0.f, 0.f, 0.f};
+    if (bj < bi) {
+      const f4 av = *reinterpret_cast<const f4*>(sM + (16 * bi + li) * kL64 + 16 * bi + 4 * g);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j], sV[(16 * bj + 4 * g + j) * kLS + li], acc2, 0, 0,
+                                                    0);
+    }
+    __syncthreads();
+    if (bj < bi) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sM[(16 * bi + 4 * g + q) * kL64 + 16 * bj + li] = -acc2[q];
+    }
+    __syncthreads();
+  }
+
+  // 4. M out; T = M Diag(beta) in place
+  float* const Mg = p.Mb + ck.wi * (64 * 64);
+  for (int e = t; e < 64 * 64; e += kNT) {
+    const int r = e >> 6, c = e & 63;
+    const float m = sM[r * kL64 + c];
+    Mg[e] = m;
+    sM[r * kL64 + c] = m * sb[c];
+  }
+  __syncthreads();
+
+  // 5. W = T Kr Diag(gamma_m), over Kr
+  {
+    f4 aw[NTW];
+    zero(aw);
+    mm<64, DK, 64, true, false, 2>(aw, sM, kL64, sKr, LD, w);
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < NTW; ++s) {
+      if (!tile_live<64, DK>(w, s)) break;
+      int m0, n0;
+      tile_origin<DK>(w, s, m0, n0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sKr[(m0 + 4 * g + q) * LD + n0 + li] = aw[s][q] * sgm[n0 + li];
+    }
+  }
+  __syncthreads();
+  float* const sW = sKr;
+
+  // 6. A_c = Diag(gamma_C) - W^T Kh Diag(gamma_C / gamma_m), stored for the
+  // chain with the columns of each row permuted (lane group g of the chain
+  // reads the columns 4j + g, j = 0 .. DK/4 - 1, contiguously).
+  {
+    f4 aa[NTA];
+    zero(aa);
+    mm<DK, DK, 64, false, false, 0>(aa, sW, LD, sKh, LD, w);
+    float* const Ag = p.Ac + ck.wi * (int64_t(DK) * DK);
+#pragma unroll
+    for (int s = 0; s < NTA; ++s) {
+      if (!tile_live<DK, DK>(w, s)) break;
+      int m0, n0;
+      tile_origin<DK>(w, s, m0, n0);
+      const int c = n0 + li;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = m0 + 4 * g + q;
+        float v = -sgq[c] * aa[s][q];
+        if (r == c) v += sgm[r] * sgq[r];
+        Ag[r * DK + (c & 3) * (DK / 4) + (c >> 2)] = v;
+      }
+    }
+  }
+
+  // 7. per 16 value columns: Vn = T V - W S;  b_c = Diag(gamma_m) Qr^T dO - W^T (P^T dO)
+  const float* const S = chunk_state<DK>(p, ck);
+  float* const Vng = p.Vnb + ck.wi * (64 * int64_t(DV));
+  float* const bg = p.bc + ck.wi * (int64_t(DK) * DV);
+  for (int js = 0; js < DV / 16; ++js) {
+    for (int e = t; e < 64 * 16; e += kNT) {
+      const int r = e >> 4, j = e & 15;
+      const int64_t x = ((ck.tok0 + r) * H + h) * int64_t(DV) + 16 * js + j;
+      sV[r * kLS + j] = r < nv ? ld_in<BF16>(p.v, x) : 0.f;
+      sO[r * kLS + j] = r < nv ? p.d_o[x] : 0.f;
+    }
+    for (int e = t; e < DK * 16; e += kNT) {
+      const int r = e >> 4, j = e & 15;
+      sS[r * kLS + j] = S ? S[int64_t(r) * DV + 16 * js + j] : 0.f;
+    }
+    __syncthreads();
+    f4 au[1], an[1], az[1];
+    zero(au);
+    zero(an);
+    zero(az);
+    mm<64, 16, 64, true, false, 2>(au, sM, kL64, sV, kLS, w);
+    mm<64, 16, DK, true, false, 0>(an, sW, LD, sS, kLS, w);
+    mm<64, 16, 64, false, false, 3>(az, sP, kL64, sO, kLS, (w + 4) & 7);
+    if (w < 4) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) Vng[(16 * w + 4 * g + q) * DV + 16 * js + li] = au[0][q] - an[0][q];
+    }
+    __syncthreads();
+    if (w >= 4) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sV[(16 * (w - 4) + 4 * g + q) * kLS + li] = az[0][q];
+    }
+    __syncthreads();
+    f4 b1[1], b2[1];
+    zero(b1);
+    zero(b2);
+    mm<DK, 16, 64, false, false, 0>(b1, sQr, LD, sO, kLS, w);
+    mm<DK, 16, 64, false, false, 0>(b2, sW, LD, sV, kLS, w);
+    if (tile_live<DK, 16>(w, 0)) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = 16 * w + 4 * g + q;
+        bg[r * DV + 16 * js + li] = sgm[r] * b1[0][q] - b2[0][q];
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------- chain -----
+// dS (adjoint of the state entering a chunk) = b_c + A_c dS'.  One workgroup
+// per (sequence, head, 16 value columns); wave w holds rows 16w .. 16w + 15 of
+// the slab in the MFMA result layout.  dS' of every chunk goes to dSend.
+template <int DK>
+__global__ __launch_bounds__(64 * (DK / 16), 1) void kda_bwdc_chain_kernel(BwdChunkArgs p) {
+  constexpr int KQ = DK / 4;
+  __shared__ __attribute__((aligned(16))) float sD[2][DK * 16];
+  const int t = threadIdx.x, w = t >> 6, l = t & 63, li = l & 15, g = l >> 4;
+  const int H = p.H, DV = p.DV, nsl = DV / 16;
+  const int64_t bid = blockIdx.x;
+  const int slab = int(bid % nsl);
+  const int64_t pr = bid / nsl;
+  const int h = int(pr % H);
+  const int64_t n = pr / H;
+  int64_t s0, len;
+  if (p.cu_seqlens) {
+    s0 = p.cu_seqlens[n];
+    len = p.cu_seqlens[n + 1] - s0;
+  } else {
+    s0 = n * p.T;
+    len = p.T;
+  }
+  (void)s0;
+  const int64_t nch = (len + kC - 1) / kC;
+  const int64_t c_hi = nch - 1 - p.win_lo;
+  const int64_t hs = (n * H + h) * int64_t(DK) * DV;
+  const int col = 16 * slab + li;
+  f4 dS;
+  if (p.win_lo == 0 || c_hi < 0) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      dS[q] = p.d_state_out ? p.d_state_out[hs + int64_t(16 * w + 4 * g + q) * DV + col] : 0.f;
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dS[q] = p.carry[hs + int64_t(16 * w + 4 * g + q) * DV + col];
+  }
+  if (c_hi < 0) {   // no chunk in this window: only an empty sequence writes (window 0)
+    if (p.win_lo == 0 && p.d_state_in) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) p.d_state_in[hs + int64_t(16 * w + 4 * g + q) * DV + col] = dS[q];
+    }
+    return;
+  }
+  int64_t c = c_hi;
+  for (int64_t jw = 0; jw < p.win_k && c >= 0; ++jw, --c) {
+    const int64_t wi = (n * p.win_k + jw) * H + h;
+    float* const sd = sD[jw & 1];
+    float* const de = p.dSend + wi * (int64_t(DK) * DV);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = 16 * w + 4 * g + q;
+      sd[r * 16 + li] = dS[q];
+      de[r * DV + col] = dS[q];
+    }
+    const float* const ar = p.Ac + wi * (int64_t(DK) * DK) + (16 * w + li) * DK + g * KQ;
+    f4 a[KQ / 4];
+#pragma unroll
+    for (int j = 0; j < KQ / 4; ++j) a[j] = *reinterpret_cast<const f4*>(ar + 4 * j);
+    f4 acc0, acc1 = f4{0.f, 0.f, 0.f, 0.f};
+    const float* const br = p.bc + wi * (int64_t(DK) * DV);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc0[q] = br[(16 * w + 4 * g + q) * DV + col];
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < KQ; j += 2) {
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j >> 2][j & 3], sd[(4 * j + g) * 16 + li], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[(j + 1) >> 2][(j + 1) & 3], sd[(4 * (j + 1) + g) * 16 + li],
+                                                  acc1, 0, 0, 0);
+    }
+    dS = acc0 + acc1;
+  }
+  float* const dst = (c < 0) ? p.d_state_in : p.carry + hs;
+  if (c < 0 && !p.d_state_in) return;
+  const int64_t off = (c < 0) ? hs : 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) dst[off + int64_t(16 * w + 4 * g + q) * DV + col] = dS[q];
+}
+
+// ---------------------------------------------------------------- post ------
+template <int DK, bool BF16, bool SG>
+__global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
+  constexpr int LD = DK + 4;
+  constexpr int NT4 = (4 * (DK / 16) + kNW - 1) / kNW;   // 64 x DK tiles per wave
+  __shared__ __attribute__((aligned(16))) float sm[3 * 64 * LD + 3 * 64 * kL64 + 3 * DK + 2 * 64 +
+                                                   4 * DK];
+  float* const R1 = sm;               // Kh
+  float* const R2 = R1 + 64 * LD;     // slabs (with R3), then -dW', then Qr, then dg
+  float* const R3 = R2 + 64 * LD;     // Qr (for P), slabs, then Kr
+  float* const sM = R3 + 64 * LD;     // M
+  float* const sP = sM + 64 * kL64;   // P, then dP, then dM M^T
+  float* const sX = sP + 64 * kL64;   // dT, then dM, then Diag(beta) dA
+  float* const sgm = sX + 64 * kL64;
+  float* const sgq = sgm + DK;
+  float* const sdgc = sgq + DK;
+  float* const sb = sdgc + DK;
+  float* const sdb = sb + 64;
+  float* const red = sdb + 64;        // [4][DK]
+  // slab buffers (inside R2 .. R3)
+  float* const sO = R2;
+  float* const sVn = sO + 64 * kLS;
+  float* const sV = sVn + 64 * kLS;
+  float* const sdVn = sV + 64 * kLS;
+  float* const sD = sdVn + 64 * kLS;  // dS' Diag(gamma_C / gamma_m) rows, [DK][16]
+  float* const sS = sD + DK * kLS;    // S Diag(gamma_m) rows
+
+  const int t = threadIdx.x, w = t >> 6, l = t & 63, li = l & 15, g = l >> 4;
+  const int H = p.H, DV = p.DV;
+  const int64_t bid = blockIdx.x;
+  const int h = int(bid % H);
+  const int64_t jw = (bid / H) % p.win_k, n = bid / H / p.win_k;
+  Chunk ck;
+  if (!locate(p, n, jw, h, ck)) return;
+  const int nv = ck.nv;
+  const float* const rho = p.rho + ck.wi * (64 * DK);
+
+  // 1. decay factors, beta, Kh, Qr, M
+  if (t < DK) {
+    float gm = 1.f, gq = 1.f;
+#pragma unroll 4
+    for (int r = 0; r <= kMid; ++r) {
+      const int64_t row = (ck.tok0 + r) * H + h;
+      gm *= r < nv ? (SG ? p.alpha[row] : p.alpha[row * DK + t]) : 1.f;
+    }
+    gq = rho[(kC - 1) * DK + t];
+    sgm[t] = gm;
+    sgq[t] = gq;
+  }
+  if (t < 64) sb[t] = t < nv ? p.beta[(ck.tok0 + t) * H + h] : 0.f;
+  for (int e = t; e < 64 * DK; e += kNT) {
+    const int r = e / DK, c = e % DK;
+    const float rh = rho[e];
+    const int64_t x = ((ck.tok0 + r) * H + h) * int64_t(DK) + c;
+    const float kv = r < nv ? ld_in<BF16>(p.k, x) : 0.f;
+    const float qv = r < nv ? ld_in<BF16>(p.q, x) : 0.f;
+    R1[r * LD + c] = kv / rh;
+    R3[r * LD + c] = qv * rh;
+  }
+  {
+    const float* const Mg = p.Mb + ck.wi * (64 * 64);
+    for (int e = t; e < 64 * 64; e += kNT) sM[(e >> 6) * kL64 + (e & 63)] = Mg[e];
+  }
+  __syncthreads();
+  {
+    f4 ap[2];
+    zero(ap);
+    mm<64, 64, DK, true, true, 1>(ap, R3, LD, R1, LD, w);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      int m0, n0;
+      tile_origin<64>(w, s, m0, n0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = m0 + 4 * g + q, c = n0 + li;
+        sP[r * kL64 + c] = c <= r ? ap[s][q] : 0.f;
+      }
+    }
+  }
+  __syncthreads();
+
+  // 2. over the value columns, 16 at a time
+  f4 aq[NT4], ah[NT4], awn[NT4], adp[2], adt[2];
+  zero(aq);
+  zero(ah);
+  zero(awn);
+  zero(adp);
+  zero(adt);
+  float dgcs = 0.f;
+  const float* const S = chunk_state<DK>(p, ck);
+  const float* const dSe = p.dSend + ck.wi * (int64_t(DK) * DV);
+  const float* const Vng = p.Vnb + ck.wi * (64 * int64_t(DV));
+  for (int js = 0; js < DV / 16; ++js) {
+    for (int e = t; e < 64 * 16; e += kNT) {
+      const int r = e >> 4, j = e & 15;
+      const int64_t x = ((ck.tok0 + r) * H + h) * int64_t(DV) + 16 * js + j;
+      sO[r * kLS + j] = r < nv ? p.d_o[x] : 0.f;
+      sV[r * kLS + j] = r < nv ? ld_in<BF16>(p.v, x) : 0.f;
+      sVn[r * kLS + j] = Vng[r * DV + 16 * js + j];
+    }
+    for (int e = t; e < DK * 16; e += kNT) {
+      const int r = e >> 4, j = e & 15;
+      const int64_t x = int64_t(r) * DV + 16 * js + j;
+      sD[r * kLS + j] = dSe[x] * sgq[r];
+      sS[r * kLS + j] = S ? S[x] * sgm[r] : 0.f;
+    }
+    __syncthreads();
+    {
+      f4 adv[1];
+      zero(adv);
+      mm<64, 16, 64, false, false, 3>(adv, sP, kL64, sO, kLS, w);
+      mm<64, 16, DK, true, false, 0>(adv, R1, LD, sD, kLS, w);
+      if (w < 4) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sdVn[(16 * w + 4 * g + q) * kLS + li] = adv[0][q];
+      }
+      if (t < DK) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) dgcs += sS[t * kLS + j] * sD[t * kLS + j];
+      }
+    }
+    __syncthreads();
+    mm<64, DK, 16, true, true, 0>(aq, sO, kLS, sS, kLS, w);
+    mm<64, DK, 16, true, true, 0>(awn, sdVn, kLS, sS, kLS, w);
+    mm<64, DK, 16, true, true, 0>(ah, sVn, kLS, sD, kLS, w);
+    mm<64, 64, 16, true, true, 0>(adp, sO, kLS, sVn, kLS, w);
+    mm<64, 64, 16, true, true, 0>(adt, sdVn, kLS, sV, kLS, w);
+    {
+      f4 adv2[1];
+      zero(adv2);
+      const int wv = (w + 4) & 7;
+      mm<64, 16, 64, false, false, 3>(adv2, sM, kL64, sdVn, kLS, wv);
+      if (wv < 4) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r = 16 * wv + 4 * g + q;
+          if (r < nv) p.dv[((ck.tok0 + r) * H + h) * int64_t(DV) + 16 * js + li] = sb[r] * adv2[0][q];
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // 3. gamma_C's gradient: the column sums of dKend' * Kh plus sum_j S dS'
+  // gamma_C, both in the scaled forms.  dP, dT, -dW' to LDS.
+#pragma unroll
+  for (int s = 0; s < NT4; ++s) {
+    if (!tile_live<64, DK>(w, s)) break;
+    int m0, n0;
+    tile_origin<DK>(w, s, m0, n0);
+    float v = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v += ah[s][q] * R1[(m0 + 4 * g + q) * LD + n0 + li];
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    if (g == 0) red[(m0 >> 4) * DK + n0 + li] = v;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) R2[(m0 + 4 * g + q) * LD + n0 + li] = -awn[s][q];
+  }
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    int m0, n0;
+    tile_origin<64>(w, s, m0, n0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = m0 + 4 * g + q, c = n0 + li;
+      sP[r * kL64 + c] = c <= r ? adp[s][q] : 0.f;
+      sX[r * kL64 + c] = adt[s][q];
+    }
+  }
+  __syncthreads();
+  if (t < DK) sdgc[t] = red[t] + red[DK + t] + red[2 * DK + t] + red[3 * DK + t] + dgcs;
+  for (int e = t; e < 64 * DK; e += kNT) {   // Kr
+    const int r = e / DK, c = e % DK;
+    const float kv = r < nv ? ld_in<BF16>(p.k, ((ck.tok0 + r) * H + h) * int64_t(DK) + c) : 0.f;
+    R3[r * LD + c] = kv * rho[e];
+  }
+  __syncthreads();
+
+  // 4. dT += dW' Kr^T;  AR = Diag(beta) M^T dW'
+  f4 ar[NT4];
+  zero(ar);
+  {
+    f4 at[2];
+    zero(at);
+    mm<64, 64, DK, true, true, 0>(at, R2, LD, R3, LD, w);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      int m0, n0;
+      tile_origin<64>(w, s, m0, n0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sX[(m0 + 4 * g + q) * kL64 + n0 + li] += at[s][q];
+    }
+  }
+  mm<64, DK, 64, false, false, 3>(ar, sM, kL64, R2, LD, w);
+#pragma unroll
+  for (int s = 0; s < NT4; ++s) {
+    if (!tile_live<64, DK>(w, s)) break;
+    int m0, n0;
+    tile_origin<DK>(w, s, m0, n0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) ar[s][q] *= sb[m0 + 4 * g + q];
+  }
+  __syncthreads();
+  for (int e = t; e < 64 * DK; e += kNT) {   // Qr
+    const int r = e / DK, c = e % DK;
+    const float qv = r < nv ? ld_in<BF16>(p.q, ((ck.tok0 + r) * H + h) * int64_t(DK) + c) : 0.f;
+    R2[r * LD + c] = qv * rho[e];
+  }
+  __syncthreads();
+
+  // 5. AH += dP^T Qr;  AQ += dP Kh;  dbeta from T
+  mm<64, DK, 64, false, false, 3>(ah, sP, kL64, R2, LD, w);
+  mm<64, DK, 64, true, false, 2>(aq, sP, kL64, R1, LD, w);
+  if (t < 64) {
+    float s = 0.f;
+    for (int r = t; r < 64; ++r) s += sM[r * kL64 + t] * sX[r * kL64 + t];
+    sdb[t] = s;
+  }
+  __syncthreads();
+  for (int e = t; e < 64 * 64; e += kNT) {   // dM = dT Diag(beta)
+    const int r = e >> 6, c = e & 63;
+    sX[r * kL64 + c] *= sb[c];
+  }
+  __syncthreads();
+  {
+    f4 atm[2];
+    zero(atm);
+    mm<64, 64, 64, true, true, 0>(atm, sX, kL64, sM, kL64, w);   // dM M^T
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      int m0, n0;
+      tile_origin<64>(w, s, m0, n0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sP[(m0 + 4 * g + q) * kL64 + n0 + li] = atm[s][q];
+    }
+  }
+  __syncthreads();
+  {
+    f4 ada[2], axx[2];
+    zero(ada);
+    zero(axx);
+    mm<64, 64, 64, false, false, 3>(ada, sM, kL64, sP, kL64, w);   // M^T (dM M^T)
+    mm<64, 64, DK, true, true, 1>(axx, R3, LD, R1, LD, w);          // Kr Kh^T
+    // dA = -M^T dM M^T (strictly lower); dbeta_r += sum_s dA_rs X_rs
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      int m0, n0;
+      tile_origin<64>(w, s, m0, n0);
+      float v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = m0 + 4 * g + q, c = n0 + li;
+        const float da = c < r ? -ada[s][q] : 0.f;
+        ada[s][q] = da;
+        v[q] = da * axx[s][q];
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float x = v[q];
+        x += __shfl_xor(x, 1);
+        x += __shfl_xor(x, 2);
+        x += __shfl_xor(x, 4);
+        x += __shfl_xor(x, 8);
+        if (li == 0) red[(n0 >> 4) * 64 + m0 + 4 * g + q] = x;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      int m0, n0;
+      tile_origin<64>(w, s, m0, n0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = m0 + 4 * g + q;
+        sX[r * kL64 + n0 + li] = sb[r] * ada[s][q];
+      }
+    }
+    if (t < 64) sdb[t] += red[t] + red[64 + t] + red[128 + t] + red[192 + t];
+  }
+  __syncthreads();
+
+  // 6. AR += B Kh;  AH += B^T Kr  (B = Diag(beta) dA)
+  mm<64, DK, 64, true, false, 2>(ar, sX, kL64, R1, LD, w);
+  mm<64, DK, 64, false, false, 3>(ah, sX, kL64, R3, LD, w);
+
+  // 7. dq, dk; dg = AQ Qr + AR Kr - AH Kh (+ gamma_C's gradient on the last row)
+  float dgv[NT4][4];
+#pragma unroll
+  for (int s = 0; s < NT4; ++s) {
+    if (!tile_live<64, DK>(w, s)) break;
+    int m0, n0;
+    tile_origin<DK>(w, s, m0, n0);
+    const int c = n0 + li;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = m0 + 4 * g + q;
+      const float rh = rho[r * DK + c];
+      const float kr = R3[r * LD + c], kh = R1[r * LD + c], qr = R2[r * LD + c];
+      float dg = aq[s][q] * qr + ar[s][q] * kr - ah[s][q] * kh;
+      if (r == kC - 1) dg += sdgc[c];
+      dgv[s][q] = dg;
+      if (r < nv) {
+        const int64_t x = ((ck.tok0 + r) * H + h) * int64_t(DK) + c;
+        p.dq[x] = aq[s][q] * rh;
+        p.dk[x] = ar[s][q] * rh + ah[s][q] / rh;
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < NT4; ++s) {
+    if (!tile_live<64, DK>(w, s)) break;
+    int m0, n0;
+    tile_origin<DK>(w, s, m0, n0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) R2[(m0 + 4 * g + q) * LD + n0 + li] = dgv[s][q];
+  }
+  if (t < 64 && t < nv) p.dbeta[(ck.tok0 + t) * H + h] = sdb[t];
+  __syncthreads();
+  // 8. dlog(alpha)_t = sum_{r >= t} dg_r within the chunk; dalpha = that / alpha
+  if (t < DK) {
+    float s = 0.f;
+    for (int r = kC - 1; r >= 0; --r) {
+      s += R2[r * LD + t];
+      R2[r * LD + t] = s;
+    }
+  }
+  __syncthreads();
+  if constexpr (SG) {
+    if (t < 64 && t < nv) {
+      float s = 0.f;
+      for (int c = 0; c < DK; ++c) s += R2[t * LD + c];
+      const int64_t row = (ck.tok0 + t) * H + h;
+      p.dalpha[row] = s / p.alpha[row];
+    }
+  } else {
+    for (int e = t; e < 64 * DK; e += kNT) {
+      const int r = e / DK, c = e % DK;
+      if (r < nv) {
+        const int64_t x = ((ck.tok0 + r) * H + h) * int64_t(DK) + c;
+        p.dalpha[x] = R2[r * LD + c] / p.alpha[x];
+      }
+    }
+  }
+}
+
+template <int DK, bool BF16, bool SG>
+void launch_t(const BwdChunkArgs& a, int stage, hipStream_t st) {
+  const unsigned nchunk = unsigned(int64_t(a.N) * a.win_k * a.H);
+  if (stage == 0) {
+    hipLaunchKernelGGL((kda_bwdc_prep_kernel<DK, BF16, SG>), dim3(nchunk), dim3(kNT), 0, st, a);
+  } else if (stage == 1) {
+    const unsigned nb = unsigned(int64_t(a.N) * a.H * (a.DV / 16));
+    hipLaunchKernelGGL((kda_bwdc_chain_kernel<DK>), dim3(nb), dim3(64 * (DK / 16)), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((kda_bwdc_post_kernel<DK, BF16, SG>), dim3(nchunk), dim3(kNT), 0, st, a);
+  }
+}
+
+template <int DK>
+void launch_dk(const BwdChunkArgs& a, int stage, hipStream_t st) {
+  if (a.alpha_scalar) {
+    if (a.in_bf16) launch_t<DK, true, true>(a, stage, st);
+    else launch_t<DK, false, true>(a, stage, st);
+  } else {
+    if (a.in_bf16) launch_t<DK, true, false>(a, stage, st);
+    else launch_t<DK, false, false>(a, stage, st);
+  }
+}
+
+}  // namespace
+
+size_t backward_chunk_floats(int DK, int DV) {
+  // A_c, b_c, dS', M, Vn, rho per chunk-head
+  return size_t(DK) * DK + 2 * size_t(DK) * DV + 64 * 64 + 64 * size_t(DV) + 64 * size_t(DK);
+}
+
+int launch_backward_chunk(const BwdChunkArgs& a, int stage, void* stream, const char** msg) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (a.DK == 128) launch_dk<128>(a, stage, st);
+  else if (a.DK == 64) launch_dk<64>(a, stage, st);
+  else {
+    *msg = "unsupported DK";
+    return 1;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    *msg = hipGetErrorString(e);
+    return 1;
+  }
+  return 0;
+}
+
+}  // namespace kda

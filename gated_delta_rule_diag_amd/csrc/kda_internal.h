@@ -100,11 +100,50 @@ struct BackwardArgs {
   float* part_db;              // [DV / 16][rows]
 };
 
+// The backward in chunk form: three launches per window of chunks (stage 0 =
+// per-chunk matrices, 1 = the adjoint's pass over the chunks, 2 = per-chunk
+// gradients).  Window buffers hold, per chunk-head of the window (index
+// (n * win_k + j) * H + h, j = reverse index within the window):
+//   Ac [DK][DK] (columns permuted for the chain), bc [DK][DV], dSend [DK][DV],
+//   Mb [64][64], Vnb [64][DV], rho [64][DK].
+struct BwdChunkArgs {
+  int N, H, DK, DV;
+  int64_t T;                   // tokens per sequence (fixed length)
+  const int32_t* cu_seqlens;   // packed sequences: device [N + 1], or nullptr
+  bool in_bf16;
+  bool alpha_scalar;
+  int64_t win_lo, win_k;
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* alpha;
+  const float* beta;
+  const float* state_in;
+  const float* d_o;
+  const float* d_state_out;
+  const float* snapshots;      // as in BackwardArgs
+  float* dq;
+  float* dk;
+  float* dv;
+  float* dalpha;
+  float* dbeta;
+  float* d_state_in;
+  float* carry;                // [N, H, DK, DV] between windows, or nullptr
+  float* Ac;
+  float* bc;
+  float* dSend;
+  float* Mb;
+  float* Vnb;
+  float* rho;
+};
+
 // Launchers return 0 on success, else a non-zero code and a static message.
 int launch_prefill(const PrefillArgs& a, void* stream, const char** msg);
 int launch_decode(const DecodeArgs& a, void* stream, const char** msg);
 int launch_decode_pool(const PoolDecodeArgs& a, void* stream, const char** msg);
 int launch_backward(const BackwardArgs& a, void* stream, const char** msg);
+int launch_backward_chunk(const BwdChunkArgs& a, int stage, void* stream, const char** msg);
+size_t backward_chunk_floats(int DK, int DV);   // window-buffer floats per chunk-head
 size_t backward_scratch_bytes(int N, int H, int DK, int DV);
 size_t prefill_workspace_bytes(int N, int64_t T_total, int H, int DK, int DV, bool varlen);
 
