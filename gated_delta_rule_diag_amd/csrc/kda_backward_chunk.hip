@@ -38,6 +38,15 @@ constexpr int kNT = 64 * kNW;
 constexpr int kLS = 20;     // pitch (floats) of a 16-column slab
 constexpr int kL64 = 68;    // pitch of a 64-column array
 
+// Workgroup barrier that orders LDS only: global loads (prefetches) and stores
+// stay in flight across it.  No kernel here reads global memory that another
+// thread of the same launch writes.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 template <bool BF16>
 __device__ __forceinline__ float ld_in(const void* p, int64_t i) {
   if constexpr (BF16) {
@@ -49,46 +58,58 @@ __device__ __forceinline__ float ld_in(const void* p, int64_t i) {
 }
 
 // acc[s] += A(tile rows, 0:K) B(0:K, tile cols) for the tiles t = wv + 8 s of
-// the (M/16) x (N/16) tile grid (row-major), wv being the caller's wave slot.
+// the (M/16) x (N/16) tile grid (row-major), wv being the caller's wave slot
+// (wave-uniform; a slot past the grid does nothing).  All tiles of a wave
+// share one column block, so each B fragment is loaded once for them.
 //   A(m, k) = AK ? a[m * lda + k] : a[k * lda + m]
 //   B(k, n) = BK ? b[n * ldb + k] : b[k * ldb + n]
 // Within each 16-wide block of K, lane group g takes k = 4g .. 4g + 3 over the
-// four products (lane i = row of A / column of B).  TRI skips work known to be
-// zero: 1 = tiles above the diagonal of the output; 2 = A lower triangular
-// (k <= m); 3 = A upper triangular (k >= m).  The result lane holds rows
-// 4g + q of column i of its tile.
-template <int M, int N, int K, bool AK, bool BK, int TRI, int NT>
+// four products (lane i = row of A / column of B); the result lane holds rows
+// 4g + q of column i of its tile.  The fragments of KG blocks of K are loaded
+// before their products.  Triangular operands are stored with their zeros, so
+// the products run over the whole of K (exact zeros do not change a sum).
+template <int M, int N, int K, bool AK, bool BK, int NT>
 __device__ __forceinline__ void mm(f4 (&acc)[NT], const float* a, int lda, const float* b, int ldb,
                                    int wv) {
-  constexpr int TN = N / 16, NTILE = (M / 16) * TN;
+  constexpr int TN = N / 16, NTILE = (M / 16) * TN, KB = K / 16;
+  static_assert(kNW % TN == 0, "a wave's tiles share one column block");
+  static_assert(NTILE % kNW == 0 ? NT == NTILE / kNW : (NT == 1 && NTILE < kNW), "tiles per wave");
+  constexpr int KG0 = NT >= 8 ? 1 : (NT >= 4 ? 2 : 4);
+  constexpr int KG = KB < KG0 ? KB : KG0;
+  static_assert(KB % KG == 0, "K blocks in whole groups");
+  if (NTILE < kNW && wv >= NTILE) return;
   const int l = threadIdx.x & 63, i = l & 15, g = l >> 4;
+  const int n0 = (wv % TN) * 16;
 #pragma unroll
-  for (int s = 0; s < NT; ++s) {
-    const int t = wv + kNW * s;
-    if (t >= NTILE) break;
-    const int m0 = (t / TN) * 16, n0 = (t % TN) * 16;
-    if (TRI == 1 && n0 > m0) continue;
-    const int klo = TRI == 3 ? m0 : 0;
-    const int khi = TRI == 2 ? m0 + 16 : K;
+  for (int kg = 0; kg < KB; kg += KG) {
+    f4 bv[KG], av[KG][NT];
 #pragma unroll
-    for (int k0 = 0; k0 < K; k0 += 16) {
-      if (k0 < klo || k0 >= khi) continue;
-      f4 av, bv;
-      if constexpr (AK) {
-        av = *reinterpret_cast<const f4*>(a + (m0 + i) * lda + k0 + 4 * g);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) av[j] = a[(k0 + 4 * g + j) * lda + m0 + i];
-      }
+    for (int u = 0; u < KG; ++u) {
+      const int k0 = 16 * (kg + u);
       if constexpr (BK) {
-        bv = *reinterpret_cast<const f4*>(b + (n0 + i) * ldb + k0 + 4 * g);
+        bv[u] = *reinterpret_cast<const f4*>(b + (n0 + i) * ldb + k0 + 4 * g);
       } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) bv[j] = b[(k0 + 4 * g + j) * ldb + n0 + i];
+        for (int j = 0; j < 4; ++j) bv[u][j] = b[(k0 + 4 * g + j) * ldb + n0 + i];
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[s] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j], bv[j], acc[s], 0, 0, 0);
+      for (int s = 0; s < NT; ++s) {
+        const int m0 = ((wv + kNW * s) / TN) * 16;
+        if constexpr (AK) {
+          av[u][s] = *reinterpret_cast<const f4*>(a + (m0 + i) * lda + k0 + 4 * g);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) av[u][s][j] = a[(k0 + 4 * g + j) * lda + m0 + i];
+        }
+      }
     }
+#pragma unroll
+    for (int u = 0; u < KG; ++u)
+#pragma unroll
+      for (int s = 0; s < NT; ++s)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[s] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u][s][j], bv[u][j], acc[s], 0, 0, 0);
   }
 }
 
@@ -108,6 +129,21 @@ __device__ __forceinline__ void tile_origin(int wv, int s, int& m0, int& n0) {
 template <int M, int N>
 __device__ __forceinline__ bool tile_live(int wv, int s) {
   return wv + kNW * s < (M / 16) * (N / 16);
+}
+
+// Layouts of the chain's operands, in its fragment order so that each wave
+// instruction moves one contiguous block.  A_c: wave w (rows 16w..16w+15)
+// takes DK/16 float4 per lane, lane (i, g) holding A_c[16w + i][4j + g] for
+// j = 0 .. DK/4 - 1.  b_c and dS': per 16-column slab and wave, one float4
+// per lane holding rows 16w + 4g .. 16w + 4g + 3 of column i.
+template <int DK>
+__device__ __forceinline__ int frag_a(int r, int c) {
+  const int j = c >> 2;
+  return (((r >> 4) * (DK / 16) + (j >> 2)) * 64 + (r & 15) + 16 * (c & 3)) * 4 + (j & 3);
+}
+template <int DK>
+__device__ __forceinline__ int64_t frag_s(int js, int w, int l) {
+  return ((int64_t(js) * (DK / 16) + w) * 64 + l) * 4;
 }
 
 // The chunk a workgroup works on: sequence n, chunk c counted from the start
@@ -136,7 +172,7 @@ __device__ __forceinline__ bool locate(const BwdChunkArgs& p, int64_t n, int64_t
   ck.tok0 = s0 + ck.c * kC;
   const int64_t rem = len - ck.c * kC;
   ck.nv = int(rem < kC ? rem : kC);
-  ck.wi = (n * p.win_k + jw) * p.H + h;
+  ck.wi = (n * p.H + h) * p.win_k + jw;
   return true;
 }
 
@@ -186,6 +222,7 @@ __device__ __forceinline__ void decays(const BwdChunkArgs& p, const Chunk& ck, f
   }
   sgm[c] = gm;
   sgq[c] = x;
+  rho_g[kC * DK + c] = gm;   // gamma_m after the 64 rows
 }
 
 // ---------------------------------------------------------------- prep ------
@@ -208,7 +245,8 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_prep_kernel(BwdChunkArgs p) {
   float* const sO = sV + 64 * kLS;   // dO slab
   float* const sS = sO + 64 * kLS;   // S slab [DK][16]
 
-  const int t = threadIdx.x, w = t >> 6, l = t & 63, li = l & 15, g = l >> 4;
+  const int t = threadIdx.x, w = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63, li = l & 15,
+            g = l >> 4;
   const int H = p.H, DV = p.DV;
   const int64_t bid = blockIdx.x;
   const int h = int(bid % H);
@@ -218,11 +256,13 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_prep_kernel(BwdChunkArgs p) {
   const int nv = ck.nv;
 
   // 1. decays, scaled keys and queries, beta
-  float* const rho_g = p.rho + ck.wi * (64 * DK);
+  float* const rho_g = p.rho + ck.wi * (65 * DK);
   decays<DK, SG>(p, ck, sQr, LD, rho_g, sgm, sgq);   // rho parked in sQr
   if (t < 64) sb[t] = t < nv ? p.beta[(ck.tok0 + t) * H + h] : 0.f;
-  __syncthreads();
-  for (int e = t; e < 64 * DK; e += kNT) {
+  lds_barrier();
+#pragma unroll
+  for (int u = 0; u < 64 * DK / kNT; ++u) {
+    const int e = t + u * kNT;
     const int r = e / DK, c = e % DK;
     const float rh = sQr[r * LD + c];
     const int64_t x = ((ck.tok0 + r) * H + h) * int64_t(DK) + c;
@@ -232,15 +272,15 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_prep_kernel(BwdChunkArgs p) {
     sKh[r * LD + c] = kv / rh;
     sQr[r * LD + c] = qv * rh;
   }
-  __syncthreads();
+  lds_barrier();
 
   // 2. Diag(beta) X and P
   {
     f4 ax[2], ap[2];
     zero(ax);
     zero(ap);
-    mm<64, 64, DK, true, true, 1>(ax, sKr, LD, sKh, LD, w);
-    mm<64, 64, DK, true, true, 1>(ap, sQr, LD, sKh, LD, w);
+    mm<64, 64, DK, true, true>(ax, sKr, LD, sKh, LD, w);
+    mm<64, 64, DK, true, true>(ap, sQr, LD, sKh, LD, w);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       int m0, n0;
@@ -253,7 +293,7 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_prep_kernel(BwdChunkArgs p) {
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // 3. M = (I + Diag(beta) X)^-1 in place: the four diagonal 16x16 blocks by
   // forward substitution (wave 0, lane = column of a block), then block rows
@@ -271,7 +311,7 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_prep_kernel(BwdChunkArgs p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) sM[(o + r) * kL64 + o + li] = x[r];
   }
-  __syncthreads();
+  lds_barrier();
   for (int bi = 1; bi < 4; ++bi) {
     f4 acc = f4{0.f, 0.f, 0.f, 0.f};
     const int bj = w;
@@ -286,7 +326,7 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_prep_kernel(BwdChunkArgs p) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) sV[(16 * bj + 4 * g + q) * kLS + li] = acc[q];
     }
-    __syncthreads();
+    lds_barrier();
     f4 acc2 = f4{0.f, 0.f, 0.f, 0.f};
     if (bj < bi) {
       const f4 av = *reinterpret_cast<const f4*>(sM + (16 * bi + li) * kL64 + 16 * bi + 4 * g);
@@ -295,30 +335,32 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_prep_kernel(BwdChunkArgs p) {
         acc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j], sV[(16 * bj + 4 * g + j) * kLS + li], acc2, 0, 0,
                                                     0);
     }
-    __syncthreads();
+    lds_barrier();
     if (bj < bi) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) sM[(16 * bi + 4 * g + q) * kL64 + 16 * bj + li] = -acc2[q];
     }
-    __syncthreads();
+    lds_barrier();
   }
 
   // 4. M out; T = M Diag(beta) in place
   float* const Mg = p.Mb + ck.wi * (64 * 64);
-  for (int e = t; e < 64 * 64; e += kNT) {
+#pragma unroll
+  for (int u = 0; u < 64 * 64 / kNT; ++u) {
+    const int e = t + u * kNT;
     const int r = e >> 6, c = e & 63;
     const float m = sM[r * kL64 + c];
     Mg[e] = m;
     sM[r * kL64 + c] = m * sb[c];
   }
-  __syncthreads();
+  lds_barrier();
 
   // 5. W = T Kr Diag(gamma_m), over Kr
   {
     f4 aw[NTW];
     zero(aw);
-    mm<64, DK, 64, true, false, 2>(aw, sM, kL64, sKr, LD, w);
-    __syncthreads();
+    mm<64, DK, 64, true, false>(aw, sM, kL64, sKr, LD, w);
+    lds_barrier();
 #pragma unroll
     for (int s = 0; s < NTW; ++s) {
       if (!tile_live<64, DK>(w, s)) break;
@@ -328,16 +370,15 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_prep_kernel(BwdChunkArgs p) {
       for (int q = 0; q < 4; ++q) sKr[(m0 + 4 * g + q) * LD + n0 + li] = aw[s][q] * sgm[n0 + li];
     }
   }
-  __syncthreads();
+  lds_barrier();
   float* const sW = sKr;
 
-  // 6. A_c = Diag(gamma_C) - W^T Kh Diag(gamma_C / gamma_m), stored for the
-  // chain with the columns of each row permuted (lane group g of the chain
-  // reads the columns 4j + g, j = 0 .. DK/4 - 1, contiguously).
+  // 6. A_c = Diag(gamma_C) - W^T Kh Diag(gamma_C / gamma_m), stored in the
+  // chain's fragment order.
   {
     f4 aa[NTA];
     zero(aa);
-    mm<DK, DK, 64, false, false, 0>(aa, sW, LD, sKh, LD, w);
+    mm<DK, DK, 64, false, false>(aa, sW, LD, sKh, LD, w);
     float* const Ag = p.Ac + ck.wi * (int64_t(DK) * DK);
 #pragma unroll
     for (int s = 0; s < NTA; ++s) {
@@ -350,7 +391,7 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_prep_kernel(BwdChunkArgs p) {
         const int r = m0 + 4 * g + q;
         float v = -sgq[c] * aa[s][q];
         if (r == c) v += sgm[r] * sgq[r];
-        Ag[r * DK + (c & 3) * (DK / 4) + (c >> 2)] = v;
+        Ag[frag_a<DK>(r, c)] = v;
       }
     }
   }
@@ -359,48 +400,73 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_prep_kernel(BwdChunkArgs p) {
   const float* const S = chunk_state<DK>(p, ck);
   float* const Vng = p.Vnb + ck.wi * (64 * int64_t(DV));
   float* const bg = p.bc + ck.wi * (int64_t(DK) * DV);
-  for (int js = 0; js < DV / 16; ++js) {
-    for (int e = t; e < 64 * 16; e += kNT) {
+  // (the next slab's inputs are fetched into registers during this slab's
+  // products; past the last slab the last one is fetched again)
+  constexpr int NR = 64 * 16 / kNT, NS = DK * 16 / kNT;
+  struct Slab {
+    float v[NR], o[NR], s[NS];
+  };
+  auto fetch = [&](Slab& R, int js) {
+    if (js >= DV / 16) js = DV / 16 - 1;
+#pragma unroll
+    for (int u = 0; u < NR; ++u) {
+      const int e = t + u * kNT;
       const int r = e >> 4, j = e & 15;
       const int64_t x = ((ck.tok0 + r) * H + h) * int64_t(DV) + 16 * js + j;
-      sV[r * kLS + j] = r < nv ? ld_in<BF16>(p.v, x) : 0.f;
-      sO[r * kLS + j] = r < nv ? p.d_o[x] : 0.f;
+      R.v[u] = r < nv ? ld_in<BF16>(p.v, x) : 0.f;
+      R.o[u] = r < nv ? p.d_o[x] : 0.f;
     }
-    for (int e = t; e < DK * 16; e += kNT) {
-      const int r = e >> 4, j = e & 15;
-      sS[r * kLS + j] = S ? S[int64_t(r) * DV + 16 * js + j] : 0.f;
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      const int e = t + u * kNT;
+      R.s[u] = S ? S[int64_t(e >> 4) * DV + 16 * js + (e & 15)] : 0.f;
     }
-    __syncthreads();
+  };
+  Slab R;
+  fetch(R, 0);
+  for (int js = 0; js < DV / 16; ++js) {
+#pragma unroll
+    for (int u = 0; u < NR; ++u) {
+      const int e = t + u * kNT;
+      sV[(e >> 4) * kLS + (e & 15)] = R.v[u];
+      sO[(e >> 4) * kLS + (e & 15)] = R.o[u];
+    }
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      const int e = t + u * kNT;
+      sS[(e >> 4) * kLS + (e & 15)] = R.s[u];
+    }
+    fetch(R, js + 1);
+    lds_barrier();
     f4 au[1], an[1], az[1];
     zero(au);
     zero(an);
     zero(az);
-    mm<64, 16, 64, true, false, 2>(au, sM, kL64, sV, kLS, w);
-    mm<64, 16, DK, true, false, 0>(an, sW, LD, sS, kLS, w);
-    mm<64, 16, 64, false, false, 3>(az, sP, kL64, sO, kLS, (w + 4) & 7);
+    mm<64, 16, 64, true, false>(au, sM, kL64, sV, kLS, w);
+    mm<64, 16, DK, true, false>(an, sW, LD, sS, kLS, w);
+    mm<64, 16, 64, false, false>(az, sP, kL64, sO, kLS, (w + 4) & 7);
     if (w < 4) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) Vng[(16 * w + 4 * g + q) * DV + 16 * js + li] = au[0][q] - an[0][q];
     }
-    __syncthreads();
+    lds_barrier();
     if (w >= 4) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) sV[(16 * (w - 4) + 4 * g + q) * kLS + li] = az[0][q];
     }
-    __syncthreads();
+    lds_barrier();
     f4 b1[1], b2[1];
     zero(b1);
     zero(b2);
-    mm<DK, 16, 64, false, false, 0>(b1, sQr, LD, sO, kLS, w);
-    mm<DK, 16, 64, false, false, 0>(b2, sW, LD, sV, kLS, w);
+    mm<DK, 16, 64, false, false>(b1, sQr, LD, sO, kLS, w);
+    mm<DK, 16, 64, false, false>(b2, sW, LD, sV, kLS, w);
     if (tile_live<DK, 16>(w, 0)) {
+      f4 v;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int r = 16 * w + 4 * g + q;
-        bg[r * DV + 16 * js + li] = sgm[r] * b1[0][q] - b2[0][q];
-      }
+      for (int q = 0; q < 4; ++q) v[q] = sgm[16 * w + 4 * g + q] * b1[0][q] - b2[0][q];
+      *reinterpret_cast<f4*>(bg + frag_s<DK>(js, w, l)) = v;
     }
-    __syncthreads();
+    lds_barrier();
   }
 }
 
@@ -412,22 +478,19 @@ template <int DK>
 __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_bwdc_chain_kernel(BwdChunkArgs p) {
   constexpr int KQ = DK / 4;
   __shared__ __attribute__((aligned(16))) float sD[2][DK * 16];
-  const int t = threadIdx.x, w = t >> 6, l = t & 63, li = l & 15, g = l >> 4;
+  const int t = threadIdx.x, w = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63, li = l & 15,
+            g = l >> 4;
   const int H = p.H, DV = p.DV, nsl = DV / 16;
-  const int64_t bid = blockIdx.x;
+  // Workgroups go to the 8 XCDs round-robin; remap so that the slabs of one
+  // (sequence, head), which read the same A_c, run on one XCD and share its L2.
+  int64_t bid = blockIdx.x;
+  const int64_t G = gridDim.x;
+  if ((G & 7) == 0) bid = (bid & 7) * (G >> 3) + (bid >> 3);
   const int slab = int(bid % nsl);
   const int64_t pr = bid / nsl;
   const int h = int(pr % H);
   const int64_t n = pr / H;
-  int64_t s0, len;
-  if (p.cu_seqlens) {
-    s0 = p.cu_seqlens[n];
-    len = p.cu_seqlens[n + 1] - s0;
-  } else {
-    s0 = n * p.T;
-    len = p.T;
-  }
-  (void)s0;
+  const int64_t len = p.cu_seqlens ? p.cu_seqlens[n + 1] - p.cu_seqlens[n] : p.T;
   const int64_t nch = (len + kC - 1) / kC;
   const int64_t c_hi = nch - 1 - p.win_lo;
   const int64_t hs = (n * H + h) * int64_t(DK) * DV;
@@ -448,39 +511,58 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_bwdc_chain_kernel(BwdCh
     }
     return;
   }
-  int64_t c = c_hi;
-  for (int64_t jw = 0; jw < p.win_k && c >= 0; ++jw, --c) {
-    const int64_t wi = (n * p.win_k + jw) * H + h;
-    float* const sd = sD[jw & 1];
-    float* const de = p.dSend + wi * (int64_t(DK) * DV);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int r = 16 * w + 4 * g + q;
-      sd[r * 16 + li] = dS[q];
-      de[r * DV + col] = dS[q];
-    }
-    const float* const ar = p.Ac + wi * (int64_t(DK) * DK) + (16 * w + li) * DK + g * KQ;
+  const int64_t steps = c_hi + 1 < p.win_k ? c_hi + 1 : p.win_k;
+  // Operands of a step: this lane's A_c fragments and b_c values.  Three sets
+  // in rotation: the loads for the next two chunks are in flight during this
+  // chunk's products (past the last step the last chunk is loaded again, so
+  // the loads stay unconditional).
+  struct Ops {
     f4 a[KQ / 4];
+    f4 b;
+  };
+  auto load = [&](Ops& o, int64_t jw) {
+    if (jw >= steps) jw = steps - 1;
+    const int64_t wi = (n * H + h) * p.win_k + jw;
+    const float* const ar = p.Ac + wi * (int64_t(DK) * DK) + (w * (KQ / 4) * 64 + l) * 4;
 #pragma unroll
-    for (int j = 0; j < KQ / 4; ++j) a[j] = *reinterpret_cast<const f4*>(ar + 4 * j);
-    f4 acc0, acc1 = f4{0.f, 0.f, 0.f, 0.f};
-    const float* const br = p.bc + wi * (int64_t(DK) * DV);
+    for (int j = 0; j < KQ / 4; ++j) o.a[j] = *reinterpret_cast<const f4*>(ar + j * 256);
+    o.b = *reinterpret_cast<const f4*>(p.bc + wi * (int64_t(DK) * DV) + frag_s<DK>(slab, w, l));
+  };
+  auto step = [&](const Ops& o, int64_t jw) {
+    const int64_t wi = (n * H + h) * p.win_k + jw;
+    float* const sd = sD[jw & 1];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) acc0[q] = br[(16 * w + 4 * g + q) * DV + col];
-    __syncthreads();
+    for (int q = 0; q < 4; ++q) sd[(16 * w + 4 * g + q) * 16 + li] = dS[q];
+    *reinterpret_cast<f4*>(p.dSend + wi * (int64_t(DK) * DV) + frag_s<DK>(slab, w, l)) = dS;
+    lds_barrier();
+    f4 acc0 = o.b, acc1 = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < KQ; j += 2) {
-      acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j >> 2][j & 3], sd[(4 * j + g) * 16 + li], acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[(j + 1) >> 2][(j + 1) & 3], sd[(4 * (j + 1) + g) * 16 + li],
-                                                  acc1, 0, 0, 0);
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(o.a[j >> 2][j & 3], sd[(4 * j + g) * 16 + li], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(o.a[(j + 1) >> 2][(j + 1) & 3],
+                                                  sd[(4 * (j + 1) + g) * 16 + li], acc1, 0, 0, 0);
     }
     dS = acc0 + acc1;
+  };
+  Ops A, B, C;
+  load(A, 0);
+  load(B, 1);
+  int64_t jw = 0;
+  for (; jw + 2 < steps; jw += 3) {
+    load(C, jw + 2);
+    step(A, jw);
+    load(A, jw + 3);
+    step(B, jw + 1);
+    load(B, jw + 4);
+    step(C, jw + 2);
   }
-  float* const dst = (c < 0) ? p.d_state_in : p.carry + hs;
+  if (jw < steps) step(A, jw);
+  if (jw + 1 < steps) step(B, jw + 1);
+  const int64_t c = c_hi - steps;   // last chunk done: c + 1
   if (c < 0 && !p.d_state_in) return;
-  const int64_t off = (c < 0) ? hs : 0;
+  float* const dst = c < 0 ? p.d_state_in + hs : p.carry + hs;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) dst[off + int64_t(16 * w + 4 * g + q) * DV + col] = dS[q];
+  for (int q = 0; q < 4; ++q) dst[int64_t(16 * w + 4 * g + q) * DV + col] = dS[q];
 }
 
 // ---------------------------------------------------------------- post ------
@@ -510,7 +592,8 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
   float* const sD = sdVn + 64 * kLS;  // dS' Diag(gamma_C / gamma_m) rows, [DK][16]
   float* const sS = sD + DK * kLS;    // S Diag(gamma_m) rows
 
-  const int t = threadIdx.x, w = t >> 6, l = t & 63, li = l & 15, g = l >> 4;
+  const int t = threadIdx.x, w = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63, li = l & 15,
+            g = l >> 4;
   const int H = p.H, DV = p.DV;
   const int64_t bid = blockIdx.x;
   const int h = int(bid % H);
@@ -518,22 +601,17 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
   Chunk ck;
   if (!locate(p, n, jw, h, ck)) return;
   const int nv = ck.nv;
-  const float* const rho = p.rho + ck.wi * (64 * DK);
+  const float* const rho = p.rho + ck.wi * (65 * DK);
 
   // 1. decay factors, beta, Kh, Qr, M
   if (t < DK) {
-    float gm = 1.f, gq = 1.f;
-#pragma unroll 4
-    for (int r = 0; r <= kMid; ++r) {
-      const int64_t row = (ck.tok0 + r) * H + h;
-      gm *= r < nv ? (SG ? p.alpha[row] : p.alpha[row * DK + t]) : 1.f;
-    }
-    gq = rho[(kC - 1) * DK + t];
-    sgm[t] = gm;
-    sgq[t] = gq;
+    sgm[t] = rho[kC * DK + t];
+    sgq[t] = rho[(kC - 1) * DK + t];
   }
   if (t < 64) sb[t] = t < nv ? p.beta[(ck.tok0 + t) * H + h] : 0.f;
-  for (int e = t; e < 64 * DK; e += kNT) {
+#pragma unroll 8
+  for (int u = 0; u < 64 * DK / kNT; ++u) {
+    const int e = t + u * kNT;
     const int r = e / DK, c = e % DK;
     const float rh = rho[e];
     const int64_t x = ((ck.tok0 + r) * H + h) * int64_t(DK) + c;
@@ -544,13 +622,17 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
   }
   {
     const float* const Mg = p.Mb + ck.wi * (64 * 64);
-    for (int e = t; e < 64 * 64; e += kNT) sM[(e >> 6) * kL64 + (e & 63)] = Mg[e];
+#pragma unroll
+    for (int u = 0; u < 64 * 64 / kNT; ++u) {
+      const int e = t + u * kNT;
+      sM[(e >> 6) * kL64 + (e & 63)] = Mg[e];
+    }
   }
-  __syncthreads();
+  lds_barrier();
   {
     f4 ap[2];
     zero(ap);
-    mm<64, 64, DK, true, true, 1>(ap, R3, LD, R1, LD, w);
+    mm<64, 64, DK, true, true>(ap, R3, LD, R1, LD, w);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       int m0, n0;
@@ -562,7 +644,7 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // 2. over the value columns, 16 at a time
   f4 aq[NT4], ah[NT4], awn[NT4], adp[2], adt[2];
@@ -575,26 +657,62 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
   const float* const S = chunk_state<DK>(p, ck);
   const float* const dSe = p.dSend + ck.wi * (int64_t(DK) * DV);
   const float* const Vng = p.Vnb + ck.wi * (64 * int64_t(DV));
-  for (int js = 0; js < DV / 16; ++js) {
-    for (int e = t; e < 64 * 16; e += kNT) {
+  // The next slab's operands are fetched into registers during this slab's
+  // products (past the last slab the last one is fetched again).
+  constexpr int NR = 64 * 16 / kNT, NS = DK * 16 / kNT;
+  struct Slab {
+    float o[NR], v[NR], vn[NR], s[NS];
+    f4 d;   // dS' of rows 16 (t / 64) + 4 g .. + 3, column t % 16 (t < 4 DK)
+  };
+  auto fetch = [&](Slab& R, int js) {
+    if (js >= DV / 16) js = DV / 16 - 1;
+#pragma unroll
+    for (int u = 0; u < NR; ++u) {
+      const int e = t + u * kNT;
       const int r = e >> 4, j = e & 15;
       const int64_t x = ((ck.tok0 + r) * H + h) * int64_t(DV) + 16 * js + j;
-      sO[r * kLS + j] = r < nv ? p.d_o[x] : 0.f;
-      sV[r * kLS + j] = r < nv ? ld_in<BF16>(p.v, x) : 0.f;
-      sVn[r * kLS + j] = Vng[r * DV + 16 * js + j];
+      R.o[u] = r < nv ? p.d_o[x] : 0.f;
+      R.v[u] = r < nv ? ld_in<BF16>(p.v, x) : 0.f;
+      R.vn[u] = Vng[r * DV + 16 * js + j];
     }
-    for (int e = t; e < DK * 16; e += kNT) {
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      const int e = t + u * kNT;
+      R.s[u] = S ? S[int64_t(e >> 4) * DV + 16 * js + (e & 15)] : 0.f;
+    }
+    if (t < DK * 4) R.d = *reinterpret_cast<const f4*>(dSe + frag_s<DK>(js, t >> 6, t & 63));
+  };
+  Slab R;
+  fetch(R, 0);
+  for (int js = 0; js < DV / 16; ++js) {
+#pragma unroll
+    for (int u = 0; u < NR; ++u) {
+      const int e = t + u * kNT;
       const int r = e >> 4, j = e & 15;
-      const int64_t x = int64_t(r) * DV + 16 * js + j;
-      sD[r * kLS + j] = dSe[x] * sgq[r];
-      sS[r * kLS + j] = S ? S[x] * sgm[r] : 0.f;
+      sO[r * kLS + j] = R.o[u];
+      sV[r * kLS + j] = R.v[u];
+      sVn[r * kLS + j] = R.vn[u];
     }
-    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      const int e = t + u * kNT;
+      const int r = e >> 4, j = e & 15;
+      sS[r * kLS + j] = R.s[u] * sgm[r];
+    }
+    if (t < DK * 4) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = 16 * (t >> 6) + 4 * (g) + q;
+        sD[r * kLS + li] = R.d[q] * sgq[r];
+      }
+    }
+    fetch(R, js + 1);
+    lds_barrier();
     {
       f4 adv[1];
       zero(adv);
-      mm<64, 16, 64, false, false, 3>(adv, sP, kL64, sO, kLS, w);
-      mm<64, 16, DK, true, false, 0>(adv, R1, LD, sD, kLS, w);
+      mm<64, 16, 64, false, false>(adv, sP, kL64, sO, kLS, w);
+      mm<64, 16, DK, true, false>(adv, R1, LD, sD, kLS, w);
       if (w < 4) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) sdVn[(16 * w + 4 * g + q) * kLS + li] = adv[0][q];
@@ -604,17 +722,17 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
         for (int j = 0; j < 16; ++j) dgcs += sS[t * kLS + j] * sD[t * kLS + j];
       }
     }
-    __syncthreads();
-    mm<64, DK, 16, true, true, 0>(aq, sO, kLS, sS, kLS, w);
-    mm<64, DK, 16, true, true, 0>(awn, sdVn, kLS, sS, kLS, w);
-    mm<64, DK, 16, true, true, 0>(ah, sVn, kLS, sD, kLS, w);
-    mm<64, 64, 16, true, true, 0>(adp, sO, kLS, sVn, kLS, w);
-    mm<64, 64, 16, true, true, 0>(adt, sdVn, kLS, sV, kLS, w);
+    lds_barrier();
+    mm<64, DK, 16, true, true>(aq, sO, kLS, sS, kLS, w);
+    mm<64, DK, 16, true, true>(awn, sdVn, kLS, sS, kLS, w);
+    mm<64, DK, 16, true, true>(ah, sVn, kLS, sD, kLS, w);
+    mm<64, 64, 16, true, true>(adp, sO, kLS, sVn, kLS, w);
+    mm<64, 64, 16, true, true>(adt, sdVn, kLS, sV, kLS, w);
     {
       f4 adv2[1];
       zero(adv2);
       const int wv = (w + 4) & 7;
-      mm<64, 16, 64, false, false, 3>(adv2, sM, kL64, sdVn, kLS, wv);
+      mm<64, 16, 64, false, false>(adv2, sM, kL64, sdVn, kLS, wv);
       if (wv < 4) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -623,7 +741,7 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
 
   // 3. gamma_C's gradient: the column sums of dKend' * Kh plus sum_j S dS'
@@ -653,14 +771,16 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
       sX[r * kL64 + c] = adt[s][q];
     }
   }
-  __syncthreads();
+  lds_barrier();
   if (t < DK) sdgc[t] = red[t] + red[DK + t] + red[2 * DK + t] + red[3 * DK + t] + dgcs;
-  for (int e = t; e < 64 * DK; e += kNT) {   // Kr
+#pragma unroll 4
+  for (int u = 0; u < 64 * DK / kNT; ++u) {   // Kr
+    const int e = t + u * kNT;
     const int r = e / DK, c = e % DK;
     const float kv = r < nv ? ld_in<BF16>(p.k, ((ck.tok0 + r) * H + h) * int64_t(DK) + c) : 0.f;
     R3[r * LD + c] = kv * rho[e];
   }
-  __syncthreads();
+  lds_barrier();
 
   // 4. dT += dW' Kr^T;  AR = Diag(beta) M^T dW'
   f4 ar[NT4];
@@ -668,7 +788,7 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
   {
     f4 at[2];
     zero(at);
-    mm<64, 64, DK, true, true, 0>(at, R2, LD, R3, LD, w);
+    mm<64, 64, DK, true, true>(at, R2, LD, R3, LD, w);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       int m0, n0;
@@ -677,7 +797,7 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
       for (int q = 0; q < 4; ++q) sX[(m0 + 4 * g + q) * kL64 + n0 + li] += at[s][q];
     }
   }
-  mm<64, DK, 64, false, false, 3>(ar, sM, kL64, R2, LD, w);
+  mm<64, DK, 64, false, false>(ar, sM, kL64, R2, LD, w);
 #pragma unroll
   for (int s = 0; s < NT4; ++s) {
     if (!tile_live<64, DK>(w, s)) break;
@@ -686,32 +806,36 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) ar[s][q] *= sb[m0 + 4 * g + q];
   }
-  __syncthreads();
-  for (int e = t; e < 64 * DK; e += kNT) {   // Qr
+  lds_barrier();
+#pragma unroll 4
+  for (int u = 0; u < 64 * DK / kNT; ++u) {   // Qr
+    const int e = t + u * kNT;
     const int r = e / DK, c = e % DK;
     const float qv = r < nv ? ld_in<BF16>(p.q, ((ck.tok0 + r) * H + h) * int64_t(DK) + c) : 0.f;
     R2[r * LD + c] = qv * rho[e];
   }
-  __syncthreads();
+  lds_barrier();
 
   // 5. AH += dP^T Qr;  AQ += dP Kh;  dbeta from T
-  mm<64, DK, 64, false, false, 3>(ah, sP, kL64, R2, LD, w);
-  mm<64, DK, 64, true, false, 2>(aq, sP, kL64, R1, LD, w);
+  mm<64, DK, 64, false, false>(ah, sP, kL64, R2, LD, w);
+  mm<64, DK, 64, true, false>(aq, sP, kL64, R1, LD, w);
   if (t < 64) {
     float s = 0.f;
     for (int r = t; r < 64; ++r) s += sM[r * kL64 + t] * sX[r * kL64 + t];
     sdb[t] = s;
   }
-  __syncthreads();
-  for (int e = t; e < 64 * 64; e += kNT) {   // dM = dT Diag(beta)
+  lds_barrier();
+#pragma unroll
+  for (int u = 0; u < 64 * 64 / kNT; ++u) {   // dM = dT Diag(beta)
+    const int e = t + u * kNT;
     const int r = e >> 6, c = e & 63;
     sX[r * kL64 + c] *= sb[c];
   }
-  __syncthreads();
+  lds_barrier();
   {
     f4 atm[2];
     zero(atm);
-    mm<64, 64, 64, true, true, 0>(atm, sX, kL64, sM, kL64, w);   // dM M^T
+    mm<64, 64, 64, true, true>(atm, sX, kL64, sM, kL64, w);   // dM M^T
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       int m0, n0;
@@ -720,13 +844,13 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
       for (int q = 0; q < 4; ++q) sP[(m0 + 4 * g + q) * kL64 + n0 + li] = atm[s][q];
     }
   }
-  __syncthreads();
+  lds_barrier();
   {
     f4 ada[2], axx[2];
     zero(ada);
     zero(axx);
-    mm<64, 64, 64, false, false, 3>(ada, sM, kL64, sP, kL64, w);   // M^T (dM M^T)
-    mm<64, 64, DK, true, true, 1>(axx, R3, LD, R1, LD, w);          // Kr Kh^T
+    mm<64, 64, 64, false, false>(ada, sM, kL64, sP, kL64, w);   // M^T (dM M^T)
+    mm<64, 64, DK, true, true>(axx, R3, LD, R1, LD, w);          // Kr Kh^T
     // dA = -M^T dM M^T (strictly lower); dbeta_r += sum_s dA_rs X_rs
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -750,7 +874,7 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
         if (li == 0) red[(n0 >> 4) * 64 + m0 + 4 * g + q] = x;
       }
     }
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       int m0, n0;
@@ -763,11 +887,11 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
     }
     if (t < 64) sdb[t] += red[t] + red[64 + t] + red[128 + t] + red[192 + t];
   }
-  __syncthreads();
+  lds_barrier();
 
   // 6. AR += B Kh;  AH += B^T Kr  (B = Diag(beta) dA)
-  mm<64, DK, 64, true, false, 2>(ar, sX, kL64, R1, LD, w);
-  mm<64, DK, 64, false, false, 3>(ah, sX, kL64, R3, LD, w);
+  mm<64, DK, 64, true, false>(ar, sX, kL64, R1, LD, w);
+  mm<64, DK, 64, false, false>(ah, sX, kL64, R3, LD, w);
 
   // 7. dq, dk; dg = AQ Qr + AR Kr - AH Kh (+ gamma_C's gradient on the last row)
   float dgv[NT4][4];
@@ -792,7 +916,7 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
 #pragma unroll
   for (int s = 0; s < NT4; ++s) {
     if (!tile_live<64, DK>(w, s)) break;
@@ -802,7 +926,7 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
     for (int q = 0; q < 4; ++q) R2[(m0 + 4 * g + q) * LD + n0 + li] = dgv[s][q];
   }
   if (t < 64 && t < nv) p.dbeta[(ck.tok0 + t) * H + h] = sdb[t];
-  __syncthreads();
+  lds_barrier();
   // 8. dlog(alpha)_t = sum_{r >= t} dg_r within the chunk; dalpha = that / alpha
   if (t < DK) {
     float s = 0.f;
@@ -811,7 +935,7 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
       R2[r * LD + t] = s;
     }
   }
-  __syncthreads();
+  lds_barrier();
   if constexpr (SG) {
     if (t < 64 && t < nv) {
       float s = 0.f;
@@ -820,7 +944,9 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
       p.dalpha[row] = s / p.alpha[row];
     }
   } else {
-    for (int e = t; e < 64 * DK; e += kNT) {
+#pragma unroll
+    for (int u = 0; u < 64 * DK / kNT; ++u) {
+      const int e = t + u * kNT;
       const int r = e / DK, c = e % DK;
       if (r < nv) {
         const int64_t x = ((ck.tok0 + r) * H + h) * int64_t(DK) + c;
@@ -857,8 +983,8 @@ void launch_dk(const BwdChunkArgs& a, int stage, hipStream_t st) {
 }  // namespace
 
 size_t backward_chunk_floats(int DK, int DV) {
-  // A_c, b_c, dS', M, Vn, rho per chunk-head
-  return size_t(DK) * DK + 2 * size_t(DK) * DV + 64 * 64 + 64 * size_t(DV) + 64 * size_t(DK);
+  // A_c, b_c, dS', M, Vn, rho (+ gamma_m) per chunk-head
+  return size_t(DK) * DK + 2 * size_t(DK) * DV + 64 * 64 + 64 * size_t(DV) + 65 * size_t(DK);
 }
 
 int launch_backward_chunk(const BwdChunkArgs& a, int stage, void* stream, const char** msg) {

@@ -103,9 +103,9 @@ struct BackwardArgs {
 // The backward in chunk form: three launches per window of chunks (stage 0 =
 // per-chunk matrices, 1 = the adjoint's pass over the chunks, 2 = per-chunk
 // gradients).  Window buffers hold, per chunk-head of the window (index
-// (n * win_k + j) * H + h, j = reverse index within the window):
+// (n * H + h) * win_k + j, j = reverse index within the window):
 //   Ac [DK][DK] (columns permuted for the chain), bc [DK][DV], dSend [DK][DV],
-//   Mb [64][64], Vnb [64][DV], rho [64][DK].
+//   Mb [64][64], Vnb [64][DV], rho [65][DK] (row 64: gamma_m).
 struct BwdChunkArgs {
   int N, H, DK, DV;
   int64_t T;                   // tokens per sequence (fixed length)
