@@ -448,37 +448,30 @@ kda_status_t kda_decode_pool(int N, int L, int H, int DK, int DV, kda_dtype_t in
 namespace {
 
 // Byte offsets of the backward workspace: [forward prefill workspace, later the
-// per-slab partial sums | o of the forward | snapshots | token-state scratch].
+// window buffers | o of the forward | snapshots | adjoint carried between
+// windows].
 struct BwdLayout {
-  size_t fwd_or_part, o, snaps, scratch, carry, total;
+  size_t fwd_or_win, o, snaps, carry, total;
   int64_t win_k, nwin;   // chunks per window of the reverse pass, windows
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Workspace of a backward call: the forward's workspace (fixed length only)
-// or the per-slab partial sums of one window of chunks, whichever is larger
-// (they are not live at the same time), the forward's o, one state per full
-// chunk, the reverse pass's token-state scratch, and the adjoint carried
-// between windows.  The reverse pass goes through the chunks in windows of
-// win_k chunks counted from each sequence's end, so that the partial sums
-// (8 (3 DK + 1) floats per token-head at DV = 128) take at most 4 GiB
-// whatever the length; KDA_BWD_WINDOW=k forces k chunks per window.
-// Packed sequences: T_fixed = 0, max_chunks from the longest sequence, and
-// the snapshot rows are T_total / 64 (chunk j of the sequence starting at
-// token s is row s / 64 + j).
-bool bwd_token_walk() {
-  const char* e = getenv("KDA_BWD_TOKEN");
-  return e && e[0] == '1';
-}
-
+// Workspace of a backward call: the forward's workspace (fixed length only) or
+// the buffers of one window of chunks, whichever is larger (they are not live
+// at the same time), the forward's o, one state per full chunk, and the
+// adjoint carried between windows.  The reverse pass goes through the chunks
+// in windows of win_k chunks counted from each sequence's end, so that the
+// window buffers (backward_chunk_floats per chunk-head) take at most 4 GiB
+// whatever the length; KDA_BWD_WINDOW=k forces k chunks per window.  Packed
+// sequences: T_fixed = 0, max_chunks from the longest sequence, and the
+// snapshot rows are T_total / 64 (chunk j of the sequence starting at token s
+// is row s / 64 + j).
 BwdLayout bwd_layout(int N, int T_fixed, int64_t T_total, int64_t max_chunks, int H, int DK,
                      int DV, bool varlen) {
   BwdLayout L{};
-  const size_t rows = size_t(T_total) * H, nslab = size_t(DV) / 16;
-  const size_t per_chunk = bwd_token_walk()
-                               ? size_t(N) * 64 * H * (3 * size_t(DK) + 1) * nslab * 4
-                               : size_t(N) * H * kda::backward_chunk_floats(DK, DV) * 4;
+  const size_t rows = size_t(T_total) * H;
+  const size_t per_chunk = size_t(N) * H * kda::backward_chunk_floats(DK, DV) * 4;
   int64_t k = int64_t((size_t(4) << 30) / per_chunk);
   if (const char* e = getenv("KDA_BWD_WINDOW")) {
     const long v = atol(e);
@@ -490,13 +483,12 @@ BwdLayout bwd_layout(int N, int T_fixed, int64_t T_total, int64_t max_chunks, in
   L.win_k = k;
   L.nwin = (max_chunks + k - 1) / k;
   const size_t pw = varlen ? 0 : kda::prefill_workspace_bytes(N, T_total, H, DK, DV, false);
-  const size_t part = size_t(k) * per_chunk;
+  const size_t win = size_t(k) * per_chunk;
   const size_t snap_rows = varlen ? size_t(T_total / 64) : size_t(N) * size_t(T_fixed / 64);
-  L.fwd_or_part = 0;
-  L.o = align256(pw > part ? pw : part);
+  L.fwd_or_win = 0;
+  L.o = align256(pw > win ? pw : win);
   L.snaps = L.o + align256(rows * DV * 4);
-  L.scratch = L.snaps + align256(snap_rows * H * DK * DV * 4);
-  L.carry = L.scratch + (bwd_token_walk() ? align256(kda::backward_scratch_bytes(N, H, DK, DV)) : 0);
+  L.carry = L.snaps + align256(snap_rows * H * DK * DV * 4);
   L.total = L.carry + (L.nwin > 1 ? align256(size_t(N) * H * DK * DV * 4) : 0);
   return L;
 }
@@ -590,7 +582,7 @@ kda_status_t run_backward(int N, int T_fixed, const int32_t* cu_seqlens, int64_t
   f.H = H; f.DK = DK; f.DV = DV; f.in_bf16 = in_dtype == KDA_BF16;
   f.q = q; f.k = k; f.v = v; f.alpha = alpha; f.beta = beta; f.alpha_scalar = alpha_scalar;
   f.state_in = state_in; f.o = reinterpret_cast<float*>(ws + L.o); f.state_out = nullptr;
-  f.workspace = ws + L.fwd_or_part; f.workspace_bytes = L.o;
+  f.workspace = ws + L.fwd_or_win; f.workspace_bytes = L.o;
   const int64_t snap_rows = varlen ? T_total / 64 : int64_t(N) * (T_fixed / 64);
   f.snapshots = snap_rows > 0 ? reinterpret_cast<float*>(ws + L.snaps) : nullptr;
   f.snap_every = 1;
@@ -599,58 +591,29 @@ kda_status_t run_backward(int N, int T_fixed, const int32_t* cu_seqlens, int64_t
   const char* msg = nullptr;
   if (kda::launch_prefill(f, stream, &msg) != 0)
     return fail(KDA_ERR_HIP, "backward: forward launch failed: %s", msg ? msg : "?");
-  if (!bwd_token_walk()) {
-    // 2. per window of chunks: per-chunk matrices, the adjoint's pass, gradients
-    kda::BwdChunkArgs c{};
-    c.N = N; c.H = H; c.DK = DK; c.DV = DV; c.T = varlen ? 0 : T_fixed; c.cu_seqlens = cu_seqlens;
-    c.in_bf16 = in_dtype == KDA_BF16;
-    c.alpha_scalar = alpha_scalar;
-    c.q = q; c.k = k; c.v = v; c.alpha = alpha; c.beta = beta; c.state_in = state_in;
-    c.d_o = d_o; c.d_state_out = d_state_out;
-    c.snapshots = reinterpret_cast<const float*>(ws + L.snaps);
-    c.dq = dq; c.dk = dk; c.dv = dv; c.dalpha = dalpha; c.dbeta = dbeta; c.d_state_in = d_state_in;
-    c.carry = L.nwin > 1 ? reinterpret_cast<float*>(ws + L.carry) : nullptr;
-    c.win_k = L.win_k;
-    const size_t per = size_t(N) * size_t(L.win_k) * H;   // chunk-heads of a window
-    c.Ac = reinterpret_cast<float*>(ws + L.fwd_or_part);
-    c.bc = c.Ac + per * DK * DK;
-    c.dSend = c.bc + per * DK * DV;
-    c.Mb = c.dSend + per * DK * DV;
-    c.Vnb = c.Mb + per * 64 * 64;
-    c.rho = c.Vnb + per * 64 * DV;
-    for (int64_t w = 0; w < L.nwin; ++w) {
-      c.win_lo = w * L.win_k;
-      for (int stage = 0; stage < 3; ++stage)
-        if (kda::launch_backward_chunk(c, stage, stream, &msg) != 0)
-          return fail(KDA_ERR_HIP, "backward launch failed: %s", msg ? msg : "?");
-    }
-    return ok();
-  }
-  // 2-3. reverse pass and the reduction of the per-slab sums
-  kda::BackwardArgs a{};
-  a.N = N; a.H = H; a.DK = DK; a.DV = DV; a.T = varlen ? 0 : T_fixed; a.cu_seqlens = cu_seqlens;
-  a.rows = int64_t(rows);
-  a.in_bf16 = in_dtype == KDA_BF16;
-  a.alpha_scalar = alpha_scalar;
-  a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.state_in = state_in;
-  a.d_o = d_o; a.d_state_out = d_state_out;
-  a.snapshots = reinterpret_cast<const float*>(ws + L.snaps); a.snap_per_seq = varlen ? 0 : T_fixed / 64;
-  a.dq = dq; a.dk = dk; a.dv = dv; a.dalpha = dalpha; a.dbeta = dbeta; a.d_state_in = d_state_in;
-  a.scratch = reinterpret_cast<float*>(ws + L.scratch);
-  const size_t nslab = size_t(DV) / 16;
-  const size_t prows = size_t(N) * size_t(L.win_k) * 64 * H;
-  float* part = reinterpret_cast<float*>(ws + L.fwd_or_part);
-  a.part_dq = part;
-  a.part_dk = part + nslab * prows * DK;
-  a.part_da = part + 2 * nslab * prows * DK;
-  a.part_db = part + 3 * nslab * prows * DK;
-  a.part_rows = int64_t(prows);
-  a.win_k = L.win_k;
-  a.g_carry = L.nwin > 1 ? reinterpret_cast<float*>(ws + L.carry) : nullptr;
+  // 2. per window of chunks: per-chunk matrices, the adjoint's pass, gradients
+  kda::BwdChunkArgs c{};
+  c.N = N; c.H = H; c.DK = DK; c.DV = DV; c.T = varlen ? 0 : T_fixed; c.cu_seqlens = cu_seqlens;
+  c.in_bf16 = in_dtype == KDA_BF16;
+  c.alpha_scalar = alpha_scalar;
+  c.q = q; c.k = k; c.v = v; c.alpha = alpha; c.beta = beta; c.state_in = state_in;
+  c.d_o = d_o; c.d_state_out = d_state_out;
+  c.snapshots = reinterpret_cast<const float*>(ws + L.snaps);
+  c.dq = dq; c.dk = dk; c.dv = dv; c.dalpha = dalpha; c.dbeta = dbeta; c.d_state_in = d_state_in;
+  c.carry = L.nwin > 1 ? reinterpret_cast<float*>(ws + L.carry) : nullptr;
+  c.win_k = L.win_k;
+  const size_t per = size_t(N) * size_t(L.win_k) * H;   // chunk-heads of a window
+  c.Ac = reinterpret_cast<float*>(ws + L.fwd_or_win);
+  c.bc = c.Ac + per * DK * DK;
+  c.dSend = c.bc + per * DK * DV;
+  c.Mb = c.dSend + per * DK * DV;
+  c.Vnb = c.Mb + per * 64 * 64;
+  c.rho = c.Vnb + per * 64 * DV;
   for (int64_t w = 0; w < L.nwin; ++w) {
-    a.win_lo = w * L.win_k;
-    if (kda::launch_backward(a, stream, &msg) != 0)
-      return fail(KDA_ERR_HIP, "backward launch failed: %s", msg ? msg : "?");
+    c.win_lo = w * L.win_k;
+    for (int stage = 0; stage < 3; ++stage)
+      if (kda::launch_backward_chunk(c, stage, stream, &msg) != 0)
+        return fail(KDA_ERR_HIP, "backward launch failed: %s", msg ? msg : "?");
   }
   return ok();
 }

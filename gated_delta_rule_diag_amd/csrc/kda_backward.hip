@@ -1,615 +1,1001 @@
-// KDA backward pass on gfx950: gradients of the operator's outputs with
-// respect to q, k, v, alpha, beta and the initial state.
+// KDA backward in chunk form (training).
 //
-// The chunk algorithm regroups the token recurrence of "Kimi Delta Attention
-// 徹底解説" (tech-tide.dev), section "Kimi Delta Attention の仕組み"; its gradient
-// is the gradient of that recurrence.  Reverse mode of one token
-//     St = Diag(a) S;  p = St^T k;  u = b (v - p);  S' = St + k u^T;  o = S'^T q
-// with G the adjoint of S' (including o's term q do^T) gives
-//     dq = S' do;  du = G^T k;  dv = b du;  db = du . (v - p);  dp = -b du
-//     dSt = G + k dp^T;  dk = G u + St dp;  da = rowsum(dSt * S);  G <- Diag(a) dSt
-//
-// Plan of a call:
-//   1. the forward prefill with a state snapshot after every chunk (the
-//      states at chunk starts are the checkpoints);
-//   2. kda_bwd_kernel: one workgroup per (sequence, head, 16 value columns).
-//      Every step above keeps value columns apart except the row sums (dq,
-//      dk, da) and db, so the slab of G and of the state needs no exchange;
-//      the row sums go to per-slab partial buffers.  Chunks are visited from
-//      the last to the first.  While chunk c is walked backwards, chunk c-1's
-//      token states are recomputed forward from its checkpoint into the other
-//      half of a per-workgroup scratch: the two token chains are independent,
-//      so their latencies overlap;
-//   3. kda_bwd_reduce_kernel: sums the per-slab partials (a fixed order, so
-//      the result is deterministic).
-//
-// Layout: wave w of a workgroup owns value columns 4w .. 4w+3 of the
-// workgroup's 16 and every key row (lane l holds rows DK/64 * l ..), so the
-// column sums of a step (St^T k and G^T k) are reductions inside one wave
-// (DPP within rows of 16 lanes, then row broadcasts into the last row, whose
-// lane 63 is read out): no barrier for them.  The row sums (dq, dk, da, over
-// the wave's 4 columns) and db are
-// outputs only: each wave stages them in LDS and after one barrier per token
-// the workgroup adds the four waves' values in a fixed order and writes the
-// slab's partials.
-
+// The pages give the chunkwise algorithm as the training form of the
+// recurrence ("Kimi Linear、独自の土俵でFull Attentionを上回る" (remio.ai),
+// section "Kimi Linearがより賢いRecurrent Memoryを使う方法") but print neither
+// it nor its gradient.  This is the reverse mode of the chunk form the prefill
+// uses, taken through its matrices.  Per chunk of 64 tokens, with
+// rho_r = gamma_r / gamma_m the decay of row r relative to row m = 31
+// (products of alpha, no logarithms):
+//   Kr = k rho,  Kh = k / rho,  Qr = q rho                 (per row and channel)
+//   X = strict_lower(Kr Kh^T),  M = (I + Diag(beta) X)^-1,  T = M Diag(beta)
+//   W = T Kr Diag(gamma_m),  U = T V,  Vn = U - W S
+//   P = lower(Qr Kh^T),  O = Qr Diag(gamma_m) S + P Vn
+//   S' = Diag(gamma_C) S + (Kh Diag(gamma_C / gamma_m))^T Vn
+// S is the state entering the chunk (the forward's snapshot).  The adjoint of
+// the state entering a chunk is affine in the adjoint of the state leaving it,
+// dS = b_c + A_c dS' with A_c = Diag(gamma_C) - W^T Kend and
+// b_c = (Qa - P W)^T dO (Kend = Kh Diag(gamma_C / gamma_m),
+// Qa = Qr Diag(gamma_m)), so the reverse pass is three launches per window of
+// chunks:
+//   prep   one workgroup per chunk-head: A_c, b_c, M, Vn and rho;
+//   chain  one workgroup per (sequence, head, 16 value columns): the adjoints
+//          dS' at every chunk end, sequentially from the last chunk;
+//   post   one workgroup per chunk-head: dq, dk, dv, dalpha, dbeta from S, dS',
+//          M and Vn (the solve's adjoint dA = -M^T dM M^T, the decays'
+//          gradient as a reverse cumulative sum within the chunk).
+// All products are fp32 MFMA (16x16x4) on LDS operands.
 #include <hip/hip_runtime.h>
-#include <stdint.h>
 
 #include "kda_internal.h"
 
 namespace kda {
 namespace {
 
-constexpr int kC = 64;     // chunk length (checkpoint interval)
-constexpr int kVS = 16;    // value columns per workgroup
-constexpr int kCPW = 4;    // value columns per wave
-constexpr int kNW = kVS / kCPW;   // waves per workgroup
-constexpr int kNT = 64 * kNW;     // threads per workgroup
+typedef float f4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ void lds_sync() {
+constexpr int kC = 64;      // chunk
+constexpr int kMid = 31;    // reference row of the relative decays
+constexpr int kNW = 8;      // waves per workgroup (prep, post)
+constexpr int kNT = 64 * kNW;
+constexpr int kLS = 20;     // pitch (floats) of a 16-column slab
+constexpr int kL64 = 68;    // pitch of a 64-column array
+
+// Workgroup barrier that orders LDS only: global loads (prefetches) and stores
+// stay in flight across it.  No kernel here reads global memory that another
+// thread of the same launch writes.
+__device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-template <int N>
-__device__ __forceinline__ void ld_f(const float* p, float (&x)[N]) {
-  if constexpr (N == 2) {
-    const float2 a = *reinterpret_cast<const float2*>(p);
-    x[0] = a.x;
-    x[1] = a.y;
-  } else {
-    x[0] = p[0];
-  }
-}
-
-// N = 2 or 4 consecutive floats (8- or 16-byte aligned).
-template <int N>
-__device__ __forceinline__ void ldfn(const float* p, float* x) {
-  if constexpr (N == 4) {
-    const float4 a = *reinterpret_cast<const float4*>(p);
-    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-  } else {
-    static_assert(N == 2, "two or four floats");
-    const float2 a = *reinterpret_cast<const float2*>(p);
-    x[0] = a.x; x[1] = a.y;
-  }
-}
-
-template <int N>
-__device__ __forceinline__ void stfn(float* p, const float* x) {
-  if constexpr (N == 4) {
-    *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
-  } else {
-    static_assert(N == 2, "two or four floats");
-    *reinterpret_cast<float2*>(p) = make_float2(x[0], x[1]);
-  }
-}
-
-// E floats in pieces of at most four.
-template <int E>
-__device__ __forceinline__ void ld_elems(const float* p, float* x) {
-#pragma unroll
-  for (int e = 0; e < E; e += (E >= 4 ? 4 : E)) ldfn<(E >= 4 ? 4 : E)>(p + e, x + e);
-}
-
-template <int E>
-__device__ __forceinline__ void st_elems(float* p, const float* x) {
-#pragma unroll
-  for (int e = 0; e < E; e += (E >= 4 ? 4 : E)) stfn<(E >= 4 ? 4 : E)>(p + e, x + e);
-}
-
-// Key rows (RPL of them) or four value columns of a bf16 or float input, kept
-// as loaded and converted at use (so that a prefetched value is not waited
-// for where it is loaded).
-template <bool BF16, int RPL>
-struct RowsIn;
-template <int RPL>
-struct RowsIn<true, RPL> {
-  uint32_t w;
-  __device__ void load(const void* p, int64_t i) {
-    const uint16_t* b = static_cast<const uint16_t*>(p) + i;
-    if constexpr (RPL == 2) w = *reinterpret_cast<const uint32_t*>(b);
-    else w = *b;
-  }
-  __device__ float operator[](int r) const {
-    return r == 0 ? __uint_as_float(w << 16) : __uint_as_float(w & 0xffff0000u);
-  }
-};
-template <int RPL>
-struct RowsIn<false, RPL> {
-  float x[RPL];
-  __device__ void load(const void* p, int64_t i) { ld_f<RPL>(static_cast<const float*>(p) + i, x); }
-  __device__ float operator[](int r) const { return x[r]; }
-};
 template <bool BF16>
-struct ColsIn;
-template <>
-struct ColsIn<true> {
-  uint32_t w[kCPW / 2];
-  __device__ void load(const void* p, int64_t i) {
-    const uint16_t* b = static_cast<const uint16_t*>(p) + i;
-    if constexpr (kCPW == 4) {
-      const uint2 r = *reinterpret_cast<const uint2*>(b);
-      w[0] = r.x;
-      w[kCPW / 2 - 1] = r.y;
-    } else {
-      w[0] = *reinterpret_cast<const uint32_t*>(b);
-    }
-  }
-  __device__ float operator[](int e) const {
-    const uint32_t x = w[e >> 1];
-    return (e & 1) ? __uint_as_float(x & 0xffff0000u) : __uint_as_float(x << 16);
-  }
-};
-template <>
-struct ColsIn<false> {
-  float x[kCPW];
-  __device__ void load(const void* p, int64_t i) { ldfn<kCPW>(static_cast<const float*>(p) + i, x); }
-  __device__ float operator[](int e) const { return x[e]; }
-};
-
-// Sum of the kNW per-wave values r[0], r[stride], ..., pairwise.
-__device__ __forceinline__ float sum_waves(const float* r, int stride) {
-  float x[kNW];
-#pragma unroll
-  for (int i = 0; i < kNW; ++i) x[i] = r[i * stride];
-#pragma unroll
-  for (int h = 1; h < kNW; h <<= 1)
-#pragma unroll
-    for (int i = 0; i + h < kNW; i += 2 * h) x[i] += x[i + h];
-  return x[0];
-}
-
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
-                                                                0xF, 0xF, false));
-}
-
-__device__ __forceinline__ float lane_val(float x, int lane) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
-}
-
-template <int CTRL, int ROWS>
-__device__ __forceinline__ float dpp_rows(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
-                                                                ROWS, 0xF, false));
-}
-
-// Sums over the 64 lanes of a wave of N values each (every lane gets the
-// totals): lane pairs and quads, then rotations by 4 and 8 inside each row
-// of 16 lanes (every lane holds its row's sum), then lane 15 of rows 0 and 2
-// added into rows 1 and 3 and lane 31 into rows 2 and 3, so that lane 63
-// holds (r2 + r3) + (r0 + r1); it is read out for all lanes.
-template <int N>
-__device__ __forceinline__ void wave_sums(float (&x)[N]) {
-#pragma unroll
-  for (int i = 0; i < N; ++i) x[i] += dpp<0xB1>(x[i]);    // quad_perm [1,0,3,2]
-#pragma unroll
-  for (int i = 0; i < N; ++i) x[i] += dpp<0x4E>(x[i]);    // quad_perm [2,3,0,1]
-#pragma unroll
-  for (int i = 0; i < N; ++i) x[i] += dpp<0x124>(x[i]);   // row_ror:4
-#pragma unroll
-  for (int i = 0; i < N; ++i) x[i] += dpp<0x128>(x[i]);   // row_ror:8
-#pragma unroll
-  for (int i = 0; i < N; ++i) x[i] += dpp_rows<0x142, 0xA>(x[i]);   // row_bcast:15 into rows 1, 3
-#pragma unroll
-  for (int i = 0; i < N; ++i) x[i] += dpp_rows<0x143, 0xC>(x[i]);   // row_bcast:31 into rows 2, 3
-#pragma unroll
-  for (int i = 0; i < N; ++i) x[i] = lane_val(x[i], 63);
-}
-
-// SG: one gate per token and head (alpha [rows]), the same for every key row.
-template <int DK, bool BF16, bool SG>
-__global__ __launch_bounds__(kNT) void kda_bwd_kernel(BackwardArgs p) {
-  constexpr int RPL = DK / 64;       // key rows per lane
-  constexpr int E = RPL * kCPW;      // state elements per lane
-  __shared__ float sU[2][kC][kVS];   // u of a chunk's tokens (this slab), two chunks
-  __shared__ float sR[2][kC][kVS];   // v - p
-  __shared__ float ring[2][3][kNW][DK];   // dq, dk, da per wave, two tokens
-  __shared__ float ringb[2][kNW];         // db per wave
-
-  const int t = threadIdx.x;
-  const int l = t & 63;
-  const int w = t >> 6;
-  const int i0 = RPL * l;                // first key row of this lane
-  const int jc = kCPW * w;               // first of this wave's columns in the slab
-  const int H = p.H, DV = p.DV;
-  const int nslab = DV / kVS;
-
-  // Workgroups of one (sequence, head) run on one XCD (they read the same
-  // q, k, alpha rows).
-  int64_t b = blockIdx.x;
-  const int64_t G_ = gridDim.x;
-  if ((G_ & 7) == 0) b = (b & 7) * (G_ >> 3) + (b >> 3);
-  const int slab = int(b % nslab);
-  const int64_t pr = b / nslab;
-  const int h = int(pr % H);
-  const int64_t n = pr / H;
-  const int col = slab * kVS + jc;       // first value column of this wave
-  // this sequence's tokens: fixed length, or packed by cu_seqlens
-  const int64_t tok0 = p.cu_seqlens ? int64_t(p.cu_seqlens[n]) : n * p.T;
-  const int64_t T = p.cu_seqlens ? int64_t(p.cu_seqlens[n + 1]) - tok0 : p.T;
-  const int64_t nchunks = T > 0 ? (T + kC - 1) / kC : 0;
-  const int64_t state_off = pr * DK * DV + int64_t(i0) * DV + col;
-  // token states: [2 chunk buffers][64 tokens][kNT threads][E floats]
-  float* scratch = p.scratch + b * (2 * int64_t(kC) * kNT * E) + int64_t(t) * E;
-  auto slot = [&](int64_t c, int s) { return scratch + ((c & 1) * kC + s) * int64_t(kNT) * E; };
-  auto row_of = [&](int64_t c, int s) { return (tok0 + c * kC + s) * H + h; };
-
-  auto ld_state = [&](const float* src, float (&S)[E]) {
-#pragma unroll
-    for (int r = 0; r < RPL; ++r) ldfn<kCPW>(src + int64_t(r) * DV, S + r * kCPW);
-  };
-  // state at the start of chunk c (snapshot c-1 is the state after chunk c-1)
-  auto checkpoint = [&](int64_t c, float (&S)[E]) {
-    if (c > 0) {
-      // snapshot of chunk c-1: row n * snap_per_seq + c - 1, or tok0 / 64 + c - 1 when packed
-      const int64_t srow = (p.cu_seqlens ? tok0 / kC : n * p.snap_per_seq) + (c - 1);
-      ld_state(p.snapshots + (srow * H + h) * int64_t(DK) * DV + int64_t(i0) * DV + col, S);
-    } else if (p.state_in) {
-      ld_state(p.state_in + state_off, S);
-    } else {
-#pragma unroll
-      for (int e = 0; e < E; ++e) S[e] = 0.f;
-    }
-  };
-
-  // This launch's window: the chunks c_lo .. c_hi, counted from the
-  // sequence's end (reverse indices win_lo .. win_lo + win_k - 1).  The
-  // adjoint G comes from d_state_out in the first window and from the
-  // previous window's carry otherwise.
-  const int64_t c_hi = nchunks - 1 - p.win_lo;
-  const int64_t c_lo = c_hi - p.win_k + 1 > 0 ? c_hi - p.win_k + 1 : 0;
-  float G[E], S[E];
-  if (p.win_lo > 0) {
-    ld_state(p.g_carry + state_off, G);
-  } else if (p.d_state_out) {
-    ld_state(p.d_state_out + state_off, G);
+__device__ __forceinline__ float ld_in(const void* p, int64_t i) {
+  if constexpr (BF16) {
+    const uint16_t b = static_cast<const uint16_t*>(p)[i];
+    return __uint_as_float(uint32_t(b) << 16);
   } else {
-#pragma unroll
-    for (int e = 0; e < E; ++e) G[e] = 0.f;
+    return static_cast<const float*>(p)[i];
   }
-  if (c_hi < 0) {
-    // nothing of this sequence in the window; an empty sequence passes the
-    // final state's gradient through (once, in the first window)
-    if (nchunks == 0 && p.win_lo == 0 && p.d_state_in) {
-#pragma unroll
-      for (int r = 0; r < RPL; ++r)
-        stfn<kCPW>(p.d_state_in + state_off + int64_t(r) * DV, G + r * kCPW);
-    }
-    return;
-  }
-  // row of the window's partial sums for token sb of chunk c
-  auto prow_of = [&](int64_t c, int sb) {
-    return ((n * p.win_k + (nchunks - 1 - c - p.win_lo)) * kC + sb) * H + h;
-  };
+}
 
-  // Inputs of one forward token and of one backward token, loaded a step
-  // ahead of their use (within a chunk: the backward token's state was
-  // stored when its chunk was recomputed, a pass earlier).
-  struct FIn {
-    float a[RPL], b;
-    RowsIn<BF16, RPL> k;
-    ColsIn<BF16> v;
-  };
-  struct BIn {
-    float a[RPL], b, dout[kCPW], Sp[E];
-    RowsIn<BF16, RPL> k, q;
-  };
-  auto load_alpha = [&](int64_t row, float (&a)[RPL]) {
-    if constexpr (SG) {
-      const float g = p.alpha[row];
+// acc[s] += A(tile rows, 0:K) B(0:K, tile cols) for the tiles t = wv + 8 s of
+// the (M/16) x (N/16) tile grid (row-major), wv being the caller's wave slot
+// (wave-uniform; a slot past the grid does nothing).  All tiles of a wave
+// share one column block, so each B fragment is loaded once for them.
+//   A(m, k) = AK ? a[m * lda + k] : a[k * lda + m]
+//   B(k, n) = BK ? b[n * ldb + k] : b[k * ldb + n]
+// Within each 16-wide block of K, lane group g takes k = 4g .. 4g + 3 over the
+// four products (lane i = row of A / column of B); the result lane holds rows
+// 4g + q of column i of its tile.  The fragments of KG blocks of K are loaded
+// before their products.  Triangular operands are stored with their zeros, so
+// the products run over the whole of K (exact zeros do not change a sum).
+template <int M, int N, int K, bool AK, bool BK, int NT>
+__device__ __forceinline__ void mm(f4 (&acc)[NT], const float* a, int lda, const float* b, int ldb,
+                                   int wv) {
+  constexpr int TN = N / 16, NTILE = (M / 16) * TN, KB = K / 16;
+  static_assert(kNW % TN == 0, "a wave's tiles share one column block");
+  static_assert(NTILE % kNW == 0 ? NT == NTILE / kNW : (NT == 1 && NTILE < kNW), "tiles per wave");
+  constexpr int KG0 = NT >= 8 ? 1 : (NT >= 4 ? 2 : 4);
+  constexpr int KG = KB < KG0 ? KB : KG0;
+  static_assert(KB % KG == 0, "K blocks in whole groups");
+  if (NTILE < kNW && wv >= NTILE) return;
+  const int l = threadIdx.x & 63, i = l & 15, g = l >> 4;
+  const int n0 = (wv % TN) * 16;
 #pragma unroll
-      for (int r = 0; r < RPL; ++r) a[r] = g;
-    } else {
-      ld_f<RPL>(p.alpha + row * DK + i0, a);
-    }
-  };
-  auto load_f = [&](int64_t c, int s, FIn& x) {
-    const int64_t row = row_of(c, s);
-    load_alpha(row, x.a);
-    x.k.load(p.k, row * DK + i0);
-    x.b = p.beta[row];
-    x.v.load(p.v, row * DV + col);
-  };
-  auto load_b = [&](int64_t c, int sb, BIn& x) {
-    const int64_t row = row_of(c, sb);
-    load_alpha(row, x.a);
-    x.k.load(p.k, row * DK + i0);
-    x.q.load(p.q, row * DK + i0);
-    x.b = p.beta[row];
-    ldfn<kCPW>(p.d_o + row * DV + col, x.dout);
-    const float* src = slot(c, sb);
-    ld_elems<E>(src, x.Sp);
-  };
-
-  // One forward token of chunk c: keeps S before the token, then
-  // S <- Diag(a) S + k u^T with u = b (v - St^T k).
-  auto fwd_token = [&](int64_t c, int s, const FIn& f) {
-    float* dst = slot(c, s);
-    st_elems<E>(dst, S);
-    float x[kCPW];
+  for (int kg = 0; kg < KB; kg += KG) {
+    f4 bv[KG], av[KG][NT];
 #pragma unroll
-    for (int e = 0; e < kCPW; ++e) {
-      x[e] = 0.f;
+    for (int u = 0; u < KG; ++u) {
+      const int k0 = 16 * (kg + u);
+      if constexpr (BK) {
+        bv[u] = *reinterpret_cast<const f4*>(b + (n0 + i) * ldb + k0 + 4 * g);
+      } else {
 #pragma unroll
-      for (int r = 0; r < RPL; ++r) {
-        S[r * kCPW + e] *= f.a[r];
-        x[e] += S[r * kCPW + e] * f.k[r];
+        for (int j = 0; j < 4; ++j) bv[u][j] = b[(k0 + 4 * g + j) * ldb + n0 + i];
       }
-    }
-    wave_sums<kCPW>(x);
 #pragma unroll
-    for (int e = 0; e < kCPW; ++e) {
-      const float r_ = f.v[e] - x[e];   // v - p
-      const float u = f.b * r_;
-#pragma unroll
-      for (int r = 0; r < RPL; ++r) S[r * kCPW + e] += f.k[r] * u;
-      if (l == 0) {
-        sU[c & 1][s][jc + e] = u;
-        sR[c & 1][s][jc + e] = r_;
-      }
-    }
-  };
-
-  // Backward token sb of chunk c with inputs x (and, when f is given, the
-  // forward token s of chunk c-1 between its two halves).  Every memory
-  // instruction is issued by every lane, so each step issues the same number
-  // of them and the memory-counter waits for loads issued a step earlier do
-  // not cover the stores in between: the per-wave row sums go through LDS
-  // (one barrier per token) and all threads write the slab's sums; values
-  // that are the same in every lane (dv, db) are stored by all lanes.
-  int par = 0;
-  auto bwd_token = [&](int64_t c, int sb, const BIn& x, int64_t cf_c, int cf_s, const FIn* f) {
-    const int64_t brow = row_of(c, sb);
-    float u[kCPW], rr[kCPW], St[E];
-#pragma unroll
-    for (int e = 0; e < kCPW; ++e) {
-      u[e] = sU[c & 1][sb][jc + e];
-      rr[e] = sR[c & 1][sb][jc + e];
-    }
-    // G += q do^T (o_t = S'^T q_t); dq = S' do; du = G^T k
-    float dq[RPL], du[kCPW];
-#pragma unroll
-    for (int r = 0; r < RPL; ++r) {
-      float xq = 0.f;
-#pragma unroll
-      for (int e = 0; e < kCPW; ++e) {
-        const int q_ = r * kCPW + e;
-        St[q_] = x.a[r] * x.Sp[q_];
-        G[q_] += x.q[r] * x.dout[e];
-        xq += (St[q_] + x.k[r] * u[e]) * x.dout[e];
-      }
-      dq[r] = xq;
-    }
-#pragma unroll
-    for (int e = 0; e < kCPW; ++e) {
-      du[e] = 0.f;
-#pragma unroll
-      for (int r = 0; r < RPL; ++r) du[e] += G[r * kCPW + e] * x.k[r];
-    }
-    // the forward token of chunk c-1 at the same step: its column sum is
-    // independent of this one, so the two reductions overlap
-    if (f) fwd_token(cf_c, cf_s, *f);
-    wave_sums<kCPW>(du);
-    float dk[RPL], da[RPL], db = 0.f;
-#pragma unroll
-    for (int r = 0; r < RPL; ++r) dk[r] = da[r] = 0.f;
-#pragma unroll
-    for (int e = 0; e < kCPW; ++e) {
-      const float dp = -x.b * du[e];
-      db += du[e] * rr[e];
-#pragma unroll
-      for (int r = 0; r < RPL; ++r) {
-        const int q_ = r * kCPW + e;
-        const float dSt = G[q_] + x.k[r] * dp;
-        dk[r] += G[q_] * u[e] + St[q_] * dp;
-        da[r] += dSt * x.Sp[q_];
-        G[q_] = x.a[r] * dSt;
-      }
-    }
-    float dv4[kCPW];
-#pragma unroll
-    for (int e = 0; e < kCPW; ++e) dv4[e] = x.b * du[e];
-    stfn<kCPW>(p.dv + brow * DV + col, dv4);
-    if (l == 0) ringb[par][w] = db;
-#pragma unroll
-    for (int r = 0; r < RPL; ++r) {
-      ring[par][0][w][i0 + r] = dq[r];
-      ring[par][1][w][i0 + r] = dk[r];
-      ring[par][2][w][i0 + r] = da[r];
-    }
-    lds_sync();
-    // the slab's sums over the waves, in a fixed order: index x = t + kNT j
-    // is quantity min(x / DK, 2) (dq, dk, da) of row x % DK (indices past
-    // 3 DK write da values again), and every thread writes the same db
-    {
-      const int64_t lrow = prow_of(c, sb);
-      constexpr int NPASS = (3 * DK + kNT - 1) / kNT;
-#pragma unroll
-      for (int j = 0; j < NPASS; ++j) {
-        const int x = t + kNT * j;
-        const int i = x % DK;
-        const int qn = x / DK < 2 ? x / DK : 2;
-        const float v = sum_waves(&ring[par][qn][0][i], DK);
-        const int64_t prow = (slab * p.part_rows + lrow) * DK + i;   // slab-major: one row is 512 B
-        (qn == 0 ? p.part_dq : (qn == 1 ? p.part_dk : p.part_da))[prow] = v;
-      }
-      p.part_db[slab * p.part_rows + lrow] = sum_waves(ringb[par], 1);
-    }
-    par ^= 1;
-  };
-
-  FIn cf, nf;
-  BIn cb, nb;
-  // prologue: the token states of the window's last chunk
-  {
-    const int64_t c = c_hi;
-    const int len = int(T - c * kC < kC ? T - c * kC : kC);
-    checkpoint(c, S);
-    for (int s = 0; s < len; ++s) {
-      load_f(c, s, cf);
-      fwd_token(c, s, cf);
-    }
-  }
-
-  for (int64_t c = c_hi; c >= c_lo; --c) {
-    const int len = int(T - c * kC < kC ? T - c * kC : kC);
-    const bool fwd = c > c_lo;              // chunk c-1 is recomputed meanwhile (always full)
-    if (fwd) checkpoint(c - 1, S);
-    if (fwd && len == kC) {
-      // the steady state: both tokens in every step, inputs a step ahead in
-      // two sets used alternately (no register copies, so each wait sits at
-      // the first use of its input; the loads past the chunk's end repeat
-      // its last token: no branch)
-      load_f(c - 1, 0, cf);
-      load_b(c, kC - 1, cb);
-      for (int s = 0; s < kC; s += 2) {
-        load_b(c, kC - 2 - s, nb);
-        load_f(c - 1, s + 1, nf);
-        bwd_token(c, kC - 1 - s, cb, c - 1, s, &cf);
-        const int sn = s + 2 < kC ? s + 2 : kC - 1;
-        load_b(c, kC - 1 - sn, cb);
-        load_f(c - 1, sn, cf);
-        bwd_token(c, kC - 2 - s, nb, c - 1, s + 1, &nf);
-      }
-    } else {
-      const int steps = fwd ? kC : len;
-      for (int s = 0; s < steps; ++s) {
-        if (fwd) load_f(c - 1, s, cf);
-        if (s < len) {
-          load_b(c, len - 1 - s, cb);
-          bwd_token(c, len - 1 - s, cb, c - 1, s, fwd ? &cf : nullptr);
+      for (int s = 0; s < NT; ++s) {
+        const int m0 = ((wv + kNW * s) / TN) * 16;
+        if constexpr (AK) {
+          av[u][s] = *reinterpret_cast<const f4*>(a + (m0 + i) * lda + k0 + 4 * g);
         } else {
-          fwd_token(c - 1, s, cf);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) av[u][s][j] = a[(k0 + 4 * g + j) * lda + m0 + i];
         }
       }
     }
+#pragma unroll
+    for (int u = 0; u < KG; ++u)
+#pragma unroll
+      for (int s = 0; s < NT; ++s)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[s] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u][s][j], bv[u][j], acc[s], 0, 0, 0);
   }
-  // after chunk 0 the initial state's gradient; otherwise the carry for
-  // the next window
-  float* gdst = c_lo == 0 ? p.d_state_in : p.g_carry;
-#pragma unroll
-  for (int r = 0; r < RPL; ++r)
-    if (gdst) stfn<kCPW>(gdst + state_off + int64_t(r) * DV, G + r * kCPW);
 }
 
-// The global token row of row lrow of a window's partial sums, or -1 when
-// that row is past its sequence (or before its first chunk).
-__device__ __forceinline__ int64_t window_row(const BackwardArgs& p, int64_t lrow) {
-  const int64_t h = lrow % p.H;
-  int64_t x = lrow / p.H;
-  const int s = int(x % 64);
-  x /= 64;
-  const int64_t jj = x % p.win_k;
-  const int64_t n = x / p.win_k;
-  const int64_t tok0 = p.cu_seqlens ? int64_t(p.cu_seqlens[n]) : n * p.T;
-  const int64_t T = p.cu_seqlens ? int64_t(p.cu_seqlens[n + 1]) - tok0 : p.T;
-  const int64_t nch = (T + 63) / 64;
-  const int64_t c = nch - 1 - (p.win_lo + jj);
-  const int64_t t = c * 64 + s;
-  if (c < 0 || t >= T) return -1;
-  return (tok0 + t) * p.H + h;
+template <int NT>
+__device__ __forceinline__ void zero(f4 (&acc)[NT]) {
+#pragma unroll
+  for (int s = 0; s < NT; ++s) acc[s] = f4{0.f, 0.f, 0.f, 0.f};
 }
 
-// dq, dk, dalpha (per element) and dbeta: sums of the NS per-slab partials,
-// which are stored slab-major (the walk writes whole 512-byte rows), so a
-// thread reads NS values `stride` apart and a wave reads NS contiguous
-// streams; the slabs are added pairwise in a fixed order.
-template <int NS>
-__device__ __forceinline__ float sum_ns(const float* p, int64_t stride) {
-  float x[NS];
-#pragma unroll
-  for (int v = 0; v < NS; ++v) x[v] = p[v * stride];
-#pragma unroll
-  for (int h = 1; h < NS; h <<= 1)
-#pragma unroll
-    for (int v = 0; v + h < NS; v += 2 * h) x[v] += x[v + h];
-  return x[0];
+// Tile s of a wave: first row m0, first column n0 (N columns in the grid).
+template <int N>
+__device__ __forceinline__ void tile_origin(int wv, int s, int& m0, int& n0) {
+  const int t = wv + kNW * s;
+  m0 = (t / (N / 16)) * 16;
+  n0 = (t % (N / 16)) * 16;
+}
+template <int M, int N>
+__device__ __forceinline__ bool tile_live(int wv, int s) {
+  return wv + kNW * s < (M / 16) * (N / 16);
 }
 
-template <int DK, int NS, bool SG>
-__global__ __launch_bounds__(256) void kda_bwd_reduce_kernel(BackwardArgs p) {
-  const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;   // window row * DK + key row
-  if (idx >= p.part_rows * DK) return;
-  const int64_t lrow = idx / DK;
-  const int i = int(idx % DK);
-  const int64_t grow = window_row(p, lrow);
-  if (grow < 0) return;
-  const int64_t o = grow * DK + i;
-  const int64_t st = p.part_rows * DK;
-  p.dq[o] = sum_ns<NS>(p.part_dq + idx, st);
-  p.dk[o] = sum_ns<NS>(p.part_dk + idx, st);
-  if constexpr (!SG) p.dalpha[o] = sum_ns<NS>(p.part_da + idx, st);
-  if (i == 0) p.dbeta[grow] = sum_ns<NS>(p.part_db + lrow, p.part_rows);
+// Layouts of the chain's operands, in its fragment order so that each wave
+// instruction moves one contiguous block.  A_c: wave w (rows 16w..16w+15)
+// takes DK/16 float4 per lane, lane (i, g) holding A_c[16w + i][4j + g] for
+// j = 0 .. DK/4 - 1.  b_c and dS': per 16-column slab and wave, one float4
+// per lane holding rows 16w + 4g .. 16w + 4g + 3 of column i.
+template <int DK>
+__device__ __forceinline__ int frag_a(int r, int c) {
+  const int j = c >> 2;
+  return (((r >> 4) * (DK / 16) + (j >> 2)) * 64 + (r & 15) + 16 * (c & 3)) * 4 + (j & 3);
+}
+template <int DK>
+__device__ __forceinline__ int64_t frag_s(int js, int w, int l) {
+  return ((int64_t(js) * (DK / 16) + w) * 64 + l) * 4;
 }
 
-// A scalar gate's gradient: the sum over key rows and slabs of the per-row
-// partials (chain rule: the gate is every row's decay), one wave per token
-// row; each lane adds the slabs of its DK / 64 key rows, then the lanes are
-// added in a fixed order (deterministic).
-template <int DK, int NS>
-__global__ __launch_bounds__(256) void kda_bwd_dgate_kernel(BackwardArgs p) {
-  constexpr int PER = DK / 64;   // key rows per lane
-  const int64_t lrow = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  const int l = threadIdx.x & 63;
-  if (lrow >= p.part_rows) return;
-  const int64_t row = window_row(p, lrow);
-  if (row < 0) return;
-  float s = 0.f;
+// The chunk a workgroup works on: sequence n, chunk c counted from the start
+// (the window holds reverse indices win_lo .. win_lo + win_k - 1).
+struct Chunk {
+  int64_t n, c, s0, tok0, wi;
+  int nv, h;
+};
+
+__device__ __forceinline__ bool locate(const BwdChunkArgs& p, int64_t n, int64_t jw, int h,
+                                       Chunk& ck) {
+  int64_t s0, len;
+  if (p.cu_seqlens) {
+    s0 = p.cu_seqlens[n];
+    len = p.cu_seqlens[n + 1] - s0;
+  } else {
+    s0 = n * p.T;
+    len = p.T;
+  }
+  const int64_t nch = (len + kC - 1) / kC;
+  ck.n = n;
+  ck.h = h;
+  ck.s0 = s0;
+  ck.c = nch - 1 - (p.win_lo + jw);
+  if (ck.c < 0) return false;
+  ck.tok0 = s0 + ck.c * kC;
+  const int64_t rem = len - ck.c * kC;
+  ck.nv = int(rem < kC ? rem : kC);
+  ck.wi = (n * p.H + h) * p.win_k + jw;
+  return true;
+}
+
+// The state entering chunk c: state_in for the first chunk (nullptr = zero),
+// else the forward's snapshot after chunk c - 1.
+template <int DK>
+__device__ __forceinline__ const float* chunk_state(const BwdChunkArgs& p, const Chunk& ck) {
+  const int64_t hs = int64_t(DK) * p.DV;
+  if (ck.c == 0) return p.state_in ? p.state_in + (ck.n * p.H + ck.h) * hs : nullptr;
+  const int64_t base = p.cu_seqlens ? ck.s0 / kC : ck.n * (p.T / kC);
+  return p.snapshots + ((base + ck.c - 1) * p.H + ck.h) * hs;
+}
+
+// rho (relative decays) of the chunk into rho_out[64][ld] and the global copy;
+// gm = gamma_m, gq = gamma_C / gamma_m per channel.  Threads 0..DK-1, one
+// channel each; rows past the chunk's end take alpha = 1.
+template <int DK, bool SG>
+__device__ __forceinline__ void decays(const BwdChunkArgs& p, const Chunk& ck, float* rho, int ld,
+                                       float* rho_g, float* sgm, float* sgq) {
+  const int c = threadIdx.x;
+  if (c >= DK) return;
+  float a[kC];
 #pragma unroll
-  for (int r = 0; r < PER; ++r) s += sum_ns<NS>(p.part_da + lrow * DK + l * PER + r, p.part_rows * DK);
+  for (int r = 0; r < kC; ++r) {
+    const int64_t row = (ck.tok0 + r) * p.H + ck.h;
+    a[r] = r < ck.nv ? (SG ? p.alpha[row] : p.alpha[row * DK + c]) : 1.f;
+  }
+  float gm = 1.f;
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) s += __shfl_xor(s, off);
-  if (l == 0) p.dalpha[row] = s;
+  for (int r = 0; r <= kMid; ++r) gm *= a[r];
+  float x = 1.f;
+  rho[kMid * ld + c] = 1.f;
+  rho_g[kMid * DK + c] = 1.f;
+#pragma unroll
+  for (int r = kMid - 1; r >= 0; --r) {   // sigma_r = prod_{r < i <= m} alpha_i
+    x *= a[r + 1];
+    const float v = 1.f / x;
+    rho[r * ld + c] = v;
+    rho_g[r * DK + c] = v;
+  }
+  x = 1.f;
+#pragma unroll
+  for (int r = kMid + 1; r < kC; ++r) {
+    x *= a[r];
+    rho[r * ld + c] = x;
+    rho_g[r * DK + c] = x;
+  }
+  sgm[c] = gm;
+  sgq[c] = x;
+  rho_g[kC * DK + c] = gm;   // gamma_m after the 64 rows
+}
+
+// ---------------------------------------------------------------- prep ------
+template <int DK, bool BF16, bool SG>
+__global__ __launch_bounds__(kNT, 1) void kda_bwdc_prep_kernel(BwdChunkArgs p) {
+  constexpr int LD = DK + 4;
+  constexpr int NTW = (4 * (DK / 16) + kNW - 1) / kNW;          // 64 x DK tiles per wave
+  constexpr int NTA = ((DK / 16) * (DK / 16) + kNW - 1) / kNW;  // DK x DK
+  __shared__ __attribute__((aligned(16))) float sm[3 * 64 * LD + 2 * 64 * kL64 + 2 * DK + 64 +
+                                                   (128 + DK) * kLS];
+  float* const sKr = sm;             // Kr, then W
+  float* const sKh = sKr + 64 * LD;
+  float* const sQr = sKh + 64 * LD;
+  float* const sM = sQr + 64 * LD;   // Diag(beta) X, then M, then T
+  float* const sP = sM + 64 * kL64;
+  float* const sgm = sP + 64 * kL64;
+  float* const sgq = sgm + DK;
+  float* const sb = sgq + DK;
+  float* const sV = sb + 64;         // V slab, then Z slab (also the solve's scratch)
+  float* const sO = sV + 64 * kLS;   // dO slab
+  float* const sS = sO + 64 * kLS;   // S slab [DK][16]
+
+  const int t = threadIdx.x, w = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63, li = l & 15,
+            g = l >> 4;
+  const int H = p.H, DV = p.DV;
+  const int64_t bid = blockIdx.x;
+  const int h = int(bid % H);
+  const int64_t jw = (bid / H) % p.win_k, n = bid / H / p.win_k;
+  Chunk ck;
+  if (!locate(p, n, jw, h, ck)) return;
+  const int nv = ck.nv;
+
+  // 1. decays, scaled keys and queries, beta
+  float* const rho_g = p.rho + ck.wi * (65 * DK);
+  decays<DK, SG>(p, ck, sQr, LD, rho_g, sgm, sgq);   // rho parked in sQr
+  if (t < 64) sb[t] = t < nv ? p.beta[(ck.tok0 + t) * H + h] : 0.f;
+  lds_barrier();
+#pragma unroll
+  for (int u = 0; u < 64 * DK / kNT; ++u) {
+    const int e = t + u * kNT;
+    const int r = e / DK, c = e % DK;
+    const float rh = sQr[r * LD + c];
+    const int64_t x = ((ck.tok0 + r) * H + h) * int64_t(DK) + c;
+    const float kv = r < nv ? ld_in<BF16>(p.k, x) : 0.f;
+    const float qv = r < nv ? ld_in<BF16>(p.q, x) : 0.f;
+    sKr[r * LD + c] = kv * rh;
+    sKh[r * LD + c] = kv / rh;
+    sQr[r * LD + c] = qv * rh;
+  }
+  lds_barrier();
+
+  // 2. Diag(beta) X and P
+  {
+    f4 ax[2], ap[2];
+    zero(ax);
+    zero(ap);
+    mm<64, 64, DK, true, true>(ax, sKr, LD, sKh, LD, w);
+    mm<64, 64, DK, true, true>(ap, sQr, LD, sKh, LD, w);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      int m0, n0;
+      tile_origin<64>(w, s, m0, n0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = m0 + 4 * g + q, c = n0 + li;
+        sM[r * kL64 + c] = c < r ? sb[r] * ax[s][q] : 0.f;
+        sP[r * kL64 + c] = c <= r ? ap[s][q] : 0.f;
+      }
+    }
+  }
+  lds_barrier();
+
+  // 3. M = (I + Diag(beta) X)^-1 in place: the four diagonal 16x16 blocks by
+  // forward substitution (wave 0, lane = column of a block), then block rows
+  // 1..3: M_ij = -M_ii sum_{j <= k < i} A_ik M_kj.
+  if (w == 0) {
+    const int o = 16 * g;
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float s = r == li ? 1.f : 0.f;
+#pragma unroll
+      for (int u = 0; u < r; ++u) s -= sM[(o + r) * kL64 + o + u] * x[u];
+      x[r] = s;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sM[(o + r) * kL64 + o + li] = x[r];
+  }
+  lds_barrier();
+  for (int bi = 1; bi < 4; ++bi) {
+    f4 acc = f4{0.f, 0.f, 0.f, 0.f};
+    const int bj = w;
+    if (bj < bi) {
+      for (int bk = bj; bk < bi; ++bk) {
+        const f4 av = *reinterpret_cast<const f4*>(sM + (16 * bi + li) * kL64 + 16 * bk + 4 * g);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j], sM[(16 * bk + 4 * g + j) * kL64 + 16 * bj + li],
+                                                     acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sV[(16 * bj + 4 * g + q) * kLS + li] = acc[q];
+    }
+    lds_barrier();
+    f4 acc2 = f4{0.f, 0.f, 0.f, 0.f};
+    if (bj < bi) {
+      const f4 av = *reinterpret_cast<const f4*>(sM + (16 * bi + li) * kL64 + 16 * bi + 4 * g);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j], sV[(16 * bj + 4 * g + j) * kLS + li], acc2, 0, 0,
+                                                    0);
+    }
+    lds_barrier();
+    if (bj < bi) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sM[(16 * bi + 4 * g + q) * kL64 + 16 * bj + li] = -acc2[q];
+    }
+    lds_barrier();
+  }
+
+  // 4. M out; T = M Diag(beta) in place
+  float* const Mg = p.Mb + ck.wi * (64 * 64);
+#pragma unroll
+  for (int u = 0; u < 64 * 64 / kNT; ++u) {
+    const int e = t + u * kNT;
+    const int r = e >> 6, c = e & 63;
+    const float m = sM[r * kL64 + c];
+    Mg[e] = m;
+    sM[r * kL64 + c] = m * sb[c];
+  }
+  lds_barrier();
+
+  // 5. W = T Kr Diag(gamma_m), over Kr
+  {
+    f4 aw[NTW];
+    zero(aw);
+    mm<64, DK, 64, true, false>(aw, sM, kL64, sKr, LD, w);
+    lds_barrier();
+#pragma unroll
+    for (int s = 0; s < NTW; ++s) {
+      if (!tile_live<64, DK>(w, s)) break;
+      int m0, n0;
+      tile_origin<DK>(w, s, m0, n0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sKr[(m0 + 4 * g + q) * LD + n0 + li] = aw[s][q] * sgm[n0 + li];
+    }
+  }
+  lds_barrier();
+  float* const sW = sKr;
+
+  // 6. A_c = Diag(gamma_C) - W^T Kh Diag(gamma_C / gamma_m), stored in the
+  // chain's fragment order.
+  {
+    f4 aa[NTA];
+    zero(aa);
+    mm<DK, DK, 64, false, false>(aa, sW, LD, sKh, LD, w);
+    float* const Ag = p.Ac + ck.wi * (int64_t(DK) * DK);
+#pragma unroll
+    for (int s = 0; s < NTA; ++s) {
+      if (!tile_live<DK, DK>(w, s)) break;
+      int m0, n0;
+      tile_origin<DK>(w, s, m0, n0);
+      const int c = n0 + li;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = m0 + 4 * g + q;
+        float v = -sgq[c] * aa[s][q];
+        if (r == c) v += sgm[r] * sgq[r];
+        Ag[frag_a<DK>(r, c)] = v;
+      }
+    }
+  }
+
+  // 7. per 16 value columns: Vn = T V - W S;  b_c = Diag(gamma_m) Qr^T dO - W^T (P^T dO)
+  const float* const S = chunk_state<DK>(p, ck);
+  float* const Vng = p.Vnb + ck.wi * (64 * int64_t(DV));
+  float* const bg = p.bc + ck.wi * (int64_t(DK) * DV);
+  // (the next slab's inputs are fetched into registers during this slab's
+  // products; past the last slab the last one is fetched again)
+  constexpr int NR = 64 * 16 / kNT, NS = DK * 16 / kNT;
+  struct Slab {
+    float v[NR], o[NR], s[NS];
+  };
+  auto fetch = [&](Slab& R, int js) {
+    if (js >= DV / 16) js = DV / 16 - 1;
+#pragma unroll
+    for (int u = 0; u < NR; ++u) {
+      const int e = t + u * kNT;
+      const int r = e >> 4, j = e & 15;
+      const int64_t x = ((ck.tok0 + r) * H + h) * int64_t(DV) + 16 * js + j;
+      R.v[u] = r < nv ? ld_in<BF16>(p.v, x) : 0.f;
+      R.o[u] = r < nv ? p.d_o[x] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      const int e = t + u * kNT;
+      R.s[u] = S ? S[int64_t(e >> 4) * DV + 16 * js + (e & 15)] : 0.f;
+    }
+  };
+  Slab R;
+  fetch(R, 0);
+  for (int js = 0; js < DV / 16; ++js) {
+#pragma unroll
+    for (int u = 0; u < NR; ++u) {
+      const int e = t + u * kNT;
+      sV[(e >> 4) * kLS + (e & 15)] = R.v[u];
+      sO[(e >> 4) * kLS + (e & 15)] = R.o[u];
+    }
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      const int e = t + u * kNT;
+      sS[(e >> 4) * kLS + (e & 15)] = R.s[u];
+    }
+    fetch(R, js + 1);
+    lds_barrier();
+    f4 au[1], an[1], az[1];
+    zero(au);
+    zero(an);
+    zero(az);
+    mm<64, 16, 64, true, false>(au, sM, kL64, sV, kLS, w);
+    mm<64, 16, DK, true, false>(an, sW, LD, sS, kLS, w);
+    mm<64, 16, 64, false, false>(az, sP, kL64, sO, kLS, (w + 4) & 7);
+    if (w < 4) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) Vng[(16 * w + 4 * g + q) * DV + 16 * js + li] = au[0][q] - an[0][q];
+    }
+    lds_barrier();
+    if (w >= 4) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sV[(16 * (w - 4) + 4 * g + q) * kLS + li] = az[0][q];
+    }
+    lds_barrier();
+    f4 b1[1], b2[1];
+    zero(b1);
+    zero(b2);
+    mm<DK, 16, 64, false, false>(b1, sQr, LD, sO, kLS, w);
+    mm<DK, 16, 64, false, false>(b2, sW, LD, sV, kLS, w);
+    if (tile_live<DK, 16>(w, 0)) {
+      f4 v;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] = sgm[16 * w + 4 * g + q] * b1[0][q] - b2[0][q];
+      *reinterpret_cast<f4*>(bg + frag_s<DK>(js, w, l)) = v;
+    }
+    lds_barrier();
+  }
+}
+
+// ---------------------------------------------------------------- chain -----
+// dS (adjoint of the state entering a chunk) = b_c + A_c dS'.  One workgroup
+// per (sequence, head, 16 value columns); wave w holds rows 16w .. 16w + 15 of
+// the slab in the MFMA result layout.  dS' of every chunk goes to dSend.
+template <int DK>
+__global__ __launch_bounds__(64 * (DK / 16), 1) void kda_bwdc_chain_kernel(BwdChunkArgs p) {
+  constexpr int KQ = DK / 4;
+  __shared__ __attribute__((aligned(16))) float sD[2][DK * 16];
+  const int t = threadIdx.x, w = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63, li = l & 15,
+            g = l >> 4;
+  const int H = p.H, DV = p.DV, nsl = DV / 16;
+  // Workgroups go to the 8 XCDs round-robin; remap so that the slabs of one
+  // (sequence, head), which read the same A_c, run on one XCD and share its L2.
+  int64_t bid = blockIdx.x;
+  const int64_t G = gridDim.x;
+  if ((G & 7) == 0) bid = (bid & 7) * (G >> 3) + (bid >> 3);
+  const int slab = int(bid % nsl);
+  const int64_t pr = bid / nsl;
+  const int h = int(pr % H);
+  const int64_t n = pr / H;
+  const int64_t len = p.cu_seqlens ? p.cu_seqlens[n + 1] - p.cu_seqlens[n] : p.T;
+  const int64_t nch = (len + kC - 1) / kC;
+  const int64_t c_hi = nch - 1 - p.win_lo;
+  const int64_t hs = (n * H + h) * int64_t(DK) * DV;
+  const int col = 16 * slab + li;
+  f4 dS;
+  if (p.win_lo == 0 || c_hi < 0) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      dS[q] = p.d_state_out ? p.d_state_out[hs + int64_t(16 * w + 4 * g + q) * DV + col] : 0.f;
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dS[q] = p.carry[hs + int64_t(16 * w + 4 * g + q) * DV + col];
+  }
+  if (c_hi < 0) {   // no chunk in this window: only an empty sequence writes (window 0)
+    if (p.win_lo == 0 && p.d_state_in) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) p.d_state_in[hs + int64_t(16 * w + 4 * g + q) * DV + col] = dS[q];
+    }
+    return;
+  }
+  const int64_t steps = c_hi + 1 < p.win_k ? c_hi + 1 : p.win_k;
+  // Operands of a step: this lane's A_c fragments and b_c values.  Three sets
+  // in rotation: the loads for the next two chunks are in flight during this
+  // chunk's products (past the last step the last chunk is loaded again, so
+  // the loads stay unconditional).
+  struct Ops {
+    f4 a[KQ / 4];
+    f4 b;
+  };
+  auto load = [&](Ops& o, int64_t jw) {
+    if (jw >= steps) jw = steps - 1;
+    const int64_t wi = (n * H + h) * p.win_k + jw;
+    const float* const ar = p.Ac + wi * (int64_t(DK) * DK) + (w * (KQ / 4) * 64 + l) * 4;
+#pragma unroll
+    for (int j = 0; j < KQ / 4; ++j) o.a[j] = *reinterpret_cast<const f4*>(ar + j * 256);
+    o.b = *reinterpret_cast<const f4*>(p.bc + wi * (int64_t(DK) * DV) + frag_s<DK>(slab, w, l));
+  };
+  auto step = [&](const Ops& o, int64_t jw) {
+    const int64_t wi = (n * H + h) * p.win_k + jw;
+    float* const sd = sD[jw & 1];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) sd[(16 * w + 4 * g + q) * 16 + li] = dS[q];
+    *reinterpret_cast<f4*>(p.dSend + wi * (int64_t(DK) * DV) + frag_s<DK>(slab, w, l)) = dS;
+    lds_barrier();
+    f4 acc0 = o.b, acc1 = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < KQ; j += 2) {
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(o.a[j >> 2][j & 3], sd[(4 * j + g) * 16 + li], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(o.a[(j + 1) >> 2][(j + 1) & 3],
+                                                  sd[(4 * (j + 1) + g) * 16 + li], acc1, 0, 0, 0);
+    }
+    dS = acc0 + acc1;
+  };
+  Ops A, B, C;
+  load(A, 0);
+  load(B, 1);
+  int64_t jw = 0;
+  for (; jw + 2 < steps; jw += 3) {
+    load(C, jw + 2);
+    step(A, jw);
+    load(A, jw + 3);
+    step(B, jw + 1);
+    load(B, jw + 4);
+    step(C, jw + 2);
+  }
+  if (jw < steps) step(A, jw);
+  if (jw + 1 < steps) step(B, jw + 1);
+  const int64_t c = c_hi - steps;   // last chunk done: c + 1
+  if (c < 0 && !p.d_state_in) return;
+  float* const dst = c < 0 ? p.d_state_in + hs : p.carry + hs;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) dst[int64_t(16 * w + 4 * g + q) * DV + col] = dS[q];
+}
+
+// ---------------------------------------------------------------- post ------
+template <int DK, bool BF16, bool SG>
+__global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
+  constexpr int LD = DK + 4;
+  constexpr int NT4 = (4 * (DK / 16) + kNW - 1) / kNW;   // 64 x DK tiles per wave
+  __shared__ __attribute__((aligned(16))) float sm[3 * 64 * LD + 3 * 64 * kL64 + 3 * DK + 2 * 64 +
+                                                   4 * DK];
+  float* const R1 = sm;               // Kh
+  float* const R2 = R1 + 64 * LD;     // slabs (with R3), then -dW', then Qr, then dg
+  float* const R3 = R2 + 64 * LD;     // Qr (for P), slabs, then Kr
+  float* const sM = R3 + 64 * LD;     // M
+  float* const sP = sM + 64 * kL64;   // P, then dP, then dM M^T
+  float* const sX = sP + 64 * kL64;   // dT, then dM, then Diag(beta) dA
+  float* const sgm = sX + 64 * kL64;
+  float* const sgq = sgm + DK;
+  float* const sdgc = sgq + DK;
+  float* const sb = sdgc + DK;
+  float* const sdb = sb + 64;
+  float* const red = sdb + 64;        // [4][DK]
+  // slab buffers (inside R2 .. R3)
+  float* const sO = R2;
+  float* const sVn = sO + 64 * kLS;
+  float* const sV = sVn + 64 * kLS;
+  float* const sdVn = sV + 64 * kLS;
+  float* const sD = sdVn + 64 * kLS;  // dS' Diag(gamma_C / gamma_m) rows, [DK][16]
+  float* const sS = sD + DK * kLS;    // S Diag(gamma_m) rows
+
+  const int t = threadIdx.x, w = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63, li = l & 15,
+            g = l >> 4;
+  const int H = p.H, DV = p.DV;
+  const int64_t bid = blockIdx.x;
+  const int h = int(bid % H);
+  const int64_t jw = (bid / H) % p.win_k, n = bid / H / p.win_k;
+  Chunk ck;
+  if (!locate(p, n, jw, h, ck)) return;
+  const int nv = ck.nv;
+  const float* const rho = p.rho + ck.wi * (65 * DK);
+
+  // 1. decay factors, beta, Kh, Qr, M
+  if (t < DK) {
+    sgm[t] = rho[kC * DK + t];
+    sgq[t] = rho[(kC - 1) * DK + t];
+  }
+  if (t < 64) sb[t] = t < nv ? p.beta[(ck.tok0 + t) * H + h] : 0.f;
+#pragma unroll 8
+  for (int u = 0; u < 64 * DK / kNT; ++u) {
+    const int e = t + u * kNT;
+    const int r = e / DK, c = e % DK;
+    const float rh = rho[e];
+    const int64_t x = ((ck.tok0 + r) * H + h) * int64_t(DK) + c;
+    const float kv = r < nv ? ld_in<BF16>(p.k, x) : 0.f;
+    const float qv = r < nv ? ld_in<BF16>(p.q, x) : 0.f;
+    R1[r * LD + c] = kv / rh;
+    R3[r * LD + c] = qv * rh;
+  }
+  {
+    const float* const Mg = p.Mb + ck.wi * (64 * 64);
+#pragma unroll
+    for (int u = 0; u < 64 * 64 / kNT; ++u) {
+      const int e = t + u * kNT;
+      sM[(e >> 6) * kL64 + (e & 63)] = Mg[e];
+    }
+  }
+  lds_barrier();
+  {
+    f4 ap[2];
+    zero(ap);
+    mm<64, 64, DK, true, true>(ap, R3, LD, R1, LD, w);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      int m0, n0;
+      tile_origin<64>(w, s, m0, n0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = m0 + 4 * g + q, c = n0 + li;
+        sP[r * kL64 + c] = c <= r ? ap[s][q] : 0.f;
+      }
+    }
+  }
+  lds_barrier();
+
+  // 2. over the value columns, 16 at a time
+  f4 aq[NT4], ah[NT4], awn[NT4], adp[2], adt[2];
+  zero(aq);
+  zero(ah);
+  zero(awn);
+  zero(adp);
+  zero(adt);
+  float dgcs = 0.f;
+  const float* const S = chunk_state<DK>(p, ck);
+  const float* const dSe = p.dSend + ck.wi * (int64_t(DK) * DV);
+  const float* const Vng = p.Vnb + ck.wi * (64 * int64_t(DV));
+  // The next slab's operands are fetched into registers during this slab's
+  // products (past the last slab the last one is fetched again).
+  constexpr int NR = 64 * 16 / kNT, NS = DK * 16 / kNT;
+  struct Slab {
+    float o[NR], v[NR], vn[NR], s[NS];
+    f4 d;   // dS' of rows 16 (t / 64) + 4 g .. + 3, column t % 16 (t < 4 DK)
+  };
+  auto fetch = [&](Slab& R, int js) {
+    if (js >= DV / 16) js = DV / 16 - 1;
+#pragma unroll
+    for (int u = 0; u < NR; ++u) {
+      const int e = t + u * kNT;
+      const int r = e >> 4, j = e & 15;
+      const int64_t x = ((ck.tok0 + r) * H + h) * int64_t(DV) + 16 * js + j;
+      R.o[u] = r < nv ? p.d_o[x] : 0.f;
+      R.v[u] = r < nv ? ld_in<BF16>(p.v, x) : 0.f;
+      R.vn[u] = Vng[r * DV + 16 * js + j];
+    }
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      const int e = t + u * kNT;
+      R.s[u] = S ? S[int64_t(e >> 4) * DV + 16 * js + (e & 15)] : 0.f;
+    }
+    if (t < DK * 4) R.d = *reinterpret_cast<const f4*>(dSe + frag_s<DK>(js, t >> 6, t & 63));
+  };
+  Slab R;
+  fetch(R, 0);
+  for (int js = 0; js < DV / 16; ++js) {
+#pragma unroll
+    for (int u = 0; u < NR; ++u) {
+      const int e = t + u * kNT;
+      const int r = e >> 4, j = e & 15;
+      sO[r * kLS + j] = R.o[u];
+      sV[r * kLS + j] = R.v[u];
+      sVn[r * kLS + j] = R.vn[u];
+    }
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      const int e = t + u * kNT;
+      const int r = e >> 4, j = e & 15;
+      sS[r * kLS + j] = R.s[u] * sgm[r];
+    }
+    if (t < DK * 4) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = 16 * (t >> 6) + 4 * (g) + q;
+        sD[r * kLS + li] = R.d[q] * sgq[r];
+      }
+    }
+    fetch(R, js + 1);
+    lds_barrier();
+    {
+      f4 adv[1];
+      zero(adv);
+      mm<64, 16, 64, false, false>(adv, sP, kL64, sO, kLS, w);
+      mm<64, 16, DK, true, false>(adv, R1, LD, sD, kLS, w);
+      if (w < 4) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sdVn[(16 * w + 4 * g + q) * kLS + li] = adv[0][q];
+      }
+      if (t < DK) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) dgcs += sS[t * kLS + j] * sD[t * kLS + j];
+      }
+    }
+    lds_barrier();
+    mm<64, DK, 16, true, true>(aq, sO, kLS, sS, kLS, w);
+    mm<64, DK, 16, true, true>(awn, sdVn, kLS, sS, kLS, w);
+    mm<64, DK, 16, true, true>(ah, sVn, kLS, sD, kLS, w);
+    mm<64, 64, 16, true, true>(adp, sO, kLS, sVn, kLS, w);
+    mm<64, 64, 16, true, true>(adt, sdVn, kLS, sV, kLS, w);
+    {
+      f4 adv2[1];
+      zero(adv2);
+      const int wv = (w + 4) & 7;
+      mm<64, 16, 64, false, false>(adv2, sM, kL64, sdVn, kLS, wv);
+      if (wv < 4) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r = 16 * wv + 4 * g + q;
+          if (r < nv) p.dv[((ck.tok0 + r) * H + h) * int64_t(DV) + 16 * js + li] = sb[r] * adv2[0][q];
+        }
+      }
+    }
+    lds_barrier();
+  }
+
+  // 3. gamma_C's gradient: the column sums of dKend' * Kh plus sum_j S dS'
+  // gamma_C, both in the scaled forms.  dP, dT, -dW' to LDS.
+#pragma unroll
+  for (int s = 0; s < NT4; ++s) {
+    if (!tile_live<64, DK>(w, s)) break;
+    int m0, n0;
+    tile_origin<DK>(w, s, m0, n0);
+    float v = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v += ah[s][q] * R1[(m0 + 4 * g + q) * LD + n0 + li];
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    if (g == 0) red[(m0 >> 4) * DK + n0 + li] = v;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) R2[(m0 + 4 * g + q) * LD + n0 + li] = -awn[s][q];
+  }
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    int m0, n0;
+    tile_origin<64>(w, s, m0, n0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = m0 + 4 * g + q, c = n0 + li;
+      sP[r * kL64 + c] = c <= r ? adp[s][q] : 0.f;
+      sX[r * kL64 + c] = adt[s][q];
+    }
+  }
+  lds_barrier();
+  if (t < DK) sdgc[t] = red[t] + red[DK + t] + red[2 * DK + t] + red[3 * DK + t] + dgcs;
+#pragma unroll 4
+  for (int u = 0; u < 64 * DK / kNT; ++u) {   // Kr
+    const int e = t + u * kNT;
+    const int r = e / DK, c = e % DK;
+    const float kv = r < nv ? ld_in<BF16>(p.k, ((ck.tok0 + r) * H + h) * int64_t(DK) + c) : 0.f;
+    R3[r * LD + c] = kv * rho[e];
+  }
+  lds_barrier();
+
+  // 4. dT += dW' Kr^T;  AR = Diag(beta) M^T dW'
+  f4 ar[NT4];
+  zero(ar);
+  {
+    f4 at[2];
+    zero(at);
+    mm<64, 64, DK, true, true>(at, R2, LD, R3, LD, w);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      int m0, n0;
+      tile_origin<64>(w, s, m0, n0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sX[(m0 + 4 * g + q) * kL64 + n0 + li] += at[s][q];
+    }
+  }
+  mm<64, DK, 64, false, false>(ar, sM, kL64, R2, LD, w);
+#pragma unroll
+  for (int s = 0; s < NT4; ++s) {
+    if (!tile_live<64, DK>(w, s)) break;
+    int m0, n0;
+    tile_origin<DK>(w, s, m0, n0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) ar[s][q] *= sb[m0 + 4 * g + q];
+  }
+  lds_barrier();
+#pragma unroll 4
+  for (int u = 0; u < 64 * DK / kNT; ++u) {   // Qr
+    const int e = t + u * kNT;
+    const int r = e / DK, c = e % DK;
+    const float qv = r < nv ? ld_in<BF16>(p.q, ((ck.tok0 + r) * H + h) * int64_t(DK) + c) : 0.f;
+    R2[r * LD + c] = qv * rho[e];
+  }
+  lds_barrier();
+
+  // 5. AH += dP^T Qr;  AQ += dP Kh;  dbeta from T
+  mm<64, DK, 64, false, false>(ah, sP, kL64, R2, LD, w);
+  mm<64, DK, 64, true, false>(aq, sP, kL64, R1, LD, w);
+  if (t < 64) {
+    float s = 0.f;
+    for (int r = t; r < 64; ++r) s += sM[r * kL64 + t] * sX[r * kL64 + t];
+    sdb[t] = s;
+  }
+  lds_barrier();
+#pragma unroll
+  for (int u = 0; u < 64 * 64 / kNT; ++u) {   // dM = dT Diag(beta)
+    const int e = t + u * kNT;
+    const int r = e >> 6, c = e & 63;
+    sX[r * kL64 + c] *= sb[c];
+  }
+  lds_barrier();
+  {
+    f4 atm[2];
+    zero(atm);
+    mm<64, 64, 64, true, true>(atm, sX, kL64, sM, kL64, w);   // dM M^T
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      int m0, n0;
+      tile_origin<64>(w, s, m0, n0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sP[(m0 + 4 * g + q) * kL64 + n0 + li] = atm[s][q];
+    }
+  }
+  lds_barrier();
+  {
+    f4 ada[2], axx[2];
+    zero(ada);
+    zero(axx);
+    mm<64, 64, 64, false, false>(ada, sM, kL64, sP, kL64, w);   // M^T (dM M^T)
+    mm<64, 64, DK, true, true>(axx, R3, LD, R1, LD, w);          // Kr Kh^T
+    // dA = -M^T dM M^T (strictly lower); dbeta_r += sum_s dA_rs X_rs
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      int m0, n0;
+      tile_origin<64>(w, s, m0, n0);
+      float v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = m0 + 4 * g + q, c = n0 + li;
+        const float da = c < r ? -ada[s][q] : 0.f;
+        ada[s][q] = da;
+        v[q] = da * axx[s][q];
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float x = v[q];
+        x += __shfl_xor(x, 1);
+        x += __shfl_xor(x, 2);
+        x += __shfl_xor(x, 4);
+        x += __shfl_xor(x, 8);
+        if (li == 0) red[(n0 >> 4) * 64 + m0 + 4 * g + q] = x;
+      }
+    }
+    lds_barrier();
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      int m0, n0;
+      tile_origin<64>(w, s, m0, n0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = m0 + 4 * g + q;
+        sX[r * kL64 + n0 + li] = sb[r] * ada[s][q];
+      }
+    }
+    if (t < 64) sdb[t] += red[t] + red[64 + t] + red[128 + t] + red[192 + t];
+  }
+  lds_barrier();
+
+  // 6. AR += B Kh;  AH += B^T Kr  (B = Diag(beta) dA)
+  mm<64, DK, 64, true, false>(ar, sX, kL64, R1, LD, w);
+  mm<64, DK, 64, false, false>(ah, sX, kL64, R3, LD, w);
+
+  // 7. dq, dk; dg = AQ Qr + AR Kr - AH Kh (+ gamma_C's gradient on the last row)
+  float dgv[NT4][4];
+#pragma unroll
+  for (int s = 0; s < NT4; ++s) {
+    if (!tile_live<64, DK>(w, s)) break;
+    int m0, n0;
+    tile_origin<DK>(w, s, m0, n0);
+    const int c = n0 + li;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = m0 + 4 * g + q;
+      const float rh = rho[r * DK + c];
+      const float kr = R3[r * LD + c], kh = R1[r * LD + c], qr = R2[r * LD + c];
+      float dg = aq[s][q] * qr + ar[s][q] * kr - ah[s][q] * kh;
+      if (r == kC - 1) dg += sdgc[c];
+      dgv[s][q] = dg;
+      if (r < nv) {
+        const int64_t x = ((ck.tok0 + r) * H + h) * int64_t(DK) + c;
+        p.dq[x] = aq[s][q] * rh;
+        p.dk[x] = ar[s][q] * rh + ah[s][q] / rh;
+      }
+    }
+  }
+  lds_barrier();
+#pragma unroll
+  for (int s = 0; s < NT4; ++s) {
+    if (!tile_live<64, DK>(w, s)) break;
+    int m0, n0;
+    tile_origin<DK>(w, s, m0, n0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) R2[(m0 + 4 * g + q) * LD + n0 + li] = dgv[s][q];
+  }
+  if (t < 64 && t < nv) p.dbeta[(ck.tok0 + t) * H + h] = sdb[t];
+  lds_barrier();
+  // 8. dlog(alpha)_t = sum_{r >= t} dg_r within the chunk; dalpha = that / alpha
+  if (t < DK) {
+    float s = 0.f;
+    for (int r = kC - 1; r >= 0; --r) {
+      s += R2[r * LD + t];
+      R2[r * LD + t] = s;
+    }
+  }
+  lds_barrier();
+  if constexpr (SG) {
+    if (t < 64 && t < nv) {
+      float s = 0.f;
+      for (int c = 0; c < DK; ++c) s += R2[t * LD + c];
+      const int64_t row = (ck.tok0 + t) * H + h;
+      p.dalpha[row] = s / p.alpha[row];
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < 64 * DK / kNT; ++u) {
+      const int e = t + u * kNT;
+      const int r = e / DK, c = e % DK;
+      if (r < nv) {
+        const int64_t x = ((ck.tok0 + r) * H + h) * int64_t(DK) + c;
+        p.dalpha[x] = R2[r * LD + c] / p.alpha[x];
+      }
+    }
+  }
 }
 
 template <int DK, bool BF16, bool SG>
-void launch_bwd_t(const BackwardArgs& a, hipStream_t st) {
-  const unsigned nb = unsigned(int64_t(a.N) * a.H * (a.DV / kVS));
-  hipLaunchKernelGGL((kda_bwd_kernel<DK, BF16, SG>), dim3(nb), dim3(kNT), 0, st, a);
-  if (a.rows == 0) return;   // no tokens: only d_state_in (= d_state_out) is written
-  const int64_t threads = a.part_rows * DK;
-  const dim3 grid(unsigned((threads + 255) / 256));
-  const dim3 grid_g(unsigned((a.part_rows + 3) / 4));
-  if (a.DV == 128) {
-    hipLaunchKernelGGL((kda_bwd_reduce_kernel<DK, 8, SG>), grid, dim3(256), 0, st, a);
-    if (SG) hipLaunchKernelGGL((kda_bwd_dgate_kernel<DK, 8>), grid_g, dim3(256), 0, st, a);
+void launch_t(const BwdChunkArgs& a, int stage, hipStream_t st) {
+  const unsigned nchunk = unsigned(int64_t(a.N) * a.win_k * a.H);
+  if (stage == 0) {
+    hipLaunchKernelGGL((kda_bwdc_prep_kernel<DK, BF16, SG>), dim3(nchunk), dim3(kNT), 0, st, a);
+  } else if (stage == 1) {
+    const unsigned nb = unsigned(int64_t(a.N) * a.H * (a.DV / 16));
+    hipLaunchKernelGGL((kda_bwdc_chain_kernel<DK>), dim3(nb), dim3(64 * (DK / 16)), 0, st, a);
   } else {
-    hipLaunchKernelGGL((kda_bwd_reduce_kernel<DK, 4, SG>), grid, dim3(256), 0, st, a);
-    if (SG) hipLaunchKernelGGL((kda_bwd_dgate_kernel<DK, 4>), grid_g, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((kda_bwdc_post_kernel<DK, BF16, SG>), dim3(nchunk), dim3(kNT), 0, st, a);
+  }
+}
+
+template <int DK>
+void launch_dk(const BwdChunkArgs& a, int stage, hipStream_t st) {
+  if (a.alpha_scalar) {
+    if (a.in_bf16) launch_t<DK, true, true>(a, stage, st);
+    else launch_t<DK, false, true>(a, stage, st);
+  } else {
+    if (a.in_bf16) launch_t<DK, true, false>(a, stage, st);
+    else launch_t<DK, false, false>(a, stage, st);
   }
 }
 
 }  // namespace
 
-size_t backward_scratch_bytes(int N, int H, int DK, int DV) {
-  return size_t(N) * H * (DV / kVS) * 2 * size_t(kC) * DK * kVS * 4;
+size_t backward_chunk_floats(int DK, int DV) {
+  // A_c, b_c, dS', M, Vn, rho (+ gamma_m) per chunk-head
+  return size_t(DK) * DK + 2 * size_t(DK) * DV + 64 * 64 + 64 * size_t(DV) + 65 * size_t(DK);
 }
 
-int launch_backward(const BackwardArgs& a, void* stream, const char** msg) {
+int launch_backward_chunk(const BwdChunkArgs& a, int stage, void* stream, const char** msg) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  if (a.DK == 128) {
-    if (a.alpha_scalar) {
-      if (a.in_bf16) launch_bwd_t<128, true, true>(a, st);
-      else launch_bwd_t<128, false, true>(a, st);
-    } else {
-      if (a.in_bf16) launch_bwd_t<128, true, false>(a, st);
-      else launch_bwd_t<128, false, false>(a, st);
-    }
-  } else if (a.DK == 64) {
-    if (a.alpha_scalar) {
-      if (a.in_bf16) launch_bwd_t<64, true, true>(a, st);
-      else launch_bwd_t<64, false, true>(a, st);
-    } else {
-      if (a.in_bf16) launch_bwd_t<64, true, false>(a, st);
-      else launch_bwd_t<64, false, false>(a, st);
-    }
-  } else {
+  if (a.DK == 128) launch_dk<128>(a, stage, st);
+  else if (a.DK == 64) launch_dk<64>(a, stage, st);
+  else {
     *msg = "unsupported DK";
     return 1;
   }

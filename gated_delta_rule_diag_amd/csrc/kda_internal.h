@@ -65,47 +65,12 @@ struct PoolDecodeArgs {
   bool alpha_scalar;           // alpha is [N, L, H]
 };
 
-// Backward pass (fixed-length batches, per-channel alpha).
-struct BackwardArgs {
-  int N, H, DK, DV;
-  int64_t T;                   // tokens per sequence (fixed length)
-  const int32_t* cu_seqlens;   // packed sequences: device [N + 1] (then T is unused), or nullptr
-  int64_t rows;                // token rows: N * T * H, or T_total * H when packed
-  bool in_bf16;
-  bool alpha_scalar;           // alpha and dalpha are [rows] (one gate per token-head)
-  int64_t win_lo, win_k;       // this launch: chunks with reverse index win_lo .. win_lo + win_k - 1
-  int64_t part_rows;           // rows of the window's partial sums: N * win_k * 64 * H
-  float* g_carry;              // [N, H, DK, DV]: the adjoint between windows (several windows only)
-  const void* q;
-  const void* k;
-  const void* v;
-  const float* alpha;
-  const float* beta;
-  const float* state_in;       // [N, H, DK, DV] or nullptr
-  const float* d_o;            // [N, T, H, DV]
-  const float* d_state_out;    // [N, H, DK, DV] or nullptr
-  const float* snapshots;      // state after every chunk: [N, snap_per_seq, H, DK, DV]; packed:
-                               // chunk j of the sequence starting at token s is row s / 64 + j
-  int64_t snap_per_seq;        // T / 64
-  float* dq;                   // [N, T, H, DK]
-  float* dk;
-  float* dv;                   // [N, T, H, DV]
-  float* dalpha;               // [N, T, H, DK]
-  float* dbeta;                // [N, T, H]
-  float* d_state_in;           // [N, H, DK, DV] or nullptr
-  float* scratch;              // backward_scratch_bytes()
-  float* part_dq;              // [DV / 16][rows][DK] each
-  float* part_dk;
-  float* part_da;
-  float* part_db;              // [DV / 16][rows]
-};
-
-// The backward in chunk form: three launches per window of chunks (stage 0 =
+// Backward pass in chunk form: three launches per window of chunks (stage 0 =
 // per-chunk matrices, 1 = the adjoint's pass over the chunks, 2 = per-chunk
 // gradients).  Window buffers hold, per chunk-head of the window (index
 // (n * H + h) * win_k + j, j = reverse index within the window):
-//   Ac [DK][DK] (columns permuted for the chain), bc [DK][DV], dSend [DK][DV],
-//   Mb [64][64], Vnb [64][DV], rho [65][DK] (row 64: gamma_m).
+//   Ac [DK][DK], bc [DK][DV], dSend [DK][DV] (these three in the pass's
+//   fragment order), Mb [64][64], Vnb [64][DV], rho [65][DK] (row 64: gamma_m).
 struct BwdChunkArgs {
   int N, H, DK, DV;
   int64_t T;                   // tokens per sequence (fixed length)
@@ -121,7 +86,9 @@ struct BwdChunkArgs {
   const float* state_in;
   const float* d_o;
   const float* d_state_out;
-  const float* snapshots;      // as in BackwardArgs
+  const float* snapshots;      // state after every full chunk: [N, T / 64, H, DK, DV];
+                               // packed: chunk j of the sequence starting at token s is
+                               // row s / 64 + j
   float* dq;
   float* dk;
   float* dv;
@@ -141,10 +108,8 @@ struct BwdChunkArgs {
 int launch_prefill(const PrefillArgs& a, void* stream, const char** msg);
 int launch_decode(const DecodeArgs& a, void* stream, const char** msg);
 int launch_decode_pool(const PoolDecodeArgs& a, void* stream, const char** msg);
-int launch_backward(const BackwardArgs& a, void* stream, const char** msg);
 int launch_backward_chunk(const BwdChunkArgs& a, int stage, void* stream, const char** msg);
 size_t backward_chunk_floats(int DK, int DV);   // window-buffer floats per chunk-head
-size_t backward_scratch_bytes(int N, int H, int DK, int DV);
 size_t prefill_workspace_bytes(int N, int64_t T_total, int H, int DK, int DV, bool varlen);
 
 }  // namespace kda

@@ -262,15 +262,17 @@ kda_status_t kda_decode_pool(int N, int L, int H, int DK, int DV, kda_dtype_t in
  *   workspace    at least kda_chunk_backward_workspace_size() bytes, 16-byte
  *                aligned, not overlapping any argument (holds the forward's
  *                chunk-boundary states and outputs, DV + DK DV / 64 floats per
- *                token-head; the per-slab partial sums of the reverse pass, at
- *                most 4 GiB: the chunks are processed in windows sized for that;
- *                1 MiB per (sequence, head, 16 value columns) of token states;
- *                one state per (sequence, head) when there are several windows).
+ *                token-head; per chunk-head of a window of chunks
+ *                DK^2 + 2 DK DV + 64 DV + 65 DK + 4096 floats (279 KB at
+ *                d = 128), the windows sized to keep this at most 4 GiB; one
+ *                state per (sequence, head) when there are several windows).
  * Outputs must not overlap inputs or each other.  The forward is recomputed
- * (with a state checkpoint per chunk); the reverse pass walks every chunk
- * backwards from its checkpoint; the result is deterministic.  With T == 0
- * only d_state_in is written (= d_state_out, or zeros) and no workspace is
- * needed.
+ * (with a state checkpoint per chunk).  The reverse pass is in chunk form: the
+ * adjoint of the state at every chunk boundary comes from one sequential pass
+ * over the chunks (an affine map per chunk), then every chunk's gradients are
+ * computed independently from its checkpoint.  The result is deterministic.
+ * With T == 0 only d_state_in is written (= d_state_out, or zeros) and no
+ * workspace is needed.
  */
 size_t kda_chunk_backward_workspace_size(int B, int T, int H, int DK, int DV, int chunk);
 kda_status_t kda_chunk_backward(int B, int T, int H, int DK, int DV, int chunk,

@@ -260,12 +260,12 @@ def test_scalar_gate_argument_errors(lib):
 def test_backward_argument_errors(lib):
     # B=1, T=64, H=2, d=64 (f32): rows = 128
     need = lib.kda_chunk_backward_workspace_size(1, 64, 2, 64, 64, 64)
-    # partial sums (3 * 4 slabs * 128 rows * 64 + 4 * 128) floats, o of the
-    # forward, one snapshot per sequence-head, and per workgroup (8 of them) the
-    # token states of two chunks: 2 * 64 tokens * 64 rows * 16 columns floats
-    part = (3 * 4 * 128 * 64 + 4 * 128) * 4
+    # the window buffers of one chunk for the 2 heads (A_c, b_c, dS', M, Vn and
+    # the 65 rows of decays: 64^2 + 2 * 64^2 + 64^2 + 64 * 64 + 65 * 64 floats
+    # each), o of the forward, one snapshot per sequence-head
     al = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    assert need == al(part) + al(128 * 64 * 4) + al(2 * 64 * 64 * 4) + al(8 * 2 * 64 * 64 * 16 * 4)
+    win = 2 * (5 * 64 * 64 + 65 * 64) * 4
+    assert need == al(win) + al(128 * 64 * 4) + al(2 * 64 * 64 * 4)
     assert lib.kda_chunk_backward_workspace_size(1, 64, 2, 96, 64, 64) == 0
     big = ctypes.c_void_p(0x40000000)
     Q = [ctypes.c_void_p(0x100000 * (i + 1)) for i in range(14)]
@@ -296,15 +296,14 @@ def test_backward_argument_errors(lib):
 
 def test_backward_varlen_argument_errors(lib, monkeypatch):
     # N=3 sequences, T_total=200 tokens, longest 100, H=2, d=64 (f32): the
-    # reverse pass's partial sums cover a window of chunks counted from each
-    # sequence's end, N * 64 * H * (3 DK + 1) * (DV / 16) floats per chunk of
-    # the window (at most 4 GiB, here every chunk: ceil(100 / 64) = 2); the
-    # forward's o; snapshot rows T_total // 64 = 3 (chunk j of the sequence
-    # starting at token s is row s // 64 + j); 3 * 2 * 4 slab workgroups of
-    # two-chunk token states
-    per_chunk = 3 * 64 * 2 * (3 * 64 + 1) * 4 * 4
+    # reverse pass's buffers cover a window of chunks counted from each
+    # sequence's end, N * H * (DK^2 + 2 DK DV + 64^2 + 64 DV + 65 DK) floats
+    # per chunk of the window (at most 4 GiB, here every chunk:
+    # ceil(100 / 64) = 2); the forward's o; snapshot rows T_total // 64 = 3
+    # (chunk j of the sequence starting at token s is row s // 64 + j)
+    per_chunk = 3 * 2 * (5 * 64 * 64 + 65 * 64) * 4
     al = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    rest = al(400 * 64 * 4) + al(3 * 2 * 64 * 64 * 4) + al(3 * 2 * 4 * 2 * 64 * 64 * 16 * 4)
+    rest = al(400 * 64 * 4) + al(3 * 2 * 64 * 64 * 4)
     need = lib.kda_chunk_backward_varlen_workspace_size(3, 200, 100, 2, 64, 64, 64)
     assert need == al(2 * per_chunk) + rest
     # max_seqlen unknown (0): T_total is assumed, 4 chunks
