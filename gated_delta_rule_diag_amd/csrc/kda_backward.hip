@@ -573,8 +573,9 @@ template <int DK, bool BF16, bool SG>
 __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
   constexpr int LD = DK + 4;
   constexpr int NT4 = (4 * (DK / 16) + kNW - 1) / kNW;   // 64 x DK tiles per wave
+  constexpr int RED = 4 * DK > kNT ? 4 * DK : kNT;
   __shared__ __attribute__((aligned(16))) float sm[3 * 64 * LD + 3 * 64 * kL64 + 3 * DK + 2 * 64 +
-                                                   4 * DK];
+                                                   RED];
   float* const R1 = sm;               // Kh
   float* const R2 = R1 + 64 * LD;     // slabs (with R3), then -dW', then Qr, then dg
   float* const R3 = R2 + 64 * LD;     // Qr (for P), slabs, then Kr
@@ -586,7 +587,7 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
   float* const sdgc = sgq + DK;
   float* const sb = sdgc + DK;
   float* const sdb = sb + 64;
-  float* const red = sdb + 64;        // [4][DK]
+  float* const red = sdb + 64;        // [4][DK] or [kNT] partial sums
   // slab buffers (inside R2 .. R3)
   float* const sO = R2;
   float* const sVn = sO + 64 * kLS;
@@ -810,7 +811,7 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
     for (int q = 0; q < 4; ++q) ar[s][q] *= sb[m0 + 4 * g + q];
   }
   lds_barrier();
-#pragma unroll 4
+#pragma unroll 8
   for (int u = 0; u < 64 * DK / kNT; ++u) {   // Qr
     const int e = t + u * kNT;
     const int r = e / DK, c = e % DK;
@@ -822,12 +823,20 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
   // 5. AH += dP^T Qr;  AQ += dP Kh;  dbeta from T
   mm<64, DK, 64, false, false>(ah, sP, kL64, R2, LD, w);
   mm<64, DK, 64, true, false>(aq, sP, kL64, R1, LD, w);
-  if (t < 64) {
+  {   // column sums of M o dT (M is lower triangular), 8 rows per thread
+    const int col = t & 63, part = t >> 6;
     float s = 0.f;
-    for (int r = t; r < 64; ++r) s += sM[r * kL64 + t] * sX[r * kL64 + t];
-    sdb[t] = s;
+#pragma unroll
+    for (int r = 8 * part; r < 8 * part + 8; ++r) s += sM[r * kL64 + col] * sX[r * kL64 + col];
+    red[part * 64 + col] = s;
   }
   lds_barrier();
+  if (t < 64) {
+    float s = 0.f;
+#pragma unroll
+    for (int part = 0; part < kNT / 64; ++part) s += red[part * 64 + t];
+    sdb[t] = s;
+  }
 #pragma unroll
   for (int u = 0; u < 64 * 64 / kNT; ++u) {   // dM = dT Diag(beta)
     const int e = t + u * kNT;
@@ -930,31 +939,49 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
   }
   if (t < 64 && t < nv) p.dbeta[(ck.tok0 + t) * H + h] = sdb[t];
   lds_barrier();
-  // 8. dlog(alpha)_t = sum_{r >= t} dg_r within the chunk; dalpha = that / alpha
-  if (t < DK) {
-    float s = 0.f;
-    for (int r = kC - 1; r >= 0; --r) {
-      s += R2[r * LD + t];
-      R2[r * LD + t] = s;
+  // 8. dlog(alpha)_t = sum_{r >= t} dg_r within the chunk; dalpha = that / alpha.
+  // Each channel's 64 rows in NP parts of RP rows: sums from the end within a
+  // part, plus the totals of the later parts.
+  constexpr int NP = kNT / DK, RP = 64 / NP;
+  {
+    const int c = t % DK, pp = t / DK;
+    float v[RP];
+    float run = 0.f;
+#pragma unroll
+    for (int i = RP - 1; i >= 0; --i) {
+      run += R2[(pp * RP + i) * LD + c];
+      v[i] = run;
+    }
+    red[pp * DK + c] = run;
+    lds_barrier();
+    float off = 0.f;
+    for (int q2 = pp + 1; q2 < NP; ++q2) off += red[q2 * DK + c];
+    if constexpr (SG) {
+#pragma unroll
+      for (int i = 0; i < RP; ++i) R2[(pp * RP + i) * LD + c] = v[i] + off;
+    } else {
+#pragma unroll
+      for (int i = 0; i < RP; ++i) {
+        const int r = pp * RP + i;
+        if (r < nv) {
+          const int64_t x = ((ck.tok0 + r) * H + h) * int64_t(DK) + c;
+          p.dalpha[x] = (v[i] + off) / p.alpha[x];
+        }
+      }
     }
   }
-  lds_barrier();
-  if constexpr (SG) {
-    if (t < 64 && t < nv) {
-      float s = 0.f;
-      for (int c = 0; c < DK; ++c) s += R2[t * LD + c];
-      const int64_t row = (ck.tok0 + t) * H + h;
-      p.dalpha[row] = s / p.alpha[row];
-    }
-  } else {
+  if constexpr (SG) {   // one gate per token: the sum over the channels, 8 threads per row
+    lds_barrier();
+    const int r = t >> 3, part = t & 7;
+    float s = 0.f;
 #pragma unroll
-    for (int u = 0; u < 64 * DK / kNT; ++u) {
-      const int e = t + u * kNT;
-      const int r = e / DK, c = e % DK;
-      if (r < nv) {
-        const int64_t x = ((ck.tok0 + r) * H + h) * int64_t(DK) + c;
-        p.dalpha[x] = R2[r * LD + c] / p.alpha[x];
-      }
+    for (int c = part * (DK / 8); c < (part + 1) * (DK / 8); ++c) s += R2[r * LD + c];
+    s += __shfl_xor(s, 1);
+    s += __shfl_xor(s, 2);
+    s += __shfl_xor(s, 4);
+    if (part == 0 && r < nv) {
+      const int64_t row = (ck.tok0 + r) * H + h;
+      p.dalpha[row] = s / p.alpha[row];
     }
   }
 }
