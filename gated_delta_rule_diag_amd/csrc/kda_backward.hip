@@ -749,7 +749,18 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
   }
 
   // 3. gamma_C's gradient: the column sums of dKend' * Kh plus sum_j S dS'
-  // gamma_C, both in the scaled forms.  dP, dT, -dW' to LDS.
+  // gamma_C, both in the scaled forms.  dP, dT, -dW' to LDS.  The inputs of
+  // Kr and Qr (rebuilt below) are loaded first, so that their latency overlaps
+  // this work.
+  constexpr int NE = 64 * DK / kNT;
+  float pk[NE], pr[NE];
+#pragma unroll
+  for (int u = 0; u < NE; ++u) {
+    const int e = t + u * kNT;
+    const int r = e / DK, c = e % DK;
+    pk[u] = r < nv ? ld_in<BF16>(p.k, ((ck.tok0 + r) * H + h) * int64_t(DK) + c) : 0.f;
+    pr[u] = rho[e];
+  }
 #pragma unroll
   for (int s = 0; s < NT4; ++s) {
     if (!tile_live<64, DK>(w, s)) break;
@@ -777,16 +788,21 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
   }
   lds_barrier();
   if (t < DK) sdgc[t] = red[t] + red[DK + t] + red[2 * DK + t] + red[3 * DK + t] + dgcs;
-#pragma unroll 4
-  for (int u = 0; u < 64 * DK / kNT; ++u) {   // Kr
+#pragma unroll
+  for (int u = 0; u < NE; ++u) {   // Kr
     const int e = t + u * kNT;
-    const int r = e / DK, c = e % DK;
-    const float kv = r < nv ? ld_in<BF16>(p.k, ((ck.tok0 + r) * H + h) * int64_t(DK) + c) : 0.f;
-    R3[r * LD + c] = kv * rho[e];
+    R3[(e / DK) * LD + e % DK] = pk[u] * pr[u];
   }
   lds_barrier();
 
   // 4. dT += dW' Kr^T;  AR = Diag(beta) M^T dW'
+  float pq[NE];
+#pragma unroll
+  for (int u = 0; u < NE; ++u) {
+    const int e = t + u * kNT;
+    const int r = e / DK, c = e % DK;
+    pq[u] = r < nv ? ld_in<BF16>(p.q, ((ck.tok0 + r) * H + h) * int64_t(DK) + c) : 0.f;
+  }
   f4 ar[NT4];
   zero(ar);
   {
@@ -811,12 +827,10 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
     for (int q = 0; q < 4; ++q) ar[s][q] *= sb[m0 + 4 * g + q];
   }
   lds_barrier();
-#pragma unroll 8
-  for (int u = 0; u < 64 * DK / kNT; ++u) {   // Qr
+#pragma unroll
+  for (int u = 0; u < NE; ++u) {   // Qr
     const int e = t + u * kNT;
-    const int r = e / DK, c = e % DK;
-    const float qv = r < nv ? ld_in<BF16>(p.q, ((ck.tok0 + r) * H + h) * int64_t(DK) + c) : 0.f;
-    R2[r * LD + c] = qv * rho[e];
+    R2[(e / DK) * LD + e % DK] = pq[u] * pr[u];
   }
   lds_barrier();
 
@@ -901,7 +915,30 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
   }
   lds_barrier();
 
-  // 6. AR += B Kh;  AH += B^T Kr  (B = Diag(beta) dA)
+  // 6. AR += B Kh;  AH += B^T Kr  (B = Diag(beta) dA).  The decays of this
+  // lane's output elements and the alphas of step 8 are loaded first.
+  float rh[NT4][4];
+#pragma unroll
+  for (int s = 0; s < NT4; ++s) {
+    int m0, n0;
+    tile_origin<DK>(w, s, m0, n0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      rh[s][q] = tile_live<64, DK>(w, s) ? rho[(m0 + 4 * g + q) * DK + n0 + li] : 1.f;
+  }
+  constexpr int NP = kNT / DK, RP = 64 / NP;
+  float al[SG ? 1 : RP];
+  if constexpr (SG) {
+    const int r = t >> 3;
+    al[0] = r < nv ? p.alpha[(ck.tok0 + r) * H + h] : 1.f;
+  } else {
+    const int c = t % DK, pp = t / DK;
+#pragma unroll
+    for (int i = 0; i < RP; ++i) {
+      const int r = pp * RP + i;
+      al[i] = r < nv ? p.alpha[((ck.tok0 + r) * H + h) * int64_t(DK) + c] : 1.f;
+    }
+  }
   mm<64, DK, 64, true, false>(ar, sX, kL64, R1, LD, w);
   mm<64, DK, 64, false, false>(ah, sX, kL64, R3, LD, w);
 
@@ -916,15 +953,14 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int r = m0 + 4 * g + q;
-      const float rh = rho[r * DK + c];
       const float kr = R3[r * LD + c], kh = R1[r * LD + c], qr = R2[r * LD + c];
       float dg = aq[s][q] * qr + ar[s][q] * kr - ah[s][q] * kh;
       if (r == kC - 1) dg += sdgc[c];
       dgv[s][q] = dg;
       if (r < nv) {
         const int64_t x = ((ck.tok0 + r) * H + h) * int64_t(DK) + c;
-        p.dq[x] = aq[s][q] * rh;
-        p.dk[x] = ar[s][q] * rh + ah[s][q] / rh;
+        p.dq[x] = aq[s][q] * rh[s][q];
+        p.dk[x] = ar[s][q] * rh[s][q] + ah[s][q] / rh[s][q];
       }
     }
   }
@@ -942,7 +978,6 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
   // 8. dlog(alpha)_t = sum_{r >= t} dg_r within the chunk; dalpha = that / alpha.
   // Each channel's 64 rows in NP parts of RP rows: sums from the end within a
   // part, plus the totals of the later parts.
-  constexpr int NP = kNT / DK, RP = 64 / NP;
   {
     const int c = t % DK, pp = t / DK;
     float v[RP];
@@ -965,7 +1000,7 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
         const int r = pp * RP + i;
         if (r < nv) {
           const int64_t x = ((ck.tok0 + r) * H + h) * int64_t(DK) + c;
-          p.dalpha[x] = (v[i] + off) / p.alpha[x];
+          p.dalpha[x] = (v[i] + off) / al[i];
         }
       }
     }
@@ -981,7 +1016,7 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
     s += __shfl_xor(s, 4);
     if (part == 0 && r < nv) {
       const int64_t row = (ck.tok0 + r) * H + h;
-      p.dalpha[row] = s / p.alpha[row];
+      p.dalpha[row] = s / al[0];
     }
   }
 }
