@@ -258,22 +258,30 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_prep_kernel(BwdChunkArgs p) {
   if (!locate(p, n, jw, h, ck)) return;
   const int nv = ck.nv;
 
-  // 1. decays, scaled keys and queries, beta
+  // 1. decays, scaled keys and queries, beta (the keys and queries are loaded
+  // before the decays' products, so that both latencies overlap)
+  constexpr int NE = 64 * DK / kNT;
+  float pk[NE], pq[NE];
+#pragma unroll
+  for (int u = 0; u < NE; ++u) {
+    const int e = t + u * kNT;
+    const int r = e / DK, c = e % DK;
+    const int64_t x = ((ck.tok0 + r) * H + h) * int64_t(DK) + c;
+    pk[u] = r < nv ? ld_in<BF16>(p.k, x) : 0.f;
+    pq[u] = r < nv ? ld_in<BF16>(p.q, x) : 0.f;
+  }
   float* const rho_g = p.rho + ck.wi * (65 * DK);
   decays<DK, SG>(p, ck, sQr, LD, rho_g, sgm, sgq);   // rho parked in sQr
   if (t < 64) sb[t] = t < nv ? p.beta[(ck.tok0 + t) * H + h] : 0.f;
   lds_barrier();
 #pragma unroll
-  for (int u = 0; u < 64 * DK / kNT; ++u) {
+  for (int u = 0; u < NE; ++u) {
     const int e = t + u * kNT;
     const int r = e / DK, c = e % DK;
     const float rh = sQr[r * LD + c];
-    const int64_t x = ((ck.tok0 + r) * H + h) * int64_t(DK) + c;
-    const float kv = r < nv ? ld_in<BF16>(p.k, x) : 0.f;
-    const float qv = r < nv ? ld_in<BF16>(p.q, x) : 0.f;
-    sKr[r * LD + c] = kv * rh;
-    sKh[r * LD + c] = kv / rh;
-    sQr[r * LD + c] = qv * rh;
+    sKr[r * LD + c] = pk[u] * rh;
+    sKh[r * LD + c] = pk[u] / rh;
+    sQr[r * LD + c] = pq[u] * rh;
   }
   lds_barrier();
 
@@ -358,6 +366,36 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_prep_kernel(BwdChunkArgs p) {
   }
   lds_barrier();
 
+  // Inputs of the value-column loop (step 7); the first slab is fetched here,
+  // ahead of steps 5 and 6.
+  const float* const S = chunk_state<DK>(p, ck);
+  float* const Vng = p.Vnb + ck.wi * (64 * int64_t(DV));
+  float* const bg = p.bc + ck.wi * (int64_t(DK) * DV);
+  // (the next slab's inputs are fetched into registers during this slab's
+  // products; past the last slab the last one is fetched again)
+  constexpr int NR = 64 * 16 / kNT, NS = DK * 16 / kNT;
+  struct Slab {
+    float v[NR], o[NR], s[NS];
+  };
+  auto fetch = [&](Slab& R, int js) {
+    if (js >= DV / 16) js = DV / 16 - 1;
+#pragma unroll
+    for (int u = 0; u < NR; ++u) {
+      const int e = t + u * kNT;
+      const int r = e >> 4, j = e & 15;
+      const int64_t x = ((ck.tok0 + r) * H + h) * int64_t(DV) + 16 * js + j;
+      R.v[u] = r < nv ? ld_in<BF16>(p.v, x) : 0.f;
+      R.o[u] = r < nv ? p.d_o[x] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      const int e = t + u * kNT;
+      R.s[u] = S ? S[int64_t(e >> 4) * DV + 16 * js + (e & 15)] : 0.f;
+    }
+  };
+  Slab R;
+  fetch(R, 0);
+
   // 5. W = T Kr Diag(gamma_m), over Kr
   {
     f4 aw[NTW];
@@ -400,33 +438,6 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_prep_kernel(BwdChunkArgs p) {
   }
 
   // 7. per 16 value columns: Vn = T V - W S;  b_c = Diag(gamma_m) Qr^T dO - W^T (P^T dO)
-  const float* const S = chunk_state<DK>(p, ck);
-  float* const Vng = p.Vnb + ck.wi * (64 * int64_t(DV));
-  float* const bg = p.bc + ck.wi * (int64_t(DK) * DV);
-  // (the next slab's inputs are fetched into registers during this slab's
-  // products; past the last slab the last one is fetched again)
-  constexpr int NR = 64 * 16 / kNT, NS = DK * 16 / kNT;
-  struct Slab {
-    float v[NR], o[NR], s[NS];
-  };
-  auto fetch = [&](Slab& R, int js) {
-    if (js >= DV / 16) js = DV / 16 - 1;
-#pragma unroll
-    for (int u = 0; u < NR; ++u) {
-      const int e = t + u * kNT;
-      const int r = e >> 4, j = e & 15;
-      const int64_t x = ((ck.tok0 + r) * H + h) * int64_t(DV) + 16 * js + j;
-      R.v[u] = r < nv ? ld_in<BF16>(p.v, x) : 0.f;
-      R.o[u] = r < nv ? p.d_o[x] : 0.f;
-    }
-#pragma unroll
-    for (int u = 0; u < NS; ++u) {
-      const int e = t + u * kNT;
-      R.s[u] = S ? S[int64_t(e >> 4) * DV + 16 * js + (e & 15)] : 0.f;
-    }
-  };
-  Slab R;
-  fetch(R, 0);
   for (int js = 0; js < DV / 16; ++js) {
 #pragma unroll
     for (int u = 0; u < NR; ++u) {
@@ -607,6 +618,39 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
   const int nv = ck.nv;
   const float* const rho = p.rho + ck.wi * (65 * DK);
 
+  // Inputs of the value-column loop (step 2); the first slab is fetched here,
+  // ahead of step 1.
+  const float* const S = chunk_state<DK>(p, ck);
+  const float* const dSe = p.dSend + ck.wi * (int64_t(DK) * DV);
+  const float* const Vng = p.Vnb + ck.wi * (64 * int64_t(DV));
+  // The next slab's operands are fetched into registers during this slab's
+  // products (past the last slab the last one is fetched again).
+  constexpr int NR = 64 * 16 / kNT, NS = DK * 16 / kNT;
+  struct Slab {
+    float o[NR], v[NR], vn[NR], s[NS];
+    f4 d;   // dS' of rows 16 (t / 64) + 4 g .. + 3, column t % 16 (t < 4 DK)
+  };
+  auto fetch = [&](Slab& R, int js) {
+    if (js >= DV / 16) js = DV / 16 - 1;
+#pragma unroll
+    for (int u = 0; u < NR; ++u) {
+      const int e = t + u * kNT;
+      const int r = e >> 4, j = e & 15;
+      const int64_t x = ((ck.tok0 + r) * H + h) * int64_t(DV) + 16 * js + j;
+      R.o[u] = r < nv ? p.d_o[x] : 0.f;
+      R.v[u] = r < nv ? ld_in<BF16>(p.v, x) : 0.f;
+      R.vn[u] = Vng[r * DV + 16 * js + j];
+    }
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      const int e = t + u * kNT;
+      R.s[u] = S ? S[int64_t(e >> 4) * DV + 16 * js + (e & 15)] : 0.f;
+    }
+    if (t < DK * 4) R.d = *reinterpret_cast<const f4*>(dSe + frag_s<DK>(js, t >> 6, t & 63));
+  };
+  Slab R;
+  fetch(R, 0);
+
   // 1. decay factors, beta, Kh, Qr, M
   if (t < DK) {
     sgm[t] = rho[kC * DK + t];
@@ -658,36 +702,6 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
   zero(adp);
   zero(adt);
   float dgcs = 0.f;
-  const float* const S = chunk_state<DK>(p, ck);
-  const float* const dSe = p.dSend + ck.wi * (int64_t(DK) * DV);
-  const float* const Vng = p.Vnb + ck.wi * (64 * int64_t(DV));
-  // The next slab's operands are fetched into registers during this slab's
-  // products (past the last slab the last one is fetched again).
-  constexpr int NR = 64 * 16 / kNT, NS = DK * 16 / kNT;
-  struct Slab {
-    float o[NR], v[NR], vn[NR], s[NS];
-    f4 d;   // dS' of rows 16 (t / 64) + 4 g .. + 3, column t % 16 (t < 4 DK)
-  };
-  auto fetch = [&](Slab& R, int js) {
-    if (js >= DV / 16) js = DV / 16 - 1;
-#pragma unroll
-    for (int u = 0; u < NR; ++u) {
-      const int e = t + u * kNT;
-      const int r = e >> 4, j = e & 15;
-      const int64_t x = ((ck.tok0 + r) * H + h) * int64_t(DV) + 16 * js + j;
-      R.o[u] = r < nv ? p.d_o[x] : 0.f;
-      R.v[u] = r < nv ? ld_in<BF16>(p.v, x) : 0.f;
-      R.vn[u] = Vng[r * DV + 16 * js + j];
-    }
-#pragma unroll
-    for (int u = 0; u < NS; ++u) {
-      const int e = t + u * kNT;
-      R.s[u] = S ? S[int64_t(e >> 4) * DV + 16 * js + (e & 15)] : 0.f;
-    }
-    if (t < DK * 4) R.d = *reinterpret_cast<const f4*>(dSe + frag_s<DK>(js, t >> 6, t & 63));
-  };
-  Slab R;
-  fetch(R, 0);
   for (int js = 0; js < DV / 16; ++js) {
 #pragma unroll
     for (int u = 0; u < NR; ++u) {
