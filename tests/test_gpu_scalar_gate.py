@@ -164,3 +164,29 @@ def test_scalar_gate_backward_varlen_matches_oracle(dt, d):
     errs = {n: max_rel_err(x, r) for n, x, r in zip(GRADS, got, ref)}
     flush("    " + " ".join(f"{n}={e:.1e}" for n, e in errs.items()))
     assert max(errs.values()) <= TOL[dt], errs
+
+
+@pytest.mark.parametrize("window", ["1", "2"])
+def test_scalar_gate_backward_varlen_windows_are_exact(window, monkeypatch):
+    """A scalar gate with the reverse pass in windows of 1 or 2 chunks: bit for
+    bit the single-window result (the adjoint carried between windows, the
+    gate's gradient summed over the channels within each chunk)."""
+    lengths = [150, 0, 64, 3, 129]
+    H, d = 2, 64
+    flush(f"[scalar gate] backward varlen windows of {window} chunks lengths={lengths}")
+    q, k, v, a, b, cu = I.packed_inputs(650, lengths, H, d, d, "bf16")
+    g = gate_of(a)
+    rng = np.random.default_rng(651)
+    do = rng.standard_normal((int(cu[-1]), H, d)).astype(np.float32)
+    S0 = random_state(rng, (len(lengths), H, d, d))
+    dST = random_state(rng, (len(lengths), H, d, d))
+    td = tdtype("bf16")
+    x = (dev(q, td), dev(k, td), dev(v, td), dev(g), dev(b), torch.from_numpy(cu).cuda(), dev(do),
+         dev(S0), dev(dST))
+    ref = kda.chunk_backward_varlen(*x)
+    monkeypatch.setenv("KDA_BWD_WINDOW", window)
+    got = kda.chunk_backward_varlen(*x, max_seqlen=max(lengths))
+    monkeypatch.delenv("KDA_BWD_WINDOW")
+    torch.cuda.synchronize()
+    for n, u, w in zip(GRADS, got, ref):
+        assert torch.equal(u, w), n
