@@ -313,6 +313,11 @@ def main():
             "decode_pool_512_slots_L4_us": pool4_us,
             "decode_pool_512_slots_L4_us_per_token": pool4_us / L4,
             "backward_b1_h32_t8192_us": bwd_us,
+            # algorithmic bytes of a backward call: q, k, v (bf16), alpha, beta,
+            # d_o in; dq, dk, dalpha, dv, dbeta out (3,848 B per token-head at d=128)
+            "backward_b1_h32_t8192_hbm_frac": B * T * H * (3 * D * 2 + 4 * D + 4 + 4 * D
+                                                           + 3 * 4 * D + 4 * D + 4)
+            / (bwd_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
             "backward_scalar_gate_b1_h32_t8192_us": bwd_sg_us,
             "decode_n1_h32_eager_us_per_step": n1_eager_us,
             "decode_n1_h32_hip_graph_us_per_step": n1_graph_us,

@@ -71,7 +71,10 @@ __device__ __forceinline__ float ld_in(const void* p, int64_t i) {
 // 4g + q of column i of its tile.  The fragments of KG blocks of K are loaded
 // before their products.  Triangular operands are stored with their zeros, so
 // the products run over the whole of K (exact zeros do not change a sum).
-template <int M, int N, int K, bool AK, bool BK, int NT>
+// TRI (used where the tiles' rows are known at compile time, N == 16 * kNW:
+// tile s starts at row 16 s) skips the blocks of K where a triangular A is
+// zero: 2 = A lower triangular (k <= m), 3 = A upper triangular (k >= m).
+template <int M, int N, int K, bool AK, bool BK, int NT, int TRI = 0>
 __device__ __forceinline__ void mm(f4 (&acc)[NT], const float* a, int lda, const float* b, int ldb,
                                    int wv) {
   constexpr int TN = N / 16, NTILE = (M / 16) * TN, KB = K / 16;
@@ -80,7 +83,12 @@ __device__ __forceinline__ void mm(f4 (&acc)[NT], const float* a, int lda, const
   constexpr int KG0 = NT >= 8 ? 1 : (NT >= 4 ? 2 : 4);
   constexpr int KG = KB < KG0 ? KB : KG0;
   static_assert(KB % KG == 0, "K blocks in whole groups");
+  static_assert(TRI == 0 || N / 16 == kNW, "triangular skips need compile-time tile rows");
   if (NTILE < kNW && wv >= NTILE) return;
+  // block k0 of tile s contributes (compile-time after unrolling)
+  auto need = [](int s, int k0) {
+    return TRI == 0 || (TRI == 2 && k0 <= 16 * s) || (TRI == 3 && k0 >= 16 * s);
+  };
   const int l = threadIdx.x & 63, i = l & 15, g = l >> 4;
   const int n0 = (wv % TN) * 16;
 #pragma unroll
@@ -89,6 +97,10 @@ __device__ __forceinline__ void mm(f4 (&acc)[NT], const float* a, int lda, const
 #pragma unroll
     for (int u = 0; u < KG; ++u) {
       const int k0 = 16 * (kg + u);
+      bool any = false;
+#pragma unroll
+      for (int s = 0; s < NT; ++s) any = any || need(s, k0);
+      if (!any) continue;
       if constexpr (BK) {
         bv[u] = *reinterpret_cast<const f4*>(b + (n0 + i) * ldb + k0 + 4 * g);
       } else {
@@ -97,6 +109,7 @@ __device__ __forceinline__ void mm(f4 (&acc)[NT], const float* a, int lda, const
       }
 #pragma unroll
       for (int s = 0; s < NT; ++s) {
+        if (!need(s, k0)) continue;
         const int m0 = ((wv + kNW * s) / TN) * 16;
         if constexpr (AK) {
           av[u][s] = *reinterpret_cast<const f4*>(a + (m0 + i) * lda + k0 + 4 * g);
@@ -109,12 +122,18 @@ __device__ __forceinline__ void mm(f4 (&acc)[NT], const float* a, int lda, const
 #pragma unroll
     for (int u = 0; u < KG; ++u)
 #pragma unroll
-      for (int s = 0; s < NT; ++s)
+      for (int s = 0; s < NT; ++s) {
+        if (!need(s, 16 * (kg + u))) continue;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           acc[s] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u][s][j], bv[u][j], acc[s], 0, 0, 0);
+      }
   }
 }
+
+// A triangular skip for products with DK output columns: only where a wave's
+// tiles have compile-time rows (DK == 16 * kNW).
+#define TRI_DK(t) (DK == 16 * kNW ? (t) : 0)
 
 template <int NT>
 __device__ __forceinline__ void zero(f4 (&acc)[NT]) {
@@ -400,7 +419,7 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_prep_kernel(BwdChunkArgs p) {
   {
     f4 aw[NTW];
     zero(aw);
-    mm<64, DK, 64, true, false>(aw, sM, kL64, sKr, LD, w);
+    mm<64, DK, 64, true, false, NTW, TRI_DK(2)>(aw, sM, kL64, sKr, LD, w);
     lds_barrier();
 #pragma unroll
     for (int s = 0; s < NTW; ++s) {
@@ -831,7 +850,7 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
       for (int q = 0; q < 4; ++q) sX[(m0 + 4 * g + q) * kL64 + n0 + li] += at[s][q];
     }
   }
-  mm<64, DK, 64, false, false>(ar, sM, kL64, R2, LD, w);
+  mm<64, DK, 64, false, false, NT4, TRI_DK(3)>(ar, sM, kL64, R2, LD, w);
 #pragma unroll
   for (int s = 0; s < NT4; ++s) {
     if (!tile_live<64, DK>(w, s)) break;
@@ -849,8 +868,8 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
   lds_barrier();
 
   // 5. AH += dP^T Qr;  AQ += dP Kh;  dbeta from T
-  mm<64, DK, 64, false, false>(ah, sP, kL64, R2, LD, w);
-  mm<64, DK, 64, true, false>(aq, sP, kL64, R1, LD, w);
+  mm<64, DK, 64, false, false, NT4, TRI_DK(3)>(ah, sP, kL64, R2, LD, w);
+  mm<64, DK, 64, true, false, NT4, TRI_DK(2)>(aq, sP, kL64, R1, LD, w);
   {   // column sums of M o dT (M is lower triangular), 8 rows per thread
     const int col = t & 63, part = t >> 6;
     float s = 0.f;
@@ -953,8 +972,8 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
       al[i] = r < nv ? p.alpha[((ck.tok0 + r) * H + h) * int64_t(DK) + c] : 1.f;
     }
   }
-  mm<64, DK, 64, true, false>(ar, sX, kL64, R1, LD, w);
-  mm<64, DK, 64, false, false>(ah, sX, kL64, R3, LD, w);
+  mm<64, DK, 64, true, false, NT4, TRI_DK(2)>(ar, sX, kL64, R1, LD, w);
+  mm<64, DK, 64, false, false, NT4, TRI_DK(3)>(ah, sX, kL64, R3, LD, w);
 
   // 7. dq, dk; dg = AQ Qr + AR Kr - AH Kh (+ gamma_C's gradient on the last row)
   float dgv[NT4][4];
