@@ -70,7 +70,7 @@ __device__ __forceinline__ float ld_in(const void* p, int64_t i) {
 // four products (lane i = row of A / column of B); the result lane holds rows
 // 4g + q of column i of its tile.  The fragments of KG blocks of K are loaded
 // before their products.  Triangular operands are stored with their zeros, so
-// the products run over the whole of K (exact zeros do not change a sum).
+// the products may run over the whole of K (exact zeros do not change a sum).
 // TRI (used where the tiles' rows are known at compile time, N == 16 * kNW:
 // tile s starts at row 16 s) skips the blocks of K where a triangular A is
 // zero: 2 = A lower triangular (k <= m), 3 = A upper triangular (k >= m).
