@@ -133,7 +133,10 @@ __device__ __forceinline__ void mm(f4 (&acc)[NT], const float* a, int lda, const
 
 // A triangular skip for products with DK output columns: only where a wave's
 // tiles have compile-time rows (DK == 16 * kNW).
-#define TRI_DK(t) (DK == 16 * kNW ? (t) : 0)
+template <int DK>
+constexpr int tri_dk(int t) {
+  return DK == 16 * kNW ? t : 0;
+}
 
 template <int NT>
 __device__ __forceinline__ void zero(f4 (&acc)[NT]) {
@@ -419,7 +422,7 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_prep_kernel(BwdChunkArgs p) {
   {
     f4 aw[NTW];
     zero(aw);
-    mm<64, DK, 64, true, false, NTW, TRI_DK(2)>(aw, sM, kL64, sKr, LD, w);
+    mm<64, DK, 64, true, false, NTW, tri_dk<DK>(2)>(aw, sM, kL64, sKr, LD, w);
     lds_barrier();
 #pragma unroll
     for (int s = 0; s < NTW; ++s) {
@@ -850,7 +853,7 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
       for (int q = 0; q < 4; ++q) sX[(m0 + 4 * g + q) * kL64 + n0 + li] += at[s][q];
     }
   }
-  mm<64, DK, 64, false, false, NT4, TRI_DK(3)>(ar, sM, kL64, R2, LD, w);
+  mm<64, DK, 64, false, false, NT4, tri_dk<DK>(3)>(ar, sM, kL64, R2, LD, w);
 #pragma unroll
   for (int s = 0; s < NT4; ++s) {
     if (!tile_live<64, DK>(w, s)) break;
@@ -868,8 +871,8 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
   lds_barrier();
 
   // 5. AH += dP^T Qr;  AQ += dP Kh;  dbeta from T
-  mm<64, DK, 64, false, false, NT4, TRI_DK(3)>(ah, sP, kL64, R2, LD, w);
-  mm<64, DK, 64, true, false, NT4, TRI_DK(2)>(aq, sP, kL64, R1, LD, w);
+  mm<64, DK, 64, false, false, NT4, tri_dk<DK>(3)>(ah, sP, kL64, R2, LD, w);
+  mm<64, DK, 64, true, false, NT4, tri_dk<DK>(2)>(aq, sP, kL64, R1, LD, w);
   {   // column sums of M o dT (M is lower triangular), 8 rows per thread
     const int col = t & 63, part = t >> 6;
     float s = 0.f;
@@ -972,8 +975,8 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
       al[i] = r < nv ? p.alpha[((ck.tok0 + r) * H + h) * int64_t(DK) + c] : 1.f;
     }
   }
-  mm<64, DK, 64, true, false, NT4, TRI_DK(2)>(ar, sX, kL64, R1, LD, w);
-  mm<64, DK, 64, false, false, NT4, TRI_DK(3)>(ah, sX, kL64, R3, LD, w);
+  mm<64, DK, 64, true, false, NT4, tri_dk<DK>(2)>(ar, sX, kL64, R1, LD, w);
+  mm<64, DK, 64, false, false, NT4, tri_dk<DK>(3)>(ah, sX, kL64, R3, LD, w);
 
   // 7. dq, dk; dg = AQ Qr + AR Kr - AH Kh (+ gamma_C's gradient on the last row)
   float dgv[NT4][4];
