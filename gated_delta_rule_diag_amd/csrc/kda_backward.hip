@@ -211,7 +211,7 @@ __device__ __forceinline__ const float* chunk_state(const BwdChunkArgs& p, const
   return p.snapshots + ((base + ck.c - 1) * p.H + ck.h) * hs;
 }
 
-// rho (relative decays) of the chunk into rho_out[64][ld] and the global copy;
+// rho (relative decays) of the chunk into rho[64][ld] and the global copy;
 // gm = gamma_m, gq = gamma_C / gamma_m per channel.  Threads 0..DK-1, one
 // channel each; rows past the chunk's end take alpha = 1.
 template <int DK, bool SG>
