@@ -922,9 +922,11 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int r = m0 + 4 * g + q, c = n0 + li;
+        // (selected, not multiplied by a zero: above the diagonal Kr Kh^T holds
+        // rho_r / rho_s > 1, which overflows at strong decay)
         const float da = c < r ? -ada[s][q] : 0.f;
         ada[s][q] = da;
-        v[q] = da * axx[s][q];
+        v[q] = c < r ? da * axx[s][q] : 0.f;
       }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {

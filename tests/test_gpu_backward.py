@@ -210,3 +210,27 @@ def test_backward_varlen_windows_are_exact(window, max_seqlen, monkeypatch):
     oref = varlen_backward_reference(q, k, v, a, b, cu, do, S0, dST)
     errs = {n: max_rel_err(host(u), r) for n, u, r in zip(NAMES, got, oref)}
     assert max(errs.values()) <= TOL["f32"], errs
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_backward_at_the_decay_domain_edge(dt):
+    """Strong decay, alpha ~ U[0.07, 0.2]: the backward's relative decays reach
+    ~1e36 within a chunk (the same factoring as the forward).  Every gradient
+    against the oracle."""
+    B, T, H, D = 1, 200, 2, 64
+    flush(f"[backward] alpha in [0.07, 0.2] T={T} {dt}")
+    q, k, v, _, b = I.batch_inputs(890, B, T, H, D, D, dt)
+    rng = np.random.default_rng(891)
+    a = rng.uniform(0.07, 0.2, (B, T, H, D)).astype(np.float32)
+    do = rng.standard_normal((B, T, H, D)).astype(np.float32)
+    S0 = random_state(rng, (B, H, D, D))
+    dST = random_state(rng, (B, H, D, D))
+    td = tdtype(dt)
+    got = kda.chunk_backward(dev(q, td), dev(k, td), dev(v, td), dev(a), dev(b), dev(do),
+                             dev(S0), dev(dST))
+    torch.cuda.synchronize()
+    got = [host(g) for g in got]
+    ref = kda_backward(q, k, v, a, b, S0, do, dST)
+    errs = {n: max_rel_err(g, r) for n, g, r in zip(NAMES, got, ref)}
+    flush("    " + " ".join(f"{n}={e:.1e}" for n, e in errs.items()))
+    assert all(np.isfinite(g).all() for g in got) and max(errs.values()) <= TOL[dt], errs

@@ -202,3 +202,25 @@ def test_binding_rejects_bad_arguments():
         kda.chunk_prefill(x, x, x, a, b)
     with pytest.raises(ValueError):
         kda.chunk_prefill(x.float(), x, x, a, b)
+
+
+@pytest.mark.parametrize("path", ["fused", "split"])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_prefill_at_the_decay_domain_edge(path, dt, monkeypatch):
+    """Strong decay, alpha ~ U[0.07, 0.2] on every channel: the product over
+    32 tokens reaches ~1e-37, the edge of the data domain the header states
+    (the decays are factored through each chunk's row 31).  Output and final
+    state against the oracle."""
+    monkeypatch.setenv("KDA_PREFILL_PATH", path)
+    B, T, H, D = 1, 300, 2, 64
+    flush(f"[domain] prefill alpha in [0.07, 0.2] T={T} {dt} {path}")
+    q, k, v, _, b = I.batch_inputs(880, B, T, H, D, D, dt)
+    a = np.random.default_rng(881).uniform(0.07, 0.2, (B, T, H, D)).astype(np.float32)
+    S0 = random_state(np.random.default_rng(882), (B, H, D, D))
+    td = torch.float32 if dt == "f32" else bf
+    o, S = kda.chunk_prefill(dev(q, td), dev(k, td), dev(v, td), dev(a), dev(b), dev(S0))
+    torch.cuda.synchronize()
+    ro, rS = kda_recurrent(q, k, v, a, b, S0)
+    e = (max_rel_err(host(o), ro), max_rel_err(host(S), rS))
+    flush(f"    o={e[0]:.1e} S={e[1]:.1e}")
+    assert np.isfinite(host(o)).all() and max(e) <= TOL[dt], e
