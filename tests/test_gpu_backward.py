@@ -10,7 +10,7 @@ import torch
 from gated_delta_rule_diag_amd import inputs as I
 from gated_delta_rule_diag_amd import kda
 from kda_testlib import TOL, dev, flush, host, random_state, tdtype
-from oracle import kda_backward, max_rel_err
+from oracle import kda_backward, kda_recurrent, max_rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -234,3 +234,27 @@ def test_backward_at_the_decay_domain_edge(dt):
     errs = {n: max_rel_err(g, r) for n, g, r in zip(NAMES, got, ref)}
     flush("    " + " ".join(f"{n}={e:.1e}" for n, e in errs.items()))
     assert all(np.isfinite(g).all() for g in got) and max(errs.values()) <= TOL[dt], errs
+
+
+def test_prefill_and_backward_with_beta_outside_0_1():
+    """beta ~ U[-0.5, 1.5] (any finite beta keeps I + Diag(beta) X unit lower
+    triangular): the prefill's output and state and every gradient against
+    the oracle."""
+    B, T, H, D = 1, 150, 2, 64
+    flush(f"[backward] beta in [-0.5, 1.5] T={T} f32")
+    q, k, v, a, _ = I.batch_inputs(895, B, T, H, D, D, "f32")
+    rng = np.random.default_rng(896)
+    b = rng.uniform(-0.5, 1.5, (B, T, H)).astype(np.float32)
+    do = rng.standard_normal((B, T, H, D)).astype(np.float32)
+    S0 = random_state(rng, (B, H, D, D))
+    dST = random_state(rng, (B, H, D, D))
+    x = (dev(q), dev(k), dev(v), dev(a), dev(b))
+    o, S = kda.chunk_prefill(*x, dev(S0))
+    got = kda.chunk_backward(*x, dev(do), dev(S0), dev(dST))
+    torch.cuda.synchronize()
+    ro, rS = kda_recurrent(q, k, v, a, b, S0)
+    ref = kda_backward(q, k, v, a, b, S0, do, dST)
+    errs = {"o": max_rel_err(host(o), ro), "S": max_rel_err(host(S), rS)}
+    errs.update({n: max_rel_err(host(g), r) for n, g, r in zip(NAMES, got, ref)})
+    flush("    " + " ".join(f"{n}={e:.1e}" for n, e in errs.items()))
+    assert max(errs.values()) <= TOL["f32"], errs
