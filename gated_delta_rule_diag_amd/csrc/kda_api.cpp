@@ -587,6 +587,7 @@ kda_status_t run_backward(int N, int T_fixed, const int32_t* cu_seqlens, int64_t
   f.snapshots = snap_rows > 0 ? reinterpret_cast<float*>(ws + L.snaps) : nullptr;
   f.snap_every = 1;
   f.snap_offsets = nullptr;
+  f.states_only = true;   // the reverse pass reads the checkpoints only
   f.snap_rows = snap_rows;
   const char* msg = nullptr;
   if (kda::launch_prefill(f, stream, &msg) != 0)

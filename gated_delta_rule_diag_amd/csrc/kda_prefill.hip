@@ -62,6 +62,7 @@ struct Params {
                             // (NULL: row cu[n] / 64 + j)
   int64_t snap_rows;        // varlen: rows of snap (rows outside [0, snap_rows) are skipped)
   int alpha_scalar;   // alpha is [tokens][H] (one gate per token and head)
+  int states_only;    // staged form: o is not needed (states and snapshots only)
 };
 
 // ---------------------------------------------------------------- layout ----
@@ -1080,6 +1081,7 @@ struct StageParams {
   int snap_every;
   int64_t snap_per_seq;
   int alpha_scalar;  // alpha is [tokens][H]
+  int states_only;   // o is not written (NOO kernels)
 };
 
 template <bool BF> struct FL;
@@ -1179,7 +1181,9 @@ __device__ __forceinline__ void export_frags(char* dst, const char* src, int pit
 // Steps 1-3 and the folded products for every (chunk, sequence, head) of a
 // segment.  Persistent: workgroup b takes items b, b + G, ...; the raw inputs
 // of its next item are loaded while it works on the current one.
-template <int DK, int DV, bool BF>
+// NOO: the call needs the states only, so Q_g and P (used by o alone) are not
+// stored.
+template <int DK, int DV, bool BF, bool NOO>
 __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_stage_kernel(StageParams p) {
   using L = Lay<DK>;
   using SL = Slot<DK, DV>;
@@ -1303,9 +1307,11 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_stage_kernel(StageParam
     const float* sGN = reinterpret_cast<const float*>(smem + L::OFF_GN);
 
     // F1: Qg = Ql Diag(gamma_m), Kg (already scaled in step 1), P, gamma_n.
-    export_frags<BF, DK, kC, NW, false, true>(slot + SL::OFF_Q, smem + L::OFF_QL, L::P_OP, nullptr, sGM);
+    if constexpr (!NOO)
+      export_frags<BF, DK, kC, NW, false, true>(slot + SL::OFF_Q, smem + L::OFF_QL, L::P_OP, nullptr, sGM);
     export_frags<BF, kC, DK, NW, false, false>(slot + SL::OFF_K, smem + L::OFF_KRT, L::P_T, nullptr, nullptr);
-    export_frags<BF, kC, kC, NW, false, false>(slot + SL::OFF_P, smem + L::OFF_P, L::P_T, nullptr, nullptr);
+    if constexpr (!NOO)
+      export_frags<BF, kC, kC, NW, false, false>(slot + SL::OFF_P, smem + L::OFF_P, L::P_T, nullptr, nullptr);
     reinterpret_cast<float*>(slot + SL::OFF_G)[t % DK] = sGN[t % DK];
     lds_barrier();
 
@@ -1392,7 +1398,8 @@ __device__ __forceinline__ f4 gemm_ra(f4 acc, const typename Mma<BF>::Frag (&a)[
 // The state pass over the chunks of a segment, operands from the slots.  One
 // workgroup per (sequence, head, value slab of 16*NSUB columns); the slab of S
 // lives in registers, wave w holding rows 16w..16w+15.
-template <int DK, int NSUB, bool BF, bool SNAP>
+// NOO: states (and snapshots) only; no o, so no Q_g, P or output products.
+template <int DK, int NSUB, bool BF, bool SNAP, bool NOO>
 __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_chain_kernel(StageParams p) {
   using M = Mma<BF>;
   using F = FL<BF>;
@@ -1442,7 +1449,7 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_chain_kernel(StageParam
   // 4-7 the output rows 16(w-4)..; with 4 waves every wave does both.
   constexpr bool kSplitO = NW >= 8;
   const bool xw = w < 4;
-  const bool owave = kSplitO ? (w >= 4) : true;
+  const bool owave = NOO ? false : (kSplitO ? (w >= 4) : true);
   const int ow = w & 3;
   constexpr int NA = kSplitO ? 1 : 2;   // row blocks of W / Qg held by a wave
   // P is lower triangular: its row block ow is zero past token 16 ow + 15.
@@ -1463,6 +1470,7 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_chain_kernel(StageParam
 #pragma unroll
     for (int a = 0; a < NA; ++a) {
       const bool wside = kSplitO ? xw : (a == 0);
+      if (NOO && !wside) continue;
       F::load(o.a[a], slot + (wside ? OFF_W : OFF_Q) + ow * RBK);
     }
   };
@@ -1685,6 +1693,7 @@ void launch_staged_t(const Params& base, int64_t T, int nsub, hipStream_t st, ch
   sp.snap_every = base.snap_every;
   sp.snap_per_seq = base.snap_per_seq;
   sp.alpha_scalar = base.alpha_scalar;
+  sp.states_only = base.states_only;
   const int64_t nsegs = (nchunks + seg - 1) / seg;
   const int64_t cus = device_cus();
   for (int64_t si = 0; si < nsegs; ++si) {
@@ -1693,24 +1702,35 @@ void launch_staged_t(const Params& base, int64_t T, int nsub, hipStream_t st, ch
     sp.s_in = si == 0 ? base.s_in : state_ws;
     sp.s_out = si == nsegs - 1 ? base.s_out : state_ws;
     const int64_t items = sp.pairs * sp.nseg;
-    hipLaunchKernelGGL((kda_stage_kernel<DK, DV, BF>), dim3(unsigned(items < cus ? items : cus)),
-                       dim3(Lay<DK>::NT), 0, st, sp);
+    const unsigned ns = unsigned(items < cus ? items : cus);
+    const bool noo = sp.snap && sp.states_only;   // the backward's checkpoints
+    if (noo)
+      hipLaunchKernelGGL((kda_stage_kernel<DK, DV, BF, true>), dim3(ns), dim3(Lay<DK>::NT), 0, st, sp);
+    else
+      hipLaunchKernelGGL((kda_stage_kernel<DK, DV, BF, false>), dim3(ns), dim3(Lay<DK>::NT), 0, st, sp);
     const unsigned nb = unsigned(sp.pairs * sp.nslab);
-    if (nsub == 4) {
-      if (sp.snap)
-        hipLaunchKernelGGL((kda_chain_kernel<DK, 4, BF, true>), dim3(nb), dim3(Lay<DK>::NT), 0, st, sp);
+    if (noo) {
+      if (nsub == 4)
+        hipLaunchKernelGGL((kda_chain_kernel<DK, 4, BF, true, true>), dim3(nb), dim3(Lay<DK>::NT), 0, st, sp);
+      else if (nsub == 2)
+        hipLaunchKernelGGL((kda_chain_kernel<DK, 2, BF, true, true>), dim3(nb), dim3(Lay<DK>::NT), 0, st, sp);
       else
-        hipLaunchKernelGGL((kda_chain_kernel<DK, 4, BF, false>), dim3(nb), dim3(Lay<DK>::NT), 0, st, sp);
+        hipLaunchKernelGGL((kda_chain_kernel<DK, 1, BF, true, true>), dim3(nb), dim3(Lay<DK>::NT), 0, st, sp);
+    } else if (nsub == 4) {
+      if (sp.snap)
+        hipLaunchKernelGGL((kda_chain_kernel<DK, 4, BF, true, false>), dim3(nb), dim3(Lay<DK>::NT), 0, st, sp);
+      else
+        hipLaunchKernelGGL((kda_chain_kernel<DK, 4, BF, false, false>), dim3(nb), dim3(Lay<DK>::NT), 0, st, sp);
     } else if (nsub == 2) {
       if (sp.snap)
-        hipLaunchKernelGGL((kda_chain_kernel<DK, 2, BF, true>), dim3(nb), dim3(Lay<DK>::NT), 0, st, sp);
+        hipLaunchKernelGGL((kda_chain_kernel<DK, 2, BF, true, false>), dim3(nb), dim3(Lay<DK>::NT), 0, st, sp);
       else
-        hipLaunchKernelGGL((kda_chain_kernel<DK, 2, BF, false>), dim3(nb), dim3(Lay<DK>::NT), 0, st, sp);
+        hipLaunchKernelGGL((kda_chain_kernel<DK, 2, BF, false, false>), dim3(nb), dim3(Lay<DK>::NT), 0, st, sp);
     } else {
       if (sp.snap)
-        hipLaunchKernelGGL((kda_chain_kernel<DK, 1, BF, true>), dim3(nb), dim3(Lay<DK>::NT), 0, st, sp);
+        hipLaunchKernelGGL((kda_chain_kernel<DK, 1, BF, true, false>), dim3(nb), dim3(Lay<DK>::NT), 0, st, sp);
       else
-        hipLaunchKernelGGL((kda_chain_kernel<DK, 1, BF, false>), dim3(nb), dim3(Lay<DK>::NT), 0, st, sp);
+        hipLaunchKernelGGL((kda_chain_kernel<DK, 1, BF, false, false>), dim3(nb), dim3(Lay<DK>::NT), 0, st, sp);
     }
   }
 }
@@ -1773,6 +1793,7 @@ int launch_prefill(const PrefillArgs& a, void* stream, const char** msg) {
   p.snap_off = a.snap_offsets;
   p.snap_rows = a.snap_rows;
   p.alpha_scalar = a.alpha_scalar ? 1 : 0;
+  p.states_only = a.states_only ? 1 : 0;
   const int64_t pairs = int64_t(a.N) * a.H;
   const bool varlen = a.cu_seqlens != nullptr;
   const int64_t nchunks = varlen ? 0 : (a.T_fixed + kC - 1) / kC;
