@@ -32,7 +32,7 @@ struct PrefillArgs {
   const int32_t* snap_offsets; // varlen: device [N+1], sequence n owns rows [off[n], off[n+1])
   int64_t snap_rows;           // varlen: rows of snapshots
   bool alpha_scalar;           // alpha is [tokens, H]: one gate per token and head
-  bool states_only;            // staged form: o is not written (the caller needs states or
+  bool states_only;            // with snapshots: o is not written (the caller needs the
                                // snapshots only; o must still point at valid memory)
 };
 

@@ -62,7 +62,7 @@ struct Params {
                             // (NULL: row cu[n] / 64 + j)
   int64_t snap_rows;        // varlen: rows of snap (rows outside [0, snap_rows) are skipped)
   int alpha_scalar;   // alpha is [tokens][H] (one gate per token and head)
-  int states_only;    // staged form: o is not needed (states and snapshots only)
+  int states_only;    // with snapshots: o is not needed (NOO kernels)
 };
 
 // ---------------------------------------------------------------- layout ----
@@ -777,7 +777,8 @@ __device__ __forceinline__ void store_snapshot(float* snap, int64_t row, int h, 
     for (int q = 0; q < 4; ++q) dst[uint32_t((16 * w + 4 * (l >> 4) + q) * DV + 16 * js)] = S[js][q];
 }
 
-template <int DK, int NSUB, bool BF, bool SNAP>
+// NOO: states and snapshots only (no output products; o is not written).
+template <int DK, int NSUB, bool BF, bool SNAP, bool NOO>
 __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_prefill_kernel(Params p) {
   using L = Lay<DK>;
   constexpr int NW = L::NW;         // waves; wave w owns rows 16w..16w+15 of the state
@@ -930,7 +931,7 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_prefill_kernel(Params p
     // overlaps X and U), else by waves 0..3 after U.
     constexpr bool kSplitO = NW >= 8;
     const bool xw = w < 4;
-    const bool owave = kSplitO ? (w >= 4) : (w < 4);
+    const bool owave = NOO ? false : (kSplitO ? (w >= 4) : (w < 4));
     const int ow = w & 3;
 #pragma unroll
     for (int js = 0; js < NSUB; ++js) {
@@ -1592,11 +1593,14 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_chain_kernel(StageParam
 
 template <int DK, int NSUB, bool BF>
 void launch_t(const Params& p, int64_t nblocks, hipStream_t st) {
-  if (p.snap)
-    hipLaunchKernelGGL((kda_prefill_kernel<DK, NSUB, BF, true>), dim3(unsigned(nblocks)),
+  if (p.snap && p.states_only)   // the backward's checkpoints
+    hipLaunchKernelGGL((kda_prefill_kernel<DK, NSUB, BF, true, true>), dim3(unsigned(nblocks)),
+                       dim3(Lay<DK>::NT), 0, st, p);
+  else if (p.snap)
+    hipLaunchKernelGGL((kda_prefill_kernel<DK, NSUB, BF, true, false>), dim3(unsigned(nblocks)),
                        dim3(Lay<DK>::NT), 0, st, p);
   else
-    hipLaunchKernelGGL((kda_prefill_kernel<DK, NSUB, BF, false>), dim3(unsigned(nblocks)),
+    hipLaunchKernelGGL((kda_prefill_kernel<DK, NSUB, BF, false, false>), dim3(unsigned(nblocks)),
                        dim3(Lay<DK>::NT), 0, st, p);
 }
 
