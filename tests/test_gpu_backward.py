@@ -258,3 +258,29 @@ def test_prefill_and_backward_with_beta_outside_0_1():
     errs.update({n: max_rel_err(host(g), r) for n, g, r in zip(NAMES, got, ref)})
     flush("    " + " ".join(f"{n}={e:.1e}" for n, e in errs.items()))
     assert max(errs.values()) <= TOL["f32"], errs
+
+
+@pytest.mark.parametrize("window", [None, "1"])
+def test_backward_varlen_rectangular(window, monkeypatch):
+    """Packed sequences with d_k = 64, d_v = 128 (four waves per chain
+    workgroup, eight value slabs), in one window or in windows of one chunk:
+    every gradient against the per-sequence oracle."""
+    lengths = [70, 0, 128, 5, 193]
+    H, dk, dv = 2, 64, 128
+    flush(f"[backward] varlen rectangular dk={dk} dv={dv} window={window} lengths={lengths}")
+    q, k, v, a, b, cu = I.packed_inputs(900, lengths, H, dk, dv, "bf16")
+    rng = np.random.default_rng(901)
+    do = rng.standard_normal((int(cu[-1]), H, dv)).astype(np.float32)
+    S0 = random_state(rng, (len(lengths), H, dk, dv))
+    dST = random_state(rng, (len(lengths), H, dk, dv))
+    td = tdtype("bf16")
+    if window:
+        monkeypatch.setenv("KDA_BWD_WINDOW", window)
+    got = kda.chunk_backward_varlen(dev(q, td), dev(k, td), dev(v, td), dev(a), dev(b),
+                                    torch.from_numpy(cu).cuda(), dev(do), dev(S0), dev(dST),
+                                    max_seqlen=max(lengths))
+    torch.cuda.synchronize()
+    ref = varlen_backward_reference(q, k, v, a, b, cu, do, S0, dST)
+    errs = {n: max_rel_err(host(g), r) for n, g, r in zip(NAMES, got, ref)}
+    flush("    " + " ".join(f"{n}={e:.1e}" for n, e in errs.items()))
+    assert max(errs.values()) <= TOL["bf16"], errs
