@@ -12,6 +12,12 @@ Prints ONE JSON line.  `value` is prefill tokens/s (tokens of the 8192-token
 sequence per second of prefill-kernel time); decode us/step is reported next
 to it.  Kernel times come from HIP events recorded on the stream the kernels
 are launched on (torch's current stream), averaged over the timed steps.
+The line also carries: `parity` (the timed launches' outputs against the
+fp64 oracle: prefill o and state on heads 0 and 31, o on every head for the
+tokens the cpu_baseline leg ran, the decode step on three sequences),
+`more_configs` (the packed 64-sequence prefill and the 1M-token prefill with
+1024 decode steps after it: times, HBM fractions, sampled parity), and `run`
+(GPU, software versions, commit or kernel-source hash).
 """
 
 from __future__ import annotations
@@ -58,14 +64,16 @@ def cpu_baseline(seconds, q, k, v, a, b):
     B, T, H, D = q.shape
     step = 256
     done, t_used, S = 0, 0.0, None
+    outs = []
     with threadpool_limits(limits=1):
         while t_used < seconds and done < T:
             sl = slice(done, min(done + step, T))
             t0 = time.perf_counter()
-            _, S = kda_recurrent(q[:, sl], k[:, sl], v[:, sl], a[:, sl], b[:, sl], S)
+            o, S = kda_recurrent(q[:, sl], k[:, sl], v[:, sl], a[:, sl], b[:, sl], S)
             t_used += time.perf_counter() - t0
+            outs.append(o)
             done = sl.stop
-    return {
+    return np.concatenate(outs, axis=1), {
         "value": done / t_used,
         "unit": "tokens/s",
         "cores": 1,
@@ -74,6 +82,140 @@ def cpu_baseline(seconds, q, k, v, a, b):
                   f"first {done} of {T} tokens ({t_used:.1f} s, BLAS limited to 1 thread); "
                   f"host {platform.machine()}, {len(os.sched_getaffinity(0))} cores visible",
     }
+
+
+def run_info(torch):
+    """What the evaluation pages ask a measurement to state besides the
+    numbers: hardware, software versions and the code measured ("Kimi Linear、
+    独自の土俵でFull Attentionを上回る" (remio.ai), section "オープンコードにより
+    主張は検証可能になる…")."""
+    import hashlib
+    import subprocess
+
+    here = os.path.dirname(os.path.abspath(__file__))
+    h = hashlib.sha256()
+    csrc = os.path.join(here, "gated_delta_rule_diag_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    try:
+        commit = subprocess.run(["git", "-C", here, "rev-parse", "HEAD"], capture_output=True,
+                                text=True, timeout=10).stdout.strip() or None
+    except (OSError, subprocess.SubprocessError):
+        commit = None
+    props = torch.cuda.get_device_properties(0)
+    return {
+        "gpu": torch.cuda.get_device_name(0),
+        "gpu_arch": getattr(props, "gcnArchName", None),
+        "compute_units": props.multi_processor_count,
+        "torch": torch.__version__,
+        "hip": torch.version.hip,
+        "git_commit": commit,
+        "kernel_source_sha256_16": h.hexdigest()[:16],
+        "host_cpu": platform.processor() or platform.machine(),
+    }
+
+
+def extra_configs(torch, kda, I, reps=3):
+    """The packed-sequence prefill (64 sequences, lengths ~U{512..16384},
+    H=32, d=128) and the 1M-token prefill followed by 1024 decode steps
+    (B=1, H=32, d=128): times, rates, HBM fractions, and parity of a sample of
+    their outputs against the oracle.  Inputs are drawn on the device with the
+    recipe's distributions (normalisation in fp32)."""
+    from oracle import kda_recurrent, max_rel_err
+
+    dev = torch.device("cuda:0")
+    bf = torch.bfloat16
+    H, D = 32, 128
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(I.SEED + 34)
+
+    def draw(shape):
+        q = torch.randn(shape + (D,), generator=gen, device=dev)
+        q = (q / q.norm(dim=-1, keepdim=True)).to(bf)
+        k = torch.randn(shape + (D,), generator=gen, device=dev)
+        k = (k / k.norm(dim=-1, keepdim=True)).to(bf)
+        v = torch.randn(shape + (D,), generator=gen, device=dev).to(bf)
+        b = torch.sigmoid(torch.randn(shape, generator=gen, device=dev))
+        a = torch.exp(-torch.exp(torch.rand(shape + (D,), generator=gen, device=dev) * 4 - 5))
+        return q, k, v, a, b
+
+    def timed(fn, n):
+        fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        for _ in range(n):
+            fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / n * 1e3   # us per call
+
+    host = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
+    res = {}
+    # ---- packed sequences ----
+    lengths = I.varlen_lengths(3, 64, 512, 16384)
+    Tt = int(lengths.sum())
+    cu_h = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    cu = torch.from_numpy(cu_h).to(dev)
+    q, k, v, a, b = draw((Tt, H))
+    o = torch.empty((Tt, H, D), device=dev, dtype=torch.float32)
+    S = torch.empty((64, H, D, D), device=dev, dtype=torch.float32)
+    us = timed(lambda: kda.chunk_prefill_varlen(q, k, v, a, b, cu, None, True, 64, o, S), reps)
+    nbytes = prefill_algorithmic_bytes(Tt, H, D, D, False, False) + 64 * H * D * D * 4
+    n = int(np.argmin(lengths))   # the shortest sequence, head 0, through the oracle
+    s0, s1 = int(cu_h[n]), int(cu_h[n + 1])
+    sl = lambda t: host(t[s0:s1, 0])[None, :, None]  # noqa: E731
+    ro, rS = kda_recurrent(sl(q), sl(k), sl(v), sl(a), host(b[s0:s1, 0])[None, :, None])
+    res["varlen_n64_h32_d128"] = {
+        "tokens": Tt, "us": us, "tokens_per_s": Tt / (us * 1e-6),
+        "hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": nbytes,
+        "parity": {"sample": f"sequence {n} ({s1 - s0} tokens), head 0",
+                   "o": max_rel_err(host(o[s0:s1, 0]), ro[0, :, 0]),
+                   "state": max_rel_err(host(S[n, 0]), rS[0, 0])},
+    }
+    del q, k, v, a, b, o, S, cu
+    torch.cuda.empty_cache()
+    # ---- 1M-token prefill, then 1024 decode steps from its state ----
+    T = 1 << 20
+    q, k, v, a, b = draw((1, T, H))
+    o = torch.empty((1, T, H, D), device=dev, dtype=torch.float32)
+    S = torch.empty((1, H, D, D), device=dev, dtype=torch.float32)
+    ws = torch.empty(max(kda.lib().kda_chunk_prefill_workspace_size(1, T, H, D, D, 64), 1),
+                     device=dev, dtype=torch.uint8)
+    us = timed(lambda: kda.chunk_prefill(q, k, v, a, b, None, True, 64, o, S, ws), 2)
+    nbytes = prefill_algorithmic_bytes(T, H, D, D, False, True)
+    P = 2048   # the first P tokens of head 0 through the oracle
+    sl = lambda t: host(t[:, :P, 0])[:, :, None]  # noqa: E731
+    ro, _ = kda_recurrent(sl(q), sl(k), sl(v), sl(a), host(b[:, :P, 0])[:, :, None])
+    par = {"sample": f"head 0, the first {P} of {T} tokens (o)",
+           "o": max_rel_err(host(o[:, :P, 0]), ro[:, :, 0])}
+    del q, k, v, a, o, ws
+    torch.cuda.empty_cache()
+    dq, dk, dv, da, db = draw((1, H))
+    od = torch.empty((1, H, D), device=dev, dtype=torch.float32)
+    step = lambda: kda.decode_step(dq, dk, dv, da, db, S, od)  # noqa: E731
+    eager = timed(step, 1024)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(16):
+            step()
+    in_graph = timed(graph.replay, 64) / 16
+    res["long_context_t1m_h32_d128"] = {
+        "tokens": T, "prefill_us": us, "prefill_tokens_per_s": T / (us * 1e-6),
+        "prefill_hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": nbytes,
+        "decode_1024_steps_us_per_step_eager": eager,
+        "decode_us_per_step_hip_graph_16_steps": in_graph,
+        "parity": par,
+    }
+    del graph, S, dq, dk, dv, da, db, od, b
+    torch.cuda.empty_cache()
+    return res
 
 
 def long_context(torch):
@@ -151,6 +293,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the serving variants timed after the steps (profiled runs)")
+    ap.add_argument("--no-extra-configs", action="store_true",
+                    help="skip the packed-sequence and 1M-token workloads timed after the steps")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one plain 512 MiB device-to-device copy before the timed region "
                          "(reference for HBM byte counters)")
@@ -204,6 +348,7 @@ def main():
     _, dstate = kda.chunk_prefill(wq.to(bf), wk.to(bf), wv.to(bf), wa.contiguous(), wb.contiguous())
     del x, wq, wk, wv, wa, wb
     do = torch.empty((ND, H, D), device=dev, dtype=torch.float32)
+    dstate0 = dstate.clone()   # the decode's parity is taken from this copy after timing
     if args.copy_calibration:
         src = torch.ones(512 << 18, device=dev, dtype=torch.float32)  # 512 MiB
         dst = torch.empty_like(src)
@@ -233,6 +378,35 @@ def main():
     wall = time.perf_counter() - t0
     pre_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     dec_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+
+    # ---- parity of the timed launches (same kernels, same launch shapes) ----
+    # prefill: po / pst of the last timed step (checked before anything else
+    # writes them); decode: one step from the saved start states, checked for
+    # sequences 0, 97 and 255 (all heads).
+    from oracle import kda_decode_step, kda_recurrent, max_rel_err
+
+    sel = [0, 97, 255]
+    d_o = torch.empty_like(do)
+    st = dstate0.clone()
+    kda.decode_step(dq, dk_, dv_, da, db, st, d_o)
+    torch.cuda.synchronize()
+    hostf = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
+    s0h = hostf(dstate0[sel])
+    xs = [hostf(t[sel]) for t in (dq, dk_, dv_, da, db)]
+    ro_d, rS_d = kda_decode_step(*xs, s0h)
+    parity = {
+        "tolerance": 2e-3,
+        "decode_o": max_rel_err(hostf(d_o[sel]), ro_d),
+        "decode_state": max_rel_err(hostf(st[sel]), rS_d),
+        "decode_sample": "sequences 0, 97, 255, all 32 heads, the first step from the timed start states",
+    }
+    del st, d_o, dstate0
+    hp = [0, 31]
+    ro_p, rS_p = kda_recurrent(q[:, :, hp], k[:, :, hp], v[:, :, hp], a[:, :, hp], b[:, :, hp])
+    parity["prefill_o_heads_0_31"] = max_rel_err(hostf(po[:, :, hp]), ro_p)
+    parity["prefill_state_heads_0_31"] = max_rel_err(hostf(pst[:, hp]), rS_p)
+    po_first = hostf(po)   # compared with the cpu_baseline leg (the oracle) below
+
 
     # ---- the serving variants, timed after (and outside) the steps above ----
     def time_call(fn, reps=max(args.steps, 5)):
@@ -323,6 +497,12 @@ def main():
             "decode_n1_h32_hip_graph_us_per_step": n1_graph_us,
         }
 
+    extra = None
+    if not args.no_extra_configs:
+        del pq, pk, pv, pa, pb, pws, dq, dk_, dv_, da, db, dstate, do
+        torch.cuda.empty_cache()
+        extra = extra_configs(torch, kda, I)
+
     pre_bytes = prefill_algorithmic_bytes(T, H, D, D, False, True)
     pre_gbs = pre_bytes / (pre_ms * 1e-3) / 1e9
     dec_gbs = dec_bytes / (dec_ms * 1e-3) / 1e9
@@ -391,7 +571,10 @@ def main():
             "algorithmic_tflops": pre_tflops,
             "mfma_frac_algorithmic": pre_tflops / BF16_MFMA_PEAK_TFLOPS,
         },
+        "parity": parity,
+        "more_configs": extra,
         "serving_variants": variants,
+        "run": run_info(torch),
         "roofline_decode": {
             "bound": "hbm",
             "kernel": "kda_decode_kernel",
@@ -404,7 +587,11 @@ def main():
         },
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(args.cpu_seconds, q, k, v, a, b)
+        ro_c, out["cpu_baseline"] = cpu_baseline(args.cpu_seconds, q, k, v, a, b)
+        n_c = ro_c.shape[1]
+        n_c = min(n_c, po_first.shape[1])
+        parity["prefill_o_all_heads_first_tokens"] = max_rel_err(po_first[:, :n_c], ro_c[:, :n_c])
+        parity["prefill_o_all_heads_first_tokens_sample"] = f"all {H} heads, tokens 0..{n_c - 1}"
     print(json.dumps(out), flush=True)
 
 

@@ -9,12 +9,15 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
 #include <string>
 
 #include "kda.h"
 #include "kda_internal.h"
 
 namespace {
+
+std::atomic<int> g_prefill_form{0}, g_prefill_nsub{0}, g_prefill_seg{0}, g_bwd_window{0};
 
 thread_local std::string g_last_error;
 
@@ -93,9 +96,32 @@ kda_status_t check_prefill(int nseq, int64_t ntok, int H, int DK, int DV, int ch
 
 }  // namespace
 
+namespace kda {
+Tuning tuning() {
+  return Tuning{g_prefill_form.load(std::memory_order_relaxed), g_prefill_nsub.load(std::memory_order_relaxed),
+                g_prefill_seg.load(std::memory_order_relaxed), g_bwd_window.load(std::memory_order_relaxed)};
+}
+}  // namespace kda
+
 extern "C" {
 
-int kda_abi_version(void) { return (1 << 16) | 0; }
+int kda_abi_version(void) { return (1 << 16) | 1; }
+
+kda_status_t kda_internal_set_tuning(int prefill_form, int prefill_nsub, int prefill_seg,
+                                     int bwd_window) {
+  if (prefill_form < 0 || prefill_form > 2)
+    return fail(KDA_ERR_SHAPE, "prefill_form=%d: 0 (by shape), 1 (fused) or 2 (staged)", prefill_form);
+  if (prefill_nsub != 0 && prefill_nsub != 1 && prefill_nsub != 2 && prefill_nsub != 4 &&
+      prefill_nsub != 8)
+    return fail(KDA_ERR_SHAPE, "prefill_nsub=%d: 0, 1, 2, 4 or 8", prefill_nsub);
+  if (prefill_seg < 0 || bwd_window < 0)
+    return fail(KDA_ERR_SHAPE, "prefill_seg=%d bwd_window=%d: must be >= 0", prefill_seg, bwd_window);
+  g_prefill_form.store(prefill_form, std::memory_order_relaxed);
+  g_prefill_nsub.store(prefill_nsub, std::memory_order_relaxed);
+  g_prefill_seg.store(prefill_seg, std::memory_order_relaxed);
+  g_bwd_window.store(bwd_window, std::memory_order_relaxed);
+  return ok();
+}
 
 const char* kda_status_string(kda_status_t s) {
   switch (s) {
@@ -448,10 +474,9 @@ kda_status_t kda_decode_pool(int N, int L, int H, int DK, int DV, kda_dtype_t in
 namespace {
 
 // Byte offsets of the backward workspace: [forward prefill workspace, later the
-// window buffers | o of the forward | snapshots | adjoint carried between
-// windows].
+// window buffers | snapshots | adjoint carried between windows].
 struct BwdLayout {
-  size_t fwd_or_win, o, snaps, carry, total;
+  size_t fwd_or_win, snaps, carry, total;
   int64_t win_k, nwin;   // chunks per window of the reverse pass, windows
 };
 
@@ -459,24 +484,20 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Workspace of a backward call: the forward's workspace (fixed length only) or
 // the buffers of one window of chunks, whichever is larger (they are not live
-// at the same time), the forward's o, one state per full chunk, and the
-// adjoint carried between windows.  The reverse pass goes through the chunks
+// at the same time), one state per full chunk, and the adjoint carried between
+// windows.  (The forward runs in its states-only form, which writes no o.)  The reverse pass goes through the chunks
 // in windows of win_k chunks counted from each sequence's end, so that the
 // window buffers (backward_chunk_floats per chunk-head) take at most 4 GiB
-// whatever the length; KDA_BWD_WINDOW=k forces k chunks per window.  Packed
+// whatever the length (the tuning override bwd_window forces a window size).  Packed
 // sequences: T_fixed = 0, max_chunks from the longest sequence, and the
 // snapshot rows are T_total / 64 (chunk j of the sequence starting at token s
 // is row s / 64 + j).
 BwdLayout bwd_layout(int N, int T_fixed, int64_t T_total, int64_t max_chunks, int H, int DK,
                      int DV, bool varlen) {
   BwdLayout L{};
-  const size_t rows = size_t(T_total) * H;
   const size_t per_chunk = size_t(N) * H * kda::backward_chunk_floats(DK, DV) * 4;
   int64_t k = int64_t((size_t(4) << 30) / per_chunk);
-  if (const char* e = getenv("KDA_BWD_WINDOW")) {
-    const long v = atol(e);
-    if (v > 0) k = v;
-  }
+  if (const int v = kda::tuning().bwd_window; v > 0) k = v;
   if (k < 1) k = 1;
   if (max_chunks < 1) max_chunks = 1;
   if (k > max_chunks) k = max_chunks;
@@ -486,8 +507,7 @@ BwdLayout bwd_layout(int N, int T_fixed, int64_t T_total, int64_t max_chunks, in
   const size_t win = size_t(k) * per_chunk;
   const size_t snap_rows = varlen ? size_t(T_total / 64) : size_t(N) * size_t(T_fixed / 64);
   L.fwd_or_win = 0;
-  L.o = align256(pw > win ? pw : win);
-  L.snaps = L.o + align256(rows * DV * 4);
+  L.snaps = align256(pw > win ? pw : win);
   L.carry = L.snaps + align256(snap_rows * H * DK * DV * 4);
   L.total = L.carry + (L.nwin > 1 ? align256(size_t(N) * H * DK * DV * 4) : 0);
   return L;
@@ -581,8 +601,9 @@ kda_status_t run_backward(int N, int T_fixed, const int32_t* cu_seqlens, int64_t
   f.N = N; f.T_fixed = varlen ? 0 : T_fixed; f.cu_seqlens = cu_seqlens; f.T_total = T_total;
   f.H = H; f.DK = DK; f.DV = DV; f.in_bf16 = in_dtype == KDA_BF16;
   f.q = q; f.k = k; f.v = v; f.alpha = alpha; f.beta = beta; f.alpha_scalar = alpha_scalar;
-  f.state_in = state_in; f.o = reinterpret_cast<float*>(ws + L.o); f.state_out = nullptr;
-  f.workspace = ws + L.fwd_or_win; f.workspace_bytes = L.o;
+  // (states only: o is never written, but must be a valid address)
+  f.state_in = state_in; f.o = reinterpret_cast<float*>(ws); f.state_out = nullptr;
+  f.workspace = ws + L.fwd_or_win; f.workspace_bytes = L.snaps;
   const int64_t snap_rows = varlen ? T_total / 64 : int64_t(N) * (T_fixed / 64);
   f.snapshots = snap_rows > 0 ? reinterpret_cast<float*>(ws + L.snaps) : nullptr;
   f.snap_every = 1;
@@ -608,7 +629,8 @@ kda_status_t run_backward(int N, int T_fixed, const int32_t* cu_seqlens, int64_t
   c.bc = c.Ac + per * DK * DK;
   c.dSend = c.bc + per * DK * DV;
   c.Mb = c.dSend + per * DK * DV;
-  c.Vnb = c.Mb + per * 64 * 64;
+  c.PX = c.Mb + per * 64 * 64;
+  c.Vnb = c.PX + per * 64 * 64;
   c.rho = c.Vnb + per * 64 * DV;
   for (int64_t w = 0; w < L.nwin; ++w) {
     c.win_lo = w * L.win_k;

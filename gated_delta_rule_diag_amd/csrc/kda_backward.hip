@@ -4,26 +4,38 @@
 // recurrence ("Kimi Linear、独自の土俵でFull Attentionを上回る" (remio.ai),
 // section "Kimi Linearがより賢いRecurrent Memoryを使う方法") but print neither
 // it nor its gradient.  This is the reverse mode of the chunk form the prefill
-// uses, taken through its matrices.  Per chunk of 64 tokens, with
-// rho_r = gamma_r / gamma_m the decay of row r relative to row m = 31
-// (products of alpha, no logarithms):
+// uses, taken through its matrices.  Per chunk of 64 tokens, per key channel,
+// with gamma_r the product of alpha over rows 0..r and rho_r = gamma_r /
+// gamma_mR the decay of row r relative to the reference row m_R = 16R + 7 of
+// its 16-row block R (products of alpha, no logarithms):
 //   Kr = k rho,  Kh = k / rho,  Qr = q rho                 (per row and channel)
-//   X = strict_lower(Kr Kh^T),  M = (I + Diag(beta) X)^-1,  T = M Diag(beta)
-//   W = T Kr Diag(gamma_m),  U = T V,  Vn = U - W S
-//   P = lower(Qr Kh^T),  O = Qr Diag(gamma_m) S + P Vn
-//   S' = Diag(gamma_C) S + (Kh Diag(gamma_C / gamma_m))^T Vn
-// S is the state entering the chunk (the forward's snapshot).  The adjoint of
-// the state entering a chunk is affine in the adjoint of the state leaving it,
-// dS = b_c + A_c dS' with A_c = Diag(gamma_C) - W^T Kend and
-// b_c = (Qa - P W)^T dO (Kend = Kh Diag(gamma_C / gamma_m),
-// Qa = Qr Diag(gamma_m)), so the reverse pass is three launches per window of
-// chunks:
-//   prep   one workgroup per chunk-head: A_c, b_c, M, Vn and rho;
+//   X = strict_lower(G_K),  P = lower(G_Q)     G[r,s] = Kr_r . Kh_s D_rs
+//   M = (I + Diag(beta) X)^-1,  T = M Diag(beta)
+//   Kg = k gamma,  Qg = q gamma,  Ke = k gamma_C / gamma   (Kr, Qr, Kh rescaled)
+//   W = T Kg,  U = T V,  Vn = U - W S
+//   O = Qg S + P Vn,   S' = Diag(gamma_C) S + Ke^T Vn
+// D_rs = gamma_mR / gamma_mI for rows r of block R and s of block I < R,
+// applied to the column operand in two steps (S1_I, then E_RI) and to the row
+// operand of the transposed sums in two steps (P1_R, then F_RI), so that no
+// intermediate leaves the range of the entries it builds (the forward's
+// factoring; see kda_prefill.hip).  S is the state entering the chunk (the
+// forward's snapshot).  The adjoint of the state entering a chunk is affine in
+// the adjoint of the state leaving it, dS = b_c + A_c dS' with
+// A_c = Diag(gamma_C) - W^T Ke and b_c = (Qg - P W)^T dO, so the reverse pass
+// is three launches per window of chunks:
+//   prep   one workgroup per chunk-head: A_c, b_c, M, Vn, P and X, the decays;
 //   chain  one workgroup per (sequence, head, 16 value columns): the adjoints
 //          dS' at every chunk end, sequentially from the last chunk;
 //   post   one workgroup per chunk-head: dq, dk, dv, dalpha, dbeta from S, dS',
-//          M and Vn (the solve's adjoint dA = -M^T dM M^T, the decays'
+//          M, Vn, P and X (the solve's adjoint dA = -M^T dM M^T, the decays'
 //          gradient as a reverse cumulative sum within the chunk).
+// The gradient of the log-decays per row is
+//   dg = AQ Qr + AR Kr - AH Kh   (+ the chunk-end decay's terms on the last row)
+// with AQ, AR, AH the row and column sums of the factored products.  The
+// diagonal of P carries no decay (gamma_r / gamma_r): its contributions to dq
+// and dk are added apart, so that dg holds no pair of equal and opposite terms
+// that would cancel in fp32 (dalpha = d log(alpha) / alpha would magnify the
+// rounding of such a pair by 1 / alpha).
 // All products are fp32 MFMA (16x16x4) on LDS operands.
 #include <hip/hip_runtime.h>
 
@@ -35,7 +47,19 @@ namespace {
 typedef float f4 __attribute__((ext_vector_type(4)));
 
 constexpr int kC = 64;      // chunk
-constexpr int kMid = 31;    // reference row of the relative decays
+// Decay buffer of a chunk-head ([kDecayRows][DK] floats): rho (rows 0..63),
+// then per-channel vectors (row indices):
+constexpr int kGM = 64;     // gamma_mR, R = 0..3           (rows 0 .. 16R + 7)
+constexpr int kGNM = 68;    // gamma_C / gamma_mI, I = 0..3 (rows 16I + 8 .. 63)
+constexpr int kS1 = 72;     // S1_I, I = 0..3               (rows 16I + 8 .. 16I + 15)
+constexpr int kE = 76;      // E_RI, 6 pairs I < R          (rows 16I + 16 .. 16R + 7)
+constexpr int kP1 = 82;     // P1_R, R = 0..3               (rows 16R .. 16R + 7)
+constexpr int kF = 86;      // F_RI, 6 pairs I < R          (rows 16I + 8 .. 16R - 1)
+constexpr int kGC = 92;     // gamma_C                      (rows 0 .. 63)
+constexpr int kDecayRows = 93;
+constexpr int kVecRows = kDecayRows - 64;
+// index of the block pair (R, I), I < R, among the six
+__host__ __device__ constexpr int pidx(int R, int I) { return R * (R - 1) / 2 + I; }
 constexpr int kNW = 8;      // waves per workgroup (prep, post)
 constexpr int kNT = 64 * kNW;
 constexpr int kLS = 20;     // pitch (floats) of a 16-column slab
@@ -211,12 +235,14 @@ __device__ __forceinline__ const float* chunk_state(const BwdChunkArgs& p, const
   return p.snapshots + ((base + ck.c - 1) * p.H + ck.h) * hs;
 }
 
-// rho (relative decays) of the chunk into rho[64][ld] and the global copy;
-// gm = gamma_m, gq = gamma_C / gamma_m per channel.  Threads 0..DK-1, one
-// channel each; rows past the chunk's end take alpha = 1.
+// The chunk's decays: rho into rho[64][ld] (LDS), the vectors into
+// vec[kVecRows][DK] (LDS, rows counted from kGM), all of it into the global
+// buffer dg ([kDecayRows][DK]).  Threads 0..DK-1, one channel each; rows past
+// the chunk's end take alpha = 1.  Every value is a product of alpha over
+// consecutive rows (or its reciprocal for rho above the reference row).
 template <int DK, bool SG>
 __device__ __forceinline__ void decays(const BwdChunkArgs& p, const Chunk& ck, float* rho, int ld,
-                                       float* rho_g, float* sgm, float* sgq) {
+                                       float* vec, float* dg) {
   const int c = threadIdx.x;
   if (c >= DK) return;
   float a[kC];
@@ -225,29 +251,131 @@ __device__ __forceinline__ void decays(const BwdChunkArgs& p, const Chunk& ck, f
     const int64_t row = (ck.tok0 + r) * p.H + ck.h;
     a[r] = r < ck.nv ? (SG ? p.alpha[row] : p.alpha[row * DK + c]) : 1.f;
   }
-  float gm = 1.f;
+  auto put = [&](int row, float v) {
+    dg[row * DK + c] = v;
+    if (row < kC) rho[row * ld + c] = v;
+    else vec[(row - kGM) * DK + c] = v;
+  };
+  // product of alpha over rows r0 .. r1 (inclusive)
+  auto prod = [&](int r0, int r1) {
+    float x = 1.f;
 #pragma unroll
-  for (int r = 0; r <= kMid; ++r) gm *= a[r];
-  float x = 1.f;
-  rho[kMid * ld + c] = 1.f;
-  rho_g[kMid * DK + c] = 1.f;
+    for (int r = 0; r < kC; ++r)
+      if (r >= r0 && r <= r1) x *= a[r];
+    return x;
+  };
 #pragma unroll
-  for (int r = kMid - 1; r >= 0; --r) {   // sigma_r = prod_{r < i <= m} alpha_i
-    x *= a[r + 1];
-    const float v = 1.f / x;
-    rho[r * ld + c] = v;
-    rho_g[r * DK + c] = v;
+  for (int R = 0; R < 4; ++R) {
+    const int m = 16 * R + 7;
+    float x = 1.f;
+    put(m, 1.f);
+#pragma unroll
+    for (int r = m - 1; r >= 16 * R; --r) {   // 1 / prod_{r < s <= m} alpha_s
+      x *= a[r + 1];
+      put(r, 1.f / x);
+    }
+    x = 1.f;
+#pragma unroll
+    for (int r = m + 1; r < 16 * R + 16; ++r) {   // prod_{m < s <= r} alpha_s
+      x *= a[r];
+      put(r, x);
+    }
   }
-  x = 1.f;
 #pragma unroll
-  for (int r = kMid + 1; r < kC; ++r) {
-    x *= a[r];
-    rho[r * ld + c] = x;
-    rho_g[r * DK + c] = x;
+  for (int R = 0; R < 4; ++R) {
+    put(kGM + R, prod(0, 16 * R + 7));
+    put(kGNM + R, prod(16 * R + 8, kC - 1));
+    put(kS1 + R, prod(16 * R + 8, 16 * R + 15));
+    put(kP1 + R, prod(16 * R, 16 * R + 7));
+#pragma unroll
+    for (int I = 0; I < R; ++I) {
+      put(kE + pidx(R, I), prod(16 * I + 16, 16 * R + 7));
+      put(kF + pidx(R, I), prod(16 * I + 8, 16 * R - 1));
+    }
   }
-  sgm[c] = gm;
-  sgq[c] = x;
-  rho_g[kC * DK + c] = gm;   // gamma_m after the 64 rows
+  put(kGC, prod(0, kC - 1));
+}
+
+// The two 64 x 64 Gram tiles of wave wv, G = lower(Ar Kh^T) with the decay
+// factors of the off-diagonal blocks (row block R = wv / 4 + 2 s, column
+// block I = wv % 4): for I < R the column operand is scaled by S1_I and then
+// E_RI per channel (vec rows from kGM, LDS); blocks above the diagonal are
+// left zero.  On diagonal blocks the entries above the diagonal may be
+// infinite: the caller selects them away.
+template <int DK>
+__device__ __forceinline__ void gram_bw(f4 (&acc)[2], const float* ar, const float* kh, int ld,
+                                        const float* vec, int wv) {
+  const int l = threadIdx.x & 63, i = l & 15, g = l >> 4;
+  const int I = wv & 3;
+#pragma unroll
+  for (int kb = 0; kb < DK / 16; ++kb) {
+    const int k0 = 16 * kb + 4 * g;
+    const f4 bv = *reinterpret_cast<const f4*>(kh + (16 * I + i) * ld + k0);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int R = (wv >> 2) + 2 * s;
+      if (I > R) continue;
+      f4 b = bv;
+      if (I < R) {
+        const f4 s1 = *reinterpret_cast<const f4*>(vec + (kS1 - kGM + I) * DK + k0);
+        const f4 e = *reinterpret_cast<const f4*>(vec + (kE - kGM + pidx(R, I)) * DK + k0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b[j] = (b[j] * s1[j]) * e[j];
+      }
+      const f4 av = *reinterpret_cast<const f4*>(ar + (16 * R + i) * ld + k0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[s] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j], b[j], acc[s], 0, 0, 0);
+    }
+  }
+}
+
+// acc[s] += A B for the wave's tiles of a 64 x DK output, K = the 64 tokens,
+// where the product of output row (token) r and K token u carries the decay
+// between them in factored form:
+//   ROWS (AK: A(m,k) = a[m * lda + k], lower triangular):  row block R, K
+//        block I < R: B rows scaled by S1_I, then E_RI (per output column);
+//   COLS (A(m,k) = a[k * lda + m], i.e. A^T of a lower-triangular array):
+//        row block I, K block R > I: B rows scaled by P1_R, then F_RI.
+// Diagonal K blocks are unscaled, K blocks on the zero side are skipped.
+// B(k, n) = b[k * ldb + n].  Tile s: rows 16 (wv / TN + (8 / TN) s)..,
+// columns 16 (wv % TN).., TN = DK / 16; the scales of the lane's column are
+// read from the chunk's global decay buffer dg.
+template <int DK, bool COLS>
+__device__ __forceinline__ void gsum(f4 (&acc)[(4 * (DK / 16) + kNW - 1) / kNW], const float* a, int lda,
+                                     const float* b, int ldb, int wv, const float* dg) {
+  constexpr int TN = DK / 16, NT = (4 * TN + kNW - 1) / kNW;
+  const int l = threadIdx.x & 63, i = l & 15, g = l >> 4;
+  const int n0 = (wv % TN) * 16;
+  // COLS: P1_R (R = 1..3) and F_RI;  rows: S1_I (I = 0..2) and E_RI
+  float s1v[4], s2v[6];
+#pragma unroll
+  for (int x = 0; x < 3; ++x) s1v[x + (COLS ? 1 : 0)] = dg[((COLS ? kP1 + 1 : kS1) + x) * DK + n0 + i];
+#pragma unroll
+  for (int x = 0; x < 6; ++x) s2v[x] = dg[((COLS ? kF : kE) + x) * DK + n0 + i];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {   // K block (16 tokens)
+    f4 bv;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bv[j] = b[(16 * u + 4 * g + j) * ldb + n0 + i];
+#pragma unroll
+    for (int s = 0; s < NT; ++s) {
+      const int ro = (wv + kNW * s) / TN;   // output row block
+      if (COLS ? (u < ro) : (u > ro)) continue;
+      f4 bs = bv;
+      if (u != ro) {
+        const float s1 = s1v[u];
+        const float s2 = s2v[COLS ? pidx(u, ro) : pidx(ro, u)];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bs[j] = (bs[j] * s1) * s2;
+      }
+      f4 av;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        av[j] = COLS ? a[(16 * u + 4 * g + j) * lda + 16 * ro + i] : a[(16 * ro + i) * lda + 16 * u + 4 * g + j];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[s] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j], bs[j], acc[s], 0, 0, 0);
+    }
+  }
 }
 
 // ---------------------------------------------------------------- prep ------
@@ -263,12 +391,13 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_prep_kernel(BwdChunkArgs p) {
   float* const sQr = sKh + 64 * LD;
   float* const sM = sQr + 64 * LD;   // Diag(beta) X, then M, then T
   float* const sP = sM + 64 * kL64;
-  float* const sgm = sP + 64 * kL64;
-  float* const sgq = sgm + DK;
-  float* const sb = sgq + DK;
-  float* const sV = sb + 64;         // V slab, then Z slab (also the solve's scratch)
+  float* const sgc = sP + 64 * kL64;   // gamma_C
+  float* const sb = sgc + 2 * DK;
+  float* const sV = sb + 64;         // decay vectors, V slab, then Z slab (also the solve's scratch)
   float* const sO = sV + 64 * kLS;   // dO slab
   float* const sS = sO + 64 * kLS;   // S slab [DK][16]
+  float* const sVec = sV;            // steps 1-2: [kVecRows][DK] from kGM
+  static_assert(kVecRows * DK <= (128 + DK) * kLS, "decay vectors fit the slab space");
 
   const int t = threadIdx.x, w = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63, li = l & 15,
             g = l >> 4;
@@ -292,8 +421,8 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_prep_kernel(BwdChunkArgs p) {
     pk[u] = r < nv ? ld_in<BF16>(p.k, x) : 0.f;
     pq[u] = r < nv ? ld_in<BF16>(p.q, x) : 0.f;
   }
-  float* const rho_g = p.rho + ck.wi * (65 * DK);
-  decays<DK, SG>(p, ck, sQr, LD, rho_g, sgm, sgq);   // rho parked in sQr
+  float* const rho_g = p.rho + ck.wi * (kDecayRows * DK);
+  decays<DK, SG>(p, ck, sQr, LD, sVec, rho_g);   // rho parked in sQr
   if (t < 64) sb[t] = t < nv ? p.beta[(ck.tok0 + t) * H + h] : 0.f;
   lds_barrier();
 #pragma unroll
@@ -307,24 +436,55 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_prep_kernel(BwdChunkArgs p) {
   }
   lds_barrier();
 
-  // 2. Diag(beta) X and P
+  // 2. Diag(beta) X and P; both also to the global P/X array (P on and below
+  // the diagonal, X transposed above it) for the post kernel.
   {
     f4 ax[2], ap[2];
     zero(ax);
     zero(ap);
-    mm<64, 64, DK, true, true>(ax, sKr, LD, sKh, LD, w);
-    mm<64, 64, DK, true, true>(ap, sQr, LD, sKh, LD, w);
+    gram_bw<DK>(ax, sKr, sKh, LD, sVec, w);
+    gram_bw<DK>(ap, sQr, sKh, LD, sVec, w);
+    float* const PXg = p.PX + ck.wi * (64 * 64);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       int m0, n0;
       tile_origin<64>(w, s, m0, n0);
+      f4 xt;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int r = m0 + 4 * g + q, c = n0 + li;
-        sM[r * kL64 + c] = c < r ? sb[r] * ax[s][q] : 0.f;
-        sP[r * kL64 + c] = c <= r ? ap[s][q] : 0.f;
+        // (selected, not multiplied by a zero: above the diagonal the factored
+        // products may be infinite)
+        const float x = c < r ? ax[s][q] : 0.f;
+        const float pv = c <= r ? ap[s][q] : 0.f;
+        sM[r * kL64 + c] = sb[r] * x;
+        sP[r * kL64 + c] = pv;
+        if (c <= r) PXg[r * 64 + c] = pv;
+        xt[q] = x;
+      }
+      // X^T above the diagonal: row c, columns r = m0 + 4g .. +3 (> c)
+      if (n0 < m0 || (n0 == m0 && 4 * g > li)) {
+        *reinterpret_cast<f4*>(PXg + (n0 + li) * 64 + m0 + 4 * g) = xt;
+      } else if (n0 == m0) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (4 * g + q > li) PXg[(n0 + li) * 64 + m0 + 4 * g + q] = xt[q];
       }
     }
+    if (t < DK) sgc[t] = sVec[(kGC - kGM) * DK + t];
+  }
+  lds_barrier();
+  // Kr -> Kg = Kr Diag(gamma_mR), Qr -> Qg, Kh -> Ke = Kh Diag(gamma_C / gamma_mR)
+  // (rows of block R): the operands of W, b_c and A_c.
+#pragma unroll
+  for (int u = 0; u < NE; ++u) {
+    const int e = t + u * kNT;
+    const int r = e / DK, c = e % DK;
+    const float gm = sVec[(kGM - kGM + (r >> 4)) * DK + c];
+    const float gq = sVec[(kGNM - kGM + (r >> 4)) * DK + c];
+    sKr[r * LD + c] *= gm;
+    sQr[r * LD + c] *= gm;
+    sKh[r * LD + c] *= gq;
   }
   lds_barrier();
 
@@ -418,7 +578,7 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_prep_kernel(BwdChunkArgs p) {
   Slab R;
   fetch(R, 0);
 
-  // 5. W = T Kr Diag(gamma_m), over Kr
+  // 5. W = T Kg, over Kg
   {
     f4 aw[NTW];
     zero(aw);
@@ -430,14 +590,13 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_prep_kernel(BwdChunkArgs p) {
       int m0, n0;
       tile_origin<DK>(w, s, m0, n0);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) sKr[(m0 + 4 * g + q) * LD + n0 + li] = aw[s][q] * sgm[n0 + li];
+      for (int q = 0; q < 4; ++q) sKr[(m0 + 4 * g + q) * LD + n0 + li] = aw[s][q];
     }
   }
   lds_barrier();
   float* const sW = sKr;
 
-  // 6. A_c = Diag(gamma_C) - W^T Kh Diag(gamma_C / gamma_m), stored in the
-  // chain's fragment order.
+  // 6. A_c = Diag(gamma_C) - W^T Ke, stored in the chain's fragment order.
   {
     f4 aa[NTA];
     zero(aa);
@@ -452,14 +611,14 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_prep_kernel(BwdChunkArgs p) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int r = m0 + 4 * g + q;
-        float v = -sgq[c] * aa[s][q];
-        if (r == c) v += sgm[r] * sgq[r];
+        float v = -aa[s][q];
+        if (r == c) v += sgc[r];
         Ag[frag_a<DK>(r, c)] = v;
       }
     }
   }
 
-  // 7. per 16 value columns: Vn = T V - W S;  b_c = Diag(gamma_m) Qr^T dO - W^T (P^T dO)
+  // 7. per 16 value columns: Vn = T V - W S;  b_c = Qg^T dO - W^T (P^T dO)
   for (int js = 0; js < DV / 16; ++js) {
 #pragma unroll
     for (int u = 0; u < NR; ++u) {
@@ -499,7 +658,7 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_prep_kernel(BwdChunkArgs p) {
     if (tile_live<DK, 16>(w, 0)) {
       f4 v;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) v[q] = sgm[16 * w + 4 * g + q] * b1[0][q] - b2[0][q];
+      for (int q = 0; q < 4; ++q) v[q] = b1[0][q] - b2[0][q];
       *reinterpret_cast<f4*>(bg + frag_s<DK>(js, w, l)) = v;
     }
     lds_barrier();
@@ -596,38 +755,60 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_bwdc_chain_kernel(BwdCh
   if (jw + 1 < steps) step(B, jw + 1);
   const int64_t c = c_hi - steps;   // last chunk done: c + 1
   if (c < 0 && !p.d_state_in) return;
+  // chunks remain but no later window will take them: the caller's max_seqlen
+  // was below this sequence's length (nothing to carry to, nothing written)
+  if (c >= 0 && !p.carry) return;
   float* const dst = c < 0 ? p.d_state_in + hs : p.carry + hs;
 #pragma unroll
   for (int q = 0; q < 4; ++q) dst[int64_t(16 * w + 4 * g + q) * DV + col] = dS[q];
 }
 
 // ---------------------------------------------------------------- post ------
+// Ke dS' for the wave's 16 rows (row block rb = wave): acc += (Kh_rb Diag(gq)) D,
+// Kh [64][LD] (rows = tokens, K = channels), D [DK][kLS] (K = channels, 16
+// columns), gq the block's gamma_C / gamma_mR per channel.
+template <int DK, int LD>
+__device__ __forceinline__ f4 ke_ds(f4 acc, const float* kh, const float* d, const float* gq, int rb) {
+  const int l = threadIdx.x & 63, i = l & 15, g = l >> 4;
+#pragma unroll
+  for (int kb = 0; kb < DK / 16; ++kb) {
+    const int k0 = 16 * kb + 4 * g;
+    const f4 a = *reinterpret_cast<const f4*>(kh + (16 * rb + i) * LD + k0);
+    const f4 sc = *reinterpret_cast<const f4*>(gq + k0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j] * sc[j], d[(k0 + j) * kLS + i], acc, 0, 0, 0);
+  }
+  return acc;
+}
+
 template <int DK, bool BF16, bool SG>
 __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
   constexpr int LD = DK + 4;
   constexpr int NT4 = (4 * (DK / 16) + kNW - 1) / kNW;   // 64 x DK tiles per wave
   constexpr int RED = 4 * DK > kNT ? 4 * DK : kNT;
-  __shared__ __attribute__((aligned(16))) float sm[3 * 64 * LD + 3 * 64 * kL64 + 3 * DK + 2 * 64 +
+  __shared__ __attribute__((aligned(16))) float sm[3 * 64 * LD + 3 * 64 * kL64 + 9 * DK + 3 * 64 +
                                                    RED];
   float* const R1 = sm;               // Kh
-  float* const R2 = R1 + 64 * LD;     // slabs (with R3), then -dW', then Qr, then dg
-  float* const R3 = R2 + 64 * LD;     // Qr (for P), slabs, then Kr
+  float* const R2 = R1 + 64 * LD;     // slabs (with R3), then dW, then Qr, then dg
+  float* const R3 = R2 + 64 * LD;     // slabs, then Kr
   float* const sM = R3 + 64 * LD;     // M
-  float* const sP = sM + 64 * kL64;   // P, then dP, then dM M^T
+  float* const sP = sM + 64 * kL64;   // P, then strict dP, then dM M^T
   float* const sX = sP + 64 * kL64;   // dT, then dM, then Diag(beta) dA
-  float* const sgm = sX + 64 * kL64;
-  float* const sgq = sgm + DK;
-  float* const sdgc = sgq + DK;
+  float* const sGM = sX + 64 * kL64;  // gamma_mR [4][DK]
+  float* const sGQ = sGM + 4 * DK;    // gamma_C / gamma_mR [4][DK]
+  float* const sdgc = sGQ + 4 * DK;
   float* const sb = sdgc + DK;
   float* const sdb = sb + 64;
-  float* const red = sdb + 64;        // [4][DK] or [kNT] partial sums
+  float* const sdpd = sdb + 64;       // diagonal of dP
+  float* const red = sdpd + 64;       // [4][DK] or [kNT] partial sums
   // slab buffers (inside R2 .. R3)
   float* const sO = R2;
   float* const sVn = sO + 64 * kLS;
   float* const sV = sVn + 64 * kLS;
   float* const sdVn = sV + 64 * kLS;
-  float* const sD = sdVn + 64 * kLS;  // dS' Diag(gamma_C / gamma_m) rows, [DK][16]
-  float* const sS = sD + DK * kLS;    // S Diag(gamma_m) rows
+  float* const sD = sdVn + 64 * kLS;  // dS' rows, [DK][16]
+  float* const sS = sD + DK * kLS;    // S rows
 
   const int t = threadIdx.x, w = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63, li = l & 15,
             g = l >> 4;
@@ -638,7 +819,8 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
   Chunk ck;
   if (!locate(p, n, jw, h, ck)) return;
   const int nv = ck.nv;
-  const float* const rho = p.rho + ck.wi * (65 * DK);
+  const float* const rho = p.rho + ck.wi * (kDecayRows * DK);
+  const float* const PXg = p.PX + ck.wi * (64 * 64);
 
   // Inputs of the value-column loop (step 2); the first slab is fetched here,
   // ahead of step 1.
@@ -673,11 +855,9 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
   Slab R;
   fetch(R, 0);
 
-  // 1. decay factors, beta, Kh, Qr, M
-  if (t < DK) {
-    sgm[t] = rho[kC * DK + t];
-    sgq[t] = rho[(kC - 1) * DK + t];
-  }
+  // 1. decay vectors, beta, Kh, M, P
+  for (int e = t; e < 8 * DK; e += kNT)
+    sGM[e] = rho[(e < 4 * DK ? kGM * DK + e : kGNM * DK + e - 4 * DK)];
   if (t < 64) sb[t] = t < nv ? p.beta[(ck.tok0 + t) * H + h] : 0.f;
 #pragma unroll 8
   for (int u = 0; u < 64 * DK / kNT; ++u) {
@@ -686,32 +866,16 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
     const float rh = rho[e];
     const int64_t x = ((ck.tok0 + r) * H + h) * int64_t(DK) + c;
     const float kv = r < nv ? ld_in<BF16>(p.k, x) : 0.f;
-    const float qv = r < nv ? ld_in<BF16>(p.q, x) : 0.f;
     R1[r * LD + c] = kv / rh;
-    R3[r * LD + c] = qv * rh;
   }
   {
     const float* const Mg = p.Mb + ck.wi * (64 * 64);
 #pragma unroll
     for (int u = 0; u < 64 * 64 / kNT; ++u) {
       const int e = t + u * kNT;
-      sM[(e >> 6) * kL64 + (e & 63)] = Mg[e];
-    }
-  }
-  lds_barrier();
-  {
-    f4 ap[2];
-    zero(ap);
-    mm<64, 64, DK, true, true>(ap, R3, LD, R1, LD, w);
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      int m0, n0;
-      tile_origin<64>(w, s, m0, n0);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int r = m0 + 4 * g + q, c = n0 + li;
-        sP[r * kL64 + c] = c <= r ? ap[s][q] : 0.f;
-      }
+      const int r = e >> 6, c = e & 63;
+      sM[r * kL64 + c] = Mg[e];
+      sP[r * kL64 + c] = c <= r ? PXg[e] : 0.f;
     }
   }
   lds_barrier();
@@ -737,23 +901,24 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
     for (int u = 0; u < NS; ++u) {
       const int e = t + u * kNT;
       const int r = e >> 4, j = e & 15;
-      sS[r * kLS + j] = R.s[u] * sgm[r];
+      sS[r * kLS + j] = R.s[u];
     }
     if (t < DK * 4) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int r = 16 * (t >> 6) + 4 * (g) + q;
-        sD[r * kLS + li] = R.d[q] * sgq[r];
+        sD[r * kLS + li] = R.d[q];
       }
     }
     fetch(R, js + 1);
     lds_barrier();
     {
+      // dVn = P^T dO + Ke dS'
       f4 adv[1];
       zero(adv);
       mm<64, 16, 64, false, false>(adv, sP, kL64, sO, kLS, w);
-      mm<64, 16, DK, true, false>(adv, R1, LD, sD, kLS, w);
       if (w < 4) {
+        adv[0] = ke_ds<DK, LD>(adv[0], R1, sD, sGQ + w * DK, w);
 #pragma unroll
         for (int q = 0; q < 4; ++q) sdVn[(16 * w + 4 * g + q) * kLS + li] = adv[0][q];
       }
@@ -763,9 +928,9 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
       }
     }
     lds_barrier();
-    mm<64, DK, 16, true, true>(aq, sO, kLS, sS, kLS, w);
-    mm<64, DK, 16, true, true>(awn, sdVn, kLS, sS, kLS, w);
-    mm<64, DK, 16, true, true>(ah, sVn, kLS, sD, kLS, w);
+    mm<64, DK, 16, true, true>(aq, sO, kLS, sS, kLS, w);      // dO S^T
+    mm<64, DK, 16, true, true>(awn, sdVn, kLS, sS, kLS, w);   // dVn S^T = -dW
+    mm<64, DK, 16, true, true>(ah, sVn, kLS, sD, kLS, w);     // Vn dS'^T = dKe
     mm<64, 64, 16, true, true>(adp, sO, kLS, sVn, kLS, w);
     mm<64, 64, 16, true, true>(adt, sdVn, kLS, sV, kLS, w);
     {
@@ -784,10 +949,15 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
     lds_barrier();
   }
 
-  // 3. gamma_C's gradient: the column sums of dKend' * Kh plus sum_j S dS'
-  // gamma_C, both in the scaled forms.  dP, dT, -dW' to LDS.  The inputs of
-  // Kr and Qr (rebuilt below) are loaded first, so that their latency overlaps
-  // this work.
+  // 3. Into the factored forms: AQ = (dO S^T) Diag(gamma_mR) and
+  // AHe = dKe Diag(gamma_C / gamma_mR) per row block R (kept apart from the
+  // other terms of AH: AHe * Kh = dKe * Ke is the gradient through the
+  // chunk-end decays gamma_C / gamma_r, which enters d log(alpha)_t as the sum
+  // over the rows before t; folding it into the per-row sums instead would
+  // pair it with its own total on the last row, and the pair cancels).
+  // gamma_C's other gradient: gamma_C sum_j S dS'.  dW, strict dP and its
+  // diagonal, dT to LDS.  The inputs of Kr and Qr (rebuilt below) are loaded
+  // first, so that their latency overlaps this work.
   constexpr int NE = 64 * DK / kNT;
   float pk[NE], pr[NE];
 #pragma unroll
@@ -797,19 +967,22 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
     pk[u] = r < nv ? ld_in<BF16>(p.k, ((ck.tok0 + r) * H + h) * int64_t(DK) + c) : 0.f;
     pr[u] = rho[e];
   }
+  f4 ahe[NT4];
 #pragma unroll
   for (int s = 0; s < NT4; ++s) {
     if (!tile_live<64, DK>(w, s)) break;
     int m0, n0;
     tile_origin<DK>(w, s, m0, n0);
-    float v = 0.f;
+    const int c = n0 + li, rb = m0 >> 4;
+    const float gm = sGM[rb * DK + c], gq = sGQ[rb * DK + c];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) v += ah[s][q] * R1[(m0 + 4 * g + q) * LD + n0 + li];
-    v += __shfl_xor(v, 16);
-    v += __shfl_xor(v, 32);
-    if (g == 0) red[(m0 >> 4) * DK + n0 + li] = v;
+    for (int q = 0; q < 4; ++q) {
+      aq[s][q] *= gm;
+      ahe[s][q] = ah[s][q] * gq;
+      ah[s][q] = 0.f;
+    }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) R2[(m0 + 4 * g + q) * LD + n0 + li] = -awn[s][q];
+    for (int q = 0; q < 4; ++q) R2[(m0 + 4 * g + q) * LD + c] = -awn[s][q];
   }
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
@@ -818,12 +991,13 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int r = m0 + 4 * g + q, c = n0 + li;
-      sP[r * kL64 + c] = c <= r ? adp[s][q] : 0.f;
+      sP[r * kL64 + c] = c < r ? adp[s][q] : 0.f;
+      if (c == r) sdpd[r] = adp[s][q];
       sX[r * kL64 + c] = adt[s][q];
     }
   }
   lds_barrier();
-  if (t < DK) sdgc[t] = red[t] + red[DK + t] + red[2 * DK + t] + red[3 * DK + t] + dgcs;
+  if (t < DK) sdgc[t] = rho[kGC * DK + t] * dgcs;
 #pragma unroll
   for (int u = 0; u < NE; ++u) {   // Kr
     const int e = t + u * kNT;
@@ -831,7 +1005,8 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
   }
   lds_barrier();
 
-  // 4. dT += dW' Kr^T;  AR = Diag(beta) M^T dW'
+  // 4. dT += dW Kg^T (Kg rows of block R: Kr Diag(gamma_mR));
+  //    AR = Diag(gamma_mR) applied to dKg = Diag(beta) M^T dW
   float pq[NE];
 #pragma unroll
   for (int u = 0; u < NE; ++u) {
@@ -844,7 +1019,25 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
   {
     f4 at[2];
     zero(at);
-    mm<64, 64, DK, true, true>(at, R2, LD, R3, LD, w);
+    // (A = dW rows r, B = Kr rows s of column block n0: B scaled by gamma_m of
+    // that block, per channel k)
+    const int i = li;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      int m0, n0;
+      tile_origin<64>(w, s2, m0, n0);
+      const float* const gmb = sGM + (n0 >> 4) * DK;
+#pragma unroll 2
+      for (int kb = 0; kb < DK / 16; ++kb) {
+        const int k0 = 16 * kb + 4 * g;
+        const f4 av = *reinterpret_cast<const f4*>(R2 + (m0 + i) * LD + k0);
+        const f4 bv = *reinterpret_cast<const f4*>(R3 + (n0 + i) * LD + k0);
+        const f4 sc = *reinterpret_cast<const f4*>(gmb + k0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          at[s2] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j], bv[j] * sc[j], at[s2], 0, 0, 0);
+      }
+    }
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       int m0, n0;
@@ -859,8 +1052,9 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
     if (!tile_live<64, DK>(w, s)) break;
     int m0, n0;
     tile_origin<DK>(w, s, m0, n0);
+    const float gm = sGM[(m0 >> 4) * DK + n0 + li];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) ar[s][q] *= sb[m0 + 4 * g + q];
+    for (int q = 0; q < 4; ++q) ar[s][q] *= sb[m0 + 4 * g + q] * gm;
   }
   lds_barrier();
 #pragma unroll
@@ -870,9 +1064,9 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
   }
   lds_barrier();
 
-  // 5. AH += dP^T Qr;  AQ += dP Kh;  dbeta from T
-  mm<64, DK, 64, false, false, NT4, tri_dk<DK>(3)>(ah, sP, kL64, R2, LD, w);
-  mm<64, DK, 64, true, false, NT4, tri_dk<DK>(2)>(aq, sP, kL64, R1, LD, w);
+  // 5. AH += dP^T Qr;  AQ += dP Kh (strict dP, factored);  dbeta from T
+  gsum<DK, true>(ah, sP, kL64, R2, LD, w, rho);
+  gsum<DK, false>(aq, sP, kL64, R1, LD, w, rho);
   {   // column sums of M o dT (M is lower triangular), 8 rows per thread
     const int col = t & 63, part = t >> 6;
     float s = 0.f;
@@ -908,12 +1102,11 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
   }
   lds_barrier();
   {
-    f4 ada[2], axx[2];
+    f4 ada[2];
     zero(ada);
-    zero(axx);
     mm<64, 64, 64, false, false>(ada, sM, kL64, sP, kL64, w);   // M^T (dM M^T)
-    mm<64, 64, DK, true, true>(axx, R3, LD, R1, LD, w);          // Kr Kh^T
-    // dA = -M^T dM M^T (strictly lower); dbeta_r += sum_s dA_rs X_rs
+    // dA = -M^T dM M^T (strictly lower); dbeta_r += sum_s dA_rs X_rs, X from
+    // the prep kernel (stored transposed above the diagonal)
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       int m0, n0;
@@ -922,11 +1115,9 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int r = m0 + 4 * g + q, c = n0 + li;
-        // (selected, not multiplied by a zero: above the diagonal Kr Kh^T holds
-        // rho_r / rho_s > 1, which overflows at strong decay)
         const float da = c < r ? -ada[s][q] : 0.f;
         ada[s][q] = da;
-        v[q] = c < r ? da * axx[s][q] : 0.f;
+        v[q] = c < r ? da * PXg[c * 64 + r] : 0.f;
       }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -953,8 +1144,9 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
   }
   lds_barrier();
 
-  // 6. AR += B Kh;  AH += B^T Kr  (B = Diag(beta) dA).  The decays of this
-  // lane's output elements and the alphas of step 8 are loaded first.
+  // 6. AR += B Kh;  AH += B^T Kr  (B = Diag(beta) dA, factored).  The decays
+  // of this lane's output elements are loaded first, the alphas of step 8
+  // after the products.
   float rh[NT4][4];
 #pragma unroll
   for (int s = 0; s < NT4; ++s) {
@@ -964,6 +1156,8 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
     for (int q = 0; q < 4; ++q)
       rh[s][q] = tile_live<64, DK>(w, s) ? rho[(m0 + 4 * g + q) * DK + n0 + li] : 1.f;
   }
+  gsum<DK, false>(ar, sX, kL64, R1, LD, w, rho);
+  gsum<DK, true>(ah, sX, kL64, R3, LD, w, rho);
   constexpr int NP = kNT / DK, RP = 64 / NP;
   float al[SG ? 1 : RP];
   if constexpr (SG) {
@@ -977,10 +1171,10 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
       al[i] = r < nv ? p.alpha[((ck.tok0 + r) * H + h) * int64_t(DK) + c] : 1.f;
     }
   }
-  mm<64, DK, 64, true, false, NT4, tri_dk<DK>(2)>(ar, sX, kL64, R1, LD, w);
-  mm<64, DK, 64, false, false, NT4, tri_dk<DK>(3)>(ah, sX, kL64, R3, LD, w);
 
-  // 7. dq, dk; dg = AQ Qr + AR Kr - AH Kh (+ gamma_C's gradient on the last row)
+  // 7. dq, dk (the diagonal of dP added apart: q_r . k_r carries no decay);
+  // dg = AQ Qr + AR Kr - AH Kh without AHe (+ gamma_C S dS' on the last row);
+  // z = AHe Kh into R1 (each lane overwrites only the Kh entries it read)
   float dgv[NT4][4];
 #pragma unroll
   for (int s = 0; s < NT4; ++s) {
@@ -995,10 +1189,12 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
       float dg = aq[s][q] * qr + ar[s][q] * kr - ah[s][q] * kh;
       if (r == kC - 1) dg += sdgc[c];
       dgv[s][q] = dg;
+      R1[r * LD + c] = ahe[s][q] * kh;
       if (r < nv) {
         const int64_t x = ((ck.tok0 + r) * H + h) * int64_t(DK) + c;
-        p.dq[x] = aq[s][q] * rh[s][q];
-        p.dk[x] = ar[s][q] * rh[s][q] + ah[s][q] / rh[s][q];
+        const float pd = sdpd[r];
+        p.dq[x] = aq[s][q] * rh[s][q] + pd * (kh * rh[s][q]);
+        p.dk[x] = ar[s][q] * rh[s][q] + (ah[s][q] + ahe[s][q]) / rh[s][q] + pd * (qr / rh[s][q]);
       }
     }
   }
@@ -1013,22 +1209,32 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
   }
   if (t < 64 && t < nv) p.dbeta[(ck.tok0 + t) * H + h] = sdb[t];
   lds_barrier();
-  // 8. dlog(alpha)_t = sum_{r >= t} dg_r within the chunk; dalpha = that / alpha.
-  // Each channel's 64 rows in NP parts of RP rows: sums from the end within a
-  // part, plus the totals of the later parts.
+  // 8. dlog(alpha)_t = sum_{r >= t} dg_r + sum_{r < t} z_r within the chunk;
+  // dalpha = that / alpha.  Each channel's 64 rows in NP parts of RP rows:
+  // sums from the end (dg) and from the start (z) within a part, plus the
+  // totals of the later (dg) and earlier (z) parts.
   {
     const int c = t % DK, pp = t / DK;
+    float* const red2 = sGM;   // [NP][DK] over sGM and sGQ (no longer needed)
+    static_assert(NP * DK <= 8 * DK && NP * DK <= RED, "partial sums fit");
     float v[RP];
-    float run = 0.f;
+    float run = 0.f, zr = 0.f;
 #pragma unroll
     for (int i = RP - 1; i >= 0; --i) {
       run += R2[(pp * RP + i) * LD + c];
       v[i] = run;
     }
+#pragma unroll
+    for (int i = 0; i < RP; ++i) {
+      v[i] += zr;
+      zr += R1[(pp * RP + i) * LD + c];
+    }
     red[pp * DK + c] = run;
+    red2[pp * DK + c] = zr;
     lds_barrier();
     float off = 0.f;
     for (int q2 = pp + 1; q2 < NP; ++q2) off += red[q2 * DK + c];
+    for (int q2 = 0; q2 < pp; ++q2) off += red2[q2 * DK + c];
     if constexpr (SG) {
 #pragma unroll
       for (int i = 0; i < RP; ++i) R2[(pp * RP + i) * LD + c] = v[i] + off;
@@ -1086,8 +1292,9 @@ void launch_dk(const BwdChunkArgs& a, int stage, hipStream_t st) {
 }  // namespace
 
 size_t backward_chunk_floats(int DK, int DV) {
-  // A_c, b_c, dS', M, Vn, rho (+ gamma_m) per chunk-head
-  return size_t(DK) * DK + 2 * size_t(DK) * DV + 64 * 64 + 64 * size_t(DV) + 65 * size_t(DK);
+  // A_c, b_c, dS', M, Vn, the decays, P and X per chunk-head
+  return size_t(DK) * DK + 2 * size_t(DK) * DV + 64 * 64 + 64 * size_t(DV) + kDecayRows * size_t(DK) +
+         64 * 64;
 }
 
 int launch_backward_chunk(const BwdChunkArgs& a, int stage, void* stream, const char** msg) {

@@ -34,6 +34,7 @@ struct PrefillArgs {
   bool alpha_scalar;           // alpha is [tokens, H]: one gate per token and head
   bool states_only;            // with snapshots: o is not written (the caller needs the
                                // snapshots only; o must still point at valid memory)
+  int64_t seg_budget;          // staged form: bytes of slots per segment at most (0: default)
 };
 
 struct DecodeArgs {
@@ -72,7 +73,9 @@ struct PoolDecodeArgs {
 // gradients).  Window buffers hold, per chunk-head of the window (index
 // (n * H + h) * win_k + j, j = reverse index within the window):
 //   Ac [DK][DK], bc [DK][DV], dSend [DK][DV] (these three in the pass's
-//   fragment order), Mb [64][64], Vnb [64][DV], rho [65][DK] (row 64: gamma_m).
+//   fragment order), Mb [64][64], PX [64][64] (P on and below the diagonal,
+//   X^T above it), Vnb [64][DV], rho [93][DK] (the chunk's decays: rows 0..63
+//   relative to each 16-row block's reference row, then per-channel vectors).
 struct BwdChunkArgs {
   int N, H, DK, DV;
   int64_t T;                   // tokens per sequence (fixed length)
@@ -102,9 +105,19 @@ struct BwdChunkArgs {
   float* bc;
   float* dSend;
   float* Mb;
+  float* PX;
   float* Vnb;
   float* rho;
 };
+
+// Tuning overrides (kda_internal_set_tuning); 0 everywhere = choose by shape.
+struct Tuning {
+  int prefill_form;   // 0 by shape, 1 one-kernel (fused), 2 staged
+  int prefill_nsub;   // 0 by shape, else value blocks of 16 per workgroup
+  int prefill_seg;    // 0 by size, else chunks per staged segment
+  int bwd_window;     // 0 by size, else chunks per backward window
+};
+Tuning tuning();
 
 // Launchers return 0 on success, else a non-zero code and a static message.
 int launch_prefill(const PrefillArgs& a, void* stream, const char** msg);
@@ -112,6 +125,7 @@ int launch_decode(const DecodeArgs& a, void* stream, const char** msg);
 int launch_decode_pool(const PoolDecodeArgs& a, void* stream, const char** msg);
 int launch_backward_chunk(const BwdChunkArgs& a, int stage, void* stream, const char** msg);
 size_t backward_chunk_floats(int DK, int DV);   // window-buffer floats per chunk-head
-size_t prefill_workspace_bytes(int N, int64_t T_total, int H, int DK, int DV, bool varlen);
+size_t prefill_workspace_bytes(int N, int64_t T_total, int H, int DK, int DV, bool varlen,
+                               int64_t seg_budget = 0);
 
 }  // namespace kda

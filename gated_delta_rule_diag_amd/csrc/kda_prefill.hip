@@ -7,20 +7,29 @@
 // Memoryを使う方法": the chunkwise algorithm rests on a diagonal-plus-low-rank
 // transition).  The pages print no chunk formula; the one used here follows
 // from unrolling the recurrence inside a chunk of n <= 64 tokens with
-// incoming state S (d_k x d_v, rows = key channels).  With m = 31 the chunk's
-// reference position and f_r = prod_{s<=r} alpha_s / prod_{s<=m} alpha_s
-// (per key channel; > 1 before m, <= 1 after it):
-//     Kl = K * f,   Ql = Q * f,   Kr = K / f           (row-wise, per channel)
-//     A  = Diag(beta) strict_lower(Kl Kr^T)            (= beta_r k_r.(decayed k_i))
-//     P  = lower(Ql Kr^T)
-//     T  = (I + A)^-1 Diag(beta)                       (unit-lower solve)
-//     S_B = Diag(gamma_m) S                            (state decayed to m)
-//     X  = V - Kl S_B ;  U = T X                       (values actually written)
-//     O  = Ql S_B + P U
-//     S' = Diag(gamma_n) S + Diag(gamma_n / gamma_m) Kr^T U
+// incoming state S (d_k x d_v, rows = key channels).  Per key channel, with
+// gamma_r the product of alpha over the chunk's rows 0..r:
+//     K_g = K * gamma,  Q_g = Q * gamma,  K_e = K * (gamma_n / gamma)
+//     A   = Diag(beta) strict_lower(G_K),  P = lower(G_Q),
+//           G_K[r,i] = sum_c k_rc k_ic gamma_rc / gamma_ic  (G_Q: q_r)
+//     T   = (I + A)^-1 Diag(beta)                 (unit-lower solve)
+//     U   = T (V - K_g S)                         (values actually written)
+//     O   = Q_g S + P U
+//     S'  = Diag(gamma_n) S + K_e^T U
 // All products are dense MFMA contractions.  bf16 inputs use split bf16
 // operands (x = hi + lo, three MFMAs per product) so that the products carry
 // ~16 significant bits; fp32 inputs use the fp32 MFMA.  Accumulation is fp32.
+//
+// Decay factors are products of alpha (no exp / log).  The Gram matrices need
+// gamma_r / gamma_i split into a row factor and a column factor; each 16-row
+// block R takes its own reference row m_R = 16 R + 7, so a factor spans at
+// most 8 tokens and stays within alpha^-8 (finite in fp32 down to alpha ~ 2e-5):
+//     Kl = K * rho,  Ql = Q * rho,  Kr = K / rho,   rho_r = gamma_r / gamma_m(R(r))
+// Diagonal 16x16 blocks are Kl_R Kr_R^T.  An off-diagonal block (R, I < R)
+// also needs gamma_mR / gamma_mI, which can underflow where the block's
+// entries do not; its column operand is therefore rescaled in two steps,
+// first to the end of block I (Kr_I * S1_I <= 1), then on to m_R (* E_RI):
+// every intermediate stays within the range of the true entries.
 //
 // One workgroup (4 waves) per (sequence, head, value slab): the value columns
 // of the state evolve independently, so the sequential pass over the chunks
@@ -85,17 +94,22 @@ struct Lay {
   static constexpr int SZ_X = (kC * P_OP > 2 * kC * P_T) ? kC * P_OP : 2 * kC * P_T;
   static constexpr int OFF_A = OFF_X;                        // fp32 [64][68]
   static constexpr int OFF_P = OFF_X + kC * P_T;             // [64][64]
-  static constexpr int OFF_SBT = OFF_X;                      // S_B^T [16][DK]  (after the solve)
+  static constexpr int OFF_SBT = OFF_X;                      // S^T [16][DK]  (after the solve)
   static constexpr int OFF_XT = OFF_SBT + 16 * P_OP;         // X^T [16][64]
   static constexpr int OFF_UT = OFF_XT + 16 * P_T;           // U^T [16][64]
   static constexpr int OFF_T = OFF_X + SZ_X;                 // T [64][64] (fp32 L^-1 first)
   static constexpr int RG = 16;                              // row groups (4 rows) of the decay prep
-  static constexpr int OFF_GP = OFF_T;                       // group products [RG][DK] (step 1 only)
-  static constexpr int OFF_GM = OFF_T + kC * P_T;           // gamma_m [DK]
-  static constexpr int OFF_DL = OFF_GM + DK * 4;             // gamma_n / gamma_m [DK]
-  static constexpr int OFF_GN = OFF_DL + DK * 4;             // gamma_n [DK]
+  // Steps 1-2 only (the T space is free until the solve):
+  static constexpr int OFF_GP = OFF_T;                       // group products [RG][DK]
+  static constexpr int OFF_S1 = OFF_GP + RG * DK * 4;        // S1_I = gamma_(16I+15) / gamma_mI [4][DK]
+  static constexpr int OFF_E = OFF_S1 + 4 * DK * 4;          // E_RI = gamma_mR / gamma_(16I+15) [6][DK]
+  static constexpr int OFF_GNM = OFF_E + 6 * DK * 4;         // gamma_n / gamma_mI [4][DK]
+  // Kept for the whole chunk:
+  static constexpr int OFF_GM = OFF_T + kC * P_T;           // gamma_mR [4][DK]
+  static constexpr int OFF_GN = OFF_GM + 4 * DK * 4;         // gamma_n [DK]
   static constexpr int OFF_BE = OFF_GN + DK * 4;             // beta [64]
   static constexpr int TOTAL = OFF_BE + kC * 4;
+  static_assert(OFF_GNM + 4 * DK * 4 <= OFF_T + kC * P_T, "decay vectors fit the T space");
   static_assert(NT == RG * DK / 4, "decay prep: one thread per (channel quad, row group)");
   static_assert(RG * DK * 4 <= kC * P_T, "group products fit the T space");
   static_assert(OFF_UT + 16 * P_T <= OFF_X + kC * P_T, "step buffers fit in A's space");
@@ -405,9 +419,10 @@ __device__ __forceinline__ void xpose16_f32(const float (&a4)[4], int rb, int cb
 }
 
 // Transposes the columns of a [64][DK] LDS operand array (rows = tokens) into
-// a [DK][64] array, scaled per column by scale[] (LDS): the work is spread
-// over the NW waves.
-template <bool BF, int DK, int NW>
+// a [DK][64] array, scaled per column by scale[] (LDS; with PER_RB, rows of
+// 16-row block rb by scale[rb * DK + column]): the work is spread over the NW
+// waves.
+template <bool BF, int DK, int NW, bool PER_RB>
 __device__ __forceinline__ void xpose_lds(const char* src, int spitch, const float* scale, char* dst,
                                           int dpitch) {
   const int l = lane_id(), lr = l & 15, lg = l >> 4, w = threadIdx.x >> 6;
@@ -417,8 +432,9 @@ __device__ __forceinline__ void xpose_lds(const char* src, int spitch, const flo
 #pragma unroll
     for (int i = 0; i < NU / NW; ++i) {
       const int u = w + NW * i, rb = u & 3, kc = u >> 2;
+      const float* sc = PER_RB ? scale + rb * DK : scale;
       const Mma<true>::Frag a = Mma<true>::load(src, spitch, 16 * rb, kc);
-      xpose32_bf<false>(a, rb, kc, scale[32 * kc + lr], scale[32 * kc + 16 + lr], dst, dpitch);
+      xpose32_bf<false>(a, rb, kc, sc[32 * kc + lr], sc[32 * kc + 16 + lr], dst, dpitch);
     }
   } else {
     constexpr int NU = 4 * (DK / 16);   // (row block, 16-column block) units
@@ -426,11 +442,50 @@ __device__ __forceinline__ void xpose_lds(const char* src, int spitch, const flo
 #pragma unroll
     for (int i = 0; i < NU / NW; ++i) {
       const int u = w + NW * i, rb = u & 3, cb = u >> 2;
+      const float* sc = PER_RB ? scale + rb * DK : scale;
       const float4 v = *reinterpret_cast<const float4*>(src + (16 * rb + lr) * spitch + 4 * (16 * cb + 4 * lg));
       const float a4[4] = {v.x, v.y, v.z, v.w};
-      xpose16_f32(a4, rb, cb, scale[16 * cb + lr], dst, dpitch);
+      xpose16_f32(a4, rb, cb, sc[16 * cb + lr], dst, dpitch);
     }
   }
+}
+
+// A fragment of the column operand Kr with every K (channel) element scaled
+// by s1[k] and then by e[k] (two roundings, so that no intermediate leaves the
+// range of the result).  Split bf16: the lane's 8 channels 32kc + 8lg .. +7
+// are rebuilt in fp32, scaled and split again; fp32: channel 4kc + lg.
+__device__ __forceinline__ float bf_lo16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ Mma<true>::Frag rescale_frag(const Mma<true>::Frag& f, const float* s1,
+                                                       const float* e, int kc) {
+  const int k0 = 32 * kc + 8 * (lane_id() >> 4);
+  const float4 sa = *reinterpret_cast<const float4*>(s1 + k0), sb = *reinterpret_cast<const float4*>(s1 + k0 + 4);
+  const float4 ea = *reinterpret_cast<const float4*>(e + k0), eb = *reinterpret_cast<const float4*>(e + k0 + 4);
+  const float sv[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
+  const float ev[8] = {ea.x, ea.y, ea.z, ea.w, eb.x, eb.y, eb.z, eb.w};
+  const uint4 hi = __builtin_bit_cast(uint4, f.hi), lo = __builtin_bit_cast(uint4, f.lo);
+  const uint32_t hw[4] = {hi.x, hi.y, hi.z, hi.w}, lw[4] = {lo.x, lo.y, lo.z, lo.w};
+  uint32_t nh[4], nl[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float x0 = ((bf_lo16(hw[j]) + bf_lo16(lw[j])) * sv[2 * j]) * ev[2 * j];
+    const float x1 = ((bf_hi16(hw[j]) + bf_hi16(lw[j])) * sv[2 * j + 1]) * ev[2 * j + 1];
+    uint16_t h0, l0, h1, l1;
+    split(x0, h0, l0);
+    split(x1, h1, l1);
+    nh[j] = uint32_t(h0) | (uint32_t(h1) << 16);
+    nl[j] = uint32_t(l0) | (uint32_t(l1) << 16);
+  }
+  Mma<true>::Frag r;
+  r.hi = __builtin_bit_cast(bf8, make_uint4(nh[0], nh[1], nh[2], nh[3]));
+  r.lo = __builtin_bit_cast(bf8, make_uint4(nl[0], nl[1], nl[2], nl[3]));
+  return r;
+}
+
+__device__ __forceinline__ float rescale_frag(float f, const float* s1, const float* e, int kc) {
+  const int k = 4 * kc + (lane_id() >> 4);
+  return (f * s1[k]) * e[k];
 }
 
 // Destination of output stores for rows past the end of a sequence, and of
@@ -465,53 +520,53 @@ __device__ __forceinline__ void quad_map(int t, int& cq, int& grp) {
   grp = t / QUADS;
 }
 
-// One wave's tiles of the intra-chunk Gram matrices, A = Kl Kr^T (type 0)
-// and P = Ql Kr^T (type 1): up to three (type, R, I) tiles (type < 0:
-// unused), each computed transposed (Kr rows as the first operand) so that a
-// lane ends up with four consecutive columns of one row.  Row and column blocks shared by the tiles are loaded once per K
-// chunk (this step is bound by LDS read bandwidth, not by the MFMA rate).
-template <bool BF, int DK, int T0, int R0, int I0, int T1, int R1, int I1, int T2, int R2, int I2>
-__device__ __forceinline__ void gram_tiles(const char* sKl, const char* sQl, const char* sKr,
-                                           f4 (&acc)[3]) {
+// Index of the off-diagonal block (R, I), I < R, in the [6][DK] E vectors.
+__host__ __device__ constexpr int eidx(int R, int I) { return R * (R - 1) / 2 + I; }
+
+// One wave's tiles of the intra-chunk Gram matrices A = Kl Kr^T (type 0) and
+// P = Ql Kr^T (type 1) for the block pair (R, I), plus with XD >= 0 the
+// diagonal tile (type XD, R, R).  For I < R the column operand Kr_I is scaled
+// by S1_I and then E_RI (the decay from the tokens of block I to the
+// reference row of block R, see the top of the file).  Tiles are computed
+// transposed (Kr rows as the first operand) so that a lane ends up with four
+// consecutive columns of one row; operands shared by the tiles are loaded once
+// per K chunk (this step is bound by LDS read bandwidth, not by the MFMA rate).
+template <bool BF, int DK, int R, int I, int XD>
+__device__ __forceinline__ void gram_group(const char* sKl, const char* sQl, const char* sKr,
+                                           const float* sS1, const float* sE, f4 (&acc)[3]) {
   using M = Mma<BF>;
   constexpr int P = DK * 4 + 16;
 #pragma unroll
   for (int kc = 0; kc < DK / M::KU; ++kc) {
-    const auto c0 = M::load(sKr, P, 16 * I0, kc);
-    const auto r0 = M::load(T0 == 0 ? sKl : sQl, P, 16 * R0, kc);
-    acc[0] = M::mma(c0, r0, acc[0]);
-    if constexpr (T1 >= 0) {
-      const auto c1 = (I1 == I0) ? c0 : M::load(sKr, P, 16 * I1, kc);
-      const auto r1 = (T1 == T0 && R1 == R0) ? r0 : M::load(T1 == 0 ? sKl : sQl, P, 16 * R1, kc);
-      acc[1] = M::mma(c1, r1, acc[1]);
-      if constexpr (T2 >= 0) {
-        const auto c2 = (I2 == I0) ? c0 : ((I2 == I1) ? c1 : M::load(sKr, P, 16 * I2, kc));
-        const auto r2 = (T2 == T0 && R2 == R0)
-                            ? r0
-                            : ((T2 == T1 && R2 == R1) ? r1 : M::load(T2 == 0 ? sKl : sQl, P, 16 * R2, kc));
-        acc[2] = M::mma(c2, r2, acc[2]);
-      }
+    auto c = M::load(sKr, P, 16 * I, kc);
+    if constexpr (I < R) c = rescale_frag(c, sS1 + I * DK, sE + eidx(R, I) * DK, kc);
+    const auto rk = M::load(sKl, P, 16 * R, kc);
+    const auto rq = M::load(sQl, P, 16 * R, kc);
+    acc[0] = M::mma(c, rk, acc[0]);
+    acc[1] = M::mma(c, rq, acc[1]);
+    if constexpr (XD >= 0) {
+      const auto cd = M::load(sKr, P, 16 * R, kc);
+      acc[2] = M::mma(cd, XD == 0 ? rk : rq, acc[2]);
     }
   }
 }
 
 // Steps 1-3 of one chunk (everything that does not depend on the state):
 // decay factors and decayed operands, the Gram tiles A and P, and
-// T = (I + A)^-1 Diag(beta).  On return the LDS holds Kl, Ql,
-// Kg = Diag(gamma_n / gamma_m) Kr^T (in the Kr^T array), T, P and
-// gamma_m, gamma_n / gamma_m, gamma_n for the chunk.  av/kv/qv are this
-// thread's 4 rows (4g .. 4g+3) of 4 channels (4c .. 4c+3), c = t % (DK/4),
-// g = t / (DK/4) (rows past the sequence end: alpha = 1, k = q = 0), bev is
-// beta of token (threadIdx.x & 63) (0 past the end).
+// T = (I + A)^-1 Diag(beta).  On return the LDS holds Kl, Ql (CONVERT: K_g and
+// Q_g in their place), K_e^T (in the Kr^T array), T, P, gamma_mR of the four
+// row blocks and gamma_n.  av/kv/qv are this thread's 4 rows (4g .. 4g+3) of
+// 4 channels (4c .. 4c+3), c = t % (DK/4), g = t / (DK/4) (rows past the
+// sequence end: alpha = 1, k = q = 0), bev is beta of token (threadIdx.x & 63)
+// (0 past the end).
 // after_gram() runs between steps 2 and 3 (callers issue global loads there,
 // when the memory pipeline is idle).
-template <int DK, bool BF, typename Hook>
+template <int DK, bool BF, bool CONVERT, typename Hook>
 __device__ __forceinline__ void prep_chunk(char* smem, const float4 (&av)[4], const float4 (&kv)[4],
                                            const float4 (&qv)[4], float bev, Hook&& after_gram) {
   using L = Lay<DK>;
   constexpr int NW = L::NW;
   constexpr int NT = L::NT;
-  constexpr int RG = L::RG;        // row groups of 4 rows
   char* const sKl = smem + L::OFF_KL;
   char* const sQl = smem + L::OFF_QL;
   char* const sKrT = smem + L::OFF_KRT;
@@ -521,8 +576,10 @@ __device__ __forceinline__ void prep_chunk(char* smem, const float4 (&av)[4], co
   char* const sT = smem + L::OFF_T;
   float* const sLi = reinterpret_cast<float*>(smem + L::OFF_T);
   float* const sGP = reinterpret_cast<float*>(smem + L::OFF_GP);
+  float* const sS1 = reinterpret_cast<float*>(smem + L::OFF_S1);
+  float* const sE = reinterpret_cast<float*>(smem + L::OFF_E);
+  float* const sGNM = reinterpret_cast<float*>(smem + L::OFF_GNM);
   float* const sGM = reinterpret_cast<float*>(smem + L::OFF_GM);
-  float* const sDL = reinterpret_cast<float*>(smem + L::OFF_DL);
   float* const sGN = reinterpret_cast<float*>(smem + L::OFF_GN);
   float* const sBe = reinterpret_cast<float*>(smem + L::OFF_BE);
   const int t = threadIdx.x;
@@ -537,6 +594,14 @@ __device__ __forceinline__ void prep_chunk(char* smem, const float4 (&av)[4], co
   (void)l;
   auto mul4 = [](float4 a, float4 b) { return make_float4(a.x * b.x, a.y * b.y, a.z * b.z, a.w * b.w); };
   auto gp4 = [&](int g) { return *reinterpret_cast<const float4*>(sGP + g * DK + c0); };
+  const float4 one4 = make_float4(1.f, 1.f, 1.f, 1.f);
+  // product of the group products g0 .. g1 (inclusive; empty: 1)
+  auto gprod = [&](int g0, int g1) {
+    float4 x = one4;
+    for (int g = g0; g <= g1; ++g) x = mul4(x, gp4(g));
+    return x;
+  };
+  auto st4v = [&](float* dst, float4 x) { *reinterpret_cast<float4*>(dst + c0) = x; };
 
   // ---- step 1: decay factors and decayed operands ------------------------
   {
@@ -546,62 +611,88 @@ __device__ __forceinline__ void prep_chunk(char* smem, const float4 (&av)[4], co
   }
   lds_barrier();
   {
-    float4 krs[4];
-    constexpr int half = RG / 2;  // groups 0..7 = rows 0..31, up to the reference row 31
-    if (grp >= half) {
-      // rows after the reference: f = prod_{m < s <= r} alpha_s <= 1
-      float4 P = make_float4(1.f, 1.f, 1.f, 1.f);
-      for (int g2 = half; g2 < grp; ++g2) P = mul4(P, gp4(g2));
+    // Row r of block R = r / 16 (reference row m_R = 16R + 7, the last row of
+    // group 4R + 1): rho_r = gamma_r / gamma_mR.
+    const int R = grp >> 2;
+    if ((grp & 3) >= 2) {
+      // rows after the reference: rho = prod_{m_R < s <= r} alpha_s <= 1
+      float4 P = gprod(4 * R + 2, grp - 1);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         P = mul4(P, av[i]);
         const float4 iv = make_float4(rcp(P.x), rcp(P.y), rcp(P.z), rcp(P.w));
         const int r = r0 + i;
-        const float4 a = mul4(kv[i], P), b = mul4(qv[i], P);
-        krs[i] = mul4(kv[i], iv);
+        const float4 a = mul4(kv[i], P), b = mul4(qv[i], P), c = mul4(kv[i], iv);
         const float xa[4] = {a.x, a.y, a.z, a.w}, xb[4] = {b.x, b.y, b.z, b.w};
-        const float xc[4] = {krs[i].x, krs[i].y, krs[i].z, krs[i].w};
+        const float xc[4] = {c.x, c.y, c.z, c.w};
         st4<BF>(sKl, L::P_OP, r, c0, xa);
         st4<BF>(sQl, L::P_OP, r, c0, xb);
         st4<BF>(sKr, L::P_OP, r, c0, xc);
       }
     } else {
-      // rows up to the reference: 1/f = prod_{r < s <= m} alpha_s <= 1
-      float4 Q = make_float4(1.f, 1.f, 1.f, 1.f);
-      for (int g2 = grp + 1; g2 < half; ++g2) Q = mul4(Q, gp4(g2));
+      // rows up to the reference: 1/rho = prod_{r < s <= m_R} alpha_s <= 1
+      float4 Q = gprod(grp + 1, 4 * R + 1);
 #pragma unroll
       for (int i = 3; i >= 0; --i) {
         const float4 f = make_float4(rcp(Q.x), rcp(Q.y), rcp(Q.z), rcp(Q.w));
         const int r = r0 + i;
-        const float4 a = mul4(kv[i], f), b = mul4(qv[i], f);
-        krs[i] = mul4(kv[i], Q);
+        const float4 a = mul4(kv[i], f), b = mul4(qv[i], f), c = mul4(kv[i], Q);
         const float xa[4] = {a.x, a.y, a.z, a.w}, xb[4] = {b.x, b.y, b.z, b.w};
-        const float xc[4] = {krs[i].x, krs[i].y, krs[i].z, krs[i].w};
+        const float xc[4] = {c.x, c.y, c.z, c.w};
         st4<BF>(sKl, L::P_OP, r, c0, xa);
         st4<BF>(sQl, L::P_OP, r, c0, xb);
         st4<BF>(sKr, L::P_OP, r, c0, xc);
         Q = mul4(Q, av[i]);
       }
     }
+    // Per-channel decay vectors, one set of threads each (chains of products,
+    // every one of them a product over consecutive tokens, so none leaves the
+    // range of what it stands for).
     if (grp == 0) {
-      // gamma_m = product of alpha up to the reference row, gamma_n / gamma_m =
-      // over the rows after it
-      float4 gm = make_float4(1.f, 1.f, 1.f, 1.f), dl = make_float4(1.f, 1.f, 1.f, 1.f);
+      // gamma_mR = gamma at row 16R + 7; gamma_n at row 63
+      float4 x = gprod(0, 1);
+      st4v(sGM, x);
 #pragma unroll
-      for (int g2 = 0; g2 < half; ++g2) gm = mul4(gm, gp4(g2));
+      for (int RR = 1; RR < 4; ++RR) {
+        x = mul4(x, gprod(4 * RR - 2, 4 * RR + 1));
+        st4v(sGM + RR * DK, x);
+      }
+      st4v(sGN, mul4(x, gprod(14, 15)));
+    } else if (grp == 1) {
+      // gamma_n / gamma_mI = product over rows 16I + 8 .. 63
+      float4 x = gprod(14, 15);
+      st4v(sGNM + 3 * DK, x);
 #pragma unroll
-      for (int g2 = half; g2 < RG; ++g2) dl = mul4(dl, gp4(g2));
-      *reinterpret_cast<float4*>(sGM + c0) = gm;
-      *reinterpret_cast<float4*>(sDL + c0) = dl;
-      *reinterpret_cast<float4*>(sGN + c0) = mul4(gm, dl);
+      for (int II = 2; II >= 0; --II) {
+        x = mul4(x, gprod(4 * II + 2, 4 * II + 5));
+        st4v(sGNM + II * DK, x);
+      }
+    } else if (grp == 2) {
+      // S1_I: rows 16I + 8 .. 16I + 15;  E_(I+1),I: rows 16I + 16 .. 16I + 23
+#pragma unroll
+      for (int II = 0; II < 3; ++II) {
+        st4v(sS1 + II * DK, gprod(4 * II + 2, 4 * II + 3));
+        st4v(sE + eidx(II + 1, II) * DK, gprod(4 * II + 4, 4 * II + 5));
+      }
+    } else if (grp == 3) {
+      // E_RI for R >= I + 2: rows 16I + 16 .. 16R + 7
+      const float4 x10 = gprod(4, 5), x21 = gprod(8, 9), x32 = gprod(12, 13);
+      const float4 m1 = gprod(6, 7), m2 = gprod(10, 11);
+      const float4 e20 = mul4(mul4(x10, m1), x21);
+      const float4 e31 = mul4(mul4(x21, m2), x32);
+      st4v(sE + eidx(2, 0) * DK, e20);
+      st4v(sE + eidx(3, 1) * DK, e31);
+      st4v(sE + eidx(3, 0) * DK, mul4(mul4(e20, m2), x32));
     }
   }
   lds_barrier();
 
-  // ---- step 2: A = beta * strict_lower(Kl Kr^T), P = lower(Ql Kr^T) -------
+  // ---- step 2: A = beta * strict_lower(G_K), P = lower(G_Q) --------------
   {
-    // The 20 lower 16x16 tiles (10 of A, 10 of P), spread so that the two
-    // waves sharing a SIMD (w and w + 4) together do 5 tiles per K chunk.
+    // The 20 lower 16x16 tiles (10 of A, 10 of P) in eight groups: per row
+    // block pair (R, I < R) the A and P tiles share the rescaled column
+    // operand; a diagonal tile joins four of the groups.  Waves w and w + 4
+    // share a SIMD and together take 5 tiles.
     f4 acc[2][3];
 #pragma unroll
     for (int g = 0; g < 2; ++g)
@@ -612,36 +703,38 @@ __device__ __forceinline__ void prep_chunk(char* smem, const float4 (&av)[4], co
     for (int g = 0; g < 2; ++g)
 #pragma unroll
       for (int j = 0; j < 3; ++j) tT[g][j] = -1, tR[g][j] = 0, tI[g][j] = 0;
-#define KDA_TILES(g, a0, b0, c0_, a1, b1, c1_, a2, b2, c2_)                                      \
-gram_tiles<BF, DK, a0, b0, c0_, a1, b1, c1_, a2, b2, c2_>(sKl, sQl, sKr, acc[g]);              \
-tT[g][0] = a0; tR[g][0] = b0; tI[g][0] = c0_;                                                  \
-tT[g][1] = a1; tR[g][1] = b1; tI[g][1] = c1_;                                                  \
-tT[g][2] = a2; tR[g][2] = b2; tI[g][2] = c2_;
+#define KDA_GROUP(g, R_, I_, XD_)                                                      \
+  gram_group<BF, DK, R_, I_, XD_>(sKl, sQl, sKr, sS1, sE, acc[g]);                     \
+  tT[g][0] = 0; tR[g][0] = R_; tI[g][0] = I_;                                          \
+  tT[g][1] = 1; tR[g][1] = R_; tI[g][1] = I_;                                          \
+  tT[g][2] = XD_; tR[g][2] = R_; tI[g][2] = R_;
     if constexpr (NW >= 8) {
       switch (w) {
-        case 0: KDA_TILES(0, 0, 3, 0, 0, 3, 1, 0, 3, 2) break;
-        case 1: KDA_TILES(0, 1, 3, 0, 1, 3, 1, 1, 3, 2) break;
-        case 2: KDA_TILES(0, 0, 2, 0, 0, 2, 1, 0, 1, 1) break;
-        case 3: KDA_TILES(0, 1, 1, 1, 1, 1, 0, 0, 1, 0) break;
-        case 4: KDA_TILES(0, 0, 3, 3, 0, 2, 2, -1, 0, 0) break;
-        case 5: KDA_TILES(0, 1, 3, 3, 1, 2, 2, -1, 0, 0) break;
-        case 6: KDA_TILES(0, 1, 2, 0, 1, 2, 1, -1, 0, 0) break;
-        default: KDA_TILES(0, 0, 0, 0, 1, 0, 0, -1, 0, 0) break;
+        case 0: KDA_GROUP(0, 3, 0, 0) break;
+        case 1: KDA_GROUP(0, 3, 1, 1) break;
+        case 2: KDA_GROUP(0, 2, 0, 0) break;
+        case 3: KDA_GROUP(0, 2, 1, 1) break;
+        case 4: KDA_GROUP(0, 0, 0, -1) break;
+        case 5: KDA_GROUP(0, 1, 1, -1) break;
+        case 6: KDA_GROUP(0, 3, 2, -1) break;
+        default: KDA_GROUP(0, 1, 0, -1) break;
       }
     } else {
       switch (w) {
-        case 0: KDA_TILES(0, 0, 3, 0, 0, 3, 1, 0, 3, 2) KDA_TILES(1, 1, 3, 0, 1, 3, 1, -1, 0, 0) break;
-        case 1: KDA_TILES(0, 1, 3, 2, 0, 3, 3, 1, 3, 3) KDA_TILES(1, 0, 2, 2, 1, 2, 2, -1, 0, 0) break;
-        case 2: KDA_TILES(0, 0, 2, 0, 0, 2, 1, 1, 2, 0) KDA_TILES(1, 1, 2, 1, 0, 1, 1, -1, 0, 0) break;
-        default: KDA_TILES(0, 1, 1, 1, 0, 1, 0, 1, 1, 0) KDA_TILES(1, 0, 0, 0, 1, 0, 0, -1, 0, 0) break;
+        case 0: KDA_GROUP(0, 3, 0, 0) KDA_GROUP(1, 0, 0, -1) break;
+        case 1: KDA_GROUP(0, 3, 1, 1) KDA_GROUP(1, 1, 1, -1) break;
+        case 2: KDA_GROUP(0, 2, 0, 0) KDA_GROUP(1, 3, 2, -1) break;
+        default: KDA_GROUP(0, 2, 1, 1) KDA_GROUP(1, 1, 0, -1) break;
       }
     }
-#undef KDA_TILES
-    // Kg = Diag(gamma_n / gamma_m) Kr^T, rows = key channels (from the Kr rows)
-    xpose_lds<BF, DK, NW>(sKr, L::P_OP, sDL, sKrT, L::P_T);
+#undef KDA_GROUP
+    // K_e^T = Diag(gamma_n / gamma_mI) Kr_I^T, rows = key channels (from the Kr rows)
+    xpose_lds<BF, DK, NW, true>(sKr, L::P_OP, sGNM, sKrT, L::P_T);
     lds_barrier();  // every read of Kr is done: A and P overwrite it
     // Tile (R, I) transposed: lane (lr, lg) holds row 16R + lr, columns
-    // 16I + 4lg .. +3.
+    // 16I + 4lg .. +3.  On diagonal tiles the entries above the diagonal may
+    // be infinite (factors up to alpha^-15): they are selected away, never
+    // multiplied.
 #pragma unroll
     for (int g = 0; g < 2; ++g)
 #pragma unroll
@@ -724,6 +817,33 @@ tT[g][2] = a2; tR[g][2] = b2; tI[g][2] = c2_;
       const int I = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
       sLi[(16 * R + rr) * L::P_AF + 16 * I + cc] = 0.f;
     }
+    if constexpr (CONVERT) {
+      // Kl -> K_g = Kl Diag(gamma_mR), Ql -> Q_g in place (rows of block R),
+      // one group of 8 channels at a time, while waves 0-3 invert.
+      constexpr int G8 = DK / 8;
+      for (int e = t - 64 * w0; e < 2 * kC * G8; e += NT - 64 * w0) {
+        char* const base = e < kC * G8 ? sKl : sQl;
+        const int e2 = e < kC * G8 ? e : e - kC * G8;
+        const int r = e2 / G8, g8 = e2 - r * G8;
+        const float* gm = sGM + (r >> 4) * DK + 8 * g8;
+        float x[8];
+        if constexpr (BF) {
+          const char* src = base + r * L::P_OP + g8 * 32;
+          const uint4 hi = *reinterpret_cast<const uint4*>(src);
+          const uint4 lo = *reinterpret_cast<const uint4*>(src + 16);
+          const uint32_t hw[4] = {hi.x, hi.y, hi.z, hi.w}, lw[4] = {lo.x, lo.y, lo.z, lo.w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            x[2 * j] = (bf_lo16(hw[j]) + bf_lo16(lw[j])) * gm[2 * j];
+            x[2 * j + 1] = (bf_hi16(hw[j]) + bf_hi16(lw[j])) * gm[2 * j + 1];
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) x[j] = reinterpret_cast<const float*>(base + r * L::P_OP)[8 * g8 + j] * gm[j];
+        }
+        st8<BF>(base, L::P_OP, r, 8 * g8, x);
+      }
+    }
   }
   lds_barrier();
   // 3b: off-diagonal blocks row block by row block:
@@ -793,7 +913,6 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_prefill_kernel(Params p
   char* const sXT = smem + L::OFF_XT;
   char* const sUT = smem + L::OFF_UT;
   char* const sT = smem + L::OFF_T;
-  float* const sGM = reinterpret_cast<float*>(smem + L::OFF_GM);
   float* const sGN = reinterpret_cast<float*>(smem + L::OFF_GN);
 
   const int t = threadIdx.x;
@@ -923,11 +1042,11 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_prefill_kernel(Params p
         vreg[js][q] = (16 * (w & 3) + 4 * lg + q) < nv ? cvt1<BF>(pv[js][q]) : 0.f;
     if (tok0 + kC < s1) load_chunk(tok0 + kC, int(s1 - tok0 - kC < kC ? s1 - tok0 - kC : kC));
 
-    prep_chunk<DK, BF>(smem, av, kv, qv, bev, [] {});
+    prep_chunk<DK, BF, true>(smem, av, kv, qv, bev, [] {});
 
     // ---- step 4: the state pass, 16 value columns at a time ----------------
     // Waves 0..3 compute X and U for rows 16w..; the output rows 16*ow.. are
-    // computed by waves 4..7 when there are eight waves (their Ql S_B product
+    // computed by waves 4..7 when there are eight waves (their Q_g S product
     // overlaps X and U), else by waves 0..3 after U.
     constexpr bool kSplitO = NW >= 8;
     const bool xw = w < 4;
@@ -935,16 +1054,14 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_prefill_kernel(Params p
     const int ow = w & 3;
 #pragma unroll
     for (int js = 0; js < NSUB; ++js) {
-      // 4a: S_B^T = (Diag(gamma_m) S)^T for these columns.
+      // 4a: S^T for these columns.
       {
         const int kr = 16 * w + 4 * lg;
-        float x[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) x[q] = S[js][q] * sGM[kr + q];
+        const float x[4] = {S[js][0], S[js][1], S[js][2], S[js][3]};
         st4<BF>(sSBT, L::P_OP, lr, kr, x);
       }
       lds_barrier();
-      // 4b: X = V - Kl S_B; the output waves start O = Ql S_B.
+      // 4b: X = V - K_g S; the output waves start O = Q_g S.
       f4 acco = f4{0.f, 0.f, 0.f, 0.f};
       if (xw) {
         f4 acc = gemm<BF, DK>(f4{0.f, 0.f, 0.f, 0.f}, sKl, L::P_OP, 16 * w, sSBT, L::P_OP, 0);
@@ -963,7 +1080,7 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_prefill_kernel(Params p
         st4<BF>(sUT, L::P_T, lr, 16 * w + 4 * lg, x);
       }
       lds_barrier();
-      // 4d: O = Ql S_B + P U
+      // 4d: O = Q_g S + P U
       if (owave) {
         if constexpr (!kSplitO)
           acco = gemm<BF, DK>(acco, sQl, L::P_OP, 16 * ow, sSBT, L::P_OP, 0);
@@ -983,7 +1100,7 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_prefill_kernel(Params p
           *dst = acco[q];
         }
       }
-      // 4e: S' = Diag(gamma_n) S + Kg U, Kg = Diag(gamma_n / gamma_m) Kr^T  (rows 16w..)
+      // 4e: S' = Diag(gamma_n) S + K_e^T U  (rows 16w..)
       {
         f4 acc = gemm<BF, kC>(f4{0.f, 0.f, 0.f, 0.f}, sKrT, L::P_T, 16 * w, sUT, L::P_T, 0);
 #pragma unroll
@@ -992,9 +1109,9 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_prefill_kernel(Params p
           S[js][q] = sGN[c] * S[js][q] + acc[q];
         }
       }
-      // With 8 waves the next column block rewrites S_B^T, X^T and U^T only
+      // With 8 waves the next column block rewrites S^T, X^T and U^T only
       // after barriers that every wave reaches after its reads of them here
-      // (S_B^T is last read in 4b).  With 4 waves S_B^T is read in 4d, and the
+      // (S^T is last read in 4b).  With 4 waves S^T is read in 4d, and the
       // next chunk's steps 1-3 overwrite everything: barrier.
       if (js == NSUB - 1 || !kSplitO) lds_barrier();
     }
@@ -1032,11 +1149,11 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_prefill_kernel(Params p
 // kernel above repeats steps 1-3 in every value slab of a chain; here they run
 // once per chunk, for all chunks at once (kda_stage_kernel), together with the
 // state-independent parts of steps 4b-4e folded into four matrices:
-//     W  = T Kl Diag(gamma_m)     [64 x DK]    so that  U = Uv - W S
+//     W  = T K_g                  [64 x DK]    so that  U = Uv - W S
 //     Uv = T V                    [64 x DV]
-//     Qg = Ql Diag(gamma_m)       [64 x DK]    so that  O = Qg S + P U
-//     Kg = Diag(delta) Kr^T       [DK x 64]    so that  S' = Diag(gamma_n) S + Kg U
-// (delta = gamma_n / gamma_m).  The sequential pass (kda_chain_kernel) then
+//     Qg = Q_g                    [64 x DK]    so that  O = Qg S + P U
+//     Kg = K_e^T                  [DK x 64]    so that  S' = Diag(gamma_n) S + Kg U
+// The sequential pass (kda_chain_kernel) then
 // streams them from a workspace straight into MFMA registers: two dependent
 // products and two barriers per chunk.
 //
@@ -1121,16 +1238,14 @@ template <> struct FL<false> {
   }
 };
 
-__device__ __forceinline__ float bf_lo16(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf_hi16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
 // Writes an LDS operand array (ROWS x K, layout of the operand arrays above)
 // to global memory in fragment order, each element times rs[row] (RS) and
-// cs[k] (CS).  The fragments are dealt out to the waves round-robin; every
-// wave writes the same number.
-template <bool BF, int K, int ROWS, int NW, bool RS, bool CS>
+// cs[k] (CS; cs[rb * K + k] for the rows of 16-row block rb with CS_RB).  The
+// fragments are dealt out to the waves round-robin; every wave writes the
+// same number.
+template <bool BF, int K, int ROWS, int NW, bool RS, bool CS, bool CS_RB = false>
 __device__ __forceinline__ void export_frags(char* dst, const char* src, int pitch, const float* rs,
-                                             const float* cs) {
+                                             const float* cs_all) {
   using F = FL<BF>;
   constexpr int NU = K / F::KU;                 // units per row block
   constexpr int NF = (ROWS / 16) * NU;
@@ -1142,6 +1257,7 @@ __device__ __forceinline__ void export_frags(char* dst, const char* src, int pit
     const int rb = f / NU, u = f - rb * NU;
     const int row = 16 * rb + (l & 15);
     const float r = RS ? rs[row] : 1.f;
+    const float* cs = CS_RB ? cs_all + rb * K : cs_all;
     if constexpr (BF) {
       const char* s = src + row * pitch + (u * 4 + (l >> 4)) * 32;
       uint4 hi = *reinterpret_cast<const uint4*>(s);
@@ -1298,7 +1414,7 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_stage_kernel(StageParam
     // The next item's raw inputs and this item's V are requested between
     // steps 2 and 3: behind this item's computation, not behind the previous
     // item's slot stores.
-    prep_chunk<DK, BF>(smem, av, kv, qv, bev, [&] {
+    prep_chunk<DK, BF, false>(smem, av, kv, qv, bev, [&] {
       load_v(it);
       if (it + gridDim.x < items) load_item(it + gridDim.x);
     });
@@ -1307,19 +1423,21 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_stage_kernel(StageParam
     const float* sGM = reinterpret_cast<const float*>(smem + L::OFF_GM);
     const float* sGN = reinterpret_cast<const float*>(smem + L::OFF_GN);
 
-    // F1: Qg = Ql Diag(gamma_m), Kg (already scaled in step 1), P, gamma_n.
+    // F1: Qg = Q_g (Ql Diag(gamma_mR) per row block R), Kg = K_e^T (scaled in
+    // step 2), P, gamma_n.
     if constexpr (!NOO)
-      export_frags<BF, DK, kC, NW, false, true>(slot + SL::OFF_Q, smem + L::OFF_QL, L::P_OP, nullptr, sGM);
+      export_frags<BF, DK, kC, NW, false, true, true>(slot + SL::OFF_Q, smem + L::OFF_QL, L::P_OP, nullptr, sGM);
     export_frags<BF, kC, DK, NW, false, false>(slot + SL::OFF_K, smem + L::OFF_KRT, L::P_T, nullptr, nullptr);
     if constexpr (!NOO)
       export_frags<BF, kC, kC, NW, false, false>(slot + SL::OFF_P, smem + L::OFF_P, L::P_T, nullptr, nullptr);
     reinterpret_cast<float*>(slot + SL::OFF_G)[t % DK] = sGN[t % DK];
     lds_barrier();
 
-    // F2: (Kl Diag(gamma_m))^T into the Kr^T space, V^T into the A/P space.
+    // F2: K_g^T (Kl Diag(gamma_mR) per row block R) into the Kr^T space, V^T
+    // into the A/P space.
     char* const sKgT = smem + L::OFF_KRT;
     char* const sVT = smem + L::OFF_X;
-    xpose_lds<BF, DK, NW>(smem + L::OFF_KL, L::P_OP, sGM, sKgT, L::P_T);
+    xpose_lds<BF, DK, NW, true>(smem + L::OFF_KL, L::P_OP, sGM, sKgT, L::P_T);
 #pragma unroll
     for (int i = 0; i < UV; ++i) {
       const int u = w + NW * i, rb = u & 3, cu = u >> 2;
@@ -1337,7 +1455,7 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_stage_kernel(StageParam
     }
     lds_barrier();
 
-    // F3: W = T (Kl Diag(gamma_m)) into a staging array (the Ql space);
+    // F3: W = T K_g into a staging array (the Ql space);
     // Uv = T V straight to the slot.  Wave w takes row block rb of T (rb = w
     // for waves 0-3, 3 - (w - 4) for waves 4-7, so that the two waves of a
     // SIMD together cover 3 of the 4 nonzero K blocks of the lower-triangular
@@ -1617,10 +1735,7 @@ void launch_dk(const Params& p, int nsub, int64_t nblocks, hipStream_t st) {
 // Columns per workgroup: as many as possible while the launch still has a
 // workgroup for every compute unit (256 on MI355X).
 int choose_nsub(int64_t pairs, int DV) {
-  if (const char* e = getenv("KDA_PREFILL_NSUB")) {
-    const int v = atoi(e);
-    if ((v == 1 || v == 2 || v == 4 || v == 8) && 16 * v <= DV) return v;
-  }
+  if (const int v = tuning().prefill_nsub; v > 0 && 16 * v <= DV) return v;
   // The widest slab that still gives every compute unit a workgroup: a
   // wider slab repeats steps 1-3 for fewer slabs (d=128, bf16: NSUB 8 over 4
   // is 11-13% faster from 256 chains up, although its registers spill).
@@ -1634,10 +1749,7 @@ int choose_nsub(int64_t pairs, int DV) {
 // slab.  Fixed-length batches only.
 bool use_staged(bool varlen, int64_t pairs, int64_t nchunks) {
   if (varlen || nchunks < 2) return false;
-  if (const char* e = getenv("KDA_PREFILL_PATH")) {
-    if (!strcmp(e, "fused")) return false;
-    if (!strcmp(e, "split")) return true;
-  }
+  if (const int f = tuning().prefill_form; f != 0) return f == 2;
   return pairs < 128;
 }
 
@@ -1649,14 +1761,15 @@ size_t slot_bytes(int DK, int DV) { return size_t(4) * (3 * 64 * DK + 64 * 64 + 
 // MI355X, budget 160 MiB of it) the chain kernel is served from there rather
 // than from HBM (B=1, H=32, T=8192, d=128: 527 -> 442 us).  The chunks are
 // split into equal segments, so that no stage launch ends on a short segment.
-// KDA_PREFILL_SEG=n forces n chunks per segment (at most 1 GiB of slots).
-int64_t seg_chunks(int64_t pairs, int64_t nchunks, int DK, int DV) {
+// The tuning override prefill_seg forces that many chunks per segment (at
+// most 1 GiB of slots, and at most `budget` bytes when one is given).
+constexpr int64_t kSegBudget = int64_t(160) << 20;
+int64_t seg_chunks(int64_t pairs, int64_t nchunks, int DK, int DV, int64_t budget = 0) {
   const int64_t per_chunk = pairs * int64_t(slot_bytes(DK, DV));
-  if (const char* e = getenv("KDA_PREFILL_SEG")) {
-    const long v = atol(e);
-    if (v > 0 && v <= (int64_t(1) << 30) / per_chunk) return v < nchunks ? v : nchunks;
-  }
-  int64_t cap = (int64_t(160) << 20) / per_chunk;
+  const int64_t limit = budget > 0 ? budget : (int64_t(1) << 30);
+  if (const int64_t v = tuning().prefill_seg; v > 0 && v <= limit / per_chunk)
+    return v < nchunks ? v : nchunks;
+  int64_t cap = (budget > 0 && budget < kSegBudget ? budget : kSegBudget) / per_chunk;
   if (cap < 1) cap = 1;
   if (cap >= nchunks) return nchunks;
   const int64_t nseg = (nchunks + cap - 1) / cap;
@@ -1748,10 +1861,7 @@ void launch_staged(const Params& base, int64_t T, int nsub, hipStream_t st, char
 
 // Value columns per chain workgroup of the staged form (1 or 2 blocks of 16).
 int staged_nsub(int64_t pairs, int DV) {
-  if (const char* e = getenv("KDA_PREFILL_NSUB")) {
-    const int v = atoi(e);
-    if ((v == 1 || v == 2 || v == 4) && 16 * v <= DV) return v;
-  }
+  if (const int v = tuning().prefill_nsub; (v == 1 || v == 2 || v == 4) && 16 * v <= DV) return v;
   (void)pairs;
   (void)DV;
   return 1;
@@ -1759,13 +1869,14 @@ int staged_nsub(int64_t pairs, int DV) {
 
 }  // namespace
 
-size_t prefill_workspace_bytes(int N, int64_t T_total, int H, int DK, int DV, bool varlen) {
+size_t prefill_workspace_bytes(int N, int64_t T_total, int H, int DK, int DV, bool varlen,
+                               int64_t seg_budget) {
   const int64_t pairs = int64_t(N) * H;
   if (pairs == 0 || varlen) return 0;
   const int64_t T = T_total / N;
   const int64_t nchunks = (T + kC - 1) / kC;
   if (!use_staged(varlen, pairs, nchunks)) return 0;
-  const int64_t seg = seg_chunks(pairs, nchunks, DK, DV);
+  const int64_t seg = seg_chunks(pairs, nchunks, DK, DV, seg_budget);
   size_t bytes = size_t(pairs) * size_t(seg) * slot_bytes(DK, DV);
   if (seg < nchunks) bytes += size_t(pairs) * DK * DV * 4;  // state carried between segments
   return bytes;
@@ -1804,7 +1915,7 @@ int launch_prefill(const PrefillArgs& a, void* stream, const char** msg) {
   (void)hipGetLastError();
   if (use_staged(varlen, pairs, nchunks)) {
     const int nsub = staged_nsub(pairs, a.DV);
-    const int64_t seg = seg_chunks(pairs, nchunks, a.DK, a.DV);
+    const int64_t seg = seg_chunks(pairs, nchunks, a.DK, a.DV, a.seg_budget);
     char* ws = static_cast<char*>(a.workspace);
     float* state_ws = seg < nchunks
         ? reinterpret_cast<float*>(ws + size_t(pairs) * size_t(seg) * slot_bytes(a.DK, a.DV))

@@ -45,6 +45,7 @@ EXPORTED = (
     "kda_chunk_backward_varlen_scalar_gate",
     "kda_status_string",
     "kda_last_error_message",
+    "kda_internal_set_tuning",
 )
 
 
@@ -104,6 +105,8 @@ def load_library(path: str = _LIB_PATH) -> ctypes.CDLL:
     lib.kda_status_string.argtypes = [i]
     lib.kda_last_error_message.restype = ctypes.c_char_p
     lib.kda_last_error_message.argtypes = []
+    lib.kda_internal_set_tuning.restype = i
+    lib.kda_internal_set_tuning.argtypes = [i, i, i, i]
     return lib
 
 
@@ -115,6 +118,25 @@ def lib() -> ctypes.CDLL:
     if _lib is None:
         _lib = load_library()
     return _lib
+
+
+_TUNING = {"prefill_form": 0, "prefill_nsub": 0, "prefill_seg": 0, "bwd_window": 0}
+_FORMS = {"auto": 0, "fused": 1, "split": 2, "staged": 2}
+
+
+def set_tuning(**kw):
+    """Internal (tests and measurements): kda_internal_set_tuning for the
+    given knobs, the others kept.  prefill_form takes "auto", "fused" or
+    "split"/"staged"; the numbers take 0 for the choice by shape.  Called
+    with no argument, restores every choice by shape."""
+    state = dict(_TUNING) if kw else {k: 0 for k in _TUNING}
+    for k, v in kw.items():
+        if k not in _TUNING:
+            raise TypeError(f"unknown tuning knob {k}")
+        state[k] = _FORMS[v] if k == "prefill_form" and isinstance(v, str) else int(v)
+    _check(lib().kda_internal_set_tuning(state["prefill_form"], state["prefill_nsub"],
+                                         state["prefill_seg"], state["bwd_window"]))
+    _TUNING.update(state)
 
 
 def _check(status):
@@ -387,13 +409,19 @@ def chunk_backward(q, k, v, alpha, beta, d_o, initial_state=None, d_final_state=
 
 def chunk_prefill_varlen_snapshots(q, k, v, alpha, beta, cu_seqlens, every, initial_state=None,
                                    output_final_state=True, chunk=64, snap_offsets=None,
-                                   out=None, final_state=None, snapshots=None, workspace=None):
+                                   out=None, final_state=None, snapshots=None, workspace=None,
+                                   num_snapshots=None):
     """Packed variable-length prefill that also returns each sequence's state
     after every ``every``-th chunk of 64 tokens.
 
     Arguments as for :func:`chunk_prefill_varlen`.  ``snap_offsets`` (int32
     device [N+1]) places sequence n's snapshots at rows snap_offsets[n] ..; by
-    default it is built from the sequence lengths (a host copy of cu_seqlens).
+    default it is built on the device from the sequence lengths
+    (floor(len_n / (64 every)) rows each, in order).  The host never reads
+    device data: ``snapshots`` (or ``num_snapshots``) gives the number of rows;
+    by default T_total // (64 every) rows, a bound of what the sequences
+    produce that the host knows without reading cu_seqlens (rows from
+    snap_offsets[N] on are then not written).
     Returns (o, final_state, snapshots [rows, H, DK, DV], snap_offsets).
     """
     Tt, H, DK = q.shape
@@ -412,15 +440,18 @@ def chunk_prefill_varlen_snapshots(q, k, v, alpha, beta, cu_seqlens, every, init
         _need(initial_state, "initial_state", torch.float32, (N, H, DK, DV))
     dev = q.device
     if snap_offsets is None:
-        lens = (cu_seqlens[1:] - cu_seqlens[:-1]).to("cpu", torch.int64)
-        per = lens // (chunk * every)
-        offs = torch.zeros(N + 1, dtype=torch.int64)
-        offs[1:] = torch.cumsum(per, 0)
-        snap_offsets = offs.to(torch.int32).to(dev)
-        rows = int(offs[-1])
+        # device ops only (asynchronous, no host copy)
+        per = torch.div(cu_seqlens[1:] - cu_seqlens[:-1], chunk * every, rounding_mode="floor")
+        snap_offsets = torch.zeros(N + 1, dtype=torch.int32, device=dev)
+        snap_offsets[1:] = torch.cumsum(per, 0)
     else:
         _need(snap_offsets, "snap_offsets", torch.int32, (N + 1,))
-        rows = int(snap_offsets[-1].item()) if snapshots is None else snapshots.shape[0]
+    if snapshots is not None:
+        rows = snapshots.shape[0]
+    elif num_snapshots is not None:
+        rows = int(num_snapshots)
+    else:
+        rows = Tt // (chunk * every)
     o = out if out is not None else torch.empty((Tt, H, DV), device=dev, dtype=torch.float32)
     _need(o, "out", torch.float32, (Tt, H, DV))
     st = None
@@ -451,8 +482,9 @@ def chunk_backward_varlen(q, k, v, alpha, beta, cu_seqlens, d_o, initial_state=N
 
     Inputs as for :func:`chunk_prefill_varlen` (alpha [T_total,H,DK], or
     [T_total,H] for a scalar gate); d_o [T_total,H,DV] float32;
-    d_final_state [N,H,DK,DV] float32 or None; max_seqlen: the longest
-    sequence (by default read from a host copy of cu_seqlens).
+    d_final_state [N,H,DK,DV] float32 or None; max_seqlen (required): the
+    longest sequence's length as a host int, as varlen attention interfaces
+    take it (the host never reads cu_seqlens), or 0 if unknown.
     Returns (dq, dk, dv, dalpha, dbeta, d_initial_state), all float32.
     """
     Tt, H, DK = q.shape
@@ -479,8 +511,9 @@ def chunk_backward_varlen(q, k, v, alpha, beta, cu_seqlens, d_o, initial_state=N
     db = torch.empty((Tt, H), **f32)
     ds0 = torch.empty((N, H, DK, DV), **f32)
     if max_seqlen is None:
-        lens = cu_seqlens[1:] - cu_seqlens[:-1]
-        max_seqlen = int(lens.max().item()) if N > 0 else 0
+        raise ValueError("max_seqlen is required: the longest sequence's length as a host int "
+                         "(0 if unknown: still correct, the library then assumes T_total and "
+                         "runs more reverse-pass windows)")
     wsz = lib().kda_chunk_backward_varlen_workspace_size(N, Tt, max_seqlen, H, DK, DV, chunk)
     if wsz and workspace is None:
         workspace = torch.empty(wsz, device=dev, dtype=torch.uint8)

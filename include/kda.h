@@ -27,9 +27,10 @@
  *   - Supported sizes: DK, DV in {64, 128}; chunk == 64; prefill and backward
  *     at most 65536 heads.
  *   - Data domain (not checked: violating it gives unspecified output):
- *     alpha in [0.07, 1] and finite inputs.  The chunked prefill scales rows by
- *     decay ratios taken about each chunk's midpoint; the product of alpha over
- *     any 32 consecutive tokens of one channel must stay above ~1e-37.
+ *     alpha in [1e-4, 1] and finite inputs.  The chunked forms split the decay
+ *     between two tokens of a chunk through a reference row in each block of
+ *     16 tokens, so every factor they build is a product of at most 8 alphas
+ *     or its reciprocal (at most 1e32 at alpha = 1e-4, within fp32).
  *   - Errors: argument errors are detected on the host before anything is
  *     enqueued; the call then returns a non-zero status, enqueues nothing and
  *     leaves every output untouched.  KDA_ERR_HIP means a launch failed.
@@ -85,9 +86,6 @@ int kda_abi_version(void);
  * Computes exactly the token recurrence (up to rounding) by the chunk form:
  * per chunk a unit-lower-triangular solve and dense products, and a
  * sequential pass of the state over the chunks.
- * The environment variable KDA_PREFILL_PATH=fused|split forces the one-kernel
- * or the staged two-kernel form (both give the same result up to rounding);
- * it must not change between the size query and the call.
  */
 size_t kda_chunk_prefill_workspace_size(int B, int T, int H, int DK, int DV, int chunk);
 kda_status_t kda_chunk_prefill(int B, int T, int H, int DK, int DV, int chunk,
@@ -261,9 +259,8 @@ kda_status_t kda_decode_pool(int N, int L, int H, int DK, int DV, kda_dtype_t in
  *   d_state_in   [B,H,DK,DV] float or NULL: gradient of the initial state
  *   workspace    at least kda_chunk_backward_workspace_size() bytes, 16-byte
  *                aligned, not overlapping any argument (holds the forward's
- *                chunk-boundary states and outputs, DV + DK DV / 64 floats per
- *                token-head; per chunk-head of a window of chunks
- *                DK^2 + 2 DK DV + 64 DV + 65 DK + 4096 floats (279 KB at
+ *                chunk-boundary states, DK DV / 64 floats per token-head; per chunk-head of a window of chunks
+ *                DK^2 + 2 DK DV + 64 DV + 93 DK + 8192 floats (310 KB at
  *                d = 128), the windows sized to keep this at most 4 GiB; one
  *                state per (sequence, head) when there are several windows).
  * Outputs must not overlap inputs or each other.  The forward is recomputed
@@ -290,10 +287,13 @@ kda_status_t kda_chunk_backward(int B, int T, int H, int DK, int DV, int chunk,
  * states [N,H,DK,DV]).
  *   cu_seqlens   int32 DEVICE [N+1], 4-byte aligned, non-decreasing, from 0 to
  *                T_total (not checked on the device)
- *   max_seqlen   host int: at least the longest sequence's length (not checked:
- *                a smaller value leaves the first chunks of longer sequences
- *                without gradients), or 0 if unknown (then T_total is assumed;
- *                correct, but the reverse pass may run more, empty, windows)
+ *   max_seqlen   host int: at least the longest sequence's length, or 0 if
+ *                unknown (then T_total is assumed; correct, but the reverse
+ *                pass may run more, empty, windows).  Not checked: with a
+ *                smaller value the reverse pass covers only the last chunks
+ *                of a longer sequence (at least ceil(max_seqlen / 64); their
+ *                gradients are right); the gradients of its earlier tokens and
+ *                its d_state_in are not written.
  *   workspace    at least kda_chunk_backward_varlen_workspace_size() bytes for
  *                the same N, T_total, max_seqlen (the host never reads the
  *                lengths)
@@ -340,6 +340,24 @@ kda_status_t kda_chunk_backward_varlen_scalar_gate(
 
 const char* kda_status_string(kda_status_t s);
 const char* kda_last_error_message(void);
+
+/*
+ * Internal: tuning overrides for tests and measurements.  Callers never need
+ * them (every entry point chooses its launch shapes from the sizes); they
+ * exist so that both prefill forms, every slab width, segment length and
+ * backward window can be exercised on small inputs.  Process-wide, taking
+ * effect at the next call; a workspace size queried before a change does not
+ * hold for calls after it.  0 restores the choice by shape:
+ *   prefill_form  0, 1 = one-kernel form, 2 = staged form (fixed-length
+ *                 batches of more than one chunk; packed batches always take
+ *                 the one-kernel form)
+ *   prefill_nsub  0, or 1, 2, 4, 8 blocks of 16 value columns per workgroup
+ *   prefill_seg   0, or chunks per segment of the staged form
+ *   bwd_window    0, or chunks per window of the backward's reverse pass
+ * Returns KDA_ERR_SHAPE, changing nothing, for values outside these.
+ */
+kda_status_t kda_internal_set_tuning(int prefill_form, int prefill_nsub, int prefill_seg,
+                                     int bwd_window);
 
 #ifdef __cplusplus
 }

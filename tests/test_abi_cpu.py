@@ -122,20 +122,27 @@ def test_workspace_size_queries(lib, monkeypatch):
     assert lib.kda_chunk_prefill_workspace_size(1, 1 << 20, 32, 128, 128, 64) == ws(32, 1 << 14)
     assert lib.kda_chunk_prefill_workspace_size(1, 4096, 8, 128, 128, 64) == ws(8, 64)
     assert ws(8, 64) == 8 * 64 * slot(128)         # fits: one segment, no carried state
-    monkeypatch.setenv("KDA_PREFILL_SEG", "5")
+    assert lib.kda_internal_set_tuning(0, 0, 5, 0) == OK    # 5 chunks per segment
     assert lib.kda_chunk_prefill_workspace_size(1, 8192, 32, 128, 128, 64) == \
         32 * 5 * slot(128) + 32 * 128 * 128 * 4
-    monkeypatch.delenv("KDA_PREFILL_SEG")
+    assert lib.kda_internal_set_tuning(0, 0, 0, 0) == OK
     # one chunk, many chains, varlen, unsupported sizes: no workspace
     assert lib.kda_chunk_prefill_workspace_size(1, 64, 32, 128, 128, 64) == 0
     assert lib.kda_chunk_prefill_workspace_size(4, 8192, 32, 128, 128, 64) == 0
     assert lib.kda_chunk_prefill_varlen_workspace_size(64, 540000, 32, 128, 128, 64) == 0
     assert lib.kda_chunk_prefill_workspace_size(1, 64, 2, 96, 64, 64) == 0
-    monkeypatch.setenv("KDA_PREFILL_PATH", "fused")
+    assert lib.kda_internal_set_tuning(1, 0, 0, 0) == OK    # one-kernel form
     assert lib.kda_chunk_prefill_workspace_size(1, 8192, 32, 128, 128, 64) == 0
-    monkeypatch.setenv("KDA_PREFILL_PATH", "split")
+    assert lib.kda_internal_set_tuning(2, 0, 0, 0) == OK    # staged form
     assert lib.kda_chunk_prefill_workspace_size(4, 8192, 32, 128, 128, 64) == ws(128, 128)
-    monkeypatch.delenv("KDA_PREFILL_PATH")
+    assert lib.kda_internal_set_tuning(0, 0, 0, 0) == OK
+    # out-of-range overrides are refused and change nothing
+    assert lib.kda_internal_set_tuning(3, 0, 0, 0) == SHAPE
+    assert lib.kda_internal_set_tuning(0, 3, 0, 0) == SHAPE
+    assert lib.kda_internal_set_tuning(0, 0, -1, 0) == SHAPE
+    assert lib.kda_internal_set_tuning(0, 0, 0, -2) == SHAPE
+    assert lib.kda_chunk_prefill_workspace_size(1, 8192, 32, 128, 128, 64) == \
+        32 * 32 * slot(128) + 32 * 128 * 128 * 4
     # a call that needs a workspace is refused without one, or with one too small
     # (B=1, T=130, H=2, d=64: 3 chunks x 2 chains)
     need = 2 * 3 * slot(64, 64)
@@ -260,12 +267,12 @@ def test_scalar_gate_argument_errors(lib):
 def test_backward_argument_errors(lib):
     # B=1, T=64, H=2, d=64 (f32): rows = 128
     need = lib.kda_chunk_backward_workspace_size(1, 64, 2, 64, 64, 64)
-    # the window buffers of one chunk for the 2 heads (A_c, b_c, dS', M, Vn and
-    # the 65 rows of decays: 64^2 + 2 * 64^2 + 64^2 + 64 * 64 + 65 * 64 floats
-    # each), o of the forward, one snapshot per sequence-head
+    # the window buffers of one chunk for the 2 heads (A_c, b_c, dS', M, P/X,
+    # Vn and the 93 rows of decays: 64^2 + 2 * 64^2 + 64^2 + 64^2 + 64 * 64 +
+    # 93 * 64 floats each), one snapshot per sequence-head
     al = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    win = 2 * (5 * 64 * 64 + 65 * 64) * 4
-    assert need == al(win) + al(128 * 64 * 4) + al(2 * 64 * 64 * 4)
+    win = 2 * (6 * 64 * 64 + 93 * 64) * 4
+    assert need == al(win) + al(2 * 64 * 64 * 4)
     assert lib.kda_chunk_backward_workspace_size(1, 64, 2, 96, 64, 64) == 0
     big = ctypes.c_void_p(0x40000000)
     Q = [ctypes.c_void_p(0x100000 * (i + 1)) for i in range(14)]
@@ -297,23 +304,27 @@ def test_backward_argument_errors(lib):
 def test_backward_varlen_argument_errors(lib, monkeypatch):
     # N=3 sequences, T_total=200 tokens, longest 100, H=2, d=64 (f32): the
     # reverse pass's buffers cover a window of chunks counted from each
-    # sequence's end, N * H * (DK^2 + 2 DK DV + 64^2 + 64 DV + 65 DK) floats
-    # per chunk of the window (at most 4 GiB, here every chunk:
-    # ceil(100 / 64) = 2); the forward's o; snapshot rows T_total // 64 = 3
-    # (chunk j of the sequence starting at token s is row s // 64 + j)
-    per_chunk = 3 * 2 * (5 * 64 * 64 + 65 * 64) * 4
+    # sequence's end, N * H * (DK^2 + 2 DK DV + 2 * 64^2 + 64 DV + 93 DK)
+    # floats per chunk of the window (at most 4 GiB, here every chunk:
+    # ceil(100 / 64) = 2); snapshot rows T_total // 64 = 3 (chunk j of the
+    # sequence starting at token s is row s // 64 + j)
+    per_chunk = 3 * 2 * (6 * 64 * 64 + 93 * 64) * 4
     al = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    rest = al(400 * 64 * 4) + al(3 * 2 * 64 * 64 * 4)
+    rest = al(3 * 2 * 64 * 64 * 4)
     need = lib.kda_chunk_backward_varlen_workspace_size(3, 200, 100, 2, 64, 64, 64)
     assert need == al(2 * per_chunk) + rest
     # max_seqlen unknown (0): T_total is assumed, 4 chunks
     assert lib.kda_chunk_backward_varlen_workspace_size(3, 200, 0, 2, 64, 64, 64) == \
         al(4 * per_chunk) + rest
     # one chunk per window: two windows, and the adjoint carried between them
-    monkeypatch.setenv("KDA_BWD_WINDOW", "1")
+    assert lib.kda_internal_set_tuning(0, 0, 0, 1) == OK
     assert lib.kda_chunk_backward_varlen_workspace_size(3, 200, 100, 2, 64, 64, 64) == \
         al(per_chunk) + rest + al(3 * 2 * 64 * 64 * 4)
-    monkeypatch.delenv("KDA_BWD_WINDOW")
+    assert lib.kda_internal_set_tuning(0, 0, 0, 0) == OK
+    # max_seqlen below the longest sequence (not checked): one window of
+    # ceil(64 / 64) = 1 chunk and no carried adjoint (nothing to carry into)
+    assert lib.kda_chunk_backward_varlen_workspace_size(3, 200, 64, 2, 64, 64, 64) == \
+        al(per_chunk) + rest
     assert lib.kda_chunk_backward_varlen_workspace_size(3, 200, 100, 2, 96, 64, 64) == 0
     assert lib.kda_chunk_backward_varlen_workspace_size(3, 0, 0, 2, 64, 64, 64) == 0
     big = ctypes.c_void_p(0x40000000)
@@ -407,3 +418,4 @@ def test_binding_fails_loudly_without_library(tmp_path):
 
     with pytest.raises(ImportError):
         load_library(str(tmp_path / "missing.so"))
+

@@ -44,7 +44,7 @@ def run_case(B, T, H, dk, dv, dt, c, with_state, heads=None):
 @pytest.mark.parametrize("T", [1, 37, 64, 65, 200])
 @pytest.mark.parametrize("dt,d", [("bf16", 128), ("f32", 64)])
 def test_backward_matches_oracle(dt, d, T, path, monkeypatch):
-    monkeypatch.setenv("KDA_PREFILL_PATH", path)
+    kda.set_tuning(prefill_form=path)
     flush(f"[backward] B=2 T={T} H=3 d={d} {dt} path={path}")
     errs = run_case(2, T, 3, d, d, dt, 700 + T, with_state=True)
     assert max(errs.values()) <= TOL[dt], errs
@@ -106,7 +106,8 @@ def test_backward_varlen_matches_oracle(dt, d):
     dST = random_state(rng, (len(lengths), H, d, d))
     td = tdtype(dt)
     got = kda.chunk_backward_varlen(dev(q, td), dev(k, td), dev(v, td), dev(a), dev(b),
-                                    torch.from_numpy(cu).cuda(), dev(do), dev(S0), dev(dST))
+                                    torch.from_numpy(cu).cuda(), dev(do), dev(S0), dev(dST),
+                                    max_seqlen=max(lengths))
     torch.cuda.synchronize()
     got = [host(g) for g in got]
     ref = varlen_backward_reference(q, k, v, a, b, cu, do, S0, dST)
@@ -120,7 +121,7 @@ def test_backward_varlen_matches_oracle(dt, d):
 def test_backward_varlen_equals_fixed_length_call(monkeypatch):
     """Equal-length packed sequences give the fixed-length backward (both
     forwards in the one-kernel form, so the checkpoints agree)."""
-    monkeypatch.setenv("KDA_PREFILL_PATH", "fused")
+    kda.set_tuning(prefill_form="fused")
     B, T, H, D = 3, 150, 2, 128
     flush(f"[backward] varlen == fixed B={B} T={T} H={H} d={D}")
     q, k, v, a, b = I.batch_inputs(740, B, T, H, D, D, "bf16")
@@ -131,7 +132,7 @@ def test_backward_varlen_equals_fixed_length_call(monkeypatch):
     g_fix = kda.chunk_backward(*x[:5], x[5], dev(S0), None)
     flat = [t.reshape(B * T, *t.shape[2:]).contiguous() for t in x]
     cu = torch.tensor([0, T, 2 * T, 3 * T], dtype=torch.int32, device="cuda")
-    g_var = kda.chunk_backward_varlen(*flat[:5], cu, flat[5], dev(S0), None)
+    g_var = kda.chunk_backward_varlen(*flat[:5], cu, flat[5], dev(S0), None, max_seqlen=T)
     torch.cuda.synchronize()
     for gf, gv in zip(g_fix[:5], g_var[:5]):
         err = max_rel_err(host(gv), host(gf).reshape(host(gv).shape))
@@ -149,7 +150,7 @@ def test_backward_without_tokens_passes_state_gradient(varlen):
     if varlen:
         cu = torch.zeros(N + 1, dtype=torch.int32, device="cuda")
         g = kda.chunk_backward_varlen(e, e, e, e, torch.empty((0, H), device="cuda"), cu, e,
-                                      None, dev(dST))
+                                      None, dev(dST), max_seqlen=0)
     else:
         e4 = torch.empty((N, 0, H, D), device="cuda", dtype=torch.float32)
         g = kda.chunk_backward(e4, e4, e4, e4, torch.empty((N, 0, H), device="cuda"), e4, None,
@@ -173,10 +174,10 @@ def test_backward_windows_are_exact(window, monkeypatch):
     bf = torch.bfloat16
     x = (dev(q, bf), dev(k, bf), dev(v, bf), dev(a), dev(b), dev(do), dev(S0), dev(dST))
     ref = kda.chunk_backward(*x)
-    monkeypatch.setenv("KDA_BWD_WINDOW", window)
+    kda.set_tuning(bwd_window=window)
     got = kda.chunk_backward(*x)
     g_gate = kda.chunk_backward(*x[:3], x[3][..., 0].contiguous(), *x[4:])
-    monkeypatch.delenv("KDA_BWD_WINDOW")
+    kda.set_tuning(bwd_window=0)
     r_gate = kda.chunk_backward(*x[:3], x[3][..., 0].contiguous(), *x[4:])
     torch.cuda.synchronize()
     for n, u, w in zip(NAMES, got, ref):
@@ -185,7 +186,7 @@ def test_backward_windows_are_exact(window, monkeypatch):
         assert torch.equal(u, w), n
 
 
-@pytest.mark.parametrize("window,max_seqlen", [("1", None), ("2", 0), ("1", 0)])
+@pytest.mark.parametrize("window,max_seqlen", [("1", 200), ("2", 0), ("1", 0)])
 def test_backward_varlen_windows_are_exact(window, max_seqlen, monkeypatch):
     """Packed sequences in windows (with the longest length given, or unknown:
     then windows past every sequence's start do nothing) against the
@@ -200,10 +201,10 @@ def test_backward_varlen_windows_are_exact(window, max_seqlen, monkeypatch):
     dST = random_state(rng, (len(lengths), H, D, D))
     x = (dev(q), dev(k), dev(v), dev(a), dev(b), torch.from_numpy(cu).cuda(), dev(do), dev(S0),
          dev(dST))
-    ref = kda.chunk_backward_varlen(*x)
-    monkeypatch.setenv("KDA_BWD_WINDOW", window)
+    ref = kda.chunk_backward_varlen(*x, max_seqlen=0)   # unknown: T_total assumed
+    kda.set_tuning(bwd_window=window)
     got = kda.chunk_backward_varlen(*x, max_seqlen=max_seqlen)
-    monkeypatch.delenv("KDA_BWD_WINDOW")
+    kda.set_tuning(bwd_window=0)
     torch.cuda.synchronize()
     for n, u, w in zip(NAMES, got, ref):
         assert torch.equal(u, w), n
@@ -275,7 +276,7 @@ def test_backward_varlen_rectangular(window, monkeypatch):
     dST = random_state(rng, (len(lengths), H, dk, dv))
     td = tdtype("bf16")
     if window:
-        monkeypatch.setenv("KDA_BWD_WINDOW", window)
+        kda.set_tuning(bwd_window=window)
     got = kda.chunk_backward_varlen(dev(q, td), dev(k, td), dev(v, td), dev(a), dev(b),
                                     torch.from_numpy(cu).cuda(), dev(do), dev(S0), dev(dST),
                                     max_seqlen=max(lengths))
@@ -284,3 +285,33 @@ def test_backward_varlen_rectangular(window, monkeypatch):
     errs = {n: max_rel_err(host(g), r) for n, g, r in zip(NAMES, got, ref)}
     flush("    " + " ".join(f"{n}={e:.1e}" for n, e in errs.items()))
     assert max(errs.values()) <= TOL["bf16"], errs
+
+
+def test_backward_varlen_max_seqlen_below_the_longest():
+    """max_seqlen below the longest sequence (one window of 2 chunks, so no
+    adjoint carry buffer): the call completes, sequences that fit get every
+    gradient, and a longer sequence gets the right gradients on its last two
+    chunks (the header: earlier tokens and its initial-state gradient are not
+    written)."""
+    lengths = [130, 40, 300]
+    H, d = 2, 64
+    flush(f"[backward] varlen max_seqlen=100 below the longest, lengths={lengths} H={H} d={d}")
+    q, k, v, a, b, cu = I.packed_inputs(780, lengths, H, d, d, "f32")
+    rng = np.random.default_rng(781)
+    do = rng.standard_normal((int(cu[-1]), H, d)).astype(np.float32)
+    S0 = random_state(rng, (len(lengths), H, d, d))
+    dST = random_state(rng, (len(lengths), H, d, d))
+    got = kda.chunk_backward_varlen(dev(q), dev(k), dev(v), dev(a), dev(b),
+                                    torch.from_numpy(cu).cuda(), dev(do), dev(S0), dev(dST),
+                                    max_seqlen=100)
+    torch.cuda.synchronize()
+    got = [host(g) for g in got]
+    for n, first in [(0, 64), (1, 0), (2, 192)]:   # first token whose chunk is covered
+        s_, e_ = int(cu[n]), int(cu[n + 1])
+        sl = lambda x: x[None, s_:e_]  # noqa: E731
+        ref = kda_backward(sl(q), sl(k), sl(v), sl(a), sl(b), S0[n:n + 1], sl(do), dST[n:n + 1])
+        for nm, g, r in zip(NAMES[:5], got[:5], ref[:5]):
+            err = max_rel_err(g[s_ + first:e_], r[0, first:])
+            assert err <= TOL["f32"], (n, nm, err)
+        if first == 0:
+            assert max_rel_err(got[5][n], ref[5][0]) <= TOL["f32"], n

@@ -37,7 +37,7 @@ def _cfg1_oracle():
 def test_prefill_bf16_b1_h32_t8192_full(path, monkeypatch):
     """B=1, H=32, T=8192, d=128, bf16 q/k/v, zero initial state: every head,
     in both prefill forms (the staged form is the default at this size)."""
-    monkeypatch.setenv("KDA_PREFILL_PATH", path)
+    kda.set_tuning(prefill_form=path)
     flush(f"[config] prefill B=1 H=32 T=8192 d=128 bf16 (all heads) path={path}")
     (q, k, v, a, b), (o_ref, S_ref) = _cfg1_oracle()
     bf = torch.bfloat16
@@ -54,7 +54,7 @@ def test_prefill_snapshots_b1_h32_t8192_head_subset(path, monkeypatch):
     16 chunks (1024 tokens): 8 snapshots per head.  Heads {0, 13, 31} are
     checked against the oracle's snapshots; o and the final state of the
     snapshot call equal the plain prefill's bit for bit."""
-    monkeypatch.setenv("KDA_PREFILL_PATH", path)
+    kda.set_tuning(prefill_form=path)
     flush(f"[config] prefill+snapshots B=1 H=32 T=8192 d=128 bf16 every=16 path={path}")
     q, k, v, a, b = _cfg1_inputs()
     bf = torch.bfloat16
@@ -180,7 +180,7 @@ def test_backward_varlen_n64_h32_sequence_head_subset():
     gen = torch.Generator(device="cuda")
     gen.manual_seed(I.SEED + 31)
     do = torch.randn((Tt, H, D), generator=gen, device="cuda")
-    grads = kda.chunk_backward_varlen(q, k, v, a, b, cu_d, do)
+    grads = kda.chunk_backward_varlen(q, k, v, a, b, cu_d, do, max_seqlen=int(lengths.max()))
     torch.cuda.synchronize()
     heads = [0, 31]
     names = ("dq", "dk", "dv", "dalpha", "dbeta")

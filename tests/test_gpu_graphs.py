@@ -90,7 +90,7 @@ def test_backward_replays_match_eager(window, monkeypatch):
     with the adjoint carried in the workspace) captured once and replayed;
     every replay equals the eager call."""
     if window:
-        monkeypatch.setenv("KDA_BWD_WINDOW", window)
+        kda.set_tuning(bwd_window=window)
     B, T, H, D = 1, 200, 3, 128
     flush(f"[graph] backward B={B} T={T} H={H} d={D} window={window}: 3 replays")
     q, k, v, a, b = I.batch_inputs(802, B, T, H, D, D, "bf16")
@@ -118,5 +118,55 @@ def test_backward_replays_match_eager(window, monkeypatch):
         torch.cuda.synchronize()
         for u, w in zip(out, ref):
             assert torch.equal(u, w), i
+        _ = (x[3] * 2).sum()                     # unrelated eager work between replays
+        torch.cuda.synchronize()
+
+
+def test_varlen_snapshots_and_backward_replay_match_eager():
+    """Packed-sequence calls under capture: the snapshot prefill (default
+    offsets built on the device) and the backward (max_seqlen from the host)
+    read no device data on the host, so both capture as plain launches; three
+    replays, each checked bit for bit against the eager calls."""
+    lengths = [70, 0, 5, 200, 64]
+    H, D = 2, 128
+    flush(f"[graph] varlen snapshots + backward lengths={lengths} H={H} d={D}: 3 replays")
+    q, k, v, a, b, cu = I.packed_inputs(804, lengths, H, D, D, "bf16")
+    rng = np.random.default_rng(805)
+    do = rng.standard_normal(v.shape).astype(np.float32)
+    S0 = random_state(rng, (len(lengths), H, D, D))
+    bf = torch.bfloat16
+    x = [dev(q, bf), dev(k, bf), dev(v, bf), dev(a), dev(b)]
+    cu_d = torch.from_numpy(cu).cuda()
+    ml = max(lengths)
+    ws = torch.empty(kda.lib().kda_chunk_backward_varlen_workspace_size(
+        len(lengths), int(cu[-1]), ml, H, D, D, 64), device="cuda", dtype=torch.uint8)
+    ref_p = [t.clone() for t in kda.chunk_prefill_varlen_snapshots(*x, cu_d, 1, dev(S0))]
+    ref_b = [t.clone() for t in kda.chunk_backward_varlen(*x, cu_d, dev(do), dev(S0), None,
+                                                          max_seqlen=ml, workspace=ws)]
+    torch.cuda.synchronize()
+
+    def calls():
+        p = kda.chunk_prefill_varlen_snapshots(*x, cu_d, 1, dev_S0)
+        g_ = kda.chunk_backward_varlen(*x, cu_d, dev_do, dev_S0, None, max_seqlen=ml, workspace=ws)
+        return p, g_
+
+    dev_S0, dev_do = dev(S0), dev(do)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        calls()                                  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out_p, out_b = calls()
+    for i in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        rows = sum(n // 64 for n in lengths)     # snapshot rows the sequences write
+        for j, (u, w) in enumerate(zip(out_p, ref_p)):
+            assert torch.equal(u[:rows] if j == 2 else u, w[:rows] if j == 2 else w), ("prefill", i)
+        for u, w in zip(out_b, ref_b):
+            assert torch.equal(u, w), ("backward", i)
         _ = (x[3] * 2).sum()                     # unrelated eager work between replays
         torch.cuda.synchronize()

@@ -44,7 +44,7 @@ PATHS = ["fused", "split"]
 def test_prefill_bf16_shapes(T, d, path, monkeypatch):
     """Both prefill forms: the one-kernel form and the staged form (per-chunk
     operands computed for all chunks first, then the state pass)."""
-    monkeypatch.setenv("KDA_PREFILL_PATH", path)
+    kda.set_tuning(prefill_form=path)
     eo, es = prefill_case(2, T, 3, d, d, "bf16", c=100 + T, with_state=True, seed=T)
     assert eo <= TOL["bf16"] and es <= TOL["bf16"]
 
@@ -53,7 +53,7 @@ def test_prefill_bf16_shapes(T, d, path, monkeypatch):
 @pytest.mark.parametrize("T", [1, 65, 200])
 @pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128), (128, 64), (64, 128)])
 def test_prefill_fp32_shapes(T, dk, dv, path, monkeypatch):
-    monkeypatch.setenv("KDA_PREFILL_PATH", path)
+    kda.set_tuning(prefill_form=path)
     eo, es = prefill_case(1, T, 2, dk, dv, "f32", c=200 + T, with_state=True, seed=T)
     assert eo <= TOL["f32"] and es <= TOL["f32"]
 
@@ -61,7 +61,7 @@ def test_prefill_fp32_shapes(T, dk, dv, path, monkeypatch):
 @pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("dk,dv", [(128, 64), (64, 128)])
 def test_prefill_bf16_rectangular(dk, dv, path, monkeypatch):
-    monkeypatch.setenv("KDA_PREFILL_PATH", path)
+    kda.set_tuning(prefill_form=path)
     eo, es = prefill_case(2, 130, 2, dk, dv, "bf16", c=300, with_state=True)
     assert eo <= TOL["bf16"] and es <= TOL["bf16"]
 
@@ -71,8 +71,8 @@ def test_prefill_bf16_rectangular(dk, dv, path, monkeypatch):
 def test_prefill_every_slab_width(nsub, path, monkeypatch):
     """The sequential pass is split into value slabs of 16*nsub columns; every
     width gives the oracle's result, in both prefill forms."""
-    monkeypatch.setenv("KDA_PREFILL_NSUB", str(nsub))
-    monkeypatch.setenv("KDA_PREFILL_PATH", path)
+    kda.set_tuning(prefill_nsub=nsub)
+    kda.set_tuning(prefill_form=path)
     eo, es = prefill_case(1, 190, 2, 128, 128, "bf16", c=400, with_state=True)
     assert eo <= TOL["bf16"] and es <= TOL["bf16"]
 
@@ -83,8 +83,8 @@ def test_prefill_split_segments(seg, dt, monkeypatch):
     """The staged form processes long sequences in segments of chunks, the
     state carried between segments in the workspace: any segment length gives
     the oracle's result (7 chunks, ragged tail, nonzero initial state)."""
-    monkeypatch.setenv("KDA_PREFILL_PATH", "split")
-    monkeypatch.setenv("KDA_PREFILL_SEG", str(seg))
+    kda.set_tuning(prefill_form="split")
+    kda.set_tuning(prefill_seg=seg)
     eo, es = prefill_case(2, 7 * 64 - 9, 2, 128, 128, dt, c=410 + seg, with_state=True, seed=seg)
     assert eo <= TOL[dt] and es <= TOL[dt]
 
@@ -93,7 +93,7 @@ def test_prefill_split_segments(seg, dt, monkeypatch):
 def test_prefill_paths_agree_on_config_shape(path, monkeypatch):
     """B=1, H=32, T=1000, d=128, bf16 (the benchmark's head count): both forms
     against the oracle."""
-    monkeypatch.setenv("KDA_PREFILL_PATH", path)
+    kda.set_tuning(prefill_form=path)
     eo, es = prefill_case(1, 1000, 32, 128, 128, "bf16", c=420, with_state=True)
     assert eo <= TOL["bf16"] and es <= TOL["bf16"]
 

@@ -27,7 +27,7 @@ def gate_of(a):
                                         ("f32", 130, 128, 64), ("bf16", 17, 64, 128),
                                         ("f32", 256, 64, 64)])
 def test_scalar_gate_prefill_matches_oracle(dt, T, dk, dv, path, monkeypatch):
-    monkeypatch.setenv("KDA_PREFILL_PATH", path)
+    kda.set_tuning(prefill_form=path)
     B, H = 2, 3
     flush(f"[scalar gate] prefill B={B} T={T} H={H} DK={dk} DV={dv} {dt} path={path}")
     q, k, v, a, b = I.batch_inputs(600 + T, B, T, H, dk, dv, dt)
@@ -89,7 +89,7 @@ def test_scalar_gate_decode_matches_oracle(dt, dk, dv):
 def test_scalar_gate_prefill_b1_h32_t8192_head_subset(path, monkeypatch):
     """The benchmark prefill shape (B=1, H=32, T=8192, d=128, bf16) with a
     scalar gate; heads {0, 31} against the oracle."""
-    monkeypatch.setenv("KDA_PREFILL_PATH", path)
+    kda.set_tuning(prefill_form=path)
     B, T, H, D = 1, 8192, 32, 128
     flush(f"[scalar gate] prefill B={B} T={T} H={H} d={D} bf16 path={path}")
     heads = [0, 31]
@@ -115,7 +115,7 @@ def test_scalar_gate_backward_matches_oracle(dt, T, d, path, monkeypatch):
     """Gradients of the scalar-gate prefill (the gate's: one value per
     token-head) against the fp64 oracle, with an initial state and a
     final-state gradient."""
-    monkeypatch.setenv("KDA_PREFILL_PATH", path)
+    kda.set_tuning(prefill_form=path)
     B, H = 2, 3
     flush(f"[scalar gate] backward B={B} T={T} H={H} d={d} {dt} path={path}")
     q, k, v, a, b = I.batch_inputs(620 + T, B, T, H, d, d, dt)
@@ -150,7 +150,8 @@ def test_scalar_gate_backward_varlen_matches_oracle(dt, d):
     dST = random_state(rng, (len(lengths), H, d, d))
     td = tdtype(dt)
     got = kda.chunk_backward_varlen(dev(q, td), dev(k, td), dev(v, td), dev(g), dev(b),
-                                    torch.from_numpy(cu).cuda(), dev(do), dev(S0), dev(dST))
+                                    torch.from_numpy(cu).cuda(), dev(do), dev(S0), dev(dST),
+                                    max_seqlen=max(lengths))
     torch.cuda.synchronize()
     got = [host(x) for x in got]
     parts = [[] for _ in range(6)]
@@ -183,10 +184,10 @@ def test_scalar_gate_backward_varlen_windows_are_exact(window, monkeypatch):
     td = tdtype("bf16")
     x = (dev(q, td), dev(k, td), dev(v, td), dev(g), dev(b), torch.from_numpy(cu).cuda(), dev(do),
          dev(S0), dev(dST))
-    ref = kda.chunk_backward_varlen(*x)
-    monkeypatch.setenv("KDA_BWD_WINDOW", window)
+    ref = kda.chunk_backward_varlen(*x, max_seqlen=max(lengths))
+    kda.set_tuning(bwd_window=window)
     got = kda.chunk_backward_varlen(*x, max_seqlen=max(lengths))
-    monkeypatch.delenv("KDA_BWD_WINDOW")
+    kda.set_tuning(bwd_window=0)
     torch.cuda.synchronize()
     for n, u, w in zip(GRADS, got, ref):
         assert torch.equal(u, w), n

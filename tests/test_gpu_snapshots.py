@@ -22,7 +22,7 @@ PATHS = ["fused", "split"]
 def test_snapshots_match_oracle(dt, dk, dv, every, path, monkeypatch):
     """B=2, H=3, T=337 (5 full chunks and a ragged tail of 17 tokens), random
     initial state: T // (64 every) snapshots, o and the final state."""
-    monkeypatch.setenv("KDA_PREFILL_PATH", path)
+    kda.set_tuning(prefill_form=path)
     B, T, H = 2, 337, 3
     flush(f"[snapshots] B={B} T={T} H={H} DK={dk} DV={dv} {dt} every={every} path={path}")
     q, k, v, a, b = I.batch_inputs(500 + every, B, T, H, dk, dv, dt)
@@ -46,7 +46,7 @@ def test_snapshots_match_oracle(dt, dk, dv, every, path, monkeypatch):
 def test_snapshot_call_matches_plain_prefill_bitwise(path, monkeypatch):
     """The snapshot kernels compute o and the final state exactly as the plain
     prefill does (the snapshots are extra stores only)."""
-    monkeypatch.setenv("KDA_PREFILL_PATH", path)
+    kda.set_tuning(prefill_form=path)
     B, T, H, D = 1, 64 * 7 + 9, 4, 128
     flush(f"[snapshots] bitwise vs plain prefill B={B} T={T} H={H} d={D} path={path}")
     q, k, v, a, b = I.batch_inputs(510, B, T, H, D, D, "bf16")
@@ -67,7 +67,7 @@ def test_resume_from_snapshot_is_exact(dt, path, monkeypatch):
     after it reproduces the full run's outputs and final state bit for bit
     (same chunk alignment, same arithmetic).  The last snapshot of a sequence
     whose length is a multiple of the interval is its final state."""
-    monkeypatch.setenv("KDA_PREFILL_PATH", path)
+    kda.set_tuning(prefill_form=path)
     B, T, H, D, every = 2, 64 * 6, 3, 128, 2
     flush(f"[snapshots] resume B={B} T={T} H={H} d={D} {dt} every={every} path={path}")
     q, k, v, a, b = I.batch_inputs(520, B, T, H, D, D, dt)
@@ -103,8 +103,8 @@ def test_snapshots_without_full_interval():
 def test_snapshots_across_staged_segments(seg, monkeypatch):
     """Staged form processed in segments of `seg` chunks (state carried
     between launches): snapshots still land at the right boundaries."""
-    monkeypatch.setenv("KDA_PREFILL_PATH", "split")
-    monkeypatch.setenv("KDA_PREFILL_SEG", str(seg))
+    kda.set_tuning(prefill_form="split")
+    kda.set_tuning(prefill_seg=seg)
     B, T, H, D, every = 1, 64 * 7 + 30, 2, 128, 3
     flush(f"[snapshots] segments seg={seg} B={B} T={T} H={H} d={D} every={every}")
     q, k, v, a, b = I.batch_inputs(540, B, T, H, D, D, "bf16")
@@ -151,12 +151,14 @@ def test_varlen_snapshots_match_oracle(dt, dk, dv, every):
     torch.cuda.synchronize()
     per = [n // (64 * every) for n in lengths]
     assert offs.cpu().tolist() == list(np.concatenate([[0], np.cumsum(per)]))
-    assert sn.shape[0] == sum(per) == sn_ref.shape[0]
+    # rows: the bound T_total // (64 every), known on the host without reading
+    # the lengths; the sequences fill the first sum(per)
+    assert sn.shape[0] == sum(lengths) // (64 * every) and sum(per) == sn_ref.shape[0]
     assert torch.equal(o, o1) and torch.equal(S, S1)
     eo, es = max_rel_err(host(o), o_ref), max_rel_err(host(S), S_ref)
     flush(f"    err o={eo:.2e} S={es:.2e}")
     assert eo <= TOL[dt] and es <= TOL[dt]
-    for r in range(sn.shape[0]):
+    for r in range(sum(per)):
         assert max_rel_err(host(sn[r]), sn_ref[r]) <= TOL[dt], r
 
 

@@ -1,0 +1,216 @@
+"""GPU parity at strong decay: channels that forget at once.
+
+The finer, per-channel gate lets some channels of the state forget at once
+("Kimi Linear、独自の土俵でFull Attentionを上回る" (remio.ai), section
+"Kimi Linearがより賢いRecurrent Memoryを使う方法"; "Kimi Delta Attention
+徹底解説" (tech-tide.dev), section "Kimi Delta Attention の仕組み": each
+channel keeps or drops its memory on its own).  The kernels factor the decays
+through a reference row per 16-token block, so their data domain reaches
+alpha = 1e-4.  Three alpha distributions, on every path (fused and staged
+prefill, snapshots, packed sequences, scalar gate, decode, backward):
+  uniform  alpha ~ U[1e-4, 0.07] on every channel
+  edge     alpha = 1e-4 on every channel
+  mixed    the benchmark distribution exp(-exp(U(-5,-1))) with 8 channels per
+           head drawn log-uniformly from [5e-4, 2e-3] (fast-forget channels)
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from gated_delta_rule_diag_amd import inputs as I
+from gated_delta_rule_diag_amd import kda
+from kda_testlib import TOL, dev, flush, host, random_state, tdtype
+from oracle import (gdn_backward, gdn_recurrent, kda_backward, kda_decode_step, kda_recurrent,
+                    kda_recurrent_snapshots, kda_recurrent_varlen, max_rel_err)
+
+pytestmark = pytest.mark.gpu
+
+PATHS = ["fused", "split"]
+DISTS = ["uniform", "edge", "mixed"]
+NAMES = ("dq", "dk", "dv", "dalpha", "dbeta", "dS0")
+
+
+def alpha_of(dist, a_bench, seed):
+    """alpha of the same shape as a_bench ([..., H, DK]) for distribution dist."""
+    rng = np.random.default_rng(seed)
+    if dist == "uniform":
+        return rng.uniform(1e-4, 0.07, a_bench.shape).astype(np.float32)
+    if dist == "edge":
+        return np.full(a_bench.shape, 1e-4, np.float32)
+    a = a_bench.copy()
+    DK = a.shape[-1]
+    H = a.shape[-2]
+    for h in range(H):
+        ch = rng.choice(DK, 8, replace=False)
+        lo = np.exp(rng.uniform(np.log(5e-4), np.log(2e-3), a[..., h, ch].shape))
+        a[..., h, ch] = lo.astype(np.float32)
+    return a
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("dt,d", [("bf16", 128), ("f32", 64), ("bf16", 64), ("f32", 128)])
+@pytest.mark.parametrize("dist", DISTS)
+def test_prefill_strong_decay(dist, dt, d, path, monkeypatch):
+    kda.set_tuning(prefill_form=path)
+    B, T, H = 1, 300, 2
+    flush(f"[strong decay] prefill {dist} B={B} T={T} H={H} d={d} {dt} {path}")
+    q, k, v, a0, b = I.batch_inputs(1100 + d, B, T, H, d, d, dt)
+    a = alpha_of(dist, a0, 1101 + d)
+    S0 = random_state(np.random.default_rng(1102), (B, H, d, d))
+    td = tdtype(dt)
+    o, S = kda.chunk_prefill(dev(q, td), dev(k, td), dev(v, td), dev(a), dev(b), dev(S0))
+    torch.cuda.synchronize()
+    ro, rS = kda_recurrent(q, k, v, a, b, S0)
+    e = (max_rel_err(host(o), ro), max_rel_err(host(S), rS))
+    flush(f"    o={e[0]:.1e} S={e[1]:.1e}")
+    assert np.isfinite(host(o)).all() and np.isfinite(host(S)).all()
+    assert max(e) <= TOL[dt], e
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("dt,d", [("bf16", 128), ("f32", 64)])
+def test_snapshots_strong_decay(dt, d, path, monkeypatch):
+    kda.set_tuning(prefill_form=path)
+    B, T, H, every = 2, 337, 2, 1
+    flush(f"[strong decay] snapshots uniform B={B} T={T} H={H} d={d} {dt} {path}")
+    q, k, v, a0, b = I.batch_inputs(1110, B, T, H, d, d, dt)
+    a = alpha_of("uniform", a0, 1111)
+    S0 = random_state(np.random.default_rng(1112), (B, H, d, d))
+    td = tdtype(dt)
+    o, S, sn = kda.chunk_prefill_snapshots(dev(q, td), dev(k, td), dev(v, td), dev(a), dev(b),
+                                           every, dev(S0))
+    torch.cuda.synchronize()
+    ro, rS, rsn = kda_recurrent_snapshots(q, k, v, a, b, every, S0)
+    e = (max_rel_err(host(o), ro), max_rel_err(host(S), rS), max_rel_err(host(sn), rsn))
+    flush(f"    o={e[0]:.1e} S={e[1]:.1e} snapshots={e[2]:.1e}")
+    assert max(e) <= TOL[dt], e
+    for j in range(sn.shape[1]):
+        assert max_rel_err(host(sn[:, j]), rsn[:, j]) <= TOL[dt]
+
+
+@pytest.mark.parametrize("dt,d", [("bf16", 128), ("f32", 64)])
+@pytest.mark.parametrize("dist", ["uniform", "mixed"])
+def test_varlen_strong_decay(dist, dt, d):
+    H = 2
+    lengths = [70, 0, 5, 200, 64, 131]
+    flush(f"[strong decay] varlen {dist} lengths={lengths} H={H} d={d} {dt}")
+    q, k, v, a0, b, cu = I.packed_inputs(1120, lengths, H, d, d, dt)
+    a = alpha_of(dist, a0, 1121)
+    S0 = random_state(np.random.default_rng(1122), (len(lengths), H, d, d))
+    td = tdtype(dt)
+    o, S = kda.chunk_prefill_varlen(dev(q, td), dev(k, td), dev(v, td), dev(a), dev(b),
+                                    torch.from_numpy(cu).cuda(), dev(S0))
+    torch.cuda.synchronize()
+    ro, rS = kda_recurrent_varlen(q, k, v, a, b, cu, S0)
+    e = (max_rel_err(host(o), ro), max_rel_err(host(S), rS))
+    flush(f"    o={e[0]:.1e} S={e[1]:.1e}")
+    assert max(e) <= TOL[dt], e
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_scalar_gate_strong_decay(path, monkeypatch):
+    """Gated DeltaNet with gates ~ U[1e-4, 0.07]: prefill, one decode step and
+    the backward against the scalar-gate oracle."""
+    kda.set_tuning(prefill_form=path)
+    B, T, H, d = 1, 200, 2, 128
+    flush(f"[strong decay] scalar gate B={B} T={T} H={H} d={d} bf16 {path}")
+    q, k, v, _, b = I.batch_inputs(1130, B, T, H, d, d, "bf16")
+    rng = np.random.default_rng(1131)
+    g = rng.uniform(1e-4, 0.07, (B, T, H)).astype(np.float32)
+    S0 = random_state(rng, (B, H, d, d))
+    bf = torch.bfloat16
+    x = (dev(q, bf), dev(k, bf), dev(v, bf))
+    o, S = kda.chunk_prefill(*x, dev(g), dev(b), dev(S0))
+    torch.cuda.synchronize()
+    ro, rS = gdn_recurrent(q, k, v, g, b, S0)
+    e = (max_rel_err(host(o), ro), max_rel_err(host(S), rS))
+    flush(f"    prefill o={e[0]:.1e} S={e[1]:.1e}")
+    assert max(e) <= TOL["bf16"], e
+    do = rng.standard_normal((B, T, H, d)).astype(np.float32)
+    dST = random_state(rng, (B, H, d, d))
+    got = [host(t) for t in kda.chunk_backward(*x, dev(g), dev(b), dev(do), dev(S0), dev(dST))]
+    torch.cuda.synchronize()
+    ref = gdn_backward(q, k, v, g, b, S0, do, dST)
+    errs = {n: max_rel_err(gg, r) for n, gg, r in zip(NAMES, got, ref)}
+    flush("    backward " + " ".join(f"{n}={x:.1e}" for n, x in errs.items()))
+    assert max(errs.values()) <= TOL["bf16"], errs
+
+
+@pytest.mark.parametrize("dt,d", [("bf16", 128), ("f32", 64)])
+def test_decode_strong_decay(dt, d):
+    N, H = 5, 3
+    flush(f"[strong decay] decode N={N} H={H} d={d} {dt}")
+    q, k, v, a0, b = I.decode_inputs(1140, N, H, d, d, dt)
+    a = alpha_of("uniform", a0, 1141)
+    S0 = random_state(np.random.default_rng(1142), (N, H, d, d))
+    td = tdtype(dt)
+    st = dev(S0)
+    o = kda.decode_step(dev(q, td), dev(k, td), dev(v, td), dev(a), dev(b), st)
+    torch.cuda.synchronize()
+    ro, rS = kda_decode_step(q, k, v, a, b, S0)
+    e = (max_rel_err(host(o), ro), max_rel_err(host(st), rS))
+    flush(f"    o={e[0]:.1e} S={e[1]:.1e}")
+    assert max(e) <= TOL[dt], e
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("dt,d", [("bf16", 128), ("f32", 64)])
+@pytest.mark.parametrize("dist", DISTS)
+def test_backward_strong_decay(dist, dt, d, path, monkeypatch):
+    """Every gradient against the oracle's reverse mode.  For fp32 inputs the
+    alpha gradient is checked as d(log alpha) = alpha * dalpha, the quantity
+    the chunk form accumulates: dalpha = d(log alpha) / alpha carries the
+    fp32 rounding of that sum (about 64 u times its largest term) divided by
+    alpha, i.e. magnified 1e4-fold at alpha = 1e-4; dalpha itself is then
+    held to the bf16 bar."""
+    kda.set_tuning(prefill_form=path)
+    B, T, H = 1, 200, 2
+    flush(f"[strong decay] backward {dist} B={B} T={T} H={H} d={d} {dt} {path}")
+    q, k, v, a0, b = I.batch_inputs(1150 + d, B, T, H, d, d, dt)
+    a = alpha_of(dist, a0, 1151)
+    rng = np.random.default_rng(1152)
+    do = rng.standard_normal((B, T, H, d)).astype(np.float32)
+    S0 = random_state(rng, (B, H, d, d))
+    dST = random_state(rng, (B, H, d, d))
+    td = tdtype(dt)
+    got = kda.chunk_backward(dev(q, td), dev(k, td), dev(v, td), dev(a), dev(b), dev(do),
+                             dev(S0), dev(dST))
+    torch.cuda.synchronize()
+    got = [host(g) for g in got]
+    ref = kda_backward(q, k, v, a, b, S0, do, dST)
+    errs = {n: max_rel_err(g, r) for n, g, r in zip(NAMES, got, ref)}
+    errs["dlogalpha"] = max_rel_err(got[3] * a, ref[3] * a)
+    flush("    " + " ".join(f"{n}={e:.1e}" for n, e in errs.items()))
+    assert all(np.isfinite(g).all() for g in got)
+    if dt == "f32":
+        assert errs["dalpha"] <= TOL["bf16"], errs
+        del errs["dalpha"]
+    assert max(errs.values()) <= TOL[dt], errs
+
+
+def test_backward_varlen_strong_decay():
+    H, d = 2, 128
+    lengths = [70, 0, 5, 200, 64]
+    flush(f"[strong decay] backward varlen uniform lengths={lengths} H={H} d={d} bf16")
+    q, k, v, a0, b, cu = I.packed_inputs(1160, lengths, H, d, d, "bf16")
+    a = alpha_of("uniform", a0, 1161)
+    rng = np.random.default_rng(1162)
+    do = rng.standard_normal(v.shape).astype(np.float32)
+    N = len(lengths)
+    S0 = random_state(rng, (N, H, d, d))
+    dST = random_state(rng, (N, H, d, d))
+    bf = torch.bfloat16
+    got = kda.chunk_backward_varlen(dev(q, bf), dev(k, bf), dev(v, bf), dev(a), dev(b),
+                                    torch.from_numpy(cu).cuda(), dev(do), dev(S0), dev(dST),
+                                    max_seqlen=max(lengths))
+    torch.cuda.synchronize()
+    got = [host(g) for g in got]
+    for n in range(N):
+        s, e = int(cu[n]), int(cu[n + 1])
+        sl = lambda x: x[None, s:e]  # noqa: E731
+        ref = kda_backward(sl(q), sl(k), sl(v), sl(a), sl(b), S0[n:n + 1], sl(do), dST[n:n + 1])
+        mine = [g[s:e][None] for g in got[:5]] + [got[5][n:n + 1]]
+        errs = {nm: (max_rel_err(g, r) if r.size else 0.0) for nm, g, r in zip(NAMES, mine, ref)}
+        flush(f"    seq {n} len {e - s}: " + " ".join(f"{nm}={x:.1e}" for nm, x in errs.items()))
+        assert max(errs.values()) <= TOL["bf16"], (n, errs)

@@ -110,18 +110,18 @@ def test_varlen_equals_separate_calls_and_permutes(monkeypatch):
             continue
         args = (t(q[None, s:e], bf), t(k[None, s:e], bf), t(v[None, s:e], bf),
                 t(a[None, s:e]), t(b[None, s:e]), t(S0[n:n + 1]))
-        monkeypatch.setenv("KDA_PREFILL_PATH", "fused")
+        kda.set_tuning(prefill_form="fused")
         o1, S1 = kda.chunk_prefill(*args)
         torch.cuda.synchronize()
         # the same kernels on the same data: identical results
         np.testing.assert_array_equal(host(o1)[0], on[s:e])
         np.testing.assert_array_equal(host(S1)[0], Sn[n])
-        monkeypatch.setenv("KDA_PREFILL_PATH", "split")
+        kda.set_tuning(prefill_form="split")
         o2, S2 = kda.chunk_prefill(*args)
         torch.cuda.synchronize()
         assert max_rel_err(host(o2)[0], on[s:e]) <= 1e-4
         assert max_rel_err(host(S2)[0], Sn[n]) <= 1e-4
-        monkeypatch.delenv("KDA_PREFILL_PATH")
+        kda.set_tuning(prefill_form="auto")
     perm = [4, 0, 5, 2, 1, 3]
     pl = [lengths[i] for i in perm]
     pcu = np.concatenate([[0], np.cumsum(pl)]).astype(np.int32)
@@ -137,7 +137,7 @@ def test_varlen_equals_separate_calls_and_permutes(monkeypatch):
 
 @pytest.mark.parametrize("path", ["fused", "split"])
 def test_deterministic_bitwise(path, monkeypatch):
-    monkeypatch.setenv("KDA_PREFILL_PATH", path)
+    kda.set_tuning(prefill_form=path)
     q, k, v, a, b = I.batch_inputs(803, 1, 1000, 8, 128, 128, "bf16")
     args = (dev(q, bf), dev(k, bf), dev(v, bf), dev(a), dev(b))
     o1, S1 = kda.chunk_prefill(*args)
@@ -156,7 +156,7 @@ def test_deterministic_bitwise(path, monkeypatch):
 
 @pytest.mark.parametrize("path", ["fused", "split"])
 def test_nan_stays_in_its_own_sequence_and_head(path, monkeypatch):
-    monkeypatch.setenv("KDA_PREFILL_PATH", path)
+    kda.set_tuning(prefill_form=path)
     B, T, H, D = 3, 150, 4, 128
     q, k, v, a, b = I.batch_inputs(804, B, T, H, D, D, "bf16")
     v = v.copy()
@@ -211,7 +211,7 @@ def test_prefill_at_the_decay_domain_edge(path, dt, monkeypatch):
     32 tokens reaches ~1e-37, the edge of the data domain the header states
     (the decays are factored through each chunk's row 31).  Output and final
     state against the oracle."""
-    monkeypatch.setenv("KDA_PREFILL_PATH", path)
+    kda.set_tuning(prefill_form=path)
     B, T, H, D = 1, 300, 2, 64
     flush(f"[domain] prefill alpha in [0.07, 0.2] T={T} {dt} {path}")
     q, k, v, _, b = I.batch_inputs(880, B, T, H, D, D, dt)
