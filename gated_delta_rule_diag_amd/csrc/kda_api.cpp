@@ -211,6 +211,49 @@ kda_status_t kda_chunk_prefill(int B, int T, int H, int DK, int DV, int chunk,
                        state_out, workspace, workspace_bytes, stream, false);
 }
 
+kda_status_t kda_chunk_prefill_noalloc(int B, int T, int H, int DK, int DV, int chunk,
+                                       kda_dtype_t in_dtype, const void* q, const void* k,
+                                       const void* v, const float* alpha, const float* beta,
+                                       const float* state_in, float* o, float* state_out,
+                                       void* stream) {
+  if (B < 0 || T < 0) return fail(KDA_ERR_SHAPE, "negative size (B=%d T=%d)", B, T);
+  kda_status_t s = check_prefill(B, int64_t(B) * T, H, DK, DV, chunk, in_dtype, q, k, v, alpha,
+                                 beta, state_in, o, state_out, false);
+  if (s != KDA_OK) return s;
+  kda::PrefillArgs a{};
+  a.N = B;
+  a.T_fixed = T;
+  a.cu_seqlens = nullptr;
+  a.T_total = int64_t(B) * T;
+  a.H = H; a.DK = DK; a.DV = DV;
+  a.in_bf16 = in_dtype == KDA_BF16;
+  a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta;
+  a.state_in = state_in; a.o = o; a.state_out = state_out;
+  // The staged form's slots go to the static scratch in segments short enough
+  // that one segment's slots and the carried state fit it.
+  const size_t cap = kda::kNoallocScratchBytes;
+  const size_t carry = size_t(B) * H * DK * DV * 4;
+  const int64_t budget = carry < cap ? int64_t(cap - carry) : 1;
+  const size_t need = kda::prefill_workspace_bytes(B, a.T_total, H, DK, DV, false, budget);
+  if (need > cap)
+    return fail(KDA_ERR_UNSUPPORTED,
+                "B*H=%d pairs: the staged form needs %zu bytes of scratch (one chunk of slots "
+                "and the carried state), the static scratch holds %zu",
+                B * H, need, cap);
+  if (a.N == 0 || a.H == 0) return ok();
+  const char* msg = nullptr;
+  if (need > 0) {
+    void* ptr = kda::noalloc_scratch(&msg);
+    if (ptr == nullptr) return fail(KDA_ERR_HIP, "static scratch: %s", msg ? msg : "?");
+    a.workspace = ptr;
+    a.workspace_bytes = cap;
+    a.seg_budget = budget;
+  }
+  if (kda::launch_prefill(a, stream, &msg) != 0)
+    return fail(KDA_ERR_HIP, "prefill launch failed: %s", msg ? msg : "?");
+  return ok();
+}
+
 kda_status_t kda_chunk_prefill_scalar_gate(int B, int T, int H, int DK, int DV, int chunk,
                                            kda_dtype_t in_dtype, const void* q, const void* k,
                                            const void* v, const float* gate, const float* beta,

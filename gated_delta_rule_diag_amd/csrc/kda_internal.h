@@ -127,5 +127,9 @@ int launch_backward_chunk(const BwdChunkArgs& a, int stage, void* stream, const 
 size_t backward_chunk_floats(int DK, int DV);   // window-buffer floats per chunk-head
 size_t prefill_workspace_bytes(int N, int64_t T_total, int H, int DK, int DV, bool varlen,
                                int64_t seg_budget = 0);
+// Static per-device scratch of kda_chunk_prefill_noalloc: its size, and its
+// device address on the current device (nullptr and a message on failure).
+constexpr size_t kNoallocScratchBytes = size_t(64) << 20;
+void* noalloc_scratch(const char** msg);
 
 }  // namespace kda

@@ -41,6 +41,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "kda_internal.h"
 
 namespace kda {
@@ -1868,6 +1870,35 @@ int staged_nsub(int64_t pairs, int DV) {
 }
 
 }  // namespace
+
+// The staged form's workspace for callers that cannot allocate
+// (kda_chunk_prefill_noalloc): one array per device, reserved with the code
+// object while the process lives.  Host code never passes `scratch` itself to
+// a kernel (on the host it names a stand-in, not device memory): it takes the
+// device address from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) char scratch[kNoallocScratchBytes];
+
+void* noalloc_scratch(const char** msg) {
+  static std::mutex mu;
+  static void* addr[64] = {nullptr};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= 64) {
+    *msg = e != hipSuccess ? hipGetErrorString(e) : "device index out of range";
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) {
+      *msg = e != hipSuccess ? hipGetErrorString(e) : "no device address for the scratch array";
+      return nullptr;
+    }
+    addr[dev] = ptr;
+  }
+  return addr[dev];
+}
 
 size_t prefill_workspace_bytes(int N, int64_t T_total, int H, int DK, int DV, bool varlen,
                                int64_t seg_budget) {

@@ -46,6 +46,7 @@ EXPORTED = (
     "kda_status_string",
     "kda_last_error_message",
     "kda_internal_set_tuning",
+    "kda_chunk_prefill_noalloc",
 )
 
 
@@ -107,6 +108,8 @@ def load_library(path: str = _LIB_PATH) -> ctypes.CDLL:
     lib.kda_last_error_message.argtypes = []
     lib.kda_internal_set_tuning.restype = i
     lib.kda_internal_set_tuning.argtypes = [i, i, i, i]
+    lib.kda_chunk_prefill_noalloc.restype = i
+    lib.kda_chunk_prefill_noalloc.argtypes = [i, i, i, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     return lib
 
 

@@ -95,6 +95,29 @@ kda_status_t kda_chunk_prefill(int B, int T, int H, int DK, int DV, int chunk,
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * kda_chunk_prefill for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same arguments without the workspace, and the same result (bit for bit).
+ * Where kda_chunk_prefill would stage per-chunk operands in the workspace
+ * (B*H < 128, T > 64), this call stages them in a static device array of
+ * 64 MiB that the library keeps on every device it runs on until the process
+ * ends, in segments short enough for one segment's operands and the carried
+ * state to fit (more segments than with a workspace: somewhat slower).
+ * Returns KDA_ERR_UNSUPPORTED, enqueuing nothing, when even one chunk does
+ * not fit (only possible under the internal tuning override that forces the
+ * staged form on 128 or more (sequence, head) pairs); KDA_ERR_HIP if the
+ * array's device address cannot be obtained.  It allocates nothing and needs
+ * nothing zeroed: every call writes the parts it reads.  All calls on one
+ * device share the array: calls that overlap in time on one device (e.g. on
+ * two streams) race and give undefined results.
+ */
+kda_status_t kda_chunk_prefill_noalloc(int B, int T, int H, int DK, int DV, int chunk,
+                                       kda_dtype_t in_dtype, const void* q, const void* k,
+                                       const void* v, const float* alpha, const float* beta,
+                                       const float* state_in, float* o, float* state_out,
+                                       void* stream);
+
+/*
  * Chunked prefill with state snapshots at chunk boundaries (prefix caching):
  * the same computation as kda_chunk_prefill, and in addition the state after
  * every `every`-th chunk, i.e. after the first 64*every*(j+1) tokens of each

@@ -419,3 +419,27 @@ def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(ImportError):
         load_library(str(tmp_path / "missing.so"))
 
+
+def test_noalloc_prefill_rejects_what_the_scratch_cannot_hold(lib):
+    # 512 (sequence, head) pairs forced into the staged form: one chunk of
+    # slots (512 * 147,968 B) and the carried state exceed the 64 MiB static
+    # scratch; refused on the host, nothing enqueued
+    # (distinct tensors, far enough apart not to overlap at these sizes)
+    q, k, v, a, b, s_in, o, s_out = [ctypes.c_void_p(0x100000000 * (i + 1)) for i in range(8)]
+    assert lib.kda_internal_set_tuning(2, 0, 0, 0) == OK
+    try:
+        st = lib.kda_chunk_prefill_noalloc(4, 128, 128, 128, 128, 64, 1, q, k, v, a, b, s_in, o,
+                                           s_out, None)
+        assert st == UNSUP
+        assert "scratch" in lib.kda_last_error_message().decode()
+    finally:
+        assert lib.kda_internal_set_tuning(0, 0, 0, 0) == OK
+    # argument errors as for kda_chunk_prefill; nothing to do for B = 0
+    assert lib.kda_chunk_prefill_noalloc(1, 64, 2, 96, 64, 64, 1, q, k, v, a, b, s_in, o, s_out,
+                                         None) == UNSUP
+    assert lib.kda_chunk_prefill_noalloc(1, 64, 2, 64, 64, 32, 1, q, k, v, a, b, s_in, o, s_out,
+                                         None) == UNSUP
+    assert lib.kda_chunk_prefill_noalloc(-1, 64, 2, 64, 64, 64, 1, q, k, v, a, b, s_in, o, s_out,
+                                         None) == SHAPE
+    assert lib.kda_chunk_prefill_noalloc(0, 64, 2, 64, 64, 64, 1, q, k, v, a, b, s_in, o, s_out,
+                                         None) == OK
