@@ -9,6 +9,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <rocprofiler-sdk-roctx/roctx.h>
+
 #include <atomic>
 #include <string>
 
@@ -16,6 +18,15 @@
 #include "kda_internal.h"
 
 namespace {
+
+// A roctx range over one ABI call (its name), so that a rocprofv3 trace with
+// markers shows which entry point launched which kernels.
+struct TraceRange {
+  explicit TraceRange(const char* name) { roctxRangePushA(name); }
+  ~TraceRange() { roctxRangePop(); }
+  TraceRange(const TraceRange&) = delete;
+  TraceRange& operator=(const TraceRange&) = delete;
+};
 
 std::atomic<int> g_prefill_form{0}, g_prefill_nsub{0}, g_prefill_seg{0}, g_bwd_window{0};
 
@@ -207,6 +218,7 @@ kda_status_t kda_chunk_prefill(int B, int T, int H, int DK, int DV, int chunk,
                                const void* v, const float* alpha, const float* beta,
                                const float* state_in, float* o, float* state_out,
                                void* workspace, size_t workspace_bytes, void* stream) {
+  TraceRange trace_range("kda_chunk_prefill");
   return prefill_fixed(B, T, H, DK, DV, chunk, in_dtype, q, k, v, alpha, beta, state_in, o,
                        state_out, workspace, workspace_bytes, stream, false);
 }
@@ -216,6 +228,7 @@ kda_status_t kda_chunk_prefill_noalloc(int B, int T, int H, int DK, int DV, int 
                                        const void* v, const float* alpha, const float* beta,
                                        const float* state_in, float* o, float* state_out,
                                        void* stream) {
+  TraceRange trace_range("kda_chunk_prefill_noalloc");
   if (B < 0 || T < 0) return fail(KDA_ERR_SHAPE, "negative size (B=%d T=%d)", B, T);
   kda_status_t s = check_prefill(B, int64_t(B) * T, H, DK, DV, chunk, in_dtype, q, k, v, alpha,
                                  beta, state_in, o, state_out, false);
@@ -260,6 +273,7 @@ kda_status_t kda_chunk_prefill_scalar_gate(int B, int T, int H, int DK, int DV, 
                                            const float* state_in, float* o, float* state_out,
                                            void* workspace, size_t workspace_bytes,
                                            void* stream) {
+  TraceRange trace_range("kda_chunk_prefill_scalar_gate");
   return prefill_fixed(B, T, H, DK, DV, chunk, in_dtype, q, k, v, gate, beta, state_in, o,
                        state_out, workspace, workspace_bytes, stream, true);
 }
@@ -270,6 +284,7 @@ kda_status_t kda_chunk_prefill_snapshots(int B, int T, int H, int DK, int DV, in
                                          const float* state_in, float* o, float* state_out,
                                          int every, float* snapshots, void* workspace,
                                          size_t workspace_bytes, void* stream) {
+  TraceRange trace_range("kda_chunk_prefill_snapshots");
   if (B < 0 || T < 0) return fail(KDA_ERR_SHAPE, "negative size (B=%d T=%d)", B, T);
   if (every < 1) return fail(KDA_ERR_SHAPE, "every=%d: must be >= 1", every);
   kda_status_t s = check_prefill(B, int64_t(B) * T, H, DK, DV, chunk, in_dtype, q, k, v, alpha,
@@ -339,6 +354,7 @@ kda_status_t kda_chunk_prefill_varlen(int N, int T_total, const int32_t* cu_seql
                                       const float* alpha, const float* beta,
                                       const float* state_in, float* o, float* state_out,
                                       void* workspace, size_t workspace_bytes, void* stream) {
+  TraceRange trace_range("kda_chunk_prefill_varlen");
   return prefill_varlen(N, T_total, cu_seqlens, H, DK, DV, chunk, in_dtype, q, k, v, alpha, beta,
                         state_in, o, state_out, workspace, workspace_bytes, stream, false);
 }
@@ -352,6 +368,7 @@ kda_status_t kda_chunk_prefill_varlen_snapshots(int N, int T_total, const int32_
                                                 const int32_t* snap_offsets, int num_snapshots,
                                                 float* snapshots, void* workspace,
                                                 size_t workspace_bytes, void* stream) {
+  TraceRange trace_range("kda_chunk_prefill_varlen_snapshots");
   if (N < 0 || T_total < 0) return fail(KDA_ERR_SHAPE, "negative size (N=%d T_total=%d)", N, T_total);
   if (every < 1) return fail(KDA_ERR_SHAPE, "every=%d: must be >= 1", every);
   if (num_snapshots < 0) return fail(KDA_ERR_SHAPE, "num_snapshots=%d is negative", num_snapshots);
@@ -400,6 +417,7 @@ kda_status_t kda_chunk_prefill_varlen_scalar_gate(int N, int T_total, const int3
                                                   const float* beta, const float* state_in,
                                                   float* o, float* state_out, void* workspace,
                                                   size_t workspace_bytes, void* stream) {
+  TraceRange trace_range("kda_chunk_prefill_varlen_scalar_gate");
   return prefill_varlen(N, T_total, cu_seqlens, H, DK, DV, chunk, in_dtype, q, k, v, gate, beta,
                         state_in, o, state_out, workspace, workspace_bytes, stream, true);
 }
@@ -448,6 +466,7 @@ static kda_status_t decode_step(int N, int H, int DK, int DV, kda_dtype_t in_dty
 kda_status_t kda_decode_step(int N, int H, int DK, int DV, kda_dtype_t in_dtype, const void* q,
                              const void* k, const void* v, const float* alpha,
                              const float* beta, float* state, float* o, void* stream) {
+  TraceRange trace_range("kda_decode_step");
   return decode_step(N, H, DK, DV, in_dtype, q, k, v, alpha, beta, state, o, stream, false);
 }
 
@@ -455,6 +474,7 @@ kda_status_t kda_decode_step_scalar_gate(int N, int H, int DK, int DV, kda_dtype
                                          const void* q, const void* k, const void* v,
                                          const float* gate, const float* beta, float* state,
                                          float* o, void* stream) {
+  TraceRange trace_range("kda_decode_step_scalar_gate");
   return decode_step(N, H, DK, DV, in_dtype, q, k, v, gate, beta, state, o, stream, true);
 }
 
@@ -463,6 +483,7 @@ kda_status_t kda_decode_pool(int N, int L, int H, int DK, int DV, kda_dtype_t in
                              const float* beta, const int32_t* state_idx,
                              const int32_t* num_tokens, float* state_pool, int pool_size,
                              float* o, float* token_states, void* stream) {
+  TraceRange trace_range("kda_decode_pool");
   if (N < 0 || H < 0 || pool_size < 0)
     return fail(KDA_ERR_SHAPE, "negative size (N=%d H=%d pool_size=%d)", N, H, pool_size);
   if (L < 1 || L > 64) return fail(KDA_ERR_UNSUPPORTED, "L=%d: 1 <= L <= 64 tokens per sequence", L);
@@ -698,6 +719,7 @@ kda_status_t kda_chunk_backward(int B, int T, int H, int DK, int DV, int chunk,
                                 const float* d_state_out, float* dq, float* dk, float* dv,
                                 float* dalpha, float* dbeta, float* d_state_in, void* workspace,
                                 size_t workspace_bytes, void* stream) {
+  TraceRange trace_range("kda_chunk_backward");
   if (B < 0 || T < 0 || H < 0) return fail(KDA_ERR_SHAPE, "negative size (B=%d T=%d H=%d)", B, T, H);
   return run_backward(B, T, nullptr, int64_t(B) * T, chunks_of(T), H, DK, DV, chunk, in_dtype, q, k, v, alpha,
                       beta, state_in, d_o, d_state_out, dq, dk, dv, dalpha, dbeta, d_state_in,
@@ -712,6 +734,7 @@ kda_status_t kda_chunk_backward_scalar_gate(int B, int T, int H, int DK, int DV,
                                             float* dv, float* dgate, float* dbeta,
                                             float* d_state_in, void* workspace,
                                             size_t workspace_bytes, void* stream) {
+  TraceRange trace_range("kda_chunk_backward_scalar_gate");
   if (B < 0 || T < 0 || H < 0) return fail(KDA_ERR_SHAPE, "negative size (B=%d T=%d H=%d)", B, T, H);
   return run_backward(B, T, nullptr, int64_t(B) * T, chunks_of(T), H, DK, DV, chunk, in_dtype, q, k, v, gate,
                       beta, state_in, d_o, d_state_out, dq, dk, dv, dgate, dbeta, d_state_in,
@@ -734,6 +757,7 @@ kda_status_t kda_chunk_backward_varlen(int N, int T_total, const int32_t* cu_seq
                                        const float* d_state_out, float* dq, float* dk, float* dv,
                                        float* dalpha, float* dbeta, float* d_state_in,
                                        void* workspace, size_t workspace_bytes, void* stream) {
+  TraceRange trace_range("kda_chunk_backward_varlen");
   if (N < 0 || T_total < 0 || H < 0)
     return fail(KDA_ERR_SHAPE, "negative size (N=%d T_total=%d H=%d)", N, T_total, H);
   if (N > 0 && cu_seqlens == nullptr) return fail(KDA_ERR_NULL, "cu_seqlens must be non-NULL");
@@ -751,6 +775,7 @@ kda_status_t kda_chunk_backward_varlen_scalar_gate(
     const float* gate, const float* beta, const float* state_in, const float* d_o,
     const float* d_state_out, float* dq, float* dk, float* dv, float* dgate, float* dbeta,
     float* d_state_in, void* workspace, size_t workspace_bytes, void* stream) {
+  TraceRange trace_range("kda_chunk_backward_varlen_scalar_gate");
   if (N < 0 || T_total < 0 || H < 0)
     return fail(KDA_ERR_SHAPE, "negative size (N=%d T_total=%d H=%d)", N, T_total, H);
   if (N > 0 && cu_seqlens == nullptr) return fail(KDA_ERR_NULL, "cu_seqlens must be non-NULL");
