@@ -11,19 +11,20 @@
 // so every state element is read once and written once: the step is bound by
 // HBM bandwidth (64 KiB read + 64 KiB written per (sequence, head) at d=128).
 //
-// The reductions run over the key rows, so the value columns split freely: one
-// workgroup of 256 threads per (sequence, head, 64 value columns).  Small
-// workgroups (32 KiB of state at d=128) keep the tail of the grid short and
-// the register count low enough for 8 workgroups per compute unit.  Thread t
-// owns columns 4*(t % CG) .. +3 of the workgroup's 64 (CG = 16 column groups,
-// 16-byte accesses) and key rows r = t / CG + RG*m (RG = 16 row groups), so
-// each wave reads four 256-byte row segments per instruction.  The two column
-// reductions go through LDS; the update is applied in registers and written
-// back in place.  The state is read and written with non-temporal accesses:
-// each line is touched once per step, and streaming it past the caches
-// (rather than letting 32 KiB per workgroup of read lines sit in L2 until
-// their write-back) measured about 8% faster for this read-all-then-write-all
-// pattern at 32 KiB per workgroup.  The
+// The reductions run over the key rows, so the value columns could split
+// freely, but they do not: one workgroup of 256 threads owns the whole state
+// of a (sequence, head), 64 KiB at d=128, i.e. whole 512-byte rows.  Thread t
+// owns columns 4*(t % CG) .. +3 (CG = DV/4 column groups, 16-byte accesses)
+// and key rows r = t / CG + RG*m (RG = 256/CG row groups), so a wave reads two
+// whole rows per instruction and a workgroup streams one contiguous 64 KiB
+// block.  The two column reductions go through LDS; the update is applied in
+// registers and written back in place with non-temporal accesses both ways.
+// Measured on a 256 x 32 step at d=128 that follows an 8192-token, 32-head
+// prefill: whole rows cut the pair from 650 to 643 us against
+// half rows (64 columns, two workgroups per state).  Ordinary loads make the
+// decode alone faster when it runs back to back (159 against 191 us), but
+// they leave the caches full of state lines that the following prefill must
+// write back first, so the pair gets slower (667 us).  The
 // state of sequence n is slot state_idx[n] of a pool (slot n without an
 // index); a slot outside the pool, or a token count of 0, marks a padding row
 // whose output is zero.
@@ -45,6 +46,7 @@ __device__ __forceinline__ float4 ld_nt(const float4* p) {
   const f4v v = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(p));
   return make_float4(v.x, v.y, v.z, v.w);
 }
+
 
 __device__ __forceinline__ void st_nt(float4* p, float4 x) {
   const f4v v = {x.x, x.y, x.z, x.w};
@@ -317,10 +319,10 @@ __global__ __launch_bounds__(kThreads) void kda_decode_pool_kernel(PoolDecodeArg
 
 // One token per sequence without per-token states: the single-step kernel;
 // otherwise the multi-token kernel.
-// Value columns per workgroup: 64 for the single step (short grid tail, low
-// register count); the whole row for several tokens (the per-token barriers
-// and small-vector loads are paid once per (sequence, head)).
-constexpr int kStepVC = 64;
+// Value columns per workgroup: the whole row, for the single step (contiguous
+// 64 KiB per workgroup streams best) and for several tokens (the per-token
+// barriers and small-vector loads are paid once per (sequence, head)).
+constexpr int kStepVC = 128;
 
 template <int DK, int DV>
 void launch_pool_t(const PoolDecodeArgs& a, hipStream_t st) {

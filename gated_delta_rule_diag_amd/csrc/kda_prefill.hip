@@ -649,7 +649,9 @@ __device__ __forceinline__ void prep_chunk(char* smem, const float4 (&av)[4], co
     }
     // Per-channel decay vectors, one set of threads each (chains of products,
     // every one of them a product over consecutive tokens, so none leaves the
-    // range of what it stands for).
+    // range of what it stands for).  The sets are the first row group of
+    // waves 0-3, so that no wave runs two of the chains one after the other.
+    constexpr int GPW = 256 / DK;   // row groups per wave
     if (grp == 0) {
       // gamma_mR = gamma at row 16R + 7; gamma_n at row 63
       float4 x = gprod(0, 1);
@@ -660,7 +662,7 @@ __device__ __forceinline__ void prep_chunk(char* smem, const float4 (&av)[4], co
         st4v(sGM + RR * DK, x);
       }
       st4v(sGN, mul4(x, gprod(14, 15)));
-    } else if (grp == 1) {
+    } else if (grp == GPW) {
       // gamma_n / gamma_mI = product over rows 16I + 8 .. 63
       float4 x = gprod(14, 15);
       st4v(sGNM + 3 * DK, x);
@@ -669,14 +671,14 @@ __device__ __forceinline__ void prep_chunk(char* smem, const float4 (&av)[4], co
         x = mul4(x, gprod(4 * II + 2, 4 * II + 5));
         st4v(sGNM + II * DK, x);
       }
-    } else if (grp == 2) {
+    } else if (grp == 2 * GPW) {
       // S1_I: rows 16I + 8 .. 16I + 15;  E_(I+1),I: rows 16I + 16 .. 16I + 23
 #pragma unroll
       for (int II = 0; II < 3; ++II) {
         st4v(sS1 + II * DK, gprod(4 * II + 2, 4 * II + 3));
         st4v(sE + eidx(II + 1, II) * DK, gprod(4 * II + 4, 4 * II + 5));
       }
-    } else if (grp == 3) {
+    } else if (grp == 3 * GPW) {
       // E_RI for R >= I + 2: rows 16I + 16 .. 16R + 7
       const float4 x10 = gprod(4, 5), x21 = gprod(8, 9), x32 = gprod(12, 13);
       const float4 m1 = gprod(6, 7), m2 = gprod(10, 11);
@@ -1335,11 +1337,21 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_stage_kernel(StageParam
   float pb = 0.f;
   // V of item `it`: loaded after steps 1-3 (it is first needed by the folded
   // products; keeping it in registers through steps 1-3 would spill).
+  // Item it = (chunk c_begin + it / pairs, pair it % pairs); items < 2^31 (the
+  // host checks), so the index arithmetic is 32-bit.
+  const uint32_t npairs = uint32_t(p.pairs), uH = uint32_t(H);
+  auto item_of = [&](int64_t it, int64_t& c, int& h, int64_t& n) {
+    const uint32_t cr = uint32_t(it) / npairs;
+    const uint32_t pr = uint32_t(it) - cr * npairs;
+    const uint32_t nn = pr / uH;
+    c = p.c_begin + cr;
+    h = int(pr - nn * uH);
+    n = nn;
+  };
   auto load_v = [&](int64_t it) {
-    const int64_t c = p.c_begin + it / p.pairs;
-    const int64_t pr = it - (it / p.pairs) * p.pairs;
-    const int h = int(pr % H);
-    const int64_t n = pr / H;
+    int64_t c, n;
+    int h;
+    item_of(it, c, h, n);
     const int64_t tok0 = n * p.T_fixed + c * kC;
     const int64_t rem = p.T_fixed - c * kC;
     const int nvv = int(rem < kC ? rem : kC);
@@ -1355,10 +1367,9 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_stage_kernel(StageParam
     }
   };
   auto load_item = [&](int64_t it) {
-    const int64_t c = p.c_begin + it / p.pairs;
-    const int64_t pr = it - (it / p.pairs) * p.pairs;
-    const int h = int(pr % H);
-    const int64_t n = pr / H;
+    int64_t c, n;
+    int h;
+    item_of(it, c, h, n);
     const int64_t tok0 = n * p.T_fixed + c * kC;
     const int64_t rem = p.T_fixed - c * kC;
     const int nvv = int(rem < kC ? rem : kC);
@@ -1397,7 +1408,7 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_stage_kernel(StageParam
     mirror_stores<(2 * NQ + NK + NP) * SPF + 1 + NBU>();
   }
   for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
-    const int64_t c = p.c_begin + it / p.pairs;
+    const int64_t c = p.c_begin + uint32_t(it) / npairs;
     const int64_t rem = p.T_fixed - c * kC;
     const int nv = int(rem < kC ? rem : kC);
 
@@ -1947,6 +1958,10 @@ int launch_prefill(const PrefillArgs& a, void* stream, const char** msg) {
   if (use_staged(varlen, pairs, nchunks)) {
     const int nsub = staged_nsub(pairs, a.DV);
     const int64_t seg = seg_chunks(pairs, nchunks, a.DK, a.DV, a.seg_budget);
+    if (pairs * seg >= (int64_t(1) << 31)) {   // the stage kernel indexes items in 32 bits
+      *msg = "staged prefill: more than 2^31 items in one segment";
+      return 1;
+    }
     char* ws = static_cast<char*>(a.workspace);
     float* state_ws = seg < nchunks
         ? reinterpret_cast<float*>(ws + size_t(pairs) * size_t(seg) * slot_bytes(a.DK, a.DV))
