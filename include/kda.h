@@ -59,7 +59,16 @@ typedef enum {
   KDA_ERR_HIP = 7          /* a HIP launch failed                                 */
 } kda_status_t;
 
-typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype_t; /* dtype of q, k, v only */
+/* dtype of q, k, v only.  The two range markers are not dtypes: they make
+ * every int a value of the type, so a caller may pass any int and an unknown
+ * one is rejected with KDA_ERR_DTYPE (rather than being out of the enum's
+ * range, which C++ does not define). */
+typedef enum {
+  KDA_F32 = 0,
+  KDA_BF16 = 1,
+  KDA_DTYPE_RANGE_MIN_ = -2147483647 - 1,
+  KDA_DTYPE_RANGE_MAX_ = 2147483647
+} kda_dtype_t;
 
 /* Version of this ABI: (major << 16) | minor. */
 int kda_abi_version(void);

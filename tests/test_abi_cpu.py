@@ -10,7 +10,9 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-LIB = os.path.join(ROOT, "gated_delta_rule_diag_amd", "libkda.so")
+# KDA_ABI_LIB: another build of the same sources (the sanitizer build runs
+# this file against its own library).
+LIB = os.environ.get("KDA_ABI_LIB") or os.path.join(ROOT, "gated_delta_rule_diag_amd", "libkda.so")
 HEADER = os.path.join(ROOT, "include", "kda.h")
 
 pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libkda.so not built")
