@@ -200,30 +200,13 @@ __device__ __forceinline__ void split(float x, uint16_t& h, uint16_t& l) {
 
 // c + A B for 16x16 blocks: lane (lr, lg) holds a[j] = A[lr][4lg + j] and
 // b[j] = B[4lg + j][lr]; the result lane holds rows 4lg + q of column lr.
-// bf16 inputs: split operands on the 16x16x16 bf16 MFMA (three products);
-// fp32 inputs: four 16x16x4 fp32 MFMAs.
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-template <bool BF>
+// Four 16x16x4 fp32 MFMAs for either input dtype: the operands are fp32
+// values in registers (the triangular solve's blocks), and splitting them into
+// bf16 parts for the bf16 MFMA costs more VALU time on the solve's dependent
+// chain than the fp32 MFMA's extra passes.
 __device__ __forceinline__ f4 mm16x16(const f4& a, const f4& b, f4 c) {
-  if constexpr (BF) {
-    s16x4 ah, al, bh, bl;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint16_t h, l;
-      split(a[j], h, l);
-      ah[j] = short(h);
-      al[j] = short(l);
-      split(b[j], h, l);
-      bh[j] = short(h);
-      bl[j] = short(l);
-    }
-    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, bh, c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bl, c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bh, c, 0, 0, 0);
-  } else {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], c, 0, 0, 0);
-  }
+  for (int j = 0; j < 4; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], c, 0, 0, 0);
   return c;
 }
 
@@ -797,13 +780,13 @@ __device__ __forceinline__ void prep_chunk(char* smem, const float4 (&av)[4], co
       Xo[q] = (4 * lg + q == lr ? 1.f : 0.f) - No[q];
     }
     const f4 zero = f4{0.f, 0.f, 0.f, 0.f};
-    f4 Po = mm16x16<BF>(Nt, No, zero), Pt = mm16x16<BF>(No, Nt, zero);   // N^2
+    f4 Po = mm16x16(Nt, No, zero), Pt = mm16x16(No, Nt, zero);   // N^2
 #pragma unroll
     for (int e = 0; e < 3; ++e) {
       // X <- X + P X with P = N^(2^(e+1)); then P <- P P
-      Xo = mm16x16<BF>(Pt, Xo, Xo);
+      Xo = mm16x16(Pt, Xo, Xo);
       if (e < 2) {
-        const f4 Po2 = mm16x16<BF>(Pt, Po, zero), Pt2 = mm16x16<BF>(Po, Pt, zero);
+        const f4 Po2 = mm16x16(Pt, Po, zero), Pt2 = mm16x16(Po, Pt, zero);
         Po = Po2;
         Pt = Pt2;
       }
@@ -864,10 +847,10 @@ __device__ __forceinline__ void prep_chunk(char* smem, const float4 (&av)[4], co
         const float* bb = sLi + (16 * J + 4 * lg) * L::P_AF + 16 * I + lr;
         const f4 a = f4{a4.x, a4.y, a4.z, a4.w};
         const f4 b = f4{bb[0], bb[L::P_AF], bb[2 * L::P_AF], bb[3 * L::P_AF]};
-        y = mm16x16<BF>(a, b, y);
+        y = mm16x16(a, b, y);
       }
       const float4 d4 = *reinterpret_cast<const float4*>(sLi + (16 * R + lr) * L::P_AF + 16 * R + 4 * lg);
-      const f4 x = mm16x16<BF>(f4{d4.x, d4.y, d4.z, d4.w}, y, f4{0.f, 0.f, 0.f, 0.f});
+      const f4 x = mm16x16(f4{d4.x, d4.y, d4.z, d4.w}, y, f4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
       for (int q = 0; q < 4; ++q) sLi[(16 * R + 4 * lg + q) * L::P_AF + 16 * I + lr] = -x[q];
     }
