@@ -532,8 +532,7 @@ def main():
 
     # Which prefill form the library takes for this shape (the same rule as in
     # the library: the staged two-kernel form below 128 (sequence, head) pairs).
-    forced = os.environ.get("KDA_PREFILL_PATH")
-    staged = forced == "split" or (forced != "fused" and B * H < 128 and T > 64)
+    staged = B * H < 128 and T > 64
     pre_kernels = ("kda_stage_kernel + kda_chain_kernel (staged form: one pair of launches per "
                    "segment of chunks)"
                    if staged else "kda_prefill_kernel")
