@@ -369,9 +369,13 @@ __device__ __forceinline__ void gsum(f4 (&acc)[(4 * (DK / 16) + kNW - 1) / kNW],
         for (int j = 0; j < 4; ++j) bs[j] = (bs[j] * s1) * s2;
       }
       f4 av;
+      if constexpr (COLS) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        av[j] = COLS ? a[(16 * u + 4 * g + j) * lda + 16 * ro + i] : a[(16 * ro + i) * lda + 16 * u + 4 * g + j];
+        for (int j = 0; j < 4; ++j) av[j] = a[(16 * u + 4 * g + j) * lda + 16 * ro + i];
+      } else {
+        // one 16-byte read: four scalar reads of this pattern conflict 4 ways
+        av = *reinterpret_cast<const f4*>(a + (16 * ro + i) * lda + 16 * u + 4 * g);
+      }
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[s] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j], bs[j], acc[s], 0, 0, 0);
     }
