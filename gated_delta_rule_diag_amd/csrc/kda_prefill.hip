@@ -885,6 +885,9 @@ __device__ __forceinline__ void store_snapshot(float* snap, int64_t row, int h, 
 }
 
 // NOO: states and snapshots only (no output products; o is not written).
+// Packed batches of up to this many sequences are taken longest first.
+constexpr int kRankedSeqs = 256;
+
 template <int DK, int NSUB, bool BF, bool SNAP, bool NOO>
 __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_prefill_kernel(Params p) {
   using L = Lay<DK>;
@@ -921,7 +924,29 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_prefill_kernel(Params p
   const int slab = int(b % p.nslab);
   const int64_t pr = b / p.nslab;
   const int h = int(pr % p.H);
-  const int n = int(pr / p.H);
+  int n = int(pr / p.H);
+  // Packed sequences: the workgroups take the sequences longest first (the
+  // n-th workgroup row gets the sequence of rank n by length, ties in pack
+  // order), so that the longest chains start first and the short ones fill in
+  // behind them, whatever the order of the pack.  The ranks are counted from
+  // cu_seqlens staged in LDS (before the LDS takes anything else), up to
+  // kRankedSeqs sequences; past that the pack order stands.
+  if (p.cu != nullptr && p.N <= kRankedSeqs) {
+    int* const sLen = reinterpret_cast<int*>(smem);
+    int* const sPick = sLen + kRankedSeqs;
+    for (int i = t; i < p.N; i += L::NT) sLen[i] = p.cu[i + 1] - p.cu[i];
+    if (t == 0) *sPick = n;
+    __syncthreads();
+    for (int i = t; i < p.N; i += L::NT) {
+      const int li = sLen[i];
+      int rank = 0;
+      for (int j = 0; j < p.N; ++j) rank += (sLen[j] > li || (sLen[j] == li && j < i)) ? 1 : 0;
+      if (rank == n) *sPick = i;
+    }
+    __syncthreads();
+    n = *sPick;
+    __syncthreads();
+  }
   const int H = p.H, DV = p.DV;
   const int col0 = slab * VS;
 
