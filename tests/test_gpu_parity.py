@@ -114,6 +114,26 @@ def test_varlen_small():
     assert eo <= TOL["bf16"] and es <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("N", [256, 257])
+def test_varlen_many_sequences_ranked_and_unranked(N):
+    """Packed batches of up to 256 sequences are taken longest first (each
+    workgroup ranks the lengths on the device), larger ones in pack order:
+    both sides of the limit, with many equal lengths and empty sequences,
+    against the oracle."""
+    lengths = np.random.default_rng(N).integers(0, 100, N)
+    H, d = 1, 64
+    flush(f"[varlen] N={N} sequences, {int(lengths.sum())} tokens, {int((lengths == 0).sum())} empty")
+    q, k, v, a, b, cu = I.packed_inputs(510, lengths, H, d, d, "f32")
+    S0 = random_state(np.random.default_rng(511), (N, H, d, d))
+    o_ref, S_ref = kda_recurrent_varlen(q, k, v, a, b, cu, S0)
+    o, S = kda.chunk_prefill_varlen(dev(q), dev(k), dev(v), dev(a), dev(b), torch.from_numpy(cu).cuda(),
+                                    dev(S0))
+    torch.cuda.synchronize()
+    eo, es = max_rel_err(host(o), o_ref), max_rel_err(host(S), S_ref)
+    flush(f"    err o={eo:.2e} S={es:.2e}")
+    assert eo <= TOL["f32"] and es <= TOL["f32"]
+
+
 @pytest.mark.parametrize("N,H,DK,DV,dt", [(3, 2, 64, 64, "f32"), (5, 3, 128, 128, "bf16"),
                                           (2, 4, 128, 64, "bf16"), (2, 2, 64, 128, "f32")])
 def test_decode_small(N, H, DK, DV, dt):
