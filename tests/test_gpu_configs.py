@@ -170,7 +170,9 @@ def test_backward_varlen_n64_h32_sequence_head_subset():
     """The backward pass of the 64-sequence packed workload (576,952 tokens,
     H=32, d=128, bf16; the reverse pass in windows of chunks): every gradient
     of the three shortest sequences on heads {0, 31} against the oracle's
-    reverse mode (which keeps every token state, hence the short ones)."""
+    reverse mode (which keeps every token state, hence the short ones), and
+    the longest sequence (16,278 tokens: 37 windows of the reverse pass) on
+    head 0."""
     H, D = 32, 128
     lengths = I.varlen_lengths(3, 64, 512, 16384)
     Tt = int(lengths.sum())
@@ -182,9 +184,9 @@ def test_backward_varlen_n64_h32_sequence_head_subset():
     do = torch.randn((Tt, H, D), generator=gen, device="cuda")
     grads = kda.chunk_backward_varlen(q, k, v, a, b, cu_d, do, max_seqlen=int(lengths.max()))
     torch.cuda.synchronize()
-    heads = [0, 31]
     names = ("dq", "dk", "dv", "dalpha", "dbeta")
-    for n in np.argsort(lengths)[:3]:
+    cases = [(int(n), [0, 31]) for n in np.argsort(lengths)[:3]] + [(int(np.argmax(lengths)), [0])]
+    for n, heads in cases:
         s_, e_ = int(cu[n]), int(cu[n + 1])
         f = lambda t: t[s_:e_][:, heads].float().cpu().numpy()[None]  # noqa: E731
         ref = kda_backward(f(q), f(k), f(v), f(a), f(b), None, f(do), None)
@@ -199,8 +201,8 @@ def test_backward_varlen_n64_h32_sequence_head_subset():
 def test_long_context_1m_prefill_then_1024_decode_steps_head_subset():
     """B=1, H=32, d=128, T=1,048,576 bf16 prefill, then 1024 recurrent decode
     steps from the resulting state.  Heads {0, 31}: the final prefill state,
-    the outputs of the last 4096 prefill tokens and of all decode steps are
-    checked against the oracle run over the whole sequence."""
+    the outputs of every prefill token and of all decode steps are checked
+    against the oracle run over the whole sequence."""
     T, H, D, ND = 1 << 20, 32, 128, 1024
     flush("[config] long context: prefill T=1048576 H=32 d=128 bf16 + 1024 decode steps")
     dt = torch.bfloat16
@@ -245,7 +247,7 @@ def test_long_context_1m_prefill_then_1024_decode_steps_head_subset():
     od_ref, Sd_ref = kda_recurrent(d[0], d[1], d[2], d[3], d[4], S_ref)
     gS = host(S)[0, heads]
     e_state = max_rel_err(gS, Sd_ref[0])
-    e_tail = max_rel_err(o[0, -4096:][:, heads].cpu().numpy(), o_ref[0, -4096:])
+    e_pre = max_rel_err(o[0][:, heads].cpu().numpy(), o_ref[0])
     e_dec = max_rel_err(np.stack([x[0, heads].cpu().numpy() for x in od]), od_ref[0])
-    flush(f"    heads {heads}: prefill tail o={e_tail:.2e} decode o={e_dec:.2e} final S={e_state:.2e}")
-    assert e_tail <= TOL["bf16"] and e_dec <= TOL["bf16"] and e_state <= TOL["bf16"]
+    flush(f"    heads {heads}: prefill o (all {T} tokens)={e_pre:.2e} decode o={e_dec:.2e} final S={e_state:.2e}")
+    assert e_pre <= TOL["bf16"] and e_dec <= TOL["bf16"] and e_state <= TOL["bf16"]

@@ -39,10 +39,10 @@ def needle_inputs(T, p, H, D, c):
     return q, k, v, a, b
 
 
-@pytest.mark.parametrize("T,p", [(4096, 3), (65536, 37), (262144, 131071)])
-def test_needle_retrieval_long_context(T, p):
-    H, D = 4, 128
-    flush(f"[needle] T={T} p={p}")
+@pytest.mark.parametrize("T,p,H", [(4096, 3, 4), (65536, 37, 4), (262144, 131071, 4), (1048576, 700001, 2)])
+def test_needle_retrieval_long_context(T, p, H):
+    D = 128
+    flush(f"[needle] T={T} p={p} H={H}")
     q, k, v, a, b = needle_inputs(T, p, H, D, 700 + p % 7)
     o, S = kda.chunk_prefill(dev(q, bf), dev(k, bf), dev(v, bf), dev(a), dev(b))
     torch.cuda.synchronize()
