@@ -288,7 +288,10 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    # 30 untimed steps (about 20 ms of sustained work): with 3 the first timed
+    # steps still ran at the GPU's ramp-up clocks (prefill 485 us against 457 us
+    # from 30 warm-up steps on, the same with 100)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true",
