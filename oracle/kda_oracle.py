@@ -25,7 +25,7 @@ Sources (web pages; cited by title and section):
   the current token (so alpha is given per token), and the chunkwise algorithm
   uses a diagonal-plus-low-rank transition.
 
-Readings taken where the pages are silent (each one is listed in the design doc):
+Readings taken where the pages are silent:
 
 * State orientation: S is d_k x d_v, row i = key channel, column j = value
   channel.  The explainer writes S|k> (a d_v x d_k map); S here is its
