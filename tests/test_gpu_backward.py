@@ -72,7 +72,7 @@ def test_backward_is_deterministic():
 
 
 def test_backward_b1_h32_t8192_head_subset():
-    """The benchmark prefill shape; heads {0, 31} against the oracle."""
+    """The B=1, H=32, T=8192, d=128 bf16 prefill shape; heads {0, 31} against the oracle."""
     flush("[backward] B=1 T=8192 H=32 d=128 bf16, heads 0 and 31")
     errs = run_case(1, 8192, 32, 128, 128, "bf16", 730, with_state=False, heads=[0, 31])
     assert max(errs.values()) <= TOL["bf16"], errs

@@ -1,4 +1,4 @@
-"""GPU parity at the benchmark workloads' full sizes, in the launch
+"""GPU parity at the five workloads' full sizes, in the launch
 configuration bench.py times.  Where the oracle cannot run every (sequence,
 head) in seconds, a seeded subset of heads is checked element by element."""
 

@@ -91,7 +91,7 @@ def test_prefill_split_segments(seg, dt, monkeypatch):
 
 @pytest.mark.parametrize("path", PATHS)
 def test_prefill_paths_agree_on_config_shape(path, monkeypatch):
-    """B=1, H=32, T=1000, d=128, bf16 (the benchmark's head count): both forms
+    """B=1, H=32, T=1000, d=128, bf16 (32 heads, as in the 8192-token workload): both forms
     against the oracle."""
     kda.set_tuning(prefill_form=path)
     eo, es = prefill_case(1, 1000, 32, 128, 128, "bf16", c=420, with_state=True)

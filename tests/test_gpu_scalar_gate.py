@@ -87,7 +87,7 @@ def test_scalar_gate_decode_matches_oracle(dt, dk, dv):
 
 @pytest.mark.parametrize("path", PATHS)
 def test_scalar_gate_prefill_b1_h32_t8192_head_subset(path, monkeypatch):
-    """The benchmark prefill shape (B=1, H=32, T=8192, d=128, bf16) with a
+    """The B=1, H=32, T=8192, d=128 bf16 prefill shape with a
     scalar gate; heads {0, 31} against the oracle."""
     kda.set_tuning(prefill_form=path)
     B, T, H, D = 1, 8192, 32, 128

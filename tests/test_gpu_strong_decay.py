@@ -10,7 +10,7 @@ alpha = 1e-4.  Three alpha distributions, on every path (fused and staged
 prefill, snapshots, packed sequences, scalar gate, decode, backward):
   uniform  alpha ~ U[1e-4, 0.07] on every channel
   edge     alpha = 1e-4 on every channel
-  mixed    the benchmark distribution exp(-exp(U(-5,-1))) with 8 channels per
+  mixed    the default input distribution exp(-exp(U(-5,-1))) with 8 channels per
            head drawn log-uniformly from [5e-4, 2e-3] (fast-forget channels)
 """
 
