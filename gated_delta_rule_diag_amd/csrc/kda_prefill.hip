@@ -1519,6 +1519,504 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_stage_kernel(StageParam
   }
 }
 
+// ------------------------------------------------ stage kernel, d = 128 ----
+// The slots of kda_stage_kernel for d_k = d_v = 128 with bf16 inputs, from a
+// workgroup of eight waves in 79.6 KB of LDS and at most 128 VGPRs, one
+// workgroup per item: two workgroups share a compute unit, four waves per
+// SIMD, so one item's barriers and memory latency are covered by the other
+// item's work (measured: the B=1, H=32, T=8192 prefill in 415 us against
+// 451 us with the one-workgroup-per-CU kernel).  What makes it fit: the
+// decayed operands Kl, Ql and Kr go through the LDS one half of the key
+// channels at a time (the Gram tiles accumulate over the halves in
+// registers; Q_g and K_e^T are exported per half), and after the solve K_g
+// is rebuilt per half from the keys and decays the threads keep in
+// registers.  Without a loop over items (and so without a prefetch of the
+// next one) the compiler keeps nothing in registers across items, which
+// holds the register count under 128 without spills.
+//
+// Decay prep: thread t takes half ht = t / 256 of the key channels, its
+// channel quad cq = t % 16 and rows 4 g4 .. 4 g4 + 3, g4 = (t / 16) % 16; the
+// two threads of an 8-row group (rows 8G .. 8G + 7) are lanes l and l ^ 16
+// of one wave.  The reference row of block R, 16R + 7, is the last row of
+// group 2R, so every per-block vector is a product of whole 8-row groups.
+struct Lay2 {
+  static constexpr int NT = 512;
+  static constexpr int P_H = 64 * 4 + 16;   // rows of 64 elements (272 B)
+  static constexpr int P_AF = 68;           // fp32 pitch of A and L^-1 (floats)
+  static constexpr int ARR = 64 * P_H;      // one 64 x 64 array
+  static constexpr int OFF_O0 = 0;          // Kl_h; A; K_g_h / W staging / K_g^T / V^T
+  static constexpr int OFF_O1 = ARR;        // Ql_h; P; K_g^T / W staging / V^T
+  static constexpr int OFF_O2 = 2 * ARR;    // Kr_h; L^-1 then T
+  static constexpr int OFF_XS = 3 * ARR;    // K_e^T of a half
+  static constexpr int OFF_GM = 4 * ARR;    // gamma_mR [4][128]
+  static constexpr int OFF_GN = OFF_GM + 4 * 128 * 4;    // gamma_n [128]
+  static constexpr int OFF_GNM = OFF_GN + 128 * 4;       // gamma_n / gamma_mI [4][128]
+  static constexpr int OFF_S1 = OFF_GNM + 4 * 128 * 4;   // S1_I [4][128]
+  static constexpr int OFF_E = OFF_S1 + 4 * 128 * 4;     // E_RI [6][128]
+  static constexpr int OFF_BE = OFF_E + 6 * 128 * 4;     // beta [64]
+  static constexpr int OFF_GP = OFF_O0;                  // 8-row group products [8][128] (steps 1-2)
+  static constexpr int TOTAL = OFF_BE + 64 * 4;
+  static_assert(2 * TOTAL <= 160 * 1024, "two workgroups per compute unit");
+  static_assert(ARR == 64 * P_AF * 4, "A and L^-1 fill one array");
+};
+
+// acc += the Gram tiles of block pair (R, I) over one half of the key
+// channels (K = 64, two 32-channel fragments); the half's operands are
+// [64][64] arrays of pitch Lay2::P_H, and s1 / e point at the half's
+// channels of S1_I and E_RI.
+template <int R, int I, int XD>
+__device__ __forceinline__ void gram_group_half(const char* sKl, const char* sQl, const char* sKr,
+                                                const float* s1, const float* e, f4 (&acc)[3]) {
+  using M = Mma<true>;
+  constexpr int P = Lay2::P_H;
+#pragma unroll 1
+  for (int kc = 0; kc < 2; ++kc) {
+    auto c = M::load(sKr, P, 16 * I, kc);
+    if constexpr (I < R) c = rescale_frag(c, s1, e, kc);
+    const auto rk = M::load(sKl, P, 16 * R, kc);
+    const auto rq = M::load(sQl, P, 16 * R, kc);
+    acc[0] = M::mma(c, rk, acc[0]);
+    acc[1] = M::mma(c, rq, acc[1]);
+    if constexpr (XD >= 0) {
+      const auto cd = M::load(sKr, P, 16 * R, kc);
+      acc[2] = M::mma(cd, XD == 0 ? rk : rq, acc[2]);
+    }
+  }
+}
+
+// One fragment (16 rows, 32 K) of a [rows][64] split-bf16 LDS array (pitch
+// Lay2::P_H) to global memory in fragment order, each element times
+// cs[row block][k] when cs is given (row stride 128 floats).
+__device__ __forceinline__ void export_frag_half(char* dst, const char* src, int rb, int u, const float* cs) {
+  const int l = lane_id();
+  const int row = 16 * rb + (l & 15);
+  const char* s = src + row * Lay2::P_H + (u * 4 + (l >> 4)) * 32;
+  uint4 hi = *reinterpret_cast<const uint4*>(s);
+  uint4 lo = *reinterpret_cast<const uint4*>(s + 16);
+  if (cs != nullptr) {
+    const float* c = cs + rb * 128 + u * 32 + 8 * (l >> 4);
+    const uint32_t hw[4] = {hi.x, hi.y, hi.z, hi.w}, lw[4] = {lo.x, lo.y, lo.z, lo.w};
+    uint32_t nh[4], nl[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float x0 = (bf_lo16(hw[j]) + bf_lo16(lw[j])) * c[2 * j];
+      const float x1 = (bf_hi16(hw[j]) + bf_hi16(lw[j])) * c[2 * j + 1];
+      uint16_t h0, l0, h1, l1;
+      split(x0, h0, l0);
+      split(x1, h1, l1);
+      nh[j] = uint32_t(h0) | (uint32_t(h1) << 16);
+      nl[j] = uint32_t(l0) | (uint32_t(l1) << 16);
+    }
+    hi = make_uint4(nh[0], nh[1], nh[2], nh[3]);
+    lo = make_uint4(nl[0], nl[1], nl[2], nl[3]);
+  }
+  *reinterpret_cast<uint4*>(dst + 16 * l) = hi;
+  *reinterpret_cast<uint4*>(dst + 1024 + 16 * l) = lo;
+}
+
+// NOO: the call needs the states only (Q_g and P are not stored).
+template <bool NOO>
+__global__ __launch_bounds__(Lay2::NT, 4) void kda_stage2_kernel(StageParams p) {
+  using L = Lay2;
+  using M = Mma<true>;
+  using SL = Slot<128, 128>;
+  constexpr int DK = 128, DV = 128;
+  __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
+  char* const sO0 = smem + L::OFF_O0;
+  char* const sO1 = smem + L::OFF_O1;
+  char* const sO2 = smem + L::OFF_O2;
+  char* const sXS = smem + L::OFF_XS;
+  float* const sGP = reinterpret_cast<float*>(smem + L::OFF_GP);
+  float* const sGM = reinterpret_cast<float*>(smem + L::OFF_GM);
+  float* const sGN = reinterpret_cast<float*>(smem + L::OFF_GN);
+  float* const sGNM = reinterpret_cast<float*>(smem + L::OFF_GNM);
+  float* const sS1 = reinterpret_cast<float*>(smem + L::OFF_S1);
+  float* const sE = reinterpret_cast<float*>(smem + L::OFF_E);
+  float* const sBe = reinterpret_cast<float*>(smem + L::OFF_BE);
+  float* const sA = reinterpret_cast<float*>(sO0);
+  char* const sP = sO1;
+  char* const sT = sO2;
+  float* const sLi = reinterpret_cast<float*>(sO2);
+
+  const int t = threadIdx.x;
+  const int l = t & 63;
+  const int w = t >> 6;
+  const int lr = l & 15, lg = l >> 4;
+  // decay prep: half ht of the key channels (waves 4ht .. 4ht + 3), channel
+  // quad cq of the half, rows 4 g4 .. 4 g4 + 3
+  const int ht = t >> 8, cq = t & 15, g4 = (t >> 4) & 15;
+  const int r0 = 4 * g4;
+  const int pos = g4 & 3;   // place of the thread's 4 rows in their 16-row block
+  const int wr = w & 3;     // row block of T for the folded products
+  const int H = p.H;
+  const int64_t items = p.nseg * p.pairs;
+  const uint32_t npairs = uint32_t(p.pairs), uH = uint32_t(H);
+  auto mul4 = [](float4 a, float4 b) { return make_float4(a.x * b.x, a.y * b.y, a.z * b.z, a.w * b.w); };
+  const float4 one4 = make_float4(1.f, 1.f, 1.f, 1.f);
+  auto rcp4 = [](float4 a) { return make_float4(rcp(a.x), rcp(a.y), rcp(a.z), rcp(a.w)); };
+  auto shfl4 = [](float4 a) {
+    return make_float4(__shfl_xor(a.x, 16), __shfl_xor(a.y, 16), __shfl_xor(a.z, 16), __shfl_xor(a.w, 16));
+  };
+
+  {
+    const int64_t it = blockIdx.x;
+    if (it >= items) return;
+    const uint32_t crel = uint32_t(it) / npairs;
+    const uint32_t pr = uint32_t(it) - crel * npairs;
+    const uint32_t nn = pr / uH;
+    const int h = int(pr - nn * uH);
+    const int64_t c = p.c_begin + crel;
+    const int64_t tok0 = int64_t(nn) * p.T_fixed + c * kC;
+    const int64_t rem = p.T_fixed - c * kC;
+    const int nv = int(rem < kC ? rem : kC);
+    const int64_t row0 = tok0 * H + h;
+    const int rsk = H * DK, rsv = H * DV;
+    char* const slot = p.ws + it * int64_t(SL::BYTES);
+
+    // ---- inputs (rows past the end: alpha = 1, k = q = 0) -----------------
+    const bool sg = p.alpha_scalar != 0;
+    const float* ab = p.alpha + (sg ? row0 : row0 * DK);
+    const char* kb = static_cast<const char*>(p.k) + row0 * DK * 2;
+    const char* qb = static_cast<const char*>(p.q) + row0 * DK * 2;
+    uint2 kraw[4], qraw[4];
+    float4 av[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = r0 + i < nv ? r0 + i : nv - 1;
+      const uint32_t off = uint32_t(r * rsk + 64 * ht + 4 * cq);
+      kraw[i] = ldraw4<true>(kb, off);
+      qraw[i] = ldraw4<true>(qb, off);
+      if (sg) {
+        const float g = ab[uint32_t(r * H)];
+        av[i] = make_float4(g, g, g, g);
+      } else {
+        av[i] = *reinterpret_cast<const float4*>(ab + off);
+      }
+      if (r0 + i >= nv) {
+        kraw[i] = make_uint2(0u, 0u);
+        qraw[i] = make_uint2(0u, 0u);
+        av[i] = one4;
+      }
+    }
+    if (t < kC) sBe[t] = t < nv ? p.beta[row0 + uint32_t(t * H)] : 0.f;
+
+    // ---- step 1: 8-row group products, then the decays of the own rows ----
+    const float4 own = mul4(mul4(av[0], av[1]), mul4(av[2], av[3]));
+    const float4 par = shfl4(own);   // the other 4 rows of the 8-row group
+    if ((g4 & 1) == 0) *reinterpret_cast<float4*>(sGP + (g4 >> 1) * DK + 64 * ht + 4 * cq) = mul4(own, par);
+    lds_barrier();
+    // rho_r = gamma_r / gamma_(16R+7), the decay of row r relative to its
+    // block's reference row, kept as the exact product ex: 1/rho for the rows
+    // up to the reference (prod_{r < s <= 16R+7} alpha_s), rho after it
+    // (prod_{16R+7 < s <= r} alpha_s); the other one is its reciprocal.
+    float4 ex[4];
+    const bool before = pos < 2;
+    if (before) {
+      float4 Q = pos == 0 ? par : one4;
+#pragma unroll
+      for (int i = 3; i >= 0; --i) {
+        ex[i] = Q;
+        Q = mul4(Q, av[i]);
+      }
+    } else {
+      float4 P = pos == 3 ? par : one4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        P = mul4(P, av[i]);
+        ex[i] = P;
+      }
+    }
+    auto rho_of = [&](int i) { return before ? rcp4(ex[i]) : ex[i]; };
+    auto irho_of = [&](int i) { return before ? ex[i] : rcp4(ex[i]); };
+    // Per-channel block vectors from the group products gp[G] (rows 8G..8G+7),
+    // one chain per wave of waves 0-3, lanes 0-31 = the 32 channel quads.
+    if (w < 4 && l < 32) {
+      const int c0 = 4 * l;
+      auto gp = [&](int G) { return *reinterpret_cast<const float4*>(sGP + G * DK + c0); };
+      auto st = [&](float* dst, float4 x) { *reinterpret_cast<float4*>(dst + c0) = x; };
+      if (w == 0) {
+        // gamma_mR = groups 0..2R; gamma_n = all groups
+        float4 x = gp(0);
+        st(sGM, x);
+        x = mul4(x, mul4(gp(1), gp(2)));
+        st(sGM + DK, x);
+        x = mul4(x, mul4(gp(3), gp(4)));
+        st(sGM + 2 * DK, x);
+        x = mul4(x, mul4(gp(5), gp(6)));
+        st(sGM + 3 * DK, x);
+        st(sGN, mul4(x, gp(7)));
+      } else if (w == 1) {
+        // gamma_n / gamma_mI = groups 2I+1 .. 7
+        float4 x = gp(7);
+        st(sGNM + 3 * DK, x);
+        x = mul4(x, mul4(gp(5), gp(6)));
+        st(sGNM + 2 * DK, x);
+        x = mul4(x, mul4(gp(3), gp(4)));
+        st(sGNM + DK, x);
+        st(sGNM, mul4(x, mul4(gp(1), gp(2))));
+      } else if (w == 2) {
+        // S1_I = group 2I+1;  E_(I+1),I = group 2I+2
+#pragma unroll
+        for (int II = 0; II < 3; ++II) {
+          st(sS1 + II * DK, gp(2 * II + 1));
+          st(sE + eidx(II + 1, II) * DK, gp(2 * II + 2));
+        }
+      } else {
+        // E_RI for R >= I + 2: groups 2I+2 .. 2R
+        const float4 e20 = mul4(mul4(gp(2), gp(3)), gp(4));
+        const float4 e31 = mul4(mul4(gp(4), gp(5)), gp(6));
+        st(sE + eidx(2, 0) * DK, e20);
+        st(sE + eidx(3, 1) * DK, e31);
+        st(sE + eidx(3, 0) * DK, mul4(e20, mul4(gp(5), gp(6))));
+      }
+    }
+    lds_barrier();
+    if (t < DK) reinterpret_cast<float*>(slot + SL::OFF_G)[t] = sGN[t];
+
+    // ---- step 2: Gram tiles over the two halves of the key channels -------
+    f4 acc[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) acc[j] = f4{0.f, 0.f, 0.f, 0.f};
+    int tT[3], tR[3], tI[3];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      if (ht == hh) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float4 kv = cvt4<true>(kraw[i]), qv = cvt4<true>(qraw[i]);
+          const float4 rh = rho_of(i);
+          const float4 a = mul4(kv, rh), b = mul4(qv, rh), cc = mul4(kv, irho_of(i));
+          const float xa[4] = {a.x, a.y, a.z, a.w}, xb[4] = {b.x, b.y, b.z, b.w};
+          const float xc[4] = {cc.x, cc.y, cc.z, cc.w};
+          st4<true>(sO0, L::P_H, r0 + i, 4 * cq, xa);
+          st4<true>(sO1, L::P_H, r0 + i, 4 * cq, xb);
+          st4<true>(sO2, L::P_H, r0 + i, 4 * cq, xc);
+        }
+      }
+      lds_barrier();
+      const float* s1h = sS1 + 64 * hh;
+      const float* eh = sE + 64 * hh;
+#define KDA_GROUP2(R_, I_, XD_)                                                                              \
+  gram_group_half<R_, I_, XD_>(sO0, sO1, sO2, s1h + (I_) * DK, eh + eidx(R_ > I_ ? R_ : 1, I_) * DK, acc); \
+  tT[0] = 0; tR[0] = R_; tI[0] = I_;                                                                          \
+  tT[1] = 1; tR[1] = R_; tI[1] = I_;                                                                          \
+  tT[2] = XD_; tR[2] = R_; tI[2] = R_;
+      switch (w) {
+        case 0: KDA_GROUP2(3, 0, 0) break;
+        case 1: KDA_GROUP2(3, 1, 1) break;
+        case 2: KDA_GROUP2(2, 0, 0) break;
+        case 3: KDA_GROUP2(2, 1, 1) break;
+        case 4: KDA_GROUP2(0, 0, -1) break;
+        case 5: KDA_GROUP2(1, 1, -1) break;
+        case 6: KDA_GROUP2(3, 2, -1) break;
+        default: KDA_GROUP2(1, 0, -1) break;
+      }
+#undef KDA_GROUP2
+      // K_e^T of this half = (Kr Diag(gamma_n / gamma_mI) per row block)^T:
+      // unit w = (row block w & 3, 32 channels w >> 2)
+      {
+        const int rb = w & 3, kc = w >> 2;
+        const float* sc = sGNM + rb * DK + 64 * hh;
+        const M::Frag a = M::load(sO2, L::P_H, 16 * rb, kc);
+        xpose32_bf<false>(a, rb, kc, sc[32 * kc + lr], sc[32 * kc + 16 + lr], sXS, L::P_H);
+      }
+      // Q_g of this half = Ql Diag(gamma_mR) per row block: fragment w
+      if constexpr (!NOO)
+        export_frag_half(slot + SL::OFF_Q + ((w >> 1) * 4 + 2 * hh + (w & 1)) * 2048, sO1, w >> 1, w & 1,
+                         sGM + 64 * hh);
+      lds_barrier();
+      // K_e^T rows (channels) 64hh.. to the slot: row blocks 4hh + (w >> 1)
+      export_frag_half(slot + SL::OFF_K + ((4 * hh + (w >> 1)) * 2 + (w & 1)) * 2048, sXS, w >> 1, w & 1,
+                       nullptr);
+    }
+
+    // A = beta * strict_lower, P = lower (the halves' operands are no longer
+    // read: the last barrier followed the last Gram products)
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      if (tT[j] >= 0) {
+        const int r = 16 * tR[j] + lr;
+        const int i0 = 16 * tI[j] + 4 * lg;
+        float x[4];
+        if (tT[j] == 1) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) x[q] = i0 + q <= r ? acc[j][q] : 0.f;
+          st4<true>(sP, L::P_H, r, i0, x);
+        } else {
+          const float be = sBe[r];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) x[q] = i0 + q < r ? be * acc[j][q] : 0.f;
+          *reinterpret_cast<float4*>(sA + r * L::P_AF + i0) = make_float4(x[0], x[1], x[2], x[3]);
+        }
+      }
+    }
+    if (w >= 6) {   // upper tiles of P are zero
+      const float z[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 3; ++e) {
+        const int blk = (w - 6) * 3 + e;   // (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
+        const int R = blk < 3 ? 0 : (blk < 5 ? 1 : 2);
+        const int I = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
+        st4<true>(sP, L::P_H, 16 * R + lr, 16 * I + 4 * lg, z);
+      }
+    }
+    lds_barrier();
+
+    // ---- step 3: T = (I + A)^-1 Diag(beta) (as in prep_chunk) -------------
+    if constexpr (!NOO) export_frag_half(slot + SL::OFF_P + w * 2048, sP, w >> 1, w & 1, nullptr);
+    if (w < 4) {
+      const int R = w;
+      const float* const Nb = sA + 16 * R * L::P_AF + 16 * R;
+      float* const Xb = sLi + 16 * R * L::P_AF + 16 * R;
+      f4 No, Nt, Xo;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        No[q] = Nb[(4 * lg + q) * L::P_AF + lr];
+        Nt[q] = Nb[lr * L::P_AF + 4 * lg + q];
+        Xo[q] = (4 * lg + q == lr ? 1.f : 0.f) - No[q];
+      }
+      const f4 zero = f4{0.f, 0.f, 0.f, 0.f};
+      f4 Po = mm16x16(Nt, No, zero), Pt = mm16x16(No, Nt, zero);
+#pragma unroll
+      for (int e = 0; e < 3; ++e) {
+        Xo = mm16x16(Pt, Xo, Xo);
+        if (e < 2) {
+          const f4 Po2 = mm16x16(Pt, Po, zero), Pt2 = mm16x16(Po, Pt, zero);
+          Po = Po2;
+          Pt = Pt2;
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) Xb[(4 * lg + q) * L::P_AF + lr] = Xo[q];
+    } else {
+      for (int e = t - 256; e < 6 * 256; e += 256) {
+        const int blk = e >> 8, rr = (e >> 4) & 15, cc = e & 15;
+        const int R = blk < 3 ? 0 : (blk < 5 ? 1 : 2);
+        const int I = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
+        sLi[(16 * R + rr) * L::P_AF + 16 * I + cc] = 0.f;
+      }
+    }
+    lds_barrier();
+#pragma unroll
+    for (int R = 1; R < 4; ++R) {
+      if (w < R) {
+        const int I = w;
+        f4 y = f4{0.f, 0.f, 0.f, 0.f};
+        for (int J = I; J < R; ++J) {
+          const float4 a4 = *reinterpret_cast<const float4*>(sA + (16 * R + lr) * L::P_AF + 16 * J + 4 * lg);
+          const float* bb = sLi + (16 * J + 4 * lg) * L::P_AF + 16 * I + lr;
+          y = mm16x16(f4{a4.x, a4.y, a4.z, a4.w}, f4{bb[0], bb[L::P_AF], bb[2 * L::P_AF], bb[3 * L::P_AF]}, y);
+        }
+        const float4 d4 = *reinterpret_cast<const float4*>(sLi + (16 * R + lr) * L::P_AF + 16 * R + 4 * lg);
+        const f4 x = mm16x16(f4{d4.x, d4.y, d4.z, d4.w}, y, f4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sLi[(16 * R + 4 * lg + q) * L::P_AF + 16 * I + lr] = -x[q];
+      }
+      lds_barrier();
+    }
+    // T = L^-1 Diag(beta) in place (split), while K_g of half 0 = Kl
+    // Diag(gamma_mR) goes into the A space (A is no longer read)
+    {
+      const int r = t >> 3, g8 = t & 7;
+      float x[8];
+      const float* src = sLi + r * L::P_AF + 8 * g8;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = src[i] * sBe[8 * g8 + i];
+      st8<true>(sT, L::P_H, r, 8 * g8, x);
+    }
+    auto put_kg = [&](char* dst, int hh) {
+      if (ht != hh) return;
+      const float4 gm = *reinterpret_cast<const float4*>(sGM + (g4 >> 2) * DK + 64 * hh + 4 * cq);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 a = mul4(mul4(cvt4<true>(kraw[i]), rho_of(i)), gm);
+        const float x[4] = {a.x, a.y, a.z, a.w};
+        st4<true>(dst, L::P_H, r0 + i, 4 * cq, x);
+      }
+    };
+    put_kg(sO0, 0);
+    // V in MFMA operand layout: lane (lr, lg) of wave w holds row 16 wr + lr,
+    // columns 32 cu + 8 lg .. +7 with cu = (w >> 2) + 2 vh, vh = 0, 1.
+    uint4 pv[2];
+    {
+      const char* vb = static_cast<const char*>(p.v) + row0 * DV * 2;
+      const int rv = 16 * wr + lr < nv ? 16 * wr + lr : nv - 1;
+#pragma unroll
+      for (int vh = 0; vh < 2; ++vh) {
+        const int cu = (w >> 2) + 2 * vh;
+        pv[vh] = *reinterpret_cast<const uint4*>(vb + uint32_t(rv * rsv + 32 * cu + 8 * lg) * 2);
+        if (16 * wr + lr >= nv) pv[vh] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+    lds_barrier();
+
+    // ---- folded products: W = T K_g, Uv = T V, per half -------------------
+    // Wave w: row block wr = w & 3 of T (zero past token 16 wr + 15), column
+    // blocks 2 (w >> 2) and 2 (w >> 2) + 1 of the half.
+    const int kmax = 16 * wr + 16;
+    M::Frag ta[2];
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) ta[kc] = M::load(sT, L::P_H, 16 * wr, kc);
+    auto xpose_kg = [&](const char* src, char* dst) {   // K_g (gamma_mR applied in put_kg) transposed
+      const int rb = w & 3, kc = w >> 2;
+      const M::Frag a = M::load(src, L::P_H, 16 * rb, kc);
+      xpose32_bf<false>(a, rb, kc, 1.f, 1.f, dst, L::P_H);
+    };
+    auto w_half = [&](const char* kgt, char* stage) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int nb = 2 * (w >> 2) + j;
+        f4 a = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc)
+          if (kc * 32 < kmax) a = M::mma(M::load(kgt, L::P_H, 16 * nb, kc), ta[kc], a);
+        const float x[4] = {a[0], a[1], a[2], a[3]};
+        st4<true>(stage, L::P_H, 16 * wr + lr, 16 * nb + 4 * lg, x);
+      }
+    };
+    auto w_export = [&](const char* stage, int hh) {
+      export_frag_half(slot + SL::OFF_W + ((w >> 1) * 4 + 2 * hh + (w & 1)) * 2048, stage, w >> 1, w & 1,
+                       nullptr);
+    };
+    auto v_xpose = [&](char* dst, int vh) {
+      M::Frag a;
+      a.hi = __builtin_bit_cast(bf8, pv[vh]);
+      a.lo = __builtin_bit_cast(bf8, make_uint4(0u, 0u, 0u, 0u));
+      xpose32_bf<true>(a, wr, w >> 2, 1.f, 1.f, dst, L::P_H);
+    };
+    auto u_half = [&](const char* vt, int vh) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int nb = 2 * (w >> 2) + j;
+        f4 a = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc)
+          if (kc * 32 < kmax) a = M::mma(ta[kc], M::load(vt, L::P_H, 16 * nb, kc), a);
+        *reinterpret_cast<f4*>(slot + SL::OFF_U + (wr * (DV / 16) + 4 * vh + nb) * 1024 + 16 * l) = a;
+      }
+    };
+    xpose_kg(sO0, sO1);   // K_g^T half 0 -> O1
+    lds_barrier();
+    w_half(sO1, sO0);     // W half 0 -> O0
+    lds_barrier();
+    w_export(sO0, 0);
+    put_kg(sO1, 1);       // K_g half 1 -> O1
+    lds_barrier();
+    xpose_kg(sO1, sO0);   // K_g^T half 1 -> O0
+    lds_barrier();
+    w_half(sO0, sO1);     // W half 1 -> O1
+    lds_barrier();
+    w_export(sO1, 1);
+    v_xpose(sO0, 0);      // V^T of value columns 0-63 -> O0
+    lds_barrier();
+    u_half(sO0, 0);
+    v_xpose(sO1, 1);      // V^T of value columns 64-127 -> O1
+    lds_barrier();
+    u_half(sO1, 1);
+    lds_barrier();
+  }
+}
+
 // acc += A B^T with the A fragments already in registers and B [16][K] in LDS;
 // K chunks kc >= n (wave-uniform) are zero in A and skipped.
 template <bool BF, int NKC>
@@ -1840,12 +2338,20 @@ void launch_staged_t(const Params& base, int64_t T, int nsub, hipStream_t st, ch
     sp.s_in = si == 0 ? base.s_in : state_ws;
     sp.s_out = si == nsegs - 1 ? base.s_out : state_ws;
     const int64_t items = sp.pairs * sp.nseg;
-    const unsigned ns = unsigned(items < cus ? items : cus);
     const bool noo = sp.snap && sp.states_only;   // the backward's checkpoints
-    if (noo)
-      hipLaunchKernelGGL((kda_stage_kernel<DK, DV, BF, true>), dim3(ns), dim3(Lay<DK>::NT), 0, st, sp);
-    else
-      hipLaunchKernelGGL((kda_stage_kernel<DK, DV, BF, false>), dim3(ns), dim3(Lay<DK>::NT), 0, st, sp);
+    if constexpr (DK == 128 && DV == 128 && BF) {
+      // one workgroup per item, two per compute unit
+      if (noo)
+        hipLaunchKernelGGL((kda_stage2_kernel<true>), dim3(unsigned(items)), dim3(Lay2::NT), 0, st, sp);
+      else
+        hipLaunchKernelGGL((kda_stage2_kernel<false>), dim3(unsigned(items)), dim3(Lay2::NT), 0, st, sp);
+    } else {
+      const unsigned ns = unsigned(items < cus ? items : cus);
+      if (noo)
+        hipLaunchKernelGGL((kda_stage_kernel<DK, DV, BF, true>), dim3(ns), dim3(Lay<DK>::NT), 0, st, sp);
+      else
+        hipLaunchKernelGGL((kda_stage_kernel<DK, DV, BF, false>), dim3(ns), dim3(Lay<DK>::NT), 0, st, sp);
+    }
     const unsigned nb = unsigned(sp.pairs * sp.nslab);
     if (noo) {
       if (nsub == 4)
