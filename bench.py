@@ -536,7 +536,8 @@ def main():
     # Which prefill form the library takes for this shape (the same rule as in
     # the library: the staged two-kernel form below 128 (sequence, head) pairs).
     staged = B * H < 128 and T > 64
-    pre_kernels = ("kda_stage_kernel + kda_chain_kernel (staged form: one pair of launches per "
+    stage_name = "kda_stage2_kernel" if D == 128 else "kda_stage_kernel"
+    pre_kernels = (f"{stage_name} + kda_chain_kernel (staged form: one pair of launches per "
                    "segment of chunks)"
                    if staged else "kda_prefill_kernel")
     out = {
