@@ -115,12 +115,23 @@ __global__ __launch_bounds__(kThreads) void kda_decode_kernel(PoolDecodeArgs p) 
   }
   float* __restrict__ state = p.pool + (int64_t(slot) * p.H + (pair - n * p.H)) * DK * DV + c0;
 
-  // Small per-pair vectors.
+  // The small per-pair vectors and this thread's slice of the state are all
+  // loaded before any of them is used, so that the workgroup waits for one
+  // memory latency, not three.  (Threads past DK or kVC read a valid element
+  // they do not use.)
+  const int tk = t < DK ? t : DK - 1;
+  const float kk = load_in<BF16>(k, pair * DK + tk);
+  const float qq = load_in<BF16>(q, pair * DK + tk);
+  const float aa = alpha[p.alpha_scalar ? pair : pair * DK + tk];
+  const float vv = load_in<BF16>(v, pair * DV + c0 + (t < kVC ? t : 0));
+  const float bb = beta[pair];
+  float4* S4 = reinterpret_cast<float4*>(state);
+  float4 s[RPT];
+#pragma unroll
+  for (int m = 0; m < RPT; ++m) s[m] = ld_nt(&S4[(rg + RG * m) * (DV / 4) + cg]);
+
   float kq_part = 0.f;
   if (t < DK) {
-    const float kk = load_in<BF16>(k, pair * DK + t);
-    const float qq = load_in<BF16>(q, pair * DK + t);
-    const float aa = p.alpha_scalar ? alpha[pair] : alpha[pair * DK + t];
     s_ak[t] = aa * kk;
     s_aq[t] = aa * qq;
     s_a[t] = aa;
@@ -130,12 +141,6 @@ __global__ __launch_bounds__(kThreads) void kda_decode_kernel(PoolDecodeArgs p) 
   // k . q: wave reduction then LDS.
   for (int off = 32; off > 0; off >>= 1) kq_part += __shfl_xor(kq_part, off);
   if ((t & 63) == 0) s_kq[t >> 6] = kq_part;
-
-  // Stream this thread's slice of the state into registers.
-  float4* S4 = reinterpret_cast<float4*>(state);
-  float4 s[RPT];
-#pragma unroll
-  for (int m = 0; m < RPT; ++m) s[m] = ld_nt(&S4[(rg + RG * m) * (DV / 4) + cg]);
   __syncthreads();
 
   // Partial column sums over this thread's rows.
@@ -165,7 +170,7 @@ __global__ __launch_bounds__(kThreads) void kda_decode_kernel(PoolDecodeArgs p) 
     float kq = 0.f;
 #pragma unroll
     for (int w = 0; w < kThreads / 64; ++w) kq += s_kq[w];
-    const float u = beta[pair] * (load_in<BF16>(v, pair * DV + c0 + t) - p);
+    const float u = bb * (vv - p);
     s_u[t] = u;
     o[pair * DV + c0 + t] = r + kq * u;
   }
@@ -230,16 +235,16 @@ __global__ __launch_bounds__(kThreads) void kda_decode_pool_kernel(PoolDecodeArg
   // Token j of this (sequence, head) is row (n*L + j)*H + h of the inputs.
   auto row_of = [&](int j) { return (n * L + j) * H + h; };
   float pk = 0.f, pq = 0.f, pa = 0.f, pv = 0.f, pb = 0.f;   // next token's inputs
+  // Unconditional loads (threads past DK or kVC read an element they do not
+  // use): loads under a branch make the compiler wait for them at the join,
+  // before the state loads that follow are issued.
+  const int tk = t < DK ? t : DK - 1, tv = t < kVC ? t : 0;
   auto load_token = [&](int64_t r) {
-    if (t < DK) {
-      pk = load_in<BF16>(p.k, r * DK + t);
-      pq = load_in<BF16>(p.q, r * DK + t);
-      pa = p.alpha_scalar ? p.alpha[r] : p.alpha[r * DK + t];
-    }
-    if (t < kVC) {
-      pv = load_in<BF16>(p.v, r * DV + c0 + t);
-      pb = p.beta[r];
-    }
+    pk = load_in<BF16>(p.k, r * DK + tk);
+    pq = load_in<BF16>(p.q, r * DK + tk);
+    pa = p.alpha[p.alpha_scalar ? r : r * DK + tk];
+    pv = load_in<BF16>(p.v, r * DV + c0 + tv);
+    pb = p.beta[r];
   };
   load_token(row_of(0));
 

@@ -1614,8 +1614,12 @@ __device__ __forceinline__ void export_frag_half(char* dst, const char* src, int
   *reinterpret_cast<uint4*>(dst + 1024 + 16 * l) = lo;
 }
 
-// NOO: the call needs the states only (Q_g and P are not stored).
-template <bool NOO>
+// NOO: the call needs the states only (Q_g and P are not stored).  SG: one
+// gate per token and head (alpha is [tokens][H]); a template parameter, so
+// that the input loads are straight-line code: a run-time branch around each
+// alpha load made the compiler wait for every row's loads before issuing the
+// next row's.
+template <bool NOO, bool SG>
 __global__ __launch_bounds__(Lay2::NT, 4) void kda_stage2_kernel(StageParams p) {
   using L = Lay2;
   using M = Mma<true>;
@@ -1674,31 +1678,37 @@ __global__ __launch_bounds__(Lay2::NT, 4) void kda_stage2_kernel(StageParams p) 
     char* const slot = p.ws + it * int64_t(SL::BYTES);
 
     // ---- inputs (rows past the end: alpha = 1, k = q = 0) -----------------
-    const bool sg = p.alpha_scalar != 0;
-    const float* ab = p.alpha + (sg ? row0 : row0 * DK);
+    // All loads are issued first, the alphas (needed first) ahead of k and q,
+    // then the rows past the end are masked.
+    const float* ab = p.alpha + (SG ? row0 : row0 * DK);
     const char* kb = static_cast<const char*>(p.k) + row0 * DK * 2;
     const char* qb = static_cast<const char*>(p.q) + row0 * DK * 2;
     uint2 kraw[4], qraw[4];
     float4 av[4];
+    uint32_t roff[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = r0 + i < nv ? r0 + i : nv - 1;
-      const uint32_t off = uint32_t(r * rsk + 64 * ht + 4 * cq);
-      kraw[i] = ldraw4<true>(kb, off);
-      qraw[i] = ldraw4<true>(qb, off);
-      if (sg) {
-        const float g = ab[uint32_t(r * H)];
-        av[i] = make_float4(g, g, g, g);
-      } else {
-        av[i] = *reinterpret_cast<const float4*>(ab + off);
-      }
+      roff[i] = uint32_t(r * rsk + 64 * ht + 4 * cq);
+      if constexpr (SG) av[i].x = ab[uint32_t(r * H)];
+      else av[i] = *reinterpret_cast<const float4*>(ab + roff[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      kraw[i] = ldraw4<true>(kb, roff[i]);
+      qraw[i] = ldraw4<true>(qb, roff[i]);
+    }
+    const float bev = p.beta[row0 + uint32_t((t & 63) < nv ? (t & 63) : nv - 1) * H];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (SG) av[i] = make_float4(av[i].x, av[i].x, av[i].x, av[i].x);
       if (r0 + i >= nv) {
+        av[i] = one4;
         kraw[i] = make_uint2(0u, 0u);
         qraw[i] = make_uint2(0u, 0u);
-        av[i] = one4;
       }
     }
-    if (t < kC) sBe[t] = t < nv ? p.beta[row0 + uint32_t(t * H)] : 0.f;
+    if (t < kC) sBe[t] = t < nv ? bev : 0.f;
 
     // ---- step 1: 8-row group products, then the decays of the own rows ----
     const float4 own = mul4(mul4(av[0], av[1]), mul4(av[2], av[3]));
@@ -2341,10 +2351,14 @@ void launch_staged_t(const Params& base, int64_t T, int nsub, hipStream_t st, ch
     const bool noo = sp.snap && sp.states_only;   // the backward's checkpoints
     if constexpr (DK == 128 && DV == 128 && BF) {
       // one workgroup per item, two per compute unit
-      if (noo)
-        hipLaunchKernelGGL((kda_stage2_kernel<true>), dim3(unsigned(items)), dim3(Lay2::NT), 0, st, sp);
-      else
-        hipLaunchKernelGGL((kda_stage2_kernel<false>), dim3(unsigned(items)), dim3(Lay2::NT), 0, st, sp);
+      const dim3 grid{unsigned(items)}, block{unsigned(Lay2::NT)};
+      if (noo) {
+        if (sp.alpha_scalar) hipLaunchKernelGGL((kda_stage2_kernel<true, true>), grid, block, 0, st, sp);
+        else hipLaunchKernelGGL((kda_stage2_kernel<true, false>), grid, block, 0, st, sp);
+      } else {
+        if (sp.alpha_scalar) hipLaunchKernelGGL((kda_stage2_kernel<false, true>), grid, block, 0, st, sp);
+        else hipLaunchKernelGGL((kda_stage2_kernel<false, false>), grid, block, 0, st, sp);
+      }
     } else {
       const unsigned ns = unsigned(items < cus ? items : cus);
       if (noo)
