@@ -1021,15 +1021,13 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_prefill_kernel(Params p
     }
   };
   if (s0 < s1) load_chunk(s0, int(s1 - s0 < kC ? s1 - s0 : kC));
-  {
-    // Mirror the output stores that follow the prefetch in every later chunk,
-    // so that the first chunk and the steady state agree on how many memory
-    // operations are in flight after the prefetched loads (otherwise the
-    // compiler's wait for them degrades to waiting for every store).
-    volatile float* sink = g_kda_sink + (blockIdx.x & 255) * (kSinkStores * 64) + l;
-#pragma unroll
-    for (int i = 0; i < 4 * NSUB; ++i) *sink = 0.f;
-  }
+  // Mirror the output stores that follow the prefetch in every later chunk,
+  // so that the first chunk and the steady state agree on how many memory
+  // operations are in flight after the prefetched loads (otherwise the
+  // compiler's wait for them degrades to waiting for every store).  Plain
+  // stores to distinct addresses: volatile ones would each be followed by a
+  // wait for every memory operation in flight, the prefetch included.
+  mirror_stores<4 * NSUB>();
 
   for (int64_t tok0 = s0; tok0 < s1; tok0 += kC) {
     const int nv = int(s1 - tok0 < kC ? s1 - tok0 : kC);
@@ -2142,14 +2140,12 @@ __global__ __launch_bounds__(64 * (DK / 16), 1) void kda_chain_kernel(StageParam
     load_part2(A, s0);
     load_part3(A, s0);
   }
-  {
-    // The output stores that follow the prefetch in every chunk, mirrored
-    // before the first one (keeps the compiler's memory-counter waits for the
-    // prefetched operands from covering the stores as well).
-    volatile float* sink = g_kda_sink + (blockIdx.x & 255) * (kSinkStores * 64) + l;
-#pragma unroll
-    for (int i = 0; i < 4 * NSUB; ++i) *sink = 0.f;
-  }
+  // The output stores that follow the prefetch in every chunk, mirrored
+  // before the first one (keeps the compiler's memory-counter waits for the
+  // prefetched operands from covering the stores as well).  Plain stores to
+  // distinct addresses: volatile ones would each be followed by a wait for
+  // every memory operation in flight, the prefetch included.
+  mirror_stores<4 * NSUB>();
 
   // One chunk with operands `cur`; the next chunk's operands go to `nxt`
   // (past the last chunk the last one is loaded again: loads stay
