@@ -1871,7 +1871,10 @@ __global__ __launch_bounds__(Lay2::NT, 4) void kda_stage2_kernel(StageParams p) 
     lds_barrier();
 
     // ---- step 3: T = (I + A)^-1 Diag(beta) (as in prep_chunk) -------------
-    if constexpr (!NOO) export_frag_half(slot + SL::OFF_P + w * 2048, sP, w >> 1, w & 1, nullptr);
+    // (fragments 1 and 3, K = 32..63 of row blocks 0 and 1, are zero and never
+    // read: the state pass takes the nonzero K chunks of P only)
+    if constexpr (!NOO)
+      if (w != 1 && w != 3) export_frag_half(slot + SL::OFF_P + w * 2048, sP, w >> 1, w & 1, nullptr);
     if (w < 4) {
       const int R = w;
       const float* const Nb = sA + 16 * R * L::P_AF + 16 * R;
