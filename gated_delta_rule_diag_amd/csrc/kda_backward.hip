@@ -84,6 +84,13 @@ __device__ __forceinline__ float ld_in(const void* p, int64_t i) {
   }
 }
 
+// Row r of a chunk with nv >= 1 rows, clamped into the chunk.  Loads of rows
+// past the end read the last row and their values are discarded where they
+// are used: a load under a per-lane branch makes the compiler wait for it
+// before the branches join, which turns a loop of such loads into one memory
+// round trip per iteration.
+__device__ __forceinline__ int in_rows(int r, int nv) { return r < nv ? r : nv - 1; }
+
 // acc[s] += A(tile rows, 0:K) B(0:K, tile cols) for the tiles t = wv + 8 s of
 // the (M/16) x (N/16) tile grid (row-major), wv being the caller's wave slot
 // (wave-uniform; a slot past the grid does nothing).  All tiles of a wave
@@ -248,9 +255,12 @@ __device__ __forceinline__ void decays(const BwdChunkArgs& p, const Chunk& ck, f
   float a[kC];
 #pragma unroll
   for (int r = 0; r < kC; ++r) {
-    const int64_t row = (ck.tok0 + r) * p.H + ck.h;
-    a[r] = r < ck.nv ? (SG ? p.alpha[row] : p.alpha[row * DK + c]) : 1.f;
+    const int64_t row = (ck.tok0 + in_rows(r, ck.nv)) * p.H + ck.h;
+    a[r] = SG ? p.alpha[row] : p.alpha[row * DK + c];
   }
+#pragma unroll
+  for (int r = 0; r < kC; ++r)
+    if (r >= ck.nv) a[r] = 1.f;
   auto put = [&](int row, float v) {
     dg[row * DK + c] = v;
     if (row < kC) rho[row * ld + c] = v;
@@ -421,22 +431,26 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_prep_kernel(BwdChunkArgs p) {
   for (int u = 0; u < NE; ++u) {
     const int e = t + u * kNT;
     const int r = e / DK, c = e % DK;
-    const int64_t x = ((ck.tok0 + r) * H + h) * int64_t(DK) + c;
-    pk[u] = r < nv ? ld_in<BF16>(p.k, x) : 0.f;
-    pq[u] = r < nv ? ld_in<BF16>(p.q, x) : 0.f;
+    const int64_t x = ((ck.tok0 + in_rows(r, nv)) * H + h) * int64_t(DK) + c;
+    pk[u] = ld_in<BF16>(p.k, x);
+    pq[u] = ld_in<BF16>(p.q, x);
   }
   float* const rho_g = p.rho + ck.wi * (kDecayRows * DK);
   decays<DK, SG>(p, ck, sQr, LD, sVec, rho_g);   // rho parked in sQr
-  if (t < 64) sb[t] = t < nv ? p.beta[(ck.tok0 + t) * H + h] : 0.f;
+  {
+    const float bv = p.beta[(ck.tok0 + in_rows(t & 63, nv)) * H + h];
+    if (t < 64) sb[t] = t < nv ? bv : 0.f;
+  }
   lds_barrier();
 #pragma unroll
   for (int u = 0; u < NE; ++u) {
     const int e = t + u * kNT;
     const int r = e / DK, c = e % DK;
     const float rh = sQr[r * LD + c];
-    sKr[r * LD + c] = pk[u] * rh;
-    sKh[r * LD + c] = pk[u] / rh;
-    sQr[r * LD + c] = pq[u] * rh;
+    const float kv = r < nv ? pk[u] : 0.f, qv = r < nv ? pq[u] : 0.f;
+    sKr[r * LD + c] = kv * rh;
+    sKh[r * LD + c] = kv / rh;
+    sQr[r * LD + c] = qv * rh;
   }
   lds_barrier();
 
@@ -569,9 +583,9 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_prep_kernel(BwdChunkArgs p) {
     for (int u = 0; u < NR; ++u) {
       const int e = t + u * kNT;
       const int r = e >> 4, j = e & 15;
-      const int64_t x = ((ck.tok0 + r) * H + h) * int64_t(DV) + 16 * js + j;
-      R.v[u] = r < nv ? ld_in<BF16>(p.v, x) : 0.f;
-      R.o[u] = r < nv ? p.d_o[x] : 0.f;
+      const int64_t x = ((ck.tok0 + in_rows(r, nv)) * H + h) * int64_t(DV) + 16 * js + j;
+      R.v[u] = ld_in<BF16>(p.v, x);   // rows past the end: zeroed where stored
+      R.o[u] = p.d_o[x];
     }
 #pragma unroll
     for (int u = 0; u < NS; ++u) {
@@ -627,8 +641,8 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_prep_kernel(BwdChunkArgs p) {
 #pragma unroll
     for (int u = 0; u < NR; ++u) {
       const int e = t + u * kNT;
-      sV[(e >> 4) * kLS + (e & 15)] = R.v[u];
-      sO[(e >> 4) * kLS + (e & 15)] = R.o[u];
+      sV[(e >> 4) * kLS + (e & 15)] = (e >> 4) < nv ? R.v[u] : 0.f;
+      sO[(e >> 4) * kLS + (e & 15)] = (e >> 4) < nv ? R.o[u] : 0.f;
     }
 #pragma unroll
     for (int u = 0; u < NS; ++u) {
@@ -844,9 +858,9 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
     for (int u = 0; u < NR; ++u) {
       const int e = t + u * kNT;
       const int r = e >> 4, j = e & 15;
-      const int64_t x = ((ck.tok0 + r) * H + h) * int64_t(DV) + 16 * js + j;
-      R.o[u] = r < nv ? p.d_o[x] : 0.f;
-      R.v[u] = r < nv ? ld_in<BF16>(p.v, x) : 0.f;
+      const int64_t x = ((ck.tok0 + in_rows(r, nv)) * H + h) * int64_t(DV) + 16 * js + j;
+      R.o[u] = p.d_o[x];   // rows past the end: zeroed where stored
+      R.v[u] = ld_in<BF16>(p.v, x);
       R.vn[u] = Vng[r * DV + 16 * js + j];
     }
 #pragma unroll
@@ -862,24 +876,33 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
   // 1. decay vectors, beta, Kh, M, P
   for (int e = t; e < 8 * DK; e += kNT)
     sGM[e] = rho[(e < 4 * DK ? kGM * DK + e : kGNM * DK + e - 4 * DK)];
-  if (t < 64) sb[t] = t < nv ? p.beta[(ck.tok0 + t) * H + h] : 0.f;
+  {
+    const float bv = p.beta[(ck.tok0 + in_rows(t & 63, nv)) * H + h];
+    if (t < 64) sb[t] = t < nv ? bv : 0.f;
+  }
 #pragma unroll 8
   for (int u = 0; u < 64 * DK / kNT; ++u) {
     const int e = t + u * kNT;
     const int r = e / DK, c = e % DK;
     const float rh = rho[e];
-    const int64_t x = ((ck.tok0 + r) * H + h) * int64_t(DK) + c;
-    const float kv = r < nv ? ld_in<BF16>(p.k, x) : 0.f;
-    R1[r * LD + c] = kv / rh;
+    const float kv = ld_in<BF16>(p.k, ((ck.tok0 + in_rows(r, nv)) * H + h) * int64_t(DK) + c);
+    R1[r * LD + c] = (r < nv ? kv : 0.f) / rh;
   }
   {
     const float* const Mg = p.Mb + ck.wi * (64 * 64);
+    constexpr int NU = 64 * 64 / kNT;
+    float mv[NU], pv[NU];
 #pragma unroll
-    for (int u = 0; u < 64 * 64 / kNT; ++u) {
+    for (int u = 0; u < NU; ++u) {   // all loads first (P's upper part is read and dropped)
+      mv[u] = Mg[t + u * kNT];
+      pv[u] = PXg[t + u * kNT];
+    }
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
       const int e = t + u * kNT;
       const int r = e >> 6, c = e & 63;
-      sM[r * kL64 + c] = Mg[e];
-      sP[r * kL64 + c] = c <= r ? PXg[e] : 0.f;
+      sM[r * kL64 + c] = mv[u];
+      sP[r * kL64 + c] = c <= r ? pv[u] : 0.f;
     }
   }
   lds_barrier();
@@ -897,8 +920,8 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
     for (int u = 0; u < NR; ++u) {
       const int e = t + u * kNT;
       const int r = e >> 4, j = e & 15;
-      sO[r * kLS + j] = R.o[u];
-      sV[r * kLS + j] = R.v[u];
+      sO[r * kLS + j] = r < nv ? R.o[u] : 0.f;
+      sV[r * kLS + j] = r < nv ? R.v[u] : 0.f;
       sVn[r * kLS + j] = R.vn[u];
     }
 #pragma unroll
@@ -968,7 +991,7 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
   for (int u = 0; u < NE; ++u) {
     const int e = t + u * kNT;
     const int r = e / DK, c = e % DK;
-    pk[u] = r < nv ? ld_in<BF16>(p.k, ((ck.tok0 + r) * H + h) * int64_t(DK) + c) : 0.f;
+    pk[u] = ld_in<BF16>(p.k, ((ck.tok0 + in_rows(r, nv)) * H + h) * int64_t(DK) + c);
     pr[u] = rho[e];
   }
   f4 ahe[NT4];
@@ -1005,7 +1028,7 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
 #pragma unroll
   for (int u = 0; u < NE; ++u) {   // Kr
     const int e = t + u * kNT;
-    R3[(e / DK) * LD + e % DK] = pk[u] * pr[u];
+    R3[(e / DK) * LD + e % DK] = (e / DK < nv ? pk[u] : 0.f) * pr[u];
   }
   lds_barrier();
 
@@ -1016,7 +1039,7 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
   for (int u = 0; u < NE; ++u) {
     const int e = t + u * kNT;
     const int r = e / DK, c = e % DK;
-    pq[u] = r < nv ? ld_in<BF16>(p.q, ((ck.tok0 + r) * H + h) * int64_t(DK) + c) : 0.f;
+    pq[u] = ld_in<BF16>(p.q, ((ck.tok0 + in_rows(r, nv)) * H + h) * int64_t(DK) + c);
   }
   f4 ar[NT4];
   zero(ar);
@@ -1064,7 +1087,7 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
 #pragma unroll
   for (int u = 0; u < NE; ++u) {   // Qr
     const int e = t + u * kNT;
-    R2[(e / DK) * LD + e % DK] = pq[u] * pr[u];
+    R2[(e / DK) * LD + e % DK] = (e / DK < nv ? pq[u] : 0.f) * pr[u];
   }
   lds_barrier();
 
@@ -1166,13 +1189,13 @@ __global__ __launch_bounds__(kNT, 1) void kda_bwdc_post_kernel(BwdChunkArgs p) {
   float al[SG ? 1 : RP];
   if constexpr (SG) {
     const int r = t >> 3;
-    al[0] = r < nv ? p.alpha[(ck.tok0 + r) * H + h] : 1.f;
+    al[0] = p.alpha[(ck.tok0 + in_rows(r, nv)) * H + h];   // used for rows < nv only
   } else {
     const int c = t % DK, pp = t / DK;
 #pragma unroll
     for (int i = 0; i < RP; ++i) {
       const int r = pp * RP + i;
-      al[i] = r < nv ? p.alpha[((ck.tok0 + r) * H + h) * int64_t(DK) + c] : 1.f;
+      al[i] = p.alpha[((ck.tok0 + in_rows(r, nv)) * H + h) * int64_t(DK) + c];   // rows < nv only
     }
   }
 
