@@ -1684,6 +1684,9 @@ __global__ __launch_bounds__(Lay2::NT, 4) void kda_stage2_kernel(StageParams p) 
     uint2 kraw[4], qraw[4];
     float4 av[4];
     uint32_t roff[4];
+    // (beta first: it is stored to LDS before the barrier that the alphas
+    // need, and loads complete in order)
+    const float bev = p.beta[row0 + uint32_t((t & 63) < nv ? (t & 63) : nv - 1) * H];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = r0 + i < nv ? r0 + i : nv - 1;
@@ -1696,7 +1699,6 @@ __global__ __launch_bounds__(Lay2::NT, 4) void kda_stage2_kernel(StageParams p) 
       kraw[i] = ldraw4<true>(kb, roff[i]);
       qraw[i] = ldraw4<true>(qb, roff[i]);
     }
-    const float bev = p.beta[row0 + uint32_t((t & 63) < nv ? (t & 63) : nv - 1) * H];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if constexpr (SG) av[i] = make_float4(av[i].x, av[i].x, av[i].x, av[i].x);
