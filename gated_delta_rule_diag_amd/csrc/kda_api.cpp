@@ -549,13 +549,13 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // Workspace of a backward call: the forward's workspace (fixed length only) or
 // the buffers of one window of chunks, whichever is larger (they are not live
 // at the same time), one state per full chunk, and the adjoint carried between
-// windows.  (The forward runs in its states-only form, which writes no o.)  The reverse pass goes through the chunks
-// in windows of win_k chunks counted from each sequence's end, so that the
-// window buffers (backward_chunk_floats per chunk-head) take at most 4 GiB
-// whatever the length (the tuning override bwd_window forces a window size).  Packed
-// sequences: T_fixed = 0, max_chunks from the longest sequence, and the
-// snapshot rows are T_total / 64 (chunk j of the sequence starting at token s
-// is row s / 64 + j).
+// windows.  (The forward runs in its states-only form, which writes no o.)
+// The reverse pass goes through the chunks in windows of win_k chunks counted
+// from each sequence's end, so that the window buffers (backward_chunk_floats
+// per chunk-head) take at most 4 GiB whatever the length (the tuning override
+// bwd_window forces a window size).  Packed sequences: T_fixed = 0,
+// max_chunks from the longest sequence, and the snapshot rows are T_total / 64
+// (chunk j of the sequence starting at token s is row s / 64 + j).
 BwdLayout bwd_layout(int N, int T_fixed, int64_t T_total, int64_t max_chunks, int H, int DK,
                      int DV, bool varlen) {
   BwdLayout L{};
