@@ -103,6 +103,15 @@ def run_info(torch):
                                 text=True, timeout=10).stdout.strip() or None
     except (OSError, subprocess.SubprocessError):
         commit = None
+    # Git blob ids (what `git hash-object FILE` prints) of the measured code:
+    # they identify the committed files also where the tree runs without its
+    # history, so git_commit is null.
+    blobs = {}
+    for rel in ["bench.py", "include/kda.h", "gated_delta_rule_diag_amd/kda.py"] + \
+            [f"gated_delta_rule_diag_amd/csrc/{n}" for n in sorted(os.listdir(csrc))]:
+        with open(os.path.join(here, rel), "rb") as f:
+            data = f.read()
+        blobs[rel] = hashlib.sha1(b"blob %d\0" % len(data) + data).hexdigest()[:12]
     props = torch.cuda.get_device_properties(0)
     return {
         "gpu": torch.cuda.get_device_name(0),
@@ -112,6 +121,7 @@ def run_info(torch):
         "hip": torch.version.hip,
         "git_commit": commit,
         "kernel_source_sha256_16": h.hexdigest()[:16],
+        "git_blob_ids": blobs,
         "host_cpu": platform.processor() or platform.machine(),
     }
 

@@ -38,10 +38,11 @@ def hipcc():
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source and link libkda.so; returns its path."""
+    """Compile every source and link libkda.so; returns its path.  The sources
+    compile in parallel (one hipcc process each)."""
     out_dir = os.path.join(PKG, "_build")
     os.makedirs(out_dir, exist_ok=True)
-    objs = []
+    objs, procs = [], []
     for src in SOURCES:
         path = os.path.join(CSRC, src)
         obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
@@ -51,11 +52,16 @@ def build(verbose: bool = False) -> str:
                    "-I", CSRC, "-c", path, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
-        r = subprocess.run(cmd, capture_output=True, text=True)
-        if r.returncode != 0:
-            sys.stderr.write(r.stdout + r.stderr)
-            raise RuntimeError(f"compiling {src} failed")
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
         objs.append(obj)
+    failed = []
+    for src, pr in procs:
+        out, _ = pr.communicate()
+        if pr.returncode != 0:
+            sys.stderr.write(out)
+            failed.append(src)
+    if failed:
+        raise RuntimeError(f"compiling {', '.join(failed)} failed")
     tmp = LIB + ".tmp"
     cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp,
            "-L/opt/rocm/lib", "-lrocprofiler-sdk-roctx", "-Wl,-rpath,/opt/rocm/lib"]
