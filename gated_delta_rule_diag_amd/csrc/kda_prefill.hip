@@ -2028,6 +2028,7 @@ __device__ __forceinline__ f4 gemm_ra(f4 acc, const typename Mma<BF>::Frag (&a)[
 #pragma unroll
   for (int kc = 0; kc < NKC; ++kc)
     if (kc < n) b[kc] = M::load(B, bp, 0, kc);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int kc = 0; kc < NKC; ++kc)
     if (kc < n) acc = M::mma(a[kc], b[kc], acc);
