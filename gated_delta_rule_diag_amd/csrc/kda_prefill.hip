@@ -2019,7 +2019,10 @@ __global__ __launch_bounds__(Lay2::NT, 4) void kda_stage2_kernel(StageParams p) 
 }
 
 // acc += A B^T with the A fragments already in registers and B [16][K] in LDS;
-// K chunks kc >= n (wave-uniform) are zero in A and skipped.
+// K chunks kc >= n (wave-uniform) are zero in A and skipped.  Every B read is
+// issued before the first product: the scheduling barrier keeps the compiler
+// from interleaving one read per K chunk with the products, which waited for
+// the LDS once per K chunk on the state pass's critical path.
 template <bool BF, int NKC>
 __device__ __forceinline__ f4 gemm_ra(f4 acc, const typename Mma<BF>::Frag (&a)[NKC],
                                       const char* B, int bp, int n = NKC) {
