@@ -84,6 +84,22 @@ def cpu_baseline(seconds, q, k, v, a, b):
     }
 
 
+def source_blob_ids(here):
+    """Git blob ids (what `git hash-object FILE` prints, 12 hex digits) of the
+    measured code: they identify the committed files also where the tree runs
+    without its history (git_commit null)."""
+    import hashlib
+
+    csrc = os.path.join(here, "gated_delta_rule_diag_amd", "csrc")
+    blobs = {}
+    for rel in ["bench.py", "include/kda.h", "gated_delta_rule_diag_amd/kda.py"] + \
+            [f"gated_delta_rule_diag_amd/csrc/{n}" for n in sorted(os.listdir(csrc))]:
+        with open(os.path.join(here, rel), "rb") as f:
+            data = f.read()
+        blobs[rel] = hashlib.sha1(b"blob %d\0" % len(data) + data).hexdigest()[:12]
+    return blobs
+
+
 def run_info(torch):
     """What the evaluation pages ask a measurement to state besides the
     numbers: hardware, software versions and the code measured ("Kimi Linear、
@@ -103,15 +119,7 @@ def run_info(torch):
                                 text=True, timeout=10).stdout.strip() or None
     except (OSError, subprocess.SubprocessError):
         commit = None
-    # Git blob ids (what `git hash-object FILE` prints) of the measured code:
-    # they identify the committed files also where the tree runs without its
-    # history, so git_commit is null.
-    blobs = {}
-    for rel in ["bench.py", "include/kda.h", "gated_delta_rule_diag_amd/kda.py"] + \
-            [f"gated_delta_rule_diag_amd/csrc/{n}" for n in sorted(os.listdir(csrc))]:
-        with open(os.path.join(here, rel), "rb") as f:
-            data = f.read()
-        blobs[rel] = hashlib.sha1(b"blob %d\0" % len(data) + data).hexdigest()[:12]
+    blobs = source_blob_ids(here)
     props = torch.cuda.get_device_properties(0)
     return {
         "gpu": torch.cuda.get_device_name(0),

@@ -445,3 +445,21 @@ def test_noalloc_prefill_rejects_what_the_scratch_cannot_hold(lib):
                                          None) == SHAPE
     assert lib.kda_chunk_prefill_noalloc(0, 64, 2, 64, 64, 64, 1, q, k, v, a, b, s_in, o, s_out,
                                          None) == OK
+
+
+def test_bench_blob_ids_match_git_hash_object():
+    """bench.py names the measured files by their git blob ids: the same ids
+    `git hash-object` gives (checked where git and the history are present)."""
+    import shutil
+    import subprocess
+
+    import bench
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    ids = bench.source_blob_ids(root)
+    assert "gated_delta_rule_diag_amd/csrc/kda_prefill.hip" in ids and "include/kda.h" in ids
+    if shutil.which("git") is None or not os.path.isdir(os.path.join(root, ".git")):
+        pytest.skip("no git history here")
+    for rel, blob in ids.items():
+        out = subprocess.run(["git", "-C", root, "hash-object", rel], capture_output=True, text=True)
+        assert out.returncode == 0 and out.stdout.strip()[:12] == blob, rel
